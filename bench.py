@@ -1,0 +1,273 @@
+"""Benchmark of the paged GQA decode hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline] [--no-extras]
+
+A step is one attn_paged_decode call (split planner, paged split-KV kernel
+and log-sum-exp combine) over one batch of the workload, with every input
+already resident in HBM.  To keep reads cold, R independent input sets are
+rotated so that more than 1 GB is touched between two uses of a set (more
+than the 256 MB Infinity Cache plus the L2s).
+
+Prints ONE JSON line: value = algorithmic HBM bytes per call / measured time
+per call (GB/s); us_per_call beside it.  "roofline" covers the split kernel
+(timed alone with HIP events on the launch stream, same split count as the
+timed calls); "traffic" comes from the committed rocprofv3 counter summary
+when its recorded kernel-source hash matches the current source, else null.
+"cpu_baseline" times the CPU oracle on a bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+COUNTERS = os.path.join(ROOT, "profiles", "decode_split_b128_counters.json")
+DECODE_SRC = os.path.join(ROOT, "paged_kv_gqa_03_amd", "csrc", "decode.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="paged_b128",
+                    choices=["paged_b128", "paged_b32", "paged_b128_kv4096", "paged_b32_kv4096"])
+    ap.add_argument("--num-splits", type=int, default=0, help="0 = planner")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true")
+    return ap.parse_args()
+
+
+def decode_bytes(case):
+    """Algorithmic bytes of one paged decode call: every K and V row once,
+    the block-table entries used, kv_lens, Q read and O written."""
+    lens = case["kv_lens"].tolist()
+    ps, Hkv, D, B, Hq = case["page_size"], case["Hkv"], case["D"], case["B"], case["Hq"]
+    kv = sum(n * Hkv * D * 2 * 2 for n in lens)
+    bt = sum((n + ps - 1) // ps * 4 for n in lens)
+    return kv + bt + 4 * B + 2 * B * Hq * D * 2
+
+
+def make_sets(name, device, n_sets):
+    import workloads
+    B = 128 if "b128" in name else 32
+    fixed = 4096 if "kv4096" in name else None
+    base = 1004 if B == 128 else 1003
+    return [workloads.serving_paged_decode(B, device=device, fixed_len=fixed, seed=base + 7919 * r)
+            for r in range(n_sets)]
+
+
+def rotation_count(bytes_per_call):
+    """Input sets to rotate so >= 1.5 GB is read between two uses of a set."""
+    return max(2, math.ceil(1.5e9 / bytes_per_call))
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def load_traffic(bytes_per_launch):
+    """HBM traffic of one split-kernel launch from the committed counter
+    summary, or None when absent or taken on another kernel source."""
+    if not os.path.exists(COUNTERS):
+        return None
+    with open(COUNTERS) as f:
+        c = json.load(f)
+    if c.get("decode_src_sha256") != source_hash(DECODE_SRC):
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+def time_calls(torch, fn, sets, steps, warmup):
+    for i in range(warmup):
+        fn(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        fn(sets[i % len(sets)])
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps  # ms per call
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(every configuration fits one MI355X); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import paged_kv_gqa_03_amd as pa
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    probe = make_sets(args.workload, dev, 1)
+    per_call = decode_bytes(probe[0])
+    R = rotation_count(per_call)
+    sets = probe + make_sets(args.workload, dev, R)[1:]
+    for s in sets:
+        s["out"] = torch.empty_like(s["q"])
+        s["bytes"] = decode_bytes(s)
+    c0 = sets[0]
+    S = args.num_splits or pa.attn_plan_splits(c0["B"], c0["Hkv"], c0["Hq"] // c0["Hkv"], c0["max_kv_len"],
+                                               c0["page_size"])
+    max_len = max(s["max_kv_len"] for s in sets)
+    ws_bytes = pa.attn_decode_workspace_bytes(c0["B"], c0["Hq"], c0["D"], S)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+
+    def call(s):
+        pa.attn_paged_decode(s["q"], s["k_pool"], s["v_pool"], s["block_table"], s["kv_lens"], max_len,
+                             s["out"], s["page_size"], s["scale"], num_splits=S, workspace=ws)
+
+    # --- timed region: K whole calls --------------------------------------
+    torch.cuda.synchronize()
+    ms = time_calls(torch, call, sets, args.steps, args.warmup)
+    mean_bytes = sum(sets[i % R]["bytes"] for i in range(args.steps)) / args.steps
+    gbs = mean_bytes / (ms * 1e-3) / 1e9
+
+    # --- per-kernel breakdown with HIP events on the launch stream ---------
+    stream = torch.cuda.current_stream()
+    n_k = max(20, args.steps)
+    split_ms, comb_ms = [], []
+    if S > 1:
+        for i in range(args.warmup + n_k):
+            s = sets[i % R]
+            e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            e0.record(stream)
+            pa.attn_paged_decode_split(s["q"], s["k_pool"], s["v_pool"], s["block_table"], s["kv_lens"],
+                                       max_len, s["page_size"], s["scale"], S, ws)
+            e1.record(stream)
+            pa.attn_decode_combine(ws, s["B"], s["Hq"], s["D"], S, s["kv_lens"], max_len, s["out"])
+            e2.record(stream)
+            if i >= args.warmup:
+                split_ms.append((e0, e1, e2, s["bytes"]))
+        torch.cuda.synchronize()
+        ks = [(a.elapsed_time(b), b.elapsed_time(c), nb) for a, b, c, nb in split_ms]
+        k_ms = sum(k[0] for k in ks) / len(ks)
+        comb = sum(k[1] for k in ks) / len(ks)
+        k_bytes = sum(k[2] for k in ks) / len(ks)
+        kernel = "decode_split_kernel<128,4,paged> (fp32 partials)"
+    else:
+        k_ms, comb, k_bytes = ms, 0.0, mean_bytes
+        kernel = "decode_split_kernel<128,4,paged> (direct write)"
+    achieved = k_bytes / (k_ms * 1e-3) / 1e9
+    traffic = load_traffic(k_bytes)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kernel,
+                "kernel_us": round(k_ms * 1e3, 2), "combine_us": round(comb * 1e3, 2),
+                "algorithmic_bytes_per_launch": int(k_bytes)}
+
+    # --- CPU oracle on a bounded sample -------------------------------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        host = {k: (v.cpu() if torch.is_tensor(v) else v) for k, v in c0.items()
+                if k in ("q", "k_pool", "v_pool", "block_table", "kv_lens", "scale")}
+        lens = host["kv_lens"].tolist()
+        t_budget, m = 12.0, 1
+        spent, done_bytes = 0.0, 0
+        order = list(range(c0["B"]))
+        while spent < t_budget and m <= len(order):
+            idx = torch.tensor(order[:m])
+            sub = dict(q=host["q"][idx], k_pool=host["k_pool"], v_pool=host["v_pool"],
+                       block_table=host["block_table"][idx], kv_lens=host["kv_lens"][idx])
+            t0 = time.perf_counter()
+            oracle.paged_decode(sub["q"], sub["k_pool"], sub["v_pool"], sub["block_table"], sub["kv_lens"],
+                                host["scale"])
+            dt = time.perf_counter() - t0
+            spent += dt
+            sb = sum(n * c0["Hkv"] * c0["D"] * 4 + (n + 15) // 16 * 4 + 4 for n in lens[:m]) \
+                + 2 * m * c0["Hq"] * c0["D"] * 2
+            best = (dt, sb, m)
+            if m == len(order):
+                break
+            m = min(len(order), m * 2)
+        dt, sb, m = best
+        cpu = {"value": round(sb / dt / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
+               "kind": "oracle", "sample": "first %d of %d sequences of set 0 (%.2f s)" % (m, c0["B"], dt)}
+
+    # --- other workloads of the path (context lines, not the headline) -----
+    extras = {}
+    if not args.no_extras:
+        extras = run_extras(torch, pa, dev, args)
+
+    kv_desc = "4096" if "kv4096" in args.workload else "U[512,4096]"
+    line = {
+        "metric": "paged decode us/call + achieved HBM GB/s (% of peak) at B=32..128, kv 4K",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "us_per_call": round(ms * 1e3, 2),
+        "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16, pages scattered in a 1.5x pool)",
+        "config": {"workload": "paged GQA decode B=%d Hq=32 Hkv=8 D=128 page_size=16 kv_lens %s"
+                               % (c0["B"], kv_desc),
+                   "B": c0["B"], "Hq": 32, "Hkv": 8, "D": 128, "page_size": 16, "kv_lens": kv_desc,
+                   "num_splits": S, "rotation_sets": R, "algorithmic_bytes_per_call": int(mean_bytes)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extra": extras,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def run_extras(torch, pa, dev, args):
+    """Short timings of the other decode workloads (same protocol)."""
+    import workloads
+    out = {}
+    steps, warm = 20, 5
+    for name in ("paged_b32", "paged_b128_kv4096", "paged_b32_kv4096"):
+        probe = make_sets(name, dev, 1)
+        per = decode_bytes(probe[0])
+        R = rotation_count(per)
+        sets = probe + make_sets(name, dev, R)[1:]
+        mx = max(s["max_kv_len"] for s in sets)
+        c0 = sets[0]
+        S = pa.attn_plan_splits(c0["B"], 8, 4, mx, 16)
+        ws = torch.empty(max(256, pa.attn_decode_workspace_bytes(c0["B"], 32, 128, S)), dtype=torch.uint8,
+                         device=dev)
+        for s in sets:
+            s["out"] = torch.empty_like(s["q"])
+
+        def call(s):
+            pa.attn_paged_decode(s["q"], s["k_pool"], s["v_pool"], s["block_table"], s["kv_lens"], mx,
+                                 s["out"], 16, s["scale"], num_splits=S, workspace=ws)
+        ms = time_calls(torch, call, sets, steps, warm)
+        nb = sum(decode_bytes(sets[i % R]) for i in range(steps)) / steps
+        out[name] = {"us_per_call": round(ms * 1e3, 2), "GB/s": round(nb / (ms * 1e-3) / 1e9, 1),
+                     "hbm_peak_frac": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "num_splits": S,
+                     "rotation_sets": R}
+        del sets
+        torch.cuda.empty_cache()
+    # contiguous decode, B=16 Hq=32 Hkv=8 D=128 kv=2048 (bhld)
+    c = workloads.contiguous_decode(device=dev)
+    nb = 16 * 8 * 2048 * 128 * 4 + 2 * 16 * 32 * 128 * 2
+    R = rotation_count(nb)
+    cs = [c] + [workloads.contig_decode_case(1002 + 7919 * r, 16, 32, 8, 128, 2048, device=dev)
+                for r in range(1, R)]
+    for s in cs:
+        s["out"] = torch.empty_like(s["q"])
+    S = pa.attn_plan_splits(16, 8, 4, 2048, 0)
+    ws = torch.empty(max(256, pa.attn_decode_workspace_bytes(16, 32, 128, S)), dtype=torch.uint8, device=dev)
+
+    def ccall(s):
+        pa.attn_decode(s["q"], s["k"], s["v"], s["out"], s["scale"], num_splits=S, workspace=ws)
+    ms = time_calls(torch, ccall, cs, steps, warm)
+    out["contiguous_b16_kv2048"] = {"us_per_call": round(ms * 1e3, 2), "GB/s": round(nb / (ms * 1e-3) / 1e9, 1),
+                                    "hbm_peak_frac": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                    "num_splits": S, "rotation_sets": R}
+    return out
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,267 @@
+/*
+ * paged_attn.h -- C ABI of the MI355X (gfx950) paged GQA attention library.
+ *
+ * Grouped-query attention over a paged KV cache, as the AstrAI "CUDA
+ * Kernels" developer doc describes it (Overview table: attn_decode,
+ * attn_paged_decode, attn_paged_prefill), plus the fp8 sliding-window decode
+ * of native_swa_decode.py (nvfp4-megamoe-kernel).  Every function computes
+ * out = softmax(scale * q K^T + mask) V exactly, up to rounding.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller, except
+ *     where a parameter name ends in _host.  The library never allocates or
+ *     frees device memory, never synchronises the stream, and keeps no
+ *     state between calls besides the per-thread error message.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     and runs on the calling thread's current HIP device.
+ *   - Element types: q, k, v and outputs are bf16 (stored as uint16 bit
+ *     patterns); indices and lengths are int32 unless stated otherwise.
+ *   - Strides are in ELEMENTS of the tensor they describe.  The innermost
+ *     (head-dim) stride is 1.  Rows of bf16 data must start at 16-byte
+ *     aligned addresses: base pointers 16-byte aligned and every stride a
+ *     multiple of 8 elements; otherwise ATTN_ERR_UNSUPPORTED is returned
+ *     (there is no scalar fallback path).
+ *   - GQA head mapping: query head h reads KV head h / (Hq / Hkv), so
+ *     consecutive query heads share a KV head.
+ *   - A query row with no admissible key (empty sequence, everything masked)
+ *     produces an all-zero output row.
+ *   - Return value: ATTN_OK (0) or a negative ATTN_ERR_* code; then
+ *     attn_last_error() gives a message.  Argument checks happen before any
+ *     device work is enqueued, so a failed call leaves outputs untouched.
+ *     Bad device-side data (a block-table entry outside the pool, a length
+ *     above the stated maximum, a slot index beyond the cache) is undefined
+ *     behaviour: it is not checked on the device.
+ */
+#ifndef PAGED_ATTN_H
+#define PAGED_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_OK 0
+#define ATTN_ERR_INVALID_ARG (-1) /* null pointer, negative size, bad stride ... */
+#define ATTN_ERR_UNSUPPORTED (-2) /* valid but not built: head dim, alignment   */
+#define ATTN_ERR_WORKSPACE (-3)   /* workspace missing or too small              */
+#define ATTN_ERR_LAUNCH (-4)      /* the HIP runtime refused a launch            */
+
+/* Message for the last failed call on this thread ("" if none).  The
+ * pointer stays valid until the next call on the same thread. */
+const char *attn_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int attn_version(void);
+
+/* ------------------------------------------------------------ split plan */
+
+/*
+ * Split-count planner for decode (AstrAI csrc commit history: the commit
+ * that partitions KV across gridDim.z and sizes the split count to fill the
+ * device, and the later one that retargets it at a fixed total block count
+ * after a grid search).  Chooses S >= 1 so that the B * Hkv * S independent
+ * work units fill `num_cus` compute units (0 = query the current device).
+ * S = 1 means a single pass that writes the normalised output directly.
+ * page_size 0 plans for a contiguous source.  For a paged source S is at
+ * least ceil(max_kv_len / (510 * page_size)) (rounded to 16 tokens), the most
+ * pages one split's LDS slice of the block table holds; attn_paged_decode
+ * rejects a smaller explicit num_splits with ATTN_ERR_UNSUPPORTED.
+ * Host-only and deterministic; returns S, or a negative error code.
+ */
+int attn_plan_splits(int B, int Hkv, int G, int max_kv_len, int page_size, int num_cus);
+
+/*
+ * Tokens per split for a given split count: the KV range of sequence b is
+ * cut into chunks [s*chunk, (s+1)*chunk) clipped to kv_lens[b]; chunk is a
+ * multiple of 16.  Returns the chunk, or a negative error code.
+ */
+int attn_split_chunk(int max_kv_len, int num_splits);
+
+/*
+ * Bytes of device workspace that decode needs for S = num_splits:
+ *   o_part  float [S, B, Hq, D]   unnormalised partial outputs
+ *   ml_part float [S, B, Hq, 2]   (m, l) per partial, starting at the first
+ *                                 256-byte boundary after o_part
+ * m is a reference value in natural-log units of the scaled score and l the
+ * sum of exp(score - m) over the split; o = sum exp(score - m) v.  The split
+ * kernel writes every slot a non-empty split owns, so the workspace needs
+ * no initialisation (cf. the commit that switched alloc_split_partials to
+ * torch::empty).  attn_decode / attn_paged_decode with one split write the
+ * output directly and need no workspace; attn_paged_decode_split always
+ * does.  Returns 0 for empty shapes.
+ */
+size_t attn_decode_workspace_bytes(int B, int Hq, int D, int num_splits);
+
+/* ---------------------------------------------------------------- decode */
+
+/*
+ * Contiguous GQA decode, one query token per sequence (AstrAI "CUDA Kernels"
+ * doc, Overview: attn_decode, GQA decode with split-KV; layout-agnostic
+ * stride addressing from the csrc commit that added bhld/blhd strides).
+ *   q   [B, Hq, D]: element (b, h, d) at q + b*q_sb + h*q_sh + d
+ *   k,v [B, Hkv, L, D] logical: (b, g, j, d) at k + b*k_sb + g*k_sh + j*k_sl + d
+ *       (bhld and blhd are both stride choices)
+ *   o   [B, Hq, D]: (b, h, d) at o + b*o_sb + h*o_sh + d
+ *   kv_lens  device int32 [B], each in [0, kv_len]; NULL = all equal kv_len
+ *   scale    multiplies q.k before the softmax (normally 1/sqrt(D))
+ *   num_splits  0 = attn_plan_splits() on the current device, else S >= 1
+ *   workspace   >= attn_decode_workspace_bytes(B, Hq, D, S) bytes, device
+ * Supported: D in {64, 128}, G = Hq/Hkv in {1, 2, 4, 8}.
+ * Launches the split kernel and, when S > 1, the combine kernel.
+ */
+int attn_decode(const void *q, int64_t q_sb, int64_t q_sh,
+                const void *k, int64_t k_sb, int64_t k_sh, int64_t k_sl,
+                const void *v, int64_t v_sb, int64_t v_sh, int64_t v_sl,
+                void *o, int64_t o_sb, int64_t o_sh,
+                const int32_t *kv_lens, int kv_len,
+                int B, int Hq, int Hkv, int D, float scale, int num_splits,
+                void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Paged GQA decode (AstrAI "CUDA Kernels" doc, Overview: attn_paged_decode;
+ * per-element page lookup from the csrc commit that replaced the per-tile
+ * lookup, which works for any page size).
+ *   q      [B, Hq, D] as in attn_decode
+ *   k_pool, v_pool  paged pools sharing one addressing: element
+ *          (page, slot, g, d) at pool + page*kv_s_page + slot*kv_s_slot
+ *          + g*kv_s_head + d  ([P, ps, Hkv, D] and [P, Hkv, ps, D] both fit)
+ *   block_table  int32, row b at block_table + b*bt_sb; logical token j of
+ *          sequence b lives in page block_table[b*bt_sb + j/page_size] at
+ *          slot j % page_size.  Entries past a sequence's last page are
+ *          never read.
+ *   kv_lens  int32 [B], each in [0, max_kv_len]
+ *   max_kv_len  host-side bound used to size the grid; max_kv_len *
+ *          page_size must stay below 2^32
+ *   o      [B, Hq, D] bf16 output
+ * Supported: D in {64, 128}, G in {1, 2, 4, 8}, any page_size >= 1.
+ */
+int attn_paged_decode(const void *q, int64_t q_sb, int64_t q_sh,
+                      const void *k_pool, const void *v_pool,
+                      int64_t kv_s_page, int64_t kv_s_slot, int64_t kv_s_head,
+                      const int32_t *block_table, int64_t bt_sb,
+                      const int32_t *kv_lens, int max_kv_len,
+                      void *o, int64_t o_sb, int64_t o_sh,
+                      int B, int Hq, int Hkv, int D, int page_size, float scale,
+                      int num_splits, void *workspace, size_t workspace_bytes,
+                      void *stream);
+
+/*
+ * The two halves of attn_paged_decode, for callers that schedule them
+ * separately (e.g. to combine partials gathered from several devices, or to
+ * time each kernel).  attn_paged_decode_split takes the arguments of
+ * attn_paged_decode minus the output and always writes fp32 partials for
+ * the effective split count into `workspace` (laid out as documented at
+ * attn_decode_workspace_bytes), even when S = 1.  attn_decode_combine then
+ * writes o [B, Hq, D] bf16 from that workspace; it must be given the same
+ * B, Hq, D, num_splits (after planning, i.e. the explicit S), kv_lens and
+ * max_kv_len, and reads only the splits that can hold keys of each sequence.
+ */
+int attn_paged_decode_split(const void *q, int64_t q_sb, int64_t q_sh,
+                            const void *k_pool, const void *v_pool,
+                            int64_t kv_s_page, int64_t kv_s_slot, int64_t kv_s_head,
+                            const int32_t *block_table, int64_t bt_sb,
+                            const int32_t *kv_lens, int max_kv_len,
+                            int B, int Hq, int Hkv, int D, int page_size, float scale,
+                            int num_splits, void *workspace, size_t workspace_bytes, void *stream);
+
+int attn_decode_combine(const void *workspace, size_t workspace_bytes, int B, int Hq, int D, int num_splits,
+                        const int32_t *kv_lens, int max_kv_len, void *o, int64_t o_sb, int64_t o_sh,
+                        void *stream);
+
+/*
+ * Log-sum-exp combine of split partials (AstrAI csrc commit history: the
+ * combine kernel that reduces the unnormalised (O, m, l) partials; one
+ * combine kernel serves every decode path).  Rows are independent:
+ *   o_part  float [S, R, D], ml_part float [S, R, 2] = (m, l), natural log
+ *   out_f32  NULL or float [R, D];  out_bf16 NULL or bf16 [R, D]
+ *   lse      NULL or float [R]: M + log(sum_s exp(m_s - M) l_s)
+ * out = sum_s exp(m_s - M) o_s / sum_s exp(m_s - M) l_s with M = max_s m_s;
+ * a partial with m = -inf contributes nothing; a row whose partials are all
+ * empty gives 0 (lse = -inf).  D in {64, 128}.
+ */
+int attn_split_combine(const float *o_part, const float *ml_part, int S, int R, int D,
+                       float *out_f32, void *out_bf16, float *lse, void *stream);
+
+/* --------------------------------------------------------------- prefill */
+
+/*
+ * Ragged work map (AstrAI "CUDA Kernels" doc, section "Q Scheduling and KV
+ * Addressing"): from per-sequence query lengths builds qo_indptr (prefix sum,
+ * B + 1 entries) and, for every tile of `tile_rows` query rows, the sequence
+ * it belongs to and its index inside that sequence, in sequence order.  All
+ * arrays are HOST memory.  Writes *num_tiles; fails with ATTN_ERR_INVALID_ARG
+ * if more than `cap` tiles would be needed.
+ */
+int attn_prefill_plan(const int32_t *q_lens_host, int B, int tile_rows,
+                      int32_t *qo_indptr_host, int32_t *tile_to_batch_host,
+                      int32_t *tile_to_index_host, int cap, int *num_tiles);
+
+/* Query rows per tile that attn_paged_prefill expects in its work map. */
+int attn_prefill_tile_rows(int D);
+
+/*
+ * Ragged paged prefill (AstrAI "CUDA Kernels" doc, Overview:
+ * attn_paged_prefill; "Q Scheduling and KV Addressing": packed Q schedule +
+ * paged KV source; csrc commits on the unified causal_offset and on 2-D/3-D
+ * masks that coexist with causality).
+ *   q  packed [total_q, Hq, D]: row r, head h at q + r*q_st + h*q_sh
+ *   qo_indptr  device int32 [B + 1]; sequence b owns rows
+ *          qo_indptr[b] .. qo_indptr[b+1]
+ *   tile_to_batch, tile_to_index  device copies of attn_prefill_plan's
+ *          output for tile_rows = attn_prefill_tile_rows(D); num_tiles tiles
+ *   k_pool, v_pool, kv_s_*, block_table, bt_sb, page_size  as in
+ *          attn_paged_decode; kv_lens [B] = keys held by each sequence
+ *          (prior context plus the new rows)
+ *   causal_offset  NULL = no causality; else device int32 [B]: -1 turns it
+ *          off for that sequence, c >= 0 admits key j for local row i iff
+ *          j <= c + i (c is the absolute position of the sequence's first
+ *          new row)
+ *   mask   NULL, or uint8 keep-mask (nonzero = keep): mask_ndim 2 reads
+ *          mask[b*m_sb + j], mask_ndim 3 reads mask[b*m_sb + i*m_sq + j]
+ *          with i the local row; combined with causality by AND
+ *   o      packed [total_q, Hq, D] bf16: row r, head h at o + r*o_st + h*o_sh
+ * Supported: D = 128, G in {1, 2, 4, 8}.
+ */
+int attn_paged_prefill(const void *q, int64_t q_st, int64_t q_sh, const int32_t *qo_indptr,
+                       const int32_t *tile_to_batch, const int32_t *tile_to_index, int num_tiles,
+                       const void *k_pool, const void *v_pool,
+                       int64_t kv_s_page, int64_t kv_s_slot, int64_t kv_s_head,
+                       const int32_t *block_table, int64_t bt_sb, const int32_t *kv_lens,
+                       const int32_t *causal_offset,
+                       const uint8_t *mask, int mask_ndim, int64_t m_sb, int64_t m_sq,
+                       void *o, int64_t o_st, int64_t o_sh,
+                       int B, int Hq, int Hkv, int D, int page_size, float scale,
+                       void *stream);
+
+/* --------------------------------------------------- fp8 sliding window */
+
+/*
+ * fp8 sliding-window decode, MLA style with K = V (native_swa_decode.py:
+ * the host wrapper's signature and the batched-SDPA fallback's steps).
+ *   q       [T, NH, HD] bf16: (t, h, d) at q + t*q_st + h*q_sh + d
+ *   kv_cache  uint8 OCP e4m3fn codes; slot idx lives at
+ *           kv_cache + (idx / block_size)*c_sb + (idx % block_size)*c_ss
+ *   inv_scale  bf16 per slot at inv_scale + idx*s_ss; the dequantised row
+ *           is e4m3(code) * inv_scale (exact product)
+ *   swa_indices int64 [T, W], row t at swa_indices + t*i_st
+ *   swa_lens    int64 [T]; window position j of token t is admitted iff
+ *           j < swa_lens[t] and swa_indices[t, j] >= 0
+ *   o       [T, NH, HD] bf16
+ * Every head of a token attends the same rows (K = V).  Supported: HD = 512,
+ * NH a multiple of 16, W <= 1024; slots must lie below num_blocks*block_size.
+ */
+int attn_swa_fp8_decode(const void *q, int64_t q_st, int64_t q_sh,
+                        const uint8_t *kv_cache, int64_t c_sb, int64_t c_ss,
+                        const void *inv_scale, int64_t s_ss,
+                        const int64_t *swa_indices, int64_t i_st, const int64_t *swa_lens,
+                        void *o, int64_t o_st, int64_t o_sh,
+                        int T, int NH, int HD, int window, int block_size, int num_blocks,
+                        float scale, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_ATTN_H */

@@ -1,0 +1,275 @@
+"""Python binding of libpaged_attn.so (gfx950 paged GQA attention).
+
+Argument marshalling only: every function below forwards device pointers,
+element strides and sizes of torch tensors to the C entry point of the same
+name (include/paged_attn.h) and raises AttnError when it returns an error.
+All compute runs in the HIP kernels.  There is no fallback: if the library is
+not built, every call raises.
+"""
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "AttnError", "lib", "attn_version", "attn_last_error", "attn_plan_splits", "attn_split_chunk",
+    "attn_decode_workspace_bytes", "attn_decode", "attn_paged_decode", "attn_paged_decode_split",
+    "attn_decode_combine", "attn_split_combine",
+    "attn_prefill_plan", "attn_prefill_tile_rows", "attn_paged_prefill", "attn_swa_fp8_decode",
+    "EXPORTED_SYMBOLS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpaged_attn.so")
+
+ATTN_OK = 0
+ATTN_ERR_INVALID_ARG = -1
+ATTN_ERR_UNSUPPORTED = -2
+ATTN_ERR_WORKSPACE = -3
+ATTN_ERR_LAUNCH = -4
+
+_P, _I, _L, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+_SIGS = {
+    "attn_last_error": ([], ctypes.c_char_p),
+    "attn_version": ([], _I),
+    "attn_plan_splits": ([_I, _I, _I, _I, _I, _I], _I),
+    "attn_split_chunk": ([_I, _I], _I),
+    "attn_decode_workspace_bytes": ([_I, _I, _I, _I], _Z),
+    "attn_decode": ([_P, _L, _L, _P, _L, _L, _L, _P, _L, _L, _L, _P, _L, _L, _P, _I,
+                     _I, _I, _I, _I, _F, _I, _P, _Z, _P], _I),
+    "attn_paged_decode": ([_P, _L, _L, _P, _P, _L, _L, _L, _P, _L, _P, _I, _P, _L, _L,
+                           _I, _I, _I, _I, _I, _F, _I, _P, _Z, _P], _I),
+    "attn_paged_decode_split": ([_P, _L, _L, _P, _P, _L, _L, _L, _P, _L, _P, _I,
+                                 _I, _I, _I, _I, _I, _F, _I, _P, _Z, _P], _I),
+    "attn_decode_combine": ([_P, _Z, _I, _I, _I, _I, _P, _I, _P, _L, _L, _P], _I),
+    "attn_split_combine": ([_P, _P, _I, _I, _I, _P, _P, _P, _P], _I),
+    "attn_prefill_plan": ([_P, _I, _I, _P, _P, _P, _I, _P], _I),
+    "attn_prefill_tile_rows": ([_I], _I),
+    "attn_paged_prefill": ([_P, _L, _L, _P, _P, _P, _I, _P, _P, _L, _L, _L, _P, _L, _P, _P,
+                            _P, _I, _L, _L, _P, _L, _L, _I, _I, _I, _I, _I, _F, _P], _I),
+    "attn_swa_fp8_decode": ([_P, _L, _L, _P, _L, _L, _P, _L, _P, _L, _P, _P, _L, _L,
+                             _I, _I, _I, _I, _I, _I, _F, _P], _I),
+}
+EXPORTED_SYMBOLS = tuple(_SIGS)
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__("%s (code %d)" % (msg, code))
+        self.code = code
+
+
+def lib():
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libpaged_attn.so is not built (python -m paged_kv_gqa_03_amd.build)")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            fn = getattr(l, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = l
+    return _lib
+
+
+def attn_last_error():
+    return lib().attn_last_error().decode()
+
+
+def _check(rc):
+    if rc != ATTN_OK:
+        raise AttnError(rc, attn_last_error())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _unit_inner(*ts):
+    for t in ts:
+        if t is not None and t.stride(-1) != 1:
+            raise ValueError("innermost stride must be 1")
+
+
+def attn_version():
+    return lib().attn_version()
+
+
+def attn_plan_splits(B, Hkv, G, max_kv_len, page_size, num_cus=0):
+    rc = lib().attn_plan_splits(B, Hkv, G, max_kv_len, page_size, num_cus)
+    if rc < 0:
+        _check(rc)
+    return rc
+
+
+def attn_split_chunk(max_kv_len, num_splits):
+    rc = lib().attn_split_chunk(max_kv_len, num_splits)
+    if rc < 0:
+        _check(rc)
+    return rc
+
+
+def attn_decode_workspace_bytes(B, Hq, D, num_splits):
+    return int(lib().attn_decode_workspace_bytes(B, Hq, D, num_splits))
+
+
+def _workspace(workspace, B, Hq, D, S, device):
+    if workspace is not None:
+        return workspace, workspace.numel() * workspace.element_size()
+    if S <= 1:
+        return None, 0
+    n = attn_decode_workspace_bytes(B, Hq, D, S)
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    return ws, n
+
+
+def attn_paged_decode(q, k_pool, v_pool, block_table, kv_lens, max_kv_len, out, page_size, scale,
+                      num_splits=0, workspace=None, stream=None, num_cus=0):
+    """q [B, Hq, D]; k_pool / v_pool 4-D (page, slot, head, dim) views with
+    identical strides; block_table [B, *] int32; kv_lens [B] int32; out
+    [B, Hq, D] bf16.  num_splits 0 asks the planner."""
+    _unit_inner(q, k_pool, v_pool, out, block_table)
+    assert k_pool.stride() == v_pool.stride(), "K and V pools must share strides"
+    B, Hq, D = q.shape
+    Hkv = k_pool.shape[2]
+    S = num_splits or attn_plan_splits(B, Hkv, Hq // Hkv, max_kv_len, page_size, num_cus)
+    ws, nbytes = _workspace(workspace, B, Hq, D, S, q.device)
+    _check(lib().attn_paged_decode(
+        _ptr(q), q.stride(0), q.stride(1), _ptr(k_pool), _ptr(v_pool),
+        k_pool.stride(0), k_pool.stride(1), k_pool.stride(2),
+        _ptr(block_table), block_table.stride(0), _ptr(kv_lens), int(max_kv_len),
+        _ptr(out), out.stride(0), out.stride(1), B, Hq, Hkv, D, int(page_size), float(scale),
+        int(S), _ptr(ws), nbytes, _stream(stream)))
+    return out
+
+
+def attn_paged_decode_split(q, k_pool, v_pool, block_table, kv_lens, max_kv_len, page_size, scale,
+                            num_splits, workspace, stream=None):
+    """Split kernel only: fp32 partials for `num_splits` splits into the
+    workspace (a uint8 device tensor of attn_decode_workspace_bytes)."""
+    _unit_inner(q, k_pool, v_pool, block_table)
+    assert k_pool.stride() == v_pool.stride()
+    B, Hq, D = q.shape
+    Hkv = k_pool.shape[2]
+    _check(lib().attn_paged_decode_split(
+        _ptr(q), q.stride(0), q.stride(1), _ptr(k_pool), _ptr(v_pool),
+        k_pool.stride(0), k_pool.stride(1), k_pool.stride(2),
+        _ptr(block_table), block_table.stride(0), _ptr(kv_lens), int(max_kv_len),
+        B, Hq, Hkv, D, int(page_size), float(scale), int(num_splits), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def attn_decode_combine(workspace, B, Hq, D, num_splits, kv_lens, max_kv_len, out, stream=None):
+    """Combine step of decode over a workspace filled by attn_paged_decode_split."""
+    _unit_inner(out)
+    _check(lib().attn_decode_combine(
+        _ptr(workspace), workspace.numel() * workspace.element_size(), int(B), int(Hq), int(D),
+        int(num_splits), _ptr(kv_lens), int(max_kv_len), _ptr(out), out.stride(0), out.stride(1),
+        _stream(stream)))
+    return out
+
+
+def attn_decode(q, k, v, out, scale, kv_lens=None, kv_len=None, num_splits=0, workspace=None,
+                stream=None, num_cus=0):
+    """q [B, Hq, D]; k, v 4-D (b, head, pos, dim) views; out [B, Hq, D]."""
+    _unit_inner(q, k, v, out)
+    B, Hq, D = q.shape
+    Hkv, L = k.shape[1], k.shape[2]
+    kv_len = L if kv_len is None else kv_len
+    S = num_splits or attn_plan_splits(B, Hkv, Hq // Hkv, kv_len, 0, num_cus)
+    ws, nbytes = _workspace(workspace, B, Hq, D, S, q.device)
+    _check(lib().attn_decode(
+        _ptr(q), q.stride(0), q.stride(1),
+        _ptr(k), k.stride(0), k.stride(1), k.stride(2),
+        _ptr(v), v.stride(0), v.stride(1), v.stride(2),
+        _ptr(out), out.stride(0), out.stride(1), _ptr(kv_lens), int(kv_len),
+        B, Hq, Hkv, D, float(scale), int(S), _ptr(ws), nbytes, _stream(stream)))
+    return out
+
+
+def attn_split_combine(o_part, ml_part, out_f32=None, out_bf16=None, lse=None, stream=None):
+    """o_part [S, R, D] float32, ml_part [S, R, 2] float32 (contiguous)."""
+    S, R, D = o_part.shape
+    assert o_part.is_contiguous() and ml_part.is_contiguous()
+    for t in (out_f32, out_bf16, lse):
+        assert t is None or t.is_contiguous()
+    _check(lib().attn_split_combine(_ptr(o_part), _ptr(ml_part), S, R, D, _ptr(out_f32),
+                                    _ptr(out_bf16), _ptr(lse), _stream(stream)))
+
+
+def attn_prefill_tile_rows(D):
+    rc = lib().attn_prefill_tile_rows(D)
+    if rc < 0:
+        _check(rc)
+    return rc
+
+
+def attn_prefill_plan(q_lens, tile_rows):
+    """Host work map: returns (qo_indptr, tile_to_batch, tile_to_index) as
+    int32 CPU tensors."""
+    q_lens = torch.as_tensor(q_lens, dtype=torch.int32).contiguous()
+    B = q_lens.numel()
+    cap = sum((int(x) + tile_rows - 1) // tile_rows for x in q_lens.tolist() if x > 0) + 1
+    indptr = torch.empty(B + 1, dtype=torch.int32)
+    t2b = torch.empty(cap, dtype=torch.int32)
+    t2i = torch.empty(cap, dtype=torch.int32)
+    n = ctypes.c_int(0)
+    _check(lib().attn_prefill_plan(_ptr(q_lens), B, int(tile_rows), _ptr(indptr), _ptr(t2b),
+                                   _ptr(t2i), cap, ctypes.byref(n)))
+    return indptr, t2b[:n.value].clone(), t2i[:n.value].clone()
+
+
+def attn_paged_prefill(q, qo_indptr, tile_to_batch, tile_to_index, k_pool, v_pool, block_table,
+                       kv_lens, out, page_size, scale, causal_offset=None, mask=None, stream=None):
+    """q / out packed [total_q, Hq, D]; work map and index arrays on the
+    device (int32); mask None, [B, kv] or [B, q, kv] uint8/bool keep-mask."""
+    _unit_inner(q, k_pool, v_pool, out, block_table)
+    assert k_pool.stride() == v_pool.stride()
+    total_q, Hq, D = q.shape
+    Hkv = k_pool.shape[2]
+    B = qo_indptr.numel() - 1
+    ndim, m_sb, m_sq = 0, 0, 0
+    if mask is not None:
+        if mask.dtype == torch.bool:
+            mask = mask.view(torch.uint8)
+        _unit_inner(mask)
+        ndim = mask.dim()
+        m_sb = mask.stride(0)
+        m_sq = mask.stride(1) if ndim == 3 else 0
+    _check(lib().attn_paged_prefill(
+        _ptr(q), q.stride(0), q.stride(1), _ptr(qo_indptr), _ptr(tile_to_batch), _ptr(tile_to_index),
+        int(tile_to_batch.numel()), _ptr(k_pool), _ptr(v_pool),
+        k_pool.stride(0), k_pool.stride(1), k_pool.stride(2), _ptr(block_table), block_table.stride(0),
+        _ptr(kv_lens), _ptr(causal_offset), _ptr(mask), ndim, m_sb, m_sq,
+        _ptr(out), out.stride(0), out.stride(1), B, Hq, Hkv, D, int(page_size), float(scale),
+        _stream(stream)))
+    return out
+
+
+def attn_swa_fp8_decode(q, kv_cache, inv_scale, swa_indices, swa_lens, out, block_size, scale,
+                        stream=None):
+    """q / out [T, NH, HD] bf16; kv_cache [num_blocks, block_size, HD] uint8
+    e4m3fn codes; inv_scale [max_slots, 1] bf16; swa_indices [T, W] int64;
+    swa_lens [T] int64."""
+    _unit_inner(q, kv_cache, swa_indices, out)
+    T, NH, HD = q.shape
+    W = swa_indices.shape[1]
+    num_blocks = kv_cache.shape[0]
+    _check(lib().attn_swa_fp8_decode(
+        _ptr(q), q.stride(0), q.stride(1), _ptr(kv_cache), kv_cache.stride(0), kv_cache.stride(1),
+        _ptr(inv_scale), inv_scale.stride(0), _ptr(swa_indices), swa_indices.stride(0), _ptr(swa_lens),
+        _ptr(out), out.stride(0), out.stride(1), T, NH, HD, W, int(block_size), num_blocks,
+        float(scale), _stream(stream)))
+    return out

@@ -1,0 +1,385 @@
+// api.hip -- the C ABI declared in include/paged_attn.h: argument checks,
+// the split planner, the ragged work map, workspace layout and launches.
+// Every check runs before anything is enqueued; nothing here allocates
+// device memory or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "kernels.hpp"
+#include "paged_attn.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int ok() {
+    g_err.clear();
+    return ATTN_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool mult8(int64_t s) { return (s & 7) == 0; }
+
+int launch_status(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(ATTN_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+int device_cus() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return -1;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+    return cus;
+}
+
+constexpr int kTileTokens = 16;   // decode tile; split chunks are multiples of it
+constexpr int kMaxSplits = 256;
+constexpr int kWavesPerCuTarget = 16;  // resident waves per CU the planner aims at
+
+// Longest split (tokens) whose block-table slice fits the kernel's LDS slice:
+// a chunk of c tokens spans at most (c - 1) / ps + 2 pages.
+int max_paged_chunk(int page_size) {
+    const long c = (long)(pa::kDecodeMaxSplitPages - 2) * page_size;
+    const long capped = c > (1L << 30) ? (1L << 30) : c;
+    return (int)(capped / kTileTokens * kTileTokens);
+}
+
+// page_size 0 stands for a contiguous source, which has no such limit.
+int min_paged_splits(int max_kv_len, int page_size) {
+    if (page_size <= 0) return 1;
+    const int c = max_paged_chunk(page_size);
+    return max_kv_len > 0 ? (max_kv_len + c - 1) / c : 1;
+}
+
+int chunk_for(int max_kv_len, int S) {
+    const int per = (max_kv_len + S - 1) / S;
+    const int chunk = ((per + kTileTokens - 1) / kTileTokens) * kTileTokens;
+    return chunk < kTileTokens ? kTileTokens : chunk;
+}
+
+int check_heads(int Hq, int Hkv, int D, int *G) {
+    if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0)
+        return fail(ATTN_ERR_INVALID_ARG, "Hq (%d) must be a positive multiple of Hkv (%d)", Hq, Hkv);
+    *G = Hq / Hkv;
+    if (*G != 1 && *G != 2 && *G != 4 && *G != 8)
+        return fail(ATTN_ERR_UNSUPPORTED, "group size Hq/Hkv = %d not built (1, 2, 4, 8)", *G);
+    return ATTN_OK;
+}
+
+size_t ws_ml_offset(int B, int Hq, int D, int S) {
+    const size_t o_bytes = (size_t)S * B * Hq * D * sizeof(float);
+    return (o_bytes + 255) & ~(size_t)255;
+}
+
+// Splits that can hold keys for a given requested count (always-empty
+// trailing splits are dropped) and the chunk they use.
+void effective_splits(int max_kv_len, int S, int *S_eff, int *chunk) {
+    *chunk = chunk_for(max_kv_len, S);
+    int s = max_kv_len > 0 ? (max_kv_len + *chunk - 1) / *chunk : 1;
+    *S_eff = s < 1 ? 1 : s;
+}
+
+int check_workspace(void *workspace, size_t workspace_bytes, int B, int Hq, int D, int S, bool need_any) {
+    if (!need_any && S == 1) return ATTN_OK;
+    const size_t need = attn_decode_workspace_bytes(B, Hq, D, S);
+    if (!workspace || workspace_bytes < need)
+        return fail(ATTN_ERR_WORKSPACE, "decode with %d splits needs %zu workspace bytes, got %zu", S, need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(ATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    return ATTN_OK;
+}
+
+pa::CombineParams decode_combine_params(const void *workspace, int B, int Hq, int D, int S, int chunk,
+                                        const int32_t *kv_lens, int kv_len_const, void *o, int64_t o_sb,
+                                        int64_t o_sh) {
+    pa::CombineParams c{};
+    c.o_part = static_cast<const float *>(workspace);
+    c.ml_part = reinterpret_cast<const float *>(static_cast<const char *>(workspace) + ws_ml_offset(B, Hq, D, S));
+    c.S = S;
+    c.R = B * Hq;
+    c.kv_lens = kv_lens;
+    c.kv_len_const = kv_len_const;
+    c.chunk = chunk;
+    c.rows_per_seq = Hq;
+    c.out_bf16 = static_cast<uint16_t *>(o);
+    c.o_sb = o_sb;
+    c.o_sh = o_sh;
+    return c;
+}
+
+// Shared tail of the decode entry points: splits, workspace, launches.
+// mode 0: split (+ combine when S > 1, direct write when S == 1);
+// mode 1: split kernel only, always writing fp32 partials.
+int run_decode(pa::DecodeParams &p, int D, int G, bool paged, int max_kv_len, int num_splits,
+               void *workspace, size_t workspace_bytes, int page_size, hipStream_t stream, int mode) {
+    int S = num_splits;
+    if (S == 0) {
+        S = attn_plan_splits(p.B, p.Hkv, G, max_kv_len, page_size, 0);
+        if (S < 0) return S;
+    }
+    if (S < 1 || S > kMaxSplits) return fail(ATTN_ERR_INVALID_ARG, "num_splits %d outside [1, %d]", S, kMaxSplits);
+    if (paged && S < min_paged_splits(max_kv_len, page_size))
+        return fail(ATTN_ERR_UNSUPPORTED,
+                    "paged decode with page_size %d needs >= %d splits for max_kv_len %d (got %d)", page_size,
+                    min_paged_splits(max_kv_len, page_size), max_kv_len, S);
+    effective_splits(max_kv_len, S, &S, &p.chunk);
+    p.S = S;
+    p.direct = (S == 1 && mode == 0) ? 1 : 0;
+    if (S == 1 && !paged) p.chunk = max_kv_len > 0 ? max_kv_len : 1;
+    p.units = p.B * p.Hkv * S;
+    int rc = check_workspace(workspace, workspace_bytes, p.B, p.Hq, D, S, mode == 1);
+    if (rc) return rc;
+    if (!p.direct) {
+        p.o_part = static_cast<float *>(workspace);
+        p.ml_part = reinterpret_cast<float *>(static_cast<char *>(workspace) + ws_ml_offset(p.B, p.Hq, D, S));
+    }
+    if (p.B == 0) return ok();
+    hipError_t e = pa::launch_decode(p, D, G, paged, stream);
+    if (e != hipSuccess) return launch_status(e, "decode split kernel");
+    if (mode == 0 && S > 1) {
+        pa::CombineParams c = decode_combine_params(workspace, p.B, p.Hq, D, S, p.chunk, p.kv_lens,
+                                                    p.kv_len_const, p.o, p.o_sb, p.o_sh);
+        e = pa::launch_combine(c, D, stream);
+        if (e != hipSuccess) return launch_status(e, "combine kernel");
+    }
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *attn_last_error(void) { return g_err.c_str(); }
+
+int attn_version(void) { return 100; }
+
+int attn_plan_splits(int B, int Hkv, int G, int max_kv_len, int page_size, int num_cus) {
+    if (B < 0 || Hkv <= 0 || G <= 0 || max_kv_len < 0 || page_size < 0)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_plan_splits: bad sizes");
+    if (num_cus <= 0) {
+        num_cus = device_cus();
+        if (num_cus <= 0) return fail(ATTN_ERR_LAUNCH, "attn_plan_splits: cannot query the device");
+    }
+    const long units = (long)B * Hkv;
+    if (units == 0 || max_kv_len <= kTileTokens) return min_paged_splits(max_kv_len, page_size);
+    const long target = (long)num_cus * kWavesPerCuTarget;
+    long S = (target + units - 1) / units;
+    const long max_by_len = (max_kv_len + 4 * kTileTokens - 1) / (4 * kTileTokens);  // >= 64 tokens a split
+    if (S > max_by_len) S = max_by_len;
+    if (S > kMaxSplits) S = kMaxSplits;
+    const long s_min = min_paged_splits(max_kv_len, page_size);
+    if (S < s_min) S = s_min;
+    if (S < 1) S = 1;
+    return (int)S;
+}
+
+int attn_split_chunk(int max_kv_len, int num_splits) {
+    if (max_kv_len < 0 || num_splits < 1) return fail(ATTN_ERR_INVALID_ARG, "attn_split_chunk: bad sizes");
+    return chunk_for(max_kv_len, num_splits);
+}
+
+size_t attn_decode_workspace_bytes(int B, int Hq, int D, int num_splits) {
+    if (B <= 0 || Hq <= 0 || D <= 0 || num_splits < 1) return 0;
+    return ws_ml_offset(B, Hq, D, num_splits) + (size_t)num_splits * B * Hq * 2 * sizeof(float);
+}
+
+int attn_decode(const void *q, int64_t q_sb, int64_t q_sh,
+                const void *k, int64_t k_sb, int64_t k_sh, int64_t k_sl,
+                const void *v, int64_t v_sb, int64_t v_sh, int64_t v_sl,
+                void *o, int64_t o_sb, int64_t o_sh,
+                const int32_t *kv_lens, int kv_len,
+                int B, int Hq, int Hkv, int D, float scale, int num_splits,
+                void *workspace, size_t workspace_bytes, void *stream) {
+    int G = 0, rc = check_heads(Hq, Hkv, D, &G);
+    if (rc) return rc;
+    if (B < 0 || kv_len < 0) return fail(ATTN_ERR_INVALID_ARG, "attn_decode: negative B or kv_len");
+    if (D != 64 && D != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_decode: head dim %d not built (64, 128)", D);
+    if (!q || !k || !v || !o) return fail(ATTN_ERR_INVALID_ARG, "attn_decode: null tensor pointer");
+    if (!std::isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "attn_decode: scale is not finite");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+        !mult8(q_sb) || !mult8(q_sh) || !mult8(k_sb) || !mult8(k_sh) || !mult8(k_sl) ||
+        !mult8(v_sb) || !mult8(v_sh) || !mult8(v_sl) || !mult8(o_sb) || !mult8(o_sh))
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_decode: rows must be 16-byte aligned (pointers, strides %% 8)");
+    pa::DecodeParams p{};
+    p.q = static_cast<const uint16_t *>(q);
+    p.q_sb = q_sb; p.q_sh = q_sh;
+    p.k = static_cast<const uint16_t *>(k);
+    p.v = static_cast<const uint16_t *>(v);
+    p.k_sb = k_sb; p.k_sh = k_sh; p.k_sl = k_sl;
+    p.v_sb = v_sb; p.v_sh = v_sh; p.v_sl = v_sl;
+    p.kv_lens = kv_lens;
+    p.kv_len_const = kv_len;
+    p.o = static_cast<uint16_t *>(o);
+    p.o_sb = o_sb; p.o_sh = o_sh;
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv;
+    p.sl2 = scale * 1.4426950408889634f;
+    return run_decode(p, D, G, false, kv_len, num_splits, workspace, workspace_bytes, 0,
+                      static_cast<hipStream_t>(stream), 0);
+}
+
+static int paged_decode_impl(const void *q, int64_t q_sb, int64_t q_sh,
+                             const void *k_pool, const void *v_pool,
+                             int64_t kv_s_page, int64_t kv_s_slot, int64_t kv_s_head,
+                             const int32_t *block_table, int64_t bt_sb,
+                             const int32_t *kv_lens, int max_kv_len,
+                             void *o, int64_t o_sb, int64_t o_sh,
+                             int B, int Hq, int Hkv, int D, int page_size, float scale,
+                             int num_splits, void *workspace, size_t workspace_bytes,
+                             void *stream, int mode) {
+    const char *fn = mode ? "attn_paged_decode_split" : "attn_paged_decode";
+    int G = 0, rc = check_heads(Hq, Hkv, D, &G);
+    if (rc) return rc;
+    if (B < 0 || max_kv_len < 0) return fail(ATTN_ERR_INVALID_ARG, "%s: negative B or max_kv_len", fn);
+    if (page_size <= 0) return fail(ATTN_ERR_INVALID_ARG, "%s: page_size must be >= 1", fn);
+    if ((uint64_t)max_kv_len * (uint64_t)page_size >= (1ull << 32))
+        return fail(ATTN_ERR_UNSUPPORTED, "%s: max_kv_len * page_size must be < 2^32", fn);
+    if (D != 64 && D != 128) return fail(ATTN_ERR_UNSUPPORTED, "%s: head dim %d not built (64, 128)", fn, D);
+    if (!q || !k_pool || !v_pool || (!o && mode == 0) || !block_table || !kv_lens)
+        return fail(ATTN_ERR_INVALID_ARG, "%s: null pointer", fn);
+    if (!std::isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "%s: scale is not finite", fn);
+    if (bt_sb < 0) return fail(ATTN_ERR_INVALID_ARG, "%s: negative block-table stride", fn);
+    if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(o) ||
+        !mult8(q_sb) || !mult8(q_sh) || !mult8(kv_s_page) || !mult8(kv_s_slot) || !mult8(kv_s_head) ||
+        !mult8(o_sb) || !mult8(o_sh))
+        return fail(ATTN_ERR_UNSUPPORTED, "%s: rows must be 16-byte aligned (pointers, strides %% 8)", fn);
+    pa::DecodeParams p{};
+    p.q = static_cast<const uint16_t *>(q);
+    p.q_sb = q_sb; p.q_sh = q_sh;
+    p.k = static_cast<const uint16_t *>(k_pool);
+    p.v = static_cast<const uint16_t *>(v_pool);
+    p.s_page = kv_s_page; p.s_slot = kv_s_slot; p.s_head = kv_s_head;
+    p.bt = block_table;
+    p.bt_sb = bt_sb;
+    p.ps = (uint32_t)page_size;
+    p.ps_magic = ((1ull << 32) + (uint64_t)page_size - 1) / (uint64_t)page_size;
+    p.kv_lens = kv_lens;
+    p.o = static_cast<uint16_t *>(o);
+    p.o_sb = o_sb; p.o_sh = o_sh;
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv;
+    p.sl2 = scale * 1.4426950408889634f;
+    return run_decode(p, D, G, true, max_kv_len, num_splits, workspace, workspace_bytes, page_size,
+                      static_cast<hipStream_t>(stream), mode);
+}
+
+int attn_paged_decode(const void *q, int64_t q_sb, int64_t q_sh,
+                      const void *k_pool, const void *v_pool,
+                      int64_t kv_s_page, int64_t kv_s_slot, int64_t kv_s_head,
+                      const int32_t *block_table, int64_t bt_sb,
+                      const int32_t *kv_lens, int max_kv_len,
+                      void *o, int64_t o_sb, int64_t o_sh,
+                      int B, int Hq, int Hkv, int D, int page_size, float scale,
+                      int num_splits, void *workspace, size_t workspace_bytes,
+                      void *stream) {
+    return paged_decode_impl(q, q_sb, q_sh, k_pool, v_pool, kv_s_page, kv_s_slot, kv_s_head, block_table,
+                             bt_sb, kv_lens, max_kv_len, o, o_sb, o_sh, B, Hq, Hkv, D, page_size, scale,
+                             num_splits, workspace, workspace_bytes, stream, 0);
+}
+
+int attn_paged_decode_split(const void *q, int64_t q_sb, int64_t q_sh,
+                            const void *k_pool, const void *v_pool,
+                            int64_t kv_s_page, int64_t kv_s_slot, int64_t kv_s_head,
+                            const int32_t *block_table, int64_t bt_sb,
+                            const int32_t *kv_lens, int max_kv_len,
+                            int B, int Hq, int Hkv, int D, int page_size, float scale,
+                            int num_splits, void *workspace, size_t workspace_bytes, void *stream) {
+    const void *o_dummy = q;  // never written in split-only mode; keeps the shared checks uniform
+    return paged_decode_impl(q, q_sb, q_sh, k_pool, v_pool, kv_s_page, kv_s_slot, kv_s_head, block_table,
+                             bt_sb, kv_lens, max_kv_len, const_cast<void *>(o_dummy), q_sb, q_sh, B, Hq, Hkv,
+                             D, page_size, scale, num_splits, workspace, workspace_bytes, stream, 1);
+}
+
+int attn_decode_combine(const void *workspace, size_t workspace_bytes, int B, int Hq, int D, int num_splits,
+                        const int32_t *kv_lens, int max_kv_len, void *o, int64_t o_sb, int64_t o_sh,
+                        void *stream) {
+    if (B < 0 || Hq <= 0 || max_kv_len < 0 || num_splits < 1 || num_splits > kMaxSplits)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_decode_combine: bad sizes");
+    if (D != 64 && D != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_combine: head dim %d not built", D);
+    if (!o) return fail(ATTN_ERR_INVALID_ARG, "attn_decode_combine: null output");
+    if (!aligned16(o) || !mult8(o_sb) || !mult8(o_sh))
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_combine: output rows must be 16-byte aligned");
+    int S = 0, chunk = 0;
+    effective_splits(max_kv_len, num_splits, &S, &chunk);
+    int rc = check_workspace(const_cast<void *>(workspace), workspace_bytes, B, Hq, D, S, true);
+    if (rc) return rc;
+    if (B == 0) return ok();
+    pa::CombineParams c = decode_combine_params(workspace, B, Hq, D, S, chunk, kv_lens, max_kv_len, o, o_sb, o_sh);
+    return launch_status(pa::launch_combine(c, D, static_cast<hipStream_t>(stream)), "combine kernel");
+}
+
+int attn_split_combine(const float *o_part, const float *ml_part, int S, int R, int D,
+                       float *out_f32, void *out_bf16, float *lse, void *stream) {
+    if (S < 1 || R < 0) return fail(ATTN_ERR_INVALID_ARG, "attn_split_combine: bad S or R");
+    if (D != 64 && D != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_split_combine: head dim %d not built", D);
+    if (!o_part || !ml_part) return fail(ATTN_ERR_INVALID_ARG, "attn_split_combine: null partials");
+    if (!out_f32 && !out_bf16 && !lse) return fail(ATTN_ERR_INVALID_ARG, "attn_split_combine: no output");
+    if (((uintptr_t)ml_part & 7u) || ((uintptr_t)o_part & 7u) || (out_bf16 && ((uintptr_t)out_bf16 & 3u)))
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_split_combine: misaligned buffers");
+    pa::CombineParams c{};
+    c.o_part = o_part;
+    c.ml_part = ml_part;
+    c.S = S;
+    c.R = R;
+    c.chunk = 0;
+    c.rows_per_seq = 1;
+    c.out_f32 = out_f32;
+    c.out_bf16 = static_cast<uint16_t *>(out_bf16);
+    c.o_sb = D;
+    c.o_sh = 0;
+    c.lse = lse;
+    return launch_status(pa::launch_combine(c, D, static_cast<hipStream_t>(stream)), "combine kernel");
+}
+
+int attn_prefill_plan(const int32_t *q_lens_host, int B, int tile_rows,
+                      int32_t *qo_indptr_host, int32_t *tile_to_batch_host,
+                      int32_t *tile_to_index_host, int cap, int *num_tiles) {
+    if (B < 0 || tile_rows <= 0 || !qo_indptr_host || !num_tiles || (B > 0 && !q_lens_host))
+        return fail(ATTN_ERR_INVALID_ARG, "attn_prefill_plan: bad arguments");
+    int t = 0;
+    qo_indptr_host[0] = 0;
+    for (int b = 0; b < B; ++b) {
+        if (q_lens_host[b] < 0) return fail(ATTN_ERR_INVALID_ARG, "attn_prefill_plan: negative q_len");
+        qo_indptr_host[b + 1] = qo_indptr_host[b] + q_lens_host[b];
+        const int tiles = (q_lens_host[b] + tile_rows - 1) / tile_rows;
+        for (int i = 0; i < tiles; ++i) {
+            if (t >= cap) return fail(ATTN_ERR_INVALID_ARG, "attn_prefill_plan: more than cap=%d tiles", cap);
+            tile_to_batch_host[t] = b;
+            tile_to_index_host[t] = i;
+            ++t;
+        }
+    }
+    *num_tiles = t;
+    return ok();
+}
+
+int attn_prefill_tile_rows(int D) { return D == 128 ? 64 : fail(ATTN_ERR_UNSUPPORTED, "prefill head dim %d", D); }
+
+int attn_paged_prefill(const void *, int64_t, int64_t, const int32_t *, const int32_t *, const int32_t *, int,
+                       const void *, const void *, int64_t, int64_t, int64_t, const int32_t *, int64_t,
+                       const int32_t *, const int32_t *, const uint8_t *, int, int64_t, int64_t, void *,
+                       int64_t, int64_t, int, int, int, int, int, float, void *) {
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_paged_prefill: not built yet");
+}
+
+int attn_swa_fp8_decode(const void *, int64_t, int64_t, const uint8_t *, int64_t, int64_t, const void *, int64_t,
+                        const int64_t *, int64_t, const int64_t *, void *, int64_t, int64_t, int, int, int, int,
+                        int, int, float, void *) {
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_swa_fp8_decode: not built yet");
+}
+
+}  // extern "C"

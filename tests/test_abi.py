@@ -1,0 +1,176 @@
+"""Host-side checks of the C ABI: the library loads and exports every symbol
+the header declares, host-only helpers (planner, chunking, workspace size,
+ragged work map) behave, and bad arguments are rejected before any device
+work.  No test here needs a GPU or makes a compute call."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+import torch
+
+import paged_kv_gqa_03_amd as pa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "paged_attn.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_path_entry_points():
+    names = declared_functions()
+    for n in ("attn_decode", "attn_paged_decode", "attn_paged_prefill", "attn_swa_fp8_decode",
+              "attn_split_combine", "attn_plan_splits", "attn_prefill_plan", "attn_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    l = ctypes.CDLL(pa.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(l, n), n
+    assert set(declared_functions()) == set(pa.EXPORTED_SYMBOLS)
+
+
+def test_version():
+    assert pa.attn_version() >= 100
+
+
+@pytest.mark.parametrize("B,Hkv,max_len", [(2, 2, 300), (16, 8, 2048), (32, 8, 4096), (128, 8, 4096),
+                                           (1, 1, 100000), (512, 8, 4096), (4, 8, 16), (3, 1, 0)])
+def test_planner_bounds(B, Hkv, max_len):
+    S = pa.attn_plan_splits(B, Hkv, 4, max_len, 16, 256)
+    assert 1 <= S <= 256
+    if max_len > 64:
+        chunk = pa.attn_split_chunk(max_len, S)
+        assert chunk % 16 == 0 and chunk >= 64 or S == 1
+    # a larger batch never asks for more splits
+    assert pa.attn_plan_splits(2 * B, Hkv, 4, max_len, 16, 256) <= S or max_len <= 16
+
+
+def test_planner_fills_the_device_for_small_batches():
+    S = pa.attn_plan_splits(16, 8, 4, 2048, 16, 256)
+    assert 16 * 8 * S >= 256 * 4
+
+
+def test_planner_respects_page_slice_limit():
+    # page_size 1 and a 4096-token sequence need at least ceil(4096 / 496) splits
+    S = pa.attn_plan_splits(512, 8, 4, 4096, 1, 256)
+    assert S >= 9
+    assert pa.attn_split_chunk(4096, S) <= 496
+
+
+def test_split_chunk_covers_the_range():
+    for L in (1, 15, 16, 17, 300, 2048, 4095):
+        for S in (1, 2, 3, 7, 64):
+            c = pa.attn_split_chunk(L, S)
+            assert c % 16 == 0 and c * S >= L and c >= 16
+
+
+def test_workspace_bytes_layout():
+    assert pa.attn_decode_workspace_bytes(0, 32, 128, 4) == 0
+    assert pa.attn_decode_workspace_bytes(32, 32, 128, 1) == 32 * 32 * 128 * 4 + 32 * 32 * 2 * 4
+    n = pa.attn_decode_workspace_bytes(32, 32, 128, 4)
+    o_bytes = 4 * 32 * 32 * 128 * 4
+    assert n == ((o_bytes + 255) // 256) * 256 + 4 * 32 * 32 * 2 * 4
+
+
+def test_work_map_matches_worked_example():
+    with open(os.path.join(GOLDEN, "ragged_work_map.json")) as f:
+        ex = json.load(f)
+    indptr, t2b, t2i = pa.attn_prefill_plan(ex["q_lens"], ex["tile_rows"])
+    assert indptr.tolist() == ex["qo_indptr"]
+    assert t2b.tolist() == ex["q_tile_to_batch"] and t2i.tolist() == ex["q_tile_to_index"]
+
+
+def test_work_map_matches_oracle_on_random_batches(orc):
+    g = torch.Generator().manual_seed(11)
+    for _ in range(40):
+        B = int(torch.randint(1, 12, (1,), generator=g))
+        lens = torch.randint(0, 700, (B,), generator=g).tolist()
+        R = int(torch.randint(1, 129, (1,), generator=g))
+        a = pa.attn_prefill_plan(lens, R)
+        b = orc.prefill_plan(lens, R)
+        for x, y in zip(a, b):
+            assert torch.equal(x, y)
+
+
+def test_work_map_rejects_small_cap():
+    lib = pa.lib()
+    lens = torch.tensor([70, 10, 130], dtype=torch.int32)
+    indptr = torch.empty(4, dtype=torch.int32)
+    t = torch.empty(8, dtype=torch.int32)
+    n = ctypes.c_int(0)
+    rc = lib.attn_prefill_plan(ctypes.c_void_p(lens.data_ptr()), 3, 64, ctypes.c_void_p(indptr.data_ptr()),
+                               ctypes.c_void_p(t.data_ptr()), ctypes.c_void_p(t.data_ptr()), 5, ctypes.byref(n))
+    assert rc == pa.ATTN_ERR_INVALID_ARG and "cap" in pa.attn_last_error()
+
+
+# --- argument validation (rejected on the host; no HIP call is made) -----
+FAKE = 1 << 20  # 16-byte aligned fake device address, never dereferenced
+
+
+def paged_args(**over):
+    a = dict(q=FAKE, q_sb=256, q_sh=64, k=FAKE, v=FAKE, s_page=16 * 2 * 64, s_slot=2 * 64, s_head=64,
+             bt=FAKE, bt_sb=32, lens=FAKE, max_len=300, o=FAKE, o_sb=256, o_sh=64,
+             B=2, Hq=8, Hkv=2, D=64, ps=16, scale=0.125, S=1, ws=None, ws_bytes=0)
+    a.update(over)
+    return a
+
+
+def call_paged(a):
+    return pa.lib().attn_paged_decode(
+        a["q"], a["q_sb"], a["q_sh"], a["k"], a["v"], a["s_page"], a["s_slot"], a["s_head"],
+        a["bt"], a["bt_sb"], a["lens"], a["max_len"], a["o"], a["o_sb"], a["o_sh"],
+        a["B"], a["Hq"], a["Hkv"], a["D"], a["ps"], a["scale"], a["S"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("over,code,word", [
+    (dict(Hq=6), pa.ATTN_ERR_UNSUPPORTED, "group"),
+    (dict(Hq=7), pa.ATTN_ERR_INVALID_ARG, "multiple"),
+    (dict(D=96), pa.ATTN_ERR_UNSUPPORTED, "head dim"),
+    (dict(q=None), pa.ATTN_ERR_INVALID_ARG, "null"),
+    (dict(bt=None), pa.ATTN_ERR_INVALID_ARG, "null"),
+    (dict(q=FAKE + 2), pa.ATTN_ERR_UNSUPPORTED, "aligned"),
+    (dict(s_slot=100), pa.ATTN_ERR_UNSUPPORTED, "aligned"),
+    (dict(ps=0), pa.ATTN_ERR_INVALID_ARG, "page_size"),
+    (dict(B=-1), pa.ATTN_ERR_INVALID_ARG, "negative"),
+    (dict(scale=float("nan")), pa.ATTN_ERR_INVALID_ARG, "scale"),
+    (dict(S=300), pa.ATTN_ERR_INVALID_ARG, "num_splits"),
+    (dict(S=4), pa.ATTN_ERR_WORKSPACE, "workspace"),
+    (dict(S=4, ws=FAKE + 16, ws_bytes=1 << 30), pa.ATTN_ERR_INVALID_ARG, "aligned"),
+    (dict(ps=1, max_len=5000, S=1), pa.ATTN_ERR_UNSUPPORTED, "splits"),
+    (dict(ps=1 << 20, max_len=1 << 13), pa.ATTN_ERR_UNSUPPORTED, "2^32"),
+])
+def test_paged_decode_rejects_bad_arguments(over, code, word):
+    rc = call_paged(paged_args(**over))
+    assert rc == code
+    assert word in pa.attn_last_error()
+
+
+def test_decode_rejects_bad_arguments():
+    lib = pa.lib()
+    rc = lib.attn_decode(FAKE, 256, 64, FAKE, 4096, 2048, 64, FAKE, 4096, 2048, 63,
+                         FAKE, 256, 64, None, 32, 2, 8, 2, 64, 0.125, 1, None, 0, None)
+    assert rc == pa.ATTN_ERR_UNSUPPORTED and "aligned" in pa.attn_last_error()
+    rc = lib.attn_decode(FAKE, 256, 64, FAKE, 4096, 2048, 64, FAKE, 4096, 2048, 64,
+                         FAKE, 256, 64, None, -1, 2, 8, 2, 64, 0.125, 1, None, 0, None)
+    assert rc == pa.ATTN_ERR_INVALID_ARG
+
+
+def test_combine_rejects_bad_arguments():
+    lib = pa.lib()
+    assert lib.attn_split_combine(FAKE, FAKE, 0, 4, 128, FAKE, None, None, None) == pa.ATTN_ERR_INVALID_ARG
+    assert lib.attn_split_combine(FAKE, FAKE, 2, 4, 96, FAKE, None, None, None) == pa.ATTN_ERR_UNSUPPORTED
+    assert lib.attn_split_combine(FAKE, FAKE, 2, 4, 128, None, None, None, None) == pa.ATTN_ERR_INVALID_ARG
+
+
+def test_binding_refuses_non_unit_inner_stride():
+    x = torch.zeros(2, 8, 128, dtype=torch.bfloat16)[:, :, ::2]
+    with pytest.raises(ValueError):
+        pa._unit_inner(x)

@@ -1,0 +1,214 @@
+"""GPU parity of split-KV decode and the combine against the CPU oracle.
+
+Bar: |gpu - oracle| <= 1e-2 + 1e-2 |oracle| elementwise on bf16 outputs; the
+fp32 combine is held to 1e-5 + 1e-5 |ref| against the oracle's fp64 combine
+of the same fp32 partials."""
+import math
+
+import pytest
+import torch
+
+import oracle
+import paged_kv_gqa_03_amd as pa
+import workloads
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def assert_close(got, ref, atol=1e-2, rtol=1e-2, what=""):
+    got = got.detach().to("cpu", torch.float64)
+    err = (got - ref).abs()
+    bad = err > atol + rtol * ref.abs()
+    assert not bool(bad.any()), "%s: %d of %d elements off, max err %.4g" % (
+        what, int(bad.sum()), bad.numel(), float(err.max()))
+
+
+def to_dev(case, keys):
+    return {k: (case[k].to(DEV) if torch.is_tensor(case[k]) else case[k]) for k in keys}
+
+
+def run_paged(case, S=0, workspace=None, out=None):
+    d = to_dev(case, ["q", "k_pool", "v_pool", "block_table", "kv_lens"])
+    out = torch.empty_like(d["q"]) if out is None else out
+    pa.attn_paged_decode(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["kv_lens"],
+                         case["max_kv_len"], out, case["page_size"], case["scale"], num_splits=S,
+                         workspace=workspace)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_paged(case):
+    return oracle.paged_decode(case["q"], case["k_pool"], case["v_pool"], case["block_table"],
+                               case["kv_lens"], case["scale"])
+
+
+@pytest.mark.parametrize("S", [0, 1, 2, 3, 19])
+def test_tiny_paged_decode(S):
+    case = workloads.tiny_paged_decode()
+    ref, _ = oracle_paged(case)
+    assert_close(run_paged(case, S), ref, what="tiny S=%d" % S)
+
+
+@pytest.mark.parametrize("G,D,ps,lens", [
+    (1, 64, 16, [1, 15, 16, 17, 100]),
+    (2, 128, 1, [33, 7, 250]),
+    (4, 128, 3, [0, 5, 48, 301]),
+    (8, 128, 16, [64, 200, 1000]),
+    (8, 64, 64, [700, 63, 65]),
+    (4, 64, 7, [129, 1]),
+    (4, 128, 32, [513, 2000, 1]),
+])
+@pytest.mark.parametrize("S", [0, 1, 4])
+def test_paged_decode_shapes(G, D, ps, lens, S):
+    Hkv = 2
+    case = workloads.paged_decode_case(100 + G * 7 + D + ps, len(lens), Hkv * G, Hkv, D, lens, ps)
+    if S == 1 and case["max_kv_len"] > 496 * ps:
+        S = 0
+    ref, _ = oracle_paged(case)
+    assert_close(run_paged(case, S), ref, what="G=%d D=%d ps=%d S=%d" % (G, D, ps, S))
+
+
+def test_paged_decode_empty_sequences_give_zero():
+    case = workloads.paged_decode_case(7, 3, 8, 2, 128, [0, 40, 0], 16)
+    for S in (1, 3):
+        out = run_paged(case, S)
+        assert torch.equal(out[0].cpu(), torch.zeros_like(out[0].cpu()))
+        assert torch.equal(out[2].cpu(), torch.zeros_like(out[2].cpu()))
+        ref, _ = oracle_paged(case)
+        assert_close(out, ref)
+
+
+def test_paged_decode_page_head_slot_layout():
+    case = workloads.paged_decode_case(8, 4, 32, 8, 128, [77, 512, 1, 333], 16, layout="page_head_slot")
+    ref, _ = oracle_paged(case)
+    assert_close(run_paged(case, 0), ref)
+
+
+def test_serving_paged_decode_b32():
+    case = workloads.serving_paged_decode(32, device=DEV)
+    out = run_paged(case, 0)
+    cpu = {k: (v.cpu() if torch.is_tensor(v) else v) for k, v in case.items()}
+    ref, _ = oracle_paged(cpu)
+    assert_close(out, ref, what="B=32 serving")
+
+
+def test_serving_paged_decode_b128_sampled_sequences():
+    """B=128 in the timed launch configuration; the oracle checks every 8th
+    sequence (a batch slice is an exact sub-problem)."""
+    case = workloads.serving_paged_decode(128, device=DEV)
+    out = run_paged(case, 0).cpu()
+    idx = torch.arange(0, 128, 8)
+    sub = dict(q=case["q"][idx].cpu(), k_pool=case["k_pool"].cpu(), v_pool=case["v_pool"].cpu(),
+               block_table=case["block_table"][idx].cpu(), kv_lens=case["kv_lens"][idx].cpu(),
+               scale=case["scale"])
+    ref, _ = oracle_paged(sub)
+    assert_close(out[idx], ref, what="B=128 sampled")
+
+
+@pytest.mark.parametrize("layout", ["bhld", "blhd"])
+def test_contiguous_decode(layout):
+    if layout == "bhld":
+        case = workloads.contiguous_decode(device=DEV)
+    else:
+        case = workloads.contig_decode_case(9, 4, 32, 8, 128, 600, device=DEV, layout="blhd")
+    out = torch.empty_like(case["q"])
+    pa.attn_decode(case["q"], case["k"], case["v"], out, case["scale"])
+    torch.cuda.synchronize()
+    ref, _ = oracle.decode(case["q"].cpu(), case["k"].cpu(), case["v"].cpu(), case["scale"])
+    assert_close(out, ref, what="contiguous " + layout)
+
+
+@pytest.mark.parametrize("S", [1, 3])
+def test_contiguous_decode_ragged_lengths(S):
+    case = workloads.contig_decode_case(10, 5, 16, 4, 64, 300, device=DEV, kv_lens=[300, 0, 1, 17, 256])
+    out = torch.empty_like(case["q"])
+    pa.attn_decode(case["q"], case["k"], case["v"], out, case["scale"], kv_lens=case["kv_lens"],
+                   num_splits=S)
+    torch.cuda.synchronize()
+    ref, _ = oracle.decode(case["q"].cpu(), case["k"].cpu(), case["v"].cpu(), case["scale"],
+                           kv_lens=case["kv_lens"].cpu())
+    assert_close(out, ref)
+
+
+def test_workspace_poisoned_with_nan_is_fully_overwritten():
+    case = workloads.paged_decode_case(12, 6, 32, 8, 128, [1, 100, 900, 1500, 16, 1024], 16)
+    S = 7
+    n = pa.attn_decode_workspace_bytes(6, 32, 128, S)
+    ws = torch.full((n,), 0xFF, dtype=torch.uint8, device=DEV)   # all-ones bytes are NaNs
+    ref, _ = oracle_paged(case)
+    assert_close(run_paged(case, S, workspace=ws), ref)
+
+
+def test_repeat_runs_are_bit_identical():
+    case = workloads.paged_decode_case(13, 8, 32, 8, 128, (100, 3000), 16)
+    a = run_paged(case, 0).clone()
+    b = run_paged(case, 0)
+    assert torch.equal(a, b)
+
+
+def test_combine_of_decode_partials_matches_oracle_combine():
+    """Equal lengths, so every split is non-empty; the fp32 partials the
+    split kernel leaves in the workspace are combined on the GPU and by the
+    oracle in fp64."""
+    B, Hq, D, L, S = 4, 32, 128, 1000, 5
+    case = workloads.paged_decode_case(14, B, Hq, 8, D, [L] * B, 16)
+    ws = torch.empty(pa.attn_decode_workspace_bytes(B, Hq, D, S), dtype=torch.uint8, device=DEV)
+    run_paged(case, S, workspace=ws)
+    o_bytes = S * B * Hq * D * 4
+    ml_off = (o_bytes + 255) // 256 * 256
+    o_part = ws[:o_bytes].view(torch.float32).view(S, B * Hq, D)
+    ml_part = ws[ml_off:ml_off + S * B * Hq * 8].view(torch.float32).view(S, B * Hq, 2)
+    out = torch.empty(B * Hq, D, dtype=torch.float32, device=DEV)
+    lse = torch.empty(B * Hq, dtype=torch.float32, device=DEV)
+    pa.attn_split_combine(o_part, ml_part, out_f32=out, lse=lse)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.combine_f32(o_part.cpu(), ml_part.cpu())
+    assert_close(out, ref, atol=1e-5, rtol=1e-5, what="combine")
+    assert_close(lse, ref_lse, atol=1e-5, rtol=1e-5, what="lse")
+    # and the partials themselves are a valid split of the exact result
+    full, full_lse = oracle_paged(case)
+    assert_close(out.view(B, Hq, D), full, atol=1e-2, rtol=1e-2)
+    assert_close(lse.view(B, Hq), full_lse, atol=1e-2, rtol=1e-2)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_combine_random_partials_with_empty_splits(D):
+    g = torch.Generator().manual_seed(D)
+    S, R = 9, 300
+    o = torch.randn(S, R, D, generator=g) * 5
+    m = torch.randn(S, R, generator=g) * 3
+    l = torch.rand(S, R, generator=g) * 10 + 0.1
+    empty = torch.rand(S, R, generator=g) < 0.3
+    m[empty] = -math.inf
+    l[empty] = 0
+    o[empty] = 0
+    m[:, 0] = -math.inf                      # a row with no partial at all
+    l[:, 0] = 0
+    ml = torch.stack([m, l], dim=-1).float().contiguous()
+    o = o.float().contiguous()
+    out = torch.empty(R, D, dtype=torch.float32, device=DEV)
+    outb = torch.empty(R, D, dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty(R, dtype=torch.float32, device=DEV)
+    pa.attn_split_combine(o.to(DEV), ml.to(DEV), out_f32=out, out_bf16=outb, lse=lse)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.combine_f32(o, ml)
+    assert_close(out, ref, atol=1e-5, rtol=1e-5)
+    assert_close(outb, ref, atol=1e-2, rtol=1e-2)
+    fin = torch.isfinite(ref_lse)
+    assert_close(lse[fin.to(DEV)], ref_lse[fin], atol=1e-5, rtol=1e-5)
+    assert bool(torch.isneginf(lse.cpu()[~fin]).all())
+
+
+@pytest.mark.parametrize("S", [1, 6])
+def test_split_then_combine_equals_fused_call(S):
+    case = workloads.paged_decode_case(15, 6, 32, 8, 128, [5, 300, 1200, 0, 77, 2000], 16)
+    d = to_dev(case, ["q", "k_pool", "v_pool", "block_table", "kv_lens"])
+    ws = torch.empty(pa.attn_decode_workspace_bytes(6, 32, 128, S), dtype=torch.uint8, device=DEV)
+    fused = run_paged(case, S, workspace=ws).clone()
+    pa.attn_paged_decode_split(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["kv_lens"],
+                               case["max_kv_len"], 16, case["scale"], S, ws)
+    out = torch.empty_like(d["q"])
+    pa.attn_decode_combine(ws, 6, 32, 128, S, d["kv_lens"], case["max_kv_len"], out)
+    torch.cuda.synchronize()
+    assert torch.equal(fused, out)
