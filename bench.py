@@ -39,10 +39,12 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="paged_b128",
-                    choices=["paged_b128", "paged_b32", "paged_b128_kv4096", "paged_b32_kv4096"])
+                    choices=["paged_b128", "paged_b32", "paged_b128_kv4096", "paged_b32_kv4096", "contig_b16"])
     ap.add_argument("--num-splits", type=int, default=0, help="0 = planner")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--counters", action="store_true",
+                    help="untimed: 3 split-kernel launches on set 0 and 3 copies of 1 GiB, for rocprofv3 --pmc")
     return ap.parse_args()
 
 
@@ -112,6 +114,10 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.workload == "contig_b16":
+        r = bench_contiguous(torch, pa, dev, args.steps, args.warmup, args.num_splits)
+        print(json.dumps({"workload": "contiguous decode B=16 Hq=32 Hkv=8 D=128 kv=2048 bhld", **r}), flush=True)
+        return
     probe = make_sets(args.workload, dev, 1)
     per_call = decode_bytes(probe[0])
     R = rotation_count(per_call)
@@ -120,11 +126,14 @@ def main():
         s["out"] = torch.empty_like(s["q"])
         s["bytes"] = decode_bytes(s)
     c0 = sets[0]
-    S = args.num_splits or pa.attn_plan_splits(c0["B"], c0["Hkv"], c0["Hq"] // c0["Hkv"], c0["max_kv_len"],
-                                               c0["page_size"])
     max_len = max(s["max_kv_len"] for s in sets)
+    S = args.num_splits or pa.attn_plan_splits(c0["B"], c0["Hkv"], c0["Hq"] // c0["Hkv"], c0["D"], max_len,
+                                               c0["page_size"], c0["k_pool"].stride(2))
     ws_bytes = pa.attn_decode_workspace_bytes(c0["B"], c0["Hq"], c0["D"], S)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    if args.counters:
+        run_counters(torch, pa, c0, S, max_len, ws)
+        return
 
     def call(s):
         pa.attn_paged_decode(s["q"], s["k_pool"], s["v_pool"], s["block_table"], s["kv_lens"], max_len,
@@ -221,6 +230,24 @@ def main():
     print(json.dumps(line), flush=True)
 
 
+def run_counters(torch, pa, c0, S, max_len, ws):
+    """Launches for hardware-counter runs: the split kernel of the timed
+    configuration, then a plain device copy of exactly 1 GiB (reads 1 GiB,
+    writes 1 GiB) that calibrates FETCH_SIZE / WRITE_SIZE."""
+    for _ in range(3):
+        pa.attn_paged_decode_split(c0["q"], c0["k_pool"], c0["v_pool"], c0["block_table"], c0["kv_lens"],
+                                   max_len, c0["page_size"], c0["scale"], S, ws)
+    torch.cuda.synchronize()
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=c0["q"].device).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"counters_run": True, "num_splits": S, "split_kernel_algorithmic_bytes": decode_bytes(c0),
+                      "copy_bytes": 1 << 30}), flush=True)
+
+
 def run_extras(torch, pa, dev, args):
     """Short timings of the other decode workloads (same protocol)."""
     import workloads
@@ -233,7 +260,7 @@ def run_extras(torch, pa, dev, args):
         sets = probe + make_sets(name, dev, R)[1:]
         mx = max(s["max_kv_len"] for s in sets)
         c0 = sets[0]
-        S = pa.attn_plan_splits(c0["B"], 8, 4, mx, 16)
+        S = pa.attn_plan_splits(c0["B"], 8, 4, 128, mx, 16, c0["k_pool"].stride(2))
         ws = torch.empty(max(256, pa.attn_decode_workspace_bytes(c0["B"], 32, 128, S)), dtype=torch.uint8,
                          device=dev)
         for s in sets:
@@ -249,7 +276,13 @@ def run_extras(torch, pa, dev, args):
                      "rotation_sets": R}
         del sets
         torch.cuda.empty_cache()
-    # contiguous decode, B=16 Hq=32 Hkv=8 D=128 kv=2048 (bhld)
+    out["contiguous_b16_kv2048"] = bench_contiguous(torch, pa, dev, steps, warm, 0)
+    return out
+
+
+def bench_contiguous(torch, pa, dev, steps, warm, num_splits):
+    """Contiguous decode, B=16 Hq=32 Hkv=8 D=128 kv=2048 (bhld), same protocol."""
+    import workloads
     c = workloads.contiguous_decode(device=dev)
     nb = 16 * 8 * 2048 * 128 * 4 + 2 * 16 * 32 * 128 * 2
     R = rotation_count(nb)
@@ -257,16 +290,14 @@ def run_extras(torch, pa, dev, args):
                 for r in range(1, R)]
     for s in cs:
         s["out"] = torch.empty_like(s["q"])
-    S = pa.attn_plan_splits(16, 8, 4, 2048, 0)
+    S = num_splits or pa.attn_plan_splits(16, 8, 4, 128, 2048, 0, c["k"].stride(1))
     ws = torch.empty(max(256, pa.attn_decode_workspace_bytes(16, 32, 128, S)), dtype=torch.uint8, device=dev)
 
     def ccall(s):
         pa.attn_decode(s["q"], s["k"], s["v"], s["out"], s["scale"], num_splits=S, workspace=ws)
     ms = time_calls(torch, ccall, cs, steps, warm)
-    out["contiguous_b16_kv2048"] = {"us_per_call": round(ms * 1e3, 2), "GB/s": round(nb / (ms * 1e-3) / 1e9, 1),
-                                    "hbm_peak_frac": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                                    "num_splits": S, "rotation_sets": R}
-    return out
+    return {"us_per_call": round(ms * 1e3, 2), "GB/s": round(nb / (ms * 1e-3) / 1e9, 1),
+            "hbm_peak_frac": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "num_splits": S, "rotation_sets": R}
 
 
 if __name__ == "__main__":

@@ -61,16 +61,21 @@ int attn_version(void);
  * Split-count planner for decode (AstrAI csrc commit history: the commit
  * that partitions KV across gridDim.z and sizes the split count to fill the
  * device, and the later one that retargets it at a fixed total block count
- * after a grid search).  Chooses S >= 1 so that the B * Hkv * S independent
- * work units fill `num_cus` compute units (0 = query the current device).
- * S = 1 means a single pass that writes the normalised output directly.
- * page_size 0 plans for a contiguous source.  For a paged source S is at
- * least ceil(max_kv_len / (510 * page_size)) (rounded to 16 tokens), the most
- * pages one split's LDS slice of the block table holds; attn_paged_decode
- * rejects a smaller explicit num_splits with ATTN_ERR_UNSUPPORTED.
- * Host-only and deterministic; returns S, or a negative error code.
+ * after a grid search).  The decode kernel runs one wave per (sequence,
+ * group of adjacent KV heads, split); a group is up to 8 heads when the KV
+ * head stride `kv_s_head` equals D (heads of a token contiguous), else one
+ * head.  The planner chooses S >= 1 so that those waves fill `num_cus`
+ * compute units (0 = query the current device) without splits shorter than
+ * four decode tiles.  S = 1 means a single pass that writes the normalised
+ * output directly.  page_size 0 plans for a contiguous source (pass its K
+ * head stride as kv_s_head).  For a paged source S is at least
+ * ceil(max_kv_len / (510 * page_size)) (rounded to 16 tokens), the most pages
+ * one split's LDS slice of the block table holds; attn_paged_decode rejects a
+ * smaller explicit num_splits with ATTN_ERR_UNSUPPORTED.  Host-only and
+ * deterministic; returns S, or a negative error code.
  */
-int attn_plan_splits(int B, int Hkv, int G, int max_kv_len, int page_size, int num_cus);
+int attn_plan_splits(int B, int Hkv, int G, int D, int max_kv_len, int page_size, int64_t kv_s_head,
+                     int num_cus);
 
 /*
  * Tokens per split for a given split count: the KV range of sequence b is

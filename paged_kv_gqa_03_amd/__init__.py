@@ -32,7 +32,7 @@ _P, _I, _L, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_flo
 _SIGS = {
     "attn_last_error": ([], ctypes.c_char_p),
     "attn_version": ([], _I),
-    "attn_plan_splits": ([_I, _I, _I, _I, _I, _I], _I),
+    "attn_plan_splits": ([_I, _I, _I, _I, _I, _I, _L, _I], _I),
     "attn_split_chunk": ([_I, _I], _I),
     "attn_decode_workspace_bytes": ([_I, _I, _I, _I], _Z),
     "attn_decode": ([_P, _L, _L, _P, _L, _L, _L, _P, _L, _L, _L, _P, _L, _L, _P, _I,
@@ -107,8 +107,8 @@ def attn_version():
     return lib().attn_version()
 
 
-def attn_plan_splits(B, Hkv, G, max_kv_len, page_size, num_cus=0):
-    rc = lib().attn_plan_splits(B, Hkv, G, max_kv_len, page_size, num_cus)
+def attn_plan_splits(B, Hkv, G, D, max_kv_len, page_size, kv_s_head, num_cus=0):
+    rc = lib().attn_plan_splits(B, Hkv, G, D, max_kv_len, page_size, kv_s_head, num_cus)
     if rc < 0:
         _check(rc)
     return rc
@@ -144,7 +144,7 @@ def attn_paged_decode(q, k_pool, v_pool, block_table, kv_lens, max_kv_len, out, 
     assert k_pool.stride() == v_pool.stride(), "K and V pools must share strides"
     B, Hq, D = q.shape
     Hkv = k_pool.shape[2]
-    S = num_splits or attn_plan_splits(B, Hkv, Hq // Hkv, max_kv_len, page_size, num_cus)
+    S = num_splits or attn_plan_splits(B, Hkv, Hq // Hkv, D, max_kv_len, page_size, k_pool.stride(2), num_cus)
     ws, nbytes = _workspace(workspace, B, Hq, D, S, q.device)
     _check(lib().attn_paged_decode(
         _ptr(q), q.stride(0), q.stride(1), _ptr(k_pool), _ptr(v_pool),
@@ -188,7 +188,7 @@ def attn_decode(q, k, v, out, scale, kv_lens=None, kv_len=None, num_splits=0, wo
     B, Hq, D = q.shape
     Hkv, L = k.shape[1], k.shape[2]
     kv_len = L if kv_len is None else kv_len
-    S = num_splits or attn_plan_splits(B, Hkv, Hq // Hkv, kv_len, 0, num_cus)
+    S = num_splits or attn_plan_splits(B, Hkv, Hq // Hkv, D, kv_len, 0, k.stride(1), num_cus)
     ws, nbytes = _workspace(workspace, B, Hq, D, S, q.device)
     _check(lib().attn_decode(
         _ptr(q), q.stride(0), q.stride(1),

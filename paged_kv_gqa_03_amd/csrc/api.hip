@@ -47,9 +47,21 @@ int device_cus() {
     return cus;
 }
 
-constexpr int kTileTokens = 16;   // decode tile; split chunks are multiples of it
+constexpr int kTileTokens = 16;   // split chunks are multiples of it (the largest decode tile)
 constexpr int kMaxSplits = 256;
-constexpr int kWavesPerCuTarget = 16;  // resident waves per CU the planner aims at
+constexpr int kWavesPerCuTarget = 4;   // decode waves per CU the planner aims at
+constexpr int kMinTilesPerSplit = 4;   // shortest split, in decode tiles
+
+// KV heads one decode wave covers: with the heads of a token adjacent in
+// memory (head stride == D) a wave takes up to 8 of them so each token's
+// rows form one contiguous read; otherwise one head, whose tokens are then
+// the contiguous direction.
+int heads_per_wave(int Hkv, int64_t kv_s_head, int D) {
+    if (kv_s_head != D) return 1;
+    int hw = 8;
+    while (hw > 1 && Hkv % hw != 0) hw >>= 1;
+    return hw;
+}
 
 // Longest split (tokens) whose block-table slice fits the kernel's LDS slice:
 // a chunk of c tokens spans at most (c - 1) / ps + 2 pages.
@@ -127,12 +139,14 @@ pa::CombineParams decode_combine_params(const void *workspace, int B, int Hq, in
 // mode 0: split (+ combine when S > 1, direct write when S == 1);
 // mode 1: split kernel only, always writing fp32 partials.
 int run_decode(pa::DecodeParams &p, int D, int G, bool paged, int max_kv_len, int num_splits,
-               void *workspace, size_t workspace_bytes, int page_size, hipStream_t stream, int mode) {
+               void *workspace, size_t workspace_bytes, int page_size, int64_t kv_s_head, hipStream_t stream,
+               int mode) {
     int S = num_splits;
     if (S == 0) {
-        S = attn_plan_splits(p.B, p.Hkv, G, max_kv_len, page_size, 0);
+        S = attn_plan_splits(p.B, p.Hkv, G, D, max_kv_len, page_size, kv_s_head, 0);
         if (S < 0) return S;
     }
+    p.HW = heads_per_wave(p.Hkv, kv_s_head, D);
     if (S < 1 || S > kMaxSplits) return fail(ATTN_ERR_INVALID_ARG, "num_splits %d outside [1, %d]", S, kMaxSplits);
     if (paged && S < min_paged_splits(max_kv_len, page_size))
         return fail(ATTN_ERR_UNSUPPORTED,
@@ -142,7 +156,7 @@ int run_decode(pa::DecodeParams &p, int D, int G, bool paged, int max_kv_len, in
     p.S = S;
     p.direct = (S == 1 && mode == 0) ? 1 : 0;
     if (S == 1 && !paged) p.chunk = max_kv_len > 0 ? max_kv_len : 1;
-    p.units = p.B * p.Hkv * S;
+    p.units = p.B * (p.Hkv / p.HW) * S;
     int rc = check_workspace(workspace, workspace_bytes, p.B, p.Hq, D, S, mode == 1);
     if (rc) return rc;
     if (!p.direct) {
@@ -169,21 +183,25 @@ const char *attn_last_error(void) { return g_err.c_str(); }
 
 int attn_version(void) { return 100; }
 
-int attn_plan_splits(int B, int Hkv, int G, int max_kv_len, int page_size, int num_cus) {
-    if (B < 0 || Hkv <= 0 || G <= 0 || max_kv_len < 0 || page_size < 0)
+int attn_plan_splits(int B, int Hkv, int G, int D, int max_kv_len, int page_size, int64_t kv_s_head,
+                     int num_cus) {
+    if (B < 0 || Hkv <= 0 || G <= 0 || D <= 0 || max_kv_len < 0 || page_size < 0)
         return fail(ATTN_ERR_INVALID_ARG, "attn_plan_splits: bad sizes");
     if (num_cus <= 0) {
         num_cus = device_cus();
         if (num_cus <= 0) return fail(ATTN_ERR_LAUNCH, "attn_plan_splits: cannot query the device");
     }
-    const long units = (long)B * Hkv;
-    if (units == 0 || max_kv_len <= kTileTokens) return min_paged_splits(max_kv_len, page_size);
+    const int hw = heads_per_wave(Hkv, kv_s_head, D);
+    const long waves_per_split = (long)B * (Hkv / hw);
+    const long s_min = min_paged_splits(max_kv_len, page_size);
+    if (waves_per_split == 0) return (int)s_min;
+    const long tile = 2L * (8 / hw);
     const long target = (long)num_cus * kWavesPerCuTarget;
-    long S = (target + units - 1) / units;
-    const long max_by_len = (max_kv_len + 4 * kTileTokens - 1) / (4 * kTileTokens);  // >= 64 tokens a split
+    long S = (target + waves_per_split - 1) / waves_per_split;
+    const long min_chunk = kMinTilesPerSplit * tile;
+    const long max_by_len = (max_kv_len + min_chunk - 1) / min_chunk;
     if (S > max_by_len) S = max_by_len;
     if (S > kMaxSplits) S = kMaxSplits;
-    const long s_min = min_paged_splits(max_kv_len, page_size);
     if (S < s_min) S = s_min;
     if (S < 1) S = 1;
     return (int)S;
@@ -216,6 +234,8 @@ int attn_decode(const void *q, int64_t q_sb, int64_t q_sh,
         !mult8(q_sb) || !mult8(q_sh) || !mult8(k_sb) || !mult8(k_sh) || !mult8(k_sl) ||
         !mult8(v_sb) || !mult8(v_sh) || !mult8(v_sl) || !mult8(o_sb) || !mult8(o_sh))
         return fail(ATTN_ERR_UNSUPPORTED, "attn_decode: rows must be 16-byte aligned (pointers, strides %% 8)");
+    if (k_sl < 0 || v_sl < 0 || (int64_t)kv_len * (k_sl > v_sl ? k_sl : v_sl) >= (1ll << 31))
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_decode: kv_len * position stride must stay below 2^31");
     pa::DecodeParams p{};
     p.q = static_cast<const uint16_t *>(q);
     p.q_sb = q_sb; p.q_sh = q_sh;
@@ -229,7 +249,9 @@ int attn_decode(const void *q, int64_t q_sb, int64_t q_sh,
     p.o_sb = o_sb; p.o_sh = o_sh;
     p.B = B; p.Hq = Hq; p.Hkv = Hkv;
     p.sl2 = scale * 1.4426950408889634f;
-    return run_decode(p, D, G, false, kv_len, num_splits, workspace, workspace_bytes, 0,
+    // Any heads-per-wave choice is correct for any strides; it only decides
+    // which direction one load instruction reads contiguously.
+    return run_decode(p, D, G, false, kv_len, num_splits, workspace, workspace_bytes, 0, k_sh,
                       static_cast<hipStream_t>(stream), 0);
 }
 
@@ -258,6 +280,9 @@ static int paged_decode_impl(const void *q, int64_t q_sb, int64_t q_sh,
         !mult8(q_sb) || !mult8(q_sh) || !mult8(kv_s_page) || !mult8(kv_s_slot) || !mult8(kv_s_head) ||
         !mult8(o_sb) || !mult8(o_sh))
         return fail(ATTN_ERR_UNSUPPORTED, "%s: rows must be 16-byte aligned (pointers, strides %% 8)", fn);
+    if (kv_s_page < 0 || kv_s_slot < 0 || kv_s_head < 0 || kv_s_page >= (1ll << 32) ||
+        (int64_t)(page_size - 1) * kv_s_slot + (int64_t)(Hkv - 1) * kv_s_head + D >= (1ll << 31))
+        return fail(ATTN_ERR_UNSUPPORTED, "%s: pool strides exceed the 32-bit page/slot addressing", fn);
     pa::DecodeParams p{};
     p.q = static_cast<const uint16_t *>(q);
     p.q_sb = q_sb; p.q_sh = q_sh;
@@ -273,7 +298,7 @@ static int paged_decode_impl(const void *q, int64_t q_sb, int64_t q_sh,
     p.o_sb = o_sb; p.o_sh = o_sh;
     p.B = B; p.Hq = Hq; p.Hkv = Hkv;
     p.sl2 = scale * 1.4426950408889634f;
-    return run_decode(p, D, G, true, max_kv_len, num_splits, workspace, workspace_bytes, page_size,
+    return run_decode(p, D, G, true, max_kv_len, num_splits, workspace, workspace_bytes, page_size, kv_s_head,
                       static_cast<hipStream_t>(stream), mode);
 }
 

@@ -9,29 +9,38 @@
 // the block table with a lookup per token (the commit that replaced the
 // per-tile page lookup by a per-element one) or contiguous strides.
 //
-// Work decomposition on gfx950: one wave64 per (sequence b, KV head g,
-// split s); a workgroup holds four independent waves that never synchronise
-// with each other (each owns a private LDS slice for its page ids).  The wave carries all G = Hq/Hkv query heads of its
-// KV head, so K/V bytes are read once for the whole group (cf. the GQA head
-// packing commit in the doc's history).
+// Work decomposition on gfx950: a one-wave workgroup owns one split of one
+// sequence for HW adjacent KV heads (HW in {1, 2, 4, 8}), so the dispatcher
+// refills a compute unit as soon as any split finishes, whatever the ragged
+// lengths of its neighbours.  Units are ordered split-major, so the last
+// splits of long sequences run last and the tail is at most one split long.
+// The wave carries all G = Hq/Hkv query heads of each
+// of its KV heads, so K/V bytes are read once for the whole group (cf. the
+// GQA head-packing commit in the doc's history).
 //
-// Lane layout: a tile is 16 tokens.  Lane l owns token group tok = l/8 and
-// chunk lane jj = l%8; per tile it holds tokens tok and tok+8 and, for each,
-// the 16-byte chunks jj, jj+8, ... of the K and V rows (D/64 chunks).  One
-// load instruction therefore reads 8 rows x 128 contiguous bytes.
-//   scores  v_dot2_f32_bf16 of q and K chunks, summed over the 8 lanes of a
-//           token with three DPP adds (quad_perm x2, row_half_mirror);
-//   softmax each token group keeps its own running state; the reference
-//           max is only raised when a score exceeds it by more than 2^8
-//           (base 2), so rescaling of the accumulator is rare, and every
-//           exp2 argument stays <= 8;
+// Lane layout: lane l = 8*grp + jj, with lane group grp = tg*HW + hw: hw
+// picks the KV head, tg one of TG = 8/HW token streams, jj one of 8 chunk
+// lanes.  A tile is 2*TG tokens; per tile a lane holds tokens tg and tg+TG
+// and, for each, the 16-byte chunks jj, jj+8, ... of its head's K and V rows
+// (D/64 chunks).  HW is chosen from the layout so that one load instruction
+// reads memory that is contiguous: with the KV heads of a token adjacent
+// ([pages, slot, head, dim] pools, blhd) HW = 8 and a tile is 2 tokens of
+// whole 2 KB rows (a 16-token page is one 32 KB stream); with a head's
+// tokens adjacent ([pages, head, slot, dim], bhld) HW = 1 and a tile is 16
+// tokens of one head (4 KB contiguous).
+//   scores  v_dot2_f32_bf16 of q and K chunks, summed over the 8 chunk lanes
+//           with three DPP adds (quad_perm x2, row_half_mirror);
+//   softmax each lane group keeps its own running state; the reference max
+//           is only raised when a score exceeds it by more than 2^8 (base 2),
+//           so rescaling of the accumulator is rare, and every exp2
+//           argument stays <= 8;
 //   P.V     the two tokens' V rows are interleaved into bf16 pairs and
 //           accumulated with v_dot2 against the pair of bf16 weights, so
 //           each V element costs G/2 dot2 plus half a permute.
-// The eight token groups are merged once per split (xor shuffles), then the
-// wave writes either the normalised bf16 output (single split, direct mode)
-// or the fp32 partial (m, l, o).
-// Loads run one tile ahead of the math (double-buffered registers).  The
+// The TG token streams of a head are merged once per split (xor shuffles),
+// then the wave writes either the normalised bf16 output (single split,
+// direct mode) or the fp32 partial (m, l, o).
+// Loads run two tiles ahead of the math (three register stages).  The
 // split's block-table slice is copied into LDS once per wave before the loop,
 // so page lookups inside the loop are LDS reads (lgkmcnt) and never sit in
 // the in-order vmcnt queue between K/V loads.
@@ -42,7 +51,6 @@ namespace pa {
 
 namespace {
 
-constexpr int kTile = 16;
 constexpr float kRescaleTh = 8.0f;  // log2 units
 
 template <int NCH>
@@ -60,21 +68,25 @@ __device__ __forceinline__ void load16(const uint16_t *ptr, uint32_t (&dst)[4]) 
     dst[0] = t.x; dst[1] = t.y; dst[2] = t.z; dst[3] = t.w;
 }
 
-template <int D, int G, bool PAGED>
-__global__ __launch_bounds__(256) void decode_split_kernel(const DecodeParams p) {
+template <int D, int G, int HW, bool PAGED>
+__global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) {
     constexpr int NCH = D / 64;
+    constexpr int TG = 8 / HW;          // token streams per head
+    constexpr int TILE = 2 * TG;        // tokens per tile
     const int lane = threadIdx.x & 63;
-    const int u = blockIdx.x * 4 + wave_id();
-    if (u >= p.units) return;
-    const int g = u % p.Hkv;
-    const int bsx = u / p.Hkv;
+    const int u = blockIdx.x;
+    const int ngrp = p.Hkv / HW;
+    const int hgrp = u % ngrp;
+    const int bsx = u / ngrp;
     const int b = bsx % p.B;
     const int s = bsx / p.B;
     const int n = p.kv_lens ? p.kv_lens[b] : p.kv_len_const;
     const int j0 = s * p.chunk;
     const int j1 = min(n, j0 + p.chunk);
     if (j0 >= j1 && s > 0) return;  // past the end of this sequence: no partial
-    const int tok = lane >> 3, jj = lane & 7;
+    const int grp = lane >> 3, jj = lane & 7;
+    const int hw = grp % HW, tg = grp / HW;
+    const int g = hgrp * HW + hw;       // this lane's KV head
     const int last = j1 - 1;
 
     // Query slices of the G heads of this KV head, chunks jj + 8c.
@@ -99,10 +111,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeParams p)
             for (int e = 0; e < 8; ++e) o[h][c][e] = 0.f;
     }
 
-    const int ntiles = (j1 - j0 + kTile - 1) / kTile;
+    const int ntiles = (j1 - j0 + TILE - 1) / TILE;
     // Block-table slice of this split: page indices first_pg .. (j1-1)/ps.
-    __shared__ int32_t s_pages[4][kDecodeMaxSplitPages];
-    int32_t *pages = s_pages[wave_id()];
+    __shared__ int32_t pages[kDecodeMaxSplitPages];
     int first_pg = 0;
     if constexpr (PAGED) {
         if (ntiles > 0) {
@@ -115,14 +126,19 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeParams p)
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
     }
-    const int64_t head_off_k = PAGED ? g * p.s_head : b * p.k_sb + g * p.k_sh;
-    const int64_t head_off_v = PAGED ? g * p.s_head : b * p.v_sb + g * p.v_sh;
+    // Base pointers of this (sequence, KV head) and this lane's chunk.  The
+    // host guarantees every per-token offset below fits 32 bits except the
+    // page term, which is a single 32x32->64 multiply-add.
+    const uint16_t *kbase = p.k + jj * 8 + (PAGED ? g * p.s_head : b * p.k_sb + g * p.k_sh);
+    const uint16_t *vbase = p.v + jj * 8 + (PAGED ? g * p.s_head : b * p.v_sb + g * p.v_sh);
+    const uint32_t s_page = (uint32_t)p.s_page, s_slot = (uint32_t)p.s_slot;
+    const uint32_t k_sl = (uint32_t)p.k_sl, v_sl = (uint32_t)p.v_sl;
 
     // Page ids (from the LDS slice) and slots of the lane's two tokens of tile t.
     auto lookup = [&](int t) {
         TokAddr a;
-        const int ja = min(j0 + t * kTile + tok, last);
-        const int jb = min(j0 + t * kTile + tok + 8, last);
+        const int ja = min(j0 + t * TILE + tg, last);
+        const int jb = min(j0 + t * TILE + tg + TG, last);
         if constexpr (PAGED) {
             const uint32_t ia = udiv_magic((uint32_t)ja, p.ps_magic);
             const uint32_t ib = udiv_magic((uint32_t)jb, p.ps_magic);
@@ -137,18 +153,18 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeParams p)
     };
     // Issue the 16-byte K/V loads of one tile.
     auto issue = [&](const TokAddr &a, KVRegs<NCH> &r) {
-        int64_t oka, okb, ova, ovb;
+        uint64_t oka, okb, ova, ovb;
         if constexpr (PAGED) {
-            oka = ova = (int64_t)a.pa * p.s_page + (int64_t)a.sa * p.s_slot + head_off_k;
-            okb = ovb = (int64_t)a.pb * p.s_page + (int64_t)a.sb * p.s_slot + head_off_k;
+            oka = ova = (uint64_t)(uint32_t)a.pa * s_page + (uint32_t)a.sa * s_slot;
+            okb = ovb = (uint64_t)(uint32_t)a.pb * s_page + (uint32_t)a.sb * s_slot;
         } else {
-            oka = head_off_k + (int64_t)a.sa * p.k_sl;
-            okb = head_off_k + (int64_t)a.sb * p.k_sl;
-            ova = head_off_v + (int64_t)a.sa * p.v_sl;
-            ovb = head_off_v + (int64_t)a.sb * p.v_sl;
+            oka = (uint32_t)a.sa * k_sl;
+            okb = (uint32_t)a.sb * k_sl;
+            ova = (uint32_t)a.sa * v_sl;
+            ovb = (uint32_t)a.sb * v_sl;
         }
-        const uint16_t *kA = p.k + oka + jj * 8, *kB = p.k + okb + jj * 8;
-        const uint16_t *vA = p.v + ova + jj * 8, *vB = p.v + ovb + jj * 8;
+        const uint16_t *kA = kbase + oka, *kB = kbase + okb;
+        const uint16_t *vA = vbase + ova, *vB = vbase + ovb;
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
             load16(kA + c * 64, r.ka[c]);
@@ -162,8 +178,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeParams p)
     };
     // Math of tile t on registers r.
     auto compute = [&](int t, const KVRegs<NCH> &r) {
-        const int ja = j0 + t * kTile + tok;
-        const bool oka = ja < j1, okb = ja + 8 < j1;
+        const int ja = j0 + t * TILE + tg;
+        const bool oka = ja < j1, okb = ja + TG < j1;
         float xa[G], xb[G];
 #pragma unroll
         for (int h = 0; h < G; ++h) {
@@ -226,52 +242,58 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const DecodeParams p)
     // The page lookup of a tile sits right before its loads: page ids are
     // never carried across iterations.  Past the last tile the loads repeat
     // the last tile (always in bounds, never used).
-    // The loop has a single exit at the bottom so the compiler's wait-count
-    // pass keeps exactly one tile of loads in flight across the back edge.
+    // Three register stages: while tile t is computed, tiles t+1 and t+2 are
+    // in flight.  The loop has a single exit at the bottom, so the compiler's
+    // wait-count pass keeps both tiles outstanding across the back edge.
     if (ntiles > 0) {
         const int tl = ntiles - 1;
-        KVRegs<NCH> r0, r1;
+        KVRegs<NCH> r0, r1, r2;
         issue(lookup(0), r0);
+        issue(lookup(min(1, tl)), r1);
         int t = 0;
-        for (; t + 1 < ntiles; t += 2) {
-            issue(lookup(t + 1), r1);
+        for (; t + 2 < ntiles; t += 3) {
+            issue(lookup(t + 2), r2);
             compute(t, r0);
-            issue(lookup(min(t + 2, tl)), r0);
+            issue(lookup(min(t + 3, tl)), r0);
             compute(t + 1, r1);
+            issue(lookup(min(t + 4, tl)), r1);
+            compute(t + 2, r2);
         }
         if (t < ntiles) compute(t, r0);
+        if (t + 1 < ntiles) compute(t + 1, r1);
     }
 
-    // Merge the eight token groups (lanes with equal jj).
+    // Merge the TG token streams of each head (lanes equal in hw and jj,
+    // i.e. lane ids differing in the bits above 8*HW).
+    if constexpr (TG > 1) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-        float M = mref[h];
-        M = fmaxf(M, __shfl_xor(M, 8));
-        M = fmaxf(M, __shfl_xor(M, 16));
-        M = fmaxf(M, __shfl_xor(M, 32));
-        const float f = (mref[h] == -INFINITY) ? 0.f : exp2_fast(mref[h] - M);
-        float l = lsum[h] * f;
-        l += __shfl_xor(l, 8);
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
-        lsum[h] = l;
-        mref[h] = M;
+        for (int h = 0; h < G; ++h) {
+            float M = mref[h];
 #pragma unroll
-        for (int c = 0; c < NCH; ++c)
+            for (int m = 8 * HW; m < 64; m <<= 1) M = fmaxf(M, __shfl_xor(M, m));
+            const float f = (mref[h] == -INFINITY) ? 0.f : exp2_fast(mref[h] - M);
+            float l = lsum[h] * f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float x = o[h][c][e] * f;
-                x += __shfl_xor(x, 8);
-                x += __shfl_xor(x, 16);
-                x += __shfl_xor(x, 32);
-                o[h][c][e] = x;
-            }
+            for (int m = 8 * HW; m < 64; m <<= 1) l += __shfl_xor(l, m);
+            lsum[h] = l;
+            mref[h] = M;
+#pragma unroll
+            for (int c = 0; c < NCH; ++c)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    float x = o[h][c][e] * f;
+#pragma unroll
+                    for (int m = 8 * HW; m < 64; m <<= 1) x += __shfl_xor(x, m);
+                    o[h][c][e] = x;
+                }
+        }
     }
 
-    // Token group `tok` writes head tok of the group.
+    // After the merge every token stream holds the head's totals; stream tg
+    // writes the query heads h with h % TG == tg.
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-        if (tok != h) continue;
+        if (h % TG != tg) continue;
         const int hq = g * G + h;
         if (p.direct) {
             const float inv = lsum[h] > 0.f ? 1.f / lsum[h] : 0.f;
@@ -324,13 +346,28 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineParams p) {
     for (int c = 0; c < NC; ++c) acc[c] = 0.f;
     float L = 0.f;
     if (M != -INFINITY) {
-        for (int s = 0; s < S; ++s) {
-            const float2 ml = *reinterpret_cast<const float2 *>(p.ml_part + ((size_t)s * p.R + r) * 2);
-            const float w = (ml.x == -INFINITY) ? 0.f : exp2_fast((ml.x - M) * kLog2e);
-            L += w * ml.y;
-            const float *op = p.o_part + ((size_t)s * p.R + r) * D + lane * NC;
+        // Eight splits per step, all loads issued before the math.
+        constexpr int U = 8;
+        const size_t rstride = (size_t)p.R;
+        for (int s0 = 0; s0 < S; s0 += U) {
+            float2 ml[U];
+            float ov[U][NC];
 #pragma unroll
-            for (int c = 0; c < NC; ++c) acc[c] = fmaf(w, op[c], acc[c]);
+            for (int k = 0; k < U; ++k) {
+                const int sk = min(s0 + k, S - 1);
+                ml[k] = *reinterpret_cast<const float2 *>(p.ml_part + ((size_t)sk * rstride + r) * 2);
+                const float *op = p.o_part + ((size_t)sk * rstride + r) * D + lane * NC;
+#pragma unroll
+                for (int c = 0; c < NC; ++c) ov[k][c] = op[c];
+            }
+#pragma unroll
+            for (int k = 0; k < U; ++k) {
+                const bool use = (s0 + k < S) && ml[k].x != -INFINITY;
+                const float w = use ? exp2_fast((ml[k].x - M) * kLog2e) : 0.f;
+                L = fmaf(w, use ? ml[k].y : 0.f, L);
+#pragma unroll
+                for (int c = 0; c < NC; ++c) acc[c] = fmaf(w, use ? ov[k][c] : 0.f, acc[c]);
+            }
         }
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
@@ -351,20 +388,30 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineParams p) {
     if (p.lse && lane == 0) p.lse[r] = (L > 0.f) ? M + __logf(L) : -INFINITY;
 }
 
-template <int D, int G, bool PAGED>
+template <int D, int G, int HW, bool PAGED>
 hipError_t launch_decode_t(const DecodeParams &p, hipStream_t stream) {
-    const int blocks = (p.units + 3) / 4;
-    hipLaunchKernelGGL((decode_split_kernel<D, G, PAGED>), dim3(blocks), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((decode_split_kernel<D, G, HW, PAGED>), dim3(p.units), dim3(64), 0, stream, p);
     return hipGetLastError();
 }
 
-template <int D, bool PAGED>
+template <int D, int HW, bool PAGED>
 hipError_t launch_decode_g(const DecodeParams &p, int G, hipStream_t stream) {
     switch (G) {
-        case 1: return launch_decode_t<D, 1, PAGED>(p, stream);
-        case 2: return launch_decode_t<D, 2, PAGED>(p, stream);
-        case 4: return launch_decode_t<D, 4, PAGED>(p, stream);
-        case 8: return launch_decode_t<D, 8, PAGED>(p, stream);
+        case 1: return launch_decode_t<D, 1, HW, PAGED>(p, stream);
+        case 2: return launch_decode_t<D, 2, HW, PAGED>(p, stream);
+        case 4: return launch_decode_t<D, 4, HW, PAGED>(p, stream);
+        case 8: return launch_decode_t<D, 8, HW, PAGED>(p, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int D, bool PAGED>
+hipError_t launch_decode_hw(const DecodeParams &p, int G, hipStream_t stream) {
+    switch (p.HW) {
+        case 1: return launch_decode_g<D, 1, PAGED>(p, G, stream);
+        case 2: return launch_decode_g<D, 2, PAGED>(p, G, stream);
+        case 4: return launch_decode_g<D, 4, PAGED>(p, G, stream);
+        case 8: return launch_decode_g<D, 8, PAGED>(p, G, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -373,8 +420,8 @@ hipError_t launch_decode_g(const DecodeParams &p, int G, hipStream_t stream) {
 
 hipError_t launch_decode(const DecodeParams &p, int D, int G, bool paged, hipStream_t stream) {
     if (p.units <= 0) return hipSuccess;
-    if (D == 64) return paged ? launch_decode_g<64, true>(p, G, stream) : launch_decode_g<64, false>(p, G, stream);
-    if (D == 128) return paged ? launch_decode_g<128, true>(p, G, stream) : launch_decode_g<128, false>(p, G, stream);
+    if (D == 64) return paged ? launch_decode_hw<64, true>(p, G, stream) : launch_decode_hw<64, false>(p, G, stream);
+    if (D == 128) return paged ? launch_decode_hw<128, true>(p, G, stream) : launch_decode_hw<128, false>(p, G, stream);
     return hipErrorInvalidValue;
 }
 

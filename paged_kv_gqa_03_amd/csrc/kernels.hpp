@@ -31,7 +31,8 @@ struct DecodeParams {
     float *ml_part;  // [S, B, Hq, 2]     (S > 1)
     int B, Hq, Hkv, S, chunk;
     int direct;      // 1: single split writes the normalised bf16 output
-    int units;       // B * Hkv * S
+    int HW;          // KV heads per wave (1, 2, 4, 8; divides Hkv)
+    int units;       // B * (Hkv / HW) * S
     float sl2;       // scale * log2(e)
 };
 

@@ -44,23 +44,28 @@ def test_version():
 @pytest.mark.parametrize("B,Hkv,max_len", [(2, 2, 300), (16, 8, 2048), (32, 8, 4096), (128, 8, 4096),
                                            (1, 1, 100000), (512, 8, 4096), (4, 8, 16), (3, 1, 0)])
 def test_planner_bounds(B, Hkv, max_len):
-    S = pa.attn_plan_splits(B, Hkv, 4, max_len, 16, 256)
-    assert 1 <= S <= 256
-    if max_len > 64:
-        chunk = pa.attn_split_chunk(max_len, S)
-        assert chunk % 16 == 0 and chunk >= 64 or S == 1
-    # a larger batch never asks for more splits
-    assert pa.attn_plan_splits(2 * B, Hkv, 4, max_len, 16, 256) <= S or max_len <= 16
+    for s_head, tile in ((128, 2 * (8 // min(8, Hkv))), (16 * 128, 16)):
+        S = pa.attn_plan_splits(B, Hkv, 4, 128, max_len, 16, s_head, 256)
+        assert 1 <= S <= 256
+        if max_len > 4 * tile:
+            chunk = pa.attn_split_chunk(max_len, S)
+            assert chunk % 16 == 0 and (chunk >= 4 * tile or S == 1)
+        # a larger batch never asks for more splits
+        assert pa.attn_plan_splits(2 * B, Hkv, 4, 128, max_len, 16, s_head, 256) <= S or max_len <= 16
 
 
 def test_planner_fills_the_device_for_small_batches():
-    S = pa.attn_plan_splits(16, 8, 4, 2048, 16, 256)
+    # one KV head per wave (head stride != D): 16 * 8 * S waves
+    S = pa.attn_plan_splits(16, 8, 4, 128, 2048, 16, 16 * 128, 256)
     assert 16 * 8 * S >= 256 * 4
+    # eight adjacent heads per wave: 16 * S waves
+    S8 = pa.attn_plan_splits(16, 8, 4, 128, 2048, 16, 128, 256)
+    assert 16 * S8 >= 256 * 4 and S8 == 8 * S
 
 
 def test_planner_respects_page_slice_limit():
     # page_size 1 and a 4096-token sequence need at least ceil(4096 / 496) splits
-    S = pa.attn_plan_splits(512, 8, 4, 4096, 1, 256)
+    S = pa.attn_plan_splits(512, 8, 4, 128, 4096, 1, 128, 256)
     assert S >= 9
     assert pa.attn_split_chunk(4096, S) <= 496
 

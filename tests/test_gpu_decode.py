@@ -212,3 +212,16 @@ def test_split_then_combine_equals_fused_call(S):
     pa.attn_decode_combine(ws, 6, 32, 128, S, d["kv_lens"], case["max_kv_len"], out)
     torch.cuda.synchronize()
     assert torch.equal(fused, out)
+
+
+@pytest.mark.parametrize("Hkv,G,layout", [
+    (1, 4, "page_slot_head"),    # one head per wave
+    (4, 2, "page_slot_head"),    # four adjacent heads per wave
+    (16, 2, "page_slot_head"),   # eight heads per wave, two head groups
+    (4, 8, "page_head_slot"),    # head stride != D: one head per wave
+])
+@pytest.mark.parametrize("S", [1, 5])
+def test_paged_decode_heads_per_wave(Hkv, G, layout, S):
+    case = workloads.paged_decode_case(200 + Hkv + G, 3, Hkv * G, Hkv, 128, [1, 250, 700], 16, layout=layout)
+    ref, _ = oracle_paged(case)
+    assert_close(run_paged(case, S), ref, what="Hkv=%d G=%d %s S=%d" % (Hkv, G, layout, S))
