@@ -203,8 +203,10 @@ int attn_prefill_plan(const int32_t *q_lens_host, int B, int tile_rows,
                       int32_t *qo_indptr_host, int32_t *tile_to_batch_host,
                       int32_t *tile_to_index_host, int cap, int *num_tiles);
 
-/* Query rows per tile that attn_paged_prefill expects in its work map. */
-int attn_prefill_tile_rows(int D);
+/* Query rows per tile that attn_paged_prefill expects in its work map for
+ * head dim D and group size G = Hq / Hkv: a workgroup packs min(G, 4) query
+ * heads that share a KV head, and a tile holds 64 / min(G, 4) rows. */
+int attn_prefill_tile_rows(int D, int G);
 
 /*
  * Ragged paged prefill (AstrAI "CUDA Kernels" doc, Overview:
@@ -215,7 +217,8 @@ int attn_prefill_tile_rows(int D);
  *   qo_indptr  device int32 [B + 1]; sequence b owns rows
  *          qo_indptr[b] .. qo_indptr[b+1]
  *   tile_to_batch, tile_to_index  device copies of attn_prefill_plan's
- *          output for tile_rows = attn_prefill_tile_rows(D); num_tiles tiles
+ *          output for tile_rows = attn_prefill_tile_rows(D, Hq / Hkv);
+ *          num_tiles tiles
  *   k_pool, v_pool, kv_s_*, block_table, bt_sb, page_size  as in
  *          attn_paged_decode; kv_lens [B] = keys held by each sequence
  *          (prior context plus the new rows)
@@ -227,7 +230,9 @@ int attn_prefill_tile_rows(int D);
  *          mask[b*m_sb + j], mask_ndim 3 reads mask[b*m_sb + i*m_sq + j]
  *          with i the local row; combined with causality by AND
  *   o      packed [total_q, Hq, D] bf16: row r, head h at o + r*o_st + h*o_sh
- * Supported: D = 128, G in {1, 2, 4, 8}.
+ * Alignment: q/k/v rows 16-byte aligned, o rows 8-byte aligned, mask rows
+ * (m_sb, m_sq, pointer) 4-byte aligned; mask bytes at key positions >= kv_lens[b]
+ * are never read.  Supported: D = 128, G in {1, 2, 4, 8}.
  */
 int attn_paged_prefill(const void *q, int64_t q_st, int64_t q_sh, const int32_t *qo_indptr,
                        const int32_t *tile_to_batch, const int32_t *tile_to_index, int num_tiles,

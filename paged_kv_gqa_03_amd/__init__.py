@@ -44,7 +44,7 @@ _SIGS = {
     "attn_decode_combine": ([_P, _Z, _I, _I, _I, _I, _P, _I, _P, _L, _L, _P], _I),
     "attn_split_combine": ([_P, _P, _I, _I, _I, _P, _P, _P, _P], _I),
     "attn_prefill_plan": ([_P, _I, _I, _P, _P, _P, _I, _P], _I),
-    "attn_prefill_tile_rows": ([_I], _I),
+    "attn_prefill_tile_rows": ([_I, _I], _I),
     "attn_paged_prefill": ([_P, _L, _L, _P, _P, _P, _I, _P, _P, _L, _L, _L, _P, _L, _P, _P,
                             _P, _I, _L, _L, _P, _L, _L, _I, _I, _I, _I, _I, _F, _P], _I),
     "attn_swa_fp8_decode": ([_P, _L, _L, _P, _L, _L, _P, _L, _P, _L, _P, _P, _L, _L,
@@ -209,8 +209,8 @@ def attn_split_combine(o_part, ml_part, out_f32=None, out_bf16=None, lse=None, s
                                     _ptr(out_bf16), _ptr(lse), _stream(stream)))
 
 
-def attn_prefill_tile_rows(D):
-    rc = lib().attn_prefill_tile_rows(D)
+def attn_prefill_tile_rows(D, G):
+    rc = lib().attn_prefill_tile_rows(D, G)
     if rc < 0:
         _check(rc)
     return rc

@@ -392,13 +392,64 @@ int attn_prefill_plan(const int32_t *q_lens_host, int B, int tile_rows,
     return ok();
 }
 
-int attn_prefill_tile_rows(int D) { return D == 128 ? 64 : fail(ATTN_ERR_UNSUPPORTED, "prefill head dim %d", D); }
+int attn_prefill_tile_rows(int D, int G) {
+    if (D != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill_tile_rows: head dim %d not built (128)", D);
+    if (G != 1 && G != 2 && G != 4 && G != 8)
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill_tile_rows: group size %d not built (1, 2, 4, 8)", G);
+    return 64 / pa::prefill_heads_packed(G);
+}
 
-int attn_paged_prefill(const void *, int64_t, int64_t, const int32_t *, const int32_t *, const int32_t *, int,
-                       const void *, const void *, int64_t, int64_t, int64_t, const int32_t *, int64_t,
-                       const int32_t *, const int32_t *, const uint8_t *, int, int64_t, int64_t, void *,
-                       int64_t, int64_t, int, int, int, int, int, float, void *) {
-    return fail(ATTN_ERR_UNSUPPORTED, "attn_paged_prefill: not built yet");
+int attn_paged_prefill(const void *q, int64_t q_st, int64_t q_sh, const int32_t *qo_indptr,
+                       const int32_t *tile_to_batch, const int32_t *tile_to_index, int num_tiles,
+                       const void *k_pool, const void *v_pool,
+                       int64_t kv_s_page, int64_t kv_s_slot, int64_t kv_s_head,
+                       const int32_t *block_table, int64_t bt_sb, const int32_t *kv_lens,
+                       const int32_t *causal_offset,
+                       const uint8_t *mask, int mask_ndim, int64_t m_sb, int64_t m_sq,
+                       void *o, int64_t o_st, int64_t o_sh,
+                       int B, int Hq, int Hkv, int D, int page_size, float scale,
+                       void *stream) {
+    int G = 0, rc = check_heads(Hq, Hkv, D, &G);
+    if (rc) return rc;
+    if (D != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_paged_prefill: head dim %d not built (128)", D);
+    if (B < 0 || num_tiles < 0) return fail(ATTN_ERR_INVALID_ARG, "attn_paged_prefill: negative B or num_tiles");
+    if (page_size <= 0) return fail(ATTN_ERR_INVALID_ARG, "attn_paged_prefill: page_size must be >= 1");
+    if (!q || !qo_indptr || !k_pool || !v_pool || !block_table || !kv_lens || !o ||
+        (num_tiles > 0 && (!tile_to_batch || !tile_to_index)))
+        return fail(ATTN_ERR_INVALID_ARG, "attn_paged_prefill: null pointer");
+    if (!std::isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "attn_paged_prefill: scale is not finite");
+    if (mask && mask_ndim != 2 && mask_ndim != 3)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_paged_prefill: mask_ndim must be 2 or 3");
+    if (mask && (((uintptr_t)mask & 3u) || (m_sb & 3) || (mask_ndim == 3 && (m_sq & 3)) || m_sb < 0 || m_sq < 0))
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_paged_prefill: mask rows must be 4-byte aligned");
+    if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || ((uintptr_t)o & 7u) ||
+        !mult8(q_st) || !mult8(q_sh) || !mult8(kv_s_page) || !mult8(kv_s_slot) || !mult8(kv_s_head) ||
+        (o_st & 3) || (o_sh & 3))
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_paged_prefill: q/k/v rows must be 16-byte and o rows 8-byte aligned");
+    if (kv_s_page < 0 || kv_s_slot < 0 || kv_s_head < 0 || kv_s_page >= (1ll << 32) ||
+        (int64_t)(page_size - 1) * kv_s_slot + (int64_t)(Hkv - 1) * kv_s_head + D >= (1ll << 31))
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_paged_prefill: pool strides exceed the 32-bit page/slot addressing");
+    if (B == 0 || num_tiles == 0) return ok();
+    pa::PrefillParams p{};
+    p.q = static_cast<const uint16_t *>(q);
+    p.q_st = q_st; p.q_sh = q_sh;
+    p.qo_indptr = qo_indptr; p.t2b = tile_to_batch; p.t2i = tile_to_index; p.num_tiles = num_tiles;
+    p.k = static_cast<const uint16_t *>(k_pool);
+    p.v = static_cast<const uint16_t *>(v_pool);
+    p.s_page = kv_s_page; p.s_slot = kv_s_slot; p.s_head = kv_s_head;
+    p.bt = block_table; p.bt_sb = bt_sb;
+    p.ps = (uint32_t)page_size;
+    p.ps_magic = ((1ull << 32) + (uint64_t)page_size - 1) / (uint64_t)page_size;
+    p.kv_lens = kv_lens;
+    p.causal = causal_offset;
+    p.mask = mask;
+    p.mask_ndim = mask ? mask_ndim : 0;
+    p.m_sb = m_sb; p.m_sq = m_sq;
+    p.o = static_cast<uint16_t *>(o);
+    p.o_st = o_st; p.o_sh = o_sh;
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.G = G;
+    p.sl2 = scale * 1.4426950408889634f;
+    return launch_status(pa::launch_prefill(p, static_cast<hipStream_t>(stream)), "prefill kernel");
 }
 
 int attn_swa_fp8_decode(const void *, int64_t, int64_t, const uint8_t *, int64_t, int64_t, const void *, int64_t,

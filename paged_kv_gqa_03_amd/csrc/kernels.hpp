@@ -54,7 +54,35 @@ struct CombineParams {
     float *lse;
 };
 
+// Ragged paged prefill (work-map tiles x groups of packed query heads).
+struct PrefillParams {
+    const uint16_t *q;
+    int64_t q_st, q_sh;
+    const int32_t *qo_indptr, *t2b, *t2i;
+    int num_tiles;
+    const uint16_t *k, *v;
+    int64_t s_page, s_slot, s_head;
+    const int32_t *bt;
+    int64_t bt_sb;
+    uint32_t ps;
+    uint64_t ps_magic;
+    const int32_t *kv_lens;
+    const int32_t *causal;   // NULL: no causality
+    const uint8_t *mask;     // NULL when mask_ndim == 0
+    int mask_ndim;           // 0, 2 or 3
+    int64_t m_sb, m_sq;
+    uint16_t *o;
+    int64_t o_st, o_sh;
+    int B, Hq, Hkv, G;
+    float sl2;               // scale * log2(e)
+};
+
+// Query heads one prefill workgroup packs (they share a KV head); a work-map
+// tile then has 64 / prefill_heads_packed(G) rows.
+int prefill_heads_packed(int G);
+
 hipError_t launch_decode(const DecodeParams &p, int D, int G, bool paged, hipStream_t stream);
+hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream);
 hipError_t launch_combine(const CombineParams &p, int D, hipStream_t stream);
 
 }  // namespace pa

@@ -121,7 +121,9 @@ def prefill_case(seed, B, Hq, Hkv, D, ctx_range, q_range, page_size, mask_frac=N
     qo_indptr = torch.tensor([0] + list(_cumsum(q_lens)), dtype=torch.int32, device=device)
     mask = None
     if mask_frac is not None:
-        max_n = max(kv_lens) if kv_lens else 1
+        # key dimension padded to a multiple of 4 (mask rows 4-byte aligned);
+        # entries past a sequence's keys are never read
+        max_n = (max(max(kv_lens) if kv_lens else 1, 1) + 3) // 4 * 4
         max_q = max(q_lens) if q_lens else 1
         shape = (B, max_q, max_n) if mask_ndim == 3 else (B, max_n)
         mask = torch.rand(*shape, generator=g, device=device) >= mask_frac
