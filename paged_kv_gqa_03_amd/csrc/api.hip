@@ -452,10 +452,38 @@ int attn_paged_prefill(const void *q, int64_t q_st, int64_t q_sh, const int32_t 
     return launch_status(pa::launch_prefill(p, static_cast<hipStream_t>(stream)), "prefill kernel");
 }
 
-int attn_swa_fp8_decode(const void *, int64_t, int64_t, const uint8_t *, int64_t, int64_t, const void *, int64_t,
-                        const int64_t *, int64_t, const int64_t *, void *, int64_t, int64_t, int, int, int, int,
-                        int, int, float, void *) {
-    return fail(ATTN_ERR_UNSUPPORTED, "attn_swa_fp8_decode: not built yet");
+int attn_swa_fp8_decode(const void *q, int64_t q_st, int64_t q_sh,
+                        const uint8_t *kv_cache, int64_t c_sb, int64_t c_ss,
+                        const void *inv_scale, int64_t s_ss,
+                        const int64_t *swa_indices, int64_t i_st, const int64_t *swa_lens,
+                        void *o, int64_t o_st, int64_t o_sh,
+                        int T, int NH, int HD, int window, int block_size, int num_blocks,
+                        float scale, void *stream) {
+    if (T < 0 || NH <= 0 || window < 0 || block_size <= 0 || num_blocks < 0)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_swa_fp8_decode: bad sizes");
+    if (HD != 512) return fail(ATTN_ERR_UNSUPPORTED, "attn_swa_fp8_decode: head dim %d not built (512)", HD);
+    if (NH % 16 != 0) return fail(ATTN_ERR_UNSUPPORTED, "attn_swa_fp8_decode: NH=%d is not a multiple of 16", NH);
+    if (window > 1024) return fail(ATTN_ERR_UNSUPPORTED, "attn_swa_fp8_decode: window %d above 1024", window);
+    if (!q || !kv_cache || !inv_scale || !swa_indices || !swa_lens || !o)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_swa_fp8_decode: null pointer");
+    if (!std::isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "attn_swa_fp8_decode: scale is not finite");
+    if (!aligned16(q) || !mult8(q_st) || !mult8(q_sh) || !aligned16(kv_cache) || (c_sb & 15) || (c_ss & 15) ||
+        ((uintptr_t)o & 7u) || (o_st & 3) || (o_sh & 3) || ((uintptr_t)inv_scale & 1u))
+        return fail(ATTN_ERR_UNSUPPORTED,
+                    "attn_swa_fp8_decode: q rows and cache rows must be 16-byte aligned, o rows 8-byte aligned");
+    if (c_sb < 0 || c_ss < 0 || s_ss < 0 || i_st < window)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_swa_fp8_decode: bad strides");
+    if (T == 0) return ok();
+    pa::SwaParams p{};
+    p.q = static_cast<const uint16_t *>(q);
+    p.q_st = q_st; p.q_sh = q_sh;
+    p.cache = kv_cache; p.c_sb = c_sb; p.c_ss = c_ss;
+    p.inv_scale = static_cast<const uint16_t *>(inv_scale); p.s_ss = s_ss;
+    p.ind = swa_indices; p.i_st = i_st; p.lens = swa_lens;
+    p.o = static_cast<uint16_t *>(o); p.o_st = o_st; p.o_sh = o_sh;
+    p.T = T; p.NH = NH; p.W = window; p.bs = block_size;
+    p.sl2 = scale * 1.4426950408889634f;
+    return launch_status(pa::launch_swa(p, static_cast<hipStream_t>(stream)), "swa kernel");
 }
 
 }  // extern "C"

@@ -81,7 +81,25 @@ struct PrefillParams {
 // tile then has 64 / prefill_heads_packed(G) rows.
 int prefill_heads_packed(int G);
 
+// fp8 sliding-window decode (K = V), head dim 512, 16-head groups.
+struct SwaParams {
+    const uint16_t *q;
+    int64_t q_st, q_sh;
+    const uint8_t *cache;
+    int64_t c_sb, c_ss;
+    const uint16_t *inv_scale;
+    int64_t s_ss;
+    const int64_t *ind;
+    int64_t i_st;
+    const int64_t *lens;
+    uint16_t *o;
+    int64_t o_st, o_sh;
+    int T, NH, W, bs;
+    float sl2;   // scale * log2(e)
+};
+
 hipError_t launch_decode(const DecodeParams &p, int D, int G, bool paged, hipStream_t stream);
+hipError_t launch_swa(const SwaParams &p, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream);
 hipError_t launch_combine(const CombineParams &p, int D, hipStream_t stream);
 

@@ -1,0 +1,241 @@
+// swa.hip -- fp8 (OCP e4m3fn) sliding-window decode, MLA style (K = V),
+// for gfx950.
+//
+// Method (native_swa_decode.py: the host wrapper's problem statement and the
+// batched-SDPA fallback's steps): decode token t attends at most `window`
+// cache slots listed in swa_indices[t]; position j is admitted iff
+// j < swa_lens[t] and the slot index is >= 0; the slot is split into (block,
+// offset), its 512 fp8 bytes are dequantised with the slot's inverse scale,
+// and every query head of the token attends the same rows, which serve as
+// both keys and values.
+//
+// Work decomposition (cf. the CuTeDSL stub's plan: one CTA per (token, group
+// of 16 query heads), KV streamed in tiles): one 256-thread workgroup per
+// (16-head group, token).  Per tile of up to 128 window positions:
+//   1. the token's slot offsets and inverse scales go to LDS, then the rows
+//      (fp8, 512 B each) are staged in LDS; masked positions become zero rows;
+//   2. wave w computes S^T for positions 32w..32w+31 with
+//      v_mfma_f32_16x16x32_bf16 on rows converted fp8 -> bf16 exactly
+//      (v_cvt_scalef32_pk_bf16_fp8), Q^T for the 16 heads held in registers;
+//      the score is scale * inv_scale_j * (q . e4m3(x_j)), i.e. the exact
+//      dequantised product, with the scale folded into one multiply;
+//   3. the row max / sum across the four waves go through LDS;
+//   4. P' = P * inv_scale_j (bf16) is written to LDS, and wave w computes
+//      O^T for dims 128w..128w+127 = X^T P'^T, building the X^T operands by
+//      a byte transpose (v_perm) of four dims x eight positions and the same
+//      exact fp8 -> bf16 conversion.  Lane l then holds head l % 16 and four
+//      consecutive dims per output block, written as 8-byte bf16 stores.
+// Windows longer than 128 loop over tiles with an online softmax.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace pa {
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int HD = 512;
+constexpr int KT = 128;        // window positions per tile
+constexpr int XLD = HD + 16;   // staged row stride (bytes)
+constexpr int PLD = KT + 8;    // P' row stride (elements)
+
+__device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Eight e4m3fn codes (lo: codes 0..3, hi: codes 4..7) -> eight bf16, exact.
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
+    const uint32_t a = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false));
+    const uint32_t b = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true));
+    const uint32_t c = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false));
+    const uint32_t d = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true));
+    return __builtin_bit_cast(bf16x8_t, make_uint4(a, b, c, d));
+}
+
+// v_perm_b32: result byte i = selector byte i, where 0..3 pick bytes of the
+// second operand and 4..7 bytes of the first.
+__device__ __forceinline__ uint32_t perm(uint32_t hi_src, uint32_t lo_src, uint32_t sel) {
+    return __builtin_amdgcn_perm(hi_src, lo_src, sel);
+}
+
+// Transpose a 4-position x 4-byte block: w[e] holds bytes (d0..d3) of
+// position e; out[m] holds byte d_m of positions 0..3.
+__device__ __forceinline__ void transpose4x4(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3, uint32_t (&out)[4]) {
+    const uint32_t a01 = perm(w1, w0, 0x06020400u);  // w0.b0 w1.b0 w0.b2 w1.b2
+    const uint32_t b01 = perm(w1, w0, 0x07030501u);  // w0.b1 w1.b1 w0.b3 w1.b3
+    const uint32_t a23 = perm(w3, w2, 0x06020400u);
+    const uint32_t b23 = perm(w3, w2, 0x07030501u);
+    out[0] = perm(a23, a01, 0x05040100u);  // b0 of w0..w3
+    out[2] = perm(a23, a01, 0x07060302u);  // b2
+    out[1] = perm(b23, b01, 0x05040100u);  // b1
+    out[3] = perm(b23, b01, 0x07060302u);  // b3
+}
+
+__global__ __launch_bounds__(256) void swa_kernel(const SwaParams p) {
+    __shared__ __attribute__((aligned(16))) uint8_t x_lds[KT * XLD];
+    __shared__ int64_t row_off[KT];
+    __shared__ float inv_lds[KT];
+    __shared__ __attribute__((aligned(16))) uint16_t p_lds[16 * PLD];
+    __shared__ float red_max[4][16], red_sum[4][16];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int r = lane & 15, q4 = lane >> 4;
+    const int t = blockIdx.y;
+    const int head = blockIdx.x * 16 + r;
+    int64_t len = p.lens[t];
+    len = len < 0 ? 0 : (len > p.W ? p.W : len);
+
+    // Q^T operand: head r, dims 32s + 8*q4 .. +8.
+    bf16x8_t qf[16];
+    {
+        const uint16_t *qr = p.q + (int64_t)t * p.q_st + (int64_t)head * p.q_sh + 8 * q4;
+#pragma unroll
+        for (int s = 0; s < 16; ++s) qf[s] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(qr + 32 * s));
+    }
+    f32x4_t oacc[2][4];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) oacc[a][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float M = -INFINITY, L = 0.f;
+
+    const int ntile = (int)((len + KT - 1) / KT);
+    for (int tile = 0; tile < ntile; ++tile) {
+        const int j0 = tile * KT;
+        const int nk = (int)min((int64_t)KT, len - j0);
+        const int nkb = (nk + 31) >> 5;   // 32-position blocks in this tile
+        __syncthreads();                  // the previous tile is fully consumed
+        if (tid < KT) {
+            int64_t off = -1;
+            float inv = 0.f;
+            if (tid < nk) {
+                const int64_t idx = p.ind[(int64_t)t * p.i_st + j0 + tid];
+                if (idx >= 0) {
+                    off = (idx / p.bs) * p.c_sb + (idx % p.bs) * p.c_ss;
+                    inv = bf16_lo((uint32_t)p.inv_scale[idx * p.s_ss]);
+                }
+            }
+            row_off[tid] = off;
+            inv_lds[tid] = inv;
+        }
+        __syncthreads();
+        // Stage rows of the active blocks: chunk c = 16 bytes, 32 per row.
+#pragma unroll 4
+        for (int c = tid; c < nkb * 32 * 32; c += 256) {
+            const int key = c >> 5, ch = c & 31;
+            const int64_t off = row_off[key];
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (off >= 0) v = *reinterpret_cast<const uint4 *>(p.cache + off + ch * 16);
+            *reinterpret_cast<uint4 *>(&x_lds[key * XLD + ch * 16]) = v;
+        }
+        __syncthreads();
+
+        // Scores of positions 32w .. 32w+31 (S^T blocks kb = 2w, 2w+1).
+        float x[2][4];
+        float mt = -INFINITY;
+        if (w < nkb) {
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const int kb = 2 * w + h2;
+                f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                const uint8_t *xr = &x_lds[(16 * kb + r) * XLD + 8 * q4];
+#pragma unroll
+                for (int s = 0; s < 16; ++s) {
+                    const uint2 c8 = *reinterpret_cast<const uint2 *>(xr + 32 * s);
+                    acc = mfma16(fp8x8_to_bf16(c8.x, c8.y), qf[s], acc);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int key = 16 * kb + 4 * q4 + i;
+                    x[h2][i] = row_off[key] >= 0 ? acc[i] * p.sl2 * inv_lds[key] : -INFINITY;
+                    mt = fmaxf(mt, x[h2][i]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) x[h2][i] = -INFINITY;
+        }
+        mt = fmaxf(mt, __shfl_xor(mt, 16));
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        if (q4 == 0) red_max[w][r] = mt;
+        __syncthreads();
+        mt = fmaxf(fmaxf(red_max[0][r], red_max[1][r]), fmaxf(red_max[2][r], red_max[3][r]));
+        const float M_new = fmaxf(M, mt);
+        const float M_use = M_new == -INFINITY ? 0.f : M_new;
+        const float alpha = exp2_fast(M - M_use);
+        M = M_new;
+        float psum = 0.f;
+        if (w < nkb) {
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const int key0 = 16 * (2 * w + h2) + 4 * q4;
+                float pv[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    pv[i] = exp2_fast(x[h2][i] - M_use);
+                    psum += pv[i];
+                }
+                uint2 pk;
+                pk.x = pack_bf16(pv[0] * inv_lds[key0], pv[1] * inv_lds[key0 + 1]);
+                pk.y = pack_bf16(pv[2] * inv_lds[key0 + 2], pv[3] * inv_lds[key0 + 3]);
+                *reinterpret_cast<uint2 *>(&p_lds[r * PLD + key0]) = pk;
+            }
+        }
+        psum += __shfl_xor(psum, 16);
+        psum += __shfl_xor(psum, 32);
+        if (q4 == 0) red_sum[w][r] = psum;
+        __syncthreads();
+        L = L * alpha + (red_sum[0][r] + red_sum[1][r] + red_sum[2][r] + red_sum[3][r]);
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) oacc[a][m] *= alpha;
+
+        // O^T for dims 128w .. 128w+127: block (mb, mm) covers dims
+        // 64mb + 4R + mm for A-row R.
+        for (int ks = 0; ks < nkb; ++ks) {
+            const bf16x8_t bp = __builtin_bit_cast(bf16x8_t,
+                *reinterpret_cast<const uint4 *>(&p_lds[r * PLD + 32 * ks + 8 * q4]));
+#pragma unroll
+            for (int a = 0; a < 2; ++a) {
+                const int mb = 2 * w + a;
+                const uint8_t *xc = &x_lds[(32 * ks + 8 * q4) * XLD + 64 * mb + 4 * r];
+                uint32_t dw[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) dw[e] = *reinterpret_cast<const uint32_t *>(xc + e * XLD);
+                uint32_t lo[4], hi[4];
+                transpose4x4(dw[0], dw[1], dw[2], dw[3], lo);
+                transpose4x4(dw[4], dw[5], dw[6], dw[7], hi);
+#pragma unroll
+                for (int mm = 0; mm < 4; ++mm) oacc[a][mm] = mfma16(fp8x8_to_bf16(lo[mm], hi[mm]), bp, oacc[a][mm]);
+            }
+        }
+    }
+
+    const float invL = L > 0.f ? 1.f / L : 0.f;
+    uint16_t *orow = p.o + (int64_t)t * p.o_st + (int64_t)head * p.o_sh;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int d0 = 64 * (2 * w + a) + 16 * q4 + 4 * i;
+            uint2 v;
+            v.x = pack_bf16(oacc[a][0][i] * invL, oacc[a][1][i] * invL);
+            v.y = pack_bf16(oacc[a][2][i] * invL, oacc[a][3][i] * invL);
+            *reinterpret_cast<uint2 *>(orow + d0) = v;
+        }
+}
+
+}  // namespace
+
+hipError_t launch_swa(const SwaParams &p, hipStream_t stream) {
+    if (p.T <= 0) return hipSuccess;
+    hipLaunchKernelGGL(swa_kernel, dim3(p.NH / 16, p.T), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace pa

@@ -1,0 +1,104 @@
+"""GPU parity of the fp8 sliding-window decode (K = V) against the CPU oracle.
+
+The oracle dequantises exactly (e4m3fn code * inverse scale in fp64).
+Bar: |gpu - oracle| <= 1e-2 + 1e-2 |oracle| on the bf16 outputs."""
+import pytest
+import torch
+
+import oracle
+import paged_kv_gqa_03_amd as pa
+import workloads
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def assert_close(got, ref, atol=1e-2, rtol=1e-2, what=""):
+    got = got.detach().to("cpu", torch.float64)
+    err = (got - ref).abs()
+    bad = err > atol + rtol * ref.abs()
+    assert not bool(bad.any()), "%s: %d of %d elements off, max err %.4g" % (
+        what, int(bad.sum()), bad.numel(), float(err.max()))
+
+
+def run_swa(case):
+    d = {k: case[k].to(DEV) for k in ("q", "cache", "inv_scale", "indices", "lens")}
+    out = torch.full_like(d["q"], float("nan"))
+    pa.attn_swa_fp8_decode(d["q"], d["cache"], d["inv_scale"], d["indices"], d["lens"], out,
+                           case["block_size"], case["scale"])
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_swa(case):
+    out, _ = oracle.swa_fp8_decode(case["q"], case["cache"], case["inv_scale"], case["indices"], case["lens"],
+                                   case["block_size"], case["scale"])
+    return out
+
+
+def test_swa_config():
+    case = workloads.swa_fp8()
+    assert_close(run_swa(case), oracle_swa(case), what="swa fp8 config")
+
+
+@pytest.mark.parametrize("W,lens,neg", [
+    (128, [128, 1, 64, 127], 0.0),
+    (128, [128, 90, 33, 2], 0.25),    # masked slots inside the window
+    (300, [300, 129, 128, 257], 0.1),  # several 128-position tiles
+    (64, [64, 17, 0, 63], 0.0),        # an empty window
+    (96, [200, 96, 50, 1], 0.0),       # lens above the window are clipped to it
+])
+def test_swa_windows(W, lens, neg):
+    case = workloads.swa_case(400 + W + len(lens), len(lens), 32, 512, W, 256, 8, lens=lens, neg_frac=neg)
+    assert_close(run_swa(case), oracle_swa(case), what="W=%d" % W)
+
+
+def test_swa_empty_window_gives_zero():
+    case = workloads.swa_case(410, 3, 16, 512, 32, 256, 2, lens=[0, 5, 3])
+    case["indices"][2, :] = -1
+    out = run_swa(case).cpu()
+    assert torch.equal(out[0], torch.zeros_like(out[0])) and torch.equal(out[2], torch.zeros_like(out[2]))
+    assert_close(out, oracle_swa(case))
+
+
+def test_swa_every_fp8_code():
+    """Cache rows that hold every finite e4m3fn code (and signed zeros)."""
+    case = workloads.swa_case(420, 2, 16, 512, 128, 256, 1, lens=[128, 77])
+    codes = torch.tensor([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=torch.uint8)
+    rows = torch.stack([codes[torch.randperm(254, generator=torch.Generator().manual_seed(i))].repeat(3)[:512]
+                        for i in range(256)])
+    case["cache"] = rows.view(1, 256, 512).contiguous()
+    case["inv_scale"] = torch.full((256, 1), 0.01).to(torch.bfloat16)
+    assert_close(run_swa(case), oracle_swa(case), what="all codes")
+
+
+def test_swa_strided_query_and_output():
+    case = workloads.swa_case(430, 5, 48, 512, 128, 256, 4, len_range=(1, 128))
+    qbig = torch.zeros(5, 64, 512, dtype=torch.bfloat16)
+    qbig[:, 8:56] = case["q"]
+    case["q"] = qbig[:, 8:56]                       # head stride 512, token stride 64*512
+    d = {k: case[k].to(DEV) for k in ("cache", "inv_scale", "indices", "lens")}
+    qd = qbig.to(DEV)[:, 8:56]
+    obig = torch.zeros(5, 50, 512, dtype=torch.bfloat16, device=DEV)
+    out = obig[:, 1:49]
+    pa.attn_swa_fp8_decode(qd, d["cache"], d["inv_scale"], d["indices"], d["lens"], out, 256, case["scale"])
+    torch.cuda.synchronize()
+    assert_close(out, oracle_swa(case))
+    assert torch.equal(obig[:, 0].cpu(), torch.zeros(5, 512, dtype=torch.bfloat16))
+    assert torch.equal(obig[:, 49].cpu(), torch.zeros(5, 512, dtype=torch.bfloat16))
+
+
+def test_swa_matches_fallback_rounding_within_tolerance():
+    """The fallback rounds the dequantised rows to bf16; the exact-product
+    result the kernel computes stays within the same tolerance of it."""
+    case = workloads.swa_case(440, 8, 32, 512, 128, 256, 4, len_range=(1, 128))
+    ref_rounded, _ = oracle.swa_fp8_decode(case["q"], case["cache"], case["inv_scale"], case["indices"],
+                                           case["lens"], case["block_size"], case["scale"],
+                                           emulate_bf16_dequant=True)
+    assert_close(run_swa(case), ref_rounded)
+
+
+def test_swa_repeat_runs_are_bit_identical():
+    case = workloads.swa_fp8(seed=1016)
+    a = run_swa(case).clone()
+    assert torch.equal(a, run_swa(case))

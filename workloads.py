@@ -163,7 +163,7 @@ def swa_case(seed, T, NH, HD, W, block_size, num_blocks, len_range=None, lens=No
     cache = codes.view(torch.uint8).reshape(num_blocks, block_size, HD)
     ind = torch.full((T, W), -1, dtype=torch.int64, device=device)
     for t in range(T):
-        n = lens[t]
+        n = min(lens[t], W)   # a length above the window admits the whole window
         if n > 0:
             pick = torch.randperm(slots, generator=g, device=device)[:n]
             ind[t, :n] = pick
