@@ -77,16 +77,18 @@ def source_hash(path):
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def load_traffic(bytes_per_launch):
-    """HBM traffic of one split-kernel launch from the committed counter
-    summary, or None when absent or taken on another kernel source."""
+def load_traffic():
+    """HBM bytes (read + write) of one split-kernel launch of this workload,
+    from the committed rocprofv3 counter summary (calibrated FETCH_SIZE +
+    WRITE_SIZE), and its read / algorithmic ratio; (None, None) when the
+    summary is absent or was taken on another kernel source."""
     if not os.path.exists(COUNTERS):
-        return None
+        return None, None
     with open(COUNTERS) as f:
         c = json.load(f)
     if c.get("decode_src_sha256") != source_hash(DECODE_SRC):
-        return None
-    return c.get("hbm_bytes_per_launch")
+        return None, None
+    return c.get("hbm_bytes_per_launch"), c.get("read_over_algorithmic")
 
 
 def time_calls(torch, fn, sets, steps, warmup):
@@ -171,9 +173,10 @@ def main():
         k_ms, comb, k_bytes = ms, 0.0, mean_bytes
         kernel = "decode_split_kernel<128,4,paged> (direct write)"
     achieved = k_bytes / (k_ms * 1e-3) / 1e9
-    traffic = load_traffic(k_bytes)
+    traffic, read_ratio = load_traffic() if args.workload == "paged_b128" else (None, None)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kernel,
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "traffic_read_over_algorithmic": read_ratio, "kernel": kernel,
                 "kernel_us": round(k_ms * 1e3, 2), "combine_us": round(comb * 1e3, 2),
                 "algorithmic_bytes_per_launch": int(k_bytes)}
 
@@ -277,7 +280,68 @@ def run_extras(torch, pa, dev, args):
         del sets
         torch.cuda.empty_cache()
     out["contiguous_b16_kv2048"] = bench_contiguous(torch, pa, dev, steps, warm, 0)
+    out["ragged_prefill"] = bench_prefill(torch, pa, dev, steps, warm, masked=False)
+    out["ragged_prefill_masked"] = bench_prefill(torch, pa, dev, steps, warm, masked=True)
+    out["swa_fp8"] = bench_swa(torch, pa, dev, steps, warm)
     return out
+
+
+def prefill_flops(case):
+    """4 * D * Hq per visible (query row, key) pair: keys j <= c_b + i of the
+    n_b keys (the random mask is not subtracted: it removes no tile work)."""
+    total = 0
+    for c, qn, n in zip(case["ctx_lens"], case["q_lens"], case["kv_lens"].tolist()):
+        for i in range(qn):
+            total += min(n, c + i + 1)
+    return 4 * case["D"] * case["Hq"] * total
+
+
+def bench_prefill(torch, pa, dev, steps, warm, masked):
+    """Ragged paged prefill: 8 sequences, context U[0,2048], new rows U[1,512],
+    Hq=32 Hkv=8 D=128 ps=16, causal; optionally the 10%-dropped 3-D mask."""
+    import workloads
+    sets = [workloads.ragged_prefill(device=dev, masked=masked, seed=1005 + 7919 * r) for r in range(4)]
+    R = pa.attn_prefill_tile_rows(128, 4)
+    for s in sets:
+        _, t2b, t2i = pa.attn_prefill_plan(s["q_lens"], R)
+        s["t2b"], s["t2i"] = t2b.to(dev), t2i.to(dev)
+        s["out"] = torch.empty_like(s["q"])
+        s["flops"] = prefill_flops(s)
+
+    def call(s):
+        pa.attn_paged_prefill(s["q"], s["qo_indptr"], s["t2b"], s["t2i"], s["k_pool"], s["v_pool"],
+                              s["block_table"], s["kv_lens"], s["out"], 16, s["scale"],
+                              causal_offset=s["causal_offset"], mask=s["mask"])
+    ms = time_calls(torch, call, sets, steps, warm)
+    fl = sum(sets[i % len(sets)]["flops"] for i in range(steps)) / steps
+    tf = fl / (ms * 1e-3) / 1e12
+    return {"us_per_call": round(ms * 1e3, 2), "TFLOP/s": round(tf, 1), "gflop_per_call": round(fl / 1e9, 2),
+            "mfma_util": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "rotation_sets": len(sets)}
+
+
+def swa_bytes(case):
+    T, NH, HD, W = case["T"], case["NH"], case["HD"], case["W"]
+    lens = [min(int(x), W) for x in case["lens"].tolist()]
+    return 2 * T * NH * HD * 2 + sum(n * (HD + 2 + 8) for n in lens) + 8 * T
+
+
+def bench_swa(torch, pa, dev, steps, warm):
+    """fp8 sliding-window decode: T=64, NH=128, HD=512, window 128."""
+    import workloads
+    per = swa_bytes(workloads.swa_fp8(device=dev))
+    R = min(32, max(2, math.ceil(6.0e8 / per)))
+    sets = [workloads.swa_fp8(device=dev, seed=1006 + 7919 * r) for r in range(R)]
+    for s in sets:
+        s["out"] = torch.empty_like(s["q"])
+
+    def call(s):
+        pa.attn_swa_fp8_decode(s["q"], s["cache"], s["inv_scale"], s["indices"], s["lens"], s["out"],
+                               s["block_size"], s["scale"])
+    ms = time_calls(torch, call, sets, steps, warm)
+    nb = sum(swa_bytes(sets[i % R]) for i in range(steps)) / steps
+    gbs = nb / (ms * 1e-3) / 1e9
+    return {"us_per_call": round(ms * 1e3, 2), "GB/s": round(gbs, 1), "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "bytes_per_call": int(nb), "rotation_sets": R}
 
 
 def bench_contiguous(torch, pa, dev, steps, warm, num_splits):
