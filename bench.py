@@ -148,30 +148,29 @@ def main():
     gbs = mean_bytes / (ms * 1e-3) / 1e9
 
     # --- per-kernel breakdown with HIP events on the launch stream ---------
+    # The split kernel alone (attn_paged_decode_split: same launch, every
+    # piece written as a partial) and the combine, each bracketed by events.
     stream = torch.cuda.current_stream()
     n_k = max(20, args.steps)
-    split_ms, comb_ms = [], []
-    if S > 1:
-        for i in range(args.warmup + n_k):
-            s = sets[i % R]
-            e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-            e0.record(stream)
-            pa.attn_paged_decode_split(s["q"], s["k_pool"], s["v_pool"], s["block_table"], s["kv_lens"],
-                                       max_len, s["page_size"], s["scale"], S, ws)
-            e1.record(stream)
-            pa.attn_decode_combine(ws, s["B"], s["Hq"], s["D"], S, s["kv_lens"], max_len, s["out"])
-            e2.record(stream)
-            if i >= args.warmup:
-                split_ms.append((e0, e1, e2, s["bytes"]))
-        torch.cuda.synchronize()
-        ks = [(a.elapsed_time(b), b.elapsed_time(c), nb) for a, b, c, nb in split_ms]
-        k_ms = sum(k[0] for k in ks) / len(ks)
-        comb = sum(k[1] for k in ks) / len(ks)
-        k_bytes = sum(k[2] for k in ks) / len(ks)
-        kernel = "decode_split_kernel<128,4,paged> (fp32 partials)"
-    else:
-        k_ms, comb, k_bytes = ms, 0.0, mean_bytes
-        kernel = "decode_split_kernel<128,4,paged> (direct write)"
+    marks = []
+    for i in range(args.warmup + n_k):
+        s = sets[i % R]
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        e0.record(stream)
+        pa.attn_paged_decode_split(s["q"], s["k_pool"], s["v_pool"], s["block_table"], s["kv_lens"],
+                                   max_len, s["page_size"], s["scale"], S, ws)
+        e1.record(stream)
+        pa.attn_decode_combine(ws, s["B"], s["Hq"], s["Hkv"], s["D"], S, s["k_pool"].stride(2), s["kv_lens"],
+                               max_len, s["out"])
+        e2.record(stream)
+        if i >= args.warmup:
+            marks.append((e0, e1, e2, s["bytes"]))
+    torch.cuda.synchronize()
+    ks = [(a.elapsed_time(b), b.elapsed_time(c), nb) for a, b, c, nb in marks]
+    k_ms = sum(k[0] for k in ks) / len(ks)
+    comb = sum(k[1] for k in ks) / len(ks)
+    k_bytes = sum(k[2] for k in ks) / len(ks)
+    kernel = "decode_split_kernel<128,4,8,paged> (balanced partition, %d slices)" % S
     achieved = k_bytes / (k_ms * 1e-3) / 1e9
     traffic, read_ratio = load_traffic() if args.workload == "paged_b128" else (None, None)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

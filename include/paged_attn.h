@@ -58,44 +58,37 @@ int attn_version(void);
 /* ------------------------------------------------------------ split plan */
 
 /*
- * Split-count planner for decode (AstrAI csrc commit history: the commit
- * that partitions KV across gridDim.z and sizes the split count to fill the
+ * Decode work partition (AstrAI csrc commit history: the commit that
+ * partitions KV across gridDim.z and sizes the split count to fill the
  * device, and the later one that retargets it at a fixed total block count
- * after a grid search).  The decode kernel runs one wave per (sequence,
- * group of adjacent KV heads, split); a group is up to 8 heads when the KV
- * head stride `kv_s_head` equals D (heads of a token contiguous), else one
- * head.  The planner chooses S >= 1 so that those waves fill `num_cus`
- * compute units (0 = query the current device) without splits shorter than
- * four decode tiles.  S = 1 means a single pass that writes the normalised
- * output directly.  page_size 0 plans for a contiguous source (pass its K
- * head stride as kv_s_head).  For a paged source S is at least
- * ceil(max_kv_len / (510 * page_size)) (rounded to 16 tokens), the most pages
- * one split's LDS slice of the block table holds; attn_paged_decode rejects a
- * smaller explicit num_splits with ATTN_ERR_UNSUPPORTED.  Host-only and
- * deterministic; returns S, or a negative error code.
+ * after a grid search).  Decode runs one wave per slice of a balanced
+ * partition: the rows (sequence, group of adjacent KV heads) are laid end to
+ * end and the line of all their tokens is cut into `num_splits` = W equal
+ * slices, whatever the spread of kv_lens.  A row is a group of up to 8 KV
+ * heads when the KV head stride `kv_s_head` equals D (heads of a token
+ * contiguous), else one head.  This planner returns W for `num_cus`
+ * compute units (0 = query the current device): about two waves per unit,
+ * and no slice shorter than 64 tokens of a row given max_kv_len.  page_size
+ * 0 stands for a contiguous source (pass its K head stride as kv_s_head).
+ * Host-only and deterministic; returns W >= 1, or a negative error code.
  */
 int attn_plan_splits(int B, int Hkv, int G, int D, int max_kv_len, int page_size, int64_t kv_s_head,
                      int num_cus);
 
 /*
- * Tokens per split for a given split count: the KV range of sequence b is
- * cut into chunks [s*chunk, (s+1)*chunk) clipped to kv_lens[b]; chunk is a
- * multiple of 16.  Returns the chunk, or a negative error code.
- */
-int attn_split_chunk(int max_kv_len, int num_splits);
-
-/*
- * Bytes of device workspace that decode needs for S = num_splits:
- *   o_part  float [S, B, Hq, D]   unnormalised partial outputs
- *   ml_part float [S, B, Hq, 2]   (m, l) per partial, starting at the first
- *                                 256-byte boundary after o_part
- * m is a reference value in natural-log units of the scaled score and l the
- * sum of exp(score - m) over the split; o = sum exp(score - m) v.  The split
- * kernel writes every slot a non-empty split owns, so the workspace needs
- * no initialisation (cf. the commit that switched alloc_split_partials to
- * torch::empty).  attn_decode / attn_paged_decode with one split write the
- * output directly and need no workspace; attn_paged_decode_split always
- * does.  Returns 0 for empty shapes.
+ * Bytes of device workspace decode needs with W = num_splits slices:
+ *   o_part  float [(B + W) * Hq, D]  unnormalised partial outputs
+ *   ml_part float [(B + W) * Hq, 2]  (m, l) per partial, starting at the
+ *                                    first 256-byte boundary after o_part
+ * The piece of row r in slice w is stored at slot r + w (every row or slice
+ * boundary along the line advances r or w, so slots are unique); local query
+ * head i of the row sits at partial row slot * heads_per_row + i.  m is a
+ * reference value in natural-log units of the scaled score (every
+ * exp(score - m) <= e^(8 ln 2)); l = sum exp(score - m), o = sum exp(score -
+ * m) v over the piece.  The split kernel writes every slot it owns, so the
+ * workspace needs no initialisation (cf. the commit that switched
+ * alloc_split_partials to torch::empty).  attn_decode / attn_paged_decode
+ * with W = 1 need no workspace.  Returns 0 for empty shapes.
  */
 size_t attn_decode_workspace_bytes(int B, int Hq, int D, int num_splits);
 
@@ -111,10 +104,13 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int D, int num_splits);
  *   o   [B, Hq, D]: (b, h, d) at o + b*o_sb + h*o_sh + d
  *   kv_lens  device int32 [B], each in [0, kv_len]; NULL = all equal kv_len
  *   scale    multiplies q.k before the softmax (normally 1/sqrt(D))
- *   num_splits  0 = attn_plan_splits() on the current device, else S >= 1
- *   workspace   >= attn_decode_workspace_bytes(B, Hq, D, S) bytes, device
+ *   num_splits  slices W of the balanced partition; 0 = attn_plan_splits()
+ *               on the current device
+ *   workspace   >= attn_decode_workspace_bytes(B, Hq, D, W) bytes, device,
+ *               256-byte aligned (may be NULL when W = 1)
  * Supported: D in {64, 128}, G = Hq/Hkv in {1, 2, 4, 8}.
- * Launches the split kernel and, when S > 1, the combine kernel.
+ * Launches the split kernel, then the combine kernel, which merges rows
+ * spread over several slices and zeroes rows without keys.
  */
 int attn_decode(const void *q, int64_t q_sb, int64_t q_sh,
                 const void *k, int64_t k_sb, int64_t k_sh, int64_t k_sl,
@@ -137,10 +133,11 @@ int attn_decode(const void *q, int64_t q_sb, int64_t q_sh,
  *          slot j % page_size.  Entries past a sequence's last page are
  *          never read.
  *   kv_lens  int32 [B], each in [0, max_kv_len]
- *   max_kv_len  host-side bound used to size the grid; max_kv_len *
- *          page_size must stay below 2^32
+ *   max_kv_len  host-side bound on kv_lens, used by the planner;
+ *          max_kv_len * page_size must stay below 2^32
  *   o      [B, Hq, D] bf16 output
  * Supported: D in {64, 128}, G in {1, 2, 4, 8}, any page_size >= 1.
+ * A slice longer than 510 pages is processed as consecutive sub-pieces.
  */
 int attn_paged_decode(const void *q, int64_t q_sb, int64_t q_sh,
                       const void *k_pool, const void *v_pool,
@@ -156,12 +153,12 @@ int attn_paged_decode(const void *q, int64_t q_sb, int64_t q_sh,
  * The two halves of attn_paged_decode, for callers that schedule them
  * separately (e.g. to combine partials gathered from several devices, or to
  * time each kernel).  attn_paged_decode_split takes the arguments of
- * attn_paged_decode minus the output and always writes fp32 partials for
- * the effective split count into `workspace` (laid out as documented at
- * attn_decode_workspace_bytes), even when S = 1.  attn_decode_combine then
- * writes o [B, Hq, D] bf16 from that workspace; it must be given the same
- * B, Hq, D, num_splits (after planning, i.e. the explicit S), kv_lens and
- * max_kv_len, and reads only the splits that can hold keys of each sequence.
+ * attn_paged_decode minus the output and writes every piece as an fp32
+ * partial into `workspace` (layout at attn_decode_workspace_bytes).
+ * attn_decode_combine then writes o [B, Hq, D] bf16 from that workspace; it
+ * must be given the same B, Hq, Hkv, D, num_splits (after planning, i.e.
+ * the explicit W), KV head stride, kv_lens (NULL = all max_kv_len) and
+ * max_kv_len, from which it recomputes where each row's pieces lie.
  */
 int attn_paged_decode_split(const void *q, int64_t q_sb, int64_t q_sh,
                             const void *k_pool, const void *v_pool,
@@ -171,9 +168,9 @@ int attn_paged_decode_split(const void *q, int64_t q_sb, int64_t q_sh,
                             int B, int Hq, int Hkv, int D, int page_size, float scale,
                             int num_splits, void *workspace, size_t workspace_bytes, void *stream);
 
-int attn_decode_combine(const void *workspace, size_t workspace_bytes, int B, int Hq, int D, int num_splits,
-                        const int32_t *kv_lens, int max_kv_len, void *o, int64_t o_sb, int64_t o_sh,
-                        void *stream);
+int attn_decode_combine(const void *workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int D,
+                        int num_splits, int64_t kv_s_head, const int32_t *kv_lens, int max_kv_len, void *o,
+                        int64_t o_sb, int64_t o_sh, void *stream);
 
 /*
  * Log-sum-exp combine of split partials (AstrAI csrc commit history: the

@@ -12,7 +12,7 @@ import os
 import torch
 
 __all__ = [
-    "AttnError", "lib", "attn_version", "attn_last_error", "attn_plan_splits", "attn_split_chunk",
+    "AttnError", "lib", "attn_version", "attn_last_error", "attn_plan_splits",
     "attn_decode_workspace_bytes", "attn_decode", "attn_paged_decode", "attn_paged_decode_split",
     "attn_decode_combine", "attn_split_combine",
     "attn_prefill_plan", "attn_prefill_tile_rows", "attn_paged_prefill", "attn_swa_fp8_decode",
@@ -33,7 +33,6 @@ _SIGS = {
     "attn_last_error": ([], ctypes.c_char_p),
     "attn_version": ([], _I),
     "attn_plan_splits": ([_I, _I, _I, _I, _I, _I, _L, _I], _I),
-    "attn_split_chunk": ([_I, _I], _I),
     "attn_decode_workspace_bytes": ([_I, _I, _I, _I], _Z),
     "attn_decode": ([_P, _L, _L, _P, _L, _L, _L, _P, _L, _L, _L, _P, _L, _L, _P, _I,
                      _I, _I, _I, _I, _F, _I, _P, _Z, _P], _I),
@@ -41,7 +40,7 @@ _SIGS = {
                            _I, _I, _I, _I, _I, _F, _I, _P, _Z, _P], _I),
     "attn_paged_decode_split": ([_P, _L, _L, _P, _P, _L, _L, _L, _P, _L, _P, _I,
                                  _I, _I, _I, _I, _I, _F, _I, _P, _Z, _P], _I),
-    "attn_decode_combine": ([_P, _Z, _I, _I, _I, _I, _P, _I, _P, _L, _L, _P], _I),
+    "attn_decode_combine": ([_P, _Z, _I, _I, _I, _I, _I, _L, _P, _I, _P, _L, _L, _P], _I),
     "attn_split_combine": ([_P, _P, _I, _I, _I, _P, _P, _P, _P], _I),
     "attn_prefill_plan": ([_P, _I, _I, _P, _P, _P, _I, _P], _I),
     "attn_prefill_tile_rows": ([_I, _I], _I),
@@ -114,13 +113,6 @@ def attn_plan_splits(B, Hkv, G, D, max_kv_len, page_size, kv_s_head, num_cus=0):
     return rc
 
 
-def attn_split_chunk(max_kv_len, num_splits):
-    rc = lib().attn_split_chunk(max_kv_len, num_splits)
-    if rc < 0:
-        _check(rc)
-    return rc
-
-
 def attn_decode_workspace_bytes(B, Hq, D, num_splits):
     return int(lib().attn_decode_workspace_bytes(B, Hq, D, num_splits))
 
@@ -171,12 +163,12 @@ def attn_paged_decode_split(q, k_pool, v_pool, block_table, kv_lens, max_kv_len,
         workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
-def attn_decode_combine(workspace, B, Hq, D, num_splits, kv_lens, max_kv_len, out, stream=None):
+def attn_decode_combine(workspace, B, Hq, Hkv, D, num_splits, kv_s_head, kv_lens, max_kv_len, out, stream=None):
     """Combine step of decode over a workspace filled by attn_paged_decode_split."""
     _unit_inner(out)
     _check(lib().attn_decode_combine(
-        _ptr(workspace), workspace.numel() * workspace.element_size(), int(B), int(Hq), int(D),
-        int(num_splits), _ptr(kv_lens), int(max_kv_len), _ptr(out), out.stride(0), out.stride(1),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), int(B), int(Hq), int(Hkv), int(D),
+        int(num_splits), int(kv_s_head), _ptr(kv_lens), int(max_kv_len), _ptr(out), out.stride(0), out.stride(1),
         _stream(stream)))
     return out
 

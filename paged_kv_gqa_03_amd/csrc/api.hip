@@ -47,10 +47,9 @@ int device_cus() {
     return cus;
 }
 
-constexpr int kTileTokens = 16;   // split chunks are multiples of it (the largest decode tile)
-constexpr int kMaxSplits = 256;
-constexpr int kWavesPerCuTarget = 4;   // decode waves per CU the planner aims at
-constexpr int kMinTilesPerSplit = 4;   // shortest split, in decode tiles
+constexpr int kMaxWaves = 1 << 16;     // upper bound on decode slices (num_splits)
+constexpr int kWavesPerCuTarget = 2;   // decode waves per CU the planner aims at
+constexpr int kMinSliceTokens = 64;    // shortest slice the planner makes, in tokens of a row
 
 // KV heads one decode wave covers: with the heads of a token adjacent in
 // memory (head stride == D) a wave takes up to 8 of them so each token's
@@ -63,25 +62,12 @@ int heads_per_wave(int Hkv, int64_t kv_s_head, int D) {
     return hw;
 }
 
-// Longest split (tokens) whose block-table slice fits the kernel's LDS slice:
-// a chunk of c tokens spans at most (c - 1) / ps + 2 pages.
-int max_paged_chunk(int page_size) {
+// Longest sub-piece (tokens) whose block-table slice fits the kernel's LDS
+// slice: c tokens span at most (c - 1) / ps + 2 pages.
+int max_sub_piece(int page_size) {
+    if (page_size <= 0) return 1 << 30;
     const long c = (long)(pa::kDecodeMaxSplitPages - 2) * page_size;
-    const long capped = c > (1L << 30) ? (1L << 30) : c;
-    return (int)(capped / kTileTokens * kTileTokens);
-}
-
-// page_size 0 stands for a contiguous source, which has no such limit.
-int min_paged_splits(int max_kv_len, int page_size) {
-    if (page_size <= 0) return 1;
-    const int c = max_paged_chunk(page_size);
-    return max_kv_len > 0 ? (max_kv_len + c - 1) / c : 1;
-}
-
-int chunk_for(int max_kv_len, int S) {
-    const int per = (max_kv_len + S - 1) / S;
-    const int chunk = ((per + kTileTokens - 1) / kTileTokens) * kTileTokens;
-    return chunk < kTileTokens ? kTileTokens : chunk;
+    return (int)(c > (1L << 30) ? (1L << 30) : c);
 }
 
 int check_heads(int Hq, int Hkv, int D, int *G) {
@@ -93,83 +79,80 @@ int check_heads(int Hq, int Hkv, int D, int *G) {
     return ATTN_OK;
 }
 
-size_t ws_ml_offset(int B, int Hq, int D, int S) {
-    const size_t o_bytes = (size_t)S * B * Hq * D * sizeof(float);
+// Workspace: o_part [(B + W) * Hq, D] f32, then ml_part [(B + W) * Hq, 2] f32
+// at the next 256-byte boundary.  Partial of slot s (row r + wave w), local
+// query head i of the row, sits at row s * heads_per_row + i < (B + W) * Hq.
+size_t ws_rows(int B, int Hq, int W) { return ((size_t)B + (size_t)W) * (size_t)Hq; }
+size_t ws_ml_offset(int B, int Hq, int D, int W) {
+    const size_t o_bytes = ws_rows(B, Hq, W) * D * sizeof(float);
     return (o_bytes + 255) & ~(size_t)255;
 }
 
-// Splits that can hold keys for a given requested count (always-empty
-// trailing splits are dropped) and the chunk they use.
-void effective_splits(int max_kv_len, int S, int *S_eff, int *chunk) {
-    *chunk = chunk_for(max_kv_len, S);
-    int s = max_kv_len > 0 ? (max_kv_len + *chunk - 1) / *chunk : 1;
-    *S_eff = s < 1 ? 1 : s;
-}
-
-int check_workspace(void *workspace, size_t workspace_bytes, int B, int Hq, int D, int S, bool need_any) {
-    if (!need_any && S == 1) return ATTN_OK;
-    const size_t need = attn_decode_workspace_bytes(B, Hq, D, S);
+int check_workspace(const void *workspace, size_t workspace_bytes, int B, int Hq, int D, int W) {
+    const size_t need = attn_decode_workspace_bytes(B, Hq, D, W);
     if (!workspace || workspace_bytes < need)
-        return fail(ATTN_ERR_WORKSPACE, "decode with %d splits needs %zu workspace bytes, got %zu", S, need,
+        return fail(ATTN_ERR_WORKSPACE, "decode with %d slices needs %zu workspace bytes, got %zu", W, need,
                     workspace ? workspace_bytes : (size_t)0);
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
         return fail(ATTN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
     return ATTN_OK;
 }
 
-pa::CombineParams decode_combine_params(const void *workspace, int B, int Hq, int D, int S, int chunk,
-                                        const int32_t *kv_lens, int kv_len_const, void *o, int64_t o_sb,
-                                        int64_t o_sh) {
-    pa::CombineParams c{};
+pa::DecodeCombineParams combine_params(const void *workspace, int B, int Hq, int D, int W, int HW, int Hkv,
+                                       const int32_t *kv_lens, int kv_len_const, void *o, int64_t o_sb,
+                                       int64_t o_sh, int direct_single) {
+    pa::DecodeCombineParams c{};
     c.o_part = static_cast<const float *>(workspace);
-    c.ml_part = reinterpret_cast<const float *>(static_cast<const char *>(workspace) + ws_ml_offset(B, Hq, D, S));
-    c.S = S;
-    c.R = B * Hq;
+    c.ml_part = reinterpret_cast<const float *>(static_cast<const char *>(workspace) + ws_ml_offset(B, Hq, D, W));
     c.kv_lens = kv_lens;
     c.kv_len_const = kv_len_const;
-    c.chunk = chunk;
-    c.rows_per_seq = Hq;
-    c.out_bf16 = static_cast<uint16_t *>(o);
+    c.B = B;
+    c.Hq = Hq;
+    c.ngrp = Hkv / HW;
+    c.R = B * c.ngrp;
+    c.W = W;
+    c.direct_single = direct_single;
+    c.o = static_cast<uint16_t *>(o);
     c.o_sb = o_sb;
     c.o_sh = o_sh;
     return c;
 }
 
-// Shared tail of the decode entry points: splits, workspace, launches.
-// mode 0: split (+ combine when S > 1, direct write when S == 1);
-// mode 1: split kernel only, always writing fp32 partials.
+// Shared tail of the decode entry points: partition, workspace, launches.
+// mode 0: split kernel (direct writes on) + combine;
+// mode 1: split kernel only, every piece written as an fp32 partial.
 int run_decode(pa::DecodeParams &p, int D, int G, bool paged, int max_kv_len, int num_splits,
                void *workspace, size_t workspace_bytes, int page_size, int64_t kv_s_head, hipStream_t stream,
                int mode) {
-    int S = num_splits;
-    if (S == 0) {
-        S = attn_plan_splits(p.B, p.Hkv, G, D, max_kv_len, page_size, kv_s_head, 0);
-        if (S < 0) return S;
+    int W = num_splits;
+    if (W == 0) {
+        W = attn_plan_splits(p.B, p.Hkv, G, D, max_kv_len, page_size, kv_s_head, 0);
+        if (W < 0) return W;
     }
+    if (W < 1 || W > kMaxWaves) return fail(ATTN_ERR_INVALID_ARG, "num_splits %d outside [1, %d]", W, kMaxWaves);
     p.HW = heads_per_wave(p.Hkv, kv_s_head, D);
-    if (S < 1 || S > kMaxSplits) return fail(ATTN_ERR_INVALID_ARG, "num_splits %d outside [1, %d]", S, kMaxSplits);
-    if (paged && S < min_paged_splits(max_kv_len, page_size))
-        return fail(ATTN_ERR_UNSUPPORTED,
-                    "paged decode with page_size %d needs >= %d splits for max_kv_len %d (got %d)", page_size,
-                    min_paged_splits(max_kv_len, page_size), max_kv_len, S);
-    effective_splits(max_kv_len, S, &S, &p.chunk);
-    p.S = S;
-    p.direct = (S == 1 && mode == 0) ? 1 : 0;
-    if (S == 1 && !paged) p.chunk = max_kv_len > 0 ? max_kv_len : 1;
-    p.units = p.B * (p.Hkv / p.HW) * S;
-    int rc = check_workspace(workspace, workspace_bytes, p.B, p.Hq, D, S, mode == 1);
-    if (rc) return rc;
-    if (!p.direct) {
+    p.ngrp = p.Hkv / p.HW;
+    p.R = p.B * p.ngrp;
+    p.W = W;
+    if ((int64_t)p.R * (int64_t)max_kv_len >= (1ll << 31))
+        return fail(ATTN_ERR_UNSUPPORTED, "decode: rows * max_kv_len must stay below 2^31 tokens");
+    p.max_sub = max_sub_piece(paged ? page_size : 0);
+    p.direct = mode == 0 ? 1 : 0;
+    if (mode == 1 || W > 1) {
+        const int rc = check_workspace(workspace, workspace_bytes, p.B, p.Hq, D, W);
+        if (rc) return rc;
         p.o_part = static_cast<float *>(workspace);
-        p.ml_part = reinterpret_cast<float *>(static_cast<char *>(workspace) + ws_ml_offset(p.B, p.Hq, D, S));
+        p.ml_part = reinterpret_cast<float *>(static_cast<char *>(workspace) + ws_ml_offset(p.B, p.Hq, D, W));
     }
     if (p.B == 0) return ok();
     hipError_t e = pa::launch_decode(p, D, G, paged, stream);
     if (e != hipSuccess) return launch_status(e, "decode split kernel");
-    if (mode == 0 && S > 1) {
-        pa::CombineParams c = decode_combine_params(workspace, p.B, p.Hq, D, S, p.chunk, p.kv_lens,
-                                                    p.kv_len_const, p.o, p.o_sb, p.o_sh);
-        e = pa::launch_combine(c, D, stream);
+    if (mode == 0) {
+        // Rows spanning several slices are merged; empty rows are zeroed;
+        // rows written directly are left alone.
+        pa::DecodeCombineParams c = combine_params(workspace, p.B, p.Hq, D, W, p.HW, p.Hkv, p.kv_lens,
+                                                   p.kv_len_const, p.o, p.o_sb, p.o_sh, 1);
+        e = pa::launch_decode_combine(c, D, stream);
         if (e != hipSuccess) return launch_status(e, "combine kernel");
     }
     return ok();
@@ -192,29 +175,19 @@ int attn_plan_splits(int B, int Hkv, int G, int D, int max_kv_len, int page_size
         if (num_cus <= 0) return fail(ATTN_ERR_LAUNCH, "attn_plan_splits: cannot query the device");
     }
     const int hw = heads_per_wave(Hkv, kv_s_head, D);
-    const long waves_per_split = (long)B * (Hkv / hw);
-    const long s_min = min_paged_splits(max_kv_len, page_size);
-    if (waves_per_split == 0) return (int)s_min;
-    const long tile = 2L * (8 / hw);
-    const long target = (long)num_cus * kWavesPerCuTarget;
-    long S = (target + waves_per_split - 1) / waves_per_split;
-    const long min_chunk = kMinTilesPerSplit * tile;
-    const long max_by_len = (max_kv_len + min_chunk - 1) / min_chunk;
-    if (S > max_by_len) S = max_by_len;
-    if (S > kMaxSplits) S = kMaxSplits;
-    if (S < s_min) S = s_min;
-    if (S < 1) S = 1;
-    return (int)S;
-}
-
-int attn_split_chunk(int max_kv_len, int num_splits) {
-    if (max_kv_len < 0 || num_splits < 1) return fail(ATTN_ERR_INVALID_ARG, "attn_split_chunk: bad sizes");
-    return chunk_for(max_kv_len, num_splits);
+    const long rows = (long)B * (Hkv / hw);
+    const long line = rows * (long)max_kv_len;   // upper bound on the tokens of all rows
+    long W = (line + kMinSliceTokens - 1) / kMinSliceTokens;
+    const long cap = (long)num_cus * kWavesPerCuTarget;
+    if (W > cap) W = cap;
+    if (W > kMaxWaves) W = kMaxWaves;
+    if (W < 1) W = 1;
+    return (int)W;
 }
 
 size_t attn_decode_workspace_bytes(int B, int Hq, int D, int num_splits) {
     if (B <= 0 || Hq <= 0 || D <= 0 || num_splits < 1) return 0;
-    return ws_ml_offset(B, Hq, D, num_splits) + (size_t)num_splits * B * Hq * 2 * sizeof(float);
+    return ws_ml_offset(B, Hq, D, num_splits) + ws_rows(B, Hq, num_splits) * 2 * sizeof(float);
 }
 
 int attn_decode(const void *q, int64_t q_sb, int64_t q_sh,
@@ -329,22 +302,23 @@ int attn_paged_decode_split(const void *q, int64_t q_sb, int64_t q_sh,
                              D, page_size, scale, num_splits, workspace, workspace_bytes, stream, 1);
 }
 
-int attn_decode_combine(const void *workspace, size_t workspace_bytes, int B, int Hq, int D, int num_splits,
-                        const int32_t *kv_lens, int max_kv_len, void *o, int64_t o_sb, int64_t o_sh,
-                        void *stream) {
-    if (B < 0 || Hq <= 0 || max_kv_len < 0 || num_splits < 1 || num_splits > kMaxSplits)
+int attn_decode_combine(const void *workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int D,
+                        int num_splits, int64_t kv_s_head, const int32_t *kv_lens, int max_kv_len, void *o,
+                        int64_t o_sb, int64_t o_sh, void *stream) {
+    int G = 0, rc = check_heads(Hq, Hkv, D, &G);
+    if (rc) return rc;
+    if (B < 0 || max_kv_len < 0 || num_splits < 1 || num_splits > kMaxWaves)
         return fail(ATTN_ERR_INVALID_ARG, "attn_decode_combine: bad sizes");
     if (D != 64 && D != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_combine: head dim %d not built", D);
     if (!o) return fail(ATTN_ERR_INVALID_ARG, "attn_decode_combine: null output");
     if (!aligned16(o) || !mult8(o_sb) || !mult8(o_sh))
         return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_combine: output rows must be 16-byte aligned");
-    int S = 0, chunk = 0;
-    effective_splits(max_kv_len, num_splits, &S, &chunk);
-    int rc = check_workspace(const_cast<void *>(workspace), workspace_bytes, B, Hq, D, S, true);
+    rc = check_workspace(workspace, workspace_bytes, B, Hq, D, num_splits);
     if (rc) return rc;
     if (B == 0) return ok();
-    pa::CombineParams c = decode_combine_params(workspace, B, Hq, D, S, chunk, kv_lens, max_kv_len, o, o_sb, o_sh);
-    return launch_status(pa::launch_combine(c, D, static_cast<hipStream_t>(stream)), "combine kernel");
+    pa::DecodeCombineParams c = combine_params(workspace, B, Hq, D, num_splits, heads_per_wave(Hkv, kv_s_head, D),
+                                               Hkv, kv_lens, max_kv_len, o, o_sb, o_sh, 0);
+    return launch_status(pa::launch_decode_combine(c, D, static_cast<hipStream_t>(stream)), "combine kernel");
 }
 
 int attn_split_combine(const float *o_part, const float *ml_part, int S, int R, int D,
@@ -360,12 +334,8 @@ int attn_split_combine(const float *o_part, const float *ml_part, int S, int R, 
     c.ml_part = ml_part;
     c.S = S;
     c.R = R;
-    c.chunk = 0;
-    c.rows_per_seq = 1;
     c.out_f32 = out_f32;
     c.out_bf16 = static_cast<uint16_t *>(out_bf16);
-    c.o_sb = D;
-    c.o_sh = 0;
     c.lse = lse;
     return launch_status(pa::launch_combine(c, D, static_cast<hipStream_t>(stream)), "combine kernel");
 }

@@ -1,33 +1,35 @@
 // decode.hip -- split-KV GQA decode and the log-sum-exp combine for gfx950.
 //
 // Method (AstrAI csrc commit history, the split-KV decode commit): the KV
-// range of every (sequence, KV head) is cut into splits; each split keeps a
+// range of every (sequence, KV head) is cut into pieces; each piece keeps a
 // running max, a sum of exponentials and an unnormalised weighted-V
-// accumulator, and a combine kernel merges the splits.  When one split per
-// sequence already fills the device the kernel writes the normalised output
-// directly (same commit).  The KV source is either a paged pool read through
-// the block table with a lookup per token (the commit that replaced the
-// per-tile page lookup by a per-element one) or contiguous strides.
+// accumulator, and a combine kernel merges the pieces.  A sequence that one
+// piece covers entirely is written directly, normalised (same commit's
+// single-pass direct write).  The KV source is either a paged pool read
+// through the block table with a lookup per token (the commit that replaced
+// the per-tile page lookup by a per-element one) or contiguous strides.
 //
-// Work decomposition on gfx950: a one-wave workgroup owns one split of one
-// sequence for HW adjacent KV heads (HW in {1, 2, 4, 8}), so the dispatcher
-// refills a compute unit as soon as any split finishes, whatever the ragged
-// lengths of its neighbours.  Units are ordered split-major, so the last
-// splits of long sequences run last and the tail is at most one split long.
-// The wave carries all G = Hq/Hkv query heads of each
-// of its KV heads, so K/V bytes are read once for the whole group (cf. the
-// GQA head-packing commit in the doc's history).
+// Balanced partition.  The rows r = (sequence b, group of HW adjacent KV
+// heads) are laid end to end, row r holding kv_lens[b] tokens; the whole
+// line of T tokens is cut into W equal slices and wave w takes tokens
+// [w*T/W, (w+1)*T/W).  Every wave therefore streams the same number of
+// bytes whatever the spread of lengths, and the planner keeps W near two
+// waves per compute unit (long, contiguous streams).  A wave finds its
+// slice with a wave-wide scan of kv_lens (no extra launch) and writes one
+// partial per row it touches at slot r + w: moving along the line, every
+// wave or row boundary increments w or r, so r + w names each piece
+// uniquely and a row's pieces occupy consecutive slots.
 //
 // Lane layout: lane l = 8*grp + jj, with lane group grp = tg*HW + hw: hw
-// picks the KV head, tg one of TG = 8/HW token streams, jj one of 8 chunk
-// lanes.  A tile is 2*TG tokens; per tile a lane holds tokens tg and tg+TG
-// and, for each, the 16-byte chunks jj, jj+8, ... of its head's K and V rows
-// (D/64 chunks).  HW is chosen from the layout so that one load instruction
-// reads memory that is contiguous: with the KV heads of a token adjacent
-// ([pages, slot, head, dim] pools, blhd) HW = 8 and a tile is 2 tokens of
-// whole 2 KB rows (a 16-token page is one 32 KB stream); with a head's
-// tokens adjacent ([pages, head, slot, dim], bhld) HW = 1 and a tile is 16
-// tokens of one head (4 KB contiguous).
+// picks the KV head of the row, tg one of TG = 8/HW token streams, jj one
+// of 8 chunk lanes.  A tile is 2*TG tokens; per tile a lane holds tokens tg
+// and tg+TG and, for each, the 16-byte chunks jj, jj+8, ... of its head's K
+// and V rows (D/64 chunks).  HW is chosen from the layout so that one load
+// instruction reads memory that is contiguous: with the KV heads of a token
+// adjacent ([pages, slot, head, dim] pools, blhd) HW = 8 and a tile is two
+// tokens of whole 2 KB rows (a 16-token page is one 32 KB stream); with a
+// head's tokens adjacent ([pages, head, slot, dim], bhld) HW = 1 and a tile
+// is 16 tokens of one head (4 KB contiguous).
 //   scores  v_dot2_f32_bf16 of q and K chunks, summed over the 8 chunk lanes
 //           with three DPP adds (quad_perm x2, row_half_mirror);
 //   softmax each lane group keeps its own running state; the reference max
@@ -37,13 +39,11 @@
 //   P.V     the two tokens' V rows are interleaved into bf16 pairs and
 //           accumulated with v_dot2 against the pair of bf16 weights, so
 //           each V element costs G/2 dot2 plus half a permute.
-// The TG token streams of a head are merged once per split (xor shuffles),
-// then the wave writes either the normalised bf16 output (single split,
-// direct mode) or the fp32 partial (m, l, o).
 // Loads run two tiles ahead of the math (three register stages).  The
-// split's block-table slice is copied into LDS once per wave before the loop,
-// so page lookups inside the loop are LDS reads (lgkmcnt) and never sit in
-// the in-order vmcnt queue between K/V loads.
+// piece's block-table slice is copied into LDS before its tile loop, so page
+// lookups inside the loop are LDS reads (lgkmcnt) and never sit in the
+// in-order vmcnt queue between K/V loads; pieces longer than the slice run
+// as consecutive sub-pieces.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -58,7 +58,8 @@ struct KVRegs {
     uint32_t ka[NCH][4], kb[NCH][4], va[NCH][4], vb[NCH][4];
 };
 
-// Per-lane page id and slot of the tile's two tokens (paged source only).
+// Page id and slot of the lane's two tokens of a tile (slot = position for
+// a contiguous source).
 struct TokAddr {
     int pa, sa, pb, sb;
 };
@@ -68,321 +69,418 @@ __device__ __forceinline__ void load16(const uint16_t *ptr, uint32_t (&dst)[4]) 
     dst[0] = t.x; dst[1] = t.y; dst[2] = t.z; dst[3] = t.w;
 }
 
+__device__ __forceinline__ int row_len(const DecodeParams &p, int r) {
+    return p.kv_lens ? p.kv_lens[r / p.ngrp] : p.kv_len_const;
+}
+
+// Row totals of the balanced partition: lane i sums rows [i*rpl, (i+1)*rpl);
+// `base` is the exclusive prefix of those sums across lanes.  The host keeps
+// the whole line below 2^31 tokens.
+struct RowScan {
+    int base, sum, total, rpl;
+};
+
+__device__ __forceinline__ RowScan scan_rows(const DecodeParams &p) {
+    const int lane = threadIdx.x & 63;
+    RowScan s;
+    s.rpl = (p.R + 63) / 64;
+    int sum = 0;
+    const int r0 = lane * s.rpl, r1 = min(p.R, r0 + s.rpl);
+    for (int r = r0; r < r1; ++r) sum += row_len(p, r);
+    int inc = sum;
+#pragma unroll
+    for (int k = 1; k < 64; k <<= 1) {
+        const int o = __shfl_up(inc, k);
+        if (lane >= k) inc += o;
+    }
+    s.sum = sum;
+    s.base = inc - sum;
+    s.total = __builtin_amdgcn_readfirstlane(__shfl(inc, 63));
+    return s;
+}
+
+// Wave of the partition that holds line position x (0 <= x < T).
+__device__ __forceinline__ int wave_of(int64_t x, int64_t T, int W) {
+    const int64_t w = ((x + 1) * W - 1) / T;
+    return (int)(w < W - 1 ? w : W - 1);
+}
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 template <int D, int G, int HW, bool PAGED>
-__global__ __launch_bounds__(64) void decode_split_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(64, (G >= 8 ? 1 : 2)) void decode_split_kernel(const DecodeParams p) {
     constexpr int NCH = D / 64;
     constexpr int TG = 8 / HW;          // token streams per head
     constexpr int TILE = 2 * TG;        // tokens per tile
+    constexpr int HWG = HW * G;         // query heads per row
     const int lane = threadIdx.x & 63;
-    const int u = blockIdx.x;
-    const int ngrp = p.Hkv / HW;
-    const int hgrp = u % ngrp;
-    const int bsx = u / ngrp;
-    const int b = bsx % p.B;
-    const int s = bsx / p.B;
-    const int n = p.kv_lens ? p.kv_lens[b] : p.kv_len_const;
-    const int j0 = s * p.chunk;
-    const int j1 = min(n, j0 + p.chunk);
-    if (j0 >= j1 && s > 0) return;  // past the end of this sequence: no partial
+    const int w = blockIdx.x;
     const int grp = lane >> 3, jj = lane & 7;
     const int hw = grp % HW, tg = grp / HW;
-    const int g = hgrp * HW + hw;       // this lane's KV head
-    const int last = j1 - 1;
 
-    // Query slices of the G heads of this KV head, chunks jj + 8c.
-    uint32_t qv[G][NCH][4];
-    {
-        const uint16_t *qb = p.q + b * p.q_sb + (int64_t)(g * G) * p.q_sh + jj * 8;
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-            for (int c = 0; c < NCH; ++c) load16(qb + h * p.q_sh + c * 64, qv[h][c]);
+    // This wave's slice [a, e) of the line of all rows (wave-uniform values,
+    // kept in scalar registers).
+    const RowScan rs = scan_rows(p);
+    const int T = rs.total;
+    const int a = uniform((int)((int64_t)w * T / p.W)), e = uniform((int)((int64_t)(w + 1) * T / p.W));
+    if (a >= e) return;
+    // First row that ends after a: the lane whose rows hold it, then a walk.
+    const uint64_t hit = __ballot(rs.base + rs.sum > a && rs.sum > 0);
+    const int l0 = uniform(__ffsll((unsigned long long)hit) - 1);
+    int r = l0 * rs.rpl;
+    int P = uniform(__shfl(rs.base, l0));
+    for (int n0 = uniform(row_len(p, r)); P + n0 <= a; n0 = uniform(row_len(p, r))) {
+        P += n0;
+        ++r;
     }
 
-    float o[G][NCH][8];
-    float mref[G], lsum[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        mref[h] = -INFINITY;
-        lsum[h] = 0.f;
-#pragma unroll
-        for (int c = 0; c < NCH; ++c)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) o[h][c][e] = 0.f;
-    }
-
-    const int ntiles = (j1 - j0 + TILE - 1) / TILE;
-    // Block-table slice of this split: page indices first_pg .. (j1-1)/ps.
     __shared__ int32_t pages[kDecodeMaxSplitPages];
-    int first_pg = 0;
-    if constexpr (PAGED) {
-        if (ntiles > 0) {
-            const int32_t *bt_row = p.bt + b * p.bt_sb;
-            first_pg = (int)udiv_magic((uint32_t)j0, p.ps_magic);
-            const int npg = (int)udiv_magic((uint32_t)last, p.ps_magic) - first_pg + 1;
-            for (int i = lane; i < npg; i += 64) pages[i] = bt_row[first_pg + i];
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        }
-    }
-    // Base pointers of this (sequence, KV head) and this lane's chunk.  The
-    // host guarantees every per-token offset below fits 32 bits except the
-    // page term, which is a single 32x32->64 multiply-add.
-    const uint16_t *kbase = p.k + jj * 8 + (PAGED ? g * p.s_head : b * p.k_sb + g * p.k_sh);
-    const uint16_t *vbase = p.v + jj * 8 + (PAGED ? g * p.s_head : b * p.v_sb + g * p.v_sh);
     const uint32_t s_page = (uint32_t)p.s_page, s_slot = (uint32_t)p.s_slot;
     const uint32_t k_sl = (uint32_t)p.k_sl, v_sl = (uint32_t)p.v_sl;
 
-    // Page ids (from the LDS slice) and slots of the lane's two tokens of tile t.
-    auto lookup = [&](int t) {
-        TokAddr a;
-        const int ja = min(j0 + t * TILE + tg, last);
-        const int jb = min(j0 + t * TILE + tg + TG, last);
-        if constexpr (PAGED) {
-            const uint32_t ia = udiv_magic((uint32_t)ja, p.ps_magic);
-            const uint32_t ib = udiv_magic((uint32_t)jb, p.ps_magic);
-            a.pa = pages[ia - first_pg];
-            a.pb = pages[ib - first_pg];
-            a.sa = ja - (int)(ia * p.ps);
-            a.sb = jb - (int)(ib * p.ps);
-        } else {
-            a.pa = 0; a.pb = 0; a.sa = ja; a.sb = jb;
-        }
-        return a;
-    };
-    // Issue the 16-byte K/V loads of one tile.
-    auto issue = [&](const TokAddr &a, KVRegs<NCH> &r) {
-        uint64_t oka, okb, ova, ovb;
-        if constexpr (PAGED) {
-            oka = ova = (uint64_t)(uint32_t)a.pa * s_page + (uint32_t)a.sa * s_slot;
-            okb = ovb = (uint64_t)(uint32_t)a.pb * s_page + (uint32_t)a.sb * s_slot;
-        } else {
-            oka = (uint32_t)a.sa * k_sl;
-            okb = (uint32_t)a.sb * k_sl;
-            ova = (uint32_t)a.sa * v_sl;
-            ovb = (uint32_t)a.sb * v_sl;
-        }
-        const uint16_t *kA = kbase + oka, *kB = kbase + okb;
-        const uint16_t *vA = vbase + ova, *vB = vbase + ovb;
+    for (; P < e && r < p.R; ++r) {
+        const int n = uniform(row_len(p, r));
+        const int lo = max(a, P) - P, hi = min(e, P + n) - P;
+        P += n;
+        if (lo >= hi) continue;
+        const int b = r / p.ngrp, hgrp = r % p.ngrp;
+        const int g = hgrp * HW + hw;   // this lane's KV head
+
+        // Query slices of the G heads of this KV head, chunks jj + 8c.
+        uint32_t qv[G][NCH][4];
+        {
+            const uint16_t *qb = p.q + b * p.q_sb + (int64_t)(g * G) * p.q_sh + jj * 8;
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            load16(kA + c * 64, r.ka[c]);
-            load16(kB + c * 64, r.kb[c]);
-        }
+            for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            load16(vA + c * 64, r.va[c]);
-            load16(vB + c * 64, r.vb[c]);
+                for (int c = 0; c < NCH; ++c) load16(qb + h * p.q_sh + c * 64, qv[h][c]);
         }
-    };
-    // Math of tile t on registers r.
-    auto compute = [&](int t, const KVRegs<NCH> &r) {
-        const int ja = j0 + t * TILE + tg;
-        const bool oka = ja < j1, okb = ja + TG < j1;
-        float xa[G], xb[G];
+        float o[G][NCH][8];
+        float mref[G], lsum[G];
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            float sa = 0.f, sb = 0.f;
+            mref[h] = -INFINITY;
+            lsum[h] = 0.f;
 #pragma unroll
             for (int c = 0; c < NCH; ++c)
 #pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    sa = dot2(r.ka[c][w], qv[h][c][w], sa);
-                    sb = dot2(r.kb[c][w], qv[h][c][w], sb);
+                for (int x = 0; x < 8; ++x) o[h][c][x] = 0.f;
+        }
+        // Base pointers of this (sequence, KV head) and this lane's chunk.
+        // The host guarantees every per-token offset below fits 32 bits
+        // except the page term, a single 32x32->64 multiply-add.
+        const uint16_t *kbase = p.k + jj * 8 + (PAGED ? g * p.s_head : b * p.k_sb + g * p.k_sh);
+        const uint16_t *vbase = p.v + jj * 8 + (PAGED ? g * p.s_head : b * p.v_sb + g * p.v_sh);
+
+        // Sub-pieces small enough for the LDS page slice.
+        for (int j0 = lo; j0 < hi; j0 += p.max_sub) {
+            const int j1 = min(hi, j0 + p.max_sub);
+            const int last = j1 - 1;
+            const int ntiles = (j1 - j0 + TILE - 1) / TILE;
+            int first_pg = 0;
+            if constexpr (PAGED) {
+                const int32_t *bt_row = p.bt + b * p.bt_sb;
+                first_pg = (int)udiv_magic((uint32_t)j0, p.ps_magic);
+                const int npg = (int)udiv_magic((uint32_t)last, p.ps_magic) - first_pg + 1;
+                __builtin_amdgcn_wave_barrier();   // earlier readers of the slice are done
+                for (int i = lane; i < npg; i += 64) pages[i] = bt_row[first_pg + i];
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            }
+
+            auto lookup = [&](int t) {
+                TokAddr ad;
+                const int ja = min(j0 + t * TILE + tg, last);
+                const int jb = min(j0 + t * TILE + tg + TG, last);
+                if constexpr (PAGED) {
+                    const uint32_t ia = udiv_magic((uint32_t)ja, p.ps_magic);
+                    const uint32_t ib = udiv_magic((uint32_t)jb, p.ps_magic);
+                    ad.pa = pages[ia - first_pg];
+                    ad.pb = pages[ib - first_pg];
+                    ad.sa = ja - (int)(ia * p.ps);
+                    ad.sb = jb - (int)(ib * p.ps);
+                } else {
+                    ad.pa = 0; ad.pb = 0; ad.sa = ja; ad.sb = jb;
                 }
-            sa = sum8(sa);
-            sb = sum8(sb);
-            xa[h] = oka ? sa * p.sl2 : -INFINITY;
-            xb[h] = okb ? sb * p.sl2 : -INFINITY;
-        }
-        bool need = false;
-        float mt[G];
+                return ad;
+            };
+            auto issue = [&](const TokAddr &ad, KVRegs<NCH> &rg) {
+                uint64_t oka, okb, ova, ovb;
+                if constexpr (PAGED) {
+                    oka = ova = (uint64_t)(uint32_t)ad.pa * s_page + (uint32_t)ad.sa * s_slot;
+                    okb = ovb = (uint64_t)(uint32_t)ad.pb * s_page + (uint32_t)ad.sb * s_slot;
+                } else {
+                    oka = (uint32_t)ad.sa * k_sl;
+                    okb = (uint32_t)ad.sb * k_sl;
+                    ova = (uint32_t)ad.sa * v_sl;
+                    ovb = (uint32_t)ad.sb * v_sl;
+                }
+                const uint16_t *kA = kbase + oka, *kB = kbase + okb;
+                const uint16_t *vA = vbase + ova, *vB = vbase + ovb;
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            mt[h] = fmaxf(xa[h], xb[h]);
-            need |= mt[h] > mref[h] + kRescaleTh;
-        }
-        if (need) {
+                for (int c = 0; c < NCH; ++c) {
+                    load16(kA + c * 64, rg.ka[c]);
+                    load16(kB + c * 64, rg.kb[c]);
+                }
 #pragma unroll
-            for (int h = 0; h < G; ++h) {
-                if (mt[h] > mref[h] + kRescaleTh) {
-                    const float alpha = exp2_fast(mref[h] - mt[h]);
-                    lsum[h] *= alpha;
+                for (int c = 0; c < NCH; ++c) {
+                    load16(vA + c * 64, rg.va[c]);
+                    load16(vB + c * 64, rg.vb[c]);
+                }
+            };
+            auto compute = [&](int t, const KVRegs<NCH> &rg) {
+                const int ja = j0 + t * TILE + tg;
+                const bool oka = ja < j1, okb = ja + TG < j1;
+                float xa[G], xb[G];
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    float sa = 0.f, sb = 0.f;
 #pragma unroll
                     for (int c = 0; c < NCH; ++c)
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) o[h][c][e] *= alpha;
-                    mref[h] = mt[h];
+                        for (int q = 0; q < 4; ++q) {
+                            sa = dot2(rg.ka[c][q], qv[h][c][q], sa);
+                            sb = dot2(rg.kb[c][q], qv[h][c][q], sb);
+                        }
+                    sa = sum8(sa);
+                    sb = sum8(sb);
+                    xa[h] = oka ? sa * p.sl2 : -INFINITY;
+                    xb[h] = okb ? sb * p.sl2 : -INFINITY;
                 }
-            }
-        }
-        uint32_t pp[G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const float mu = fmaxf(mref[h], -3.0e38f);
-            pp[h] = pack_bf16(exp2_fast(xa[h] - mu), exp2_fast(xb[h] - mu));
-            lsum[h] += bf16_lo(pp[h]) + bf16_hi(pp[h]);
-        }
-#pragma unroll
-        for (int c = 0; c < NCH; ++c)
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const uint32_t A = r.va[c][w], Bv = r.vb[c][w];
-                const uint32_t lo = (A & 0xffffu) | (Bv << 16);
-                const uint32_t hi = (A >> 16) | (Bv & 0xffff0000u);
+                bool need = false;
+                float mt[G];
 #pragma unroll
                 for (int h = 0; h < G; ++h) {
-                    o[h][c][2 * w] = dot2(lo, pp[h], o[h][c][2 * w]);
-                    o[h][c][2 * w + 1] = dot2(hi, pp[h], o[h][c][2 * w + 1]);
+                    mt[h] = fmaxf(xa[h], xb[h]);
+                    need |= mt[h] > mref[h] + kRescaleTh;
                 }
+                if (need) {
+#pragma unroll
+                    for (int h = 0; h < G; ++h) {
+                        if (mt[h] > mref[h] + kRescaleTh) {
+                            const float alpha = exp2_fast(mref[h] - mt[h]);
+                            lsum[h] *= alpha;
+#pragma unroll
+                            for (int c = 0; c < NCH; ++c)
+#pragma unroll
+                                for (int x = 0; x < 8; ++x) o[h][c][x] *= alpha;
+                            mref[h] = mt[h];
+                        }
+                    }
+                }
+                uint32_t pp[G];
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    const float mu = fmaxf(mref[h], -3.0e38f);
+                    pp[h] = pack_bf16(exp2_fast(xa[h] - mu), exp2_fast(xb[h] - mu));
+                    lsum[h] += bf16_lo(pp[h]) + bf16_hi(pp[h]);
+                }
+#pragma unroll
+                for (int c = 0; c < NCH; ++c)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const uint32_t A = rg.va[c][q], Bv = rg.vb[c][q];
+                        const uint32_t lo2 = (A & 0xffffu) | (Bv << 16);
+                        const uint32_t hi2 = (A >> 16) | (Bv & 0xffff0000u);
+#pragma unroll
+                        for (int h = 0; h < G; ++h) {
+                            o[h][c][2 * q] = dot2(lo2, pp[h], o[h][c][2 * q]);
+                            o[h][c][2 * q + 1] = dot2(hi2, pp[h], o[h][c][2 * q + 1]);
+                        }
+                    }
+            };
+
+            // Three register stages: while tile t is computed, tiles t+1 and
+            // t+2 are in flight.  The loop has a single exit at the bottom,
+            // so the compiler's wait-count pass keeps both tiles outstanding
+            // across the back edge.  Page lookups sit right before their
+            // loads and are never carried across iterations; past the last
+            // tile the loads repeat the last tile (in bounds, never used).
+            const int tl = ntiles - 1;
+            KVRegs<NCH> r0, r1, r2;
+            issue(lookup(0), r0);
+            issue(lookup(min(1, tl)), r1);
+            int t = 0;
+            for (; t + 2 < ntiles; t += 3) {
+                issue(lookup(t + 2), r2);
+                compute(t, r0);
+                issue(lookup(min(t + 3, tl)), r0);
+                compute(t + 1, r1);
+                issue(lookup(min(t + 4, tl)), r1);
+                compute(t + 2, r2);
             }
-    };
-
-    // The page lookup of a tile sits right before its loads: page ids are
-    // never carried across iterations.  Past the last tile the loads repeat
-    // the last tile (always in bounds, never used).
-    // Three register stages: while tile t is computed, tiles t+1 and t+2 are
-    // in flight.  The loop has a single exit at the bottom, so the compiler's
-    // wait-count pass keeps both tiles outstanding across the back edge.
-    if (ntiles > 0) {
-        const int tl = ntiles - 1;
-        KVRegs<NCH> r0, r1, r2;
-        issue(lookup(0), r0);
-        issue(lookup(min(1, tl)), r1);
-        int t = 0;
-        for (; t + 2 < ntiles; t += 3) {
-            issue(lookup(t + 2), r2);
-            compute(t, r0);
-            issue(lookup(min(t + 3, tl)), r0);
-            compute(t + 1, r1);
-            issue(lookup(min(t + 4, tl)), r1);
-            compute(t + 2, r2);
+            if (t < ntiles) compute(t, r0);
+            if (t + 1 < ntiles) compute(t + 1, r1);
         }
-        if (t < ntiles) compute(t, r0);
-        if (t + 1 < ntiles) compute(t + 1, r1);
-    }
 
-    // Merge the TG token streams of each head (lanes equal in hw and jj,
-    // i.e. lane ids differing in the bits above 8*HW).
-    if constexpr (TG > 1) {
+        // Merge the TG token streams of each head (lanes equal in hw and jj,
+        // i.e. lane ids differing in the bits above 8*HW).
+        if constexpr (TG > 1) {
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                float M = mref[h];
+#pragma unroll
+                for (int m = 8 * HW; m < 64; m <<= 1) M = fmaxf(M, __shfl_xor(M, m));
+                const float f = (mref[h] == -INFINITY) ? 0.f : exp2_fast(mref[h] - M);
+                float l = lsum[h] * f;
+#pragma unroll
+                for (int m = 8 * HW; m < 64; m <<= 1) l += __shfl_xor(l, m);
+                lsum[h] = l;
+                mref[h] = M;
+#pragma unroll
+                for (int c = 0; c < NCH; ++c)
+#pragma unroll
+                    for (int x = 0; x < 8; ++x) {
+                        float v = o[h][c][x] * f;
+#pragma unroll
+                        for (int m = 8 * HW; m < 64; m <<= 1) v += __shfl_xor(v, m);
+                        o[h][c][x] = v;
+                    }
+            }
+        }
+
+        // Every token stream now holds the head's totals; stream tg writes the
+        // query heads h with h % TG == tg.  A piece covering the whole row is
+        // the row's only piece: written normalised when direct writes are on.
+        const bool direct = p.direct && lo == 0 && hi == n;
+        const int64_t slot = (int64_t)r + w;
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            float M = mref[h];
+            if (h % TG != tg) continue;
+            const int hq = g * G + h;
+            if (direct) {
+                const float inv = lsum[h] > 0.f ? 1.f / lsum[h] : 0.f;
+                uint16_t *dst = p.o + b * p.o_sb + hq * p.o_sh + jj * 8;
 #pragma unroll
-            for (int m = 8 * HW; m < 64; m <<= 1) M = fmaxf(M, __shfl_xor(M, m));
-            const float f = (mref[h] == -INFINITY) ? 0.f : exp2_fast(mref[h] - M);
-            float l = lsum[h] * f;
-#pragma unroll
-            for (int m = 8 * HW; m < 64; m <<= 1) l += __shfl_xor(l, m);
-            lsum[h] = l;
-            mref[h] = M;
-#pragma unroll
-            for (int c = 0; c < NCH; ++c)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    float x = o[h][c][e] * f;
-#pragma unroll
-                    for (int m = 8 * HW; m < 64; m <<= 1) x += __shfl_xor(x, m);
-                    o[h][c][e] = x;
+                for (int c = 0; c < NCH; ++c) {
+                    uint4 v;
+                    v.x = pack_bf16(o[h][c][0] * inv, o[h][c][1] * inv);
+                    v.y = pack_bf16(o[h][c][2] * inv, o[h][c][3] * inv);
+                    v.z = pack_bf16(o[h][c][4] * inv, o[h][c][5] * inv);
+                    v.w = pack_bf16(o[h][c][6] * inv, o[h][c][7] * inv);
+                    *reinterpret_cast<uint4 *>(dst + c * 64) = v;
                 }
-        }
-    }
-
-    // After the merge every token stream holds the head's totals; stream tg
-    // writes the query heads h with h % TG == tg.
+            } else {
+                const int64_t prow = slot * HWG + hw * G + h;
+                float *dst = p.o_part + prow * D + jj * 8;
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-        if (h % TG != tg) continue;
-        const int hq = g * G + h;
-        if (p.direct) {
-            const float inv = lsum[h] > 0.f ? 1.f / lsum[h] : 0.f;
-            uint16_t *dst = p.o + b * p.o_sb + hq * p.o_sh + jj * 8;
-#pragma unroll
-            for (int c = 0; c < NCH; ++c) {
-                uint4 w;
-                w.x = pack_bf16(o[h][c][0] * inv, o[h][c][1] * inv);
-                w.y = pack_bf16(o[h][c][2] * inv, o[h][c][3] * inv);
-                w.z = pack_bf16(o[h][c][4] * inv, o[h][c][5] * inv);
-                w.w = pack_bf16(o[h][c][6] * inv, o[h][c][7] * inv);
-                *reinterpret_cast<uint4 *>(dst + c * 64) = w;
+                for (int c = 0; c < NCH; ++c) {
+                    *reinterpret_cast<float4 *>(dst + c * 64) =
+                        make_float4(o[h][c][0], o[h][c][1], o[h][c][2], o[h][c][3]);
+                    *reinterpret_cast<float4 *>(dst + c * 64 + 4) =
+                        make_float4(o[h][c][4], o[h][c][5], o[h][c][6], o[h][c][7]);
+                }
+                if (jj == 0)
+                    *reinterpret_cast<float2 *>(p.ml_part + prow * 2) = make_float2(mref[h] * kLn2, lsum[h]);
             }
-        } else {
-            const size_t row = ((size_t)s * p.B + b) * p.Hq + hq;
-            float *dst = p.o_part + row * D + jj * 8;
-#pragma unroll
-            for (int c = 0; c < NCH; ++c) {
-                *reinterpret_cast<float4 *>(dst + c * 64) =
-                    make_float4(o[h][c][0], o[h][c][1], o[h][c][2], o[h][c][3]);
-                *reinterpret_cast<float4 *>(dst + c * 64 + 4) =
-                    make_float4(o[h][c][4], o[h][c][5], o[h][c][6], o[h][c][7]);
-            }
-            if (jj == 0)
-                *reinterpret_cast<float2 *>(p.ml_part + row * 2) = make_float2(mref[h] * kLn2, lsum[h]);
         }
     }
 }
 
-// One wave per output row: M = max_s m_s, w_s = exp(m_s - M),
-// out = sum_s w_s o_s / sum_s w_s l_s.
+// Log-sum-exp merge of S partials at rows first + s*stride:
+// M = max_s m_s, w_s = exp(m_s - M), out = sum_s w_s o_s / sum_s w_s l_s.
+template <int D>
+__device__ __forceinline__ void merge_partials(const float *o_part, const float *ml_part, int64_t first,
+                                               int64_t stride, int S, int lane, float (&acc)[D / 64], float &L,
+                                               float &M) {
+    constexpr int NC = D / 64;
+    M = -INFINITY;
+    for (int s = lane; s < S; s += 64) M = fmaxf(M, ml_part[(first + s * stride) * 2]);
+#pragma unroll
+    for (int k = 1; k < 64; k <<= 1) M = fmaxf(M, __shfl_xor(M, k));
+#pragma unroll
+    for (int c = 0; c < NC; ++c) acc[c] = 0.f;
+    L = 0.f;
+    if (M == -INFINITY) return;
+    // Eight partials per step, all loads issued before the math.
+    constexpr int U = 8;
+    for (int s0 = 0; s0 < S; s0 += U) {
+        float2 ml[U];
+        float ov[U][NC];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int64_t row = first + (int64_t)min(s0 + k, S - 1) * stride;
+            ml[k] = *reinterpret_cast<const float2 *>(ml_part + row * 2);
+            const float *op = o_part + row * D + lane * NC;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) ov[k][c] = op[c];
+        }
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const bool use = (s0 + k < S) && ml[k].x != -INFINITY;
+            const float wgt = use ? exp2_fast((ml[k].x - M) * kLog2e) : 0.f;
+            L = fmaf(wgt, use ? ml[k].y : 0.f, L);
+#pragma unroll
+            for (int c = 0; c < NC; ++c) acc[c] = fmaf(wgt, use ? ov[k][c] : 0.f, acc[c]);
+        }
+    }
+}
+
+// Combine of the balanced decode partition: one wave per (sequence, query
+// head), four to a workgroup.  A row's pieces are the slots r + w for the
+// waves w that hold its first and last token.
+template <int D>
+__global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeCombineParams p) {
+    constexpr int NC = D / 64;
+    const int lane = threadIdx.x & 63;
+    const int item = blockIdx.x * 4 + wave_id();
+    if (item >= p.B * p.Hq) return;
+    const int b = item / p.Hq, hq = item - b * p.Hq;
+    const int n = p.kv_lens ? p.kv_lens[b] : p.kv_len_const;
+    uint16_t *dst = p.o + (int64_t)b * p.o_sb + (int64_t)hq * p.o_sh + lane * NC;
+    if (n == 0) {   // no keys: the row is zero
+        if constexpr (NC == 2) *reinterpret_cast<uint32_t *>(dst) = 0u;
+        else dst[0] = 0;
+        return;
+    }
+    const int hwg = p.Hq / p.ngrp;                 // query heads per row
+    const int r = b * p.ngrp + hq / hwg;           // this head's row
+    // Start of row r on the line, and the line's total.
+    const int rpl = (p.R + 63) / 64;
+    int64_t sum = 0, before = 0;
+    for (int rr = lane * rpl; rr < min(p.R, (lane + 1) * rpl); ++rr) {
+        const int nr = p.kv_lens ? p.kv_lens[rr / p.ngrp] : p.kv_len_const;
+        sum += nr;
+        if (rr < r) before += nr;
+    }
+#pragma unroll
+    for (int k = 1; k < 64; k <<= 1) {
+        sum += __shfl_xor(sum, k);
+        before += __shfl_xor(before, k);
+    }
+    const int w0 = wave_of(before, sum, p.W), w1 = wave_of(before + n - 1, sum, p.W);
+    if (w0 == w1 && p.direct_single) return;   // written directly by the split kernel
+    float acc[NC], L, M;
+    merge_partials<D>(p.o_part, p.ml_part, ((int64_t)r + w0) * hwg + hq % hwg, hwg, w1 - w0 + 1, lane, acc, L, M);
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    if constexpr (NC == 2) {
+        *reinterpret_cast<uint32_t *>(dst) = pack_bf16(acc[0] * inv, acc[1] * inv);
+    } else {
+        dst[0] = (uint16_t)(pack_bf16(acc[0] * inv, 0.f) & 0xffffu);
+    }
+}
+
+// Generic combine: every row r merges partials s = 0..S-1 at rows s*R + r.
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(const CombineParams p) {
     constexpr int NC = D / 64;
     const int lane = threadIdx.x & 63;
     const int r = blockIdx.x * 4 + wave_id();
     if (r >= p.R) return;
-    int S = p.S;
-    if (p.chunk > 0) {
-        const int seq = r / p.rows_per_seq;
-        const int n = p.kv_lens ? p.kv_lens[seq] : p.kv_len_const;
-        S = min(S, max(1, (n + p.chunk - 1) / p.chunk));
-    }
-    float M = -INFINITY;
-    for (int s = lane; s < S; s += 64) M = fmaxf(M, p.ml_part[((size_t)s * p.R + r) * 2]);
-#pragma unroll
-    for (int k = 1; k < 64; k <<= 1) M = fmaxf(M, __shfl_xor(M, k));
-    float acc[NC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) acc[c] = 0.f;
-    float L = 0.f;
-    if (M != -INFINITY) {
-        // Eight splits per step, all loads issued before the math.
-        constexpr int U = 8;
-        const size_t rstride = (size_t)p.R;
-        for (int s0 = 0; s0 < S; s0 += U) {
-            float2 ml[U];
-            float ov[U][NC];
-#pragma unroll
-            for (int k = 0; k < U; ++k) {
-                const int sk = min(s0 + k, S - 1);
-                ml[k] = *reinterpret_cast<const float2 *>(p.ml_part + ((size_t)sk * rstride + r) * 2);
-                const float *op = p.o_part + ((size_t)sk * rstride + r) * D + lane * NC;
-#pragma unroll
-                for (int c = 0; c < NC; ++c) ov[k][c] = op[c];
-            }
-#pragma unroll
-            for (int k = 0; k < U; ++k) {
-                const bool use = (s0 + k < S) && ml[k].x != -INFINITY;
-                const float w = use ? exp2_fast((ml[k].x - M) * kLog2e) : 0.f;
-                L = fmaf(w, use ? ml[k].y : 0.f, L);
-#pragma unroll
-                for (int c = 0; c < NC; ++c) acc[c] = fmaf(w, use ? ov[k][c] : 0.f, acc[c]);
-            }
-        }
-    }
+    float acc[NC], L, M;
+    merge_partials<D>(p.o_part, p.ml_part, r, p.R, p.S, lane, acc, L, M);
     const float inv = L > 0.f ? 1.f / L : 0.f;
     if (p.out_f32) {
 #pragma unroll
         for (int c = 0; c < NC; ++c) p.out_f32[(size_t)r * D + lane * NC + c] = acc[c] * inv;
     }
     if (p.out_bf16) {
-        uint16_t *dst = p.out_bf16 + (int64_t)(r / p.rows_per_seq) * p.o_sb +
-                        (int64_t)(r % p.rows_per_seq) * p.o_sh + lane * NC;
+        uint16_t *dst = p.out_bf16 + (size_t)r * D + lane * NC;
         if constexpr (NC == 2) {
             *reinterpret_cast<uint32_t *>(dst) = pack_bf16(acc[0] * inv, acc[1] * inv);
         } else {
-            const uint32_t w = pack_bf16(acc[0] * inv, 0.f);
-            dst[0] = (uint16_t)(w & 0xffffu);
+            dst[0] = (uint16_t)(pack_bf16(acc[0] * inv, 0.f) & 0xffffu);
         }
     }
     if (p.lse && lane == 0) p.lse[r] = (L > 0.f) ? M + __logf(L) : -INFINITY;
@@ -390,7 +488,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineParams p) {
 
 template <int D, int G, int HW, bool PAGED>
 hipError_t launch_decode_t(const DecodeParams &p, hipStream_t stream) {
-    hipLaunchKernelGGL((decode_split_kernel<D, G, HW, PAGED>), dim3(p.units), dim3(64), 0, stream, p);
+    hipLaunchKernelGGL((decode_split_kernel<D, G, HW, PAGED>), dim3(p.W), dim3(64), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -419,10 +517,20 @@ hipError_t launch_decode_hw(const DecodeParams &p, int G, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_decode(const DecodeParams &p, int D, int G, bool paged, hipStream_t stream) {
-    if (p.units <= 0) return hipSuccess;
+    if (p.W <= 0 || p.R <= 0) return hipSuccess;
     if (D == 64) return paged ? launch_decode_hw<64, true>(p, G, stream) : launch_decode_hw<64, false>(p, G, stream);
     if (D == 128) return paged ? launch_decode_hw<128, true>(p, G, stream) : launch_decode_hw<128, false>(p, G, stream);
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_combine(const DecodeCombineParams &p, int D, hipStream_t stream) {
+    const int rows = p.B * p.Hq;
+    if (rows <= 0) return hipSuccess;
+    const int blocks = (rows + 3) / 4;
+    if (D == 64) hipLaunchKernelGGL((decode_combine_kernel<64>), dim3(blocks), dim3(256), 0, stream, p);
+    else if (D == 128) hipLaunchKernelGGL((decode_combine_kernel<128>), dim3(blocks), dim3(256), 0, stream, p);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
 }
 
 hipError_t launch_combine(const CombineParams &p, int D, hipStream_t stream) {

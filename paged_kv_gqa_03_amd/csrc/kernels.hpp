@@ -6,11 +6,13 @@
 
 namespace pa {
 
-// Most block-table entries one decode split may span; the host keeps
-// chunk / page_size + 1 within it (one LDS slice per wave).
+// Most block-table entries one decode sub-piece may span; the host caps a
+// sub-piece at (kDecodeMaxSplitPages - 2) * page_size tokens.
 constexpr int kDecodeMaxSplitPages = 512;
 
-// Split-KV decode over one KV source (paged pool or contiguous strides).
+// Split-KV decode over one KV source (paged pool or contiguous strides),
+// balanced partition: rows r = (sequence, group of HW KV heads) laid end to
+// end, W equal slices of the line, partial of row r in wave w at slot r + w.
 struct DecodeParams {
     const uint16_t *q;
     int64_t q_sb, q_sh;
@@ -27,31 +29,37 @@ struct DecodeParams {
     int kv_len_const;
     uint16_t *o;
     int64_t o_sb, o_sh;
-    float *o_part;   // [S, B, Hq, D]     (S > 1)
-    float *ml_part;  // [S, B, Hq, 2]     (S > 1)
-    int B, Hq, Hkv, S, chunk;
-    int direct;      // 1: single split writes the normalised bf16 output
-    int HW;          // KV heads per wave (1, 2, 4, 8; divides Hkv)
-    int units;       // B * (Hkv / HW) * S
+    float *o_part;   // [(B + W) * Hq, D]   partial of slot s, local head i at row s*HW*G + i
+    float *ml_part;  // [(B + W) * Hq, 2]
+    int B, Hq, Hkv;
+    int HW;          // KV heads per row (1, 2, 4, 8; divides Hkv)
+    int ngrp;        // Hkv / HW
+    int R;           // B * ngrp rows
+    int W;           // waves (slices of the line)
+    int max_sub;     // longest sub-piece (tokens) one LDS page slice covers
+    int direct;      // 1: a row covered by one piece is written normalised
     float sl2;       // scale * log2(e)
 };
 
+// Combine of the balanced partition (one wave per sequence x query head).
+struct DecodeCombineParams {
+    const float *o_part, *ml_part;
+    const int32_t *kv_lens;
+    int kv_len_const;
+    int B, Hq, ngrp, R, W;
+    int direct_single;   // 1: single-piece rows were written by the split kernel
+    uint16_t *o;
+    int64_t o_sb, o_sh;
+};
+
+// Generic combine: row r merges partials s*R + r, s = 0..S-1.
 struct CombineParams {
     const float *o_part;   // [S, R, D]
     const float *ml_part;  // [S, R, 2]
     int S, R;
-    // Optional per-row split count: rows r of sequence r / rows_per_seq use
-    // max(1, ceil(kv_lens[seq] / chunk)) splits (capped at S).
-    const int32_t *kv_lens;
-    int kv_len_const;      // used when kv_lens == NULL and chunk > 0
-    int chunk;             // 0: every row uses all S partials
-    int rows_per_seq;
-    // Outputs (any may be NULL).  Row r of the bf16 output sits at
-    // out_bf16 + (r / rows_per_seq) * o_sb + (r % rows_per_seq) * o_sh.
-    float *out_f32;
-    uint16_t *out_bf16;
-    int64_t o_sb, o_sh;
-    float *lse;
+    float *out_f32;        // NULL or [R, D]
+    uint16_t *out_bf16;    // NULL or [R, D]
+    float *lse;            // NULL or [R]
 };
 
 // Ragged paged prefill (work-map tiles x groups of packed query heads).
@@ -101,6 +109,7 @@ struct SwaParams {
 hipError_t launch_decode(const DecodeParams &p, int D, int G, bool paged, hipStream_t stream);
 hipError_t launch_swa(const SwaParams &p, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream);
+hipError_t launch_decode_combine(const DecodeCombineParams &p, int D, hipStream_t stream);
 hipError_t launch_combine(const CombineParams &p, int D, hipStream_t stream);
 
 }  // namespace pa

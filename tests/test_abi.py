@@ -43,46 +43,29 @@ def test_version():
 
 @pytest.mark.parametrize("B,Hkv,max_len", [(2, 2, 300), (16, 8, 2048), (32, 8, 4096), (128, 8, 4096),
                                            (1, 1, 100000), (512, 8, 4096), (4, 8, 16), (3, 1, 0)])
-def test_planner_bounds(B, Hkv, max_len):
-    for s_head, tile in ((128, 2 * (8 // min(8, Hkv))), (16 * 128, 16)):
-        S = pa.attn_plan_splits(B, Hkv, 4, 128, max_len, 16, s_head, 256)
-        assert 1 <= S <= 256
-        if max_len > 4 * tile:
-            chunk = pa.attn_split_chunk(max_len, S)
-            assert chunk % 16 == 0 and (chunk >= 4 * tile or S == 1)
-        # a larger batch never asks for more splits
-        assert pa.attn_plan_splits(2 * B, Hkv, 4, 128, max_len, 16, s_head, 256) <= S or max_len <= 16
+@pytest.mark.parametrize("s_head", [128, 16 * 128])
+def test_planner_bounds(B, Hkv, max_len, s_head):
+    W = pa.attn_plan_splits(B, Hkv, 4, 128, max_len, 16, s_head, 256)
+    assert 1 <= W <= 256 * 2
+    hw = min(8, Hkv) if s_head == 128 else 1
+    rows = B * (Hkv // hw)
+    # no slice shorter than 64 tokens of a row, given the longest possible line
+    assert W == 1 or rows * max_len >= 64 * (W - 1)
+    # a larger batch never asks for fewer slices
+    assert pa.attn_plan_splits(2 * B, Hkv, 4, 128, max_len, 16, s_head, 256) >= W
 
 
-def test_planner_fills_the_device_for_small_batches():
-    # one KV head per wave (head stride != D): 16 * 8 * S waves
-    S = pa.attn_plan_splits(16, 8, 4, 128, 2048, 16, 16 * 128, 256)
-    assert 16 * 8 * S >= 256 * 4
-    # eight adjacent heads per wave: 16 * S waves
-    S8 = pa.attn_plan_splits(16, 8, 4, 128, 2048, 16, 128, 256)
-    assert 16 * S8 >= 256 * 4 and S8 == 8 * S
-
-
-def test_planner_respects_page_slice_limit():
-    # page_size 1 and a 4096-token sequence need at least ceil(4096 / 496) splits
-    S = pa.attn_plan_splits(512, 8, 4, 128, 4096, 1, 128, 256)
-    assert S >= 9
-    assert pa.attn_split_chunk(4096, S) <= 496
-
-
-def test_split_chunk_covers_the_range():
-    for L in (1, 15, 16, 17, 300, 2048, 4095):
-        for S in (1, 2, 3, 7, 64):
-            c = pa.attn_split_chunk(L, S)
-            assert c % 16 == 0 and c * S >= L and c >= 16
+def test_planner_targets_two_waves_per_cu():
+    assert pa.attn_plan_splits(128, 8, 4, 128, 4096, 16, 128, 256) == 512
+    assert pa.attn_plan_splits(32, 8, 4, 128, 4096, 16, 128, 304) == 608
+    assert pa.attn_plan_splits(2, 2, 4, 64, 300, 16, 64, 256) == 10   # 600 tokens / 64
 
 
 def test_workspace_bytes_layout():
     assert pa.attn_decode_workspace_bytes(0, 32, 128, 4) == 0
-    assert pa.attn_decode_workspace_bytes(32, 32, 128, 1) == 32 * 32 * 128 * 4 + 32 * 32 * 2 * 4
-    n = pa.attn_decode_workspace_bytes(32, 32, 128, 4)
-    o_bytes = 4 * 32 * 32 * 128 * 4
-    assert n == ((o_bytes + 255) // 256) * 256 + 4 * 32 * 32 * 2 * 4
+    n = pa.attn_decode_workspace_bytes(32, 32, 128, 100)
+    rows = (32 + 100) * 32
+    assert n == ((rows * 128 * 4 + 255) // 256) * 256 + rows * 2 * 4
 
 
 def test_work_map_matches_worked_example():
@@ -146,11 +129,11 @@ def call_paged(a):
     (dict(ps=0), pa.ATTN_ERR_INVALID_ARG, "page_size"),
     (dict(B=-1), pa.ATTN_ERR_INVALID_ARG, "negative"),
     (dict(scale=float("nan")), pa.ATTN_ERR_INVALID_ARG, "scale"),
-    (dict(S=300), pa.ATTN_ERR_INVALID_ARG, "num_splits"),
+    (dict(S=1 << 20), pa.ATTN_ERR_INVALID_ARG, "num_splits"),
     (dict(S=4), pa.ATTN_ERR_WORKSPACE, "workspace"),
     (dict(S=4, ws=FAKE + 16, ws_bytes=1 << 30), pa.ATTN_ERR_INVALID_ARG, "aligned"),
-    (dict(ps=1, max_len=5000, S=1), pa.ATTN_ERR_UNSUPPORTED, "splits"),
     (dict(ps=1 << 20, max_len=1 << 13), pa.ATTN_ERR_UNSUPPORTED, "2^32"),
+    (dict(B=1 << 20, max_len=1 << 12, q_sb=256), pa.ATTN_ERR_UNSUPPORTED, "2^31"),
 ])
 def test_paged_decode_rejects_bad_arguments(over, code, word):
     rc = call_paged(paged_args(**over))

@@ -63,8 +63,6 @@ def test_tiny_paged_decode(S):
 def test_paged_decode_shapes(G, D, ps, lens, S):
     Hkv = 2
     case = workloads.paged_decode_case(100 + G * 7 + D + ps, len(lens), Hkv * G, Hkv, D, lens, ps)
-    if S == 1 and case["max_kv_len"] > 496 * ps:
-        S = 0
     ref, _ = oracle_paged(case)
     assert_close(run_paged(case, S), ref, what="G=%d D=%d ps=%d S=%d" % (G, D, ps, S))
 
@@ -147,26 +145,55 @@ def test_repeat_runs_are_bit_identical():
     assert torch.equal(a, b)
 
 
-def test_combine_of_decode_partials_matches_oracle_combine():
-    """Equal lengths, so every split is non-empty; the fp32 partials the
-    split kernel leaves in the workspace are combined on the GPU and by the
-    oracle in fp64."""
-    B, Hq, D, L, S = 4, 32, 128, 1000, 5
-    case = workloads.paged_decode_case(14, B, Hq, 8, D, [L] * B, 16)
-    ws = torch.empty(pa.attn_decode_workspace_bytes(B, Hq, D, S), dtype=torch.uint8, device=DEV)
-    run_paged(case, S, workspace=ws)
-    o_bytes = S * B * Hq * D * 4
+def partition_pieces(lens, rows_per_seq, W):
+    """Slots of each row's pieces under the balanced partition: rows laid end
+    to end, W equal slices of the line, piece of row r in slice w at r + w."""
+    n_rows = [n for n in lens for _ in range(rows_per_seq)]
+    T = sum(n_rows)
+    bounds = [w * T // W for w in range(W + 1)]
+    out, P = [], 0
+    for r, n in enumerate(n_rows):
+        ws = [w for w in range(W) if n > 0 and bounds[w] < P + n and bounds[w + 1] > P]
+        out.append([r + w for w in ws])
+        P += n
+    return out
+
+
+@pytest.mark.parametrize("lens", [[1000] * 4, [5, 700, 1, 1500]])
+def test_combine_of_decode_partials_matches_oracle_combine(lens):
+    """The fp32 partials the split kernel leaves in the workspace (located by
+    the documented slot rule) are combined on the GPU and by the oracle in
+    fp64; the partials are also a valid split of the exact result."""
+    B, Hq, Hkv, D, W = len(lens), 32, 8, 128, 9
+    case = workloads.paged_decode_case(14, B, Hq, Hkv, D, lens, 16)
+    d = to_dev(case, ["q", "k_pool", "v_pool", "block_table", "kv_lens"])
+    nbytes = pa.attn_decode_workspace_bytes(B, Hq, D, W)
+    ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device=DEV)
+    pa.attn_paged_decode_split(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["kv_lens"],
+                               case["max_kv_len"], 16, case["scale"], W, ws)
+    torch.cuda.synchronize()
+    rows_total = (B + W) * Hq
+    o_bytes = rows_total * D * 4
     ml_off = (o_bytes + 255) // 256 * 256
-    o_part = ws[:o_bytes].view(torch.float32).view(S, B * Hq, D)
-    ml_part = ws[ml_off:ml_off + S * B * Hq * 8].view(torch.float32).view(S, B * Hq, 2)
+    o_all = ws[:o_bytes].view(torch.float32).view(rows_total, D).cpu()
+    ml_all = ws[ml_off:ml_off + rows_total * 8].view(torch.float32).view(rows_total, 2).cpu()
+    pieces = partition_pieces(lens, 1, W)       # 8 adjacent heads per row: one row per sequence
+    S = max(len(p) for p in pieces)
+    o_part = torch.zeros(S, B * Hq, D)
+    ml_part = torch.zeros(S, B * Hq, 2)
+    ml_part[..., 0] = float("-inf")
+    for b, slots in enumerate(pieces):
+        for s_i, slot in enumerate(slots):
+            for h in range(Hq):
+                o_part[s_i, b * Hq + h] = o_all[slot * Hq + h]
+                ml_part[s_i, b * Hq + h] = ml_all[slot * Hq + h]
     out = torch.empty(B * Hq, D, dtype=torch.float32, device=DEV)
     lse = torch.empty(B * Hq, dtype=torch.float32, device=DEV)
-    pa.attn_split_combine(o_part, ml_part, out_f32=out, lse=lse)
+    pa.attn_split_combine(o_part.to(DEV).contiguous(), ml_part.to(DEV).contiguous(), out_f32=out, lse=lse)
     torch.cuda.synchronize()
-    ref, ref_lse = oracle.combine_f32(o_part.cpu(), ml_part.cpu())
+    ref, ref_lse = oracle.combine_f32(o_part, ml_part)
     assert_close(out, ref, atol=1e-5, rtol=1e-5, what="combine")
     assert_close(lse, ref_lse, atol=1e-5, rtol=1e-5, what="lse")
-    # and the partials themselves are a valid split of the exact result
     full, full_lse = oracle_paged(case)
     assert_close(out.view(B, Hq, D), full, atol=1e-2, rtol=1e-2)
     assert_close(lse.view(B, Hq), full_lse, atol=1e-2, rtol=1e-2)
@@ -200,7 +227,7 @@ def test_combine_random_partials_with_empty_splits(D):
     assert bool(torch.isneginf(lse.cpu()[~fin]).all())
 
 
-@pytest.mark.parametrize("S", [1, 6])
+@pytest.mark.parametrize("S", [1, 6, 40])
 def test_split_then_combine_equals_fused_call(S):
     case = workloads.paged_decode_case(15, 6, 32, 8, 128, [5, 300, 1200, 0, 77, 2000], 16)
     d = to_dev(case, ["q", "k_pool", "v_pool", "block_table", "kv_lens"])
@@ -209,7 +236,7 @@ def test_split_then_combine_equals_fused_call(S):
     pa.attn_paged_decode_split(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["kv_lens"],
                                case["max_kv_len"], 16, case["scale"], S, ws)
     out = torch.empty_like(d["q"])
-    pa.attn_decode_combine(ws, 6, 32, 128, S, d["kv_lens"], case["max_kv_len"], out)
+    pa.attn_decode_combine(ws, 6, 32, 8, 128, S, d["k_pool"].stride(2), d["kv_lens"], case["max_kv_len"], out)
     torch.cuda.synchronize()
     assert torch.equal(fused, out)
 
