@@ -123,7 +123,7 @@ __global__ __launch_bounds__(64, (G >= 8 ? 1 : 2)) void decode_split_kernel(cons
     const RowScan rs = scan_rows(p);
     const int T = rs.total;
     const int a = uniform((int)((int64_t)w * T / p.W)), e = uniform((int)((int64_t)(w + 1) * T / p.W));
-    if (a >= e) return;
+    if (a >= T) return;   // an empty slice at the end of the line
     // First row that ends after a: the lane whose rows hold it, then a walk.
     const uint64_t hit = __ballot(rs.base + rs.sum > a && rs.sum > 0);
     const int l0 = uniform(__ffsll((unsigned long long)hit) - 1);
@@ -132,6 +132,17 @@ __global__ __launch_bounds__(64, (G >= 8 ? 1 : 2)) void decode_split_kernel(cons
     for (int n0 = uniform(row_len(p, r)); P + n0 <= a; n0 = uniform(row_len(p, r))) {
         P += n0;
         ++r;
+    }
+    if (a >= e) {
+        // Empty slices exist only when W exceeds the keys of all rows.  One
+        // whose position lies strictly inside row r sits inside that row's
+        // run of slots r + w, which the combine merges whole: mark the slot
+        // empty (m = -inf, l = 0; the combine then ignores its o).
+        if (P < a)
+            for (int i = lane; i < HWG; i += 64)
+                *reinterpret_cast<float2 *>(p.ml_part + ((int64_t)(r + w) * HWG + i) * 2) =
+                    make_float2(-INFINITY, 0.f);
+        return;
     }
 
     __shared__ int32_t pages[kDecodeMaxSplitPages];

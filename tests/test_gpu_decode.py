@@ -252,3 +252,37 @@ def test_paged_decode_heads_per_wave(Hkv, G, layout, S):
     case = workloads.paged_decode_case(200 + Hkv + G, 3, Hkv * G, Hkv, 128, [1, 250, 700], 16, layout=layout)
     ref, _ = oracle_paged(case)
     assert_close(run_paged(case, S), ref, what="Hkv=%d G=%d %s S=%d" % (Hkv, G, layout, S))
+
+
+def nan_workspace(B, Hq, D, S):
+    n = max(256, pa.attn_decode_workspace_bytes(B, Hq, D, S))
+    return torch.full((n,), 0xFF, dtype=torch.uint8, device=DEV)   # all-ones bytes are NaNs
+
+
+@pytest.mark.parametrize("Hkv,layout", [(8, "page_slot_head"), (2, "page_head_slot")])
+def test_partition_every_slice_count(Hkv, layout):
+    """Every slice count from 1 to past the total key count, so slices that
+    hold nothing (inside a row and at the ends) are covered, on a batch with
+    empty and one-token sequences; the workspace starts as NaN."""
+    lens = [0, 9, 1, 0, 23, 2, 0]
+    G, D = 4, 64
+    case = workloads.paged_decode_case(260 + Hkv, len(lens), Hkv * G, Hkv, D, lens, 4, layout=layout)
+    ref, _ = oracle_paged(case)
+    groups = 1 if layout == "page_slot_head" else Hkv     # KV-head groups per sequence
+    T = sum(lens) * groups
+    for S in list(range(1, T + 8)):
+        got = run_paged(case, S, workspace=nan_workspace(len(lens), Hkv * G, D, S))
+        assert_close(got, ref, what="S=%d of T=%d" % (S, T))
+
+
+def test_planner_on_mostly_empty_batch():
+    """128 sequences of which one holds keys: the planner's slice count
+    (sized from max_kv_len) exceeds the keys, so most slices are empty."""
+    lens = [0] * 128
+    lens[77] = 100
+    case = workloads.paged_decode_case(270, 128, 32, 8, 128, lens, 16)
+    S = pa.attn_plan_splits(128, 8, 4, 128, 100, 16, case["k_pool"].stride(2))
+    assert S > 100
+    ref, _ = oracle_paged(case)
+    got = run_paged(case, 0, workspace=nan_workspace(128, 32, 128, S))
+    assert_close(got, ref, what="planner S=%d" % S)
