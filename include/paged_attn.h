@@ -202,7 +202,8 @@ int attn_prefill_plan(const int32_t *q_lens_host, int B, int tile_rows,
 
 /* Query rows per tile that attn_paged_prefill expects in its work map for
  * head dim D and group size G = Hq / Hkv: a workgroup packs min(G, 4) query
- * heads that share a KV head, and a tile holds 64 / min(G, 4) rows. */
+ * heads that share a KV head, and a tile holds 128 / min(G, 4) rows (32 per
+ * wave of the workgroup). */
 int attn_prefill_tile_rows(int D, int G);
 
 /*

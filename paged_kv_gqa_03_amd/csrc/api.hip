@@ -366,7 +366,7 @@ int attn_prefill_tile_rows(int D, int G) {
     if (D != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill_tile_rows: head dim %d not built (128)", D);
     if (G != 1 && G != 2 && G != 4 && G != 8)
         return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill_tile_rows: group size %d not built (1, 2, 4, 8)", G);
-    return 64 / pa::prefill_heads_packed(G);
+    return 128 / pa::prefill_heads_packed(G);
 }
 
 int attn_paged_prefill(const void *q, int64_t q_st, int64_t q_sh, const int32_t *qo_indptr,

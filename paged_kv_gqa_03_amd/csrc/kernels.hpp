@@ -86,7 +86,7 @@ struct PrefillParams {
 };
 
 // Query heads one prefill workgroup packs (they share a KV head); a work-map
-// tile then has 64 / prefill_heads_packed(G) rows.
+// tile then has 128 / prefill_heads_packed(G) rows (32 per wave).
 int prefill_heads_packed(int G);
 
 // fp8 sliding-window decode (K = V), head dim 512, 16-head groups.

@@ -9,22 +9,32 @@
 // an optional keep-mask, using an online softmax over KV tiles.
 //
 // Work decomposition: one 256-thread workgroup per (work-map tile, group of
-// HP query heads sharing one KV head).  Wave w handles 16 query rows of one
-// head; the HP heads of a workgroup read every K/V tile once from LDS.  A
-// tile has 64/HP rows (HP = min(G, 4)).
+// HP query heads sharing one KV head).  Wave w handles 32 query rows (two
+// 16-row MFMA blocks) of one head; the HP heads of a workgroup read every
+// K/V tile once from LDS.  A tile has 32 * 4 / HP rows (HP = min(G, 4)).
 //
 // Per KV tile of 64 keys the workgroup stages K row-major and V transposed
 // (d-major, keys permuted) in LDS; the transpose is done in registers while
-// staging.  Each wave then runs, with v_mfma_f32_16x16x32_bf16,
+// staging.  Each wave then runs, with v_mfma_f32_16x16x32_bf16, per row block
 //   S^T (64 keys x 16 rows) = K (64 x 128) . Q^T (128 x 16)     16 MFMA
 //   O^T (128 x 16)        += V^T (128 x 64) . P^T (64 x 16)     16 MFMA
-// In this transposed form lane l always holds query row l % 16: its scores
-// are 16 keys of that row (keys 4*(l/16) + i of each 16-key block), so the
-// row max / sum need only two cross-lane steps, the softmax rescale of O is
-// a per-lane scalar, and P^T feeds the second MFMA straight from registers
-// (V^T is stored with the matching key order).  Scores are scaled in fp32
-// after the dot product (csrc commit that moved the scale after Q.K^T).
-// Keys past the causal frontier of the tile are never loaded.
+// and every K or V^T operand read from LDS feeds both row blocks.  In this
+// transposed form lane l always holds query row l % 16 of a block: its
+// scores are 16 keys of that row (keys 4*(l/16) + i of each 16-key block), so
+// the row max / sum need only two cross-lane steps, the softmax rescale of O
+// is a per-lane scalar, and P^T feeds the second MFMA straight from
+// registers (V^T is stored with the matching key order).  Scores are scaled
+// in fp32 after the dot product (csrc commit that moved the scale after
+// Q.K^T).  Keys past the causal frontier of the tile are never loaded.
+//
+// Pipeline: two LDS buffers and one register stage.  While tile t is
+// computed from one buffer, tile t+1's loads (issued a whole tile earlier)
+// land and are stored into the other, and tile t+2's loads are issued; one
+// barrier per tile.  Page ids come from a slice of the block table staged in
+// LDS, so no global load sits between a tile's address math and its K/V
+// loads, and the keep-mask words of a tile travel with its stage.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -35,9 +45,10 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int BK = 64;         // keys per KV tile
-constexpr int KLD = 128 + 8;   // K tile row stride in LDS (elements): 272 B, conflict-free 16 B reads
-constexpr int VLD = BK + 8;    // V^T row stride in LDS (elements): 144 B
+constexpr int BK = 64;           // keys per KV tile
+constexpr int KLD = 128 + 8;     // K tile row stride in LDS (elements): 272 B, conflict-free 16 B reads
+constexpr int VLD = BK + 8;      // V^T row stride in LDS (elements): 144 B
+constexpr int kPages = 512;      // block-table entries staged in LDS at a time
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
@@ -59,34 +70,110 @@ struct Stage {
 };
 
 struct StageCtx {
-    int cc, kg, kv_end;
-    const int32_t *bt_row;
+    int cc, kg;
+    int first_pg, c1;               // page slice start; keys of this chunk end at c1
+    const int32_t *pages;           // LDS page slice
     const uint16_t *kbase, *vbase;
 };
 
 __device__ __forceinline__ uint64_t key_off(const PrefillParams &p, const StageCtx &sc, int key) {
-    const int kc = min(key, sc.kv_end - 1);
+    const int kc = min(key, sc.c1 - 1);   // keys past the chunk end repeat its last key
     const uint32_t pi = udiv_magic((uint32_t)kc, p.ps_magic);
-    const int page = sc.bt_row[pi];
+    const int page = sc.pages[pi - sc.first_pg];
     const uint32_t slot = (uint32_t)kc - pi * p.ps;
     return (uint64_t)(uint32_t)page * (uint32_t)p.s_page + slot * (uint32_t)p.s_slot;
 }
 
 __device__ __forceinline__ uint4 ld16(const uint16_t *ptr) { return *reinterpret_cast<const uint4 *>(ptr); }
 
+// The thread's share of tile kt: keys 4kg .. 4kg+3, chunk cc, of K and of V
+// (the pools share strides, so the four offsets serve both).  When the page
+// size is a multiple of 4 the four keys sit in one page: one lookup, then
+// slot steps.  Keys past the chunk end repeat its last key.
 __device__ __forceinline__ void load_stage(const PrefillParams &p, const StageCtx &sc, int kt, Stage &r) {
-    const int kv0 = kt * BK;
-    r.k0 = ld16(sc.kbase + key_off(p, sc, kv0 + sc.kg));
-    r.k1 = ld16(sc.kbase + key_off(p, sc, kv0 + sc.kg + 16));
-    r.k2 = ld16(sc.kbase + key_off(p, sc, kv0 + sc.kg + 32));
-    r.k3 = ld16(sc.kbase + key_off(p, sc, kv0 + sc.kg + 48));
-    r.v0 = ld16(sc.vbase + key_off(p, sc, kv0 + 4 * sc.kg));
-    r.v1 = ld16(sc.vbase + key_off(p, sc, kv0 + 4 * sc.kg + 1));
-    r.v2 = ld16(sc.vbase + key_off(p, sc, kv0 + 4 * sc.kg + 2));
-    r.v3 = ld16(sc.vbase + key_off(p, sc, kv0 + 4 * sc.kg + 3));
+    const int k0 = min(kt * BK + 4 * sc.kg, sc.c1 - 1);
+    uint64_t off[4];
+    if ((p.ps & 3u) == 0) {
+        const int rmax = sc.c1 - 1 - k0;
+        off[0] = key_off(p, sc, k0);
+#pragma unroll
+        for (int i = 1; i < 4; ++i) off[i] = off[0] + (uint32_t)min(i, rmax) * (uint32_t)p.s_slot;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) off[i] = key_off(p, sc, k0 + i);
+    }
+    r.k0 = ld16(sc.kbase + off[0]);
+    r.k1 = ld16(sc.kbase + off[1]);
+    r.k2 = ld16(sc.kbase + off[2]);
+    r.k3 = ld16(sc.kbase + off[3]);
+    r.v0 = ld16(sc.vbase + off[0]);
+    r.v1 = ld16(sc.vbase + off[1]);
+    r.v2 = ld16(sc.vbase + off[2]);
+    r.v3 = ld16(sc.vbase + off[3]);
 }
 
-// One 32-bit column pair of the 4 x 8 V block: dims (2j, 2j+1) of 4 keys.
+// Keep-mask of one tile, staged like K and V: thread t loads bytes
+// 8(t & 7) .. +8 of mask rows (t >> 3) + 32 q (q < NQ) of the tile's 64 keys,
+// and stores them as 8 bits, so LDS holds 64 bits per mask row.  A 3-D mask
+// has one row per query row of the work-map tile, a 2-D mask one row.
+template <int MASK, int NQ>
+struct MaskStage {
+    uint32_t w[NQ][2];
+};
+
+struct MaskCtx {
+    const uint8_t *base;   // mask row of the tile's first query row (2-D: the sequence's row)
+    int64_t m_sq;
+    int rows;              // mask rows that exist (3-D: query rows of the tile)
+};
+
+// Bytes [j, j + 8) of mask row `row`; bytes at or past key n read as 0 and
+// are never touched, nor are rows past `rows`.
+template <int MASK, int NQ>
+__device__ __forceinline__ void load_mask(const MaskCtx &mc, int tid, int n, int kt, MaskStage<MASK, NQ> &m) {
+    const int j = kt * BK + 8 * (tid & 7);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const int row = (tid >> 3) + 32 * q;
+        m.w[q][0] = m.w[q][1] = 0u;
+        if (row < mc.rows) {
+            const uint8_t *mp = mc.base + row * mc.m_sq + j;
+            if (j + 8 <= n) {
+                m.w[q][0] = *reinterpret_cast<const uint32_t *>(mp);
+                m.w[q][1] = *reinterpret_cast<const uint32_t *>(mp + 4);
+            } else {
+                for (int i = 0; i < 8 && j + i < n; ++i) m.w[q][i >> 2] |= (uint32_t)mp[i] << (8 * (i & 3));
+            }
+        }
+    }
+}
+
+// Four mask bytes -> four bits (bit i set iff byte i is nonzero).
+__device__ __forceinline__ uint32_t nz_bits4(uint32_t w) {
+    w |= w >> 4;
+    w |= w >> 2;
+    w |= w >> 1;
+    return ((w & 0x01010101u) * 0x01020408u) >> 24;
+}
+
+template <int MASK, int NQ>
+__device__ __forceinline__ void store_mask(const MaskStage<MASK, NQ> &m, int tid, uint8_t *bits) {
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const int row = (tid >> 3) + 32 * q;
+        if (MASK == 3 || row == 0)
+            bits[row * 8 + (tid & 7)] = (uint8_t)(nz_bits4(m.w[q][0]) | (nz_bits4(m.w[q][1]) << 4));
+    }
+}
+
+// Column of V^T row d where the 8-key group `grp` is stored: groups are
+// XOR-swizzled by the row's 16-row block, which spreads the staging stores
+// (16 lanes writing rows 8 apart) over the banks, while an operand read
+// (one 16-row block, whole 8-key groups) stays a contiguous 16 bytes.
+__device__ __forceinline__ int v_col(int d, int grp) { return 8 * (grp ^ ((d >> 4) & 7)); }
+
+// One 32-bit column pair of the 4 x 8 V block: dims (2j, 2j+1) of 4 keys
+// at permuted position ph (a multiple of 4).
 __device__ __forceinline__ void store_v_pair(uint16_t *v_lds, int d, int ph, uint32_t a, uint32_t b, uint32_t c,
                                              uint32_t e) {
     uint2 lo, hi;
@@ -94,15 +181,16 @@ __device__ __forceinline__ void store_v_pair(uint16_t *v_lds, int d, int ph, uin
     lo.y = (c & 0xffffu) | (e << 16);
     hi.x = (a >> 16) | (b & 0xffff0000u);
     hi.y = (c >> 16) | (e & 0xffff0000u);
-    *reinterpret_cast<uint2 *>(&v_lds[d * VLD + ph]) = lo;
-    *reinterpret_cast<uint2 *>(&v_lds[(d + 1) * VLD + ph]) = hi;
+    const int col = v_col(d, ph >> 3) + (ph & 7);   // d and d + 1 share a 16-row block
+    *reinterpret_cast<uint2 *>(&v_lds[d * VLD + col]) = lo;
+    *reinterpret_cast<uint2 *>(&v_lds[(d + 1) * VLD + col]) = hi;
 }
 
 __device__ __forceinline__ void store_stage(const StageCtx &sc, const Stage &r, uint16_t *k_lds, uint16_t *v_lds) {
-    *reinterpret_cast<uint4 *>(&k_lds[(sc.kg + 0) * KLD + sc.cc * 8]) = r.k0;
-    *reinterpret_cast<uint4 *>(&k_lds[(sc.kg + 16) * KLD + sc.cc * 8]) = r.k1;
-    *reinterpret_cast<uint4 *>(&k_lds[(sc.kg + 32) * KLD + sc.cc * 8]) = r.k2;
-    *reinterpret_cast<uint4 *>(&k_lds[(sc.kg + 48) * KLD + sc.cc * 8]) = r.k3;
+    *reinterpret_cast<uint4 *>(&k_lds[(4 * sc.kg + 0) * KLD + sc.cc * 8]) = r.k0;
+    *reinterpret_cast<uint4 *>(&k_lds[(4 * sc.kg + 1) * KLD + sc.cc * 8]) = r.k1;
+    *reinterpret_cast<uint4 *>(&k_lds[(4 * sc.kg + 2) * KLD + sc.cc * 8]) = r.k2;
+    *reinterpret_cast<uint4 *>(&k_lds[(4 * sc.kg + 3) * KLD + sc.cc * 8]) = r.k3;
     // 4 keys x 8 dims -> 8 dims x 4 keys
     const int ph = v_phys(4 * sc.kg), d0 = sc.cc * 8;
     store_v_pair(v_lds, d0 + 0, ph, r.v0.x, r.v1.x, r.v2.x, r.v3.x);
@@ -112,11 +200,15 @@ __device__ __forceinline__ void store_stage(const StageCtx &sc, const Stage &r, 
 }
 
 template <int HP, int MASK>
-__global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
-    constexpr int RB = 4 / HP;   // 16-row blocks per workgroup
-    constexpr int R = 16 * RB;   // rows per work-map tile
-    __shared__ __attribute__((aligned(16))) uint16_t k_lds[BK * KLD];
-    __shared__ __attribute__((aligned(16))) uint16_t v_lds[128 * VLD];
+__global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) {
+    constexpr int WPH = 4 / HP;   // waves (32-row groups) per head
+    constexpr int R = 32 * WPH;   // rows per work-map tile
+    __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][BK * KLD];
+    __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][128 * VLD];
+    __shared__ int32_t pages[kPages];
+    constexpr int MROWS = MASK == 3 ? R : 1;                  // mask rows per tile
+    constexpr int NQ = MASK == 3 ? R / 32 : 1;                // mask rows per thread
+    __shared__ __attribute__((aligned(8))) uint8_t mbits[2][MROWS * 8];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int tile = blockIdx.x;
@@ -129,138 +221,236 @@ __global__ __launch_bounds__(256) void prefill_kernel(const PrefillParams p) {
     const int n = p.kv_lens[b];
     const int c = p.causal ? p.causal[b] : -1;
     const int row0 = ti * R;
-    const int myrow = row0 + (w / HP) * 16 + (lane & 15);  // local query row of this lane
-    const int lq = lane >> 4;                               // lane group 0..3
-    const bool row_ok = myrow < qn;
+    const int lq = lane >> 4;   // lane group 0..3
+    int myrow[2];
+    bool row_ok[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        myrow[rb] = row0 + (w / HP) * 32 + 16 * rb + (lane & 15);   // local query row of this lane
+        row_ok[rb] = myrow[rb] < qn;
+    }
 
     // Keys the tile can see: all of the sequence, or up to its causal frontier.
     const int last_row = min(qn, row0 + R) - 1;
     const int kv_end = (c >= 0) ? min(n, c + last_row + 1) : n;
     const int n_kt = (kv_end + BK - 1) / BK;
 
-    // Q^T operand: row myrow, d = 32s + 8*lq .. +8.
-    bf16x8_t qf[4];
-    {
-        const uint16_t *qr = p.q + (int64_t)(q0 + min(myrow, qn - 1)) * p.q_st + (int64_t)hq * p.q_sh + 8 * lq;
+    // Q^T operands: row myrow[rb], d = 32s + 8*lq .. +8.  A negative scale
+    // is applied as |scale| on negated Q (a sign flip, exact), so the row
+    // maximum can be taken on the unscaled scores.
+    // (A zero scale is taken as a tiny positive one: masked scores then stay
+    // -inf instead of 0 * -inf, and every admitted key weighs 2^0.)
+    const float sl2 = fmaxf(fabsf(p.sl2), 1e-30f);
+    const uint32_t qsign = p.sl2 < 0.f ? 0x80008000u : 0u;
+    bf16x8_t qf[2][4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) qf[s] = as_bf16x8(*reinterpret_cast<const uint4 *>(qr + 32 * s));
+    for (int rb = 0; rb < 2; ++rb) {
+        const uint16_t *qr =
+            p.q + (int64_t)(q0 + min(myrow[rb], qn - 1)) * p.q_st + (int64_t)hq * p.q_sh + 8 * lq;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            uint4 v = *reinterpret_cast<const uint4 *>(qr + 32 * s);
+            v.x ^= qsign; v.y ^= qsign; v.z ^= qsign; v.w ^= qsign;
+            qf[rb][s] = as_bf16x8(v);
+        }
     }
 
-    f32x4_t oacc[8];
+    // O^T accumulators, and row sums of P from an MFMA against a ones
+    // operand (every entry of lacc[rb] holds the lane's row sum).
+    f32x4_t oacc[2][8], lacc[2];
 #pragma unroll
-    for (int m = 0; m < 8; ++m) oacc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m_i = -INFINITY, l_i = 0.f;
+    for (int rb = 0; rb < 2; ++rb) {
+        lacc[rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < 8; ++m) oacc[rb][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    const bf16x8_t ones = as_bf16x8(make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
+    // Softmax reference per row (scaled, log2 units), raised lazily: only
+    // when a score exceeds it by more than 2^8, so P stays <= 256 and the
+    // rescale of O is mostly skipped.
+    float m_ref[2] = {-INFINITY, -INFINITY};
+    const int wrow0 = row0 + (w / HP) * 32;   // first row of this wave
 
-    // Staging assignment: K rows kk = (tid >> 4) + 16 i, chunk cc = tid & 15;
-    // V keys 4*(tid >> 4) + r, same chunk.
+    // Staging assignment: keys 4*(tid >> 4) + r (r = 0..3) of K and of V,
+    // chunk cc = tid & 15.
     StageCtx sc;
     sc.cc = tid & 15;
     sc.kg = tid >> 4;
-    sc.bt_row = p.bt + b * p.bt_sb;
+    sc.pages = pages;
     sc.kbase = p.k + (int64_t)g * p.s_head + sc.cc * 8;
     sc.vbase = p.v + (int64_t)g * p.s_head + sc.cc * 8;
-    sc.kv_end = kv_end;
+    const int32_t *bt_row = p.bt + b * p.bt_sb;
     Stage st_regs;
 
-    const int64_t mrow = MASK == 3 ? (int64_t)b * p.m_sb + (int64_t)myrow * p.m_sq : (int64_t)b * p.m_sb;
-    if (n_kt > 0) load_stage(p, sc, 0, st_regs);
-    for (int kt = 0; kt < n_kt; ++kt) {
-        __syncthreads();   // every wave is done reading the previous tile
-        store_stage(sc, st_regs, k_lds, v_lds);
-        __syncthreads();
-        // Next tile's loads are in flight during the math (the last
-        // iteration reloads its own tile: in bounds, never stored).
-        load_stage(p, sc, min(kt + 1, n_kt - 1), st_regs);
-        const int kv0 = kt * BK;
+    MaskCtx mc;
+    mc.base = p.mask + (int64_t)b * p.m_sb + (MASK == 3 ? (int64_t)row0 * p.m_sq : 0);
+    mc.m_sq = p.m_sq;
+    mc.rows = MASK == 3 ? min(R, qn - row0) : 1;
+    MaskStage<MASK, NQ> mst;
+    // Mask row (within the tile) of each of this lane's two query rows.
+    int mloc[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) mloc[rb] = MASK == 3 ? (w / HP) * 32 + 16 * rb + (lane & 15) : 0;
 
-        // S^T blocks: keys 16kb + 4lq + i of the tile, row myrow.
-        f32x4_t st[4];
+    // Keys row myrow[rb] admits: j < lim[rb] (length and causal frontier);
+    // the wave's first row has the smallest limit.
+    int lim[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) lim[rb] = c < 0 ? n : min(n, c + myrow[rb] + 1);
+    const int lim_wave = c < 0 ? n : min(n, c + wrow0 + 1);
+
+    // One tile of math from LDS buffer `buf`.  FULL: every key of the tile is
+    // admitted by every row of the wave (the common case), so the per-key
+    // length and causal tests are skipped.
+    auto tile_math = [&](auto full_c, int kt, int buf) {
+        constexpr bool FULL = decltype(full_c)::value;
+        const uint16_t *kl = k_lds[buf];
+        const uint16_t *vl = v_lds[buf];
+        // S^T blocks: keys 16kb + 4lq + i of the tile, rows myrow[rb].
+        f32x4_t st[2][4];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-            st[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            st[0][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            st[1][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const bf16x8_t a = as_bf16x8(
-                    *reinterpret_cast<const uint4 *>(&k_lds[(16 * kb + (lane & 15)) * KLD + 32 * s + 8 * lq]));
-                st[kb] = mfma16(a, qf[s], st[kb]);
+                    *reinterpret_cast<const uint4 *>(&kl[(16 * kb + (lane & 15)) * KLD + 32 * s + 8 * lq]));
+                st[0][kb] = mfma16(a, qf[0][s], st[0][kb]);
+                st[1][kb] = mfma16(a, qf[1][s], st[1][kb]);
             }
         }
-        // Scale, causal frontier, keep-mask.
-        float x[4][4];
-        float mt = -INFINITY;
+        // Scores of keys not admitted become -inf (then P = 0).
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            const int j0 = kv0 + 16 * kb + 4 * lq;
-            uint32_t keep4 = 0x01010101u;
-            if constexpr (MASK != 0) {
-                keep4 = 0;
-                if (row_ok) {
-                    const uint8_t *mp = p.mask + mrow + j0;
-                    if (j0 + 4 <= n) {
-                        keep4 = *reinterpret_cast<const uint32_t *>(mp);
-                    } else {
+        for (int rb = 0; rb < 2; ++rb) {
+            const int room = lim[rb] - (kt * BK + 4 * lq);   // admitted iff 16kb + i < room
+            uint2 kbits = make_uint2(~0u, ~0u);               // keys 0..31, 32..63 of the tile
+            if constexpr (MASK != 0) kbits = *reinterpret_cast<const uint2 *>(&mbits[buf][mloc[rb] * 8]);
+            kbits.x >>= 4 * lq;
+            kbits.y >>= 4 * lq;
 #pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            if (j0 + i < n) keep4 |= (uint32_t)mp[i] << (8 * i);
-                    }
+            for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    bool ok = true;
+                    if constexpr (!FULL) ok = 16 * kb + i < room;
+                    if constexpr (MASK != 0) ok = ok && (((kb < 2 ? kbits.x : kbits.y) >> (16 * (kb & 1) + i)) & 1u);
+                    if constexpr (!FULL || MASK != 0) st[rb][kb][i] = ok ? st[rb][kb][i] : -INFINITY;
                 }
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int j = j0 + i;
-                const bool ok = j < n && (c < 0 || j <= c + myrow) && ((keep4 >> (8 * i)) & 0xffu);
-                x[kb][i] = ok ? st[kb][i] * p.sl2 : -INFINITY;
-                mt = fmaxf(mt, x[kb][i]);
             }
         }
-        mt = fmaxf(mt, __shfl_xor(mt, 16));
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
-        const float m_new = fmaxf(m_i, mt);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = exp2_fast(m_i - m_use);   // 0 while m_i is -inf
-        m_i = m_new;
-        uint32_t pw[2][4];
-        float psum = 0.f;
+        // Row maxima of the unscaled scores, then the lazy reference.
+        float mts[2];
+        bool raise[2];
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
+        for (int rb = 0; rb < 2; ++rb) {
+            float mt = -INFINITY;
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int kb = 2 * s2 + h;
+            for (int kb = 0; kb < 4; ++kb)
+                mt = fmaxf(fmaxf(mt, fmaxf(st[rb][kb][0], st[rb][kb][1])), fmaxf(st[rb][kb][2], st[rb][kb][3]));
+            mt = fmaxf(mt, __shfl_xor(mt, 16));
+            mt = fmaxf(mt, __shfl_xor(mt, 32));
+            mts[rb] = mt * sl2;
+            raise[rb] = mts[rb] > m_ref[rb] + 8.f;   // false for an all-masked tile
+        }
+        if (__builtin_amdgcn_ballot_w64(raise[0] || raise[1])) {
 #pragma unroll
-                for (int i = 0; i < 4; i += 2) {
-                    const uint32_t pk = pack_bf16(exp2_fast(x[kb][i] - m_use), exp2_fast(x[kb][i + 1] - m_use));
-                    psum += bf16_lo(pk) + bf16_hi(pk);
-                    pw[s2][2 * h + i / 2] = pk;
-                }
+            for (int rb = 0; rb < 2; ++rb) {
+                const float alpha = raise[rb] ? exp2_fast(m_ref[rb] - mts[rb]) : 1.f;   // 0 from -inf
+                m_ref[rb] = raise[rb] ? mts[rb] : m_ref[rb];
+                lacc[rb] *= alpha;
+#pragma unroll
+                for (int m = 0; m < 8; ++m) oacc[rb][m] *= alpha;
             }
-        l_i = l_i * alpha + psum;
+        }
+        // P = 2^(s * scale * log2 e - reference), rounded to bf16 pairs.
+        uint32_t pw[2][2][4];
 #pragma unroll
-        for (int m = 0; m < 8; ++m) oacc[m] *= alpha;
-        // O^T += V^T . P^T
+        for (int rb = 0; rb < 2; ++rb) {
+            const float neg_ref = m_ref[rb] == -INFINITY ? 0.f : -m_ref[rb];
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int kb = 2 * s2 + h;
+#pragma unroll
+                    for (int i = 0; i < 4; i += 2)
+                        pw[rb][s2][2 * h + i / 2] = pack_bf16(exp2_fast(fmaf(st[rb][kb][i], sl2, neg_ref)),
+                                                              exp2_fast(fmaf(st[rb][kb][i + 1], sl2, neg_ref)));
+                }
+        }
+        // O^T += V^T . P^T, and the row sums.
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-            const bf16x8_t pb = as_bf16x8(make_uint4(pw[s2][0], pw[s2][1], pw[s2][2], pw[s2][3]));
+            const bf16x8_t pb0 = as_bf16x8(make_uint4(pw[0][s2][0], pw[0][s2][1], pw[0][s2][2], pw[0][s2][3]));
+            const bf16x8_t pb1 = as_bf16x8(make_uint4(pw[1][s2][0], pw[1][s2][1], pw[1][s2][2], pw[1][s2][3]));
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
-                const bf16x8_t a = as_bf16x8(
-                    *reinterpret_cast<const uint4 *>(&v_lds[(16 * m + (lane & 15)) * VLD + 32 * s2 + 8 * lq]));
-                oacc[m] = mfma16(a, pb, oacc[m]);
+                const bf16x8_t a = as_bf16x8(*reinterpret_cast<const uint4 *>(
+                    &vl[(16 * m + (lane & 15)) * VLD + v_col(16 * m, 4 * s2 + lq)]));
+                oacc[0][m] = mfma16(a, pb0, oacc[0][m]);
+                oacc[1][m] = mfma16(a, pb1, oacc[1][m]);
             }
+            lacc[0] = mfma16(ones, pb0, lacc[0]);
+            lacc[1] = mfma16(ones, pb1, lacc[1]);
+        }
+    };
+    auto compute = [&](int kt, int buf) {
+        if (kt * BK + BK <= lim_wave) tile_math(std::true_type{}, kt, buf);
+        else tile_math(std::false_type{}, kt, buf);
+    };
+
+    // Keys in chunks whose pages fit the LDS slice; chunks start on tile
+    // boundaries, so no tile straddles two.
+    const int64_t ch_keys = (int64_t)(kPages - 2) * p.ps / BK * BK;
+    const int CH = (int)min<int64_t>(ch_keys > 0 ? ch_keys : BK, 1 << 30);
+    for (int c0 = 0; c0 < kv_end; c0 += CH) {
+        const int c1 = min(kv_end, c0 + CH);
+        const int t0 = c0 / BK, t1 = (c1 + BK - 1) / BK;
+        sc.first_pg = (int)udiv_magic((uint32_t)c0, p.ps_magic);
+        sc.c1 = c1;
+        const int npg = (int)udiv_magic((uint32_t)(c1 - 1), p.ps_magic) - sc.first_pg + 1;
+        __syncthreads();   // the previous chunk is done with the slice and both buffers
+        for (int i = tid; i < npg; i += 256) pages[i] = bt_row[sc.first_pg + i];
+        __syncthreads();
+        load_stage(p, sc, t0, st_regs);
+        if constexpr (MASK != 0) load_mask<MASK, NQ>(mc, tid, n, t0, mst);
+        store_stage(sc, st_regs, k_lds[t0 & 1], v_lds[t0 & 1]);
+        if constexpr (MASK != 0) store_mask<MASK, NQ>(mst, tid, mbits[t0 & 1]);
+        if (t0 + 1 < t1) {
+            load_stage(p, sc, t0 + 1, st_regs);
+            if constexpr (MASK != 0) load_mask<MASK, NQ>(mc, tid, n, t0 + 1, mst);
+        }
+        __syncthreads();
+        for (int kt = t0; kt < t1; ++kt) {
+            compute(kt, kt & 1);
+            if (kt + 1 < t1) {
+                // Tile kt+1 into the other buffer (its readers finished at
+                // the last barrier), then tile kt+2's loads go out.
+                store_stage(sc, st_regs, k_lds[(kt + 1) & 1], v_lds[(kt + 1) & 1]);
+                if constexpr (MASK != 0) store_mask<MASK, NQ>(mst, tid, mbits[(kt + 1) & 1]);
+                if (kt + 2 < t1) {
+                    load_stage(p, sc, kt + 2, st_regs);
+                    if constexpr (MASK != 0) load_mask<MASK, NQ>(mc, tid, n, kt + 2, mst);
+                }
+            }
+            __syncthreads();
         }
     }
 
-    float l_row = l_i;
-    l_row += __shfl_xor(l_row, 16);
-    l_row += __shfl_xor(l_row, 32);
-    if (!row_ok) return;
-    const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
-    uint16_t *orow = p.o + (int64_t)(q0 + myrow) * p.o_st + (int64_t)hq * p.o_sh + 4 * lq;
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        uint2 wv;
-        wv.x = pack_bf16(oacc[m][0] * inv, oacc[m][1] * inv);
-        wv.y = pack_bf16(oacc[m][2] * inv, oacc[m][3] * inv);
-        *reinterpret_cast<uint2 *>(orow + 16 * m) = wv;
+    for (int rb = 0; rb < 2; ++rb) {
+        const float l_row = lacc[rb][0];
+        if (!row_ok[rb]) continue;
+        const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
+        uint16_t *orow = p.o + (int64_t)(q0 + myrow[rb]) * p.o_st + (int64_t)hq * p.o_sh + 4 * lq;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            uint2 wv;
+            wv.x = pack_bf16(oacc[rb][m][0] * inv, oacc[rb][m][1] * inv);
+            wv.y = pack_bf16(oacc[rb][m][2] * inv, oacc[rb][m][3] * inv);
+            *reinterpret_cast<uint2 *>(orow + 16 * m) = wv;
+        }
     }
 }
 

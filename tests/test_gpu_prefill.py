@@ -100,3 +100,13 @@ def test_prefill_repeat_runs_are_bit_identical():
     a = run_prefill(case).clone()
     b = run_prefill(case)
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("ps,G", [(1, 4), (3, 2), (1, 1)])
+def test_prefill_long_context_spans_several_page_slices(ps, G):
+    """The kernel stages at most 510 block-table entries at a time; with page
+    size 1 that is 448 keys, with page size 3 1472 keys, so these contexts
+    cross several slices, with ragged ends and a 3-D mask."""
+    case = workloads.prefill_case(360 + ps + G, 2, 2 * G, 2, 128, None, None, ps,
+                                  q_lens=[70, 37], ctx_lens=[1500, 1333], mask_frac=0.05)
+    assert_close(run_prefill(case), oracle_prefill(case), what="ps=%d G=%d" % (ps, G))
