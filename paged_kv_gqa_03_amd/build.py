@@ -25,9 +25,16 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
          "-I" + os.path.join(ROOT, "include"), "-I" + CSRC, "-Wall", "-Wno-unused-function"]
 
 
+# Per-source flags.  prefill.hip runs with the IEEE mode bit off (its
+# arithmetic never produces or consumes NaN: masked scores are -inf and every
+# -inf - -inf case is guarded), which lets fmax use MFMA results directly
+# instead of quieting each input first.
+SOURCE_FLAGS = {"prefill.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
+
+
 def _compile(src, extra):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + FLAGS + extra + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + FLAGS + SOURCE_FLAGS.get(src, []) + extra + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     return src, obj, r
 

@@ -399,6 +399,8 @@ int attn_paged_prefill(const void *q, int64_t q_st, int64_t q_sh, const int32_t 
     if (kv_s_page < 0 || kv_s_slot < 0 || kv_s_head < 0 || kv_s_page >= (1ll << 32) ||
         (int64_t)(page_size - 1) * kv_s_slot + (int64_t)(Hkv - 1) * kv_s_head + D >= (1ll << 31))
         return fail(ATTN_ERR_UNSUPPORTED, "attn_paged_prefill: pool strides exceed the 32-bit page/slot addressing");
+    if ((int64_t)num_tiles * Hkv * 2 >= (1ll << 31))
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_paged_prefill: num_tiles * Hkv too large for one grid");
     if (B == 0 || num_tiles == 0) return ok();
     pa::PrefillParams p{};
     p.q = static_cast<const uint16_t *>(q);

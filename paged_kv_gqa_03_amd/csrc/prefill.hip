@@ -176,11 +176,13 @@ __device__ __forceinline__ int v_col(int d, int grp) { return 8 * (grp ^ ((d >> 
 // at permuted position ph (a multiple of 4).
 __device__ __forceinline__ void store_v_pair(uint16_t *v_lds, int d, int ph, uint32_t a, uint32_t b, uint32_t c,
                                              uint32_t e) {
+    // v_perm selectors: bytes 0-3 pick from the second operand, 4-7 from
+    // the first; 0x05040100 = (b.lo16, a.lo16), 0x07060302 = (b.hi16, a.hi16).
     uint2 lo, hi;
-    lo.x = (a & 0xffffu) | (b << 16);
-    lo.y = (c & 0xffffu) | (e << 16);
-    hi.x = (a >> 16) | (b & 0xffff0000u);
-    hi.y = (c >> 16) | (e & 0xffff0000u);
+    lo.x = __builtin_amdgcn_perm(b, a, 0x05040100u);
+    lo.y = __builtin_amdgcn_perm(e, c, 0x05040100u);
+    hi.x = __builtin_amdgcn_perm(b, a, 0x07060302u);
+    hi.y = __builtin_amdgcn_perm(e, c, 0x07060302u);
     const int col = v_col(d, ph >> 3) + (ph & 7);   // d and d + 1 share a 16-row block
     *reinterpret_cast<uint2 *>(&v_lds[d * VLD + col]) = lo;
     *reinterpret_cast<uint2 *>(&v_lds[(d + 1) * VLD + col]) = hi;
@@ -200,22 +202,29 @@ __device__ __forceinline__ void store_stage(const StageCtx &sc, const Stage &r, 
 }
 
 template <int HP, int MASK>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) {
+__global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) {
     constexpr int WPH = 4 / HP;   // waves (32-row groups) per head
     constexpr int R = 32 * WPH;   // rows per work-map tile
-    __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][BK * KLD];
-    __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][128 * VLD];
+    constexpr int SBUF = BK * KLD + 128 * VLD;                // one K tile + one V^T tile (elements)
+    __shared__ __attribute__((aligned(16))) uint16_t stage_lds[2 * 2 * SBUF];   // [team][buffer]
     __shared__ int32_t pages[kPages];
     constexpr int MROWS = MASK == 3 ? R : 1;                  // mask rows per tile
     constexpr int NQ = MASK == 3 ? R / 32 : 1;                // mask rows per thread
-    __shared__ __attribute__((aligned(8))) uint8_t mbits[2][MROWS * 8];
+    __shared__ __attribute__((aligned(8))) uint8_t mbits[2][2][MROWS * 8];
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int tile = blockIdx.x;
+    // Two teams of four waves take alternate KV tiles of the same query
+    // rows and heads; team 1 hands its state to team 0 at the end.
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int team = tid >> 8, ttid = tid & 255, w = (tid >> 6) & 3;
+    // Tiles in reverse work-map order (a sequence's last, longest tiles
+    // first), the head groups of a tile next to each other.
+    const int nhg = p.Hkv * (p.G / HP);
+    const int tile = p.num_tiles - 1 - (int)(blockIdx.x / (unsigned)nhg);
+    const int hg = (int)(blockIdx.x % (unsigned)nhg);
     const int b = p.t2b[tile], ti = p.t2i[tile];
     const int groups_per_kv = p.G / HP;
-    const int g = blockIdx.y / groups_per_kv;
-    const int hq = g * p.G + (blockIdx.y % groups_per_kv) * HP + (w % HP);
+    const int g = hg / groups_per_kv;
+    const int hq = g * p.G + (hg % groups_per_kv) * HP + (w % HP);
     const int q0 = p.qo_indptr[b];
     const int qn = p.qo_indptr[b + 1] - q0;
     const int n = p.kv_lens[b];
@@ -233,7 +242,6 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
     // Keys the tile can see: all of the sequence, or up to its causal frontier.
     const int last_row = min(qn, row0 + R) - 1;
     const int kv_end = (c >= 0) ? min(n, c + last_row + 1) : n;
-    const int n_kt = (kv_end + BK - 1) / BK;
 
     // Q^T operands: row myrow[rb], d = 32s + 8*lq .. +8.  A negative scale
     // is applied as |scale| on negated Q (a sign flip, exact), so the row
@@ -274,8 +282,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
     // Staging assignment: keys 4*(tid >> 4) + r (r = 0..3) of K and of V,
     // chunk cc = tid & 15.
     StageCtx sc;
-    sc.cc = tid & 15;
-    sc.kg = tid >> 4;
+    sc.cc = ttid & 15;
+    sc.kg = ttid >> 4;
     sc.pages = pages;
     sc.kbase = p.k + (int64_t)g * p.s_head + sc.cc * 8;
     sc.vbase = p.v + (int64_t)g * p.s_head + sc.cc * 8;
@@ -302,30 +310,33 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
     // One tile of math from LDS buffer `buf`.  FULL: every key of the tile is
     // admitted by every row of the wave (the common case), so the per-key
     // length and causal tests are skipped.
+    auto kbuf = [&](int buf) { return stage_lds + (2 * team + buf) * SBUF; };
+    auto vbuf = [&](int buf) { return stage_lds + (2 * team + buf) * SBUF + BK * KLD; };
     auto tile_math = [&](auto full_c, int kt, int buf) {
         constexpr bool FULL = decltype(full_c)::value;
-        const uint16_t *kl = k_lds[buf];
-        const uint16_t *vl = v_lds[buf];
+        const uint16_t *kl = kbuf(buf);
+        const uint16_t *vl = vbuf(buf);
         // S^T blocks: keys 16kb + 4lq + i of the tile, rows myrow[rb].
+        // Depth step outermost: eight independent accumulators per step, so
+        // no MFMA waits on the result of the one before it.
         f32x4_t st[2][4];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            st[0][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            st[1][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int kb = 0; kb < 4; ++kb) st[0][kb] = st[1][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
                 const bf16x8_t a = as_bf16x8(
                     *reinterpret_cast<const uint4 *>(&kl[(16 * kb + (lane & 15)) * KLD + 32 * s + 8 * lq]));
                 st[0][kb] = mfma16(a, qf[0][s], st[0][kb]);
                 st[1][kb] = mfma16(a, qf[1][s], st[1][kb]);
             }
-        }
         // Scores of keys not admitted become -inf (then P = 0).
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
             const int room = lim[rb] - (kt * BK + 4 * lq);   // admitted iff 16kb + i < room
             uint2 kbits = make_uint2(~0u, ~0u);               // keys 0..31, 32..63 of the tile
-            if constexpr (MASK != 0) kbits = *reinterpret_cast<const uint2 *>(&mbits[buf][mloc[rb] * 8]);
+            if constexpr (MASK != 0) kbits = *reinterpret_cast<const uint2 *>(&mbits[team][buf][mloc[rb] * 8]);
             kbits.x >>= 4 * lq;
             kbits.y >>= 4 * lq;
 #pragma unroll
@@ -410,32 +421,68 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
         sc.first_pg = (int)udiv_magic((uint32_t)c0, p.ps_magic);
         sc.c1 = c1;
         const int npg = (int)udiv_magic((uint32_t)(c1 - 1), p.ps_magic) - sc.first_pg + 1;
-        __syncthreads();   // the previous chunk is done with the slice and both buffers
-        for (int i = tid; i < npg; i += 256) pages[i] = bt_row[sc.first_pg + i];
+        __syncthreads();   // the previous chunk is done with the slice and the buffers
+        for (int i = tid; i < npg; i += 512) pages[i] = bt_row[sc.first_pg + i];
         __syncthreads();
-        load_stage(p, sc, t0, st_regs);
-        if constexpr (MASK != 0) load_mask<MASK, NQ>(mc, tid, n, t0, mst);
-        store_stage(sc, st_regs, k_lds[t0 & 1], v_lds[t0 & 1]);
-        if constexpr (MASK != 0) store_mask<MASK, NQ>(mst, tid, mbits[t0 & 1]);
-        if (t0 + 1 < t1) {
-            load_stage(p, sc, t0 + 1, st_regs);
-            if constexpr (MASK != 0) load_mask<MASK, NQ>(mc, tid, n, t0 + 1, mst);
+        // This team's tiles of the chunk: t0 + team, t0 + team + 2, ...
+        const int kt0 = t0 + team;
+        const int nit = (t1 - t0 + 1) >> 1;
+        if (kt0 < t1) {
+            load_stage(p, sc, kt0, st_regs);
+            if constexpr (MASK != 0) load_mask<MASK, NQ>(mc, ttid, n, kt0, mst);
+            store_stage(sc, st_regs, kbuf(0), vbuf(0));
+            if constexpr (MASK != 0) store_mask<MASK, NQ>(mst, ttid, mbits[team][0]);
+        }
+        if (kt0 + 2 < t1) {
+            load_stage(p, sc, kt0 + 2, st_regs);
+            if constexpr (MASK != 0) load_mask<MASK, NQ>(mc, ttid, n, kt0 + 2, mst);
         }
         __syncthreads();
-        for (int kt = t0; kt < t1; ++kt) {
-            compute(kt, kt & 1);
-            if (kt + 1 < t1) {
-                // Tile kt+1 into the other buffer (its readers finished at
-                // the last barrier), then tile kt+2's loads go out.
-                store_stage(sc, st_regs, k_lds[(kt + 1) & 1], v_lds[(kt + 1) & 1]);
-                if constexpr (MASK != 0) store_mask<MASK, NQ>(mst, tid, mbits[(kt + 1) & 1]);
-                if (kt + 2 < t1) {
-                    load_stage(p, sc, kt + 2, st_regs);
-                    if constexpr (MASK != 0) load_mask<MASK, NQ>(mc, tid, n, kt + 2, mst);
+        for (int it = 0; it < nit; ++it) {
+            const int kt = kt0 + 2 * it;
+            if (kt < t1) compute(kt, it & 1);
+            if (kt + 2 < t1) {
+                // The team's next tile into its other buffer (its readers
+                // finished at the last barrier), then the one after goes out.
+                store_stage(sc, st_regs, kbuf((it + 1) & 1), vbuf((it + 1) & 1));
+                if constexpr (MASK != 0) store_mask<MASK, NQ>(mst, ttid, mbits[team][(it + 1) & 1]);
+                if (kt + 4 < t1) {
+                    load_stage(p, sc, kt + 4, st_regs);
+                    if constexpr (MASK != 0) load_mask<MASK, NQ>(mc, ttid, n, kt + 4, mst);
                 }
             }
             __syncthreads();
         }
+    }
+
+    // Team 1's (O, reference, sum) go through its own stage buffers (free
+    // since the last barrier) to the matching wave of team 0, which merges.
+    float *xch = reinterpret_cast<float *>(stage_lds + 2 * SBUF) + w * (68 * 64);
+    if (team == 1) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+            for (int m = 0; m < 8; ++m)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) xch[(rb * 32 + m * 4 + i) * 64 + lane] = oacc[rb][m][i];
+            xch[(64 + rb) * 64 + lane] = m_ref[rb];
+            xch[(66 + rb) * 64 + lane] = lacc[rb][0];
+        }
+    }
+    __syncthreads();
+    if (team == 1) return;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        const float mb = xch[(64 + rb) * 64 + lane], lb = xch[(66 + rb) * 64 + lane];
+        const float mm = fmaxf(m_ref[rb], mb);
+        const float aa = m_ref[rb] == -INFINITY ? 0.f : exp2_fast(m_ref[rb] - mm);
+        const float ab = mb == -INFINITY ? 0.f : exp2_fast(mb - mm);
+        lacc[rb][0] = lacc[rb][0] * aa + lb * ab;
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                oacc[rb][m][i] = oacc[rb][m][i] * aa + xch[(rb * 32 + m * 4 + i) * 64 + lane] * ab;
     }
 
 #pragma unroll
@@ -456,11 +503,11 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillParams p) 
 
 template <int HP>
 hipError_t launch_hp(const PrefillParams &p, hipStream_t stream) {
-    const dim3 grid(p.num_tiles, p.Hkv * (p.G / HP));
+    const dim3 grid((unsigned)p.num_tiles * (unsigned)(p.Hkv * (p.G / HP)));
     switch (p.mask_ndim) {
-        case 0: hipLaunchKernelGGL((prefill_kernel<HP, 0>), grid, dim3(256), 0, stream, p); break;
-        case 2: hipLaunchKernelGGL((prefill_kernel<HP, 2>), grid, dim3(256), 0, stream, p); break;
-        case 3: hipLaunchKernelGGL((prefill_kernel<HP, 3>), grid, dim3(256), 0, stream, p); break;
+        case 0: hipLaunchKernelGGL((prefill_kernel<HP, 0>), grid, dim3(512), 0, stream, p); break;
+        case 2: hipLaunchKernelGGL((prefill_kernel<HP, 2>), grid, dim3(512), 0, stream, p); break;
+        case 3: hipLaunchKernelGGL((prefill_kernel<HP, 3>), grid, dim3(512), 0, stream, p); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
