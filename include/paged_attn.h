@@ -255,10 +255,11 @@ int attn_paged_prefill(const void *q, int64_t q_st, int64_t q_sh, const int32_t 
  *           is e4m3(code) * inv_scale (exact product)
  *   swa_indices int64 [T, W], row t at swa_indices + t*i_st
  *   swa_lens    int64 [T]; window position j of token t is admitted iff
- *           j < swa_lens[t] and swa_indices[t, j] >= 0
+ *           j < swa_lens[t] and 0 <= swa_indices[t, j] < num_blocks*block_size
+ *           (an index outside the pool is treated like -1 and never read)
  *   o       [T, NH, HD] bf16
  * Every head of a token attends the same rows (K = V).  Supported: HD = 512,
- * NH a multiple of 16, W <= 1024; slots must lie below num_blocks*block_size.
+ * NH a multiple of 16, W <= 1024, num_blocks*block_size < 2^31.
  */
 int attn_swa_fp8_decode(const void *q, int64_t q_st, int64_t q_sh,
                         const uint8_t *kv_cache, int64_t c_sb, int64_t c_ss,

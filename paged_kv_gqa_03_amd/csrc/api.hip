@@ -445,6 +445,8 @@ int attn_swa_fp8_decode(const void *q, int64_t q_st, int64_t q_sh,
                     "attn_swa_fp8_decode: q rows and cache rows must be 16-byte aligned, o rows 8-byte aligned");
     if (c_sb < 0 || c_ss < 0 || s_ss < 0 || i_st < window)
         return fail(ATTN_ERR_INVALID_ARG, "attn_swa_fp8_decode: bad strides");
+    if ((int64_t)num_blocks * block_size >= (1ll << 31))
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_swa_fp8_decode: num_blocks * block_size must stay below 2^31 slots");
     if (T == 0) return ok();
     pa::SwaParams p{};
     p.q = static_cast<const uint16_t *>(q);
@@ -454,6 +456,8 @@ int attn_swa_fp8_decode(const void *q, int64_t q_st, int64_t q_sh,
     p.ind = swa_indices; p.i_st = i_st; p.lens = swa_lens;
     p.o = static_cast<uint16_t *>(o); p.o_st = o_st; p.o_sh = o_sh;
     p.T = T; p.NH = NH; p.W = window; p.bs = block_size;
+    p.slots = num_blocks * block_size;
+    p.bs_magic = ((1ull << 32) + (uint64_t)block_size - 1) / (uint64_t)block_size;
     p.sl2 = scale * 1.4426950408889634f;
     return launch_status(pa::launch_swa(p, static_cast<hipStream_t>(stream)), "swa kernel");
 }

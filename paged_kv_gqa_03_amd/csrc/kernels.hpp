@@ -103,7 +103,9 @@ struct SwaParams {
     uint16_t *o;
     int64_t o_st, o_sh;
     int T, NH, W, bs;
-    float sl2;   // scale * log2(e)
+    int slots;            // num_blocks * bs: indices at or above it are not admitted
+    uint64_t bs_magic;    // ceil(2^32 / bs) for slot -> (block, offset)
+    float sl2;            // scale * log2(e)
 };
 
 hipError_t launch_decode(const DecodeParams &p, int D, int G, bool paged, hipStream_t stream);

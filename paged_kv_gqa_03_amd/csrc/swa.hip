@@ -12,8 +12,9 @@
 // Work decomposition (cf. the CuTeDSL stub's plan: one CTA per (token, group
 // of 16 query heads), KV streamed in tiles): one 256-thread workgroup per
 // (16-head group, token).  Per tile of up to 128 window positions:
-//   1. the token's slot offsets and inverse scales go to LDS, then the rows
-//      (fp8, 512 B each) are staged in LDS; masked positions become zero rows;
+//   1. the rows (fp8, 512 B each) and inverse scales are staged in LDS in
+//      two dependent load steps (indices, then rows and scales, all issued
+//      before any LDS store); masked positions become zero rows;
 //   2. wave w computes S^T for positions 32w..32w+31 with
 //      v_mfma_f32_16x16x32_bf16 on rows converted fp8 -> bf16 exactly
 //      (v_cvt_scalef32_pk_bf16_fp8), Q^T for the 16 heads held in registers;
@@ -73,9 +74,9 @@ __device__ __forceinline__ void transpose4x4(uint32_t w0, uint32_t w1, uint32_t 
     out[3] = perm(b23, b01, 0x07060302u);  // b3
 }
 
-__global__ __launch_bounds__(256) void swa_kernel(const SwaParams p) {
+__global__ __launch_bounds__(256, 2) void swa_kernel(const SwaParams p) {
     __shared__ __attribute__((aligned(16))) uint8_t x_lds[KT * XLD];
-    __shared__ int64_t row_off[KT];
+    __shared__ int32_t admit[KT];   // window position admitted (1) or masked (0)
     __shared__ float inv_lds[KT];
     __shared__ __attribute__((aligned(16))) uint16_t p_lds[16 * PLD];
     __shared__ float red_max[4][16], red_sum[4][16];
@@ -88,12 +89,14 @@ __global__ __launch_bounds__(256) void swa_kernel(const SwaParams p) {
     len = len < 0 ? 0 : (len > p.W ? p.W : len);
 
     // Q^T operand: head r, dims 32s + 8*q4 .. +8.
+    // Loaded right after the first tile's window indices: the loads complete
+    // in order, so the index -> row chain must not queue behind 16 KB of Q.
     bf16x8_t qf[16];
-    {
+    auto load_q = [&]() {
         const uint16_t *qr = p.q + (int64_t)t * p.q_st + (int64_t)head * p.q_sh + 8 * q4;
 #pragma unroll
         for (int s = 0; s < 16; ++s) qf[s] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(qr + 32 * s));
-    }
+    };
     f32x4_t oacc[2][4];
 #pragma unroll
     for (int a = 0; a < 2; ++a)
@@ -102,33 +105,49 @@ __global__ __launch_bounds__(256) void swa_kernel(const SwaParams p) {
     float M = -INFINITY, L = 0.f;
 
     const int ntile = (int)((len + KT - 1) / KT);
+    if (ntile == 0) load_q();
     for (int tile = 0; tile < ntile; ++tile) {
         const int j0 = tile * KT;
         const int nk = (int)min((int64_t)KT, len - j0);
         const int nkb = (nk + 31) >> 5;   // 32-position blocks in this tile
         __syncthreads();                  // the previous tile is fully consumed
-        if (tid < KT) {
-            int64_t off = -1;
-            float inv = 0.f;
-            if (tid < nk) {
-                const int64_t idx = p.ind[(int64_t)t * p.i_st + j0 + tid];
-                if (idx >= 0) {
-                    off = (idx / p.bs) * p.c_sb + (idx % p.bs) * p.c_ss;
-                    inv = bf16_lo((uint32_t)p.inv_scale[idx * p.s_ss]);
+        // Staging with two dependent steps: every thread first loads the
+        // window indices of its 16 rows (keys (tid >> 5) + 8i, chunk tid & 31)
+        // and, below 128, of key tid (for the scale); then all row chunks and
+        // scales go out together, and only then are they stored to LDS.
+        {
+            const int64_t *irow = p.ind + (int64_t)t * p.i_st + j0;
+            const int ch = tid & 31;
+            int64_t idx[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int key = (tid >> 5) + 8 * i;
+                idx[i] = key < nk ? irow[key] : -1;
+            }
+            const int64_t idx_s = tid < nk ? irow[tid] : -1;
+            if (tile == 0) load_q();
+            uint4 v[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                v[i] = make_uint4(0u, 0u, 0u, 0u);
+                if (idx[i] >= 0 && idx[i] < p.slots) {
+                    const uint32_t blk = udiv_magic((uint32_t)idx[i], p.bs_magic);
+                    const uint32_t off = (uint32_t)idx[i] - blk * (uint32_t)p.bs;
+                    v[i] = *reinterpret_cast<const uint4 *>(p.cache + (int64_t)blk * p.c_sb + (int64_t)off * p.c_ss +
+                                                             ch * 16);
                 }
             }
-            row_off[tid] = off;
-            inv_lds[tid] = inv;
-        }
-        __syncthreads();
-        // Stage rows of the active blocks: chunk c = 16 bytes, 32 per row.
-#pragma unroll 4
-        for (int c = tid; c < nkb * 32 * 32; c += 256) {
-            const int key = c >> 5, ch = c & 31;
-            const int64_t off = row_off[key];
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (off >= 0) v = *reinterpret_cast<const uint4 *>(p.cache + off + ch * 16);
-            *reinterpret_cast<uint4 *>(&x_lds[key * XLD + ch * 16]) = v;
+            const bool ok_s = idx_s >= 0 && idx_s < p.slots;
+            const float inv = ok_s ? bf16_lo((uint32_t)p.inv_scale[idx_s * p.s_ss]) : 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int key = (tid >> 5) + 8 * i;
+                if (key < nkb * 32) *reinterpret_cast<uint4 *>(&x_lds[key * XLD + ch * 16]) = v[i];
+            }
+            if (tid < KT) {
+                admit[tid] = ok_s ? 1 : 0;
+                inv_lds[tid] = inv;
+            }
         }
         __syncthreads();
 
@@ -149,7 +168,7 @@ __global__ __launch_bounds__(256) void swa_kernel(const SwaParams p) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int key = 16 * kb + 4 * q4 + i;
-                    x[h2][i] = row_off[key] >= 0 ? acc[i] * p.sl2 * inv_lds[key] : -INFINITY;
+                    x[h2][i] = admit[key] ? acc[i] * p.sl2 * inv_lds[key] : -INFINITY;
                     mt = fmaxf(mt, x[h2][i]);
                 }
             }

@@ -102,3 +102,18 @@ def test_swa_repeat_runs_are_bit_identical():
     case = workloads.swa_fp8(seed=1016)
     a = run_swa(case).clone()
     assert torch.equal(a, run_swa(case))
+
+
+def test_swa_index_outside_pool_is_masked():
+    """Indices at or above num_blocks * block_size are treated like -1 (never
+    read): the result equals the oracle's with those entries set to -1."""
+    case = workloads.swa_case(450, 6, 32, 512, 128, 256, 4, len_range=(20, 128))
+    slots = case["num_blocks"] * case["block_size"]
+    bad = case["indices"].clone()
+    bad[0, 3] = slots
+    bad[2, 0] = slots + 12345
+    bad[5, 7] = (1 << 40)
+    masked = bad.clone()
+    masked[masked >= slots] = -1
+    ref = oracle_swa(dict(case, indices=masked))
+    assert_close(run_swa(dict(case, indices=bad)), ref)
