@@ -39,7 +39,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="paged_b128",
-                    choices=["paged_b128", "paged_b32", "paged_b128_kv4096", "paged_b32_kv4096", "contig_b16"])
+                    choices=["paged_b128", "paged_b32", "paged_b128_kv4096", "paged_b32_kv4096", "contig_b16",
+                             "ragged_prefill", "ragged_prefill_masked", "swa_fp8"])
     ap.add_argument("--num-splits", type=int, default=0, help="0 = planner")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
@@ -119,6 +120,15 @@ def main():
     if args.workload == "contig_b16":
         r = bench_contiguous(torch, pa, dev, args.steps, args.warmup, args.num_splits)
         print(json.dumps({"workload": "contiguous decode B=16 Hq=32 Hkv=8 D=128 kv=2048 bhld", **r}), flush=True)
+        return
+    if args.workload in ("ragged_prefill", "ragged_prefill_masked"):
+        r = bench_prefill(torch, pa, dev, args.steps, args.warmup, masked=args.workload.endswith("masked"))
+        print(json.dumps({"workload": "ragged paged prefill 8 seqs ctx U[0,2048] new U[1,512] Hq=32 Hkv=8 D=128"
+                                      + (" 3-D mask" if args.workload.endswith("masked") else ""), **r}), flush=True)
+        return
+    if args.workload == "swa_fp8":
+        r = bench_swa(torch, pa, dev, args.steps, args.warmup)
+        print(json.dumps({"workload": "fp8 sliding-window decode T=64 NH=128 HD=512 W=128", **r}), flush=True)
         return
     probe = make_sets(args.workload, dev, 1)
     per_call = decode_bytes(probe[0])

@@ -67,7 +67,8 @@ int attn_version(void);
  * slices, whatever the spread of kv_lens.  A row is a group of up to 8 KV
  * heads when the KV head stride `kv_s_head` equals D (heads of a token
  * contiguous), else one head.  This planner returns W for `num_cus`
- * compute units (0 = query the current device): about two waves per unit,
+ * compute units (0 = query the current device): about three waves per unit
+ * when a wave streams eight KV heads (kv_s_head == D, Hkv >= 8), two otherwise,
  * and no slice shorter than 64 tokens of a row given max_kv_len.  page_size
  * 0 stands for a contiguous source (pass its K head stride as kv_s_head).
  * Host-only and deterministic; returns W >= 1, or a negative error code.

@@ -48,7 +48,11 @@ int device_cus() {
 }
 
 constexpr int kMaxWaves = 1 << 16;     // upper bound on decode slices (num_splits)
-constexpr int kWavesPerCuTarget = 2;   // decode waves per CU the planner aims at
+// Decode waves per CU the planner aims at: three when a wave streams whole
+// 2 KB token rows (eight KV heads), two when it streams one head (measured
+// best for each on MI355X with non-temporal K/V loads).
+constexpr int kWavesPerCuRows = 3;
+constexpr int kWavesPerCuHead = 2;
 constexpr int kMinSliceTokens = 64;    // shortest slice the planner makes, in tokens of a row
 
 // KV heads one decode wave covers: with the heads of a token adjacent in
@@ -178,7 +182,7 @@ int attn_plan_splits(int B, int Hkv, int G, int D, int max_kv_len, int page_size
     const long rows = (long)B * (Hkv / hw);
     const long line = rows * (long)max_kv_len;   // upper bound on the tokens of all rows
     long W = (line + kMinSliceTokens - 1) / kMinSliceTokens;
-    const long cap = (long)num_cus * kWavesPerCuTarget;
+    const long cap = (long)num_cus * (hw == 8 ? kWavesPerCuRows : kWavesPerCuHead);
     if (W > cap) W = cap;
     if (W > kMaxWaves) W = kMaxWaves;
     if (W < 1) W = 1;

@@ -46,8 +46,8 @@ def test_version():
 @pytest.mark.parametrize("s_head", [128, 16 * 128])
 def test_planner_bounds(B, Hkv, max_len, s_head):
     W = pa.attn_plan_splits(B, Hkv, 4, 128, max_len, 16, s_head, 256)
-    assert 1 <= W <= 256 * 2
     hw = min(8, Hkv) if s_head == 128 else 1
+    assert 1 <= W <= 256 * (3 if hw == 8 else 2)
     rows = B * (Hkv // hw)
     # no slice shorter than 64 tokens of a row, given the longest possible line
     assert W == 1 or rows * max_len >= 64 * (W - 1)
@@ -55,9 +55,12 @@ def test_planner_bounds(B, Hkv, max_len, s_head):
     assert pa.attn_plan_splits(2 * B, Hkv, 4, 128, max_len, 16, s_head, 256) >= W
 
 
-def test_planner_targets_two_waves_per_cu():
-    assert pa.attn_plan_splits(128, 8, 4, 128, 4096, 16, 128, 256) == 512
-    assert pa.attn_plan_splits(32, 8, 4, 128, 4096, 16, 128, 304) == 608
+def test_planner_waves_per_cu_target():
+    # eight KV heads per wave (whole 2 KB token rows): three waves per CU
+    assert pa.attn_plan_splits(128, 8, 4, 128, 4096, 16, 128, 256) == 768
+    assert pa.attn_plan_splits(32, 8, 4, 128, 4096, 16, 128, 304) == 912
+    # one KV head per wave (head-major source): two waves per CU
+    assert pa.attn_plan_splits(16, 8, 4, 128, 2048, 0, 2048 * 128, 256) == 512
     assert pa.attn_plan_splits(2, 2, 4, 64, 300, 16, 64, 256) == 10   # 600 tokens / 64
 
 
