@@ -65,10 +65,14 @@ def _declare(l):
     l.orc_prefill_plan.argtypes = [_P, _I, _I, _P, _P, _P, _I]
     l.orc_swa_fp8_decode.argtypes = [_P, _L, _L, _P, _L, _L, _P, _L, _P, _L, _P,
                                      _I, _I, _I, _I, _I, _D, _I, _P, _P]
+    l.orc_kv_append.argtypes = [_P, _P, _L, _L, _P, _P, _P, _P, _L, _L, _L, _P, _L, _I, _I, _I, _I]
+    l.orc_rotary.argtypes = [_P, _L, _L, _I, _I, _I, _P, _P, _L, _P, _P, _L, _L]
+    l.orc_fp8_quantize.argtypes = [_P, _L, _I, _I, _P, _P, _L, _P, _P]
     l.orc_num_threads.argtypes = []
     for name in ("orc_paged_decode", "orc_decode", "orc_paged_decode_partials", "orc_combine",
                  "orc_combine_f32", "orc_paged_prefill", "orc_prefill_plan",
-                 "orc_swa_fp8_decode", "orc_num_threads"):
+                 "orc_swa_fp8_decode", "orc_kv_append", "orc_rotary", "orc_fp8_quantize",
+                 "orc_num_threads"):
         getattr(l, name).restype = _I
 
 
@@ -247,3 +251,53 @@ def swa_fp8_decode(q, cache, inv_scale, indices, lens, block_size, scale,
         T, NH, HD, W, block_size, float(scale), 1 if emulate_bf16_dequant else 0,
         _ptr(out), _ptr(lse)))
     return out, lse
+
+
+def kv_append(k_pool, v_pool, block_table, k_new, v_new, new_indptr, start_pos):
+    """Return copies of the (page, slot, head, dim) pools with the packed new
+    rows k_new / v_new [N, Hkv, D] written at positions start_pos[b] + i of
+    sequence b (rows new_indptr[b] .. new_indptr[b+1]).  The pools' strides
+    are kept (a strided view is copied into a tensor of the same layout)."""
+    kp = torch.empty_strided(k_pool.shape, k_pool.stride(), dtype=k_pool.dtype)
+    vp = torch.empty_strided(v_pool.shape, v_pool.stride(), dtype=v_pool.dtype)
+    kp.copy_(k_pool.cpu())
+    vp.copy_(v_pool.cpu())
+    kn, vn = _cpu(k_new), _cpu(v_new)
+    assert kn.stride() == vn.stride() and kn.stride(2) == 1
+    bt = _cpu(block_table, torch.int32)
+    ind = _cpu(new_indptr, torch.int32)
+    st = _cpu(start_pos, torch.int32)
+    _check(lib().orc_kv_append(_ptr(kn), _ptr(vn), kn.stride(0), kn.stride(1), _ptr(ind), _ptr(st),
+                               _ptr(kp), _ptr(vp), kp.stride(0), kp.stride(1), kp.stride(2), _ptr(bt),
+                               bt.stride(0), ind.numel() - 1, kp.shape[2], kp.shape[3], kp.shape[1]))
+    return kp, vp
+
+
+def rotary(x, cos_tab, sin_tab, positions):
+    """x [T, H, D] bf16; cos_tab / sin_tab float32 [rows, D/2]; positions
+    int [T].  Returns the rotated [T, H, D] bf16 tensor."""
+    xc = _cpu(x)
+    assert xc.stride(2) == 1
+    c, s = _cpu(cos_tab, torch.float32), _cpu(sin_tab, torch.float32)
+    assert c.stride() == s.stride() and c.stride(1) == 1
+    pos = _cpu(positions, torch.int32)
+    T, H, D = xc.shape
+    out = torch.empty(T, H, D, dtype=torch.bfloat16)
+    _check(lib().orc_rotary(_ptr(xc), xc.stride(0), xc.stride(1), T, H, D, _ptr(c), _ptr(s), c.stride(0),
+                            _ptr(pos), _ptr(out), out.stride(0), out.stride(1)))
+    return out
+
+
+def fp8_quantize(x, mult=None):
+    """x [N, HD] bf16; mult float32 [N] or None (448 / amax per row).
+    Returns (codes uint8 [N, HD], inv_scale bf16 [N], amax float32 [N])."""
+    xc = _cpu(x)
+    assert xc.stride(1) == 1
+    N, HD = xc.shape
+    m = None if mult is None else _cpu(mult, torch.float32)
+    codes = torch.empty(N, HD, dtype=torch.uint8)
+    inv = torch.empty(N, dtype=torch.bfloat16)
+    amax = torch.empty(N, dtype=torch.float32)
+    _check(lib().orc_fp8_quantize(_ptr(xc), xc.stride(0), N, HD, _ptr(m), _ptr(codes), codes.stride(0),
+                                  _ptr(inv), _ptr(amax)))
+    return codes, inv, amax

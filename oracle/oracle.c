@@ -32,6 +32,10 @@
  *   ragged work map              AstrAI "CUDA Kernels" doc, section
  *                                "Q Scheduling and KV Addressing" (worked
  *                                example with q lengths 70, 10, 130).
+ *   paged KV append, rotary,     the cache write the backend layer owns, the
+ *   fp8 quantize-on-write        rotary kernel's complex-product rotation,
+ *                                and the FP8 multiplier convention (see each
+ *                                function below).
  *
  * Readings where the pages are silent (each also listed in the design notes):
  *   - query head h uses KV head h / (Hq / Hkv) (consecutive heads share);
@@ -463,6 +467,141 @@ int orc_swa_fp8_decode(const uint16_t *q, int64_t q_st, int64_t q_sh,
                    out + ((size_t)t * NH + h) * HD, lse + (size_t)t * NH + h, s);
         }
         free(X); free(s); free(qr); free(allow);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------ cache writes, rotary */
+
+/*
+ * Paged KV append (AstrAI "CUDA Kernels" doc, Backend Layer: the attention
+ * backend owns the KV cache writes that precede paged decode / prefill).
+ * New rows are packed [N, Hkv, D] (row i at k_new + i*n_st, head g at
+ * + g*n_sh); sequence b owns rows new_indptr[b] .. new_indptr[b+1] and its
+ * first new token sits at position start_pos[b].  Token position p of
+ * sequence b lives in page bt[b][p / ps], slot p % ps.  A pure copy: every
+ * written element equals its source bit for bit.
+ */
+int orc_kv_append(const uint16_t *k_new, const uint16_t *v_new, int64_t n_st, int64_t n_sh,
+                  const int32_t *new_indptr, const int32_t *start_pos,
+                  uint16_t *k_pool, uint16_t *v_pool, int64_t s_page, int64_t s_slot, int64_t s_head,
+                  const int32_t *bt, int64_t bt_sb, int B, int Hkv, int D, int ps)
+{
+    if (B < 0 || Hkv <= 0 || D <= 0 || ps <= 0) return -1;
+    for (int b = 0; b < B; ++b) {
+        for (int i = new_indptr[b]; i < new_indptr[b + 1]; ++i) {
+            int64_t pos = (int64_t)start_pos[b] + (i - new_indptr[b]);
+            int32_t page = bt[(int64_t)b * bt_sb + pos / ps];
+            if (page < 0) return -1;
+            int64_t base = (int64_t)page * s_page + (pos % ps) * s_slot;
+            for (int g = 0; g < Hkv; ++g)
+                for (int d = 0; d < D; ++d) {
+                    k_pool[base + g * s_head + d] = k_new[(int64_t)i * n_st + g * n_sh + d];
+                    v_pool[base + g * s_head + d] = v_new[(int64_t)i * n_st + g * n_sh + d];
+                }
+        }
+    }
+    return 0;
+}
+
+/* Round a double to the nearest bf16 (ties to even), once. */
+static double round_f64_to_bf16(double x)
+{
+    if (x == 0.0 || !isfinite(x)) return x;
+    int e;
+    frexp(x, &e);                        /* |x| = m * 2^e, 0.5 <= m < 1 */
+    int q = e - 8;                       /* bf16 keeps 8 significant bits */
+    if (q < -133) q = -133;              /* subnormal quantum 2^-133 */
+    return ldexp(nearbyint(ldexp(x, -q)), q);
+}
+
+/*
+ * Rotary embedding (AstrAI "CUDA Kernels" doc, Rotary Embedding Kernel and
+ * Rotary Backend): the cos / sin rows of each token's position are looked up
+ * in fp32 tables [rows, D/2] (row p at + p*tab_st) and every adjacent pair
+ * (x[2i], x[2i+1]) of a head is multiplied, as a complex number, by
+ * cos_i + i sin_i (the torch fallback's view_as_complex product).  x, out are
+ * [T, H, D] bf16; the product is exact here and rounded to bf16 once.
+ */
+int orc_rotary(const uint16_t *x, int64_t x_st, int64_t x_sh, int T, int H, int D,
+               const float *cos_tab, const float *sin_tab, int64_t tab_st, const int32_t *pos,
+               uint16_t *out, int64_t o_st, int64_t o_sh)
+{
+    if (T < 0 || H <= 0 || D <= 0 || (D & 1)) return -1;
+    for (int t = 0; t < T; ++t)
+        for (int h = 0; h < H; ++h)
+            for (int i = 0; i < D / 2; ++i) {
+                double c = cos_tab[(int64_t)pos[t] * tab_st + i];
+                double s = sin_tab[(int64_t)pos[t] * tab_st + i];
+                double a = orc_bf16_to_f64(x[(int64_t)t * x_st + (int64_t)h * x_sh + 2 * i]);
+                double b = orc_bf16_to_f64(x[(int64_t)t * x_st + (int64_t)h * x_sh + 2 * i + 1]);
+                double re = round_f64_to_bf16(a * c - b * s), im = round_f64_to_bf16(a * s + b * c);
+                float fr = (float)re, fi = (float)im;   /* exact: bf16 values */
+                uint32_t ur, ui;
+                memcpy(&ur, &fr, 4);
+                memcpy(&ui, &fi, 4);
+                out[(int64_t)t * o_st + (int64_t)h * o_sh + 2 * i] = (uint16_t)(ur >> 16);
+                out[(int64_t)t * o_st + (int64_t)h * o_sh + 2 * i + 1] = (uint16_t)(ui >> 16);
+            }
+    return 0;
+}
+
+/* Nearest OCP e4m3fn code to a binary32 value: ties to the even code
+ * (mantissa bit 0 clear), magnitudes at or above 448 saturate to 448, NaN
+ * gives the NaN code, the sign bit is kept (so -0 gives 0x80).  Found by
+ * comparing against every finite magnitude. */
+static uint8_t nearest_e4m3fn(float p)
+{
+    if (isnan(p)) return 0x7F;
+    uint32_t u;
+    memcpy(&u, &p, 4);
+    uint8_t sign = (u >> 31) ? 0x80 : 0x00;
+    double a = fabs((double)p);
+    if (a >= 448.0) return sign | 0x7E;
+    int best = 0;
+    double best_err = INFINITY;
+    for (int c = 0; c <= 0x7E; ++c) {
+        double err = fabs(orc_e4m3fn_to_f64((uint8_t)c) - a);
+        if (err < best_err || (err == best_err && (c & 1) == 0 && (best & 1) == 1)) {
+            best = c;
+            best_err = err;
+        }
+    }
+    return sign | (uint8_t)best;
+}
+
+/*
+ * fp8 quantize-on-write of sliding-window cache rows (native_swa_decode.py:
+ * the cache holds e4m3fn codes and a per-slot inverse scale; AstrAI "CUDA
+ * Kernels" doc, FP8 section: quantize takes the multiplier and multiplies
+ * by it, and amax is reported in the input domain).  Row n of x [N, HD]:
+ *   amax = max |x|;  m = mult[n], or 448 / amax (1 when amax is 0) when
+ *   mult is NULL;  code = nearest_e4m3fn(x * m) with the product taken in
+ *   binary32 (the precision the decision is made in);  inv = bf16(1 / m)
+ *   (binary32 division, then nearest-even to bf16).
+ */
+int orc_fp8_quantize(const uint16_t *x, int64_t x_st, int N, int HD, const float *mult,
+                     uint8_t *codes, int64_t c_st, uint16_t *inv_out, float *amax_out)
+{
+    if (N < 0 || HD <= 0) return -1;
+    for (int n = 0; n < N; ++n) {
+        float amax = 0.f;
+        for (int d = 0; d < HD; ++d) {
+            float v = fabsf((float)orc_bf16_to_f64(x[(int64_t)n * x_st + d]));
+            if (v > amax) amax = v;
+        }
+        float m = mult ? mult[n] : (amax > 0.f ? 448.0f / amax : 1.0f);
+        for (int d = 0; d < HD; ++d) {
+            float p = (float)orc_bf16_to_f64(x[(int64_t)n * x_st + d]) * m;
+            codes[(int64_t)n * c_st + d] = nearest_e4m3fn(p);
+        }
+        float inv = 1.0f / m;
+        double r = round_f64_to_bf16((double)inv);
+        float rf = (float)r;
+        uint32_t ur;
+        memcpy(&ur, &rf, 4);
+        inv_out[n] = (uint16_t)(ur >> 16);
+        if (amax_out) amax_out[n] = amax;
     }
     return 0;
 }

@@ -426,3 +426,198 @@ def test_swa_no_valid_position_gives_zero(orc):
     assert torch.equal(out[0], torch.zeros_like(out[0])) and torch.isneginf(lse[0]).all()
     assert torch.equal(out[2], torch.zeros_like(out[2]))
     assert torch.isfinite(lse[1]).all()
+
+
+# ------------------------------------------------------- paged KV append
+def test_kv_append_hand_placed_tokens(orc):
+    """Page size 4, sequence 0 starts at position 6: its three new tokens go
+    to (bt[0][1], slot 2), (bt[0][1], slot 3), (bt[0][2], slot 0); sequence 1
+    starts at 0 with one token at (bt[1][0], slot 0)."""
+    P, ps, Hkv, D = 7, 4, 2, 8
+    g = torch.Generator().manual_seed(5)
+    kp = torch.randn(P, ps, Hkv, D, generator=g).to(torch.bfloat16)
+    vp = torch.randn(P, ps, Hkv, D, generator=g).to(torch.bfloat16)
+    bt = torch.tensor([[5, 2, 6], [3, -1, -1]], dtype=torch.int32)
+    kn = torch.randn(4, Hkv, D, generator=g).to(torch.bfloat16)
+    vn = torch.randn(4, Hkv, D, generator=g).to(torch.bfloat16)
+    k2, v2 = orc.kv_append(kp, vp, bt, kn, vn, torch.tensor([0, 3, 4], dtype=torch.int32),
+                           torch.tensor([6, 0], dtype=torch.int32))
+    placed = [(2, 2, 0), (2, 3, 1), (6, 0, 2), (3, 0, 3)]   # (page, slot, new row)
+    for page, slot, i in placed:
+        assert torch.equal(k2[page, slot], kn[i]) and torch.equal(v2[page, slot], vn[i])
+    touched = torch.zeros(P, ps, dtype=torch.bool)
+    for page, slot, _ in placed:
+        touched[page, slot] = True
+    assert torch.equal(k2[~touched], kp[~touched]) and torch.equal(v2[~touched], vp[~touched])
+
+
+@pytest.mark.parametrize("layout", ["page_slot_head", "page_head_slot"])
+def test_kv_append_reads_back_through_block_table(orc, layout):
+    """After appending n_b rows at position c_b, the tokens c_b .. c_b+n_b of
+    each sequence, gathered with plain indexing, are the new rows; all other
+    pool bytes are unchanged."""
+    case = workloads.paged_decode_case(71, 5, 8, 2, 64, [37, 0, 16, 100, 3], 16, layout=layout)
+    g = torch.Generator().manual_seed(72)
+    ctx = [5, 0, 16, 60, 0]
+    new = [int(n) - c for n, c in zip(case["kv_lens"].tolist(), ctx)]
+    indptr = torch.tensor([0] + list(torch.tensor(new).cumsum(0).tolist()), dtype=torch.int32)
+    N = int(indptr[-1])
+    kn = torch.randn(N, 2, 64, generator=g).to(torch.bfloat16)
+    vn = torch.randn(N, 2, 64, generator=g).to(torch.bfloat16)
+    k2, v2 = orc.kv_append(case["k_pool"], case["v_pool"], case["block_table"], kn, vn, indptr,
+                           torch.tensor(ctx, dtype=torch.int32))
+    assert k2.stride() == case["k_pool"].stride()
+    written = torch.zeros(k2.shape[0], k2.shape[1], dtype=torch.bool)
+    for b in range(5):
+        seq_k = dense_kv(k2, case["block_table"][b], ctx[b] + new[b], 16)[ctx[b]:]
+        seq_v = dense_kv(v2, case["block_table"][b], ctx[b] + new[b], 16)[ctx[b]:]
+        assert torch.equal(seq_k, kn[indptr[b]:indptr[b + 1]])
+        assert torch.equal(seq_v, vn[indptr[b]:indptr[b + 1]])
+        for j in range(ctx[b], ctx[b] + new[b]):
+            written[int(case["block_table"][b][j // 16]), j % 16] = True
+    assert torch.equal(k2[~written], case["k_pool"][~written])
+    assert torch.equal(v2[~written], case["v_pool"][~written])
+
+
+# ---------------------------------------------------------------- rotary
+def rope_tables(rows, D, base=10000.0):
+    i = torch.arange(D // 2, dtype=torch.float64)
+    theta = base ** (-2.0 * i / D)
+    ang = torch.arange(rows, dtype=torch.float64)[:, None] * theta[None, :]
+    return ang.cos().float(), ang.sin().float(), ang
+
+
+def test_rotary_matches_numpy_complex_product(orc):
+    """The pages' fallback: view adjacent pairs as complex numbers and
+    multiply by cos + i sin.  numpy complex128 here, rounded to bf16."""
+    import numpy as np
+    T, H, D = 9, 3, 64
+    g = torch.Generator().manual_seed(80)
+    x = torch.randn(T, H, D, generator=g).to(torch.bfloat16)
+    cos, sin, _ = rope_tables(50, D)
+    pos = torch.tensor([0, 1, 2, 7, 49, 13, 13, 30, 5], dtype=torch.int32)
+    out = orc.rotary(x, cos, sin, pos)
+    xc = x.double().numpy().reshape(T, H, D // 2, 2)
+    z = xc[..., 0] + 1j * xc[..., 1]
+    w = (cos.double().numpy() + 1j * sin.double().numpy())[pos.numpy()][:, None, :]
+    r = z * w
+    ref = torch.from_numpy(np.stack([r.real, r.imag], -1).reshape(T, H, D)).to(torch.bfloat16)
+    diff = (out.double() - ref.double()).abs()
+    # both are one rounding of (nearly) the same product: at most one bf16 step apart
+    assert float((diff / ref.double().abs().clamp_min(1e-30)).max()) <= 2 ** -7
+    assert (out == ref).float().mean() > 0.99
+
+
+def test_rotary_identity_at_angle_zero_and_pair_norms(orc):
+    T, H, D = 6, 2, 32
+    g = torch.Generator().manual_seed(81)
+    x = torch.randn(T, H, D, generator=g).to(torch.bfloat16)
+    cos, sin, _ = rope_tables(20, D)
+    assert torch.equal(orc.rotary(x, cos, sin, torch.zeros(T, dtype=torch.int32)), x)
+    out = orc.rotary(x, cos, sin, torch.arange(T, dtype=torch.int32) * 3).double()
+    n_in = x.double().reshape(T, H, D // 2, 2).pow(2).sum(-1).sqrt()
+    n_out = out.reshape(T, H, D // 2, 2).pow(2).sum(-1).sqrt()
+    assert torch.allclose(n_in, n_out, rtol=2 ** -7, atol=1e-6)
+
+
+def test_rotary_dot_products_depend_on_relative_position(orc):
+    """(R_m q) . (R_n k) depends on n - m only (the property rotary
+    embeddings are built for): shifting both positions leaves it unchanged."""
+    D = 64
+    g = torch.Generator().manual_seed(82)
+    q = torch.randn(1, 1, D, generator=g).to(torch.bfloat16)
+    k = torch.randn(1, 1, D, generator=g).to(torch.bfloat16)
+    cos, sin, _ = rope_tables(200, D)
+    def dot(m, n):
+        a = orc.rotary(q, cos, sin, torch.tensor([m], dtype=torch.int32)).double()
+        b = orc.rotary(k, cos, sin, torch.tensor([n], dtype=torch.int32)).double()
+        return float((a * b).sum())
+    scale = float(q.double().norm() * k.double().norm())
+    for m, n, d in [(3, 10, 50), (0, 7, 100), (40, 41, 120)]:
+        assert abs(dot(m, n) - dot(m + d, n + d)) <= 2 ** -6 * scale
+
+
+# ------------------------------------------------------ fp8 quantize-on-write
+def test_fp8_quantize_matches_torch_cast(orc):
+    """Codes = torch's float8_e4m3fn cast (round to nearest even) of the
+    binary32 product, after clamping to +-448 (the saturating reading)."""
+    N, HD = 16, 512
+    g = torch.Generator().manual_seed(90)
+    x = (torch.randn(N, HD, generator=g) * torch.logspace(-3, 2, N)[:, None]).to(torch.bfloat16)
+    mult = torch.logspace(-1, 3, N).float()
+    codes, inv, amax = orc.fp8_quantize(x, mult)
+    prod = x.float() * mult[:, None]
+    ref = prod.clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+    assert torch.equal(codes, ref)
+    assert torch.equal(inv, (1.0 / mult).to(torch.bfloat16))
+    assert torch.equal(amax, x.float().abs().amax(1))
+
+
+def test_fp8_quantize_dynamic_scale_and_round_trip(orc):
+    """mult = 448 / amax: the largest magnitude of a row maps to 448 (code
+    0x7E / 0xFE); values that are e4m3 codes times 1/m come back exactly."""
+    N, HD = 8, 512
+    g = torch.Generator().manual_seed(91)
+    x = torch.randn(N, HD, generator=g).to(torch.bfloat16)
+    codes, inv, amax = orc.fp8_quantize(x)
+    arg = x.float().abs().argmax(1)
+    for n in range(N):
+        assert int(codes[n, arg[n]]) & 0x7F == 0x7E
+    m = (448.0 / amax)
+    assert torch.equal(inv, (1.0 / m).to(torch.bfloat16))
+    # exact round trip: representable codes scaled by a power of two
+    vals = torch.tensor([orc.e4m3fn_to_f64(c) for c in range(0x7F)], dtype=torch.float64)
+    y = torch.cat([vals, -vals])[:HD].reshape(1, -1) / 4.0      # exact in bf16
+    yb = y.to(torch.bfloat16)
+    assert torch.equal(yb.double(), y)
+    c2, _, _ = orc.fp8_quantize(yb, torch.tensor([4.0]))
+    back = torch.tensor([orc.e4m3fn_to_f64(int(c)) for c in c2[0]], dtype=torch.float64) / 4.0
+    assert torch.equal(back, y[0])
+
+
+def test_fp8_quantize_saturates_and_keeps_signed_zero(orc):
+    x = torch.tensor([[1000.0, -1000.0, 449.0, 464.0, -0.0, 0.0, 1e-4, -1e-4] + [0.0] * 8]).to(torch.bfloat16)
+    codes, _, _ = orc.fp8_quantize(x, torch.tensor([1.0]))
+    assert codes[0, :8].tolist() == [0x7E, 0xFE, 0x7E, 0x7E, 0x80, 0x00, 0x00, 0x80]
+
+
+def test_fp8_quantize_ties_go_to_even_code(orc):
+    """Every midpoint between two adjacent finite e4m3 magnitudes (exact in
+    bf16) rounds to the code with an even mantissa, as torch's cast does."""
+    vals = [orc.e4m3fn_to_f64(c) for c in range(0x7F)]
+    mids = [(vals[c] + vals[c + 1]) / 2 for c in range(0x7E)]
+    x = torch.tensor(mids + [-m for m in mids], dtype=torch.float64)
+    assert torch.equal(x.to(torch.bfloat16).double(), x)          # exact in bf16
+    pad = 512 - x.numel()
+    xb = torch.cat([x, torch.zeros(pad, dtype=torch.float64)]).to(torch.bfloat16).reshape(1, -1)
+    codes, _, _ = orc.fp8_quantize(xb, torch.tensor([1.0]))
+    got = codes[0, :x.numel()]
+    for i, c in enumerate(got.tolist()):
+        assert (c & 1) == 0, (float(x[i]), hex(c))
+    assert torch.equal(got, x.float().to(torch.float8_e4m3fn).view(torch.uint8))
+
+
+def test_fp8_quantize_decides_on_the_binary32_product(orc):
+    """The code is chosen from the product rounded to binary32 (the precision
+    the kernel decides in): a product just above the 1.0 / 1.125 midpoint
+    that rounds onto it in binary32 gives the even code 1.0 (0x38), whereas
+    rounding the exact product would give 1.125 (0x39)."""
+    import numpy as np
+    found = None
+    for xi in range(1, 128):
+        x = 1.0 + xi / 128.0                                   # bf16-exact
+        m0 = np.float32(1.0625 / x)
+        for k in range(-8, 9):
+            m = np.nextafter(m0, np.float32(np.inf if k > 0 else -np.inf), dtype=np.float32)
+            m = np.float32(m0 + (m - m0) * abs(k)) if k else m0
+            exact = x * float(m)                               # exact in double (24 x 8 bits)
+            if exact > 1.0625 and np.float32(x) * m == np.float32(1.0625):
+                found = (x, m)
+                break
+        if found:
+            break
+    assert found is not None
+    x, m = found
+    xb = torch.tensor([[x] + [0.0] * 511], dtype=torch.float64).to(torch.bfloat16)
+    codes, _, _ = orc.fp8_quantize(xb, torch.tensor([float(m)], dtype=torch.float32))
+    assert int(codes[0, 0]) == 0x38
