@@ -270,6 +270,72 @@ int attn_swa_fp8_decode(const void *q, int64_t q_st, int64_t q_sh,
                         int T, int NH, int HD, int window, int block_size, int num_blocks,
                         float scale, void *stream);
 
+/* --------------------------------------------- cache writes and rotary */
+
+/*
+ * Paged KV append: the cache write that precedes paged decode and prefill
+ * (AstrAI "CUDA Kernels" doc, Backend Layer: the attention backend owns the
+ * KV cache writes).
+ *   k_new, v_new  packed new rows [num_new, Hkv, D] bf16: row i, head g at
+ *          + i*n_st + g*n_sh (same strides for both)
+ *   new_indptr    device int32 [B + 1]: sequence b owns new rows
+ *          new_indptr[b] .. new_indptr[b+1]
+ *   start_pos     device int32 [B]: position of sequence b's first new token
+ *          (its length before the append)
+ *   k_pool, v_pool, kv_s_*, block_table, bt_sb, page_size  as in
+ *          attn_paged_decode; num_pages = pages in the pool
+ * New token i of sequence b is written to position start_pos[b] + i, i.e.
+ * page block_table[b][pos / page_size], slot pos % page_size, as an exact
+ * copy.  A token whose block-table entry is negative or >= num_pages is not
+ * written.  The block table must cover the new positions.  Supported: D a
+ * multiple of 8, 16-byte aligned rows.
+ */
+int attn_paged_kv_append(const void *k_new, const void *v_new, int64_t n_st, int64_t n_sh,
+                         const int32_t *new_indptr, const int32_t *start_pos, int num_new,
+                         void *k_pool, void *v_pool, int64_t kv_s_page, int64_t kv_s_slot, int64_t kv_s_head,
+                         int num_pages, const int32_t *block_table, int64_t bt_sb,
+                         int B, int Hkv, int D, int page_size, void *stream);
+
+/*
+ * fp8 quantize-on-write of sliding-window cache rows (native_swa_decode.py:
+ * the cache holds OCP e4m3fn codes and a bf16 inverse scale per slot;
+ * AstrAI "CUDA Kernels" doc, FP8 section: quantize takes the quantization
+ * multiplier and multiplies by it, amax is reported in the input domain).
+ *   x         [N, HD] bf16, row n at x + n*x_st
+ *   slots     device int64 [N]: cache slot of row n (block = slot / block_size,
+ *             offset = slot % block_size, as in attn_swa_fp8_decode)
+ *   multiplier  device float [N], or NULL for 448 / amax of the row (1 when
+ *             the row is all zeros)
+ *   kv_cache, c_sb, c_ss, inv_scale, s_ss  as in attn_swa_fp8_decode
+ *   amax_out  device float [N] (max |x| of each row), or NULL
+ * Row n's codes are e4m3fn(x * m): the product in binary32, rounded to the
+ * nearest code with ties to even, magnitudes >= 448 saturated to 448, the
+ * sign kept (-0 gives 0x80), NaN giving 0x7F; the slot's inverse scale is
+ * bf16(1 / m) (nearest-even), so decode dequantises code * inv_scale.  A row
+ * whose slot is negative or >= num_blocks*block_size is not written (its
+ * amax is still reported).  Supported: HD = 512.
+ */
+int attn_swa_fp8_append(const void *x, int64_t x_st, const int64_t *slots, const float *multiplier, int N, int HD,
+                        uint8_t *kv_cache, int64_t c_sb, int64_t c_ss, void *inv_scale, int64_t s_ss,
+                        int block_size, int num_blocks, float *amax_out, void *stream);
+
+/*
+ * Rotary embedding (AstrAI "CUDA Kernels" doc, Rotary Embedding Kernel: a
+ * fused cos/sin lookup and rotation; Rotary Backend: the fallback multiplies
+ * adjacent pairs, viewed as complex numbers, by the table's cos + i sin).
+ *   x, out     [T, H, D] bf16 (out may be x: in place)
+ *   cos_table, sin_table  fp32 [table_rows, D/2], row p at + p*tab_st
+ *   positions  device int32 [T]: table row of token t
+ * out[t, h, 2i] = x[2i] cos - x[2i+1] sin, out[t, h, 2i+1] = x[2i] sin +
+ * x[2i+1] cos with (cos, sin) = table row positions[t], column i; the math is
+ * fp32 and each output is rounded to bf16 once.  Tokens whose position is
+ * outside [0, table_rows) are left untouched.  Supported: D a multiple of 8,
+ * 16-byte aligned rows, tab_st a multiple of 4.
+ */
+int attn_rotary_embed(const void *x, int64_t x_st, int64_t x_sh, void *out, int64_t o_st, int64_t o_sh,
+                      int T, int H, int D, const float *cos_table, const float *sin_table, int64_t tab_st,
+                      int table_rows, const int32_t *positions, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

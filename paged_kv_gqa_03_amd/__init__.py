@@ -16,6 +16,7 @@ __all__ = [
     "attn_decode_workspace_bytes", "attn_decode", "attn_paged_decode", "attn_paged_decode_split",
     "attn_decode_combine", "attn_split_combine",
     "attn_prefill_plan", "attn_prefill_tile_rows", "attn_paged_prefill", "attn_swa_fp8_decode",
+    "attn_paged_kv_append", "attn_swa_fp8_append", "attn_rotary_embed",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -48,6 +49,10 @@ _SIGS = {
                             _P, _I, _L, _L, _P, _L, _L, _I, _I, _I, _I, _I, _F, _P], _I),
     "attn_swa_fp8_decode": ([_P, _L, _L, _P, _L, _L, _P, _L, _P, _L, _P, _P, _L, _L,
                              _I, _I, _I, _I, _I, _I, _F, _P], _I),
+    "attn_paged_kv_append": ([_P, _P, _L, _L, _P, _P, _I, _P, _P, _L, _L, _L, _I, _P, _L,
+                              _I, _I, _I, _I, _P], _I),
+    "attn_swa_fp8_append": ([_P, _L, _P, _P, _I, _I, _P, _L, _L, _P, _L, _I, _I, _P, _P], _I),
+    "attn_rotary_embed": ([_P, _L, _L, _P, _L, _L, _I, _I, _I, _P, _P, _L, _I, _P, _P], _I),
 }
 EXPORTED_SYMBOLS = tuple(_SIGS)
 
@@ -264,4 +269,45 @@ def attn_swa_fp8_decode(q, kv_cache, inv_scale, swa_indices, swa_lens, out, bloc
         _ptr(inv_scale), inv_scale.stride(0), _ptr(swa_indices), swa_indices.stride(0), _ptr(swa_lens),
         _ptr(out), out.stride(0), out.stride(1), T, NH, HD, W, int(block_size), num_blocks,
         float(scale), _stream(stream)))
+    return out
+
+
+def attn_paged_kv_append(k_new, v_new, new_indptr, start_pos, k_pool, v_pool, block_table, page_size,
+                         stream=None):
+    """k_new / v_new packed [N, Hkv, D] bf16 (identical strides); new_indptr
+    int32 [B + 1], start_pos int32 [B] on the device; pools are the 4-D
+    (page, slot, head, dim) views of attn_paged_decode."""
+    _unit_inner(k_new, v_new, k_pool, v_pool, block_table)
+    assert k_new.stride() == v_new.stride() and k_pool.stride() == v_pool.stride()
+    N, Hkv, D = k_new.shape
+    _check(lib().attn_paged_kv_append(
+        _ptr(k_new), _ptr(v_new), k_new.stride(0), k_new.stride(1), _ptr(new_indptr), _ptr(start_pos), N,
+        _ptr(k_pool), _ptr(v_pool), k_pool.stride(0), k_pool.stride(1), k_pool.stride(2), k_pool.shape[0],
+        _ptr(block_table), block_table.stride(0), new_indptr.numel() - 1, Hkv, D, int(page_size),
+        _stream(stream)))
+
+
+def attn_swa_fp8_append(x, slots, kv_cache, inv_scale, block_size, multiplier=None, amax=None, stream=None):
+    """x [N, HD] bf16; slots int64 [N]; kv_cache [num_blocks, block_size, HD]
+    uint8; inv_scale [slots, 1] bf16; multiplier float32 [N] or None;
+    amax float32 [N] output or None."""
+    _unit_inner(x, kv_cache)
+    N, HD = x.shape
+    _check(lib().attn_swa_fp8_append(
+        _ptr(x), x.stride(0), _ptr(slots), _ptr(multiplier), N, HD, _ptr(kv_cache), kv_cache.stride(0),
+        kv_cache.stride(1), _ptr(inv_scale), inv_scale.stride(0), int(block_size), kv_cache.shape[0],
+        _ptr(amax), _stream(stream)))
+
+
+def attn_rotary_embed(x, cos_table, sin_table, positions, out=None, stream=None):
+    """x [T, H, D] bf16; cos_table / sin_table float32 [rows, D/2];
+    positions int32 [T].  Writes out (default: x, in place) and returns it."""
+    out = x if out is None else out
+    _unit_inner(x, out, cos_table, sin_table)
+    assert cos_table.stride() == sin_table.stride()
+    T, H, D = x.shape
+    _check(lib().attn_rotary_embed(
+        _ptr(x), x.stride(0), x.stride(1), _ptr(out), out.stride(0), out.stride(1), T, H, D,
+        _ptr(cos_table), _ptr(sin_table), cos_table.stride(0), cos_table.shape[0], _ptr(positions),
+        _stream(stream)))
     return out

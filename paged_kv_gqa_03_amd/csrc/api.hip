@@ -466,4 +466,84 @@ int attn_swa_fp8_decode(const void *q, int64_t q_st, int64_t q_sh,
     return launch_status(pa::launch_swa(p, static_cast<hipStream_t>(stream)), "swa kernel");
 }
 
+int attn_paged_kv_append(const void *k_new, const void *v_new, int64_t n_st, int64_t n_sh,
+                         const int32_t *new_indptr, const int32_t *start_pos, int num_new,
+                         void *k_pool, void *v_pool, int64_t kv_s_page, int64_t kv_s_slot, int64_t kv_s_head,
+                         int num_pages, const int32_t *block_table, int64_t bt_sb,
+                         int B, int Hkv, int D, int page_size, void *stream) {
+    if (B < 0 || num_new < 0 || Hkv <= 0 || D <= 0 || page_size <= 0 || num_pages < 0)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_paged_kv_append: bad sizes");
+    if (D % 8 != 0) return fail(ATTN_ERR_UNSUPPORTED, "attn_paged_kv_append: D=%d is not a multiple of 8", D);
+    if (num_new == 0 || B == 0) return ok();
+    if (!k_new || !v_new || !new_indptr || !start_pos || !k_pool || !v_pool || !block_table)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_paged_kv_append: null pointer");
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool) || !mult8(n_st) ||
+        !mult8(n_sh) || !mult8(kv_s_page) || !mult8(kv_s_slot) || !mult8(kv_s_head))
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_paged_kv_append: rows must be 16-byte aligned");
+    if (n_st < 0 || n_sh < 0 || kv_s_page < 0 || kv_s_slot < 0 || kv_s_head < 0 || bt_sb < 0)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_paged_kv_append: negative stride");
+    pa::KvAppendParams p{};
+    p.k_new = static_cast<const uint16_t *>(k_new);
+    p.v_new = static_cast<const uint16_t *>(v_new);
+    p.n_st = n_st; p.n_sh = n_sh;
+    p.indptr = new_indptr; p.start_pos = start_pos;
+    p.k_pool = static_cast<uint16_t *>(k_pool);
+    p.v_pool = static_cast<uint16_t *>(v_pool);
+    p.s_page = kv_s_page; p.s_slot = kv_s_slot; p.s_head = kv_s_head;
+    p.bt = block_table; p.bt_sb = bt_sb;
+    p.B = B; p.Hkv = Hkv; p.D = D; p.ps = page_size; p.N = num_new; p.num_pages = num_pages;
+    return launch_status(pa::launch_kv_append(p, static_cast<hipStream_t>(stream)), "kv append kernel");
+}
+
+int attn_swa_fp8_append(const void *x, int64_t x_st, const int64_t *slots, const float *multiplier, int N, int HD,
+                        uint8_t *kv_cache, int64_t c_sb, int64_t c_ss, void *inv_scale, int64_t s_ss,
+                        int block_size, int num_blocks, float *amax_out, void *stream) {
+    if (N < 0 || block_size <= 0 || num_blocks < 0)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_swa_fp8_append: bad sizes");
+    if (HD != 512) return fail(ATTN_ERR_UNSUPPORTED, "attn_swa_fp8_append: head dim %d not built (512)", HD);
+    if ((int64_t)num_blocks * block_size >= (1ll << 31))
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_swa_fp8_append: num_blocks * block_size must stay below 2^31 slots");
+    if (N == 0) return ok();
+    if (!x || !slots || !kv_cache || !inv_scale)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_swa_fp8_append: null pointer");
+    if (!aligned16(x) || !mult8(x_st) || !aligned16(kv_cache) || (c_sb & 15) || (c_ss & 15) ||
+        ((uintptr_t)inv_scale & 1u))
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_swa_fp8_append: x rows and cache rows must be 16-byte aligned");
+    if (x_st < 0 || c_sb < 0 || c_ss < 0 || s_ss < 0)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_swa_fp8_append: negative stride");
+    pa::SwaQuantParams p{};
+    p.x = static_cast<const uint16_t *>(x); p.x_st = x_st;
+    p.slots = slots; p.mult = multiplier;
+    p.cache = kv_cache; p.c_sb = c_sb; p.c_ss = c_ss;
+    p.inv_scale = static_cast<uint16_t *>(inv_scale); p.s_ss = s_ss;
+    p.amax = amax_out;
+    p.N = N; p.bs = block_size;
+    p.num_slots = (int64_t)num_blocks * block_size;
+    p.bs_magic = ((1ull << 32) + (uint64_t)block_size - 1) / (uint64_t)block_size;
+    return launch_status(pa::launch_swa_quantize(p, static_cast<hipStream_t>(stream)), "swa quantize kernel");
+}
+
+int attn_rotary_embed(const void *x, int64_t x_st, int64_t x_sh, void *out, int64_t o_st, int64_t o_sh,
+                      int T, int H, int D, const float *cos_table, const float *sin_table, int64_t tab_st,
+                      int table_rows, const int32_t *positions, void *stream) {
+    if (T < 0 || H <= 0 || D <= 0 || table_rows < 0)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_rotary_embed: bad sizes");
+    if (D % 8 != 0) return fail(ATTN_ERR_UNSUPPORTED, "attn_rotary_embed: D=%d is not a multiple of 8", D);
+    if ((int64_t)T * H * (D / 8) >= (1ll << 40)) return fail(ATTN_ERR_UNSUPPORTED, "attn_rotary_embed: too large");
+    if (T == 0) return ok();
+    if (!x || !out || !cos_table || !sin_table || !positions)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_rotary_embed: null pointer");
+    if (!aligned16(x) || !aligned16(out) || !mult8(x_st) || !mult8(x_sh) || !mult8(o_st) || !mult8(o_sh) ||
+        !aligned16(cos_table) || !aligned16(sin_table) || (tab_st & 3))
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_rotary_embed: rows must be 16-byte aligned");
+    if (tab_st < D / 2) return fail(ATTN_ERR_INVALID_ARG, "attn_rotary_embed: table stride below D/2");
+    pa::RotaryParams p{};
+    p.x = static_cast<const uint16_t *>(x); p.x_st = x_st; p.x_sh = x_sh;
+    p.out = static_cast<uint16_t *>(out); p.o_st = o_st; p.o_sh = o_sh;
+    p.cos = cos_table; p.sin = sin_table; p.tab_st = tab_st;
+    p.pos = positions;
+    p.T = T; p.H = H; p.D = D; p.rows = table_rows;
+    return launch_status(pa::launch_rotary(p, static_cast<hipStream_t>(stream)), "rotary kernel");
+}
+
 }  // extern "C"

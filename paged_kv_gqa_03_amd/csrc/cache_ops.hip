@@ -1,0 +1,178 @@
+// cache_ops.hip -- the cache writes and the rotation that precede attention,
+// for gfx950: paged KV append, fp8 quantize-on-write of sliding-window cache
+// rows, and rotary embedding.  All three are HBM-bound streams of 16-byte
+// vector loads and stores.
+//
+// Method:
+//   - paged KV append (AstrAI "CUDA Kernels" doc, Backend Layer: the
+//     attention backend owns the KV cache writes that precede paged decode
+//     and prefill): new token i of sequence b lands at position
+//     start_pos[b] + i, i.e. page bt[b][pos / ps], slot pos % ps;
+//   - fp8 quantize-on-write (native_swa_decode.py: the cache holds OCP
+//     e4m3fn codes plus a per-slot inverse scale; AstrAI doc, FP8 section:
+//     quantize takes the multiplier and multiplies by it, amax is reported
+//     in the input domain): code = e4m3fn(x * m) rounded to nearest even and
+//     saturated at 448, the product taken in binary32; the slot's inverse
+//     scale is bf16(1 / m); m = 448 / amax when the caller gives none;
+//   - rotary (AstrAI doc, Rotary Embedding Kernel and Rotary Backend): the
+//     cos / sin rows of the token's position are looked up in fp32 tables
+//     and each adjacent pair (x[2i], x[2i+1]) is multiplied, as a complex
+//     number, by cos_i + i sin_i; the math is fp32 and the result is rounded
+//     to bf16 once.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace pa {
+
+namespace {
+
+__device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
+__device__ __forceinline__ void st16(void *p, uint4 v) { *reinterpret_cast<uint4 *>(p) = v; }
+
+// ------------------------------------------------------------ KV append
+
+// One workgroup per new row: the row's sequence comes from a search of the
+// indptr (uniform, scalar loads), then its K and V chunks are copied.
+__global__ __launch_bounds__(256) void kv_append_kernel(const KvAppendParams p) {
+    const int i = blockIdx.x;
+    int lo = 0, hi = p.B;   // first b with indptr[b + 1] > i
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (p.indptr[mid + 1] > i) hi = mid;
+        else lo = mid + 1;
+    }
+    const int b = lo;
+    if (b >= p.B) return;
+    const int64_t pos = (int64_t)p.start_pos[b] + (i - p.indptr[b]);
+    if (pos < 0) return;
+    const int32_t page = p.bt[(int64_t)b * p.bt_sb + pos / p.ps];
+    if (page < 0 || page >= p.num_pages) return;   // not a page of the pool: nothing is written
+    const int64_t base = (int64_t)page * p.s_page + (pos % p.ps) * p.s_slot;
+    const int cpr = p.D / 8;                         // 16-byte chunks per head row
+    const int C = p.Hkv * cpr;                        // chunks per tensor row
+    for (int c = threadIdx.x; c < 2 * C; c += blockDim.x) {
+        const bool is_v = c >= C;
+        const int cc = is_v ? c - C : c;
+        const int g = cc / cpr, d = (cc - g * cpr) * 8;
+        const uint16_t *src = (is_v ? p.v_new : p.k_new) + (int64_t)i * p.n_st + (int64_t)g * p.n_sh + d;
+        uint16_t *dst = (is_v ? p.v_pool : p.k_pool) + base + (int64_t)g * p.s_head + d;
+        st16(dst, ld16(src));
+    }
+}
+
+// ------------------------------------------------- fp8 quantize-on-write
+
+// Nearest OCP e4m3fn code of a binary32 value, from the format's definition:
+// sign bit kept, magnitudes >= 448 saturate to 448 (0x7E), NaN gives 0x7F;
+// normals keep 3 mantissa bits rounded to nearest even (a carry moves to the
+// next binade); below 2^-6 the value is a multiple of 2^-9, rounded to
+// nearest even (8 * 2^-9 is the smallest normal, code 0x08, the same bits).
+__device__ __forceinline__ uint32_t e4m3fn_code(float v) {
+    const uint32_t u = __float_as_uint(v);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7fffffffu;
+    if (a > 0x7f800000u) return 0x7Fu;
+    const float af = __uint_as_float(a);
+    if (af >= 448.0f) return sign | 0x7Eu;
+    if (af < 0.015625f) return sign | (uint32_t)rintf(af * 512.0f);
+    int e = (int)(a >> 23) - 127;
+    uint32_t q = (a >> 20) & 7u;
+    const uint32_t rem = a & 0xfffffu;
+    q += (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) ? 1u : 0u;
+    if (q == 8u) {
+        q = 0u;
+        ++e;
+    }
+    return sign | ((uint32_t)(e + 7) << 3) | q;
+}
+
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7f800000u) == 0x7f800000u) return (uint16_t)(u >> 16);
+    return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+// One wave per row of HD = 512: lane l holds elements 8l .. 8l+7.
+__global__ __launch_bounds__(256) void swa_quantize_kernel(const SwaQuantParams p) {
+    const int lane = threadIdx.x & 63;
+    const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (n >= p.N) return;
+    const uint4 raw = ld16(p.x + (int64_t)n * p.x_st + 8 * lane);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        v[2 * k] = bf16_lo(w[k]);
+        v[2 * k + 1] = bf16_hi(w[k]);
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(v[k]));
+#pragma unroll
+    for (int s = 1; s < 64; s <<= 1) amax = fmaxf(amax, __shfl_xor(amax, s));
+    const float m = p.mult ? p.mult[n] : (amax > 0.f ? 448.0f / amax : 1.0f);
+    if (lane == 0 && p.amax) p.amax[n] = amax;
+    const int64_t slot = p.slots[n];
+    if (slot < 0 || slot >= p.num_slots) return;   // not a slot of the cache: nothing is written
+    const uint32_t blk = udiv_magic((uint32_t)slot, p.bs_magic);
+    const uint32_t off = (uint32_t)slot - blk * (uint32_t)p.bs;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) lo |= e4m3fn_code(v[k] * m) << (8 * k);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) hi |= e4m3fn_code(v[4 + k] * m) << (8 * k);
+    *reinterpret_cast<uint2 *>(p.cache + (int64_t)blk * p.c_sb + (int64_t)off * p.c_ss + 8 * lane) =
+        make_uint2(lo, hi);
+    if (lane == 0) p.inv_scale[slot * p.s_ss] = bf16_rne(1.0f / m);
+}
+
+// ------------------------------------------------------------- rotary
+
+// One thread per 16 bytes (four pairs) of a head row.
+__global__ __launch_bounds__(256) void rotary_kernel(const RotaryParams p) {
+    const int cpr = p.D / 8;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (int64_t)p.T * p.H * cpr) return;
+    const int c = (int)(idx % cpr);
+    const int64_t th = idx / cpr;
+    const int h = (int)(th % p.H), t = (int)(th / p.H);
+    const int pos = p.pos[t];
+    if (pos < 0 || pos >= p.rows) return;          // outside the table: the row is left as it is
+    const uint4 raw = ld16(p.x + (int64_t)t * p.x_st + (int64_t)h * p.x_sh + 8 * c);
+    const float4 cs = *reinterpret_cast<const float4 *>(p.cos + (int64_t)pos * p.tab_st + 4 * c);
+    const float4 sn = *reinterpret_cast<const float4 *>(p.sin + (int64_t)pos * p.tab_st + 4 * c);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    const float cv[4] = {cs.x, cs.y, cs.z, cs.w}, sv[4] = {sn.x, sn.y, sn.z, sn.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float a = bf16_lo(w[k]), b = bf16_hi(w[k]);
+        const float re = fmaf(a, cv[k], -b * sv[k]);
+        const float im = fmaf(a, sv[k], b * cv[k]);
+        o[k] = (uint32_t)bf16_rne(re) | ((uint32_t)bf16_rne(im) << 16);
+    }
+    st16(p.out + (int64_t)t * p.o_st + (int64_t)h * p.o_sh + 8 * c, make_uint4(o[0], o[1], o[2], o[3]));
+}
+
+}  // namespace
+
+hipError_t launch_kv_append(const KvAppendParams &p, hipStream_t stream) {
+    if (p.N <= 0) return hipSuccess;
+    hipLaunchKernelGGL(kv_append_kernel, dim3(p.N), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_swa_quantize(const SwaQuantParams &p, hipStream_t stream) {
+    if (p.N <= 0) return hipSuccess;
+    hipLaunchKernelGGL(swa_quantize_kernel, dim3((p.N + 3) / 4), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_rotary(const RotaryParams &p, hipStream_t stream) {
+    const int64_t n = (int64_t)p.T * p.H * (p.D / 8);
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(rotary_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace pa

@@ -108,8 +108,51 @@ struct SwaParams {
     float sl2;            // scale * log2(e)
 };
 
+// Paged KV append: packed new rows [N, Hkv, D] into their (page, slot).
+struct KvAppendParams {
+    const uint16_t *k_new, *v_new;
+    int64_t n_st, n_sh;
+    const int32_t *indptr, *start_pos;
+    uint16_t *k_pool, *v_pool;
+    int64_t s_page, s_slot, s_head;
+    const int32_t *bt;
+    int64_t bt_sb;
+    int B, Hkv, D, ps, N, num_pages;
+};
+
+// fp8 quantize-on-write of sliding-window cache rows (HD = 512).
+struct SwaQuantParams {
+    const uint16_t *x;
+    int64_t x_st;
+    const int64_t *slots;
+    const float *mult;     // NULL: 448 / amax per row
+    uint8_t *cache;
+    int64_t c_sb, c_ss;
+    uint16_t *inv_scale;
+    int64_t s_ss;
+    float *amax;           // NULL: not reported
+    int N, bs;
+    int64_t num_slots;
+    uint64_t bs_magic;
+};
+
+// Rotary embedding of x [T, H, D] by fp32 cos / sin tables at positions.
+struct RotaryParams {
+    const uint16_t *x;
+    int64_t x_st, x_sh;
+    uint16_t *out;
+    int64_t o_st, o_sh;
+    const float *cos, *sin;
+    int64_t tab_st;
+    const int32_t *pos;
+    int T, H, D, rows;
+};
+
 hipError_t launch_decode(const DecodeParams &p, int D, int G, bool paged, hipStream_t stream);
 hipError_t launch_swa(const SwaParams &p, hipStream_t stream);
+hipError_t launch_kv_append(const KvAppendParams &p, hipStream_t stream);
+hipError_t launch_swa_quantize(const SwaQuantParams &p, hipStream_t stream);
+hipError_t launch_rotary(const RotaryParams &p, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream);
 hipError_t launch_decode_combine(const DecodeCombineParams &p, int D, hipStream_t stream);
 hipError_t launch_combine(const CombineParams &p, int D, hipStream_t stream);
