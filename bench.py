@@ -301,6 +301,93 @@ def run_extras(torch, pa, dev, args):
     out["ragged_prefill"] = bench_prefill(torch, pa, dev, steps, warm, masked=False)
     out["ragged_prefill_masked"] = bench_prefill(torch, pa, dev, steps, warm, masked=True)
     out["swa_fp8"] = bench_swa(torch, pa, dev, steps, warm)
+    out.update(bench_cache_ops(torch, pa, dev, steps, warm))
+    return out
+
+
+def bench_cache_ops(torch, pa, dev, steps, warm):
+    """The cache writes and rotary that precede attention, HBM-bound: GB/s of
+    algorithmic bytes (every byte read or written once), R rotated sets."""
+    import workloads
+    out = {}
+    g = torch.Generator(device=dev)
+    g.manual_seed(1007)
+
+    def timed(fn, sets, nbytes):
+        # These kernels take a few microseconds, less than the host needs to
+        # issue a call from Python, so the calls are captured once in a HIP
+        # graph and the graph is replayed (as a serving loop would issue them).
+        st = torch.cuda.Stream()
+        with torch.cuda.stream(st):
+            for i in range(warm):
+                fn(sets[i % len(sets)])
+        st.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=st):
+            for i in range(steps):
+                fn(sets[i % len(sets)])
+        graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(3):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / (3 * steps)
+        return {"us_per_call": round(ms * 1e3, 2), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                "hbm_peak_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "bytes_per_call": int(nbytes),
+                "rotation_sets": len(sets), "timing": "HIP graph of %d calls, 3 replays" % steps}
+
+    # KV append: the ragged prefill's new tokens (8 sequences, U[1,512] each)
+    # and a decode step (one token for each of 128 sequences).
+    for name, B, ctx, q_range in (("kv_append_prefill_chunk", 8, (0, 2048), (1, 512)),
+                                  ("kv_append_decode_step", 128, (0, 512), (1, 1))):
+        sets = []
+        for r in range(4):
+            c = workloads.prefill_case(1008 + 7919 * r, B, 32, 8, 128, ctx, q_range, 16, device=dev)
+            N = int(c["qo_indptr"][-1])
+            c["kn"] = torch.randn(N, 8, 128, generator=g, device=dev).to(torch.bfloat16)
+            c["vn"] = torch.randn(N, 8, 128, generator=g, device=dev).to(torch.bfloat16)
+            c["start"] = torch.tensor(c["ctx_lens"], dtype=torch.int32, device=dev)
+            sets.append(c)
+        nb = sum(int(c["qo_indptr"][-1]) * 8 * 128 * 2 * 2 * 2 + (c["B"] + 1) * 8 for c in sets) / len(sets)
+
+        def fn(c):
+            pa.attn_paged_kv_append(c["kn"], c["vn"], c["qo_indptr"], c["start"], c["k_pool"], c["v_pool"],
+                                    c["block_table"], 16)
+        out[name] = timed(fn, sets, nb)
+    # fp8 quantize-on-write of 4096 sliding-window rows (HD 512) into a
+    # 32768-slot cache, dynamic scales.
+    sets = []
+    for r in range(4):
+        x = torch.randn(4096, 512, generator=g, device=dev).to(torch.bfloat16)
+        slots = torch.randperm(32768, generator=g, device=dev)[:4096]
+        cache = torch.zeros(128, 256, 512, dtype=torch.uint8, device=dev)
+        inv = torch.zeros(32768, 1, dtype=torch.bfloat16, device=dev)
+        amax = torch.empty(4096, device=dev)
+        sets.append(dict(x=x, slots=slots, cache=cache, inv=inv, amax=amax))
+    nb = 4096 * (512 * 2 + 512 + 8 + 2 + 4)
+
+    def fq(c):
+        pa.attn_swa_fp8_append(c["x"], c["slots"], c["cache"], c["inv"], 256, amax=c["amax"])
+    out["swa_fp8_append_4096_rows"] = timed(fq, sets, nb)
+    # Rotary on Q [T, 32, 128] and K [T, 8, 128] of the ragged prefill's
+    # tokens (T = 2052), positions up to 4096, in place.
+    ang = torch.arange(4096, device=dev, dtype=torch.float64)[:, None] * \
+        (10000.0 ** (-2.0 * torch.arange(64, device=dev, dtype=torch.float64) / 128))[None, :]
+    cos, sin = ang.cos().float(), ang.sin().float()
+    sets = []
+    for r in range(4):
+        sets.append(dict(q=torch.randn(2052, 32, 128, generator=g, device=dev).to(torch.bfloat16),
+                         k=torch.randn(2052, 8, 128, generator=g, device=dev).to(torch.bfloat16),
+                         pos=torch.randint(0, 4096, (2052,), generator=g, device=dev, dtype=torch.int32)))
+    nb = 2052 * (32 + 8) * 128 * 2 * 2 + 2 * 2052 * 64 * 4 * 2 + 2 * 2052 * 4
+
+    def fr(c):
+        pa.attn_rotary_embed(c["q"], cos, sin, c["pos"])
+        pa.attn_rotary_embed(c["k"], cos, sin, c["pos"])
+    out["rotary_q_and_k_2052_tokens"] = timed(fr, sets, nb)
     return out
 
 
