@@ -244,6 +244,31 @@ int attn_paged_prefill(const void *q, int64_t q_st, int64_t q_sh, const int32_t 
                        int B, int Hq, int Hkv, int D, int page_size, float scale,
                        void *stream);
 
+/*
+ * Dense prefill over a contiguous KV source (AstrAI "CUDA Kernels" doc:
+ * attention kernels combine a Q schedule, DenseQSchedule or PackedQSchedule,
+ * with a KV source, ContigKV or PagedKV; Python Wrappers interface note:
+ * is_causal and a 2-D [batch, kv] or 3-D [batch, q, kv] keep-mask).
+ *   q   [B, Lq, Hq, D] by strides: (b, i, h) at q + b*q_sb + i*q_sl + h*q_sh
+ *       (any of blhd / bhld)
+ *   k, v  [B, Lk, Hkv, D] by the same strides for both: (b, j, g) at
+ *       k + b*k_sb + j*k_sl + g*k_sh
+ *   kv_lens  device int32 [B] keys of each sequence, or NULL for kv_len
+ *   is_causal  nonzero: query row i of sequence b admits key j iff
+ *       j <= n_b - Lq + i (bottom-right alignment: the Lq queries are the
+ *       sequence's last Lq positions); rows that admit no key give zeros
+ *   mask, mask_ndim, m_sb, m_sq  as in attn_paged_prefill
+ *   o   [B, Lq, Hq, D] bf16: (b, i, h) at o + b*o_sb + i*o_sl + h*o_sh
+ * Same kernel and numerics as attn_paged_prefill; no work map is needed.
+ * Supported: D = 128, G in {1, 2, 4, 8}; alignment as attn_paged_prefill.
+ */
+int attn_prefill(const void *q, int64_t q_sb, int64_t q_sl, int64_t q_sh,
+                 const void *k, const void *v, int64_t k_sb, int64_t k_sl, int64_t k_sh,
+                 const int32_t *kv_lens, int kv_len, int is_causal,
+                 const uint8_t *mask, int mask_ndim, int64_t m_sb, int64_t m_sq,
+                 void *o, int64_t o_sb, int64_t o_sl, int64_t o_sh,
+                 int B, int Lq, int Hq, int Hkv, int D, float scale, void *stream);
+
 /* --------------------------------------------------- fp8 sliding window */
 
 /*

@@ -16,7 +16,7 @@ __all__ = [
     "attn_decode_workspace_bytes", "attn_decode", "attn_paged_decode", "attn_paged_decode_split",
     "attn_decode_combine", "attn_split_combine",
     "attn_prefill_plan", "attn_prefill_tile_rows", "attn_paged_prefill", "attn_swa_fp8_decode",
-    "attn_paged_kv_append", "attn_swa_fp8_append", "attn_rotary_embed",
+    "attn_prefill", "attn_paged_kv_append", "attn_swa_fp8_append", "attn_rotary_embed",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -49,6 +49,8 @@ _SIGS = {
                             _P, _I, _L, _L, _P, _L, _L, _I, _I, _I, _I, _I, _F, _P], _I),
     "attn_swa_fp8_decode": ([_P, _L, _L, _P, _L, _L, _P, _L, _P, _L, _P, _P, _L, _L,
                              _I, _I, _I, _I, _I, _I, _F, _P], _I),
+    "attn_prefill": ([_P, _L, _L, _L, _P, _P, _L, _L, _L, _P, _I, _I, _P, _I, _L, _L, _P, _L, _L, _L,
+                      _I, _I, _I, _I, _I, _F, _P], _I),
     "attn_paged_kv_append": ([_P, _P, _L, _L, _P, _P, _I, _P, _P, _L, _L, _L, _I, _P, _L,
                               _I, _I, _I, _I, _P], _I),
     "attn_swa_fp8_append": ([_P, _L, _P, _P, _I, _I, _P, _L, _L, _P, _L, _I, _I, _P, _P], _I),
@@ -310,4 +312,28 @@ def attn_rotary_embed(x, cos_table, sin_table, positions, out=None, stream=None)
         _ptr(x), x.stride(0), x.stride(1), _ptr(out), out.stride(0), out.stride(1), T, H, D,
         _ptr(cos_table), _ptr(sin_table), cos_table.stride(0), cos_table.shape[0], _ptr(positions),
         _stream(stream)))
+    return out
+
+
+def attn_prefill(q, k, v, out, scale, is_causal=False, kv_lens=None, mask=None, stream=None):
+    """Dense prefill, contiguous KV.  q / out are (b, i, h, d)-indexed views
+    [B, Lq, Hq, D] (any strides with unit innermost); k / v are (b, j, g, d)
+    views [B, Lk, Hkv, D] with identical strides; kv_lens int32 [B] or None
+    (all Lk); mask None, [B, Lk] or [B, Lq, Lk] keep-mask."""
+    _unit_inner(q, k, v, out)
+    assert k.stride() == v.stride(), "K and V must share strides"
+    B, Lq, Hq, D = q.shape
+    Lk, Hkv = k.shape[1], k.shape[2]
+    ndim, m_sb, m_sq = 0, 0, 0
+    if mask is not None:
+        if mask.dtype == torch.bool:
+            mask = mask.view(torch.uint8)
+        _unit_inner(mask)
+        ndim = mask.dim()
+        m_sb = mask.stride(0)
+        m_sq = mask.stride(1) if ndim == 3 else 0
+    _check(lib().attn_prefill(
+        _ptr(q), q.stride(0), q.stride(1), q.stride(2), _ptr(k), _ptr(v), k.stride(0), k.stride(1), k.stride(2),
+        _ptr(kv_lens), int(Lk), 1 if is_causal else 0, _ptr(mask), ndim, m_sb, m_sq,
+        _ptr(out), out.stride(0), out.stride(1), out.stride(2), B, Lq, Hq, Hkv, D, float(scale), _stream(stream)))
     return out

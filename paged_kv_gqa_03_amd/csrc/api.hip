@@ -428,6 +428,53 @@ int attn_paged_prefill(const void *q, int64_t q_st, int64_t q_sh, const int32_t 
     return launch_status(pa::launch_prefill(p, static_cast<hipStream_t>(stream)), "prefill kernel");
 }
 
+int attn_prefill(const void *q, int64_t q_sb, int64_t q_sl, int64_t q_sh,
+                 const void *k, const void *v, int64_t k_sb, int64_t k_sl, int64_t k_sh,
+                 const int32_t *kv_lens, int kv_len, int is_causal,
+                 const uint8_t *mask, int mask_ndim, int64_t m_sb, int64_t m_sq,
+                 void *o, int64_t o_sb, int64_t o_sl, int64_t o_sh,
+                 int B, int Lq, int Hq, int Hkv, int D, float scale, void *stream) {
+    int G = 0, rc = check_heads(Hq, Hkv, D, &G);
+    if (rc) return rc;
+    if (D != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill: head dim %d not built (128)", D);
+    if (B < 0 || Lq < 0 || kv_len < 0) return fail(ATTN_ERR_INVALID_ARG, "attn_prefill: negative size");
+    if (!q || !k || !v || !o) return fail(ATTN_ERR_INVALID_ARG, "attn_prefill: null pointer");
+    if (!std::isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "attn_prefill: scale is not finite");
+    if (mask && mask_ndim != 2 && mask_ndim != 3)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_prefill: mask_ndim must be 2 or 3");
+    if (mask && (((uintptr_t)mask & 3u) || (m_sb & 3) || (mask_ndim == 3 && (m_sq & 3)) || m_sb < 0 || m_sq < 0))
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill: mask rows must be 4-byte aligned");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || ((uintptr_t)o & 7u) || !mult8(q_sb) || !mult8(q_sl) ||
+        !mult8(q_sh) || !mult8(k_sb) || !mult8(k_sl) || !mult8(k_sh) || (o_sb & 3) || (o_sl & 3) || (o_sh & 3))
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill: q/k/v rows must be 16-byte and o rows 8-byte aligned");
+    if (q_sb < 0 || q_sl < 0 || q_sh < 0 || k_sb < 0 || k_sl < 0 || k_sh < 0 || o_sb < 0 || o_sl < 0 || o_sh < 0)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_prefill: negative stride");
+    const int R = 128 / pa::prefill_heads_packed(G);
+    const int64_t tiles = (int64_t)B * ((Lq + R - 1) / R);
+    if (tiles * Hkv * 2 >= (1ll << 31)) return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill: too many tiles for one grid");
+    if (B == 0 || Lq == 0) return ok();
+    pa::PrefillParams p{};
+    p.q = static_cast<const uint16_t *>(q);
+    p.q_sb = q_sb; p.q_st = q_sl; p.q_sh = q_sh;
+    p.num_tiles = (int)tiles;
+    p.dense_lq = Lq;
+    p.k = static_cast<const uint16_t *>(k);
+    p.v = static_cast<const uint16_t *>(v);
+    p.k_sb = k_sb; p.s_slot = k_sl; p.s_head = k_sh;
+    p.bt = nullptr;
+    p.ps = 1;
+    p.kv_lens = kv_lens; p.kv_len_const = kv_len;
+    p.causal = nullptr; p.causal_br = is_causal ? 1 : 0;
+    p.mask = mask;
+    p.mask_ndim = mask ? mask_ndim : 0;
+    p.m_sb = m_sb; p.m_sq = m_sq;
+    p.o = static_cast<uint16_t *>(o);
+    p.o_sb = o_sb; p.o_st = o_sl; p.o_sh = o_sh;
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.G = G;
+    p.sl2 = scale * 1.4426950408889634f;
+    return launch_status(pa::launch_prefill(p, static_cast<hipStream_t>(stream)), "prefill kernel");
+}
+
 int attn_swa_fp8_decode(const void *q, int64_t q_st, int64_t q_sh,
                         const uint8_t *kv_cache, int64_t c_sb, int64_t c_ss,
                         const void *inv_scale, int64_t s_ss,

@@ -63,24 +63,31 @@ struct CombineParams {
 };
 
 // Ragged paged prefill (work-map tiles x groups of packed query heads).
+// Prefill: packed ragged Q through a work map with a paged KV source, or the
+// dense schedule (dense_lq rows per sequence, batch strides q_sb / o_sb) with
+// a contiguous KV source (bt == NULL: key j of sequence b, head g at
+// b*k_sb + g*s_head + j*s_slot).
 struct PrefillParams {
     const uint16_t *q;
-    int64_t q_st, q_sh;
+    int64_t q_sb, q_st, q_sh;
     const int32_t *qo_indptr, *t2b, *t2i;
     int num_tiles;
+    int dense_lq;            // > 0: dense schedule, no work map
     const uint16_t *k, *v;
-    int64_t s_page, s_slot, s_head;
-    const int32_t *bt;
+    int64_t k_sb, s_page, s_slot, s_head;
+    const int32_t *bt;       // NULL: contiguous source
     int64_t bt_sb;
     uint32_t ps;
     uint64_t ps_magic;
-    const int32_t *kv_lens;
-    const int32_t *causal;   // NULL: no causality
+    const int32_t *kv_lens;  // NULL: kv_len_const for every sequence
+    int kv_len_const;
+    const int32_t *causal;   // causal offsets (-1 = off), or NULL
+    int causal_br;           // with causal NULL: bottom-right causality (c = n - Lq)
     const uint8_t *mask;     // NULL when mask_ndim == 0
     int mask_ndim;           // 0, 2 or 3
     int64_t m_sb, m_sq;
     uint16_t *o;
-    int64_t o_st, o_sh;
+    int64_t o_sb, o_st, o_sh;
     int B, Hq, Hkv, G;
     float sl2;               // scale * log2(e)
 };

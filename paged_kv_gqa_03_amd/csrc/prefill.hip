@@ -87,13 +87,18 @@ __device__ __forceinline__ uint64_t key_off(const PrefillParams &p, const StageC
 __device__ __forceinline__ uint4 ld16(const uint16_t *ptr) { return *reinterpret_cast<const uint4 *>(ptr); }
 
 // The thread's share of tile kt: keys 4kg .. 4kg+3, chunk cc, of K and of V
-// (the pools share strides, so the four offsets serve both).  When the page
-// size is a multiple of 4 the four keys sit in one page: one lookup, then
-// slot steps.  Keys past the chunk end repeat its last key.
+// (the sources share strides, so the four offsets serve both).  Paged: when
+// the page size is a multiple of 4 the four keys sit in one page, one lookup
+// then slot steps.  Keys past the chunk end repeat its last key.
+template <bool PAGED>
 __device__ __forceinline__ void load_stage(const PrefillParams &p, const StageCtx &sc, int kt, Stage &r) {
     const int k0 = min(kt * BK + 4 * sc.kg, sc.c1 - 1);
     uint64_t off[4];
-    if ((p.ps & 3u) == 0) {
+    if constexpr (!PAGED) {   // contiguous source: key j at j * s_slot from the sequence's base
+        const int rmax = sc.c1 - 1 - k0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) off[i] = (uint64_t)(k0 + min(i, rmax)) * (uint64_t)p.s_slot;
+    } else if ((p.ps & 3u) == 0) {
         const int rmax = sc.c1 - 1 - k0;
         off[0] = key_off(p, sc, k0);
 #pragma unroll
@@ -201,7 +206,7 @@ __device__ __forceinline__ void store_stage(const StageCtx &sc, const Stage &r, 
     store_v_pair(v_lds, d0 + 6, ph, r.v0.w, r.v1.w, r.v2.w, r.v3.w);
 }
 
-template <int HP, int MASK>
+template <int HP, int MASK, bool PAGED>
 __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) {
     constexpr int WPH = 4 / HP;   // waves (32-row groups) per head
     constexpr int R = 32 * WPH;   // rows per work-map tile
@@ -221,14 +226,30 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) 
     const int nhg = p.Hkv * (p.G / HP);
     const int tile = p.num_tiles - 1 - (int)(blockIdx.x / (unsigned)nhg);
     const int hg = (int)(blockIdx.x % (unsigned)nhg);
-    const int b = p.t2b[tile], ti = p.t2i[tile];
+    // Work map (packed, ragged Q) or the dense schedule: Lq rows per
+    // sequence, tiles_per_seq tiles each.
+    int b, ti;
+    if (p.dense_lq > 0) {
+        const int tps = (p.dense_lq + R - 1) / R;
+        b = tile / tps;
+        ti = tile - b * tps;
+    } else {
+        b = p.t2b[tile];
+        ti = p.t2i[tile];
+    }
     const int groups_per_kv = p.G / HP;
     const int g = hg / groups_per_kv;
     const int hq = g * p.G + (hg % groups_per_kv) * HP + (w % HP);
-    const int q0 = p.qo_indptr[b];
-    const int qn = p.qo_indptr[b + 1] - q0;
-    const int n = p.kv_lens[b];
-    const int c = p.causal ? p.causal[b] : -1;
+    const int q0 = p.dense_lq > 0 ? 0 : p.qo_indptr[b];
+    const int qn = p.dense_lq > 0 ? p.dense_lq : p.qo_indptr[b + 1] - q0;
+    const int n = p.kv_lens ? p.kv_lens[b] : p.kv_len_const;
+    // Causality: an offset array (-1 = off for that sequence), or bottom-right
+    // alignment c = n - qn for every sequence; key j is admitted for local row
+    // i iff j <= c + i (c may be negative: early rows then see no key).
+    const bool causal_on = p.causal ? p.causal[b] >= 0 : p.causal_br != 0;
+    const int c = p.causal ? p.causal[b] : n - qn;
+    const int64_t qrow0 = (int64_t)b * p.q_sb + (int64_t)q0 * p.q_st;   // Q row 0 of the sequence
+    const int64_t orow0 = (int64_t)b * p.o_sb + (int64_t)q0 * p.o_st;
     const int row0 = ti * R;
     const int lq = lane >> 4;   // lane group 0..3
     int myrow[2];
@@ -241,7 +262,7 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) 
 
     // Keys the tile can see: all of the sequence, or up to its causal frontier.
     const int last_row = min(qn, row0 + R) - 1;
-    const int kv_end = (c >= 0) ? min(n, c + last_row + 1) : n;
+    const int kv_end = causal_on ? min(n, c + last_row + 1) : n;
 
     // Q^T operands: row myrow[rb], d = 32s + 8*lq .. +8.  A negative scale
     // is applied as |scale| on negated Q (a sign flip, exact), so the row
@@ -254,7 +275,7 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) 
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
         const uint16_t *qr =
-            p.q + (int64_t)(q0 + min(myrow[rb], qn - 1)) * p.q_st + (int64_t)hq * p.q_sh + 8 * lq;
+            p.q + qrow0 + (int64_t)min(myrow[rb], qn - 1) * p.q_st + (int64_t)hq * p.q_sh + 8 * lq;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             uint4 v = *reinterpret_cast<const uint4 *>(qr + 32 * s);
@@ -285,9 +306,10 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) 
     sc.cc = ttid & 15;
     sc.kg = ttid >> 4;
     sc.pages = pages;
-    sc.kbase = p.k + (int64_t)g * p.s_head + sc.cc * 8;
-    sc.vbase = p.v + (int64_t)g * p.s_head + sc.cc * 8;
-    const int32_t *bt_row = p.bt + b * p.bt_sb;
+    const int64_t seq_base = PAGED ? 0 : (int64_t)b * p.k_sb;   // contiguous: the sequence's K/V
+    sc.kbase = p.k + seq_base + (int64_t)g * p.s_head + sc.cc * 8;
+    sc.vbase = p.v + seq_base + (int64_t)g * p.s_head + sc.cc * 8;
+    const int32_t *bt_row = PAGED ? p.bt + b * p.bt_sb : nullptr;
     Stage st_regs;
 
     MaskCtx mc;
@@ -304,8 +326,8 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) 
     // the wave's first row has the smallest limit.
     int lim[2];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) lim[rb] = c < 0 ? n : min(n, c + myrow[rb] + 1);
-    const int lim_wave = c < 0 ? n : min(n, c + wrow0 + 1);
+    for (int rb = 0; rb < 2; ++rb) lim[rb] = causal_on ? min(n, c + myrow[rb] + 1) : n;
+    const int lim_wave = causal_on ? min(n, c + wrow0 + 1) : n;
 
     // One tile of math from LDS buffer `buf`.  FULL: every key of the tile is
     // admitted by every row of the wave (the common case), so the per-key
@@ -413,28 +435,30 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) 
 
     // Keys in chunks whose pages fit the LDS slice; chunks start on tile
     // boundaries, so no tile straddles two.
-    const int64_t ch_keys = (int64_t)(kPages - 2) * p.ps / BK * BK;
+    const int64_t ch_keys = PAGED ? (int64_t)(kPages - 2) * p.ps / BK * BK : (int64_t)1 << 30;
     const int CH = (int)min<int64_t>(ch_keys > 0 ? ch_keys : BK, 1 << 30);
     for (int c0 = 0; c0 < kv_end; c0 += CH) {
         const int c1 = min(kv_end, c0 + CH);
         const int t0 = c0 / BK, t1 = (c1 + BK - 1) / BK;
-        sc.first_pg = (int)udiv_magic((uint32_t)c0, p.ps_magic);
         sc.c1 = c1;
-        const int npg = (int)udiv_magic((uint32_t)(c1 - 1), p.ps_magic) - sc.first_pg + 1;
         __syncthreads();   // the previous chunk is done with the slice and the buffers
-        for (int i = tid; i < npg; i += 512) pages[i] = bt_row[sc.first_pg + i];
+        if constexpr (PAGED) {
+            sc.first_pg = (int)udiv_magic((uint32_t)c0, p.ps_magic);
+            const int npg = (int)udiv_magic((uint32_t)(c1 - 1), p.ps_magic) - sc.first_pg + 1;
+            for (int i = tid; i < npg; i += 512) pages[i] = bt_row[sc.first_pg + i];
+        }
         __syncthreads();
         // This team's tiles of the chunk: t0 + team, t0 + team + 2, ...
         const int kt0 = t0 + team;
         const int nit = (t1 - t0 + 1) >> 1;
         if (kt0 < t1) {
-            load_stage(p, sc, kt0, st_regs);
+            load_stage<PAGED>(p, sc, kt0, st_regs);
             if constexpr (MASK != 0) load_mask<MASK, NQ>(mc, ttid, n, kt0, mst);
             store_stage(sc, st_regs, kbuf(0), vbuf(0));
             if constexpr (MASK != 0) store_mask<MASK, NQ>(mst, ttid, mbits[team][0]);
         }
         if (kt0 + 2 < t1) {
-            load_stage(p, sc, kt0 + 2, st_regs);
+            load_stage<PAGED>(p, sc, kt0 + 2, st_regs);
             if constexpr (MASK != 0) load_mask<MASK, NQ>(mc, ttid, n, kt0 + 2, mst);
         }
         __syncthreads();
@@ -447,7 +471,7 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) 
                 store_stage(sc, st_regs, kbuf((it + 1) & 1), vbuf((it + 1) & 1));
                 if constexpr (MASK != 0) store_mask<MASK, NQ>(mst, ttid, mbits[team][(it + 1) & 1]);
                 if (kt + 4 < t1) {
-                    load_stage(p, sc, kt + 4, st_regs);
+                    load_stage<PAGED>(p, sc, kt + 4, st_regs);
                     if constexpr (MASK != 0) load_mask<MASK, NQ>(mc, ttid, n, kt + 4, mst);
                 }
             }
@@ -490,7 +514,7 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) 
         const float l_row = lacc[rb][0];
         if (!row_ok[rb]) continue;
         const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
-        uint16_t *orow = p.o + (int64_t)(q0 + myrow[rb]) * p.o_st + (int64_t)hq * p.o_sh + 4 * lq;
+        uint16_t *orow = p.o + orow0 + (int64_t)myrow[rb] * p.o_st + (int64_t)hq * p.o_sh + 4 * lq;
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
             uint2 wv;
@@ -501,16 +525,26 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) 
     }
 }
 
-template <int HP>
+template <int HP, bool PAGED>
 hipError_t launch_hp(const PrefillParams &p, hipStream_t stream) {
     const dim3 grid((unsigned)p.num_tiles * (unsigned)(p.Hkv * (p.G / HP)));
     switch (p.mask_ndim) {
-        case 0: hipLaunchKernelGGL((prefill_kernel<HP, 0>), grid, dim3(512), 0, stream, p); break;
-        case 2: hipLaunchKernelGGL((prefill_kernel<HP, 2>), grid, dim3(512), 0, stream, p); break;
-        case 3: hipLaunchKernelGGL((prefill_kernel<HP, 3>), grid, dim3(512), 0, stream, p); break;
+        case 0: hipLaunchKernelGGL((prefill_kernel<HP, 0, PAGED>), grid, dim3(512), 0, stream, p); break;
+        case 2: hipLaunchKernelGGL((prefill_kernel<HP, 2, PAGED>), grid, dim3(512), 0, stream, p); break;
+        case 3: hipLaunchKernelGGL((prefill_kernel<HP, 3, PAGED>), grid, dim3(512), 0, stream, p); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+template <bool PAGED>
+hipError_t launch_paged(const PrefillParams &p, hipStream_t stream) {
+    switch (prefill_heads_packed(p.G)) {
+        case 1: return launch_hp<1, PAGED>(p, stream);
+        case 2: return launch_hp<2, PAGED>(p, stream);
+        case 4: return launch_hp<4, PAGED>(p, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
@@ -519,12 +553,7 @@ int prefill_heads_packed(int G) { return G >= 4 ? 4 : G; }
 
 hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream) {
     if (p.num_tiles <= 0) return hipSuccess;
-    switch (prefill_heads_packed(p.G)) {
-        case 1: return launch_hp<1>(p, stream);
-        case 2: return launch_hp<2>(p, stream);
-        case 4: return launch_hp<4>(p, stream);
-        default: return hipErrorInvalidValue;
-    }
+    return p.bt ? launch_paged<true>(p, stream) : launch_paged<false>(p, stream);
 }
 
 }  // namespace pa

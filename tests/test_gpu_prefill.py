@@ -1,6 +1,8 @@
 """GPU parity of the ragged paged prefill (MFMA) against the CPU oracle.
 
 Bar: |gpu - oracle| <= 1e-2 + 1e-2 |oracle| on the bf16 outputs."""
+import math
+
 import pytest
 import torch
 
@@ -110,3 +112,82 @@ def test_prefill_long_context_spans_several_page_slices(ps, G):
     case = workloads.prefill_case(360 + ps + G, 2, 2 * G, 2, 128, None, None, ps,
                                   q_lens=[70, 37], ctx_lens=[1500, 1333], mask_frac=0.05)
     assert_close(run_prefill(case), oracle_prefill(case), what="ps=%d G=%d" % (ps, G))
+
+
+# ------------------------------------------------ dense Q, contiguous KV
+def dense_case(seed, B, Lq, Lk, Hq, Hkv, D=128, layout="blhd", mask_ndim=0, mask_frac=0.1):
+    g = torch.Generator().manual_seed(seed)
+    if layout == "blhd":
+        q = torch.randn(B, Lq, Hq, D, generator=g).to(torch.bfloat16)
+        k = torch.randn(B, Lk, Hkv, D, generator=g).to(torch.bfloat16)
+        v = torch.randn(B, Lk, Hkv, D, generator=g).to(torch.bfloat16)
+    else:   # bhld storage, (b, i, h, d) views
+        q = torch.randn(B, Hq, Lq, D, generator=g).to(torch.bfloat16).permute(0, 2, 1, 3)
+        k = torch.randn(B, Hkv, Lk, D, generator=g).to(torch.bfloat16).permute(0, 2, 1, 3)
+        v = torch.randn(B, Hkv, Lk, D, generator=g).to(torch.bfloat16).permute(0, 2, 1, 3)
+    mask = None
+    if mask_ndim:
+        pad = (Lk + 3) // 4 * 4
+        shape = (B, Lq, pad) if mask_ndim == 3 else (B, pad)
+        mask = torch.rand(*shape, generator=g) >= mask_frac
+    return q, k, v, mask
+
+
+def oracle_dense(q, k, v, kv_lens, is_causal, mask, scale):
+    """The dense problem restated for the oracle's paged prefill: packed Q
+    rows b*Lq + i, each sequence's K/V one page of Lk slots.  Bottom-right
+    causality (key j for row i iff j <= n_b - Lq + i, which may admit no key
+    when n_b < Lq) is given to the oracle as a 3-D keep-mask, ANDed with the
+    caller's mask."""
+    B, Lq, Hq, D = q.shape
+    Lk = k.shape[1]
+    qp = q.contiguous().reshape(B * Lq, Hq, D)
+    bt = torch.arange(B, dtype=torch.int32).reshape(B, 1)
+    indptr = torch.arange(0, (B + 1) * Lq, Lq, dtype=torch.int32)
+    m = mask
+    if is_causal:
+        width = mask.shape[-1] if mask is not None else (Lk + 3) // 4 * 4
+        j = torch.arange(width)[None, None, :]
+        i = torch.arange(Lq)[None, :, None]
+        keep = j <= (kv_lens.long() - Lq)[:, None, None] + i
+        if mask is not None:
+            keep = keep & (mask if mask.dim() == 3 else mask[:, None, :])
+        m = keep.contiguous()
+    out, _ = oracle.paged_prefill(qp, indptr, k.contiguous(), v.contiguous(), bt, kv_lens, scale,
+                                  causal_offset=None, mask=m)
+    return out.reshape(B, Lq, Hq, D)
+
+
+@pytest.mark.parametrize("B,Lq,Lk,G,layout,causal,ndim", [
+    (2, 200, 200, 4, "blhd", True, 0),
+    (3, 70, 300, 4, "bhld", True, 0),
+    (2, 130, 130, 1, "blhd", False, 0),
+    (1, 64, 500, 8, "blhd", True, 2),
+    (2, 33, 97, 2, "bhld", True, 3),
+])
+def test_dense_prefill_matches_oracle(B, Lq, Lk, G, layout, causal, ndim):
+    Hkv = 2
+    q, k, v, mask = dense_case(800 + B + Lq + G, B, Lq, Lk, Hkv * G, Hkv, layout=layout, mask_ndim=ndim)
+    scale = 1.0 / math.sqrt(128)
+    kv_lens = torch.full((B,), Lk, dtype=torch.int32)
+    ref = oracle_dense(q, k, v, kv_lens, causal, mask, scale)
+    out = torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device=DEV)
+    pa.attn_prefill(q.to(DEV), k.to(DEV), v.to(DEV), out, scale, is_causal=causal,
+                    mask=None if mask is None else mask.to(DEV))
+    torch.cuda.synchronize()
+    assert_close(out, ref, what="dense B=%d Lq=%d Lk=%d G=%d %s" % (B, Lq, Lk, G, layout))
+
+
+def test_dense_prefill_ragged_kv_lengths_and_short_sequences():
+    """Per-sequence key counts below the stored Lk, one of them shorter than
+    Lq under causality (its first rows admit no key and give zeros)."""
+    B, Lq, Lk, Hkv, G = 3, 40, 260, 2, 4
+    q, k, v, _ = dense_case(820, B, Lq, Lk, Hkv * G, Hkv)
+    kv_lens = torch.tensor([260, 100, 25], dtype=torch.int32)
+    scale = 1.0 / math.sqrt(128)
+    ref = oracle_dense(q, k, v, kv_lens, True, None, scale)
+    out = torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device=DEV)
+    pa.attn_prefill(q.to(DEV), k.to(DEV), v.to(DEV), out, scale, is_causal=True, kv_lens=kv_lens.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(out[2, :15].cpu(), torch.zeros(15, Hkv * G, 128, dtype=torch.bfloat16))
+    assert_close(out, ref, what="ragged kv")
