@@ -300,6 +300,7 @@ def run_extras(torch, pa, dev, args):
     out["contiguous_b16_kv2048"] = bench_contiguous(torch, pa, dev, steps, warm, 0)
     out["ragged_prefill"] = bench_prefill(torch, pa, dev, steps, warm, masked=False)
     out["ragged_prefill_masked"] = bench_prefill(torch, pa, dev, steps, warm, masked=True)
+    out["dense_prefill_b4_l2048_causal"] = bench_dense_prefill(torch, pa, dev, steps, warm)
     out["swa_fp8"] = bench_swa(torch, pa, dev, steps, warm)
     out.update(bench_cache_ops(torch, pa, dev, steps, warm))
     return out
@@ -419,6 +420,28 @@ def bench_prefill(torch, pa, dev, steps, warm, masked):
                               causal_offset=s["causal_offset"], mask=s["mask"])
     ms = time_calls(torch, call, sets, steps, warm)
     fl = sum(sets[i % len(sets)]["flops"] for i in range(steps)) / steps
+    tf = fl / (ms * 1e-3) / 1e12
+    return {"us_per_call": round(ms * 1e3, 2), "TFLOP/s": round(tf, 1), "gflop_per_call": round(fl / 1e9, 2),
+            "mfma_util": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "rotation_sets": len(sets)}
+
+
+def bench_dense_prefill(torch, pa, dev, steps, warm):
+    """Dense prefill, contiguous KV: B=4, Lq = Lk = 2048, Hq=32, Hkv=8, D=128,
+    causal (each row sees its prefix), blhd layout."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(1009)
+    B, L = 4, 2048
+    sets = []
+    for r in range(2):
+        sets.append(dict(q=torch.randn(B, L, 32, 128, generator=g, device=dev).to(torch.bfloat16),
+                         k=torch.randn(B, L, 8, 128, generator=g, device=dev).to(torch.bfloat16),
+                         v=torch.randn(B, L, 8, 128, generator=g, device=dev).to(torch.bfloat16),
+                         out=torch.empty(B, L, 32, 128, dtype=torch.bfloat16, device=dev)))
+
+    def call(s):
+        pa.attn_prefill(s["q"], s["k"], s["v"], s["out"], 1.0 / math.sqrt(128), is_causal=True)
+    ms = time_calls(torch, call, sets, steps, warm)
+    fl = 4 * 128 * 32 * B * (L * (L + 1) // 2)
     tf = fl / (ms * 1e-3) / 1e12
     return {"us_per_call": round(ms * 1e3, 2), "TFLOP/s": round(tf, 1), "gflop_per_call": round(fl / 1e9, 2),
             "mfma_util": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "rotation_sets": len(sets)}
