@@ -191,3 +191,26 @@ def test_dense_prefill_ragged_kv_lengths_and_short_sequences():
     torch.cuda.synchronize()
     assert torch.equal(out[2, :15].cpu(), torch.zeros(15, Hkv * G, 128, dtype=torch.bfloat16))
     assert_close(out, ref, what="ragged kv")
+
+
+def test_decode_with_2d_mask_via_paged_prefill():
+    """A decode step under a 2-D keep-mask [B, kv] runs as a paged prefill
+    with one query row per sequence: equal to the oracle's masked decode."""
+    case = workloads.paged_decode_case(860, 6, 32, 8, 128, [1, 300, 77, 1024, 5, 640], 16)
+    B = case["B"]
+    g = torch.Generator().manual_seed(861)
+    width = (case["max_kv_len"] + 3) // 4 * 4
+    mask = torch.rand(B, width, generator=g) >= 0.3
+    mask[4, :] = False                                   # a sequence with every key masked
+    ref, _ = oracle.paged_decode(case["q"], case["k_pool"], case["v_pool"], case["block_table"],
+                                 case["kv_lens"], case["scale"], mask=mask)
+    R = pa.attn_prefill_tile_rows(128, 4)
+    q_lens = [1] * B
+    indptr, t2b, t2i = pa.attn_prefill_plan(q_lens, R)
+    out = torch.full((B, 32, 128), float("nan"), dtype=torch.bfloat16, device=DEV)
+    pa.attn_paged_prefill(case["q"].to(DEV), indptr.to(DEV), t2b.to(DEV), t2i.to(DEV), case["k_pool"].to(DEV),
+                          case["v_pool"].to(DEV), case["block_table"].to(DEV), case["kv_lens"].to(DEV), out, 16,
+                          case["scale"], causal_offset=None, mask=mask.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(out[4].cpu(), torch.zeros(32, 128, dtype=torch.bfloat16))
+    assert_close(out, ref, what="masked decode")
