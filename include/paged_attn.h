@@ -137,7 +137,7 @@ int attn_decode(const void *q, int64_t q_sb, int64_t q_sh,
  *   max_kv_len  host-side bound on kv_lens, used by the planner;
  *          max_kv_len * page_size must stay below 2^32
  *   o      [B, Hq, D] bf16 output
- * Supported: D in {64, 128}, G in {1, 2, 4, 8}, any page_size >= 1.
+ * Supported: D in {32, 64, 128}, G in {1, 2, 4, 8}, any page_size >= 1.
  * A slice longer than 510 pages is processed as consecutive sub-pieces.
  */
 int attn_paged_decode(const void *q, int64_t q_sb, int64_t q_sh,
@@ -231,7 +231,7 @@ int attn_prefill_tile_rows(int D, int G);
  *   o      packed [total_q, Hq, D] bf16: row r, head h at o + r*o_st + h*o_sh
  * Alignment: q/k/v rows 16-byte aligned, o rows 8-byte aligned, mask rows
  * (m_sb, m_sq, pointer) 4-byte aligned; mask bytes at key positions >= kv_lens[b]
- * are never read.  Supported: D = 128, G in {1, 2, 4, 8}.
+ * are never read.  Supported: D in {32, 64, 128}, G in {1, 2, 4, 8}.
  */
 int attn_paged_prefill(const void *q, int64_t q_st, int64_t q_sh, const int32_t *qo_indptr,
                        const int32_t *tile_to_batch, const int32_t *tile_to_index, int num_tiles,
@@ -260,7 +260,7 @@ int attn_paged_prefill(const void *q, int64_t q_st, int64_t q_sh, const int32_t 
  *   mask, mask_ndim, m_sb, m_sq  as in attn_paged_prefill
  *   o   [B, Lq, Hq, D] bf16: (b, i, h) at o + b*o_sb + i*o_sl + h*o_sh
  * Same kernel and numerics as attn_paged_prefill; no work map is needed.
- * Supported: D = 128, G in {1, 2, 4, 8}; alignment as attn_paged_prefill.
+ * Supported: D in {32, 64, 128}, G in {1, 2, 4, 8}; alignment as attn_paged_prefill.
  */
 int attn_prefill(const void *q, int64_t q_sb, int64_t q_sl, int64_t q_sh,
                  const void *k, const void *v, int64_t k_sb, int64_t k_sl, int64_t k_sh,

@@ -367,7 +367,7 @@ int attn_prefill_plan(const int32_t *q_lens_host, int B, int tile_rows,
 }
 
 int attn_prefill_tile_rows(int D, int G) {
-    if (D != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill_tile_rows: head dim %d not built (128)", D);
+    if (D != 32 && D != 64 && D != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill_tile_rows: head dim %d not built (32, 64, 128)", D);
     if (G != 1 && G != 2 && G != 4 && G != 8)
         return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill_tile_rows: group size %d not built (1, 2, 4, 8)", G);
     return 128 / pa::prefill_heads_packed(G);
@@ -385,7 +385,7 @@ int attn_paged_prefill(const void *q, int64_t q_st, int64_t q_sh, const int32_t 
                        void *stream) {
     int G = 0, rc = check_heads(Hq, Hkv, D, &G);
     if (rc) return rc;
-    if (D != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_paged_prefill: head dim %d not built (128)", D);
+    if (D != 32 && D != 64 && D != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_paged_prefill: head dim %d not built (32, 64, 128)", D);
     if (B < 0 || num_tiles < 0) return fail(ATTN_ERR_INVALID_ARG, "attn_paged_prefill: negative B or num_tiles");
     if (page_size <= 0) return fail(ATTN_ERR_INVALID_ARG, "attn_paged_prefill: page_size must be >= 1");
     if (!q || !qo_indptr || !k_pool || !v_pool || !block_table || !kv_lens || !o ||
@@ -425,7 +425,7 @@ int attn_paged_prefill(const void *q, int64_t q_st, int64_t q_sh, const int32_t 
     p.o_st = o_st; p.o_sh = o_sh;
     p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.G = G;
     p.sl2 = scale * 1.4426950408889634f;
-    return launch_status(pa::launch_prefill(p, static_cast<hipStream_t>(stream)), "prefill kernel");
+    return launch_status(pa::launch_prefill(p, D, static_cast<hipStream_t>(stream)), "prefill kernel");
 }
 
 int attn_prefill(const void *q, int64_t q_sb, int64_t q_sl, int64_t q_sh,
@@ -436,7 +436,7 @@ int attn_prefill(const void *q, int64_t q_sb, int64_t q_sl, int64_t q_sh,
                  int B, int Lq, int Hq, int Hkv, int D, float scale, void *stream) {
     int G = 0, rc = check_heads(Hq, Hkv, D, &G);
     if (rc) return rc;
-    if (D != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill: head dim %d not built (128)", D);
+    if (D != 32 && D != 64 && D != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill: head dim %d not built (32, 64, 128)", D);
     if (B < 0 || Lq < 0 || kv_len < 0) return fail(ATTN_ERR_INVALID_ARG, "attn_prefill: negative size");
     if (!q || !k || !v || !o) return fail(ATTN_ERR_INVALID_ARG, "attn_prefill: null pointer");
     if (!std::isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "attn_prefill: scale is not finite");
@@ -472,7 +472,7 @@ int attn_prefill(const void *q, int64_t q_sb, int64_t q_sl, int64_t q_sh,
     p.o_sb = o_sb; p.o_st = o_sl; p.o_sh = o_sh;
     p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.G = G;
     p.sl2 = scale * 1.4426950408889634f;
-    return launch_status(pa::launch_prefill(p, static_cast<hipStream_t>(stream)), "prefill kernel");
+    return launch_status(pa::launch_prefill(p, D, static_cast<hipStream_t>(stream)), "prefill kernel");
 }
 
 int attn_swa_fp8_decode(const void *q, int64_t q_st, int64_t q_sh,

@@ -160,7 +160,7 @@ hipError_t launch_swa(const SwaParams &p, hipStream_t stream);
 hipError_t launch_kv_append(const KvAppendParams &p, hipStream_t stream);
 hipError_t launch_swa_quantize(const SwaQuantParams &p, hipStream_t stream);
 hipError_t launch_rotary(const RotaryParams &p, hipStream_t stream);
-hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream);
+hipError_t launch_prefill(const PrefillParams &p, int D, hipStream_t stream);
 hipError_t launch_decode_combine(const DecodeCombineParams &p, int D, hipStream_t stream);
 hipError_t launch_combine(const CombineParams &p, int D, hipStream_t stream);
 

@@ -46,7 +46,10 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int BK = 64;           // keys per KV tile
-constexpr int KLD = 128 + 8;     // K tile row stride in LDS (elements): 272 B, conflict-free 16 B reads
+// K tile row stride in LDS (elements): D + 8, e.g. 272 B at D = 128, which
+// keeps the 16-byte operand reads conflict-free.
+template <int D>
+constexpr int kld() { return D + 8; }
 constexpr int VLD = BK + 8;      // V^T row stride in LDS (elements): 144 B
 constexpr int kPages = 512;      // block-table entries staged in LDS at a time
 
@@ -71,6 +74,7 @@ struct Stage {
 
 struct StageCtx {
     int cc, kg;
+    bool stager;                    // this thread stages (16 groups of 4 keys x D/8 chunks)
     int first_pg, c1;               // page slice start; keys of this chunk end at c1
     const int32_t *pages;           // LDS page slice
     const uint16_t *kbase, *vbase;
@@ -92,6 +96,7 @@ __device__ __forceinline__ uint4 ld16(const uint16_t *ptr) { return *reinterpret
 // then slot steps.  Keys past the chunk end repeat its last key.
 template <bool PAGED>
 __device__ __forceinline__ void load_stage(const PrefillParams &p, const StageCtx &sc, int kt, Stage &r) {
+    if (!sc.stager) return;
     const int k0 = min(kt * BK + 4 * sc.kg, sc.c1 - 1);
     uint64_t off[4];
     if constexpr (!PAGED) {   // contiguous source: key j at j * s_slot from the sequence's base
@@ -193,7 +198,10 @@ __device__ __forceinline__ void store_v_pair(uint16_t *v_lds, int d, int ph, uin
     *reinterpret_cast<uint2 *>(&v_lds[(d + 1) * VLD + col]) = hi;
 }
 
+template <int D>
 __device__ __forceinline__ void store_stage(const StageCtx &sc, const Stage &r, uint16_t *k_lds, uint16_t *v_lds) {
+    if (!sc.stager) return;
+    constexpr int KLD = kld<D>();
     *reinterpret_cast<uint4 *>(&k_lds[(4 * sc.kg + 0) * KLD + sc.cc * 8]) = r.k0;
     *reinterpret_cast<uint4 *>(&k_lds[(4 * sc.kg + 1) * KLD + sc.cc * 8]) = r.k1;
     *reinterpret_cast<uint4 *>(&k_lds[(4 * sc.kg + 2) * KLD + sc.cc * 8]) = r.k2;
@@ -206,11 +214,17 @@ __device__ __forceinline__ void store_stage(const StageCtx &sc, const Stage &r, 
     store_v_pair(v_lds, d0 + 6, ph, r.v0.w, r.v1.w, r.v2.w, r.v3.w);
 }
 
-template <int HP, int MASK, bool PAGED>
+template <int D, int HP, int MASK, bool PAGED>
 __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) {
     constexpr int WPH = 4 / HP;   // waves (32-row groups) per head
     constexpr int R = 32 * WPH;   // rows per work-map tile
-    constexpr int SBUF = BK * KLD + 128 * VLD;                // one K tile + one V^T tile (elements)
+    constexpr int KLD = kld<D>();
+    constexpr int NS = D / 32;    // 32-deep steps of Q.K^T
+    constexpr int NM = D / 16;    // 16-row blocks of O^T
+    constexpr int CPR = D / 8;    // 16-byte chunks per K/V row
+    constexpr int XCH = D / 2 + 4;                            // floats per lane handed from team 1 to team 0
+    constexpr int SBUF = BK * KLD + D * VLD;                  // one K tile + one V^T tile (elements)
+    static_assert(4 * XCH * 64 * 4 <= 4 * SBUF * 2, "team exchange must fit the stage buffers");
     __shared__ __attribute__((aligned(16))) uint16_t stage_lds[2 * 2 * SBUF];   // [team][buffer]
     __shared__ int32_t pages[kPages];
     constexpr int MROWS = MASK == 3 ? R : 1;                  // mask rows per tile
@@ -271,13 +285,13 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) 
     // -inf instead of 0 * -inf, and every admitted key weighs 2^0.)
     const float sl2 = fmaxf(fabsf(p.sl2), 1e-30f);
     const uint32_t qsign = p.sl2 < 0.f ? 0x80008000u : 0u;
-    bf16x8_t qf[2][4];
+    bf16x8_t qf[2][NS];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
         const uint16_t *qr =
             p.q + qrow0 + (int64_t)min(myrow[rb], qn - 1) * p.q_st + (int64_t)hq * p.q_sh + 8 * lq;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
+        for (int s = 0; s < NS; ++s) {
             uint4 v = *reinterpret_cast<const uint4 *>(qr + 32 * s);
             v.x ^= qsign; v.y ^= qsign; v.z ^= qsign; v.w ^= qsign;
             qf[rb][s] = as_bf16x8(v);
@@ -286,12 +300,12 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) 
 
     // O^T accumulators, and row sums of P from an MFMA against a ones
     // operand (every entry of lacc[rb] holds the lane's row sum).
-    f32x4_t oacc[2][8], lacc[2];
+    f32x4_t oacc[2][NM], lacc[2];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
         lacc[rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int m = 0; m < 8; ++m) oacc[rb][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int m = 0; m < NM; ++m) oacc[rb][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
     const bf16x8_t ones = as_bf16x8(make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
     // Softmax reference per row (scaled, log2 units), raised lazily: only
@@ -303,8 +317,9 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) 
     // Staging assignment: keys 4*(tid >> 4) + r (r = 0..3) of K and of V,
     // chunk cc = tid & 15.
     StageCtx sc;
-    sc.cc = ttid & 15;
-    sc.kg = ttid >> 4;
+    sc.cc = ttid % CPR;
+    sc.kg = ttid / CPR;
+    sc.stager = sc.kg < 16;
     sc.pages = pages;
     const int64_t seq_base = PAGED ? 0 : (int64_t)b * p.k_sb;   // contiguous: the sequence's K/V
     sc.kbase = p.k + seq_base + (int64_t)g * p.s_head + sc.cc * 8;
@@ -345,7 +360,7 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) 
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) st[0][kb] = st[1][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
+        for (int s = 0; s < NS; ++s)
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
                 const bf16x8_t a = as_bf16x8(
@@ -393,7 +408,7 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) 
                 m_ref[rb] = raise[rb] ? mts[rb] : m_ref[rb];
                 lacc[rb] *= alpha;
 #pragma unroll
-                for (int m = 0; m < 8; ++m) oacc[rb][m] *= alpha;
+                for (int m = 0; m < NM; ++m) oacc[rb][m] *= alpha;
             }
         }
         // P = 2^(s * scale * log2 e - reference), rounded to bf16 pairs.
@@ -418,7 +433,7 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) 
             const bf16x8_t pb0 = as_bf16x8(make_uint4(pw[0][s2][0], pw[0][s2][1], pw[0][s2][2], pw[0][s2][3]));
             const bf16x8_t pb1 = as_bf16x8(make_uint4(pw[1][s2][0], pw[1][s2][1], pw[1][s2][2], pw[1][s2][3]));
 #pragma unroll
-            for (int m = 0; m < 8; ++m) {
+            for (int m = 0; m < NM; ++m) {
                 const bf16x8_t a = as_bf16x8(*reinterpret_cast<const uint4 *>(
                     &vl[(16 * m + (lane & 15)) * VLD + v_col(16 * m, 4 * s2 + lq)]));
                 oacc[0][m] = mfma16(a, pb0, oacc[0][m]);
@@ -454,7 +469,7 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) 
         if (kt0 < t1) {
             load_stage<PAGED>(p, sc, kt0, st_regs);
             if constexpr (MASK != 0) load_mask<MASK, NQ>(mc, ttid, n, kt0, mst);
-            store_stage(sc, st_regs, kbuf(0), vbuf(0));
+            store_stage<D>(sc, st_regs, kbuf(0), vbuf(0));
             if constexpr (MASK != 0) store_mask<MASK, NQ>(mst, ttid, mbits[team][0]);
         }
         if (kt0 + 2 < t1) {
@@ -468,7 +483,7 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) 
             if (kt + 2 < t1) {
                 // The team's next tile into its other buffer (its readers
                 // finished at the last barrier), then the one after goes out.
-                store_stage(sc, st_regs, kbuf((it + 1) & 1), vbuf((it + 1) & 1));
+                store_stage<D>(sc, st_regs, kbuf((it + 1) & 1), vbuf((it + 1) & 1));
                 if constexpr (MASK != 0) store_mask<MASK, NQ>(mst, ttid, mbits[team][(it + 1) & 1]);
                 if (kt + 4 < t1) {
                     load_stage<PAGED>(p, sc, kt + 4, st_regs);
@@ -479,34 +494,34 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) 
         }
     }
 
-    // Team 1's (O, reference, sum) go through its own stage buffers (free
-    // since the last barrier) to the matching wave of team 0, which merges.
-    float *xch = reinterpret_cast<float *>(stage_lds + 2 * SBUF) + w * (68 * 64);
+    // Team 1's (O, reference, sum) go through the stage buffers (free since
+    // the last barrier) to the matching wave of team 0, which merges.
+    float *xch = reinterpret_cast<float *>(stage_lds) + w * (XCH * 64);
     if (team == 1) {
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
 #pragma unroll
-            for (int m = 0; m < 8; ++m)
+            for (int m = 0; m < NM; ++m)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) xch[(rb * 32 + m * 4 + i) * 64 + lane] = oacc[rb][m][i];
-            xch[(64 + rb) * 64 + lane] = m_ref[rb];
-            xch[(66 + rb) * 64 + lane] = lacc[rb][0];
+                for (int i = 0; i < 4; ++i) xch[(rb * (D / 4) + m * 4 + i) * 64 + lane] = oacc[rb][m][i];
+            xch[(D / 2 + rb) * 64 + lane] = m_ref[rb];
+            xch[(D / 2 + 2 + rb) * 64 + lane] = lacc[rb][0];
         }
     }
     __syncthreads();
     if (team == 1) return;
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-        const float mb = xch[(64 + rb) * 64 + lane], lb = xch[(66 + rb) * 64 + lane];
+        const float mb = xch[(D / 2 + rb) * 64 + lane], lb = xch[(D / 2 + 2 + rb) * 64 + lane];
         const float mm = fmaxf(m_ref[rb], mb);
         const float aa = m_ref[rb] == -INFINITY ? 0.f : exp2_fast(m_ref[rb] - mm);
         const float ab = mb == -INFINITY ? 0.f : exp2_fast(mb - mm);
         lacc[rb][0] = lacc[rb][0] * aa + lb * ab;
 #pragma unroll
-        for (int m = 0; m < 8; ++m)
+        for (int m = 0; m < NM; ++m)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                oacc[rb][m][i] = oacc[rb][m][i] * aa + xch[(rb * 32 + m * 4 + i) * 64 + lane] * ab;
+                oacc[rb][m][i] = oacc[rb][m][i] * aa + xch[(rb * (D / 4) + m * 4 + i) * 64 + lane] * ab;
     }
 
 #pragma unroll
@@ -516,7 +531,7 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) 
         const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
         uint16_t *orow = p.o + orow0 + (int64_t)myrow[rb] * p.o_st + (int64_t)hq * p.o_sh + 4 * lq;
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
+        for (int m = 0; m < NM; ++m) {
             uint2 wv;
             wv.x = pack_bf16(oacc[rb][m][0] * inv, oacc[rb][m][1] * inv);
             wv.y = pack_bf16(oacc[rb][m][2] * inv, oacc[rb][m][3] * inv);
@@ -525,24 +540,24 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) 
     }
 }
 
-template <int HP, bool PAGED>
+template <int D, int HP, bool PAGED>
 hipError_t launch_hp(const PrefillParams &p, hipStream_t stream) {
     const dim3 grid((unsigned)p.num_tiles * (unsigned)(p.Hkv * (p.G / HP)));
     switch (p.mask_ndim) {
-        case 0: hipLaunchKernelGGL((prefill_kernel<HP, 0, PAGED>), grid, dim3(512), 0, stream, p); break;
-        case 2: hipLaunchKernelGGL((prefill_kernel<HP, 2, PAGED>), grid, dim3(512), 0, stream, p); break;
-        case 3: hipLaunchKernelGGL((prefill_kernel<HP, 3, PAGED>), grid, dim3(512), 0, stream, p); break;
+        case 0: hipLaunchKernelGGL((prefill_kernel<D, HP, 0, PAGED>), grid, dim3(512), 0, stream, p); break;
+        case 2: hipLaunchKernelGGL((prefill_kernel<D, HP, 2, PAGED>), grid, dim3(512), 0, stream, p); break;
+        case 3: hipLaunchKernelGGL((prefill_kernel<D, HP, 3, PAGED>), grid, dim3(512), 0, stream, p); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-template <bool PAGED>
+template <int D, bool PAGED>
 hipError_t launch_paged(const PrefillParams &p, hipStream_t stream) {
     switch (prefill_heads_packed(p.G)) {
-        case 1: return launch_hp<1, PAGED>(p, stream);
-        case 2: return launch_hp<2, PAGED>(p, stream);
-        case 4: return launch_hp<4, PAGED>(p, stream);
+        case 1: return launch_hp<D, 1, PAGED>(p, stream);
+        case 2: return launch_hp<D, 2, PAGED>(p, stream);
+        case 4: return launch_hp<D, 4, PAGED>(p, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -551,9 +566,12 @@ hipError_t launch_paged(const PrefillParams &p, hipStream_t stream) {
 
 int prefill_heads_packed(int G) { return G >= 4 ? 4 : G; }
 
-hipError_t launch_prefill(const PrefillParams &p, hipStream_t stream) {
+hipError_t launch_prefill(const PrefillParams &p, int D, hipStream_t stream) {
     if (p.num_tiles <= 0) return hipSuccess;
-    return p.bt ? launch_paged<true>(p, stream) : launch_paged<false>(p, stream);
+    if (D == 32) return p.bt ? launch_paged<32, true>(p, stream) : launch_paged<32, false>(p, stream);
+    if (D == 64) return p.bt ? launch_paged<64, true>(p, stream) : launch_paged<64, false>(p, stream);
+    if (D == 128) return p.bt ? launch_paged<128, true>(p, stream) : launch_paged<128, false>(p, stream);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace pa

@@ -214,3 +214,29 @@ def test_decode_with_2d_mask_via_paged_prefill():
     torch.cuda.synchronize()
     assert torch.equal(out[4].cpu(), torch.zeros(32, 128, dtype=torch.bfloat16))
     assert_close(out, ref, what="masked decode")
+
+
+@pytest.mark.parametrize("G,ps,mask_ndim", [(4, 16, None), (2, 5, 3), (8, 16, 2), (1, 1, None)])
+def test_prefill_head_dim_64(G, ps, mask_ndim):
+    case = workloads.prefill_case(880 + G + ps, 3, 2 * G, 2, 64, (0, 300), (1, 140), ps,
+                                  mask_frac=None if mask_ndim is None else 0.2, mask_ndim=mask_ndim or 3)
+    assert_close(run_prefill(case), oracle_prefill(case), what="D=64 G=%d ps=%d" % (G, ps))
+
+
+def test_dense_prefill_head_dim_64():
+    B, Lq, Lk, Hkv, G = 2, 150, 400, 2, 4
+    q, k, v, _ = dense_case(890, B, Lq, Lk, Hkv * G, Hkv, D=64, layout="bhld")
+    kv_lens = torch.full((B,), Lk, dtype=torch.int32)
+    scale = 1.0 / math.sqrt(64)
+    ref = oracle_dense(q, k, v, kv_lens, True, None, scale)
+    out = torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device=DEV)
+    pa.attn_prefill(q.to(DEV), k.to(DEV), v.to(DEV), out, scale, is_causal=True)
+    torch.cuda.synchronize()
+    assert_close(out, ref, what="dense D=64")
+
+
+@pytest.mark.parametrize("G,ps,mask_ndim", [(4, 16, None), (2, 3, 2), (8, 16, 3)])
+def test_prefill_head_dim_32(G, ps, mask_ndim):
+    case = workloads.prefill_case(895 + G + ps, 3, 2 * G, 2, 32, (0, 300), (1, 140), ps,
+                                  mask_frac=None if mask_ndim is None else 0.2, mask_ndim=mask_ndim or 3)
+    assert_close(run_prefill(case), oracle_prefill(case), what="D=32 G=%d ps=%d" % (G, ps))
