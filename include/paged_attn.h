@@ -202,9 +202,11 @@ int attn_prefill_plan(const int32_t *q_lens_host, int B, int tile_rows,
                       int32_t *tile_to_index_host, int cap, int *num_tiles);
 
 /* Query rows per tile that attn_paged_prefill expects in its work map for
- * head dim D and group size G = Hq / Hkv: a workgroup packs min(G, 4) query
- * heads that share a KV head, and a tile holds 128 / min(G, 4) rows (32 per
- * wave of the workgroup). */
+ * head dim D and group size G = Hq / Hkv.  A workgroup packs all G query
+ * heads that share a KV head (csrc commit on GQA head packing: K/V tiles are
+ * streamed once per block, not once per query head); a tile holds 128 / G
+ * rows for G <= 4 (32 rows of one head per wave) and 16 rows for G = 8 (two
+ * heads of the same 16 rows per wave). */
 int attn_prefill_tile_rows(int D, int G);
 
 /*
@@ -268,6 +270,58 @@ int attn_prefill(const void *q, int64_t q_sb, int64_t q_sl, int64_t q_sh,
                  const uint8_t *mask, int mask_ndim, int64_t m_sb, int64_t m_sq,
                  void *o, int64_t o_sb, int64_t o_sl, int64_t o_sh,
                  int B, int Lq, int Hq, int Hkv, int D, float scale, void *stream);
+
+/*
+ * Split-KV prefill, for short query runs over long contexts, where the
+ * tiles x KV heads of the plain prefill leave the device mostly idle (csrc
+ * commit on GQA head packing, measured on short-q / long-kv prefill; the
+ * unnormalised partials and their log-sum-exp combine are those of split-KV
+ * decode, AstrAI "CUDA Kernels" doc, Overview).  num_splits workgroups
+ * share each tile's visible keys in equal runs of 64-key tiles; each writes
+ * an unnormalised fp32 partial (o, m, l) per query row and head into the
+ * workspace, and a combine kernel merges them into o by log-sum-exp.  The
+ * arguments and results are those of attn_paged_prefill / attn_prefill,
+ * plus:
+ *   total_q     (paged) rows of the packed Q, i.e. qo_indptr[B] (host int);
+ *               the partials cover rows < total_q
+ *   num_splits  >= 1, e.g. from attn_prefill_plan_splits; 1 runs the plain
+ *               kernel and needs no workspace
+ *   workspace   device, 256-byte aligned, at least
+ *               attn_prefill_workspace_bytes(rows, Hq, D, num_splits) bytes
+ *               with rows = total_q (paged) or B * Lq (dense); its contents
+ *               need no initialisation and are scratch after the call.
+ * Layout: o_part f32 [num_splits, rows, Hq, D], then at the next 256-byte
+ * boundary ml_part f32 [num_splits, rows, Hq, 2] (m in natural-log units of
+ * the scaled score, l).  Errors: ATTN_ERR_WORKSPACE if the workspace is
+ * missing or short; ATTN_ERR_INVALID_ARG if num_splits is outside [1, 256].
+ */
+size_t attn_prefill_workspace_bytes(int rows, int Hq, int D, int num_splits);
+
+/* Host planner for the split count: with W0 = num_tiles * Hkv workgroups
+ * of the plain kernel, returns the largest S <= target_workgroups / W0 that
+ * leaves every split at least 8 key tiles of 64 at max_kv_len (at least 1,
+ * at most 256).  target_workgroups = 0 uses one per compute unit of the
+ * current device.  Negative on error. */
+int attn_prefill_plan_splits(int num_tiles, int Hq, int Hkv, int D, int max_kv_len, int target_workgroups);
+
+int attn_paged_prefill_split(const void *q, int64_t q_st, int64_t q_sh, const int32_t *qo_indptr,
+                             const int32_t *tile_to_batch, const int32_t *tile_to_index, int num_tiles,
+                             const void *k_pool, const void *v_pool,
+                             int64_t kv_s_page, int64_t kv_s_slot, int64_t kv_s_head,
+                             const int32_t *block_table, int64_t bt_sb, const int32_t *kv_lens,
+                             const int32_t *causal_offset,
+                             const uint8_t *mask, int mask_ndim, int64_t m_sb, int64_t m_sq,
+                             void *o, int64_t o_st, int64_t o_sh,
+                             int B, int Hq, int Hkv, int D, int page_size, float scale,
+                             int total_q, int num_splits, void *workspace, size_t workspace_bytes, void *stream);
+
+int attn_prefill_split(const void *q, int64_t q_sb, int64_t q_sl, int64_t q_sh,
+                       const void *k, const void *v, int64_t k_sb, int64_t k_sl, int64_t k_sh,
+                       const int32_t *kv_lens, int kv_len, int is_causal,
+                       const uint8_t *mask, int mask_ndim, int64_t m_sb, int64_t m_sq,
+                       void *o, int64_t o_sb, int64_t o_sl, int64_t o_sh,
+                       int B, int Lq, int Hq, int Hkv, int D, float scale,
+                       int num_splits, void *workspace, size_t workspace_bytes, void *stream);
 
 /* --------------------------------------------------- fp8 sliding window */
 

@@ -17,7 +17,8 @@ __all__ = [
     "attn_decode_combine", "attn_split_combine",
     "attn_prefill_plan", "attn_prefill_tile_rows", "attn_paged_prefill", "attn_swa_fp8_decode",
     "attn_prefill", "attn_paged_kv_append", "attn_swa_fp8_append", "attn_rotary_embed",
-    "EXPORTED_SYMBOLS",
+    "attn_prefill_workspace_bytes", "attn_prefill_plan_splits", "attn_paged_prefill_split",
+    "attn_prefill_split", "EXPORTED_SYMBOLS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -55,6 +56,13 @@ _SIGS = {
                               _I, _I, _I, _I, _P], _I),
     "attn_swa_fp8_append": ([_P, _L, _P, _P, _I, _I, _P, _L, _L, _P, _L, _I, _I, _P, _P], _I),
     "attn_rotary_embed": ([_P, _L, _L, _P, _L, _L, _I, _I, _I, _P, _P, _L, _I, _P, _P], _I),
+    "attn_prefill_workspace_bytes": ([_I, _I, _I, _I], _Z),
+    "attn_prefill_plan_splits": ([_I, _I, _I, _I, _I, _I], _I),
+    "attn_paged_prefill_split": ([_P, _L, _L, _P, _P, _P, _I, _P, _P, _L, _L, _L, _P, _L, _P, _P,
+                                  _P, _I, _L, _L, _P, _L, _L, _I, _I, _I, _I, _I, _F,
+                                  _I, _I, _P, _Z, _P], _I),
+    "attn_prefill_split": ([_P, _L, _L, _L, _P, _P, _L, _L, _L, _P, _I, _I, _P, _I, _L, _L, _P, _L, _L, _L,
+                            _I, _I, _I, _I, _I, _F, _I, _P, _Z, _P], _I),
 }
 EXPORTED_SYMBOLS = tuple(_SIGS)
 
@@ -239,14 +247,7 @@ def attn_paged_prefill(q, qo_indptr, tile_to_batch, tile_to_index, k_pool, v_poo
     total_q, Hq, D = q.shape
     Hkv = k_pool.shape[2]
     B = qo_indptr.numel() - 1
-    ndim, m_sb, m_sq = 0, 0, 0
-    if mask is not None:
-        if mask.dtype == torch.bool:
-            mask = mask.view(torch.uint8)
-        _unit_inner(mask)
-        ndim = mask.dim()
-        m_sb = mask.stride(0)
-        m_sq = mask.stride(1) if ndim == 3 else 0
+    mask, ndim, m_sb, m_sq = _mask_args(mask)
     _check(lib().attn_paged_prefill(
         _ptr(q), q.stride(0), q.stride(1), _ptr(qo_indptr), _ptr(tile_to_batch), _ptr(tile_to_index),
         int(tile_to_batch.numel()), _ptr(k_pool), _ptr(v_pool),
@@ -324,16 +325,87 @@ def attn_prefill(q, k, v, out, scale, is_causal=False, kv_lens=None, mask=None, 
     assert k.stride() == v.stride(), "K and V must share strides"
     B, Lq, Hq, D = q.shape
     Lk, Hkv = k.shape[1], k.shape[2]
-    ndim, m_sb, m_sq = 0, 0, 0
-    if mask is not None:
-        if mask.dtype == torch.bool:
-            mask = mask.view(torch.uint8)
-        _unit_inner(mask)
-        ndim = mask.dim()
-        m_sb = mask.stride(0)
-        m_sq = mask.stride(1) if ndim == 3 else 0
+    mask, ndim, m_sb, m_sq = _mask_args(mask)
     _check(lib().attn_prefill(
         _ptr(q), q.stride(0), q.stride(1), q.stride(2), _ptr(k), _ptr(v), k.stride(0), k.stride(1), k.stride(2),
         _ptr(kv_lens), int(Lk), 1 if is_causal else 0, _ptr(mask), ndim, m_sb, m_sq,
         _ptr(out), out.stride(0), out.stride(1), out.stride(2), B, Lq, Hq, Hkv, D, float(scale), _stream(stream)))
+    return out
+
+
+def _mask_args(mask):
+    """(mask as uint8, ndim, batch stride, row stride) of a keep-mask or None."""
+    if mask is None:
+        return None, 0, 0, 0
+    if mask.dtype == torch.bool:
+        mask = mask.view(torch.uint8)
+    _unit_inner(mask)
+    ndim = mask.dim()
+    return mask, ndim, mask.stride(0), (mask.stride(1) if ndim == 3 else 0)
+
+
+def attn_prefill_workspace_bytes(rows, Hq, D, num_splits):
+    return int(lib().attn_prefill_workspace_bytes(rows, Hq, D, num_splits))
+
+
+def attn_prefill_plan_splits(num_tiles, Hq, Hkv, D, max_kv_len, target_workgroups=0):
+    rc = lib().attn_prefill_plan_splits(num_tiles, Hq, Hkv, D, max_kv_len, target_workgroups)
+    if rc < 0:
+        _check(rc)
+    return rc
+
+
+def _prefill_workspace(workspace, rows, Hq, D, S, device):
+    if workspace is not None:
+        return workspace, workspace.numel() * workspace.element_size()
+    if S <= 1:
+        return None, 0
+    n = attn_prefill_workspace_bytes(rows, Hq, D, S)
+    return torch.empty(n, dtype=torch.uint8, device=device), n
+
+
+def attn_paged_prefill_split(q, qo_indptr, tile_to_batch, tile_to_index, k_pool, v_pool, block_table,
+                             kv_lens, out, page_size, scale, max_kv_len, causal_offset=None, mask=None,
+                             num_splits=0, workspace=None, stream=None, target_workgroups=0):
+    """attn_paged_prefill with the keys of each tile split over num_splits
+    workgroups (0 asks the planner with max_kv_len) and merged by a combine."""
+    _unit_inner(q, k_pool, v_pool, out, block_table)
+    assert k_pool.stride() == v_pool.stride()
+    total_q, Hq, D = q.shape
+    Hkv = k_pool.shape[2]
+    B = qo_indptr.numel() - 1
+    num_tiles = int(tile_to_batch.numel())
+    S = num_splits or attn_prefill_plan_splits(num_tiles, Hq, Hkv, D, max_kv_len, target_workgroups)
+    ws, nbytes = _prefill_workspace(workspace, total_q, Hq, D, S, q.device)
+    mask, ndim, m_sb, m_sq = _mask_args(mask)
+    _check(lib().attn_paged_prefill_split(
+        _ptr(q), q.stride(0), q.stride(1), _ptr(qo_indptr), _ptr(tile_to_batch), _ptr(tile_to_index),
+        num_tiles, _ptr(k_pool), _ptr(v_pool),
+        k_pool.stride(0), k_pool.stride(1), k_pool.stride(2), _ptr(block_table), block_table.stride(0),
+        _ptr(kv_lens), _ptr(causal_offset), _ptr(mask), ndim, m_sb, m_sq,
+        _ptr(out), out.stride(0), out.stride(1), B, Hq, Hkv, D, int(page_size), float(scale),
+        total_q, S, _ptr(ws), nbytes, _stream(stream)))
+    return out
+
+
+def attn_prefill_split(q, k, v, out, scale, is_causal=False, kv_lens=None, mask=None, num_splits=0,
+                       workspace=None, stream=None, target_workgroups=0):
+    """attn_prefill with split KV and a combine; num_splits 0 asks the
+    planner (the tile count of the dense schedule, max_kv_len = Lk)."""
+    _unit_inner(q, k, v, out)
+    assert k.stride() == v.stride(), "K and V must share strides"
+    B, Lq, Hq, D = q.shape
+    Lk, Hkv = k.shape[1], k.shape[2]
+    if num_splits:
+        S = num_splits
+    else:
+        R = attn_prefill_tile_rows(D, Hq // Hkv)
+        S = attn_prefill_plan_splits(B * ((Lq + R - 1) // R), Hq, Hkv, D, Lk, target_workgroups)
+    ws, nbytes = _prefill_workspace(workspace, B * Lq, Hq, D, S, q.device)
+    mask, ndim, m_sb, m_sq = _mask_args(mask)
+    _check(lib().attn_prefill_split(
+        _ptr(q), q.stride(0), q.stride(1), q.stride(2), _ptr(k), _ptr(v), k.stride(0), k.stride(1), k.stride(2),
+        _ptr(kv_lens), int(Lk), 1 if is_causal else 0, _ptr(mask), ndim, m_sb, m_sq,
+        _ptr(out), out.stride(0), out.stride(1), out.stride(2), B, Lq, Hq, Hkv, D, float(scale),
+        S, _ptr(ws), nbytes, _stream(stream)))
     return out

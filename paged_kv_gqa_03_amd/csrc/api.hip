@@ -4,6 +4,7 @@
 // device memory or synchronises.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -54,6 +55,9 @@ constexpr int kMaxWaves = 1 << 16;     // upper bound on decode slices (num_spli
 constexpr int kWavesPerCuRows = 3;
 constexpr int kWavesPerCuHead = 2;
 constexpr int kMinSliceTokens = 64;    // shortest slice the planner makes, in tokens of a row
+constexpr int kMaxPrefillSplits = 256; // upper bound on prefill KV splits
+constexpr int kPrefillWgPerCu = 1;     // prefill workgroups resident per CU (512 threads, 143 KB LDS)
+constexpr int kMinSplitKeyTiles = 8;   // fewest 64-key tiles the prefill planner gives one split
 
 // KV heads one decode wave covers: with the heads of a token adjacent in
 // memory (head stride == D) a wave takes up to 8 of them so each token's
@@ -370,10 +374,64 @@ int attn_prefill_tile_rows(int D, int G) {
     if (D != 32 && D != 64 && D != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill_tile_rows: head dim %d not built (32, 64, 128)", D);
     if (G != 1 && G != 2 && G != 4 && G != 8)
         return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill_tile_rows: group size %d not built (1, 2, 4, 8)", G);
-    return 128 / pa::prefill_heads_packed(G);
+    return pa::prefill_tile_rows(G);
 }
 
-int attn_paged_prefill(const void *q, int64_t q_st, int64_t q_sh, const int32_t *qo_indptr,
+}  // extern "C"
+
+namespace {
+
+// Split-KV prefill workspace: o_part [S, rows, Hq, D] f32, then ml_part
+// [S, rows, Hq, 2] f32 at the next 256-byte boundary.
+size_t pf_ml_offset(int rows, int Hq, int D, int S) {
+    const size_t o_bytes = (size_t)S * (size_t)rows * (size_t)Hq * (size_t)D * sizeof(float);
+    return (o_bytes + 255) & ~(size_t)255;
+}
+
+// Checks the split arguments and fills the split fields of p; S == 1 needs
+// no workspace.  rows: query rows the partials hold.
+int prefill_split_setup(pa::PrefillParams &p, const char *who, int rows, int Hq, int D, int S, void *workspace,
+                        size_t workspace_bytes) {
+    if (S < 1 || S > kMaxPrefillSplits)
+        return fail(ATTN_ERR_INVALID_ARG, "%s: num_splits %d outside [1, %d]", who, S, kMaxPrefillSplits);
+    if (rows < 0) return fail(ATTN_ERR_INVALID_ARG, "%s: negative row count", who);
+    p.kv_splits = S;
+    p.part_rows = rows;
+    if (S == 1) return ATTN_OK;
+    const size_t need = attn_prefill_workspace_bytes(rows, Hq, D, S);
+    if (!workspace || workspace_bytes < need)
+        return fail(ATTN_ERR_WORKSPACE, "%s with %d splits needs %zu workspace bytes, got %zu", who, S, need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(ATTN_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", who);
+    if ((int64_t)S * rows * Hq >= (1ll << 31))
+        return fail(ATTN_ERR_UNSUPPORTED, "%s: num_splits * rows * Hq must stay below 2^31", who);
+    p.o_part = static_cast<float *>(workspace);
+    p.ml_part = reinterpret_cast<float *>(static_cast<char *>(workspace) + pf_ml_offset(rows, Hq, D, S));
+    return ATTN_OK;
+}
+
+// Split kernel, then (S > 1) the combine into o.
+int run_prefill(const pa::PrefillParams &p, int D, hipStream_t stream) {
+    hipError_t e = pa::launch_prefill(p, D, stream);
+    if (e != hipSuccess) return launch_status(e, "prefill kernel");
+    if (p.kv_splits > 1) {
+        pa::PrefillCombineParams c{};
+        c.o_part = p.o_part;
+        c.ml_part = p.ml_part;
+        c.S = p.kv_splits;
+        c.rows = p.part_rows;
+        c.Hq = p.Hq;
+        c.dense_lq = p.dense_lq;
+        c.o = p.o;
+        c.o_sb = p.o_sb; c.o_st = p.o_st; c.o_sh = p.o_sh;
+        e = pa::launch_prefill_combine(c, D, stream);
+        if (e != hipSuccess) return launch_status(e, "prefill combine kernel");
+    }
+    return ok();
+}
+
+int paged_prefill_impl(const void *q, int64_t q_st, int64_t q_sh, const int32_t *qo_indptr,
                        const int32_t *tile_to_batch, const int32_t *tile_to_index, int num_tiles,
                        const void *k_pool, const void *v_pool,
                        int64_t kv_s_page, int64_t kv_s_slot, int64_t kv_s_head,
@@ -382,7 +440,7 @@ int attn_paged_prefill(const void *q, int64_t q_st, int64_t q_sh, const int32_t 
                        const uint8_t *mask, int mask_ndim, int64_t m_sb, int64_t m_sq,
                        void *o, int64_t o_st, int64_t o_sh,
                        int B, int Hq, int Hkv, int D, int page_size, float scale,
-                       void *stream) {
+                       int total_q, int num_splits, void *workspace, size_t workspace_bytes, void *stream) {
     int G = 0, rc = check_heads(Hq, Hkv, D, &G);
     if (rc) return rc;
     if (D != 32 && D != 64 && D != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_paged_prefill: head dim %d not built (32, 64, 128)", D);
@@ -403,10 +461,12 @@ int attn_paged_prefill(const void *q, int64_t q_st, int64_t q_sh, const int32_t 
     if (kv_s_page < 0 || kv_s_slot < 0 || kv_s_head < 0 || kv_s_page >= (1ll << 32) ||
         (int64_t)(page_size - 1) * kv_s_slot + (int64_t)(Hkv - 1) * kv_s_head + D >= (1ll << 31))
         return fail(ATTN_ERR_UNSUPPORTED, "attn_paged_prefill: pool strides exceed the 32-bit page/slot addressing");
-    if ((int64_t)num_tiles * Hkv * 2 >= (1ll << 31))
-        return fail(ATTN_ERR_UNSUPPORTED, "attn_paged_prefill: num_tiles * Hkv too large for one grid");
-    if (B == 0 || num_tiles == 0) return ok();
+    if ((int64_t)num_tiles * Hkv * (num_splits > 0 ? num_splits : 1) >= (1ll << 31))
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_paged_prefill: num_tiles * Hkv * num_splits too large for one grid");
     pa::PrefillParams p{};
+    rc = prefill_split_setup(p, "attn_paged_prefill", total_q, Hq, D, num_splits, workspace, workspace_bytes);
+    if (rc) return rc;
+    if (B == 0 || num_tiles == 0) return ok();
     p.q = static_cast<const uint16_t *>(q);
     p.q_st = q_st; p.q_sh = q_sh;
     p.qo_indptr = qo_indptr; p.t2b = tile_to_batch; p.t2i = tile_to_index; p.num_tiles = num_tiles;
@@ -425,15 +485,16 @@ int attn_paged_prefill(const void *q, int64_t q_st, int64_t q_sh, const int32_t 
     p.o_st = o_st; p.o_sh = o_sh;
     p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.G = G;
     p.sl2 = scale * 1.4426950408889634f;
-    return launch_status(pa::launch_prefill(p, D, static_cast<hipStream_t>(stream)), "prefill kernel");
+    return run_prefill(p, D, static_cast<hipStream_t>(stream));
 }
 
-int attn_prefill(const void *q, int64_t q_sb, int64_t q_sl, int64_t q_sh,
-                 const void *k, const void *v, int64_t k_sb, int64_t k_sl, int64_t k_sh,
-                 const int32_t *kv_lens, int kv_len, int is_causal,
-                 const uint8_t *mask, int mask_ndim, int64_t m_sb, int64_t m_sq,
-                 void *o, int64_t o_sb, int64_t o_sl, int64_t o_sh,
-                 int B, int Lq, int Hq, int Hkv, int D, float scale, void *stream) {
+int dense_prefill_impl(const void *q, int64_t q_sb, int64_t q_sl, int64_t q_sh,
+                       const void *k, const void *v, int64_t k_sb, int64_t k_sl, int64_t k_sh,
+                       const int32_t *kv_lens, int kv_len, int is_causal,
+                       const uint8_t *mask, int mask_ndim, int64_t m_sb, int64_t m_sq,
+                       void *o, int64_t o_sb, int64_t o_sl, int64_t o_sh,
+                       int B, int Lq, int Hq, int Hkv, int D, float scale,
+                       int num_splits, void *workspace, size_t workspace_bytes, void *stream) {
     int G = 0, rc = check_heads(Hq, Hkv, D, &G);
     if (rc) return rc;
     if (D != 32 && D != 64 && D != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill: head dim %d not built (32, 64, 128)", D);
@@ -449,11 +510,15 @@ int attn_prefill(const void *q, int64_t q_sb, int64_t q_sl, int64_t q_sh,
         return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill: q/k/v rows must be 16-byte and o rows 8-byte aligned");
     if (q_sb < 0 || q_sl < 0 || q_sh < 0 || k_sb < 0 || k_sl < 0 || k_sh < 0 || o_sb < 0 || o_sl < 0 || o_sh < 0)
         return fail(ATTN_ERR_INVALID_ARG, "attn_prefill: negative stride");
-    const int R = 128 / pa::prefill_heads_packed(G);
+    const int R = pa::prefill_tile_rows(G);
     const int64_t tiles = (int64_t)B * ((Lq + R - 1) / R);
-    if (tiles * Hkv * 2 >= (1ll << 31)) return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill: too many tiles for one grid");
-    if (B == 0 || Lq == 0) return ok();
+    if (tiles * Hkv * (num_splits > 0 ? num_splits : 1) >= (1ll << 31))
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill: too many tiles for one grid");
+    if ((int64_t)B * Lq >= (1ll << 31)) return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill: B * Lq must stay below 2^31");
     pa::PrefillParams p{};
+    rc = prefill_split_setup(p, "attn_prefill", B * Lq, Hq, D, num_splits, workspace, workspace_bytes);
+    if (rc) return rc;
+    if (B == 0 || Lq == 0) return ok();
     p.q = static_cast<const uint16_t *>(q);
     p.q_sb = q_sb; p.q_st = q_sl; p.q_sh = q_sh;
     p.num_tiles = (int)tiles;
@@ -472,7 +537,92 @@ int attn_prefill(const void *q, int64_t q_sb, int64_t q_sl, int64_t q_sh,
     p.o_sb = o_sb; p.o_st = o_sl; p.o_sh = o_sh;
     p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.G = G;
     p.sl2 = scale * 1.4426950408889634f;
-    return launch_status(pa::launch_prefill(p, D, static_cast<hipStream_t>(stream)), "prefill kernel");
+    return run_prefill(p, D, static_cast<hipStream_t>(stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t attn_prefill_workspace_bytes(int rows, int Hq, int D, int num_splits) {
+    if (rows < 0 || Hq <= 0 || D <= 0 || num_splits < 1) return 0;
+    if (num_splits == 1) return 0;
+    return pf_ml_offset(rows, Hq, D, num_splits) +
+           (size_t)num_splits * (size_t)rows * (size_t)Hq * 2 * sizeof(float);
+}
+
+int attn_prefill_plan_splits(int num_tiles, int Hq, int Hkv, int D, int max_kv_len, int target_workgroups) {
+    int G = 0, rc = check_heads(Hq, Hkv, D, &G);
+    if (rc) return rc;
+    if (num_tiles < 0 || max_kv_len < 0 || target_workgroups < 0)
+        return fail(ATTN_ERR_INVALID_ARG, "attn_prefill_plan_splits: negative argument");
+    if (target_workgroups == 0) {
+        const int cus = device_cus();
+        if (cus <= 0) return fail(ATTN_ERR_LAUNCH, "attn_prefill_plan_splits: no HIP device");
+        target_workgroups = kPrefillWgPerCu * cus;
+    }
+    const int64_t base = (int64_t)num_tiles * Hkv * (G / pa::prefill_heads_packed(G));
+    if (base == 0) return 1;
+    int64_t S = target_workgroups / base;
+    const int64_t key_tiles = ((int64_t)max_kv_len + 63) / 64;
+    S = std::min<int64_t>(S, key_tiles / kMinSplitKeyTiles);
+    S = std::min<int64_t>(S, kMaxPrefillSplits);
+    return (int)std::max<int64_t>(S, 1);
+}
+
+int attn_paged_prefill(const void *q, int64_t q_st, int64_t q_sh, const int32_t *qo_indptr,
+                       const int32_t *tile_to_batch, const int32_t *tile_to_index, int num_tiles,
+                       const void *k_pool, const void *v_pool,
+                       int64_t kv_s_page, int64_t kv_s_slot, int64_t kv_s_head,
+                       const int32_t *block_table, int64_t bt_sb, const int32_t *kv_lens,
+                       const int32_t *causal_offset,
+                       const uint8_t *mask, int mask_ndim, int64_t m_sb, int64_t m_sq,
+                       void *o, int64_t o_st, int64_t o_sh,
+                       int B, int Hq, int Hkv, int D, int page_size, float scale,
+                       void *stream) {
+    return paged_prefill_impl(q, q_st, q_sh, qo_indptr, tile_to_batch, tile_to_index, num_tiles, k_pool, v_pool,
+                              kv_s_page, kv_s_slot, kv_s_head, block_table, bt_sb, kv_lens, causal_offset, mask,
+                              mask_ndim, m_sb, m_sq, o, o_st, o_sh, B, Hq, Hkv, D, page_size, scale, 0, 1, nullptr,
+                              0, stream);
+}
+
+int attn_paged_prefill_split(const void *q, int64_t q_st, int64_t q_sh, const int32_t *qo_indptr,
+                             const int32_t *tile_to_batch, const int32_t *tile_to_index, int num_tiles,
+                             const void *k_pool, const void *v_pool,
+                             int64_t kv_s_page, int64_t kv_s_slot, int64_t kv_s_head,
+                             const int32_t *block_table, int64_t bt_sb, const int32_t *kv_lens,
+                             const int32_t *causal_offset,
+                             const uint8_t *mask, int mask_ndim, int64_t m_sb, int64_t m_sq,
+                             void *o, int64_t o_st, int64_t o_sh,
+                             int B, int Hq, int Hkv, int D, int page_size, float scale,
+                             int total_q, int num_splits, void *workspace, size_t workspace_bytes, void *stream) {
+    return paged_prefill_impl(q, q_st, q_sh, qo_indptr, tile_to_batch, tile_to_index, num_tiles, k_pool, v_pool,
+                              kv_s_page, kv_s_slot, kv_s_head, block_table, bt_sb, kv_lens, causal_offset, mask,
+                              mask_ndim, m_sb, m_sq, o, o_st, o_sh, B, Hq, Hkv, D, page_size, scale, total_q,
+                              num_splits, workspace, workspace_bytes, stream);
+}
+
+int attn_prefill(const void *q, int64_t q_sb, int64_t q_sl, int64_t q_sh,
+                 const void *k, const void *v, int64_t k_sb, int64_t k_sl, int64_t k_sh,
+                 const int32_t *kv_lens, int kv_len, int is_causal,
+                 const uint8_t *mask, int mask_ndim, int64_t m_sb, int64_t m_sq,
+                 void *o, int64_t o_sb, int64_t o_sl, int64_t o_sh,
+                 int B, int Lq, int Hq, int Hkv, int D, float scale, void *stream) {
+    return dense_prefill_impl(q, q_sb, q_sl, q_sh, k, v, k_sb, k_sl, k_sh, kv_lens, kv_len, is_causal, mask,
+                              mask_ndim, m_sb, m_sq, o, o_sb, o_sl, o_sh, B, Lq, Hq, Hkv, D, scale, 1, nullptr, 0,
+                              stream);
+}
+
+int attn_prefill_split(const void *q, int64_t q_sb, int64_t q_sl, int64_t q_sh,
+                       const void *k, const void *v, int64_t k_sb, int64_t k_sl, int64_t k_sh,
+                       const int32_t *kv_lens, int kv_len, int is_causal,
+                       const uint8_t *mask, int mask_ndim, int64_t m_sb, int64_t m_sq,
+                       void *o, int64_t o_sb, int64_t o_sl, int64_t o_sh,
+                       int B, int Lq, int Hq, int Hkv, int D, float scale,
+                       int num_splits, void *workspace, size_t workspace_bytes, void *stream) {
+    return dense_prefill_impl(q, q_sb, q_sl, q_sh, k, v, k_sb, k_sl, k_sh, kv_lens, kv_len, is_causal, mask,
+                              mask_ndim, m_sb, m_sq, o, o_sb, o_sl, o_sh, B, Lq, Hq, Hkv, D, scale, num_splits,
+                              workspace, workspace_bytes, stream);
 }
 
 int attn_swa_fp8_decode(const void *q, int64_t q_st, int64_t q_sh,

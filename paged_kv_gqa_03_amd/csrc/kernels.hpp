@@ -90,11 +90,31 @@ struct PrefillParams {
     int64_t o_sb, o_st, o_sh;
     int B, Hq, Hkv, G;
     float sl2;               // scale * log2(e)
+    // Split KV: with kv_splits > 1 each workgroup takes an equal share (in
+    // 64-key tiles) of its tile's keys and writes an unnormalised partial
+    // for split s, query row t (packed row, or b * dense_lq + i), head h at
+    // row (s * part_rows + t) * Hq + h of o_part [.., D] and ml_part [.., 2]
+    // (m in natural-log units of the scaled score, l); rows t >= part_rows
+    // are not written.
+    int kv_splits;
+    int part_rows;
+    float *o_part, *ml_part;
 };
 
-// Query heads one prefill workgroup packs (they share a KV head); a work-map
-// tile then has 128 / prefill_heads_packed(G) rows (32 per wave).
+// Query heads one prefill workgroup packs (all G heads of a KV head, G <= 8)
+// and the rows of a work-map tile: 32 per wave, 128 / G for G <= 4; 16 for
+// G = 8 (each wave then takes two heads of the same 16 rows).
 int prefill_heads_packed(int G);
+int prefill_tile_rows(int G);
+
+// Combine of split-KV prefill partials: one wave per (query row, head).
+struct PrefillCombineParams {
+    const float *o_part, *ml_part;
+    int S, rows, Hq;
+    int dense_lq;            // > 0: row t is (b, i) = (t / dense_lq, t % dense_lq)
+    uint16_t *o;
+    int64_t o_sb, o_st, o_sh;
+};
 
 // fp8 sliding-window decode (K = V), head dim 512, 16-head groups.
 struct SwaParams {
@@ -161,6 +181,7 @@ hipError_t launch_kv_append(const KvAppendParams &p, hipStream_t stream);
 hipError_t launch_swa_quantize(const SwaQuantParams &p, hipStream_t stream);
 hipError_t launch_rotary(const RotaryParams &p, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams &p, int D, hipStream_t stream);
+hipError_t launch_prefill_combine(const PrefillCombineParams &p, int D, hipStream_t stream);
 hipError_t launch_decode_combine(const DecodeCombineParams &p, int D, hipStream_t stream);
 hipError_t launch_combine(const CombineParams &p, int D, hipStream_t stream);
 

@@ -8,10 +8,16 @@
 // sequence's keys through the block table, with causality j <= c_b + i and
 // an optional keep-mask, using an online softmax over KV tiles.
 //
-// Work decomposition: one 256-thread workgroup per (work-map tile, group of
-// HP query heads sharing one KV head).  Wave w handles 32 query rows (two
-// 16-row MFMA blocks) of one head; the HP heads of a workgroup read every
-// K/V tile once from LDS.  A tile has 32 * 4 / HP rows (HP = min(G, 4)).
+// Work decomposition: one workgroup per (work-map tile, KV head), which
+// packs all HP = G query heads that share the KV head, so every K/V tile is
+// read once for the whole group (csrc commit on GQA head packing: up to one
+// head per warp of a block, K/V streamed once per block).  A wave holds two
+// 16-row MFMA blocks: for G <= 4, 32 rows of one head (a tile then has
+// 128 / G rows); for G = 8, the same 16 rows of two heads (16-row tiles).
+// Split KV (for short query runs over long contexts, where tiles x KV heads
+// would not fill the device): kv_splits workgroups share a tile's keys in
+// equal runs of 64-key tiles, each writes an unnormalised fp32 partial
+// (o, m, l) per row and head, and a combine merges them by log-sum-exp.
 //
 // Per KV tile of 64 keys the workgroup stages K row-major and V transposed
 // (d-major, keys permuted) in LDS; the transpose is done in registers while
@@ -166,12 +172,12 @@ __device__ __forceinline__ uint32_t nz_bits4(uint32_t w) {
     return ((w & 0x01010101u) * 0x01020408u) >> 24;
 }
 
-template <int MASK, int NQ>
+template <int MASK, int NQ, int ROWS>
 __device__ __forceinline__ void store_mask(const MaskStage<MASK, NQ> &m, int tid, uint8_t *bits) {
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
         const int row = (tid >> 3) + 32 * q;
-        if (MASK == 3 || row == 0)
+        if (row < ROWS)
             bits[row * 8 + (tid & 7)] = (uint8_t)(nz_bits4(m.w[q][0]) | (nz_bits4(m.w[q][1]) << 4));
     }
 }
@@ -216,8 +222,7 @@ __device__ __forceinline__ void store_stage(const StageCtx &sc, const Stage &r, 
 
 template <int D, int HP, int MASK, bool PAGED>
 __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) {
-    constexpr int WPH = 4 / HP;   // waves (32-row groups) per head
-    constexpr int R = 32 * WPH;   // rows per work-map tile
+    constexpr int R = HP <= 4 ? 128 / HP : 16;   // rows per work-map tile
     constexpr int KLD = kld<D>();
     constexpr int NS = D / 32;    // 32-deep steps of Q.K^T
     constexpr int NM = D / 16;    // 16-row blocks of O^T
@@ -228,18 +233,27 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) 
     __shared__ __attribute__((aligned(16))) uint16_t stage_lds[2 * 2 * SBUF];   // [team][buffer]
     __shared__ int32_t pages[kPages];
     constexpr int MROWS = MASK == 3 ? R : 1;                  // mask rows per tile
-    constexpr int NQ = MASK == 3 ? R / 32 : 1;                // mask rows per thread
+    constexpr int NQ = MASK == 3 && R > 32 ? R / 32 : 1;      // mask rows per thread
     __shared__ __attribute__((aligned(8))) uint8_t mbits[2][2][MROWS * 8];
 
     // Two teams of four waves take alternate KV tiles of the same query
     // rows and heads; team 1 hands its state to team 0 at the end.
     const int tid = threadIdx.x, lane = tid & 63;
-    const int team = tid >> 8, ttid = tid & 255, w = (tid >> 6) & 3;
+    // team and wave are wave-uniform: taken through readfirstlane so that
+    // what derives from them (heads, row offsets) sits in scalar registers.
+    const int ttid = tid & 255;
+    const int team = __builtin_amdgcn_readfirstlane(tid >> 8);
+    const int w = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);
     // Tiles in reverse work-map order (a sequence's last, longest tiles
     // first), the head groups of a tile next to each other.
+    // With split KV the splits of a tile follow each other, head groups
+    // innermost.
     const int nhg = p.Hkv * (p.G / HP);
-    const int tile = p.num_tiles - 1 - (int)(blockIdx.x / (unsigned)nhg);
-    const int hg = (int)(blockIdx.x % (unsigned)nhg);
+    const unsigned per_tile = (unsigned)nhg * (unsigned)p.kv_splits;
+    const int tile = p.num_tiles - 1 - (int)(blockIdx.x / per_tile);
+    const int rem = (int)(blockIdx.x % per_tile);
+    const int split = rem / nhg;
+    const int hg = rem - split * nhg;
     // Work map (packed, ragged Q) or the dense schedule: Lq rows per
     // sequence, tiles_per_seq tiles each.
     int b, ti;
@@ -253,7 +267,14 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) 
     }
     const int groups_per_kv = p.G / HP;
     const int g = hg / groups_per_kv;
-    const int hq = g * p.G + (hg % groups_per_kv) * HP + (w % HP);
+    // Row offset (in the tile) and query head of each of the wave's two row
+    // blocks.
+    int rboff[2], hq[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        rboff[rb] = HP <= 4 ? (w / HP) * 32 + 16 * rb : 0;
+        hq[rb] = g * p.G + (hg % groups_per_kv) * HP + (HP <= 4 ? w % HP : 2 * w + rb);
+    }
     const int q0 = p.dense_lq > 0 ? 0 : p.qo_indptr[b];
     const int qn = p.dense_lq > 0 ? p.dense_lq : p.qo_indptr[b + 1] - q0;
     const int n = p.kv_lens ? p.kv_lens[b] : p.kv_len_const;
@@ -270,13 +291,18 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) 
     bool row_ok[2];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-        myrow[rb] = row0 + (w / HP) * 32 + 16 * rb + (lane & 15);   // local query row of this lane
+        myrow[rb] = row0 + rboff[rb] + (lane & 15);   // local query row of this lane
         row_ok[rb] = myrow[rb] < qn;
     }
 
-    // Keys the tile can see: all of the sequence, or up to its causal frontier.
+    // Keys the tile can see: all of the sequence, or up to its causal
+    // frontier; this workgroup's share of them is [k_beg, k_end), whole
+    // 64-key tiles except at the frontier.
     const int last_row = min(qn, row0 + R) - 1;
     const int kv_end = causal_on ? min(n, c + last_row + 1) : n;
+    const int kt_all = kv_end > 0 ? (kv_end + BK - 1) / BK : 0;
+    const int k_beg = (int)((int64_t)split * kt_all / p.kv_splits) * BK;
+    const int k_end = min(kv_end, (int)((int64_t)(split + 1) * kt_all / p.kv_splits) * BK);
 
     // Q^T operands: row myrow[rb], d = 32s + 8*lq .. +8.  A negative scale
     // is applied as |scale| on negated Q (a sign flip, exact), so the row
@@ -289,7 +315,7 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) 
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
         const uint16_t *qr =
-            p.q + qrow0 + (int64_t)min(myrow[rb], qn - 1) * p.q_st + (int64_t)hq * p.q_sh + 8 * lq;
+            p.q + qrow0 + (int64_t)min(myrow[rb], qn - 1) * p.q_st + (int64_t)hq[rb] * p.q_sh + 8 * lq;
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             uint4 v = *reinterpret_cast<const uint4 *>(qr + 32 * s);
@@ -312,7 +338,7 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) 
     // when a score exceeds it by more than 2^8, so P stays <= 256 and the
     // rescale of O is mostly skipped.
     float m_ref[2] = {-INFINITY, -INFINITY};
-    const int wrow0 = row0 + (w / HP) * 32;   // first row of this wave
+    const int wrow0 = row0 + rboff[0];   // first row of this wave
 
     // Staging assignment: keys 4*(tid >> 4) + r (r = 0..3) of K and of V,
     // chunk cc = tid & 15.
@@ -335,7 +361,7 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) 
     // Mask row (within the tile) of each of this lane's two query rows.
     int mloc[2];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) mloc[rb] = MASK == 3 ? (w / HP) * 32 + 16 * rb + (lane & 15) : 0;
+    for (int rb = 0; rb < 2; ++rb) mloc[rb] = MASK == 3 ? rboff[rb] + (lane & 15) : 0;
 
     // Keys row myrow[rb] admits: j < lim[rb] (length and causal frontier);
     // the wave's first row has the smallest limit.
@@ -452,8 +478,8 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) 
     // boundaries, so no tile straddles two.
     const int64_t ch_keys = PAGED ? (int64_t)(kPages - 2) * p.ps / BK * BK : (int64_t)1 << 30;
     const int CH = (int)min<int64_t>(ch_keys > 0 ? ch_keys : BK, 1 << 30);
-    for (int c0 = 0; c0 < kv_end; c0 += CH) {
-        const int c1 = min(kv_end, c0 + CH);
+    for (int c0 = k_beg; c0 < k_end; c0 += CH) {
+        const int c1 = min(k_end, c0 + CH);
         const int t0 = c0 / BK, t1 = (c1 + BK - 1) / BK;
         sc.c1 = c1;
         __syncthreads();   // the previous chunk is done with the slice and the buffers
@@ -470,7 +496,7 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) 
             load_stage<PAGED>(p, sc, kt0, st_regs);
             if constexpr (MASK != 0) load_mask<MASK, NQ>(mc, ttid, n, kt0, mst);
             store_stage<D>(sc, st_regs, kbuf(0), vbuf(0));
-            if constexpr (MASK != 0) store_mask<MASK, NQ>(mst, ttid, mbits[team][0]);
+            if constexpr (MASK != 0) store_mask<MASK, NQ, MROWS>(mst, ttid, mbits[team][0]);
         }
         if (kt0 + 2 < t1) {
             load_stage<PAGED>(p, sc, kt0 + 2, st_regs);
@@ -484,7 +510,7 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) 
                 // The team's next tile into its other buffer (its readers
                 // finished at the last barrier), then the one after goes out.
                 store_stage<D>(sc, st_regs, kbuf((it + 1) & 1), vbuf((it + 1) & 1));
-                if constexpr (MASK != 0) store_mask<MASK, NQ>(mst, ttid, mbits[team][(it + 1) & 1]);
+                if constexpr (MASK != 0) store_mask<MASK, NQ, MROWS>(mst, ttid, mbits[team][(it + 1) & 1]);
                 if (kt + 4 < t1) {
                     load_stage<PAGED>(p, sc, kt + 4, st_regs);
                     if constexpr (MASK != 0) load_mask<MASK, NQ>(mc, ttid, n, kt + 4, mst);
@@ -522,14 +548,34 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) 
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 oacc[rb][m][i] = oacc[rb][m][i] * aa + xch[(rb * (D / 4) + m * 4 + i) * 64 + lane] * ab;
+        m_ref[rb] = mm;   // the merged (O, l) are relative to 2^mm
     }
 
+    if (p.kv_splits > 1) {
+        // Unnormalised partial: O^T column and (m, l), m back in natural-log
+        // units of the scaled score.
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            const int64_t t = (p.dense_lq > 0 ? (int64_t)b * p.dense_lq : (int64_t)q0) + myrow[rb];
+            if (!row_ok[rb] || t >= p.part_rows) continue;
+            const int64_t pr = ((int64_t)split * p.part_rows + t) * p.Hq + hq[rb];
+            float *op = p.o_part + pr * D + 4 * lq;
+#pragma unroll
+            for (int m = 0; m < NM; ++m)
+                *reinterpret_cast<float4 *>(op + 16 * m) =
+                    make_float4(oacc[rb][m][0], oacc[rb][m][1], oacc[rb][m][2], oacc[rb][m][3]);
+            if (lq == 0)
+                *reinterpret_cast<float2 *>(p.ml_part + pr * 2) =
+                    make_float2(m_ref[rb] == -INFINITY ? -INFINITY : m_ref[rb] * kLn2, lacc[rb][0]);
+        }
+        return;
+    }
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
         const float l_row = lacc[rb][0];
         if (!row_ok[rb]) continue;
         const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
-        uint16_t *orow = p.o + orow0 + (int64_t)myrow[rb] * p.o_st + (int64_t)hq * p.o_sh + 4 * lq;
+        uint16_t *orow = p.o + orow0 + (int64_t)myrow[rb] * p.o_st + (int64_t)hq[rb] * p.o_sh + 4 * lq;
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
             uint2 wv;
@@ -542,7 +588,7 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) 
 
 template <int D, int HP, bool PAGED>
 hipError_t launch_hp(const PrefillParams &p, hipStream_t stream) {
-    const dim3 grid((unsigned)p.num_tiles * (unsigned)(p.Hkv * (p.G / HP)));
+    const dim3 grid((unsigned)p.num_tiles * (unsigned)(p.Hkv * (p.G / HP)) * (unsigned)p.kv_splits);
     switch (p.mask_ndim) {
         case 0: hipLaunchKernelGGL((prefill_kernel<D, HP, 0, PAGED>), grid, dim3(512), 0, stream, p); break;
         case 2: hipLaunchKernelGGL((prefill_kernel<D, HP, 2, PAGED>), grid, dim3(512), 0, stream, p); break;
@@ -558,13 +604,82 @@ hipError_t launch_paged(const PrefillParams &p, hipStream_t stream) {
         case 1: return launch_hp<D, 1, PAGED>(p, stream);
         case 2: return launch_hp<D, 2, PAGED>(p, stream);
         case 4: return launch_hp<D, 4, PAGED>(p, stream);
+        case 8: return launch_hp<D, 8, PAGED>(p, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
+// Split-KV combine: wave per (row t, head h); lanes hold EPL consecutive
+// floats of the head row, eight partials in flight per step.
+template <int D>
+__global__ __launch_bounds__(256) void prefill_combine_kernel(const PrefillCombineParams p) {
+    constexpr int EPL = D >= 64 ? D / 64 : 1;
+    constexpr int NL = D / EPL;   // lanes that hold part of the row
+    const int lane = threadIdx.x & 63;
+    const int64_t RH = (int64_t)p.rows * p.Hq;
+    const int64_t item = (int64_t)blockIdx.x * 4 + wave_id();
+    if (item >= RH) return;
+    const int64_t t = item / p.Hq;
+    const int h = (int)(item - t * p.Hq);
+    float M = -INFINITY;
+    for (int s = lane; s < p.S; s += 64) M = fmaxf(M, p.ml_part[((int64_t)s * RH + item) * 2]);
+#pragma unroll
+    for (int k = 1; k < 64; k <<= 1) M = fmaxf(M, __shfl_xor(M, k));
+    float acc[EPL], L = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+    const int ln = min(lane, NL - 1);
+    if (M != -INFINITY) {
+        constexpr int U = 8;
+        for (int s0 = 0; s0 < p.S; s0 += U) {
+            float2 ml[U];
+            float ov[U][EPL];
+#pragma unroll
+            for (int k = 0; k < U; ++k) {
+                const int64_t row = (int64_t)min(s0 + k, p.S - 1) * RH + item;
+                ml[k] = *reinterpret_cast<const float2 *>(p.ml_part + row * 2);
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) ov[k][e] = p.o_part[row * D + ln * EPL + e];
+            }
+#pragma unroll
+            for (int k = 0; k < U; ++k) {
+                const bool use = s0 + k < p.S && ml[k].x != -INFINITY;
+                const float wgt = use ? exp2_fast((ml[k].x - M) * kLog2e) : 0.f;
+                L = fmaf(wgt, use ? ml[k].y : 0.f, L);
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) acc[e] = fmaf(wgt, use ? ov[k][e] : 0.f, acc[e]);
+            }
+        }
+    }
+    if (lane >= NL) return;
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    int64_t off;
+    if (p.dense_lq > 0) {
+        const int64_t bb = t / p.dense_lq;
+        off = bb * p.o_sb + (t - bb * p.dense_lq) * p.o_st;
+    } else {
+        off = t * p.o_st;
+    }
+    uint16_t *dst = p.o + off + (int64_t)h * p.o_sh + lane * EPL;
+    if constexpr (EPL == 2) *reinterpret_cast<uint32_t *>(dst) = pack_bf16(acc[0] * inv, acc[1] * inv);
+    else dst[0] = (uint16_t)(pack_bf16(acc[0] * inv, 0.f) & 0xffffu);
+}
+
 }  // namespace
 
-int prefill_heads_packed(int G) { return G >= 4 ? 4 : G; }
+int prefill_heads_packed(int G) { return G; }
+int prefill_tile_rows(int G) { return G <= 4 ? 128 / G : 16; }
+
+hipError_t launch_prefill_combine(const PrefillCombineParams &p, int D, hipStream_t stream) {
+    const int64_t items = (int64_t)p.rows * p.Hq;
+    if (items <= 0) return hipSuccess;
+    const dim3 grid((unsigned)((items + 3) / 4));
+    if (D == 32) hipLaunchKernelGGL((prefill_combine_kernel<32>), grid, dim3(256), 0, stream, p);
+    else if (D == 64) hipLaunchKernelGGL((prefill_combine_kernel<64>), grid, dim3(256), 0, stream, p);
+    else if (D == 128) hipLaunchKernelGGL((prefill_combine_kernel<128>), grid, dim3(256), 0, stream, p);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
 
 hipError_t launch_prefill(const PrefillParams &p, int D, hipStream_t stream) {
     if (p.num_tiles <= 0) return hipSuccess;

@@ -165,3 +165,60 @@ def test_binding_refuses_non_unit_inner_stride():
     x = torch.zeros(2, 8, 128, dtype=torch.bfloat16)[:, :, ::2]
     with pytest.raises(ValueError):
         pa._unit_inner(x)
+
+
+# --- split-KV prefill: host planner, workspace size, argument checks ------
+def test_prefill_tile_rows_pack_every_head_of_a_group():
+    # 32 rows of one head per wave for G <= 4; G = 8: two heads of 16 rows
+    assert [pa.attn_prefill_tile_rows(128, G) for G in (1, 2, 4, 8)] == [128, 64, 32, 16]
+
+
+def test_prefill_split_planner():
+    # the short-q / long-kv workload: 16 tiles x 4 KV heads = 64 workgroups
+    assert pa.attn_prefill_plan_splits(16, 32, 4, 128, 16384, 256) == 4
+    assert pa.attn_prefill_plan_splits(16, 32, 4, 128, 16384, 1024) == 16
+    # at least 8 key tiles of 64 per split
+    assert pa.attn_prefill_plan_splits(16, 32, 4, 128, 1024, 1024) == 2
+    assert pa.attn_prefill_plan_splits(16, 32, 4, 128, 511, 1024) == 1
+    # enough workgroups already: no split
+    assert pa.attn_prefill_plan_splits(72, 32, 8, 128, 2560, 256) == 1
+    assert pa.attn_prefill_plan_splits(0, 32, 8, 128, 2560, 256) == 1
+    # capped at 256
+    assert pa.attn_prefill_plan_splits(1, 8, 8, 128, 1 << 22, 1 << 20) == 256
+    assert pa.lib().attn_prefill_plan_splits(1, 6, 4, 128, 100, 256) == pa.ATTN_ERR_INVALID_ARG
+
+
+def test_prefill_workspace_bytes_layout():
+    assert pa.attn_prefill_workspace_bytes(100, 32, 128, 1) == 0
+    rows, Hq, D, S = 256, 32, 128, 4
+    o_bytes = S * rows * Hq * D * 4
+    assert pa.attn_prefill_workspace_bytes(rows, Hq, D, S) == (o_bytes + 255) // 256 * 256 + S * rows * Hq * 2 * 4
+    assert pa.attn_prefill_workspace_bytes(3, 2, 32, 3) == (3 * 3 * 2 * 32 * 4 + 255) // 256 * 256 + 3 * 3 * 2 * 8
+
+
+def call_paged_prefill_split(S, ws=None, ws_bytes=0, total_q=40):
+    # 2 sequences, Hq=8, Hkv=2, D=128, page size 16, fake device addresses
+    return pa.lib().attn_paged_prefill_split(
+        FAKE, 8 * 128, 128, FAKE, FAKE, FAKE, 2, FAKE, FAKE, 16 * 2 * 128, 2 * 128, 128, FAKE, 64, FAKE, None,
+        None, 0, 0, 0, FAKE, 8 * 128, 128, 2, 8, 2, 128, 16, 0.088, total_q, S, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("S,ws,ws_bytes,total_q,code,word", [
+    (0, None, 0, 40, pa.ATTN_ERR_INVALID_ARG, "num_splits"),
+    (257, None, 0, 40, pa.ATTN_ERR_INVALID_ARG, "num_splits"),
+    (4, None, 0, 40, pa.ATTN_ERR_WORKSPACE, "workspace"),
+    (4, FAKE, 1000, 40, pa.ATTN_ERR_WORKSPACE, "workspace"),
+    (4, FAKE + 16, 1 << 30, 40, pa.ATTN_ERR_INVALID_ARG, "aligned"),
+    (4, FAKE, 1 << 30, -1, pa.ATTN_ERR_INVALID_ARG, "row"),
+])
+def test_paged_prefill_split_rejects_bad_arguments(S, ws, ws_bytes, total_q, code, word):
+    assert call_paged_prefill_split(S, ws, ws_bytes, total_q) == code
+    assert word in pa.attn_last_error()
+
+
+def test_dense_prefill_split_rejects_short_workspace():
+    lib = pa.lib()
+    rc = lib.attn_prefill_split(FAKE, 16 * 8 * 128, 8 * 128, 128, FAKE, FAKE, 500 * 2 * 128, 2 * 128, 128,
+                                None, 500, 1, None, 0, 0, 0, FAKE, 16 * 8 * 128, 8 * 128, 128,
+                                2, 16, 8, 2, 128, 0.088, 3, FAKE, 4096, None)
+    assert rc == pa.ATTN_ERR_WORKSPACE and "workspace" in pa.attn_last_error()

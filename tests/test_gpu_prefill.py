@@ -240,3 +240,127 @@ def test_prefill_head_dim_32(G, ps, mask_ndim):
     case = workloads.prefill_case(895 + G + ps, 3, 2 * G, 2, 32, (0, 300), (1, 140), ps,
                                   mask_frac=None if mask_ndim is None else 0.2, mask_ndim=mask_ndim or 3)
     assert_close(run_prefill(case), oracle_prefill(case), what="D=32 G=%d ps=%d" % (G, ps))
+
+
+# ------------------------------------------------------------ split KV
+def nan_workspace(nbytes):
+    """Workspace filled with 0xFF bytes (every float a NaN): a partial the
+    kernel failed to write would poison the combine."""
+    return torch.full((max(nbytes, 1),), 0xFF, dtype=torch.uint8, device=DEV)
+
+
+def run_prefill_split(case, S, causal=True):
+    G = case["Hq"] // case["Hkv"]
+    R = pa.attn_prefill_tile_rows(case["D"], G)
+    _, t2b, t2i = pa.attn_prefill_plan(case["q_lens"], R)
+    d = {k: case[k].to(DEV) for k in ("q", "k_pool", "v_pool", "block_table", "kv_lens", "qo_indptr",
+                                     "causal_offset")}
+    mask = case["mask"].to(DEV) if case["mask"] is not None else None
+    total_q = d["q"].shape[0]
+    ws = nan_workspace(pa.attn_prefill_workspace_bytes(total_q, case["Hq"], case["D"], S))
+    out = torch.full_like(d["q"], float("nan"))
+    pa.attn_paged_prefill_split(d["q"], d["qo_indptr"], t2b.to(DEV), t2i.to(DEV), d["k_pool"], d["v_pool"],
+                                d["block_table"], d["kv_lens"], out, case["page_size"], case["scale"],
+                                max(case["kv_lens"].tolist() + [0]),
+                                causal_offset=d["causal_offset"] if causal else None, mask=mask,
+                                num_splits=S, workspace=ws)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("G,ps,S,D,mask_ndim", [
+    (8, 16, 4, 128, None),
+    (4, 16, 3, 128, 3),
+    (2, 5, 7, 128, 2),
+    (1, 1, 2, 128, None),
+    (8, 3, 5, 64, 3),
+    (4, 16, 6, 32, None),
+    (8, 16, 1, 128, None),
+])
+def test_split_prefill_matches_oracle(G, ps, S, D, mask_ndim):
+    """Short query runs over long contexts, keys split over S workgroups per
+    tile (S = 1 runs the plain kernel through the split entry point)."""
+    case = workloads.prefill_case(900 + G + ps + S + D, 3, 2 * G, 2, D, None, None, ps,
+                                  q_lens=[16, 5, 1], ctx_lens=[1200, 777, 1600],
+                                  mask_frac=None if mask_ndim is None else 0.2, mask_ndim=mask_ndim or 3)
+    # Over ~1000 keys the outputs are ~0.03 in size; the absolute bar is
+    # tightened to 2e-3 (rounding of P to bf16 contributes ~1e-4 here).
+    assert_close(run_prefill_split(case, S), oracle_prefill(case), atol=2e-3,
+                 what="split G=%d ps=%d S=%d D=%d" % (G, ps, S, D))
+
+
+def test_split_prefill_more_splits_than_key_tiles():
+    """Splits past a tile's last key tile hold no key: they write an empty
+    partial (m = -inf, l = 0) that the combine ignores; causal frontiers and a
+    sequence without keys give the oracle's zeros."""
+    case = workloads.prefill_case(930, 4, 16, 2, 128, None, None, 16, q_lens=[40, 3, 70, 9],
+                                  ctx_lens=[10, 0, 200, 0])
+    case["causal_offset"][3] = -1
+    out = run_prefill_split(case, 9)
+    assert_close(out, oracle_prefill(case), what="S=9 short contexts")
+
+
+def test_split_prefill_fully_masked_rows_give_zero():
+    case = workloads.prefill_case(935, 2, 8, 2, 128, None, None, 16, q_lens=[20, 9], ctx_lens=[900, 500],
+                                  mask_frac=0.0, mask_ndim=3)
+    case["mask"][0, 3, :] = False
+    case["mask"][1, :, :] = False
+    out = run_prefill_split(case, 4).cpu()
+    assert torch.equal(out[3], torch.zeros_like(out[3]))
+    assert torch.equal(out[20:29], torch.zeros_like(out[20:29]))
+    assert_close(out, oracle_prefill(case))
+
+
+@pytest.mark.parametrize("B,Lq,Lk,G,layout,S,ndim", [
+    (2, 16, 1500, 8, "blhd", 4, 0),
+    (3, 40, 900, 4, "bhld", 3, 3),
+    (2, 1, 2000, 2, "blhd", 8, 2),
+])
+def test_dense_split_prefill_matches_oracle(B, Lq, Lk, G, layout, S, ndim):
+    Hkv = 2
+    q, k, v, mask = dense_case(940 + B + Lq + S, B, Lq, Lk, Hkv * G, Hkv, layout=layout, mask_ndim=ndim)
+    scale = 1.0 / math.sqrt(128)
+    kv_lens = torch.tensor([Lk - 7 * b for b in range(B)], dtype=torch.int32)
+    ref = oracle_dense(q, k, v, kv_lens, True, mask, scale)
+    out = torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device=DEV)
+    ws = nan_workspace(pa.attn_prefill_workspace_bytes(B * Lq, Hkv * G, 128, S))
+    pa.attn_prefill_split(q.to(DEV), k.to(DEV), v.to(DEV), out, scale, is_causal=True, kv_lens=kv_lens.to(DEV),
+                          mask=None if mask is None else mask.to(DEV), num_splits=S, workspace=ws)
+    torch.cuda.synchronize()
+    assert_close(out, ref, atol=2e-3, what="dense split B=%d Lq=%d Lk=%d G=%d S=%d" % (B, Lq, Lk, G, S))
+
+
+def test_split_prefill_short_q_long_kv_workload():
+    """G = 8, 16 sequences of 16 new rows after 16368 cached keys (Hq = 32,
+    Hkv = 4, D = 128, page size 16), planner-chosen splits, in the launch
+    configuration the benchmark times.  At this size the split result is
+    checked against the unsplit kernel everywhere (same math, other
+    summation order) and against the oracle on four whole sequences.  The
+    outputs average 16384 values (~0.01 in size), so the absolute bar is
+    1e-3."""
+    case = workloads.short_q_prefill(device=DEV)
+    G = case["Hq"] // case["Hkv"]
+    R = pa.attn_prefill_tile_rows(128, G)
+    _, t2b, t2i = pa.attn_prefill_plan(case["q_lens"], R)
+    t2b, t2i = t2b.to(DEV), t2i.to(DEV)
+    args = (case["q"], case["qo_indptr"], t2b, t2i, case["k_pool"], case["v_pool"], case["block_table"],
+            case["kv_lens"])
+    S = pa.attn_prefill_plan_splits(t2b.numel(), case["Hq"], case["Hkv"], 128, max(case["kv_lens"].tolist()))
+    assert S > 1
+    out_s = torch.full_like(case["q"], float("nan"))
+    pa.attn_paged_prefill_split(*args, out_s, 16, case["scale"], max(case["kv_lens"].tolist()),
+                                causal_offset=case["causal_offset"], num_splits=S)
+    out_1 = torch.full_like(case["q"], float("nan"))
+    pa.attn_paged_prefill(*args, out_1, 16, case["scale"], causal_offset=case["causal_offset"])
+    torch.cuda.synchronize()
+    assert_close(out_s, out_1.double().cpu(), atol=1e-3, what="split vs unsplit")
+    # oracle on four sequences: the same pools through their own table rows
+    cpu = {k: case[k].cpu() for k in ("q", "k_pool", "v_pool", "block_table", "kv_lens", "causal_offset",
+                                     "qo_indptr")}
+    for b in (0, 5, 11, 15):
+        r0, r1 = int(cpu["qo_indptr"][b]), int(cpu["qo_indptr"][b + 1])
+        ref, _ = oracle.paged_prefill(cpu["q"][r0:r1], torch.tensor([0, r1 - r0], dtype=torch.int32),
+                                      cpu["k_pool"], cpu["v_pool"], cpu["block_table"][b:b + 1],
+                                      cpu["kv_lens"][b:b + 1], case["scale"],
+                                      causal_offset=cpu["causal_offset"][b:b + 1], mask=None)
+        assert_close(out_s[r0:r1], ref, atol=1e-3, what="sequence %d vs oracle" % b)

@@ -205,6 +205,14 @@ def ragged_prefill(device="cpu", masked=False, seed=1005):
                         mask_frac=0.1 if masked else None, mask_ndim=3, device=device)
 
 
+def short_q_prefill(device="cpu", seed=1007):
+    """Short query runs over long contexts: 16 sequences of 16 new rows after
+    16368 cached keys (16384 in all), Hq=32, Hkv=4 (G = 8), D=128, ps=16,
+    causal_offset = cached keys."""
+    return prefill_case(seed, 16, 32, 4, 128, None, None, 16, device=device,
+                        q_lens=[16] * 16, ctx_lens=[16368] * 16)
+
+
 def swa_fp8(device="cpu", seed=1006):
     """T=64, NH=128 (16-head groups), HD=512, window 128, lens ~ U[1, 128],
     block_size 256, 128 blocks (32768 slots)."""
