@@ -301,6 +301,7 @@ def run_extras(torch, pa, dev, args):
     out["ragged_prefill"] = bench_prefill(torch, pa, dev, steps, warm, masked=False)
     out["ragged_prefill_masked"] = bench_prefill(torch, pa, dev, steps, warm, masked=True)
     out["dense_prefill_b4_l2048_causal"] = bench_dense_prefill(torch, pa, dev, steps, warm)
+    out["short_q_prefill_g8_b16_q16_kv16384"] = bench_short_q_prefill(torch, pa, dev, steps, warm)
     out["swa_fp8"] = bench_swa(torch, pa, dev, steps, warm)
     out.update(bench_cache_ops(torch, pa, dev, steps, warm))
     return out
@@ -423,6 +424,41 @@ def bench_prefill(torch, pa, dev, steps, warm, masked):
     tf = fl / (ms * 1e-3) / 1e12
     return {"us_per_call": round(ms * 1e3, 2), "TFLOP/s": round(tf, 1), "gflop_per_call": round(fl / 1e9, 2),
             "mfma_util": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "rotation_sets": len(sets)}
+
+
+def bench_short_q_prefill(torch, pa, dev, steps, warm):
+    """Short query runs over long contexts (the head-packing benchmark shape):
+    16 sequences x 16 new rows after 16368 cached keys, Hq=32 Hkv=4 (G=8),
+    D=128, ps=16, causal.  HBM-bound: algorithmic bytes are the K/V of every
+    sequence once, Q and O, and the block table.  Timed with the planner's
+    split count and unsplit (num_splits 1), two input sets rotated."""
+    import workloads
+    sets = [workloads.short_q_prefill(device=dev, seed=1007 + 7919 * r) for r in range(2)]
+    R = pa.attn_prefill_tile_rows(128, 8)
+    for s in sets:
+        _, t2b, t2i = pa.attn_prefill_plan(s["q_lens"], R)
+        s["t2b"], s["t2i"] = t2b.to(dev), t2i.to(dev)
+        s["out"] = torch.empty_like(s["q"])
+    c0 = sets[0]
+    mx = max(c0["kv_lens"].tolist())
+    total_q = c0["q"].shape[0]
+    S = pa.attn_prefill_plan_splits(c0["t2b"].numel(), 32, 4, 128, mx)
+    ws = torch.empty(max(256, pa.attn_prefill_workspace_bytes(total_q, 32, 128, S)), dtype=torch.uint8, device=dev)
+    nbytes = (sum(c0["kv_lens"].tolist()) * 4 * 128 * 4 + 2 * total_q * 32 * 128 * 2
+              + sum((n + 15) // 16 for n in c0["kv_lens"].tolist()) * 4)
+    res = {}
+    for label, n_split in (("split", S), ("unsplit", 1)):
+        def call(s, n_split=n_split):
+            pa.attn_paged_prefill_split(s["q"], s["qo_indptr"], s["t2b"], s["t2i"], s["k_pool"], s["v_pool"],
+                                        s["block_table"], s["kv_lens"], s["out"], 16, s["scale"], mx,
+                                        causal_offset=s["causal_offset"], num_splits=n_split, workspace=ws)
+        ms = time_calls(torch, call, sets, steps, warm)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        res[label] = {"us_per_call": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
+                      "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4), "num_splits": n_split}
+    res["rotation_sets"] = len(sets)
+    res["mb_per_call"] = round(nbytes / 1e6, 1)
+    return res
 
 
 def bench_dense_prefill(torch, pa, dev, steps, warm):

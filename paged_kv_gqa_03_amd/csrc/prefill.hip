@@ -81,6 +81,7 @@ struct Stage {
 struct StageCtx {
     int cc, kg;
     bool stager;                    // this thread stages (16 groups of 4 keys x D/8 chunks)
+    bool stream;                    // no other workgroup reads these keys: non-temporal loads
     int first_pg, c1;               // page slice start; keys of this chunk end at c1
     const int32_t *pages;           // LDS page slice
     const uint16_t *kbase, *vbase;
@@ -95,6 +96,11 @@ __device__ __forceinline__ uint64_t key_off(const PrefillParams &p, const StageC
 }
 
 __device__ __forceinline__ uint4 ld16(const uint16_t *ptr) { return *reinterpret_cast<const uint4 *>(ptr); }
+__device__ __forceinline__ uint4 ld16_nt(const uint16_t *ptr) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(ptr));
+    return make_uint4(t.x, t.y, t.z, t.w);
+}
 
 // The thread's share of tile kt: keys 4kg .. 4kg+3, chunk cc, of K and of V
 // (the sources share strides, so the four offsets serve both).  Paged: when
@@ -118,14 +124,25 @@ __device__ __forceinline__ void load_stage(const PrefillParams &p, const StageCt
 #pragma unroll
         for (int i = 0; i < 4; ++i) off[i] = key_off(p, sc, k0 + i);
     }
-    r.k0 = ld16(sc.kbase + off[0]);
-    r.k1 = ld16(sc.kbase + off[1]);
-    r.k2 = ld16(sc.kbase + off[2]);
-    r.k3 = ld16(sc.kbase + off[3]);
-    r.v0 = ld16(sc.vbase + off[0]);
-    r.v1 = ld16(sc.vbase + off[1]);
-    r.v2 = ld16(sc.vbase + off[2]);
-    r.v3 = ld16(sc.vbase + off[3]);
+    if (sc.stream) {
+        r.k0 = ld16_nt(sc.kbase + off[0]);
+        r.k1 = ld16_nt(sc.kbase + off[1]);
+        r.k2 = ld16_nt(sc.kbase + off[2]);
+        r.k3 = ld16_nt(sc.kbase + off[3]);
+        r.v0 = ld16_nt(sc.vbase + off[0]);
+        r.v1 = ld16_nt(sc.vbase + off[1]);
+        r.v2 = ld16_nt(sc.vbase + off[2]);
+        r.v3 = ld16_nt(sc.vbase + off[3]);
+    } else {
+        r.k0 = ld16(sc.kbase + off[0]);
+        r.k1 = ld16(sc.kbase + off[1]);
+        r.k2 = ld16(sc.kbase + off[2]);
+        r.k3 = ld16(sc.kbase + off[3]);
+        r.v0 = ld16(sc.vbase + off[0]);
+        r.v1 = ld16(sc.vbase + off[1]);
+        r.v2 = ld16(sc.vbase + off[2]);
+        r.v3 = ld16(sc.vbase + off[3]);
+    }
 }
 
 // Keep-mask of one tile, staged like K and V: thread t loads bytes
@@ -346,6 +363,10 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) 
     sc.cc = ttid % CPR;
     sc.kg = ttid / CPR;
     sc.stager = sc.kg < 16;
+    // A sequence of one row tile has its keys read by this workgroup alone
+    // (all query heads of the KV head are packed here): stream them past the
+    // caches.  Longer sequences keep them cached for their other row tiles.
+    sc.stream = qn <= R;
     sc.pages = pages;
     const int64_t seq_base = PAGED ? 0 : (int64_t)b * p.k_sb;   // contiguous: the sequence's K/V
     sc.kbase = p.k + seq_base + (int64_t)g * p.s_head + sc.cc * 8;
