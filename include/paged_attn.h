@@ -109,7 +109,7 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int D, int num_splits);
  *               on the current device
  *   workspace   >= attn_decode_workspace_bytes(B, Hq, D, W) bytes, device,
  *               256-byte aligned (may be NULL when W = 1)
- * Supported: D in {64, 128}, G = Hq/Hkv in {1, 2, 4, 8}.
+ * Supported: D in {32, 64, 128, 256}, G = Hq/Hkv in {1, 2, 4, 8}.
  * Launches the split kernel, then the combine kernel, which merges rows
  * spread over several slices and zeroes rows without keys.
  */
@@ -137,7 +137,7 @@ int attn_decode(const void *q, int64_t q_sb, int64_t q_sh,
  *   max_kv_len  host-side bound on kv_lens, used by the planner;
  *          max_kv_len * page_size must stay below 2^32
  *   o      [B, Hq, D] bf16 output
- * Supported: D in {32, 64, 128}, G in {1, 2, 4, 8}, any page_size >= 1.
+ * Supported: D in {32, 64, 128, 256}, G in {1, 2, 4, 8}, any page_size >= 1.
  * A slice longer than 510 pages is processed as consecutive sub-pieces.
  */
 int attn_paged_decode(const void *q, int64_t q_sb, int64_t q_sh,
@@ -182,7 +182,7 @@ int attn_decode_combine(const void *workspace, size_t workspace_bytes, int B, in
  *   lse      NULL or float [R]: M + log(sum_s exp(m_s - M) l_s)
  * out = sum_s exp(m_s - M) o_s / sum_s exp(m_s - M) l_s with M = max_s m_s;
  * a partial with m = -inf contributes nothing; a row whose partials are all
- * empty gives 0 (lse = -inf).  D in {64, 128}.
+ * empty gives 0 (lse = -inf).  D in {32, 64, 128, 256}.
  */
 int attn_split_combine(const float *o_part, const float *ml_part, int S, int R, int D,
                        float *out_f32, void *out_bf16, float *lse, void *stream);

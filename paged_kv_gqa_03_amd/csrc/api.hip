@@ -60,12 +60,12 @@ constexpr int kPrefillWgPerCu = 1;     // prefill workgroups resident per CU (51
 constexpr int kMinSplitKeyTiles = 8;   // fewest 64-key tiles the prefill planner gives one split
 
 // KV heads one decode wave covers: with the heads of a token adjacent in
-// memory (head stride == D) a wave takes up to 8 of them so each token's
-// rows form one contiguous read; otherwise one head, whose tokens are then
-// the contiguous direction.
+// memory (head stride == D) a wave takes up to 8 of them (4 at D = 256,
+// where 16 lanes share a head row) so each token's rows form one contiguous
+// read; otherwise one head, whose tokens are then the contiguous direction.
 int heads_per_wave(int Hkv, int64_t kv_s_head, int D) {
     if (kv_s_head != D) return 1;
-    int hw = 8;
+    int hw = D == 256 ? 4 : 8;
     while (hw > 1 && Hkv % hw != 0) hw >>= 1;
     return hw;
 }
@@ -77,6 +77,8 @@ int max_sub_piece(int page_size) {
     const long c = (long)(pa::kDecodeMaxSplitPages - 2) * page_size;
     return (int)(c > (1L << 30) ? (1L << 30) : c);
 }
+
+bool decode_dim(int D) { return D == 32 || D == 64 || D == 128 || D == 256; }
 
 int check_heads(int Hq, int Hkv, int D, int *G) {
     if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0)
@@ -208,7 +210,7 @@ int attn_decode(const void *q, int64_t q_sb, int64_t q_sh,
     int G = 0, rc = check_heads(Hq, Hkv, D, &G);
     if (rc) return rc;
     if (B < 0 || kv_len < 0) return fail(ATTN_ERR_INVALID_ARG, "attn_decode: negative B or kv_len");
-    if (D != 64 && D != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_decode: head dim %d not built (64, 128)", D);
+    if (!decode_dim(D)) return fail(ATTN_ERR_UNSUPPORTED, "attn_decode: head dim %d not built (32, 64, 128, 256)", D);
     if (!q || !k || !v || !o) return fail(ATTN_ERR_INVALID_ARG, "attn_decode: null tensor pointer");
     if (!std::isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "attn_decode: scale is not finite");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
@@ -252,7 +254,7 @@ static int paged_decode_impl(const void *q, int64_t q_sb, int64_t q_sh,
     if (page_size <= 0) return fail(ATTN_ERR_INVALID_ARG, "%s: page_size must be >= 1", fn);
     if ((uint64_t)max_kv_len * (uint64_t)page_size >= (1ull << 32))
         return fail(ATTN_ERR_UNSUPPORTED, "%s: max_kv_len * page_size must be < 2^32", fn);
-    if (D != 64 && D != 128) return fail(ATTN_ERR_UNSUPPORTED, "%s: head dim %d not built (64, 128)", fn, D);
+    if (!decode_dim(D)) return fail(ATTN_ERR_UNSUPPORTED, "%s: head dim %d not built (32, 64, 128, 256)", fn, D);
     if (!q || !k_pool || !v_pool || (!o && mode == 0) || !block_table || !kv_lens)
         return fail(ATTN_ERR_INVALID_ARG, "%s: null pointer", fn);
     if (!std::isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "%s: scale is not finite", fn);
@@ -317,7 +319,7 @@ int attn_decode_combine(const void *workspace, size_t workspace_bytes, int B, in
     if (rc) return rc;
     if (B < 0 || max_kv_len < 0 || num_splits < 1 || num_splits > kMaxWaves)
         return fail(ATTN_ERR_INVALID_ARG, "attn_decode_combine: bad sizes");
-    if (D != 64 && D != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_combine: head dim %d not built", D);
+    if (!decode_dim(D)) return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_combine: head dim %d not built", D);
     if (!o) return fail(ATTN_ERR_INVALID_ARG, "attn_decode_combine: null output");
     if (!aligned16(o) || !mult8(o_sb) || !mult8(o_sh))
         return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_combine: output rows must be 16-byte aligned");
@@ -332,7 +334,7 @@ int attn_decode_combine(const void *workspace, size_t workspace_bytes, int B, in
 int attn_split_combine(const float *o_part, const float *ml_part, int S, int R, int D,
                        float *out_f32, void *out_bf16, float *lse, void *stream) {
     if (S < 1 || R < 0) return fail(ATTN_ERR_INVALID_ARG, "attn_split_combine: bad S or R");
-    if (D != 64 && D != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_split_combine: head dim %d not built", D);
+    if (!decode_dim(D)) return fail(ATTN_ERR_UNSUPPORTED, "attn_split_combine: head dim %d not built", D);
     if (!o_part || !ml_part) return fail(ATTN_ERR_INVALID_ARG, "attn_split_combine: null partials");
     if (!out_f32 && !out_bf16 && !lse) return fail(ATTN_ERR_INVALID_ARG, "attn_split_combine: no output");
     if (((uintptr_t)ml_part & 7u) || ((uintptr_t)o_part & 7u) || (out_bf16 && ((uintptr_t)out_bf16 & 3u)))

@@ -20,18 +20,20 @@
 // wave or row boundary increments w or r, so r + w names each piece
 // uniquely and a row's pieces occupy consecutive slots.
 //
-// Lane layout: lane l = 8*grp + jj, with lane group grp = tg*HW + hw: hw
-// picks the KV head of the row, tg one of TG = 8/HW token streams, jj one
-// of 8 chunk lanes.  A tile is 2*TG tokens; per tile a lane holds tokens tg
-// and tg+TG and, for each, the 16-byte chunks jj, jj+8, ... of its head's K
-// and V rows (D/64 chunks).  HW is chosen from the layout so that one load
-// instruction reads memory that is contiguous: with the KV heads of a token
-// adjacent ([pages, slot, head, dim] pools, blhd) HW = 8 and a tile is two
-// tokens of whole 2 KB rows (a 16-token page is one 32 KB stream); with a
-// head's tokens adjacent ([pages, head, slot, dim], bhld) HW = 1 and a tile
-// is 16 tokens of one head (4 KB contiguous).
-//   scores  v_dot2_f32_bf16 of q and K chunks, summed over the 8 chunk lanes
-//           with three DPP adds (quad_perm x2, row_half_mirror);
+// Lane layout: lane l = JJ*grp + jj, with lane group grp = tg*HW + hw: hw
+// picks the KV head of the row, tg one of TG = (64/JJ)/HW token streams, jj
+// one of JJ chunk lanes (JJ = 8 for D = 64 and 128, 4 for D = 32, 16 for
+// D = 256).  A tile is 2*TG tokens; per tile a lane holds tokens tg and
+// tg+TG and, for each, the 16-byte chunks jj, jj+JJ, ... of its head's K and
+// V rows (NCH = D/(8*JJ) chunks: 1, or 2 at D = 128 and 256).  HW is chosen
+// from the layout so that one load instruction reads memory that is
+// contiguous: with the KV heads of a token adjacent ([pages, slot, head,
+// dim] pools, blhd) HW = min(8, 64/JJ) and at D = 128 a tile is two tokens
+// of whole 2 KB rows (a 16-token page is one 32 KB stream); with a head's
+// tokens adjacent ([pages, head, slot, dim], bhld) HW = 1 and at D = 128 a
+// tile is 16 tokens of one head (4 KB contiguous).
+//   scores  v_dot2_f32_bf16 of q and K chunks, summed over the JJ chunk
+//           lanes with DPP adds (quad_perm x2, row_half_mirror, row_mirror);
 //   softmax each lane group keeps its own running state; the reference max
 //           is only raised when a score exceeds it by more than 2^8 (base 2),
 //           so rescaling of the accumulator is rare, and every exp2
@@ -116,15 +118,32 @@ __device__ __forceinline__ int wave_of(int64_t x, int64_t T, int W) {
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// Chunk lanes per head row and 16-byte chunks per lane at head dim D.
+template <int D>
+constexpr int chunk_lanes() { return D == 32 ? 4 : (D == 256 ? 16 : 8); }
+
+// Sum over aligned groups of JJ lanes (4, 8 or 16), result in every lane.
+template <int JJ>
+__device__ __forceinline__ float sum_lanes(float x) {
+    x += dpp_mov<kDppXor1>(x);
+    x += dpp_mov<kDppXor2>(x);
+    if constexpr (JJ >= 8) x += dpp_mov<kDppHalfMirror>(x);
+    if constexpr (JJ >= 16) x += dpp_mov<kDppMirror>(x);
+    return x;
+}
+
 template <int D, int G, int HW, bool PAGED>
 __global__ __launch_bounds__(64, (G >= 8 ? 1 : 2)) void decode_split_kernel(const DecodeParams p) {
-    constexpr int NCH = D / 64;
-    constexpr int TG = 8 / HW;          // token streams per head
+    constexpr int JJ = chunk_lanes<D>();
+    constexpr int NCH = D / (8 * JJ);   // 16-byte chunks per lane and row
+    constexpr int CS = 8 * JJ;          // elements between a lane's chunks
+    constexpr int TG = 64 / JJ / HW;    // token streams per head
+    static_assert(TG >= 1, "a wave holds at most 64 / JJ KV heads");
     constexpr int TILE = 2 * TG;        // tokens per tile
     constexpr int HWG = HW * G;         // query heads per row
     const int lane = threadIdx.x & 63;
     const int w = blockIdx.x;
-    const int grp = lane >> 3, jj = lane & 7;
+    const int grp = lane / JJ, jj = lane % JJ;
     const int hw = grp % HW, tg = grp / HW;
 
     // This wave's slice [a, e) of the line of all rows (wave-uniform values,
@@ -173,7 +192,7 @@ __global__ __launch_bounds__(64, (G >= 8 ? 1 : 2)) void decode_split_kernel(cons
 #pragma unroll
             for (int h = 0; h < G; ++h)
 #pragma unroll
-                for (int c = 0; c < NCH; ++c) load16(qb + h * p.q_sh + c * 64, qv[h][c]);
+                for (int c = 0; c < NCH; ++c) load16(qb + h * p.q_sh + c * CS, qv[h][c]);
         }
         float o[G][NCH][8];
         float mref[G], lsum[G];
@@ -240,13 +259,13 @@ __global__ __launch_bounds__(64, (G >= 8 ? 1 : 2)) void decode_split_kernel(cons
                 const uint16_t *vA = vbase + ova, *vB = vbase + ovb;
 #pragma unroll
                 for (int c = 0; c < NCH; ++c) {
-                    load16_stream(kA + c * 64, rg.ka[c]);
-                    load16_stream(kB + c * 64, rg.kb[c]);
+                    load16_stream(kA + c * CS, rg.ka[c]);
+                    load16_stream(kB + c * CS, rg.kb[c]);
                 }
 #pragma unroll
                 for (int c = 0; c < NCH; ++c) {
-                    load16_stream(vA + c * 64, rg.va[c]);
-                    load16_stream(vB + c * 64, rg.vb[c]);
+                    load16_stream(vA + c * CS, rg.va[c]);
+                    load16_stream(vB + c * CS, rg.vb[c]);
                 }
             };
             auto compute = [&](int t, const KVRegs<NCH> &rg) {
@@ -263,8 +282,8 @@ __global__ __launch_bounds__(64, (G >= 8 ? 1 : 2)) void decode_split_kernel(cons
                             sa = dot2(rg.ka[c][q], qv[h][c][q], sa);
                             sb = dot2(rg.kb[c][q], qv[h][c][q], sb);
                         }
-                    sa = sum8(sa);
-                    sb = sum8(sb);
+                    sa = sum_lanes<JJ>(sa);
+                    sb = sum_lanes<JJ>(sb);
                     xa[h] = oka ? sa * p.sl2 : -INFINITY;
                     xb[h] = okb ? sb * p.sl2 : -INFINITY;
                 }
@@ -335,17 +354,17 @@ __global__ __launch_bounds__(64, (G >= 8 ? 1 : 2)) void decode_split_kernel(cons
         }
 
         // Merge the TG token streams of each head (lanes equal in hw and jj,
-        // i.e. lane ids differing in the bits above 8*HW).
+        // i.e. lane ids differing in the bits above JJ*HW).
         if constexpr (TG > 1) {
 #pragma unroll
             for (int h = 0; h < G; ++h) {
                 float M = mref[h];
 #pragma unroll
-                for (int m = 8 * HW; m < 64; m <<= 1) M = fmaxf(M, __shfl_xor(M, m));
+                for (int m = JJ * HW; m < 64; m <<= 1) M = fmaxf(M, __shfl_xor(M, m));
                 const float f = (mref[h] == -INFINITY) ? 0.f : exp2_fast(mref[h] - M);
                 float l = lsum[h] * f;
 #pragma unroll
-                for (int m = 8 * HW; m < 64; m <<= 1) l += __shfl_xor(l, m);
+                for (int m = JJ * HW; m < 64; m <<= 1) l += __shfl_xor(l, m);
                 lsum[h] = l;
                 mref[h] = M;
 #pragma unroll
@@ -354,7 +373,7 @@ __global__ __launch_bounds__(64, (G >= 8 ? 1 : 2)) void decode_split_kernel(cons
                     for (int x = 0; x < 8; ++x) {
                         float v = o[h][c][x] * f;
 #pragma unroll
-                        for (int m = 8 * HW; m < 64; m <<= 1) v += __shfl_xor(v, m);
+                        for (int m = JJ * HW; m < 64; m <<= 1) v += __shfl_xor(v, m);
                         o[h][c][x] = v;
                     }
             }
@@ -379,16 +398,16 @@ __global__ __launch_bounds__(64, (G >= 8 ? 1 : 2)) void decode_split_kernel(cons
                     v.y = pack_bf16(o[h][c][2] * inv, o[h][c][3] * inv);
                     v.z = pack_bf16(o[h][c][4] * inv, o[h][c][5] * inv);
                     v.w = pack_bf16(o[h][c][6] * inv, o[h][c][7] * inv);
-                    *reinterpret_cast<uint4 *>(dst + c * 64) = v;
+                    *reinterpret_cast<uint4 *>(dst + c * CS) = v;
                 }
             } else {
                 const int64_t prow = slot * HWG + hw * G + h;
                 float *dst = p.o_part + prow * D + jj * 8;
 #pragma unroll
                 for (int c = 0; c < NCH; ++c) {
-                    *reinterpret_cast<float4 *>(dst + c * 64) =
+                    *reinterpret_cast<float4 *>(dst + c * CS) =
                         make_float4(o[h][c][0], o[h][c][1], o[h][c][2], o[h][c][3]);
-                    *reinterpret_cast<float4 *>(dst + c * 64 + 4) =
+                    *reinterpret_cast<float4 *>(dst + c * CS + 4) =
                         make_float4(o[h][c][4], o[h][c][5], o[h][c][6], o[h][c][7]);
                 }
                 if (jj == 0)
@@ -398,13 +417,20 @@ __global__ __launch_bounds__(64, (G >= 8 ? 1 : 2)) void decode_split_kernel(cons
     }
 }
 
+// Floats of a head row each combine lane holds, and the lanes that hold
+// some (D / epl; all 64 except at D = 32).
+template <int D>
+constexpr int combine_epl() { return D >= 64 ? D / 64 : 1; }
+
 // Log-sum-exp merge of S partials at rows first + s*stride:
 // M = max_s m_s, w_s = exp(m_s - M), out = sum_s w_s o_s / sum_s w_s l_s.
+// Lanes past the row (D = 32) read its last elements and are not stored.
 template <int D>
 __device__ __forceinline__ void merge_partials(const float *o_part, const float *ml_part, int64_t first,
-                                               int64_t stride, int S, int lane, float (&acc)[D / 64], float &L,
-                                               float &M) {
-    constexpr int NC = D / 64;
+                                               int64_t stride, int S, int lane,
+                                               float (&acc)[combine_epl<D>()], float &L, float &M) {
+    constexpr int NC = combine_epl<D>();
+    const int ln = min(lane, D / NC - 1);
     M = -INFINITY;
     for (int s = lane; s < S; s += 64) M = fmaxf(M, ml_part[(first + s * stride) * 2]);
 #pragma unroll
@@ -422,7 +448,7 @@ __device__ __forceinline__ void merge_partials(const float *o_part, const float 
         for (int k = 0; k < U; ++k) {
             const int64_t row = first + (int64_t)min(s0 + k, S - 1) * stride;
             ml[k] = *reinterpret_cast<const float2 *>(ml_part + row * 2);
-            const float *op = o_part + row * D + lane * NC;
+            const float *op = o_part + row * D + ln * NC;
 #pragma unroll
             for (int c = 0; c < NC; ++c) ov[k][c] = op[c];
         }
@@ -437,21 +463,36 @@ __device__ __forceinline__ void merge_partials(const float *o_part, const float 
     }
 }
 
+// The lane's NC floats of a row, scaled by inv, as bf16 (32-bit stores).
+template <int NC>
+__device__ __forceinline__ void store_row_bf16(uint16_t *dst, const float (&acc)[NC], float inv) {
+    if constexpr (NC == 1) {
+        dst[0] = (uint16_t)(pack_bf16(acc[0] * inv, 0.f) & 0xffffu);
+    } else {
+#pragma unroll
+        for (int c = 0; c < NC; c += 2)
+            *reinterpret_cast<uint32_t *>(dst + c) = pack_bf16(acc[c] * inv, acc[c + 1] * inv);
+    }
+}
+
 // Combine of the balanced decode partition: one wave per (sequence, query
 // head), four to a workgroup.  A row's pieces are the slots r + w for the
 // waves w that hold its first and last token.
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeCombineParams p) {
-    constexpr int NC = D / 64;
+    constexpr int NC = combine_epl<D>();
     const int lane = threadIdx.x & 63;
+    const bool holds = lane < D / NC;
     const int item = blockIdx.x * 4 + wave_id();
     if (item >= p.B * p.Hq) return;
     const int b = item / p.Hq, hq = item - b * p.Hq;
     const int n = p.kv_lens ? p.kv_lens[b] : p.kv_len_const;
     uint16_t *dst = p.o + (int64_t)b * p.o_sb + (int64_t)hq * p.o_sh + lane * NC;
     if (n == 0) {   // no keys: the row is zero
-        if constexpr (NC == 2) *reinterpret_cast<uint32_t *>(dst) = 0u;
-        else dst[0] = 0;
+        float zero[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) zero[c] = 0.f;
+        if (holds) store_row_bf16<NC>(dst, zero, 0.f);
         return;
     }
     const int hwg = p.Hq / p.ngrp;                 // query heads per row
@@ -474,35 +515,25 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeCombine
     float acc[NC], L, M;
     merge_partials<D>(p.o_part, p.ml_part, ((int64_t)r + w0) * hwg + hq % hwg, hwg, w1 - w0 + 1, lane, acc, L, M);
     const float inv = L > 0.f ? 1.f / L : 0.f;
-    if constexpr (NC == 2) {
-        *reinterpret_cast<uint32_t *>(dst) = pack_bf16(acc[0] * inv, acc[1] * inv);
-    } else {
-        dst[0] = (uint16_t)(pack_bf16(acc[0] * inv, 0.f) & 0xffffu);
-    }
+    if (holds) store_row_bf16<NC>(dst, acc, inv);
 }
 
 // Generic combine: every row r merges partials s = 0..S-1 at rows s*R + r.
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(const CombineParams p) {
-    constexpr int NC = D / 64;
+    constexpr int NC = combine_epl<D>();
     const int lane = threadIdx.x & 63;
+    const bool holds = lane < D / NC;
     const int r = blockIdx.x * 4 + wave_id();
     if (r >= p.R) return;
     float acc[NC], L, M;
     merge_partials<D>(p.o_part, p.ml_part, r, p.R, p.S, lane, acc, L, M);
     const float inv = L > 0.f ? 1.f / L : 0.f;
-    if (p.out_f32) {
+    if (p.out_f32 && holds) {
 #pragma unroll
         for (int c = 0; c < NC; ++c) p.out_f32[(size_t)r * D + lane * NC + c] = acc[c] * inv;
     }
-    if (p.out_bf16) {
-        uint16_t *dst = p.out_bf16 + (size_t)r * D + lane * NC;
-        if constexpr (NC == 2) {
-            *reinterpret_cast<uint32_t *>(dst) = pack_bf16(acc[0] * inv, acc[1] * inv);
-        } else {
-            dst[0] = (uint16_t)(pack_bf16(acc[0] * inv, 0.f) & 0xffffu);
-        }
-    }
+    if (p.out_bf16 && holds) store_row_bf16<NC>(p.out_bf16 + (size_t)r * D + lane * NC, acc, inv);
     if (p.lse && lane == 0) p.lse[r] = (L > 0.f) ? M + __logf(L) : -INFINITY;
 }
 
@@ -529,7 +560,9 @@ hipError_t launch_decode_hw(const DecodeParams &p, int G, hipStream_t stream) {
         case 1: return launch_decode_g<D, 1, PAGED>(p, G, stream);
         case 2: return launch_decode_g<D, 2, PAGED>(p, G, stream);
         case 4: return launch_decode_g<D, 4, PAGED>(p, G, stream);
-        case 8: return launch_decode_g<D, 8, PAGED>(p, G, stream);
+        case 8:
+            if constexpr (64 / chunk_lanes<D>() >= 8) return launch_decode_g<D, 8, PAGED>(p, G, stream);
+            else return hipErrorInvalidValue;
         default: return hipErrorInvalidValue;
     }
 }
@@ -538,8 +571,10 @@ hipError_t launch_decode_hw(const DecodeParams &p, int G, hipStream_t stream) {
 
 hipError_t launch_decode(const DecodeParams &p, int D, int G, bool paged, hipStream_t stream) {
     if (p.W <= 0 || p.R <= 0) return hipSuccess;
+    if (D == 32) return paged ? launch_decode_hw<32, true>(p, G, stream) : launch_decode_hw<32, false>(p, G, stream);
     if (D == 64) return paged ? launch_decode_hw<64, true>(p, G, stream) : launch_decode_hw<64, false>(p, G, stream);
     if (D == 128) return paged ? launch_decode_hw<128, true>(p, G, stream) : launch_decode_hw<128, false>(p, G, stream);
+    if (D == 256) return paged ? launch_decode_hw<256, true>(p, G, stream) : launch_decode_hw<256, false>(p, G, stream);
     return hipErrorInvalidValue;
 }
 
@@ -547,8 +582,10 @@ hipError_t launch_decode_combine(const DecodeCombineParams &p, int D, hipStream_
     const int rows = p.B * p.Hq;
     if (rows <= 0) return hipSuccess;
     const int blocks = (rows + 3) / 4;
-    if (D == 64) hipLaunchKernelGGL((decode_combine_kernel<64>), dim3(blocks), dim3(256), 0, stream, p);
+    if (D == 32) hipLaunchKernelGGL((decode_combine_kernel<32>), dim3(blocks), dim3(256), 0, stream, p);
+    else if (D == 64) hipLaunchKernelGGL((decode_combine_kernel<64>), dim3(blocks), dim3(256), 0, stream, p);
     else if (D == 128) hipLaunchKernelGGL((decode_combine_kernel<128>), dim3(blocks), dim3(256), 0, stream, p);
+    else if (D == 256) hipLaunchKernelGGL((decode_combine_kernel<256>), dim3(blocks), dim3(256), 0, stream, p);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }
@@ -556,8 +593,10 @@ hipError_t launch_decode_combine(const DecodeCombineParams &p, int D, hipStream_
 hipError_t launch_combine(const CombineParams &p, int D, hipStream_t stream) {
     if (p.R <= 0) return hipSuccess;
     const int blocks = (p.R + 3) / 4;
-    if (D == 64) hipLaunchKernelGGL((combine_kernel<64>), dim3(blocks), dim3(256), 0, stream, p);
+    if (D == 32) hipLaunchKernelGGL((combine_kernel<32>), dim3(blocks), dim3(256), 0, stream, p);
+    else if (D == 64) hipLaunchKernelGGL((combine_kernel<64>), dim3(blocks), dim3(256), 0, stream, p);
     else if (D == 128) hipLaunchKernelGGL((combine_kernel<128>), dim3(blocks), dim3(256), 0, stream, p);
+    else if (D == 256) hipLaunchKernelGGL((combine_kernel<256>), dim3(blocks), dim3(256), 0, stream, p);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }

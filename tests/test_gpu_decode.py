@@ -199,7 +199,7 @@ def test_combine_of_decode_partials_matches_oracle_combine(lens):
     assert_close(lse.view(B, Hq), full_lse, atol=1e-2, rtol=1e-2)
 
 
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [32, 64, 128, 256])
 def test_combine_random_partials_with_empty_splits(D):
     g = torch.Generator().manual_seed(D)
     S, R = 9, 300
@@ -286,3 +286,58 @@ def test_planner_on_mostly_empty_batch():
     ref, _ = oracle_paged(case)
     got = run_paged(case, 0, workspace=nan_workspace(128, 32, 128, S))
     assert_close(got, ref, what="planner S=%d" % S)
+
+
+# ------------------------------------------------ head dims 32 and 256
+@pytest.mark.parametrize("D", [32, 256])
+@pytest.mark.parametrize("Hkv,G,layout", [
+    (8, 4, "page_slot_head"),    # D=32: eight heads per wave; D=256: four (two head groups)
+    (2, 8, "page_slot_head"),
+    (4, 2, "page_head_slot"),    # one head per wave
+    (1, 1, "page_slot_head"),
+])
+@pytest.mark.parametrize("S", [0, 1, 5])
+def test_paged_decode_head_dims_32_and_256(D, Hkv, G, layout, S):
+    """Head dims beyond 64 and 128: 4 chunk lanes per head row at D=32, 16 at
+    D=256 (one more DPP step in the row sum).  Contexts up to 1500 keys;
+    outputs are ~0.03 in size there, so the absolute bar is 2e-3."""
+    lens = [1, 200, 0, 777, 1500]
+    case = workloads.paged_decode_case(300 + D + Hkv * G, len(lens), Hkv * G, Hkv, D, lens, 16, layout=layout)
+    ref, _ = oracle_paged(case)
+    assert_close(run_paged(case, S), ref, atol=2e-3, what="D=%d Hkv=%d G=%d %s S=%d" % (D, Hkv, G, layout, S))
+
+
+@pytest.mark.parametrize("D,ps", [(32, 1), (32, 5), (256, 3), (256, 64)])
+def test_paged_decode_head_dims_page_sizes(D, ps):
+    case = workloads.paged_decode_case(330 + D + ps, 4, 32, 8, D, [17, 1024, 333, 2], ps)
+    ref, _ = oracle_paged(case)
+    assert_close(run_paged(case, 0), ref, atol=2e-3, what="D=%d ps=%d" % (D, ps))
+
+
+@pytest.mark.parametrize("D", [32, 256])
+@pytest.mark.parametrize("layout", ["bhld", "blhd"])
+def test_contiguous_decode_head_dims_32_and_256(D, layout):
+    case = workloads.contig_decode_case(340 + D, 3, 16, 4, D, 900, device=DEV, layout=layout,
+                                        kv_lens=[900, 1, 450])
+    out = torch.empty_like(case["q"])
+    pa.attn_decode(case["q"], case["k"], case["v"], out, case["scale"], kv_lens=case["kv_lens"])
+    torch.cuda.synchronize()
+    ref, _ = oracle.decode(case["q"].cpu(), case["k"].cpu(), case["v"].cpu(), case["scale"],
+                           kv_lens=case["kv_lens"].cpu())
+    assert_close(out, ref, atol=2e-3, what="contiguous D=%d %s" % (D, layout))
+
+
+@pytest.mark.parametrize("D", [32, 256])
+def test_partition_every_slice_count_head_dims(D):
+    """Every slice count up to past the key total at D = 32 (eight heads per
+    wave) and D = 256 (four heads per wave, so two head groups per
+    sequence), empty and one-token sequences, NaN workspace."""
+    lens = [0, 9, 1, 0, 23, 2, 0]
+    Hkv, G = 8, 2
+    case = workloads.paged_decode_case(350 + D, len(lens), Hkv * G, Hkv, D, lens, 4)
+    ref, _ = oracle_paged(case)
+    groups = 1 if D == 32 else 2
+    T = sum(lens) * groups
+    for S in range(1, T + 8):
+        got = run_paged(case, S, workspace=nan_workspace(len(lens), Hkv * G, D, S))
+        assert_close(got, ref, what="D=%d S=%d of T=%d" % (D, S, T))
