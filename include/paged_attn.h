@@ -202,11 +202,12 @@ int attn_prefill_plan(const int32_t *q_lens_host, int B, int tile_rows,
                       int32_t *tile_to_index_host, int cap, int *num_tiles);
 
 /* Query rows per tile that attn_paged_prefill expects in its work map for
- * head dim D and group size G = Hq / Hkv.  A workgroup packs all G query
- * heads that share a KV head (csrc commit on GQA head packing: K/V tiles are
- * streamed once per block, not once per query head); a tile holds 128 / G
- * rows for G <= 4 (32 rows of one head per wave) and 16 rows for G = 8 (two
- * heads of the same 16 rows per wave). */
+ * head dim D and group size G = Hq / Hkv.  A workgroup packs HP query heads
+ * that share a KV head (csrc commit on GQA head packing: K/V tiles are
+ * streamed once per block, not once per query head): HP is the largest power
+ * of two dividing G, at most 8, i.e. all G heads for G in {1, 2, 4, 8}.  A
+ * tile holds 128 / HP rows for HP <= 4 (32 rows of one head per wave) and 16
+ * rows for HP = 8 (two heads of the same 16 rows per wave). */
 int attn_prefill_tile_rows(int D, int G);
 
 /*
@@ -233,7 +234,7 @@ int attn_prefill_tile_rows(int D, int G);
  *   o      packed [total_q, Hq, D] bf16: row r, head h at o + r*o_st + h*o_sh
  * Alignment: q/k/v rows 16-byte aligned, o rows 8-byte aligned, mask rows
  * (m_sb, m_sq, pointer) 4-byte aligned; mask bytes at key positions >= kv_lens[b]
- * are never read.  Supported: D in {32, 64, 128}, G in {1, 2, 4, 8}.
+ * are never read.  Supported: D in {32, 64, 128}, any G = Hq / Hkv.
  */
 int attn_paged_prefill(const void *q, int64_t q_st, int64_t q_sh, const int32_t *qo_indptr,
                        const int32_t *tile_to_batch, const int32_t *tile_to_index, int num_tiles,
@@ -262,7 +263,7 @@ int attn_paged_prefill(const void *q, int64_t q_st, int64_t q_sh, const int32_t 
  *   mask, mask_ndim, m_sb, m_sq  as in attn_paged_prefill
  *   o   [B, Lq, Hq, D] bf16: (b, i, h) at o + b*o_sb + i*o_sl + h*o_sh
  * Same kernel and numerics as attn_paged_prefill; no work map is needed.
- * Supported: D in {32, 64, 128}, G in {1, 2, 4, 8}; alignment as attn_paged_prefill.
+ * Supported: D in {32, 64, 128}, any G; alignment as attn_paged_prefill.
  */
 int attn_prefill(const void *q, int64_t q_sb, int64_t q_sl, int64_t q_sh,
                  const void *k, const void *v, int64_t k_sb, int64_t k_sl, int64_t k_sh,
@@ -297,8 +298,8 @@ int attn_prefill(const void *q, int64_t q_sb, int64_t q_sl, int64_t q_sh,
  */
 size_t attn_prefill_workspace_bytes(int rows, int Hq, int D, int num_splits);
 
-/* Host planner for the split count: with W0 = num_tiles * Hkv workgroups
- * of the plain kernel, returns the largest S <= target_workgroups / W0 that
+/* Host planner for the split count: with W0 = num_tiles * Hkv * (G / HP)
+ * workgroups of the plain kernel (HP as in attn_prefill_tile_rows), returns the largest S <= target_workgroups / W0 that
  * leaves every split at least 8 key tiles of 64 at max_kv_len (at least 1,
  * at most 256).  target_workgroups = 0 uses one per compute unit of the
  * current device.  Negative on error. */

@@ -80,6 +80,15 @@ int max_sub_piece(int page_size) {
 
 bool decode_dim(int D) { return D == 32 || D == 64 || D == 128 || D == 256; }
 
+// Prefill takes any group size: a workgroup packs the largest power of two
+// (at most 8) dividing G, and G / that many workgroups share a KV head.
+int check_prefill_heads(int Hq, int Hkv, int *G) {
+    if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0)
+        return fail(ATTN_ERR_INVALID_ARG, "Hq (%d) must be a positive multiple of Hkv (%d)", Hq, Hkv);
+    *G = Hq / Hkv;
+    return ATTN_OK;
+}
+
 int check_heads(int Hq, int Hkv, int D, int *G) {
     if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0)
         return fail(ATTN_ERR_INVALID_ARG, "Hq (%d) must be a positive multiple of Hkv (%d)", Hq, Hkv);
@@ -374,8 +383,7 @@ int attn_prefill_plan(const int32_t *q_lens_host, int B, int tile_rows,
 
 int attn_prefill_tile_rows(int D, int G) {
     if (D != 32 && D != 64 && D != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill_tile_rows: head dim %d not built (32, 64, 128)", D);
-    if (G != 1 && G != 2 && G != 4 && G != 8)
-        return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill_tile_rows: group size %d not built (1, 2, 4, 8)", G);
+    if (G < 1) return fail(ATTN_ERR_INVALID_ARG, "attn_prefill_tile_rows: group size %d", G);
     return pa::prefill_tile_rows(G);
 }
 
@@ -443,7 +451,7 @@ int paged_prefill_impl(const void *q, int64_t q_st, int64_t q_sh, const int32_t 
                        void *o, int64_t o_st, int64_t o_sh,
                        int B, int Hq, int Hkv, int D, int page_size, float scale,
                        int total_q, int num_splits, void *workspace, size_t workspace_bytes, void *stream) {
-    int G = 0, rc = check_heads(Hq, Hkv, D, &G);
+    int G = 0, rc = check_prefill_heads(Hq, Hkv, &G);
     if (rc) return rc;
     if (D != 32 && D != 64 && D != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_paged_prefill: head dim %d not built (32, 64, 128)", D);
     if (B < 0 || num_tiles < 0) return fail(ATTN_ERR_INVALID_ARG, "attn_paged_prefill: negative B or num_tiles");
@@ -463,7 +471,8 @@ int paged_prefill_impl(const void *q, int64_t q_st, int64_t q_sh, const int32_t 
     if (kv_s_page < 0 || kv_s_slot < 0 || kv_s_head < 0 || kv_s_page >= (1ll << 32) ||
         (int64_t)(page_size - 1) * kv_s_slot + (int64_t)(Hkv - 1) * kv_s_head + D >= (1ll << 31))
         return fail(ATTN_ERR_UNSUPPORTED, "attn_paged_prefill: pool strides exceed the 32-bit page/slot addressing");
-    if ((int64_t)num_tiles * Hkv * (num_splits > 0 ? num_splits : 1) >= (1ll << 31))
+    const int64_t groups = (int64_t)Hkv * (G / pa::prefill_heads_packed(G));   // workgroups per tile and split
+    if ((int64_t)num_tiles * groups * (num_splits > 0 ? num_splits : 1) >= (1ll << 31))
         return fail(ATTN_ERR_UNSUPPORTED, "attn_paged_prefill: num_tiles * Hkv * num_splits too large for one grid");
     pa::PrefillParams p{};
     rc = prefill_split_setup(p, "attn_paged_prefill", total_q, Hq, D, num_splits, workspace, workspace_bytes);
@@ -497,7 +506,7 @@ int dense_prefill_impl(const void *q, int64_t q_sb, int64_t q_sl, int64_t q_sh,
                        void *o, int64_t o_sb, int64_t o_sl, int64_t o_sh,
                        int B, int Lq, int Hq, int Hkv, int D, float scale,
                        int num_splits, void *workspace, size_t workspace_bytes, void *stream) {
-    int G = 0, rc = check_heads(Hq, Hkv, D, &G);
+    int G = 0, rc = check_prefill_heads(Hq, Hkv, &G);
     if (rc) return rc;
     if (D != 32 && D != 64 && D != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill: head dim %d not built (32, 64, 128)", D);
     if (B < 0 || Lq < 0 || kv_len < 0) return fail(ATTN_ERR_INVALID_ARG, "attn_prefill: negative size");
@@ -514,7 +523,8 @@ int dense_prefill_impl(const void *q, int64_t q_sb, int64_t q_sl, int64_t q_sh,
         return fail(ATTN_ERR_INVALID_ARG, "attn_prefill: negative stride");
     const int R = pa::prefill_tile_rows(G);
     const int64_t tiles = (int64_t)B * ((Lq + R - 1) / R);
-    if (tiles * Hkv * (num_splits > 0 ? num_splits : 1) >= (1ll << 31))
+    const int64_t groups = (int64_t)Hkv * (G / pa::prefill_heads_packed(G));
+    if (tiles * groups * (num_splits > 0 ? num_splits : 1) >= (1ll << 31))
         return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill: too many tiles for one grid");
     if ((int64_t)B * Lq >= (1ll << 31)) return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill: B * Lq must stay below 2^31");
     pa::PrefillParams p{};
@@ -554,7 +564,7 @@ size_t attn_prefill_workspace_bytes(int rows, int Hq, int D, int num_splits) {
 }
 
 int attn_prefill_plan_splits(int num_tiles, int Hq, int Hkv, int D, int max_kv_len, int target_workgroups) {
-    int G = 0, rc = check_heads(Hq, Hkv, D, &G);
+    int G = 0, rc = check_prefill_heads(Hq, Hkv, &G);
     if (rc) return rc;
     if (num_tiles < 0 || max_kv_len < 0 || target_workgroups < 0)
         return fail(ATTN_ERR_INVALID_ARG, "attn_prefill_plan_splits: negative argument");

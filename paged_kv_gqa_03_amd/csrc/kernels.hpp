@@ -101,9 +101,11 @@ struct PrefillParams {
     float *o_part, *ml_part;
 };
 
-// Query heads one prefill workgroup packs (all G heads of a KV head, G <= 8)
-// and the rows of a work-map tile: 32 per wave, 128 / G for G <= 4; 16 for
-// G = 8 (each wave then takes two heads of the same 16 rows).
+// Query heads HP one prefill workgroup packs (they share a KV head): the
+// largest power of two dividing G, at most 8, so all G heads for G in
+// {1, 2, 4, 8}; G / HP workgroups then cover a KV head.  Rows of a work-map
+// tile: 32 per wave, 128 / HP for HP <= 4; 16 for HP = 8 (each wave then
+// takes two heads of the same 16 rows).
 int prefill_heads_packed(int G);
 int prefill_tile_rows(int G);
 

@@ -688,8 +688,11 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(const PrefillCombi
 
 }  // namespace
 
-int prefill_heads_packed(int G) { return G; }
-int prefill_tile_rows(int G) { return G <= 4 ? 128 / G : 16; }
+int prefill_heads_packed(int G) { return (G & -G) < 8 ? (G & -G) : 8; }
+int prefill_tile_rows(int G) {
+    const int hp = prefill_heads_packed(G);
+    return hp <= 4 ? 128 / hp : 16;
+}
 
 hipError_t launch_prefill_combine(const PrefillCombineParams &p, int D, hipStream_t stream) {
     const int64_t items = (int64_t)p.rows * p.Hq;

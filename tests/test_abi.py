@@ -222,3 +222,11 @@ def test_dense_prefill_split_rejects_short_workspace():
                                 None, 500, 1, None, 0, 0, 0, FAKE, 16 * 8 * 128, 8 * 128, 128,
                                 2, 16, 8, 2, 128, 0.088, 3, FAKE, 4096, None)
     assert rc == pa.ATTN_ERR_WORKSPACE and "workspace" in pa.attn_last_error()
+
+
+def test_prefill_tile_rows_any_group_size():
+    # packed heads = largest power of two dividing G, at most 8
+    assert [pa.attn_prefill_tile_rows(128, G) for G in (3, 5, 6, 12, 16, 32, 24)] == [128, 128, 64, 32, 16, 16, 16]
+    # G = 32 over one KV head: four workgroups of eight heads per tile
+    assert pa.attn_prefill_plan_splits(16, 32, 1, 128, 16384, 256) == 4
+    assert pa.attn_prefill_plan_splits(16, 32, 1, 128, 16384, 1024) == 16

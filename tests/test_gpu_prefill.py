@@ -364,3 +364,38 @@ def test_split_prefill_short_q_long_kv_workload():
                                       cpu["kv_lens"][b:b + 1], case["scale"],
                                       causal_offset=cpu["causal_offset"][b:b + 1], mask=None)
         assert_close(out_s[r0:r1], ref, atol=1e-3, what="sequence %d vs oracle" % b)
+
+
+# ------------------------------------------ group sizes beyond 1, 2, 4, 8
+@pytest.mark.parametrize("Hq,Hkv,ps,mask_ndim", [
+    (6, 2, 16, None),      # G = 3: one head per workgroup, three workgroups per KV head
+    (12, 2, 5, 3),         # G = 6: two heads packed
+    (24, 2, 16, 2),        # G = 12: four heads packed
+    (32, 1, 16, None),     # G = 32: eight heads packed, four workgroups per KV head
+    (16, 1, 3, 3),         # G = 16
+])
+def test_prefill_any_group_size(Hq, Hkv, ps, mask_ndim):
+    """The pages verify head packing for G in {1, 2, 3, 4, 8, 32}; any G runs
+    here, packing the largest power of two dividing it (at most 8)."""
+    case = workloads.prefill_case(960 + Hq + ps, 3, Hq, Hkv, 128, (0, 300), (1, 140), ps,
+                                  mask_frac=None if mask_ndim is None else 0.2, mask_ndim=mask_ndim or 3)
+    assert_close(run_prefill(case), oracle_prefill(case), what="Hq=%d Hkv=%d" % (Hq, Hkv))
+
+
+@pytest.mark.parametrize("Hq,Hkv,S", [(32, 1, 4), (6, 2, 3)])
+def test_split_prefill_any_group_size(Hq, Hkv, S):
+    case = workloads.prefill_case(970 + Hq + S, 3, Hq, Hkv, 128, None, None, 16,
+                                  q_lens=[16, 3, 9], ctx_lens=[1000, 2000, 50])
+    assert_close(run_prefill_split(case, S), oracle_prefill(case), atol=2e-3, what="split Hq=%d Hkv=%d" % (Hq, Hkv))
+
+
+def test_dense_prefill_group_size_3():
+    B, Lq, Lk, Hkv, G = 2, 50, 300, 2, 3
+    q, k, v, _ = dense_case(980, B, Lq, Lk, Hkv * G, Hkv)
+    kv_lens = torch.full((B,), Lk, dtype=torch.int32)
+    scale = 1.0 / math.sqrt(128)
+    ref = oracle_dense(q, k, v, kv_lens, True, None, scale)
+    out = torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device=DEV)
+    pa.attn_prefill(q.to(DEV), k.to(DEV), v.to(DEV), out, scale, is_causal=True)
+    torch.cuda.synchronize()
+    assert_close(out, ref, what="dense G=3")
