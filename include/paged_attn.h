@@ -65,8 +65,10 @@ int attn_version(void);
  * partition: the rows (sequence, group of adjacent KV heads) are laid end to
  * end and the line of all their tokens is cut into `num_splits` = W equal
  * slices, whatever the spread of kv_lens.  A row is a group of up to 8 KV
- * heads when the KV head stride `kv_s_head` equals D (heads of a token
- * contiguous), else one head.  This planner returns W for `num_cus`
+ * heads (4 at D = 256) when the KV head stride `kv_s_head` equals D (heads
+ * of a token contiguous), else one head; when G is not 1, 2, 4 or 8 a row is
+ * one KV head and one pass over a power-of-two share of its G query heads
+ * (see attn_decode).  This planner returns W for `num_cus`
  * compute units (0 = query the current device): about three waves per unit
  * when a wave streams eight KV heads (kv_s_head == D, Hkv >= 8), two otherwise,
  * and no slice shorter than 64 tokens of a row given max_kv_len.  page_size
@@ -109,7 +111,9 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int D, int num_splits);
  *               on the current device
  *   workspace   >= attn_decode_workspace_bytes(B, Hq, D, W) bytes, device,
  *               256-byte aligned (may be NULL when W = 1)
- * Supported: D in {32, 64, 128, 256}, G = Hq/Hkv in {1, 2, 4, 8}.
+ * Supported: D in {32, 64, 128, 256}, any G = Hq/Hkv.  A wave handles Gk query
+ * heads of a KV head (the largest power of two dividing G, at most 8); for
+ * other G each (sequence, KV head) is streamed G / Gk times, once per pass.
  * Launches the split kernel, then the combine kernel, which merges rows
  * spread over several slices and zeroes rows without keys.
  */
@@ -137,7 +141,7 @@ int attn_decode(const void *q, int64_t q_sb, int64_t q_sh,
  *   max_kv_len  host-side bound on kv_lens, used by the planner;
  *          max_kv_len * page_size must stay below 2^32
  *   o      [B, Hq, D] bf16 output
- * Supported: D in {32, 64, 128, 256}, G in {1, 2, 4, 8}, any page_size >= 1.
+ * Supported: D in {32, 64, 128, 256}, any G (as attn_decode), any page_size >= 1.
  * A slice longer than 510 pages is processed as consecutive sub-pieces.
  */
 int attn_paged_decode(const void *q, int64_t q_sb, int64_t q_sh,

@@ -89,13 +89,29 @@ int check_prefill_heads(int Hq, int Hkv, int *G) {
     return ATTN_OK;
 }
 
-int check_heads(int Hq, int Hkv, int D, int *G) {
+int check_heads(int Hq, int Hkv, int *G) {
     if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0)
         return fail(ATTN_ERR_INVALID_ARG, "Hq (%d) must be a positive multiple of Hkv (%d)", Hq, Hkv);
     *G = Hq / Hkv;
-    if (*G != 1 && *G != 2 && *G != 4 && *G != 8)
-        return fail(ATTN_ERR_UNSUPPORTED, "group size Hq/Hkv = %d not built (1, 2, 4, 8)", *G);
     return ATTN_OK;
+}
+
+// Decode row layout for group size G: the kernel is built for Gk query
+// heads per pass (the largest power of two dividing G, at most 8) and a
+// (sequence, KV head) takes G / Gk passes, each a row of its own that
+// streams the KV head again; with one pass, a row may hold HW > 1 adjacent
+// KV heads.
+struct DecodeLayout {
+    int Gk, passes, HW, ngrp;
+};
+
+DecodeLayout decode_layout(int Hkv, int G, int64_t kv_s_head, int D) {
+    DecodeLayout L;
+    L.Gk = (G & -G) < 8 ? (G & -G) : 8;
+    L.passes = G / L.Gk;
+    L.HW = L.passes > 1 ? 1 : heads_per_wave(Hkv, kv_s_head, D);
+    L.ngrp = Hkv / L.HW * L.passes;
+    return L;
 }
 
 // Workspace: o_part [(B + W) * Hq, D] f32, then ml_part [(B + W) * Hq, 2] f32
@@ -117,7 +133,7 @@ int check_workspace(const void *workspace, size_t workspace_bytes, int B, int Hq
     return ATTN_OK;
 }
 
-pa::DecodeCombineParams combine_params(const void *workspace, int B, int Hq, int D, int W, int HW, int Hkv,
+pa::DecodeCombineParams combine_params(const void *workspace, int B, int Hq, int D, int W, int ngrp,
                                        const int32_t *kv_lens, int kv_len_const, void *o, int64_t o_sb,
                                        int64_t o_sh, int direct_single) {
     pa::DecodeCombineParams c{};
@@ -127,7 +143,7 @@ pa::DecodeCombineParams combine_params(const void *workspace, int B, int Hq, int
     c.kv_len_const = kv_len_const;
     c.B = B;
     c.Hq = Hq;
-    c.ngrp = Hkv / HW;
+    c.ngrp = ngrp;
     c.R = B * c.ngrp;
     c.W = W;
     c.direct_single = direct_single;
@@ -149,8 +165,11 @@ int run_decode(pa::DecodeParams &p, int D, int G, bool paged, int max_kv_len, in
         if (W < 0) return W;
     }
     if (W < 1 || W > kMaxWaves) return fail(ATTN_ERR_INVALID_ARG, "num_splits %d outside [1, %d]", W, kMaxWaves);
-    p.HW = heads_per_wave(p.Hkv, kv_s_head, D);
-    p.ngrp = p.Hkv / p.HW;
+    const DecodeLayout L = decode_layout(p.Hkv, G, kv_s_head, D);
+    p.G_all = G;
+    p.passes = L.passes;
+    p.HW = L.HW;
+    p.ngrp = L.ngrp;
     p.R = p.B * p.ngrp;
     p.W = W;
     if ((int64_t)p.R * (int64_t)max_kv_len >= (1ll << 31))
@@ -164,12 +183,12 @@ int run_decode(pa::DecodeParams &p, int D, int G, bool paged, int max_kv_len, in
         p.ml_part = reinterpret_cast<float *>(static_cast<char *>(workspace) + ws_ml_offset(p.B, p.Hq, D, W));
     }
     if (p.B == 0) return ok();
-    hipError_t e = pa::launch_decode(p, D, G, paged, stream);
+    hipError_t e = pa::launch_decode(p, D, L.Gk, paged, stream);
     if (e != hipSuccess) return launch_status(e, "decode split kernel");
     if (mode == 0) {
         // Rows spanning several slices are merged; empty rows are zeroed;
         // rows written directly are left alone.
-        pa::DecodeCombineParams c = combine_params(workspace, p.B, p.Hq, D, W, p.HW, p.Hkv, p.kv_lens,
+        pa::DecodeCombineParams c = combine_params(workspace, p.B, p.Hq, D, W, p.ngrp, p.kv_lens,
                                                    p.kv_len_const, p.o, p.o_sb, p.o_sh, 1);
         e = pa::launch_decode_combine(c, D, stream);
         if (e != hipSuccess) return launch_status(e, "combine kernel");
@@ -193,8 +212,9 @@ int attn_plan_splits(int B, int Hkv, int G, int D, int max_kv_len, int page_size
         num_cus = device_cus();
         if (num_cus <= 0) return fail(ATTN_ERR_LAUNCH, "attn_plan_splits: cannot query the device");
     }
-    const int hw = heads_per_wave(Hkv, kv_s_head, D);
-    const long rows = (long)B * (Hkv / hw);
+    const DecodeLayout L = decode_layout(Hkv, G, kv_s_head, D);
+    const int hw = L.HW;
+    const long rows = (long)B * L.ngrp;
     const long line = rows * (long)max_kv_len;   // upper bound on the tokens of all rows
     long W = (line + kMinSliceTokens - 1) / kMinSliceTokens;
     const long cap = (long)num_cus * (hw == 8 ? kWavesPerCuRows : kWavesPerCuHead);
@@ -216,7 +236,7 @@ int attn_decode(const void *q, int64_t q_sb, int64_t q_sh,
                 const int32_t *kv_lens, int kv_len,
                 int B, int Hq, int Hkv, int D, float scale, int num_splits,
                 void *workspace, size_t workspace_bytes, void *stream) {
-    int G = 0, rc = check_heads(Hq, Hkv, D, &G);
+    int G = 0, rc = check_heads(Hq, Hkv, &G);
     if (rc) return rc;
     if (B < 0 || kv_len < 0) return fail(ATTN_ERR_INVALID_ARG, "attn_decode: negative B or kv_len");
     if (!decode_dim(D)) return fail(ATTN_ERR_UNSUPPORTED, "attn_decode: head dim %d not built (32, 64, 128, 256)", D);
@@ -257,7 +277,7 @@ static int paged_decode_impl(const void *q, int64_t q_sb, int64_t q_sh,
                              int num_splits, void *workspace, size_t workspace_bytes,
                              void *stream, int mode) {
     const char *fn = mode ? "attn_paged_decode_split" : "attn_paged_decode";
-    int G = 0, rc = check_heads(Hq, Hkv, D, &G);
+    int G = 0, rc = check_heads(Hq, Hkv, &G);
     if (rc) return rc;
     if (B < 0 || max_kv_len < 0) return fail(ATTN_ERR_INVALID_ARG, "%s: negative B or max_kv_len", fn);
     if (page_size <= 0) return fail(ATTN_ERR_INVALID_ARG, "%s: page_size must be >= 1", fn);
@@ -324,7 +344,7 @@ int attn_paged_decode_split(const void *q, int64_t q_sb, int64_t q_sh,
 int attn_decode_combine(const void *workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int D,
                         int num_splits, int64_t kv_s_head, const int32_t *kv_lens, int max_kv_len, void *o,
                         int64_t o_sb, int64_t o_sh, void *stream) {
-    int G = 0, rc = check_heads(Hq, Hkv, D, &G);
+    int G = 0, rc = check_heads(Hq, Hkv, &G);
     if (rc) return rc;
     if (B < 0 || max_kv_len < 0 || num_splits < 1 || num_splits > kMaxWaves)
         return fail(ATTN_ERR_INVALID_ARG, "attn_decode_combine: bad sizes");
@@ -335,8 +355,9 @@ int attn_decode_combine(const void *workspace, size_t workspace_bytes, int B, in
     rc = check_workspace(workspace, workspace_bytes, B, Hq, D, num_splits);
     if (rc) return rc;
     if (B == 0) return ok();
-    pa::DecodeCombineParams c = combine_params(workspace, B, Hq, D, num_splits, heads_per_wave(Hkv, kv_s_head, D),
-                                               Hkv, kv_lens, max_kv_len, o, o_sb, o_sh, 0);
+    const DecodeLayout L = decode_layout(Hkv, G, kv_s_head, D);
+    pa::DecodeCombineParams c = combine_params(workspace, B, Hq, D, num_splits, L.ngrp, kv_lens, max_kv_len, o,
+                                               o_sb, o_sh, 0);
     return launch_status(pa::launch_decode_combine(c, D, static_cast<hipStream_t>(stream)), "combine kernel");
 }
 

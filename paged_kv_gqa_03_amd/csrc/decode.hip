@@ -183,12 +183,16 @@ __global__ __launch_bounds__(64, (G >= 8 ? 1 : 2)) void decode_split_kernel(cons
         P += n;
         if (lo >= hi) continue;
         const int b = r / p.ngrp, hgrp = r % p.ngrp;
-        const int g = hgrp * HW + hw;   // this lane's KV head
+        // A row is (sequence, group of HW KV heads), or with several passes
+        // (sequence, KV head, pass): pass j covers query heads j*G .. j*G+G-1
+        // of the KV head's G_all.
+        const int g = (hgrp / p.passes) * HW + hw;   // this lane's KV head
+        const int h0 = g * p.G_all + (hgrp % p.passes) * G;   // first query head of the pass
 
-        // Query slices of the G heads of this KV head, chunks jj + 8c.
+        // Query slices of the G heads of this pass, chunks jj + JJ*c.
         uint32_t qv[G][NCH][4];
         {
-            const uint16_t *qb = p.q + b * p.q_sb + (int64_t)(g * G) * p.q_sh + jj * 8;
+            const uint16_t *qb = p.q + b * p.q_sb + (int64_t)h0 * p.q_sh + jj * 8;
 #pragma unroll
             for (int h = 0; h < G; ++h)
 #pragma unroll
@@ -387,7 +391,7 @@ __global__ __launch_bounds__(64, (G >= 8 ? 1 : 2)) void decode_split_kernel(cons
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             if (h % TG != tg) continue;
-            const int hq = g * G + h;
+            const int hq = h0 + h;
             if (direct) {
                 const float inv = lsum[h] > 0.f ? 1.f / lsum[h] : 0.f;
                 uint16_t *dst = p.o + b * p.o_sb + hq * p.o_sh + jj * 8;

@@ -32,8 +32,10 @@ struct DecodeParams {
     float *o_part;   // [(B + W) * Hq, D]   partial of slot s, local head i at row s*HW*G + i
     float *ml_part;  // [(B + W) * Hq, 2]
     int B, Hq, Hkv;
+    int G_all;       // Hq / Hkv; a row's pass covers the kernel's G of them
+    int passes;      // G_all / G: rows per (sequence, KV head); > 1 only with HW = 1
     int HW;          // KV heads per row (1, 2, 4, 8; divides Hkv)
-    int ngrp;        // Hkv / HW
+    int ngrp;        // rows per sequence: Hkv / HW * passes
     int R;           // B * ngrp rows
     int W;           // waves (slices of the line)
     int max_sub;     // longest sub-piece (tokens) one LDS page slice covers

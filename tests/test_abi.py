@@ -122,7 +122,6 @@ def call_paged(a):
 
 
 @pytest.mark.parametrize("over,code,word", [
-    (dict(Hq=6), pa.ATTN_ERR_UNSUPPORTED, "group"),
     (dict(Hq=7), pa.ATTN_ERR_INVALID_ARG, "multiple"),
     (dict(D=96), pa.ATTN_ERR_UNSUPPORTED, "head dim"),
     (dict(q=None), pa.ATTN_ERR_INVALID_ARG, "null"),
@@ -230,3 +229,12 @@ def test_prefill_tile_rows_any_group_size():
     # G = 32 over one KV head: four workgroups of eight heads per tile
     assert pa.attn_prefill_plan_splits(16, 32, 1, 128, 16384, 256) == 4
     assert pa.attn_prefill_plan_splits(16, 32, 1, 128, 16384, 1024) == 16
+
+
+def test_planner_counts_one_row_per_pass_for_other_group_sizes():
+    # G = 32 over 1 KV head: four passes of 8 query heads, each a row of its own
+    # (one head per wave), so the line is 4 * B * max_len tokens
+    assert pa.attn_plan_splits(2, 1, 32, 128, 640, 16, 128, 256) == 2 * 4 * 640 // 64
+    assert pa.attn_plan_splits(2, 1, 8, 128, 640, 16, 128, 256) == 2 * 640 // 64
+    # G = 3: three passes of one head
+    assert pa.attn_plan_splits(1, 2, 3, 128, 640, 16, 128, 256) == 2 * 3 * 640 // 64

@@ -341,3 +341,61 @@ def test_partition_every_slice_count_head_dims(D):
     for S in range(1, T + 8):
         got = run_paged(case, S, workspace=nan_workspace(len(lens), Hkv * G, D, S))
         assert_close(got, ref, what="D=%d S=%d of T=%d" % (D, S, T))
+
+
+# ---------------------------------------- group sizes beyond 1, 2, 4, 8
+@pytest.mark.parametrize("Hq,Hkv,layout", [
+    (6, 2, "page_slot_head"),     # G = 3: three passes of one query head
+    (12, 2, "page_head_slot"),    # G = 6: three passes of two
+    (24, 2, "page_slot_head"),    # G = 12: three passes of four
+    (32, 1, "page_slot_head"),    # G = 32: four passes of eight
+    (16, 1, "page_head_slot"),    # G = 16
+    (40, 8, "page_slot_head"),    # G = 5
+])
+@pytest.mark.parametrize("S", [0, 1, 7])
+def test_paged_decode_any_group_size(Hq, Hkv, layout, S):
+    """Group sizes the pages verify head packing for (3, 32) and others: a
+    (sequence, KV head) is streamed once per pass of Gk query heads."""
+    lens = [1, 300, 0, 1200]
+    case = workloads.paged_decode_case(400 + Hq + Hkv, len(lens), Hq, Hkv, 128, lens, 16, layout=layout)
+    ref, _ = oracle_paged(case)
+    assert_close(run_paged(case, S), ref, atol=2e-3, what="Hq=%d Hkv=%d %s S=%d" % (Hq, Hkv, layout, S))
+
+
+def test_contiguous_decode_group_size_32():
+    case = workloads.contig_decode_case(420, 3, 32, 1, 64, 500, device=DEV, layout="blhd", kv_lens=[500, 7, 260])
+    out = torch.empty_like(case["q"])
+    pa.attn_decode(case["q"], case["k"], case["v"], out, case["scale"], kv_lens=case["kv_lens"])
+    torch.cuda.synchronize()
+    ref, _ = oracle.decode(case["q"].cpu(), case["k"].cpu(), case["v"].cpu(), case["scale"],
+                           kv_lens=case["kv_lens"].cpu())
+    assert_close(out, ref, atol=2e-3, what="contiguous G=32")
+
+
+@pytest.mark.parametrize("S", [3, 11])
+def test_split_then_combine_group_size_6(S):
+    """attn_paged_decode_split + attn_decode_combine locate a row's pieces from
+    the same pass layout as the fused call."""
+    case = workloads.paged_decode_case(430, 4, 12, 2, 128, [5, 300, 0, 900], 16)
+    d = to_dev(case, ["q", "k_pool", "v_pool", "block_table", "kv_lens"])
+    ws = torch.empty(pa.attn_decode_workspace_bytes(4, 12, 128, S), dtype=torch.uint8, device=DEV)
+    fused = run_paged(case, S, workspace=ws).clone()
+    pa.attn_paged_decode_split(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["kv_lens"],
+                               case["max_kv_len"], 16, case["scale"], S, ws)
+    out = torch.empty_like(d["q"])
+    pa.attn_decode_combine(ws, 4, 12, 2, 128, S, d["k_pool"].stride(2), d["kv_lens"], case["max_kv_len"], out)
+    torch.cuda.synchronize()
+    assert torch.equal(fused, out)
+    ref, _ = oracle_paged(case)
+    assert_close(out, ref, atol=2e-3)
+
+
+def test_partition_every_slice_count_group_size_3():
+    lens = [0, 9, 1, 0, 23, 2, 0]
+    Hkv, G, D = 2, 3, 64
+    case = workloads.paged_decode_case(440, len(lens), Hkv * G, Hkv, D, lens, 4)
+    ref, _ = oracle_paged(case)
+    T = sum(lens) * Hkv * G          # one row per (sequence, KV head, pass)
+    for S in range(1, T + 8):
+        got = run_paged(case, S, workspace=nan_workspace(len(lens), Hkv * G, D, S))
+        assert_close(got, ref, what="G=3 S=%d of T=%d" % (S, T))
