@@ -211,7 +211,9 @@ int attn_prefill_plan(const int32_t *q_lens_host, int B, int tile_rows,
  * streamed once per block, not once per query head): HP is the largest power
  * of two dividing G, at most 8, i.e. all G heads for G in {1, 2, 4, 8}.  A
  * tile holds 128 / HP rows for HP <= 4 (32 rows of one head per wave) and 16
- * rows for HP = 8 (two heads of the same 16 rows per wave). */
+ * rows for HP = 8 (two heads of the same 16 rows per wave).  At D = 256 a
+ * workgroup has four waves of 16 rows: HP is at most 4 and a tile holds
+ * 64 / HP rows. */
 int attn_prefill_tile_rows(int D, int G);
 
 /*
@@ -238,7 +240,7 @@ int attn_prefill_tile_rows(int D, int G);
  *   o      packed [total_q, Hq, D] bf16: row r, head h at o + r*o_st + h*o_sh
  * Alignment: q/k/v rows 16-byte aligned, o rows 8-byte aligned, mask rows
  * (m_sb, m_sq, pointer) 4-byte aligned; mask bytes at key positions >= kv_lens[b]
- * are never read.  Supported: D in {32, 64, 128}, any G = Hq / Hkv.
+ * are never read.  Supported: D in {32, 64, 128, 256}, any G = Hq / Hkv.
  */
 int attn_paged_prefill(const void *q, int64_t q_st, int64_t q_sh, const int32_t *qo_indptr,
                        const int32_t *tile_to_batch, const int32_t *tile_to_index, int num_tiles,
@@ -267,7 +269,7 @@ int attn_paged_prefill(const void *q, int64_t q_st, int64_t q_sh, const int32_t 
  *   mask, mask_ndim, m_sb, m_sq  as in attn_paged_prefill
  *   o   [B, Lq, Hq, D] bf16: (b, i, h) at o + b*o_sb + i*o_sl + h*o_sh
  * Same kernel and numerics as attn_paged_prefill; no work map is needed.
- * Supported: D in {32, 64, 128}, any G; alignment as attn_paged_prefill.
+ * Supported: D in {32, 64, 128, 256}, any G; alignment as attn_paged_prefill.
  */
 int attn_prefill(const void *q, int64_t q_sb, int64_t q_sl, int64_t q_sh,
                  const void *k, const void *v, int64_t k_sb, int64_t k_sl, int64_t k_sh,

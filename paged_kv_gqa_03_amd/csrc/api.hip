@@ -403,9 +403,9 @@ int attn_prefill_plan(const int32_t *q_lens_host, int B, int tile_rows,
 }
 
 int attn_prefill_tile_rows(int D, int G) {
-    if (D != 32 && D != 64 && D != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill_tile_rows: head dim %d not built (32, 64, 128)", D);
+    if (!decode_dim(D)) return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill_tile_rows: head dim %d not built (32, 64, 128, 256)", D);
     if (G < 1) return fail(ATTN_ERR_INVALID_ARG, "attn_prefill_tile_rows: group size %d", G);
-    return pa::prefill_tile_rows(G);
+    return pa::prefill_tile_rows(G, D);
 }
 
 }  // extern "C"
@@ -474,7 +474,7 @@ int paged_prefill_impl(const void *q, int64_t q_st, int64_t q_sh, const int32_t 
                        int total_q, int num_splits, void *workspace, size_t workspace_bytes, void *stream) {
     int G = 0, rc = check_prefill_heads(Hq, Hkv, &G);
     if (rc) return rc;
-    if (D != 32 && D != 64 && D != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_paged_prefill: head dim %d not built (32, 64, 128)", D);
+    if (!decode_dim(D)) return fail(ATTN_ERR_UNSUPPORTED, "attn_paged_prefill: head dim %d not built (32, 64, 128, 256)", D);
     if (B < 0 || num_tiles < 0) return fail(ATTN_ERR_INVALID_ARG, "attn_paged_prefill: negative B or num_tiles");
     if (page_size <= 0) return fail(ATTN_ERR_INVALID_ARG, "attn_paged_prefill: page_size must be >= 1");
     if (!q || !qo_indptr || !k_pool || !v_pool || !block_table || !kv_lens || !o ||
@@ -492,7 +492,7 @@ int paged_prefill_impl(const void *q, int64_t q_st, int64_t q_sh, const int32_t 
     if (kv_s_page < 0 || kv_s_slot < 0 || kv_s_head < 0 || kv_s_page >= (1ll << 32) ||
         (int64_t)(page_size - 1) * kv_s_slot + (int64_t)(Hkv - 1) * kv_s_head + D >= (1ll << 31))
         return fail(ATTN_ERR_UNSUPPORTED, "attn_paged_prefill: pool strides exceed the 32-bit page/slot addressing");
-    const int64_t groups = (int64_t)Hkv * (G / pa::prefill_heads_packed(G));   // workgroups per tile and split
+    const int64_t groups = (int64_t)Hkv * (G / pa::prefill_heads_packed(G, D));   // workgroups per tile and split
     if ((int64_t)num_tiles * groups * (num_splits > 0 ? num_splits : 1) >= (1ll << 31))
         return fail(ATTN_ERR_UNSUPPORTED, "attn_paged_prefill: num_tiles * Hkv * num_splits too large for one grid");
     pa::PrefillParams p{};
@@ -529,7 +529,7 @@ int dense_prefill_impl(const void *q, int64_t q_sb, int64_t q_sl, int64_t q_sh,
                        int num_splits, void *workspace, size_t workspace_bytes, void *stream) {
     int G = 0, rc = check_prefill_heads(Hq, Hkv, &G);
     if (rc) return rc;
-    if (D != 32 && D != 64 && D != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill: head dim %d not built (32, 64, 128)", D);
+    if (!decode_dim(D)) return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill: head dim %d not built (32, 64, 128, 256)", D);
     if (B < 0 || Lq < 0 || kv_len < 0) return fail(ATTN_ERR_INVALID_ARG, "attn_prefill: negative size");
     if (!q || !k || !v || !o) return fail(ATTN_ERR_INVALID_ARG, "attn_prefill: null pointer");
     if (!std::isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "attn_prefill: scale is not finite");
@@ -542,9 +542,9 @@ int dense_prefill_impl(const void *q, int64_t q_sb, int64_t q_sl, int64_t q_sh,
         return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill: q/k/v rows must be 16-byte and o rows 8-byte aligned");
     if (q_sb < 0 || q_sl < 0 || q_sh < 0 || k_sb < 0 || k_sl < 0 || k_sh < 0 || o_sb < 0 || o_sl < 0 || o_sh < 0)
         return fail(ATTN_ERR_INVALID_ARG, "attn_prefill: negative stride");
-    const int R = pa::prefill_tile_rows(G);
+    const int R = pa::prefill_tile_rows(G, D);
     const int64_t tiles = (int64_t)B * ((Lq + R - 1) / R);
-    const int64_t groups = (int64_t)Hkv * (G / pa::prefill_heads_packed(G));
+    const int64_t groups = (int64_t)Hkv * (G / pa::prefill_heads_packed(G, D));
     if (tiles * groups * (num_splits > 0 ? num_splits : 1) >= (1ll << 31))
         return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill: too many tiles for one grid");
     if ((int64_t)B * Lq >= (1ll << 31)) return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill: B * Lq must stay below 2^31");
@@ -594,7 +594,7 @@ int attn_prefill_plan_splits(int num_tiles, int Hq, int Hkv, int D, int max_kv_l
         if (cus <= 0) return fail(ATTN_ERR_LAUNCH, "attn_prefill_plan_splits: no HIP device");
         target_workgroups = kPrefillWgPerCu * cus;
     }
-    const int64_t base = (int64_t)num_tiles * Hkv * (G / pa::prefill_heads_packed(G));
+    const int64_t base = (int64_t)num_tiles * Hkv * (G / pa::prefill_heads_packed(G, D));
     if (base == 0) return 1;
     int64_t S = target_workgroups / base;
     const int64_t key_tiles = ((int64_t)max_kv_len + 63) / 64;

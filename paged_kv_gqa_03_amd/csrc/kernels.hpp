@@ -104,12 +104,13 @@ struct PrefillParams {
 };
 
 // Query heads HP one prefill workgroup packs (they share a KV head): the
-// largest power of two dividing G, at most 8, so all G heads for G in
-// {1, 2, 4, 8}; G / HP workgroups then cover a KV head.  Rows of a work-map
-// tile: 32 per wave, 128 / HP for HP <= 4; 16 for HP = 8 (each wave then
-// takes two heads of the same 16 rows).
-int prefill_heads_packed(int G);
-int prefill_tile_rows(int G);
+// largest power of two dividing G, at most 8 (4 at D = 256), so all G heads
+// for G in {1, 2, 4, 8}; G / HP workgroups then cover a KV head.  Rows of a
+// work-map tile: for D <= 128, 32 per wave, 128 / HP for HP <= 4 and 16 for
+// HP = 8 (each wave then takes two heads of the same 16 rows); for D = 256,
+// 16 per wave of one team, 64 / HP.
+int prefill_heads_packed(int G, int D);
+int prefill_tile_rows(int G, int D);
 
 // Combine of split-KV prefill partials: one wave per (query row, head).
 struct PrefillCombineParams {

@@ -79,8 +79,7 @@ struct Stage {
 };
 
 struct StageCtx {
-    int cc, kg;
-    bool stager;                    // this thread stages (16 groups of 4 keys x D/8 chunks)
+    int cc;                         // this thread's 16-byte chunk of a K/V row
     bool stream;                    // no other workgroup reads these keys: non-temporal loads
     int first_pg, c1;               // page slice start; keys of this chunk end at c1
     const int32_t *pages;           // LDS page slice
@@ -102,14 +101,13 @@ __device__ __forceinline__ uint4 ld16_nt(const uint16_t *ptr) {
     return make_uint4(t.x, t.y, t.z, t.w);
 }
 
-// The thread's share of tile kt: keys 4kg .. 4kg+3, chunk cc, of K and of V
-// (the sources share strides, so the four offsets serve both).  Paged: when
-// the page size is a multiple of 4 the four keys sit in one page, one lookup
+// A share of tile kt: keys 4kg .. 4kg+3, chunk cc, of K and of V (the
+// sources share strides, so the four offsets serve both).  Paged: when the
+// page size is a multiple of 4 the four keys sit in one page, one lookup
 // then slot steps.  Keys past the chunk end repeat its last key.
 template <bool PAGED>
-__device__ __forceinline__ void load_stage(const PrefillParams &p, const StageCtx &sc, int kt, Stage &r) {
-    if (!sc.stager) return;
-    const int k0 = min(kt * BK + 4 * sc.kg, sc.c1 - 1);
+__device__ __forceinline__ void load_stage(const PrefillParams &p, const StageCtx &sc, int kg, int kt, Stage &r) {
+    const int k0 = min(kt * BK + 4 * kg, sc.c1 - 1);
     uint64_t off[4];
     if constexpr (!PAGED) {   // contiguous source: key j at j * s_slot from the sequence's base
         const int rmax = sc.c1 - 1 - k0;
@@ -222,44 +220,54 @@ __device__ __forceinline__ void store_v_pair(uint16_t *v_lds, int d, int ph, uin
 }
 
 template <int D>
-__device__ __forceinline__ void store_stage(const StageCtx &sc, const Stage &r, uint16_t *k_lds, uint16_t *v_lds) {
-    if (!sc.stager) return;
+__device__ __forceinline__ void store_stage(const StageCtx &sc, int kg, const Stage &r, uint16_t *k_lds,
+                                            uint16_t *v_lds) {
     constexpr int KLD = kld<D>();
-    *reinterpret_cast<uint4 *>(&k_lds[(4 * sc.kg + 0) * KLD + sc.cc * 8]) = r.k0;
-    *reinterpret_cast<uint4 *>(&k_lds[(4 * sc.kg + 1) * KLD + sc.cc * 8]) = r.k1;
-    *reinterpret_cast<uint4 *>(&k_lds[(4 * sc.kg + 2) * KLD + sc.cc * 8]) = r.k2;
-    *reinterpret_cast<uint4 *>(&k_lds[(4 * sc.kg + 3) * KLD + sc.cc * 8]) = r.k3;
+    *reinterpret_cast<uint4 *>(&k_lds[(4 * kg + 0) * KLD + sc.cc * 8]) = r.k0;
+    *reinterpret_cast<uint4 *>(&k_lds[(4 * kg + 1) * KLD + sc.cc * 8]) = r.k1;
+    *reinterpret_cast<uint4 *>(&k_lds[(4 * kg + 2) * KLD + sc.cc * 8]) = r.k2;
+    *reinterpret_cast<uint4 *>(&k_lds[(4 * kg + 3) * KLD + sc.cc * 8]) = r.k3;
     // 4 keys x 8 dims -> 8 dims x 4 keys
-    const int ph = v_phys(4 * sc.kg), d0 = sc.cc * 8;
+    const int ph = v_phys(4 * kg), d0 = sc.cc * 8;
     store_v_pair(v_lds, d0 + 0, ph, r.v0.x, r.v1.x, r.v2.x, r.v3.x);
     store_v_pair(v_lds, d0 + 2, ph, r.v0.y, r.v1.y, r.v2.y, r.v3.y);
     store_v_pair(v_lds, d0 + 4, ph, r.v0.z, r.v1.z, r.v2.z, r.v3.z);
     store_v_pair(v_lds, d0 + 6, ph, r.v0.w, r.v1.w, r.v2.w, r.v3.w);
 }
 
+// Head dims up to 128: two teams of four waves, two 16-row blocks per wave.
+// D = 256: one team, one 16-row block per wave (O^T alone takes 64
+// registers per block, and one K + V^T stage is 71 KB of LDS).
+template <int D>
+constexpr int prefill_teams() { return D <= 128 ? 2 : 1; }
+
 template <int D, int HP, int MASK, bool PAGED>
-__global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) {
-    constexpr int R = HP <= 4 ? 128 / HP : 16;   // rows per work-map tile
+__global__ __launch_bounds__(256 * prefill_teams<D>(), D <= 128 ? 2 : 1) void prefill_kernel(const PrefillParams p) {
+    constexpr int TEAMS = prefill_teams<D>();
+    constexpr int RB = D <= 128 ? 2 : 1;          // 16-row blocks per wave
+    constexpr int NT = 256 * TEAMS;               // threads
+    static_assert(RB == 2 || HP <= 4, "one block per wave packs at most four heads");
+    constexpr int R = RB == 2 ? (HP <= 4 ? 128 / HP : 16) : 64 / HP;   // rows per work-map tile
     constexpr int KLD = kld<D>();
     constexpr int NS = D / 32;    // 32-deep steps of Q.K^T
     constexpr int NM = D / 16;    // 16-row blocks of O^T
     constexpr int CPR = D / 8;    // 16-byte chunks per K/V row
     constexpr int XCH = D / 2 + 4;                            // floats per lane handed from team 1 to team 0
     constexpr int SBUF = BK * KLD + D * VLD;                  // one K tile + one V^T tile (elements)
-    static_assert(4 * XCH * 64 * 4 <= 4 * SBUF * 2, "team exchange must fit the stage buffers");
-    __shared__ __attribute__((aligned(16))) uint16_t stage_lds[2 * 2 * SBUF];   // [team][buffer]
+    static_assert(TEAMS == 1 || 4 * XCH * 64 * 4 <= 4 * SBUF * 2, "team exchange must fit the stage buffers");
+    __shared__ __attribute__((aligned(16))) uint16_t stage_lds[TEAMS * 2 * SBUF];   // [team][buffer]
     __shared__ int32_t pages[kPages];
     constexpr int MROWS = MASK == 3 ? R : 1;                  // mask rows per tile
     constexpr int NQ = MASK == 3 && R > 32 ? R / 32 : 1;      // mask rows per thread
-    __shared__ __attribute__((aligned(8))) uint8_t mbits[2][2][MROWS * 8];
+    __shared__ __attribute__((aligned(8))) uint8_t mbits[TEAMS][2][MROWS * 8];
 
-    // Two teams of four waves take alternate KV tiles of the same query
-    // rows and heads; team 1 hands its state to team 0 at the end.
+    // With two teams of four waves, they take alternate KV tiles of the same
+    // query rows and heads; team 1 hands its state to team 0 at the end.
     const int tid = threadIdx.x, lane = tid & 63;
     // team and wave are wave-uniform: taken through readfirstlane so that
     // what derives from them (heads, row offsets) sits in scalar registers.
     const int ttid = tid & 255;
-    const int team = __builtin_amdgcn_readfirstlane(tid >> 8);
+    const int team = TEAMS == 2 ? __builtin_amdgcn_readfirstlane(tid >> 8) : 0;
     const int w = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);
     // Tiles in reverse work-map order (a sequence's last, longest tiles
     // first), the head groups of a tile next to each other.
@@ -284,13 +292,19 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) 
     }
     const int groups_per_kv = p.G / HP;
     const int g = hg / groups_per_kv;
-    // Row offset (in the tile) and query head of each of the wave's two row
+    // Row offset (in the tile) and query head of each of the wave's row
     // blocks.
-    int rboff[2], hq[2];
+    int rboff[RB], hq[RB];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-        rboff[rb] = HP <= 4 ? (w / HP) * 32 + 16 * rb : 0;
-        hq[rb] = g * p.G + (hg % groups_per_kv) * HP + (HP <= 4 ? w % HP : 2 * w + rb);
+    for (int rb = 0; rb < RB; ++rb) {
+        const int hbase = g * p.G + (hg % groups_per_kv) * HP;
+        if constexpr (RB == 2) {
+            rboff[rb] = HP <= 4 ? (w / HP) * 32 + 16 * rb : 0;
+            hq[rb] = hbase + (HP <= 4 ? w % HP : 2 * w + rb);
+        } else {
+            rboff[rb] = (w / HP) * 16;
+            hq[rb] = hbase + w % HP;
+        }
     }
     const int q0 = p.dense_lq > 0 ? 0 : p.qo_indptr[b];
     const int qn = p.dense_lq > 0 ? p.dense_lq : p.qo_indptr[b + 1] - q0;
@@ -304,10 +318,10 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) 
     const int64_t orow0 = (int64_t)b * p.o_sb + (int64_t)q0 * p.o_st;
     const int row0 = ti * R;
     const int lq = lane >> 4;   // lane group 0..3
-    int myrow[2];
-    bool row_ok[2];
+    int myrow[RB];
+    bool row_ok[RB];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < RB; ++rb) {
         myrow[rb] = row0 + rboff[rb] + (lane & 15);   // local query row of this lane
         row_ok[rb] = myrow[rb] < qn;
     }
@@ -328,9 +342,9 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) 
     // -inf instead of 0 * -inf, and every admitted key weighs 2^0.)
     const float sl2 = fmaxf(fabsf(p.sl2), 1e-30f);
     const uint32_t qsign = p.sl2 < 0.f ? 0x80008000u : 0u;
-    bf16x8_t qf[2][NS];
+    bf16x8_t qf[RB][NS];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < RB; ++rb) {
         const uint16_t *qr =
             p.q + qrow0 + (int64_t)min(myrow[rb], qn - 1) * p.q_st + (int64_t)hq[rb] * p.q_sh + 8 * lq;
 #pragma unroll
@@ -343,9 +357,9 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) 
 
     // O^T accumulators, and row sums of P from an MFMA against a ones
     // operand (every entry of lacc[rb] holds the lane's row sum).
-    f32x4_t oacc[2][NM], lacc[2];
+    f32x4_t oacc[RB][NM], lacc[RB];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < RB; ++rb) {
         lacc[rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int m = 0; m < NM; ++m) oacc[rb][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -354,15 +368,20 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) 
     // Softmax reference per row (scaled, log2 units), raised lazily: only
     // when a score exceeds it by more than 2^8, so P stays <= 256 and the
     // rescale of O is mostly skipped.
-    float m_ref[2] = {-INFINITY, -INFINITY};
+    float m_ref[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) m_ref[rb] = -INFINITY;
     const int wrow0 = row0 + rboff[0];   // first row of this wave
 
-    // Staging assignment: keys 4*(tid >> 4) + r (r = 0..3) of K and of V,
-    // chunk cc = tid & 15.
+    // Staging assignment: chunk cc = ttid % CPR of the K and V rows of keys
+    // 4kg .. 4kg+3, for key groups kg = ttid / CPR + KGS * pass < 16 (at
+    // D = 256 a team's 256 threads cover the 16 groups in two passes).
+    constexpr int KGS = 256 / CPR;                       // key groups per pass
+    constexpr int NPASS = KGS >= 16 ? 1 : 16 / KGS;
     StageCtx sc;
     sc.cc = ttid % CPR;
-    sc.kg = ttid / CPR;
-    sc.stager = sc.kg < 16;
+    const int kg0 = ttid / CPR;
+    const bool stager = kg0 < 16;
     // A sequence of one row tile has its keys read by this workgroup alone
     // (all query heads of the KV head are packed here): stream them past the
     // caches.  Longer sequences keep them cached for their other row tiles.
@@ -372,7 +391,17 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) 
     sc.kbase = p.k + seq_base + (int64_t)g * p.s_head + sc.cc * 8;
     sc.vbase = p.v + seq_base + (int64_t)g * p.s_head + sc.cc * 8;
     const int32_t *bt_row = PAGED ? p.bt + b * p.bt_sb : nullptr;
-    Stage st_regs;
+    Stage st_regs[NPASS];
+    auto load_tile = [&](int kt) {
+        if (!stager) return;
+#pragma unroll
+        for (int ps = 0; ps < NPASS; ++ps) load_stage<PAGED>(p, sc, kg0 + KGS * ps, kt, st_regs[ps]);
+    };
+    auto store_tile = [&](uint16_t *k_lds, uint16_t *v_lds) {
+        if (!stager) return;
+#pragma unroll
+        for (int ps = 0; ps < NPASS; ++ps) store_stage<D>(sc, kg0 + KGS * ps, st_regs[ps], k_lds, v_lds);
+    };
 
     MaskCtx mc;
     mc.base = p.mask + (int64_t)b * p.m_sb + (MASK == 3 ? (int64_t)row0 * p.m_sq : 0);
@@ -380,15 +409,15 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) 
     mc.rows = MASK == 3 ? min(R, qn - row0) : 1;
     MaskStage<MASK, NQ> mst;
     // Mask row (within the tile) of each of this lane's two query rows.
-    int mloc[2];
+    int mloc[RB];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) mloc[rb] = MASK == 3 ? rboff[rb] + (lane & 15) : 0;
+    for (int rb = 0; rb < RB; ++rb) mloc[rb] = MASK == 3 ? rboff[rb] + (lane & 15) : 0;
 
     // Keys row myrow[rb] admits: j < lim[rb] (length and causal frontier);
     // the wave's first row has the smallest limit.
-    int lim[2];
+    int lim[RB];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) lim[rb] = causal_on ? min(n, c + myrow[rb] + 1) : n;
+    for (int rb = 0; rb < RB; ++rb) lim[rb] = causal_on ? min(n, c + myrow[rb] + 1) : n;
     const int lim_wave = causal_on ? min(n, c + wrow0 + 1) : n;
 
     // One tile of math from LDS buffer `buf`.  FULL: every key of the tile is
@@ -403,21 +432,23 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) 
         // S^T blocks: keys 16kb + 4lq + i of the tile, rows myrow[rb].
         // Depth step outermost: eight independent accumulators per step, so
         // no MFMA waits on the result of the one before it.
-        f32x4_t st[2][4];
+        f32x4_t st[RB][4];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) st[0][kb] = st[1][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) st[rb][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < NS; ++s)
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
                 const bf16x8_t a = as_bf16x8(
                     *reinterpret_cast<const uint4 *>(&kl[(16 * kb + (lane & 15)) * KLD + 32 * s + 8 * lq]));
-                st[0][kb] = mfma16(a, qf[0][s], st[0][kb]);
-                st[1][kb] = mfma16(a, qf[1][s], st[1][kb]);
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) st[rb][kb] = mfma16(a, qf[rb][s], st[rb][kb]);
             }
         // Scores of keys not admitted become -inf (then P = 0).
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
+        for (int rb = 0; rb < RB; ++rb) {
             const int room = lim[rb] - (kt * BK + 4 * lq);   // admitted iff 16kb + i < room
             uint2 kbits = make_uint2(~0u, ~0u);               // keys 0..31, 32..63 of the tile
             if constexpr (MASK != 0) kbits = *reinterpret_cast<const uint2 *>(&mbits[team][buf][mloc[rb] * 8]);
@@ -435,10 +466,11 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) 
             }
         }
         // Row maxima of the unscaled scores, then the lazy reference.
-        float mts[2];
-        bool raise[2];
+        float mts[RB];
+        bool raise[RB];
+        bool any_raise = false;
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
+        for (int rb = 0; rb < RB; ++rb) {
             float mt = -INFINITY;
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
@@ -447,10 +479,11 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) 
             mt = fmaxf(mt, __shfl_xor(mt, 32));
             mts[rb] = mt * sl2;
             raise[rb] = mts[rb] > m_ref[rb] + 8.f;   // false for an all-masked tile
+            any_raise = any_raise || raise[rb];
         }
-        if (__builtin_amdgcn_ballot_w64(raise[0] || raise[1])) {
+        if (__builtin_amdgcn_ballot_w64(any_raise)) {
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
+            for (int rb = 0; rb < RB; ++rb) {
                 const float alpha = raise[rb] ? exp2_fast(m_ref[rb] - mts[rb]) : 1.f;   // 0 from -inf
                 m_ref[rb] = raise[rb] ? mts[rb] : m_ref[rb];
                 lacc[rb] *= alpha;
@@ -459,9 +492,9 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) 
             }
         }
         // P = 2^(s * scale * log2 e - reference), rounded to bf16 pairs.
-        uint32_t pw[2][2][4];
+        uint32_t pw[RB][2][4];
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
+        for (int rb = 0; rb < RB; ++rb) {
             const float neg_ref = m_ref[rb] == -INFINITY ? 0.f : -m_ref[rb];
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2)
@@ -477,17 +510,19 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) 
         // O^T += V^T . P^T, and the row sums.
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-            const bf16x8_t pb0 = as_bf16x8(make_uint4(pw[0][s2][0], pw[0][s2][1], pw[0][s2][2], pw[0][s2][3]));
-            const bf16x8_t pb1 = as_bf16x8(make_uint4(pw[1][s2][0], pw[1][s2][1], pw[1][s2][2], pw[1][s2][3]));
+            bf16x8_t pb[RB];
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+                pb[rb] = as_bf16x8(make_uint4(pw[rb][s2][0], pw[rb][s2][1], pw[rb][s2][2], pw[rb][s2][3]));
 #pragma unroll
             for (int m = 0; m < NM; ++m) {
                 const bf16x8_t a = as_bf16x8(*reinterpret_cast<const uint4 *>(
                     &vl[(16 * m + (lane & 15)) * VLD + v_col(16 * m, 4 * s2 + lq)]));
-                oacc[0][m] = mfma16(a, pb0, oacc[0][m]);
-                oacc[1][m] = mfma16(a, pb1, oacc[1][m]);
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) oacc[rb][m] = mfma16(a, pb[rb], oacc[rb][m]);
             }
-            lacc[0] = mfma16(ones, pb0, lacc[0]);
-            lacc[1] = mfma16(ones, pb1, lacc[1]);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) lacc[rb] = mfma16(ones, pb[rb], lacc[rb]);
         }
     };
     auto compute = [&](int kt, int buf) {
@@ -507,76 +542,78 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) 
         if constexpr (PAGED) {
             sc.first_pg = (int)udiv_magic((uint32_t)c0, p.ps_magic);
             const int npg = (int)udiv_magic((uint32_t)(c1 - 1), p.ps_magic) - sc.first_pg + 1;
-            for (int i = tid; i < npg; i += 512) pages[i] = bt_row[sc.first_pg + i];
+            for (int i = tid; i < npg; i += NT) pages[i] = bt_row[sc.first_pg + i];
         }
         __syncthreads();
-        // This team's tiles of the chunk: t0 + team, t0 + team + 2, ...
+        // This team's tiles of the chunk: t0 + team, t0 + team + TEAMS, ...
         const int kt0 = t0 + team;
-        const int nit = (t1 - t0 + 1) >> 1;
+        const int nit = (t1 - t0 + TEAMS - 1) / TEAMS;
         if (kt0 < t1) {
-            load_stage<PAGED>(p, sc, kt0, st_regs);
+            load_tile(kt0);
             if constexpr (MASK != 0) load_mask<MASK, NQ>(mc, ttid, n, kt0, mst);
-            store_stage<D>(sc, st_regs, kbuf(0), vbuf(0));
+            store_tile(kbuf(0), vbuf(0));
             if constexpr (MASK != 0) store_mask<MASK, NQ, MROWS>(mst, ttid, mbits[team][0]);
         }
-        if (kt0 + 2 < t1) {
-            load_stage<PAGED>(p, sc, kt0 + 2, st_regs);
-            if constexpr (MASK != 0) load_mask<MASK, NQ>(mc, ttid, n, kt0 + 2, mst);
+        if (kt0 + TEAMS < t1) {
+            load_tile(kt0 + TEAMS);
+            if constexpr (MASK != 0) load_mask<MASK, NQ>(mc, ttid, n, kt0 + TEAMS, mst);
         }
         __syncthreads();
         for (int it = 0; it < nit; ++it) {
-            const int kt = kt0 + 2 * it;
+            const int kt = kt0 + TEAMS * it;
             if (kt < t1) compute(kt, it & 1);
-            if (kt + 2 < t1) {
+            if (kt + TEAMS < t1) {
                 // The team's next tile into its other buffer (its readers
                 // finished at the last barrier), then the one after goes out.
-                store_stage<D>(sc, st_regs, kbuf((it + 1) & 1), vbuf((it + 1) & 1));
+                store_tile(kbuf((it + 1) & 1), vbuf((it + 1) & 1));
                 if constexpr (MASK != 0) store_mask<MASK, NQ, MROWS>(mst, ttid, mbits[team][(it + 1) & 1]);
-                if (kt + 4 < t1) {
-                    load_stage<PAGED>(p, sc, kt + 4, st_regs);
-                    if constexpr (MASK != 0) load_mask<MASK, NQ>(mc, ttid, n, kt + 4, mst);
+                if (kt + 2 * TEAMS < t1) {
+                    load_tile(kt + 2 * TEAMS);
+                    if constexpr (MASK != 0) load_mask<MASK, NQ>(mc, ttid, n, kt + 2 * TEAMS, mst);
                 }
             }
             __syncthreads();
         }
     }
 
-    // Team 1's (O, reference, sum) go through the stage buffers (free since
-    // the last barrier) to the matching wave of team 0, which merges.
-    float *xch = reinterpret_cast<float *>(stage_lds) + w * (XCH * 64);
-    if (team == 1) {
+    if constexpr (TEAMS == 2) {
+        // Team 1's (O, reference, sum) go through the stage buffers (free
+        // since the last barrier) to the matching wave of team 0, which merges.
+        float *xch = reinterpret_cast<float *>(stage_lds) + w * (XCH * 64);
+        if (team == 1) {
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
+            for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+                for (int m = 0; m < NM; ++m)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) xch[(rb * (D / 4) + m * 4 + i) * 64 + lane] = oacc[rb][m][i];
+                xch[(D / 2 + rb) * 64 + lane] = m_ref[rb];
+                xch[(D / 2 + 2 + rb) * 64 + lane] = lacc[rb][0];
+            }
+        }
+        __syncthreads();
+        if (team == 1) return;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            const float mb = xch[(D / 2 + rb) * 64 + lane], lb = xch[(D / 2 + 2 + rb) * 64 + lane];
+            const float mm = fmaxf(m_ref[rb], mb);
+            const float aa = m_ref[rb] == -INFINITY ? 0.f : exp2_fast(m_ref[rb] - mm);
+            const float ab = mb == -INFINITY ? 0.f : exp2_fast(mb - mm);
+            lacc[rb][0] = lacc[rb][0] * aa + lb * ab;
 #pragma unroll
             for (int m = 0; m < NM; ++m)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) xch[(rb * (D / 4) + m * 4 + i) * 64 + lane] = oacc[rb][m][i];
-            xch[(D / 2 + rb) * 64 + lane] = m_ref[rb];
-            xch[(D / 2 + 2 + rb) * 64 + lane] = lacc[rb][0];
+                for (int i = 0; i < 4; ++i)
+                    oacc[rb][m][i] = oacc[rb][m][i] * aa + xch[(rb * (D / 4) + m * 4 + i) * 64 + lane] * ab;
+            m_ref[rb] = mm;   // the merged (O, l) are relative to 2^mm
         }
-    }
-    __syncthreads();
-    if (team == 1) return;
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-        const float mb = xch[(D / 2 + rb) * 64 + lane], lb = xch[(D / 2 + 2 + rb) * 64 + lane];
-        const float mm = fmaxf(m_ref[rb], mb);
-        const float aa = m_ref[rb] == -INFINITY ? 0.f : exp2_fast(m_ref[rb] - mm);
-        const float ab = mb == -INFINITY ? 0.f : exp2_fast(mb - mm);
-        lacc[rb][0] = lacc[rb][0] * aa + lb * ab;
-#pragma unroll
-        for (int m = 0; m < NM; ++m)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                oacc[rb][m][i] = oacc[rb][m][i] * aa + xch[(rb * (D / 4) + m * 4 + i) * 64 + lane] * ab;
-        m_ref[rb] = mm;   // the merged (O, l) are relative to 2^mm
     }
 
     if (p.kv_splits > 1) {
         // Unnormalised partial: O^T column and (m, l), m back in natural-log
         // units of the scaled score.
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
+        for (int rb = 0; rb < RB; ++rb) {
             const int64_t t = (p.dense_lq > 0 ? (int64_t)b * p.dense_lq : (int64_t)q0) + myrow[rb];
             if (!row_ok[rb] || t >= p.part_rows) continue;
             const int64_t pr = ((int64_t)split * p.part_rows + t) * p.Hq + hq[rb];
@@ -592,7 +629,7 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) 
         return;
     }
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < RB; ++rb) {
         const float l_row = lacc[rb][0];
         if (!row_ok[rb]) continue;
         const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
@@ -610,10 +647,11 @@ __global__ __launch_bounds__(512, 2) void prefill_kernel(const PrefillParams p) 
 template <int D, int HP, bool PAGED>
 hipError_t launch_hp(const PrefillParams &p, hipStream_t stream) {
     const dim3 grid((unsigned)p.num_tiles * (unsigned)(p.Hkv * (p.G / HP)) * (unsigned)p.kv_splits);
+    const dim3 block(256 * prefill_teams<D>());
     switch (p.mask_ndim) {
-        case 0: hipLaunchKernelGGL((prefill_kernel<D, HP, 0, PAGED>), grid, dim3(512), 0, stream, p); break;
-        case 2: hipLaunchKernelGGL((prefill_kernel<D, HP, 2, PAGED>), grid, dim3(512), 0, stream, p); break;
-        case 3: hipLaunchKernelGGL((prefill_kernel<D, HP, 3, PAGED>), grid, dim3(512), 0, stream, p); break;
+        case 0: hipLaunchKernelGGL((prefill_kernel<D, HP, 0, PAGED>), grid, block, 0, stream, p); break;
+        case 2: hipLaunchKernelGGL((prefill_kernel<D, HP, 2, PAGED>), grid, block, 0, stream, p); break;
+        case 3: hipLaunchKernelGGL((prefill_kernel<D, HP, 3, PAGED>), grid, block, 0, stream, p); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -621,11 +659,13 @@ hipError_t launch_hp(const PrefillParams &p, hipStream_t stream) {
 
 template <int D, bool PAGED>
 hipError_t launch_paged(const PrefillParams &p, hipStream_t stream) {
-    switch (prefill_heads_packed(p.G)) {
+    switch (prefill_heads_packed(p.G, D)) {
         case 1: return launch_hp<D, 1, PAGED>(p, stream);
         case 2: return launch_hp<D, 2, PAGED>(p, stream);
         case 4: return launch_hp<D, 4, PAGED>(p, stream);
-        case 8: return launch_hp<D, 8, PAGED>(p, stream);
+        case 8:
+            if constexpr (D <= 128) return launch_hp<D, 8, PAGED>(p, stream);
+            else return hipErrorInvalidValue;
         default: return hipErrorInvalidValue;
     }
 }
@@ -682,15 +722,23 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(const PrefillCombi
         off = t * p.o_st;
     }
     uint16_t *dst = p.o + off + (int64_t)h * p.o_sh + lane * EPL;
-    if constexpr (EPL == 2) *reinterpret_cast<uint32_t *>(dst) = pack_bf16(acc[0] * inv, acc[1] * inv);
-    else dst[0] = (uint16_t)(pack_bf16(acc[0] * inv, 0.f) & 0xffffu);
+    if constexpr (EPL == 1) {
+        dst[0] = (uint16_t)(pack_bf16(acc[0] * inv, 0.f) & 0xffffu);
+    } else {
+#pragma unroll
+        for (int e = 0; e < EPL; e += 2) *reinterpret_cast<uint32_t *>(dst + e) = pack_bf16(acc[e] * inv, acc[e + 1] * inv);
+    }
 }
 
 }  // namespace
 
-int prefill_heads_packed(int G) { return (G & -G) < 8 ? (G & -G) : 8; }
-int prefill_tile_rows(int G) {
-    const int hp = prefill_heads_packed(G);
+int prefill_heads_packed(int G, int D) {
+    const int cap = D <= 128 ? 8 : 4;   // row blocks of a workgroup's team: eight, or four at D = 256
+    return (G & -G) < cap ? (G & -G) : cap;
+}
+int prefill_tile_rows(int G, int D) {
+    const int hp = prefill_heads_packed(G, D);
+    if (D > 128) return 64 / hp;
     return hp <= 4 ? 128 / hp : 16;
 }
 
@@ -701,6 +749,7 @@ hipError_t launch_prefill_combine(const PrefillCombineParams &p, int D, hipStrea
     if (D == 32) hipLaunchKernelGGL((prefill_combine_kernel<32>), grid, dim3(256), 0, stream, p);
     else if (D == 64) hipLaunchKernelGGL((prefill_combine_kernel<64>), grid, dim3(256), 0, stream, p);
     else if (D == 128) hipLaunchKernelGGL((prefill_combine_kernel<128>), grid, dim3(256), 0, stream, p);
+    else if (D == 256) hipLaunchKernelGGL((prefill_combine_kernel<256>), grid, dim3(256), 0, stream, p);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }
@@ -710,6 +759,7 @@ hipError_t launch_prefill(const PrefillParams &p, int D, hipStream_t stream) {
     if (D == 32) return p.bt ? launch_paged<32, true>(p, stream) : launch_paged<32, false>(p, stream);
     if (D == 64) return p.bt ? launch_paged<64, true>(p, stream) : launch_paged<64, false>(p, stream);
     if (D == 128) return p.bt ? launch_paged<128, true>(p, stream) : launch_paged<128, false>(p, stream);
+    if (D == 256) return p.bt ? launch_paged<256, true>(p, stream) : launch_paged<256, false>(p, stream);
     return hipErrorInvalidValue;
 }
 

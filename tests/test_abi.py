@@ -238,3 +238,8 @@ def test_planner_counts_one_row_per_pass_for_other_group_sizes():
     assert pa.attn_plan_splits(2, 1, 8, 128, 640, 16, 128, 256) == 2 * 640 // 64
     # G = 3: three passes of one head
     assert pa.attn_plan_splits(1, 2, 3, 128, 640, 16, 128, 256) == 2 * 3 * 640 // 64
+
+
+def test_prefill_tile_rows_head_dim_256():
+    # one team of four 16-row waves: at most four heads packed
+    assert [pa.attn_prefill_tile_rows(256, G) for G in (1, 2, 4, 8, 3, 32)] == [64, 32, 16, 16, 64, 16]

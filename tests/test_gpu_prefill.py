@@ -399,3 +399,39 @@ def test_dense_prefill_group_size_3():
     pa.attn_prefill(q.to(DEV), k.to(DEV), v.to(DEV), out, scale, is_causal=True)
     torch.cuda.synchronize()
     assert_close(out, ref, what="dense G=3")
+
+
+# ------------------------------------------------------------ head dim 256
+@pytest.mark.parametrize("G,ps,mask_ndim", [(4, 16, None), (8, 5, 3), (1, 1, 2), (2, 16, 3), (3, 16, None)])
+def test_prefill_head_dim_256(G, ps, mask_ndim):
+    """D = 256 runs one team of four waves with one 16-row block each (at
+    most four heads packed; G = 8 takes two workgroups per KV head)."""
+    case = workloads.prefill_case(990 + G + ps, 3, 2 * G, 2, 256, (0, 300), (1, 140), ps,
+                                  mask_frac=None if mask_ndim is None else 0.2, mask_ndim=mask_ndim or 3)
+    assert_close(run_prefill(case), oracle_prefill(case), what="D=256 G=%d ps=%d" % (G, ps))
+
+
+def test_prefill_head_dim_256_long_context():
+    case = workloads.prefill_case(995, 2, 8, 2, 256, None, None, 3, q_lens=[70, 37], ctx_lens=[1500, 1333],
+                                  mask_frac=0.05)
+    assert_close(run_prefill(case), oracle_prefill(case), atol=2e-3, what="D=256 long")
+
+
+@pytest.mark.parametrize("S", [1, 5])
+def test_split_prefill_head_dim_256(S):
+    case = workloads.prefill_case(996 + S, 3, 16, 2, 256, None, None, 16, q_lens=[16, 5, 1],
+                                  ctx_lens=[1200, 777, 1600])
+    assert_close(run_prefill_split(case, S), oracle_prefill(case), atol=2e-3, what="split D=256 S=%d" % S)
+
+
+def test_dense_prefill_head_dim_256():
+    B, Lq, Lk, Hkv, G = 2, 90, 300, 2, 4
+    q, k, v, mask = dense_case(997, B, Lq, Lk, Hkv * G, Hkv, D=256, layout="bhld", mask_ndim=3)
+    kv_lens = torch.tensor([300, 120], dtype=torch.int32)
+    scale = 1.0 / math.sqrt(256)
+    ref = oracle_dense(q, k, v, kv_lens, True, mask, scale)
+    out = torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device=DEV)
+    pa.attn_prefill(q.to(DEV), k.to(DEV), v.to(DEV), out, scale, is_causal=True, kv_lens=kv_lens.to(DEV),
+                    mask=mask.to(DEV))
+    torch.cuda.synchronize()
+    assert_close(out, ref, what="dense D=256")
