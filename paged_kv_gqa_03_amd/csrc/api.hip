@@ -442,8 +442,25 @@ int prefill_split_setup(pa::PrefillParams &p, const char *who, int rows, int Hq,
     return ATTN_OK;
 }
 
+// Teams per prefill workgroup.  One team uses half the LDS, so two
+// independent workgroups share a CU and their waves' MFMA and softmax
+// phases overlap: measured on MI355X 5-10% faster on ragged and dense
+// prefill, even on grids of about one workgroup per CU.  Two teams halve a
+// workgroup's serial walk over the keys and keep twice the K/V loads in
+// flight, which wins only on grids of a few long walks (short query runs
+// over long contexts, split or not).  Hence: two teams when the grid before
+// any KV split holds at most one workgroup per two CUs.  D = 256 always runs
+// one team.
+int prefill_teams_for(int64_t base_workgroups, int D) {
+    if (D > 128) return 1;
+    const int cus = device_cus();
+    return (cus > 0 && 2 * base_workgroups <= cus) ? 2 : 1;
+}
+
 // Split kernel, then (S > 1) the combine into o.
-int run_prefill(const pa::PrefillParams &p, int D, hipStream_t stream) {
+int run_prefill(pa::PrefillParams &p, int D, hipStream_t stream) {
+    const int64_t base = (int64_t)p.num_tiles * p.Hkv * (p.G / pa::prefill_heads_packed(p.G, D));
+    p.teams = prefill_teams_for(base, D);
     hipError_t e = pa::launch_prefill(p, D, stream);
     if (e != hipSuccess) return launch_status(e, "prefill kernel");
     if (p.kv_splits > 1) {

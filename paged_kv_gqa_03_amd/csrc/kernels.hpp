@@ -101,6 +101,7 @@ struct PrefillParams {
     int kv_splits;
     int part_rows;
     float *o_part, *ml_part;
+    int teams;               // 1 or 2 teams of four waves per workgroup (2 only for D <= 128)
 };
 
 // Query heads HP one prefill workgroup packs (they share a KV head): the

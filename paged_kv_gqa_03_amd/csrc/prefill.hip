@@ -65,6 +65,17 @@ __device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Maximum over the four 16-lane rows of the wave (lanes l, l^16, l^32,
+// l^48), in every lane: two row swaps in the vector ALU (v_permlane16_swap,
+// v_permlane32_swap) rather than LDS permutes, which would queue behind the
+// MFMA operand reads.  Either output order gives the same maximum.
+__device__ __forceinline__ float max_over_rows(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // Position of key k (0..63) inside the transposed V tile: within each group
 // of 32 keys, key 16h + 4q + i sits at 8q + 4h + i, so the eight keys that
 // lane group q contributes to one P^T operand are contiguous.
@@ -235,15 +246,15 @@ __device__ __forceinline__ void store_stage(const StageCtx &sc, int kg, const St
     store_v_pair(v_lds, d0 + 6, ph, r.v0.w, r.v1.w, r.v2.w, r.v3.w);
 }
 
-// Head dims up to 128: two teams of four waves, two 16-row blocks per wave.
-// D = 256: one team, one 16-row block per wave (O^T alone takes 64
-// registers per block, and one K + V^T stage is 71 KB of LDS).
-template <int D>
-constexpr int prefill_teams() { return D <= 128 ? 2 : 1; }
-
-template <int D, int HP, int MASK, bool PAGED>
-__global__ __launch_bounds__(256 * prefill_teams<D>(), D <= 128 ? 2 : 1) void prefill_kernel(const PrefillParams p) {
-    constexpr int TEAMS = prefill_teams<D>();
+// Head dims up to 128: two 16-row blocks per wave, and one or two teams of
+// four waves (two teams halve each workgroup's serial walk over the keys;
+// one team uses half the LDS, so two independent workgroups share a CU and
+// their waves' MFMA and softmax phases drift apart and overlap).  D = 256:
+// one team, one 16-row block per wave (O^T alone takes 64 registers per
+// block, and one K + V^T stage is 71 KB of LDS).
+template <int D, int HP, int MASK, bool PAGED, int TEAMS>
+__global__ __launch_bounds__(256 * TEAMS, D <= 128 ? 2 : 1) void prefill_kernel(const PrefillParams p) {
+    static_assert(TEAMS == 1 || D <= 128, "two teams only up to D = 128");
     constexpr int RB = D <= 128 ? 2 : 1;          // 16-row blocks per wave
     constexpr int NT = 256 * TEAMS;               // threads
     static_assert(RB == 2 || HP <= 4, "one block per wave packs at most four heads");
@@ -475,9 +486,7 @@ __global__ __launch_bounds__(256 * prefill_teams<D>(), D <= 128 ? 2 : 1) void pr
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
                 mt = fmaxf(fmaxf(mt, fmaxf(st[rb][kb][0], st[rb][kb][1])), fmaxf(st[rb][kb][2], st[rb][kb][3]));
-            mt = fmaxf(mt, __shfl_xor(mt, 16));
-            mt = fmaxf(mt, __shfl_xor(mt, 32));
-            mts[rb] = mt * sl2;
+            mts[rb] = max_over_rows(mt) * sl2;
             raise[rb] = mts[rb] > m_ref[rb] + 8.f;   // false for an all-masked tile
             any_raise = any_raise || raise[rb];
         }
@@ -644,17 +653,25 @@ __global__ __launch_bounds__(256 * prefill_teams<D>(), D <= 128 ? 2 : 1) void pr
     }
 }
 
-template <int D, int HP, bool PAGED>
-hipError_t launch_hp(const PrefillParams &p, hipStream_t stream) {
+template <int D, int HP, bool PAGED, int TEAMS>
+hipError_t launch_teams(const PrefillParams &p, hipStream_t stream) {
     const dim3 grid((unsigned)p.num_tiles * (unsigned)(p.Hkv * (p.G / HP)) * (unsigned)p.kv_splits);
-    const dim3 block(256 * prefill_teams<D>());
+    const dim3 block(256 * TEAMS);
     switch (p.mask_ndim) {
-        case 0: hipLaunchKernelGGL((prefill_kernel<D, HP, 0, PAGED>), grid, block, 0, stream, p); break;
-        case 2: hipLaunchKernelGGL((prefill_kernel<D, HP, 2, PAGED>), grid, block, 0, stream, p); break;
-        case 3: hipLaunchKernelGGL((prefill_kernel<D, HP, 3, PAGED>), grid, block, 0, stream, p); break;
+        case 0: hipLaunchKernelGGL((prefill_kernel<D, HP, 0, PAGED, TEAMS>), grid, block, 0, stream, p); break;
+        case 2: hipLaunchKernelGGL((prefill_kernel<D, HP, 2, PAGED, TEAMS>), grid, block, 0, stream, p); break;
+        case 3: hipLaunchKernelGGL((prefill_kernel<D, HP, 3, PAGED, TEAMS>), grid, block, 0, stream, p); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+template <int D, int HP, bool PAGED>
+hipError_t launch_hp(const PrefillParams &p, hipStream_t stream) {
+    if constexpr (D <= 128) {
+        if (p.teams == 2) return launch_teams<D, HP, PAGED, 2>(p, stream);
+    }
+    return launch_teams<D, HP, PAGED, 1>(p, stream);
 }
 
 template <int D, bool PAGED>

@@ -435,3 +435,38 @@ def test_dense_prefill_head_dim_256():
                     mask=mask.to(DEV))
     torch.cuda.synchronize()
     assert_close(out, ref, what="dense D=256")
+
+
+# ------------------------------------- one team per workgroup (full grids)
+def grid_workgroups(case, S=1):
+    G = case["Hq"] // case["Hkv"]
+    R = pa.attn_prefill_tile_rows(case["D"], G)
+    if case["D"] <= 128:
+        hp = 8 if R == 16 else 128 // R      # heads packed per workgroup
+    else:
+        hp = 64 // R
+    tiles = sum((q + R - 1) // R for q in case["q_lens"])
+    return tiles * case["Hkv"] * (G // hp) * S
+
+
+@pytest.mark.parametrize("G,D,mask_ndim,ps", [
+    (4, 128, None, 16), (4, 128, 3, 5), (8, 128, 2, 16), (2, 64, 3, 16), (1, 32, None, 3), (3, 128, None, 16),
+])
+def test_prefill_full_grid_one_team(G, D, mask_ndim, ps):
+    """Grids of more than one workgroup per two compute units run one team of
+    four waves per workgroup (two workgroups share a CU); many short
+    sequences give such a grid at a size the oracle finishes quickly.  (The
+    small cases above run two teams.)"""
+    Hkv = 8
+    case = workloads.prefill_case(1100 + G * D + ps, 96, Hkv * G, Hkv, D, (0, 120), (20, 70), ps,
+                                  mask_frac=None if mask_ndim is None else 0.2, mask_ndim=mask_ndim or 3)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert grid_workgroups(case) >= 2 * cus
+    assert_close(run_prefill(case), oracle_prefill(case), what="full grid G=%d D=%d" % (G, D))
+
+
+def test_split_prefill_full_grid_one_team():
+    case = workloads.prefill_case(1150, 64, 32, 8, 128, (100, 900), (1, 40), 16)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert grid_workgroups(case, 4) >= 2 * cus
+    assert_close(run_prefill_split(case, 4), oracle_prefill(case), atol=2e-3, what="split full grid")
