@@ -399,3 +399,16 @@ def test_partition_every_slice_count_group_size_3():
     for S in range(1, T + 8):
         got = run_paged(case, S, workspace=nan_workspace(len(lens), Hkv * G, D, S))
         assert_close(got, ref, what="G=3 S=%d of T=%d" % (S, T))
+
+
+# ------------------------------------------------------- long slices
+@pytest.mark.parametrize("ps,S", [(1, 1), (1, 3), (2, 1), (16, 1)])
+def test_paged_decode_slices_longer_than_the_page_slice(ps, S):
+    """A wave stages at most 510 block-table entries in LDS at a time, so a
+    slice longer than 510 pages runs as consecutive sub-pieces that carry
+    the softmax state across: with page size 1 a 5000-token sequence is ten
+    of them at S = 1; page size 16 covers 8160 tokens per sub-piece."""
+    lens = [5000, 1200, 17] if ps < 16 else [20000, 9000]
+    case = workloads.paged_decode_case(500 + ps + S, len(lens), 32, 8, 128, lens, ps)
+    ref, _ = oracle_paged(case)
+    assert_close(run_paged(case, S), ref, atol=2e-3, what="ps=%d S=%d" % (ps, S))
