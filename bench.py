@@ -177,6 +177,15 @@ def main():
             marks.append((e0, e1, e2, s["bytes"]))
     torch.cuda.synchronize()
     ks = [(a.elapsed_time(b), b.elapsed_time(c), nb) for a, b, c, nb in marks]
+    # Spread of the per-call times (event pair around each call's two
+    # launches): median with p10 / p90.
+    per_call = sorted((k[0] + k[1]) * 1e3 for k in ks)
+
+    def pct(q):
+        return round(per_call[min(len(per_call) - 1, int(q * (len(per_call) - 1) + 0.5))], 2)
+
+    spread = {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9), "calls": len(per_call),
+              "timing": "HIP events around each call's split and combine launches"}
     k_ms = sum(k[0] for k in ks) / len(ks)
     comb = sum(k[1] for k in ks) / len(ks)
     k_bytes = sum(k[2] for k in ks) / len(ks)
@@ -237,7 +246,7 @@ def main():
         "metric": "paged decode us/call + achieved HBM GB/s (% of peak) at B=32..128, kv 4K",
         "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 5), "us_per_call": round(ms * 1e3, 2),
-        "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4), "per_call_us": spread,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) bf16, pages scattered in a 1.5x pool)",
         "config": {"workload": "paged GQA decode B=%d Hq=32 Hkv=8 D=128 page_size=16 kv_lens %s"
