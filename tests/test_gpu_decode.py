@@ -412,3 +412,21 @@ def test_paged_decode_slices_longer_than_the_page_slice(ps, S):
     case = workloads.paged_decode_case(500 + ps + S, len(lens), 32, 8, 128, lens, ps)
     ref, _ = oracle_paged(case)
     assert_close(run_paged(case, S), ref, atol=2e-3, what="ps=%d S=%d" % (ps, S))
+
+
+@pytest.mark.parametrize("layout,S", [("page_slot_head", 0), ("page_head_slot", 0), ("page_slot_head", 5000)])
+def test_paged_decode_large_batch(layout, S):
+    """2048 sequences of 0..200 keys: the partition's scan of kv_lens walks
+    32 rows per lane (256 with one KV head per row), and S = 5000 leaves
+    many slices inside single rows.  Sampled sequences vs the oracle."""
+    g = torch.Generator().manual_seed(600)
+    lens = torch.randint(0, 201, (2048,), generator=g).tolist()
+    case = workloads.paged_decode_case(601, 2048, 16, 4, 64, lens, 16, layout=layout)
+    S = S or pa.attn_plan_splits(2048, 4, 4, 64, case["max_kv_len"], 16, case["k_pool"].stride(2))
+    out = run_paged(case, S, workspace=nan_workspace(2048, 16, 64, S)).cpu()
+    idx = torch.tensor([0, 1, 2, 511, 1000, 1023, 1024, 2000, 2046, 2047] +
+                       [i for i, n in enumerate(lens) if n == 0][:3])
+    sub = dict(q=case["q"][idx], k_pool=case["k_pool"], v_pool=case["v_pool"], block_table=case["block_table"][idx],
+               kv_lens=case["kv_lens"][idx], scale=case["scale"])
+    ref, _ = oracle_paged(sub)
+    assert_close(out[idx], ref, what="B=2048 %s S=%d" % (layout, S))

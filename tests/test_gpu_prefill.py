@@ -470,3 +470,20 @@ def test_split_prefill_full_grid_one_team():
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     assert grid_workgroups(case, 4) >= 2 * cus
     assert_close(run_prefill_split(case, 4), oracle_prefill(case), atol=2e-3, what="split full grid")
+
+
+def test_dense_split_prefill_rows_without_keys():
+    """Bottom-right causality with sequences shorter than Lq: early rows admit
+    no key in any split, so every partial is empty and the combine writes 0."""
+    B, Lq, Lk, Hkv, G, S = 2, 48, 600, 2, 4, 3
+    q, k, v, _ = dense_case(1200, B, Lq, Lk, Hkv * G, Hkv)
+    kv_lens = torch.tensor([600, 20], dtype=torch.int32)
+    scale = 1.0 / math.sqrt(128)
+    ref = oracle_dense(q, k, v, kv_lens, True, None, scale)
+    out = torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device=DEV)
+    ws = nan_workspace(pa.attn_prefill_workspace_bytes(B * Lq, Hkv * G, 128, S))
+    pa.attn_prefill_split(q.to(DEV), k.to(DEV), v.to(DEV), out, scale, is_causal=True, kv_lens=kv_lens.to(DEV),
+                          num_splits=S, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out[1, :28].cpu(), torch.zeros(28, Hkv * G, 128, dtype=torch.bfloat16))
+    assert_close(out, ref, what="dense split, rows without keys")
