@@ -85,6 +85,8 @@ def test_bf16_widening_matches_torch(orc):
     (2, 128, 1, [5, 33]),
     (8, 128, 16, [15, 16, 17, 100]),
     (4, 32, 7, [50]),
+    (3, 256, 16, [40, 90]),
+    (32, 64, 4, [33, 7]),
 ])
 def test_paged_decode_matches_sdpa(orc, G, D, ps, lens):
     Hkv = 2
@@ -305,6 +307,13 @@ def _prefill(orc, case):
 ])
 def test_paged_prefill_matches_sdpa(orc, kw):
     case = workloads.prefill_case(61, 3, 8, 2, 64, (0, 40), (1, 30), 16, **kw)
+    out, lse = _prefill(orc, case)
+    assert torch.allclose(out, sdpa_prefill_ref(case), atol=1e-12, rtol=1e-12)
+
+
+@pytest.mark.parametrize("Hq,Hkv,D", [(6, 2, 128), (8, 2, 256), (32, 1, 32)])
+def test_paged_prefill_group_sizes_and_head_dims_match_sdpa(orc, Hq, Hkv, D):
+    case = workloads.prefill_case(62 + Hq + D, 2, Hq, Hkv, D, (0, 40), (1, 30), 5, mask_frac=0.2, mask_ndim=3)
     out, lse = _prefill(orc, case)
     assert torch.allclose(out, sdpa_prefill_ref(case), atol=1e-12, rtol=1e-12)
 
