@@ -133,3 +133,27 @@ def test_random_dense_prefill(seed):
         m = (j <= (kv_lens.long() - Lq)[:, None, None] + i).contiguous()
     ref, _ = oracle.paged_prefill(qp, indptr, k, v, bt, kv_lens, scale, causal_offset=None, mask=m)
     assert_close(out, ref.reshape(B, Lq, Hkv * G, D), what)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_swa_fp8_decode(seed):
+    """fp8 sliding-window decode (K = V, head dim 512): random token counts,
+    head groups, windows (several 128-position tiles), lengths, masked slots
+    and block sizes."""
+    r = random.Random(7800 + seed)
+    T, NH = r.randint(1, 12), 16 * r.randint(1, 4)
+    W = r.choice([1, 17, 64, 128, 200, 384])
+    bs, nb = r.choice([16, 64, 256]), r.randint(1, 6)
+    slots = bs * nb
+    lens = [r.choice([0, 1, r.randint(1, W), W, W + r.randint(1, 50)]) for _ in range(T)]
+    lens = [min(n, slots) for n in lens]        # distinct slots per token
+    neg = r.choice([0.0, 0.0, 0.2])
+    what = "T=%d NH=%d W=%d bs=%d nb=%d lens=%s neg=%.1f" % (T, NH, W, bs, nb, lens, neg)
+    case = workloads.swa_case(7900 + seed, T, NH, 512, W, bs, nb, lens=lens, neg_frac=neg)
+    d = {k: case[k].to(DEV) for k in ("q", "cache", "inv_scale", "indices", "lens")}
+    out = torch.full_like(d["q"], float("nan"))
+    pa.attn_swa_fp8_decode(d["q"], d["cache"], d["inv_scale"], d["indices"], d["lens"], out, bs, case["scale"])
+    torch.cuda.synchronize()
+    ref, _ = oracle.swa_fp8_decode(case["q"], case["cache"], case["inv_scale"], case["indices"], case["lens"], bs,
+                                   case["scale"])
+    assert_close(out, ref, what)
