@@ -469,10 +469,18 @@ __global__ __launch_bounds__(256 * TEAMS, D <= 128 ? 2 : 1) void prefill_kernel(
             for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    bool ok = true;
-                    if constexpr (!FULL) ok = 16 * kb + i < room;
-                    if constexpr (MASK != 0) ok = ok && (((kb < 2 ? kbits.x : kbits.y) >> (16 * (kb & 1) + i)) & 1u);
-                    if constexpr (!FULL || MASK != 0) st[rb][kb][i] = ok ? st[rb][kb][i] : -INFINITY;
+                    if constexpr (MASK != 0) {
+                        // keep = all ones iff the key's mask bit is set (a
+                        // sign-extended one-bit field), then a bitwise select
+                        // of the score or -inf: two ALU ops per score.
+                        uint32_t keep = (uint32_t)__builtin_amdgcn_sbfe(
+                            (int)(kb < 2 ? kbits.x : kbits.y), 16 * (kb & 1) + i, 1);
+                        if constexpr (!FULL) keep = 16 * kb + i < room ? keep : 0u;
+                        st[rb][kb][i] = __uint_as_float((__float_as_uint(st[rb][kb][i]) & keep) |
+                                                        (~keep & 0xff800000u));
+                    } else if constexpr (!FULL) {
+                        st[rb][kb][i] = 16 * kb + i < room ? st[rb][kb][i] : -INFINITY;
+                    }
                 }
             }
         }
