@@ -182,6 +182,8 @@ int run_decode(pa::DecodeParams &p, int D, int G, bool paged, int max_kv_len, in
     p.W = W;
     if ((int64_t)p.R * (int64_t)max_kv_len >= (1ll << 31))
         return fail(ATTN_ERR_UNSUPPORTED, "decode: rows * max_kv_len must stay below 2^31 tokens");
+    if ((int64_t)p.B * p.Hq >= (1ll << 31))
+        return fail(ATTN_ERR_UNSUPPORTED, "decode: B * Hq must stay below 2^31");
     p.max_sub = max_sub_piece(paged ? page_size : 0);
     p.direct = mode == 0 ? 1 : 0;
     if (mode == 1 || W > 1) {
@@ -706,6 +708,8 @@ int attn_swa_fp8_decode(const void *q, int64_t q_st, int64_t q_sh,
         return fail(ATTN_ERR_INVALID_ARG, "attn_swa_fp8_decode: bad strides");
     if ((int64_t)num_blocks * block_size >= (1ll << 31))
         return fail(ATTN_ERR_UNSUPPORTED, "attn_swa_fp8_decode: num_blocks * block_size must stay below 2^31 slots");
+    if ((int64_t)T * (NH / 16) >= (1ll << 31))
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_swa_fp8_decode: T * NH / 16 must stay below 2^31");
     if (T == 0) return ok();
     pa::SwaParams p{};
     p.q = static_cast<const uint16_t *>(q);
@@ -784,7 +788,8 @@ int attn_rotary_embed(const void *x, int64_t x_st, int64_t x_sh, void *out, int6
     if (T < 0 || H <= 0 || D <= 0 || table_rows < 0)
         return fail(ATTN_ERR_INVALID_ARG, "attn_rotary_embed: bad sizes");
     if (D % 8 != 0) return fail(ATTN_ERR_UNSUPPORTED, "attn_rotary_embed: D=%d is not a multiple of 8", D);
-    if ((int64_t)T * H * (D / 8) >= (1ll << 40)) return fail(ATTN_ERR_UNSUPPORTED, "attn_rotary_embed: too large");
+    if ((int64_t)T * H * (D / 8) >= (1ll << 31))
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_rotary_embed: T * H * D / 8 must stay below 2^31");
     if (T == 0) return ok();
     if (!x || !out || !cos_table || !sin_table || !positions)
         return fail(ATTN_ERR_INVALID_ARG, "attn_rotary_embed: null pointer");

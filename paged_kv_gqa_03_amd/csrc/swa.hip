@@ -84,8 +84,11 @@ __global__ __launch_bounds__(256, 2) void swa_kernel(const SwaParams p) {
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int r = lane & 15, q4 = lane >> 4;
-    const int t = blockIdx.y;
-    const int head = blockIdx.x * 16 + r;
+    // Workgroup (token t, head group g) at t * (NH / 16) + g: the groups of a
+    // token are adjacent.
+    const int ngrp = p.NH >> 4;
+    const int t = (int)(blockIdx.x / (unsigned)ngrp);
+    const int head = (int)(blockIdx.x - (unsigned)t * (unsigned)ngrp) * 16 + r;
     int64_t len = p.lens[t];
     len = len < 0 ? 0 : (len > p.W ? p.W : len);
 
@@ -256,7 +259,7 @@ __global__ __launch_bounds__(256, 2) void swa_kernel(const SwaParams p) {
 
 hipError_t launch_swa(const SwaParams &p, hipStream_t stream) {
     if (p.T <= 0) return hipSuccess;
-    hipLaunchKernelGGL(swa_kernel, dim3(p.NH / 16, p.T), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(swa_kernel, dim3((unsigned)p.T * (unsigned)(p.NH / 16)), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 

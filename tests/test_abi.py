@@ -243,3 +243,147 @@ def test_planner_counts_one_row_per_pass_for_other_group_sizes():
 def test_prefill_tile_rows_head_dim_256():
     # one team of four 16-row waves: at most four heads packed
     assert [pa.attn_prefill_tile_rows(256, G) for G in (1, 2, 4, 8, 3, 32)] == [64, 32, 16, 16, 64, 16]
+
+
+# --- argument checks of the remaining entry points (host only) -----------
+def swa_args(**over):
+    a = dict(q=FAKE, q_st=128 * 512, q_sh=512, cache=FAKE, c_sb=256 * 512, c_ss=512, inv=FAKE, s_ss=1,
+             ind=FAKE, i_st=128, lens=FAKE, o=FAKE, o_st=128 * 512, o_sh=512, T=4, NH=128, HD=512, W=128,
+             bs=256, nb=8, scale=0.044)
+    a.update(over)
+    return a
+
+
+def call_swa(a):
+    return pa.lib().attn_swa_fp8_decode(a["q"], a["q_st"], a["q_sh"], a["cache"], a["c_sb"], a["c_ss"], a["inv"],
+                                        a["s_ss"], a["ind"], a["i_st"], a["lens"], a["o"], a["o_st"], a["o_sh"],
+                                        a["T"], a["NH"], a["HD"], a["W"], a["bs"], a["nb"], a["scale"], None)
+
+
+@pytest.mark.parametrize("over,code,word", [
+    (dict(HD=256), pa.ATTN_ERR_UNSUPPORTED, "head dim"),
+    (dict(NH=24), pa.ATTN_ERR_UNSUPPORTED, "multiple of 16"),
+    (dict(W=2048), pa.ATTN_ERR_UNSUPPORTED, "window"),
+    (dict(T=-1), pa.ATTN_ERR_INVALID_ARG, "sizes"),
+    (dict(bs=0), pa.ATTN_ERR_INVALID_ARG, "sizes"),
+    (dict(cache=None), pa.ATTN_ERR_INVALID_ARG, "null"),
+    (dict(scale=float("inf")), pa.ATTN_ERR_INVALID_ARG, "scale"),
+    (dict(q=FAKE + 8), pa.ATTN_ERR_UNSUPPORTED, "aligned"),
+    (dict(c_ss=520), pa.ATTN_ERR_UNSUPPORTED, "aligned"),
+    (dict(i_st=64), pa.ATTN_ERR_INVALID_ARG, "strides"),
+    (dict(bs=1 << 16, nb=1 << 16), pa.ATTN_ERR_UNSUPPORTED, "2^31"),
+    (dict(T=1 << 27, NH=512), pa.ATTN_ERR_UNSUPPORTED, "2^31"),
+])
+def test_swa_rejects_bad_arguments(over, code, word):
+    assert call_swa(swa_args(**over)) == code
+    assert word in pa.attn_last_error()
+
+
+def test_kv_append_rejects_bad_arguments():
+    lib = pa.lib()
+    good = [FAKE, FAKE, 8 * 128, 128, FAKE, FAKE, 10, FAKE, FAKE, 16 * 8 * 128, 8 * 128, 128, 100, FAKE, 32,
+            2, 8, 128, 16, None]
+    assert lib.attn_paged_kv_append(*good[:17], 100, *good[18:]) == pa.ATTN_ERR_UNSUPPORTED   # D % 8
+    assert "multiple of 8" in pa.attn_last_error()
+    bad = list(good); bad[0] = None
+    assert lib.attn_paged_kv_append(*bad) == pa.ATTN_ERR_INVALID_ARG and "null" in pa.attn_last_error()
+    bad = list(good); bad[3] = 100                                                            # head stride % 8
+    assert lib.attn_paged_kv_append(*bad) == pa.ATTN_ERR_UNSUPPORTED and "aligned" in pa.attn_last_error()
+    bad = list(good); bad[18] = 0                                                             # page size
+    assert lib.attn_paged_kv_append(*bad) == pa.ATTN_ERR_INVALID_ARG
+    bad = list(good); bad[6] = 0                                                              # nothing to write
+    assert lib.attn_paged_kv_append(*bad) == pa.ATTN_OK
+
+
+def test_fp8_append_rejects_bad_arguments():
+    lib = pa.lib()
+    good = [FAKE, 512, FAKE, None, 4, 512, FAKE, 256 * 512, 512, FAKE, 1, 256, 8, None, None]
+    bad = list(good); bad[5] = 256
+    assert lib.attn_swa_fp8_append(*bad) == pa.ATTN_ERR_UNSUPPORTED and "head dim" in pa.attn_last_error()
+    bad = list(good); bad[2] = None
+    assert lib.attn_swa_fp8_append(*bad) == pa.ATTN_ERR_INVALID_ARG and "null" in pa.attn_last_error()
+    bad = list(good); bad[1] = 100
+    assert lib.attn_swa_fp8_append(*bad) == pa.ATTN_ERR_UNSUPPORTED and "aligned" in pa.attn_last_error()
+    bad = list(good); bad[11] = 0
+    assert lib.attn_swa_fp8_append(*bad) == pa.ATTN_ERR_INVALID_ARG
+    bad = list(good); bad[4] = 0
+    assert lib.attn_swa_fp8_append(*bad) == pa.ATTN_OK
+
+
+def test_rotary_rejects_bad_arguments():
+    lib = pa.lib()
+    good = [FAKE, 32 * 128, 128, FAKE, 32 * 128, 128, 10, 32, 128, FAKE, FAKE, 64, 4096, FAKE, None]
+    bad = list(good); bad[8] = 100
+    assert lib.attn_rotary_embed(*bad) == pa.ATTN_ERR_UNSUPPORTED and "multiple of 8" in pa.attn_last_error()
+    bad = list(good); bad[11] = 32
+    assert lib.attn_rotary_embed(*bad) == pa.ATTN_ERR_INVALID_ARG and "table stride" in pa.attn_last_error()
+    bad = list(good); bad[13] = None
+    assert lib.attn_rotary_embed(*bad) == pa.ATTN_ERR_INVALID_ARG and "null" in pa.attn_last_error()
+    bad = list(good); bad[0] = FAKE + 4
+    assert lib.attn_rotary_embed(*bad) == pa.ATTN_ERR_UNSUPPORTED and "aligned" in pa.attn_last_error()
+    bad = list(good); bad[6] = 1 << 28
+    assert lib.attn_rotary_embed(*bad) == pa.ATTN_ERR_UNSUPPORTED and "2^31" in pa.attn_last_error()
+
+
+def paged_prefill_args(**over):
+    a = dict(q=FAKE, q_st=8 * 128, q_sh=128, indptr=FAKE, t2b=FAKE, t2i=FAKE, nt=2, k=FAKE, v=FAKE,
+             s_page=16 * 2 * 128, s_slot=2 * 128, s_head=128, bt=FAKE, bt_sb=64, lens=FAKE, causal=None,
+             mask=None, ndim=0, m_sb=0, m_sq=0, o=FAKE, o_st=8 * 128, o_sh=128, B=2, Hq=8, Hkv=2, D=128,
+             ps=16, scale=0.088)
+    a.update(over)
+    return a
+
+
+def call_paged_prefill(a):
+    return pa.lib().attn_paged_prefill(
+        a["q"], a["q_st"], a["q_sh"], a["indptr"], a["t2b"], a["t2i"], a["nt"], a["k"], a["v"], a["s_page"],
+        a["s_slot"], a["s_head"], a["bt"], a["bt_sb"], a["lens"], a["causal"], a["mask"], a["ndim"], a["m_sb"],
+        a["m_sq"], a["o"], a["o_st"], a["o_sh"], a["B"], a["Hq"], a["Hkv"], a["D"], a["ps"], a["scale"], None)
+
+
+@pytest.mark.parametrize("over,code,word", [
+    (dict(D=96), pa.ATTN_ERR_UNSUPPORTED, "head dim"),
+    (dict(Hq=7), pa.ATTN_ERR_INVALID_ARG, "multiple"),
+    (dict(ps=0), pa.ATTN_ERR_INVALID_ARG, "page_size"),
+    (dict(nt=-1), pa.ATTN_ERR_INVALID_ARG, "negative"),
+    (dict(t2b=None), pa.ATTN_ERR_INVALID_ARG, "null"),
+    (dict(lens=None), pa.ATTN_ERR_INVALID_ARG, "null"),
+    (dict(scale=float("nan")), pa.ATTN_ERR_INVALID_ARG, "scale"),
+    (dict(mask=FAKE, ndim=4), pa.ATTN_ERR_INVALID_ARG, "mask_ndim"),
+    (dict(mask=FAKE + 2, ndim=2, m_sb=64), pa.ATTN_ERR_UNSUPPORTED, "4-byte"),
+    (dict(mask=FAKE, ndim=3, m_sb=4096, m_sq=30), pa.ATTN_ERR_UNSUPPORTED, "4-byte"),
+    (dict(q=FAKE + 8), pa.ATTN_ERR_UNSUPPORTED, "aligned"),
+    (dict(o_sh=130), pa.ATTN_ERR_UNSUPPORTED, "aligned"),
+    (dict(s_page=1 << 33), pa.ATTN_ERR_UNSUPPORTED, "32-bit"),
+])
+def test_paged_prefill_rejects_bad_arguments(over, code, word):
+    assert call_paged_prefill(paged_prefill_args(**over)) == code
+    assert word in pa.attn_last_error()
+
+
+def test_dense_prefill_rejects_bad_arguments():
+    lib = pa.lib()
+
+    def call(**over):
+        a = dict(q=FAKE, q_sb=40 * 8 * 128, q_sl=8 * 128, q_sh=128, k=FAKE, v=FAKE, k_sb=500 * 2 * 128,
+                 k_sl=2 * 128, k_sh=128, lens=None, kv=500, causal=1, mask=None, ndim=0, m_sb=0, m_sq=0, o=FAKE,
+                 o_sb=40 * 8 * 128, o_sl=8 * 128, o_sh=128, B=2, Lq=40, Hq=8, Hkv=2, D=128, scale=0.088)
+        a.update(over)
+        return lib.attn_prefill(*a.values(), None)
+    assert call(D=48) == pa.ATTN_ERR_UNSUPPORTED and "head dim" in pa.attn_last_error()
+    assert call(Lq=-1) == pa.ATTN_ERR_INVALID_ARG and "negative" in pa.attn_last_error()
+    assert call(k=None) == pa.ATTN_ERR_INVALID_ARG and "null" in pa.attn_last_error()
+    assert call(k_sl=100) == pa.ATTN_ERR_UNSUPPORTED and "aligned" in pa.attn_last_error()
+    assert call(mask=FAKE, ndim=1) == pa.ATTN_ERR_INVALID_ARG and "mask_ndim" in pa.attn_last_error()
+    assert call(B=0) == pa.ATTN_OK
+
+
+def test_decode_combine_rejects_bad_arguments():
+    lib = pa.lib()
+    # workspace too small for 4 slices of B=2, Hq=8, D=128
+    rc = lib.attn_decode_combine(FAKE, 1024, 2, 8, 2, 128, 4, 128, FAKE, 300, FAKE, 8 * 128, 128, None)
+    assert rc == pa.ATTN_ERR_WORKSPACE
+    rc = lib.attn_decode_combine(FAKE, 1 << 30, 2, 8, 2, 96, 4, 128, FAKE, 300, FAKE, 8 * 128, 128, None)
+    assert rc == pa.ATTN_ERR_UNSUPPORTED
+    rc = lib.attn_decode_combine(FAKE, 1 << 30, 2, 8, 2, 128, 0, 128, FAKE, 300, FAKE, 8 * 128, 128, None)
+    assert rc == pa.ATTN_ERR_INVALID_ARG
