@@ -443,6 +443,11 @@ __global__ __launch_bounds__(256 * TEAMS, D <= 128 ? 2 : 1) void prefill_kernel(
         // S^T blocks: keys 16kb + 4lq + i of the tile, rows myrow[rb].
         // Depth step outermost: eight independent accumulators per step, so
         // no MFMA waits on the result of the one before it.
+        // The MFMA phases (S^T here, O^T below) run at a raised wave priority
+        // and the softmax between them at the normal one, so a SIMD's other
+        // wave, in its softmax, yields issue slots to the one feeding the
+        // matrix core (measured 2-3% faster on dense and masked prefill).
+        __builtin_amdgcn_s_setprio(2);
         f32x4_t st[RB][4];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
@@ -457,6 +462,7 @@ __global__ __launch_bounds__(256 * TEAMS, D <= 128 ? 2 : 1) void prefill_kernel(
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb) st[rb][kb] = mfma16(a, qf[rb][s], st[rb][kb]);
             }
+        __builtin_amdgcn_s_setprio(0);
         // Scores of keys not admitted become -inf (then P = 0).
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
@@ -524,6 +530,7 @@ __global__ __launch_bounds__(256 * TEAMS, D <= 128 ? 2 : 1) void prefill_kernel(
                                                               exp2_fast(fmaf(st[rb][kb][i + 1], sl2, neg_ref)));
                 }
         }
+        __builtin_amdgcn_s_setprio(2);
         // O^T += V^T . P^T, and the row sums.
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
@@ -541,6 +548,7 @@ __global__ __launch_bounds__(256 * TEAMS, D <= 128 ? 2 : 1) void prefill_kernel(
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) lacc[rb] = mfma16(ones, pb[rb], lacc[rb]);
         }
+        __builtin_amdgcn_s_setprio(0);
     };
     auto compute = [&](int kt, int buf) {
         if (kt * BK + BK <= lim_wave) tile_math(std::true_type{}, kt, buf);
