@@ -83,6 +83,10 @@ int attn_plan_splits(int B, int Hkv, int G, int D, int max_kv_len, int page_size
  *   o_part  float [(B + W) * Hq, D]  unnormalised partial outputs
  *   ml_part float [(B + W) * Hq, 2]  (m, l) per partial, starting at the
  *                                    first 256-byte boundary after o_part
+ *   ranges  int32 [B * Hq, 2]        per row with keys, the first and last
+ *                                    slice holding them (written by the split
+ *                                    kernel, read by the combine), at the
+ *                                    first 256-byte boundary after ml_part
  * The piece of row r in slice w is stored at slot r + w (every row or slice
  * boundary along the line advances r or w, so slots are unique); local query
  * head i of the row sits at partial row slot * heads_per_row + i.  m is a

@@ -131,6 +131,12 @@ size_t ws_ml_offset(int B, int Hq, int D, int W) {
     return (o_bytes + 255) & ~(size_t)255;
 }
 
+// Row ranges after ml_part: int32 [B * Hq, 2] (rows per sequence <= Hq).
+size_t ws_range_offset(int B, int Hq, int D, int W) {
+    const size_t end = ws_ml_offset(B, Hq, D, W) + ws_rows(B, Hq, W) * 2 * sizeof(float);
+    return (end + 255) & ~(size_t)255;
+}
+
 int check_workspace(const void *workspace, size_t workspace_bytes, int B, int Hq, int D, int W) {
     const size_t need = attn_decode_workspace_bytes(B, Hq, D, W);
     if (!workspace || workspace_bytes < need)
@@ -147,6 +153,9 @@ pa::DecodeCombineParams combine_params(const void *workspace, int B, int Hq, int
     pa::DecodeCombineParams c{};
     c.o_part = static_cast<const float *>(workspace);
     c.ml_part = reinterpret_cast<const float *>(static_cast<const char *>(workspace) + ws_ml_offset(B, Hq, D, W));
+    c.ranges = workspace ? reinterpret_cast<const int32_t *>(static_cast<const char *>(workspace) +
+                                                              ws_range_offset(B, Hq, D, W))
+                         : nullptr;
     c.kv_lens = kv_lens;
     c.kv_len_const = kv_len_const;
     c.B = B;
@@ -191,6 +200,7 @@ int run_decode(pa::DecodeParams &p, int D, int G, bool paged, int max_kv_len, in
         if (rc) return rc;
         p.o_part = static_cast<float *>(workspace);
         p.ml_part = reinterpret_cast<float *>(static_cast<char *>(workspace) + ws_ml_offset(p.B, p.Hq, D, W));
+        p.ranges = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + ws_range_offset(p.B, p.Hq, D, W));
     }
     if (p.B == 0) return ok();
     hipError_t e = pa::launch_decode(p, D, L.Gk, paged, stream);
@@ -236,7 +246,7 @@ int attn_plan_splits(int B, int Hkv, int G, int D, int max_kv_len, int page_size
 
 size_t attn_decode_workspace_bytes(int B, int Hq, int D, int num_splits) {
     if (B <= 0 || Hq <= 0 || D <= 0 || num_splits < 1) return 0;
-    return ws_ml_offset(B, Hq, D, num_splits) + ws_rows(B, Hq, num_splits) * 2 * sizeof(float);
+    return ws_range_offset(B, Hq, D, num_splits) + (size_t)B * (size_t)Hq * 2 * sizeof(int32_t);
 }
 
 int attn_decode(const void *q, int64_t q_sb, int64_t q_sh,

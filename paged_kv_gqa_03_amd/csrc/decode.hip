@@ -110,12 +110,6 @@ __device__ __forceinline__ RowScan scan_rows(const DecodeParams &p) {
     return s;
 }
 
-// Wave of the partition that holds line position x (0 <= x < T).
-__device__ __forceinline__ int wave_of(int64_t x, int64_t T, int W) {
-    const int64_t w = ((x + 1) * W - 1) / T;
-    return (int)(w < W - 1 ? w : W - 1);
-}
-
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 // Chunk lanes per head row and 16-byte chunks per lane at head dim D.
@@ -182,6 +176,13 @@ __global__ __launch_bounds__(64, (G >= 8 ? 1 : 2)) void decode_split_kernel(cons
         const int lo = max(a, P) - P, hi = min(e, P + n) - P;
         P += n;
         if (lo >= hi) continue;
+        // The waves holding the row's first and last keys record themselves,
+        // so the combine finds the row's pieces (slots r + first .. r + last)
+        // without scanning the lengths.
+        if (p.ranges && lane == 0) {
+            if (lo == 0) p.ranges[2 * (int64_t)r] = w;
+            if (hi == n) p.ranges[2 * (int64_t)r + 1] = w;
+        }
         const int b = r / p.ngrp, hgrp = r % p.ngrp;
         // A row is (sequence, group of HW KV heads), or with several passes
         // (sequence, KV head, pass): pass j covers query heads j*G .. j*G+G-1
@@ -435,16 +436,23 @@ __device__ __forceinline__ void merge_partials(const float *o_part, const float 
                                                float (&acc)[combine_epl<D>()], float &L, float &M) {
     constexpr int NC = combine_epl<D>();
     const int ln = min(lane, D / NC - 1);
+    constexpr int U = 8;
     M = -INFINITY;
-    for (int s = lane; s < S; s += 64) M = fmaxf(M, ml_part[(first + s * stride) * 2]);
-#pragma unroll
-    for (int k = 1; k < 64; k <<= 1) M = fmaxf(M, __shfl_xor(M, k));
+    L = 0.f;
 #pragma unroll
     for (int c = 0; c < NC; ++c) acc[c] = 0.f;
-    L = 0.f;
-    if (M == -INFINITY) return;
-    // Eight partials per step, all loads issued before the math.
-    constexpr int U = 8;
+    // Rows of more than 2U pieces: the maximum first, from one round of
+    // loads spread over the lanes (which also brings every (m, l) into the
+    // caches), then the sums.  Shorter rows: rounds of U pieces, every lane
+    // loading all (m, l) and its share of o, the running maximum rescaling
+    // what was summed before it.  (Measured on the B = 32 and B = 128 serving
+    // batches, whose rows have about 24 and 6-12 pieces.)
+    if (S > 2 * U) {
+        for (int s = lane; s < S; s += 64) M = fmaxf(M, ml_part[(first + s * stride) * 2]);
+#pragma unroll
+        for (int k = 1; k < 64; k <<= 1) M = fmaxf(M, __shfl_xor(M, k));
+        if (M == -INFINITY) return;
+    }
     for (int s0 = 0; s0 < S; s0 += U) {
         float2 ml[U];
         float ov[U][NC];
@@ -455,6 +463,17 @@ __device__ __forceinline__ void merge_partials(const float *o_part, const float 
             const float *op = o_part + row * D + ln * NC;
 #pragma unroll
             for (int c = 0; c < NC; ++c) ov[k][c] = op[c];
+        }
+        float mc = M;
+#pragma unroll
+        for (int k = 0; k < U; ++k) mc = (s0 + k < S) ? fmaxf(mc, ml[k].x) : mc;
+        if (mc == -INFINITY) continue;   // nothing but empty pieces so far
+        if (mc > M) {
+            const float f = M == -INFINITY ? 0.f : exp2_fast((M - mc) * kLog2e);
+            L *= f;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) acc[c] *= f;
+            M = mc;
         }
 #pragma unroll
         for (int k = 0; k < U; ++k) {
@@ -501,20 +520,15 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeCombine
     }
     const int hwg = p.Hq / p.ngrp;                 // query heads per row
     const int r = b * p.ngrp + hq / hwg;           // this head's row
-    // Start of row r on the line, and the line's total.
-    const int rpl = (p.R + 63) / 64;
-    int64_t sum = 0, before = 0;
-    for (int rr = lane * rpl; rr < min(p.R, (lane + 1) * rpl); ++rr) {
-        const int nr = p.kv_lens ? p.kv_lens[rr / p.ngrp] : p.kv_len_const;
-        sum += nr;
-        if (rr < r) before += nr;
+    // The waves that held the row's first and last keys (recorded by the
+    // split kernel); with a single slice the row was written directly.
+    if (p.W == 1 && p.direct_single) return;
+    int w0 = 0, w1 = 0;
+    if (p.W > 1) {
+        const int2 rg = *reinterpret_cast<const int2 *>(p.ranges + 2 * (int64_t)r);
+        w0 = rg.x;
+        w1 = rg.y;
     }
-#pragma unroll
-    for (int k = 1; k < 64; k <<= 1) {
-        sum += __shfl_xor(sum, k);
-        before += __shfl_xor(before, k);
-    }
-    const int w0 = wave_of(before, sum, p.W), w1 = wave_of(before + n - 1, sum, p.W);
     if (w0 == w1 && p.direct_single) return;   // written directly by the split kernel
     float acc[NC], L, M;
     merge_partials<D>(p.o_part, p.ml_part, ((int64_t)r + w0) * hwg + hq % hwg, hwg, w1 - w0 + 1, lane, acc, L, M);

@@ -31,6 +31,7 @@ struct DecodeParams {
     int64_t o_sb, o_sh;
     float *o_part;   // [(B + W) * Hq, D]   partial of slot s, local head i at row s*HW*G + i
     float *ml_part;  // [(B + W) * Hq, 2]
+    int32_t *ranges; // [R, 2]: first and last wave holding keys of row r (NULL when W = 1)
     int B, Hq, Hkv;
     int G_all;       // Hq / Hkv; a row's pass covers the kernel's G of them
     int passes;      // G_all / G: rows per (sequence, KV head); > 1 only with HW = 1
@@ -46,6 +47,7 @@ struct DecodeParams {
 // Combine of the balanced partition (one wave per sequence x query head).
 struct DecodeCombineParams {
     const float *o_part, *ml_part;
+    const int32_t *ranges;   // [R, 2] first / last wave of each row with keys (unused when W = 1)
     const int32_t *kv_lens;
     int kv_len_const;
     int B, Hq, ngrp, R, W;

@@ -68,7 +68,8 @@ def test_workspace_bytes_layout():
     assert pa.attn_decode_workspace_bytes(0, 32, 128, 4) == 0
     n = pa.attn_decode_workspace_bytes(32, 32, 128, 100)
     rows = (32 + 100) * 32
-    assert n == ((rows * 128 * 4 + 255) // 256) * 256 + rows * 2 * 4
+    ml_end = ((rows * 128 * 4 + 255) // 256) * 256 + rows * 2 * 4
+    assert n == (ml_end + 255) // 256 * 256 + 32 * 32 * 2 * 4
 
 
 def test_work_map_matches_worked_example():
