@@ -92,6 +92,18 @@ def load_traffic():
     return c.get("hbm_bytes_per_launch"), c.get("read_over_algorithmic")
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def time_calls(torch, fn, sets, steps, warmup):
     for i in range(warmup):
         fn(sets[i % len(sets)])
@@ -234,7 +246,8 @@ def main():
             calls += 1
         cpu = {"value": round(calls * sample_bytes(m) / tot_t / 1e9, 3), "unit": "GB/s",
                "cores": oracle.num_threads(), "kind": "oracle",
-               "sample": "first %d of %d sequences of set 0, %d call(s), %.1f s" % (m, c0["B"], calls, tot_t)}
+               "sample": "first %d of %d sequences of set 0, %d call(s), %.1f s" % (m, c0["B"], calls, tot_t),
+               "nproc": os.cpu_count(), "cpu_model": cpu_model()}
 
     # --- other workloads of the path (context lines, not the headline) -----
     extras = {}
