@@ -8,12 +8,17 @@
 // sequence's keys through the block table, with causality j <= c_b + i and
 // an optional keep-mask, using an online softmax over KV tiles.
 //
-// Work decomposition: one workgroup per (work-map tile, KV head), which
-// packs all HP = G query heads that share the KV head, so every K/V tile is
-// read once for the whole group (csrc commit on GQA head packing: up to one
-// head per warp of a block, K/V streamed once per block).  A wave holds two
-// 16-row MFMA blocks: for G <= 4, 32 rows of one head (a tile then has
-// 128 / G rows); for G = 8, the same 16 rows of two heads (16-row tiles).
+// Work decomposition: one workgroup per (work-map tile, KV head, head
+// group), which packs HP query heads that share the KV head (the largest
+// power of two dividing G, at most 8; all G heads for G in {1, 2, 4, 8}),
+// so every K/V tile is read once for the whole group (csrc commit on GQA
+// head packing: up to one head per warp of a block, K/V streamed once per
+// block).  A wave holds two 16-row MFMA blocks: for HP <= 4, 32 rows of one
+// head (a tile then has 128 / HP rows); for HP = 8, the same 16 rows of two
+// heads (16-row tiles).  A workgroup is one team of four waves, or two teams
+// that take alternate KV tiles of the same rows and merge at the end (the
+// host picks two only for grids of at most one workgroup per two CUs).  At
+// D = 256 a wave holds one 16-row block and a workgroup one team.
 // Split KV (for short query runs over long contexts, where tiles x KV heads
 // would not fill the device): kv_splits workgroups share a tile's keys in
 // equal runs of 64-key tiles, each writes an unnormalised fp32 partial
@@ -33,10 +38,10 @@
 // in fp32 after the dot product (csrc commit that moved the scale after
 // Q.K^T).  Keys past the causal frontier of the tile are never loaded.
 //
-// Pipeline: two LDS buffers and one register stage.  While tile t is
-// computed from one buffer, tile t+1's loads (issued a whole tile earlier)
-// land and are stored into the other, and tile t+2's loads are issued; one
-// barrier per tile.  Page ids come from a slice of the block table staged in
+// Pipeline (per team): two LDS buffers and one register stage.  While a
+// tile is computed from one buffer, the team's next tile (loaded a whole
+// iteration earlier) is stored into the other, and the one after is
+// loaded; one barrier per tile.  Page ids come from a slice of the block table staged in
 // LDS, so no global load sits between a tile's address math and its K/V
 // loads, and the keep-mask words of a tile travel with its stage.
 #include <type_traits>
