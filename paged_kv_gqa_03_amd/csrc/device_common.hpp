@@ -35,14 +35,6 @@ constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // lane i <- lane 7-i inside each half row
 constexpr int kDppMirror = 0x140;     // lane i <- lane 15-i inside each row
 
-// Sum over aligned groups of 8 lanes, result in every lane of the group.
-__device__ __forceinline__ float sum8(float x) {
-    x += dpp_mov<kDppXor1>(x);
-    x += dpp_mov<kDppXor2>(x);
-    x += dpp_mov<kDppHalfMirror>(x);
-    return x;
-}
-
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Unsigned division by a runtime divisor d via a precomputed 64-bit magic
