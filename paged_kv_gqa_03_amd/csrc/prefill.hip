@@ -57,11 +57,15 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int BK = 64;           // keys per KV tile
-// K tile row stride in LDS (elements): D + 8, e.g. 272 B at D = 128, which
-// keeps the 16-byte operand reads conflict-free.
+// Row strides in LDS (elements): K rows D + 16 (288 B at D = 128), V^T
+// rows BK + 16 (160 B).  Measured on gfx950 with SQ_LDS_BANK_CONFLICT: at
+// D + 8 / BK + 8 the 16-byte operand reads of both tiles conflicted (45% of
+// the LDS-active cycles were conflict cycles); with 16 elements of padding
+// the reads are conflict-free and only the V^T staging stores conflict
+// (14%), 3-5% less time per prefill call.
 template <int D>
-constexpr int kld() { return D + 8; }
-constexpr int VLD = BK + 8;      // V^T row stride in LDS (elements): 144 B
+constexpr int kld() { return D + 16; }
+constexpr int VLD = BK + 16;     // V^T row stride in LDS (elements): 160 B
 constexpr int kPages = 512;      // block-table entries staged in LDS at a time
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
@@ -256,7 +260,7 @@ __device__ __forceinline__ void store_stage(const StageCtx &sc, int kg, const St
 // one team uses half the LDS, so two independent workgroups share a CU and
 // their waves' MFMA and softmax phases drift apart and overlap).  D = 256:
 // one team, one 16-row block per wave (O^T alone takes 64 registers per
-// block, and one K + V^T stage is 71 KB of LDS).
+// block, and one K + V^T stage is 74 KB of LDS).
 template <int D, int HP, int MASK, bool PAGED, int TEAMS>
 __global__ __launch_bounds__(256 * TEAMS, D <= 128 ? 2 : 1) void prefill_kernel(const PrefillParams p) {
     static_assert(TEAMS == 1 || D <= 128, "two teams only up to D = 128");
