@@ -64,7 +64,7 @@ constexpr int kWavesPerCuRows = 3;
 constexpr int kWavesPerCuHead = 2;
 constexpr int kMinSliceTokens = 64;    // shortest slice the planner makes, in tokens of a row
 constexpr int kMaxPrefillSplits = 256; // upper bound on prefill KV splits
-constexpr int kPrefillWgPerCu = 1;     // prefill workgroups resident per CU (512 threads, 143 KB LDS)
+constexpr int kPrefillWgPerCu = 1;     // prefill workgroups resident per CU (512 threads, up to 159 KB LDS)
 constexpr int kMinSplitKeyTiles = 8;   // fewest 64-key tiles the prefill planner gives one split
 
 // KV heads one decode wave covers: with the heads of a token adjacent in
