@@ -420,7 +420,8 @@ int attn_swa_fp8_append(const void *x, int64_t x_st, const int64_t *slots, const
  * x[2i+1] cos with (cos, sin) = table row positions[t], column i; the math is
  * fp32 and each output is rounded to bf16 once.  Tokens whose position is
  * outside [0, table_rows) are left untouched.  Supported: D a multiple of 8,
- * 16-byte aligned rows, tab_st a multiple of 4.
+ * 16-byte aligned rows, tab_st a multiple of 4, T * H * D/8 below 2^31 and
+ * H * D/8 at most 65535 * 256 (else ATTN_ERR_UNSUPPORTED).
  */
 int attn_rotary_embed(const void *x, int64_t x_st, int64_t x_sh, void *out, int64_t o_st, int64_t o_sh,
                       int T, int H, int D, const float *cos_table, const float *sin_table, int64_t tab_st,

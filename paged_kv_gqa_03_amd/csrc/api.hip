@@ -800,6 +800,8 @@ int attn_rotary_embed(const void *x, int64_t x_st, int64_t x_sh, void *out, int6
     if (D % 8 != 0) return fail(ATTN_ERR_UNSUPPORTED, "attn_rotary_embed: D=%d is not a multiple of 8", D);
     if ((int64_t)T * H * (D / 8) >= (1ll << 31))
         return fail(ATTN_ERR_UNSUPPORTED, "attn_rotary_embed: T * H * D / 8 must stay below 2^31");
+    if ((int64_t)H * (D / 8) > 65535ll * 256)
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_rotary_embed: H * D / 8 must stay at or below 65535 * 256");
     if (T == 0) return ok();
     if (!x || !out || !cos_table || !sin_table || !positions)
         return fail(ATTN_ERR_INVALID_ARG, "attn_rotary_embed: null pointer");

@@ -31,19 +31,32 @@ __device__ __forceinline__ void st16(void *p, uint4 v) { *reinterpret_cast<uint4
 
 // ------------------------------------------------------------ KV append
 
-// One workgroup per new row: the row's sequence comes from a search of the
-// indptr (uniform, scalar loads), then its K and V chunks are copied.
+// One workgroup per new row.  The row's sequence b is the first with
+// indptr[b + 1] > i, found 64 sequences at a time by one round of vector
+// loads and a ballot; the same round brings indptr[b] and start_pos[b], so
+// the row's page lookup waits for a single dependent load instead of a
+// binary search's log2(B).
 __global__ __launch_bounds__(256) void kv_append_kernel(const KvAppendParams p) {
     const int i = blockIdx.x;
-    int lo = 0, hi = p.B;   // first b with indptr[b + 1] > i
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (p.indptr[mid + 1] > i) hi = mid;
-        else lo = mid + 1;
+    const int lane = threadIdx.x & 63;
+    int b = p.B, first = 0, start = 0;
+    for (int base = 0; base < p.B; base += 64) {
+        const int k = base + lane;
+        const bool in = k < p.B;
+        const int hi = in ? p.indptr[k + 1] : 0;
+        const int lo = in ? p.indptr[k] : 0;
+        const int sp = in ? p.start_pos[k] : 0;
+        const uint64_t hit = __ballot(in && hi > i);
+        if (hit) {
+            const int l = __ffsll((unsigned long long)hit) - 1;
+            b = base + l;
+            first = __shfl(lo, l);
+            start = __shfl(sp, l);
+            break;
+        }
     }
-    const int b = lo;
     if (b >= p.B) return;
-    const int64_t pos = (int64_t)p.start_pos[b] + (i - p.indptr[b]);
+    const int64_t pos = (int64_t)start + (i - first);
     if (pos < 0) return;
     const int32_t page = p.bt[(int64_t)b * p.bt_sb + pos / p.ps];
     if (page < 0 || page >= p.num_pages) return;   // not a page of the pool: nothing is written
@@ -128,17 +141,20 @@ __global__ __launch_bounds__(256) void swa_quantize_kernel(const SwaQuantParams 
 
 // ------------------------------------------------------------- rotary
 
-// One thread per 16 bytes (four pairs) of a head row.
+// One row of workgroups per token (blockIdx.x): its H head rows of D/8
+// 16-byte chunks (four pairs each) are spread over blockIdx.y and the
+// threads, so the token's position is one uniform load and the index math
+// stays 32-bit.
 __global__ __launch_bounds__(256) void rotary_kernel(const RotaryParams p) {
     const int cpr = p.D / 8;
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= (int64_t)p.T * p.H * cpr) return;
-    const int c = (int)(idx % cpr);
-    const int64_t th = idx / cpr;
-    const int h = (int)(th % p.H), t = (int)(th / p.H);
+    const int t = blockIdx.x;
+    const int j = blockIdx.y * blockDim.x + threadIdx.x;   // chunk among the token's H rows
+    if (j >= p.H * cpr) return;
+    const int h = j / cpr, c = j - h * cpr;
+    // The row's chunk goes out with the position load, not after it.
+    const uint4 raw = ld16(p.x + (int64_t)t * p.x_st + (int64_t)h * p.x_sh + 8 * c);
     const int pos = p.pos[t];
     if (pos < 0 || pos >= p.rows) return;          // outside the table: the row is left as it is
-    const uint4 raw = ld16(p.x + (int64_t)t * p.x_st + (int64_t)h * p.x_sh + 8 * c);
     const float4 cs = *reinterpret_cast<const float4 *>(p.cos + (int64_t)pos * p.tab_st + 4 * c);
     const float4 sn = *reinterpret_cast<const float4 *>(p.sin + (int64_t)pos * p.tab_st + 4 * c);
     const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
@@ -169,9 +185,12 @@ hipError_t launch_swa_quantize(const SwaQuantParams &p, hipStream_t stream) {
 }
 
 hipError_t launch_rotary(const RotaryParams &p, hipStream_t stream) {
-    const int64_t n = (int64_t)p.T * p.H * (p.D / 8);
-    if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(rotary_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p);
+    const int per_token = p.H * (p.D / 8);   // 16-byte chunks of one token
+    if (p.T <= 0 || per_token <= 0) return hipSuccess;
+    const int threads = per_token >= 256 ? 256 : (per_token + 63) / 64 * 64;
+    const int ny = (per_token + threads - 1) / threads;
+    if (ny > 65535) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(rotary_kernel, dim3((unsigned)p.T, (unsigned)ny), dim3(threads), 0, stream, p);
     return hipGetLastError();
 }
 
