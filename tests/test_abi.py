@@ -324,6 +324,9 @@ def test_rotary_rejects_bad_arguments():
     assert lib.attn_rotary_embed(*bad) == pa.ATTN_ERR_UNSUPPORTED and "aligned" in pa.attn_last_error()
     bad = list(good); bad[6] = 1 << 28
     assert lib.attn_rotary_embed(*bad) == pa.ATTN_ERR_UNSUPPORTED and "2^31" in pa.attn_last_error()
+    # one token with more head chunks than a grid column of 65535 workgroups holds
+    bad = list(good); bad[6] = 1; bad[7] = 65535 * 256 // 16 + 1
+    assert lib.attn_rotary_embed(*bad) == pa.ATTN_ERR_UNSUPPORTED and "65535" in pa.attn_last_error()
 
 
 def paged_prefill_args(**over):
