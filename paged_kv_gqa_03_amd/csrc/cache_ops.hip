@@ -75,30 +75,6 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const KvAppendParams p) 
 
 // ------------------------------------------------- fp8 quantize-on-write
 
-// Nearest OCP e4m3fn code of a binary32 value, from the format's definition:
-// sign bit kept, magnitudes >= 448 saturate to 448 (0x7E), NaN gives 0x7F;
-// normals keep 3 mantissa bits rounded to nearest even (a carry moves to the
-// next binade); below 2^-6 the value is a multiple of 2^-9, rounded to
-// nearest even (8 * 2^-9 is the smallest normal, code 0x08, the same bits).
-__device__ __forceinline__ uint32_t e4m3fn_code(float v) {
-    const uint32_t u = __float_as_uint(v);
-    const uint32_t sign = (u >> 24) & 0x80u;
-    const uint32_t a = u & 0x7fffffffu;
-    if (a > 0x7f800000u) return 0x7Fu;
-    const float af = __uint_as_float(a);
-    if (af >= 448.0f) return sign | 0x7Eu;
-    if (af < 0.015625f) return sign | (uint32_t)rintf(af * 512.0f);
-    int e = (int)(a >> 23) - 127;
-    uint32_t q = (a >> 20) & 7u;
-    const uint32_t rem = a & 0xfffffu;
-    q += (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) ? 1u : 0u;
-    if (q == 8u) {
-        q = 0u;
-        ++e;
-    }
-    return sign | ((uint32_t)(e + 7) << 3) | q;
-}
-
 __device__ __forceinline__ uint16_t bf16_rne(float f) {
     const uint32_t u = __float_as_uint(f);
     if ((u & 0x7f800000u) == 0x7f800000u) return (uint16_t)(u >> 16);
@@ -129,11 +105,29 @@ __global__ __launch_bounds__(256) void swa_quantize_kernel(const SwaQuantParams 
     if (slot < 0 || slot >= p.num_slots) return;   // not a slot of the cache: nothing is written
     const uint32_t blk = udiv_magic((uint32_t)slot, p.bs_magic);
     const uint32_t off = (uint32_t)slot - blk * (uint32_t)p.bs;
-    uint32_t lo = 0, hi = 0;
+    // Codes from the hardware conversion (v_cvt_pk_fp8_f32: nearest even,
+    // OCP e4m3fn on gfx950).  Checked against the format's definition on
+    // every code, every midpoint between neighbouring codes and its two
+    // neighbouring floats, subnormals and signed zeros: bit-exact, except
+    // that the conversion turns overflow and infinities into NaN and keeps
+    // a NaN's sign.  So magnitudes are clamped to 448 first (saturation), and
+    // NaN products give 0x7F through a byte mask.
+    float y[8];
+    uint32_t nan_lo = 0, nan_hi = 0;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) lo |= e4m3fn_code(v[k] * m) << (8 * k);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) hi |= e4m3fn_code(v[4 + k] * m) << (8 * k);
+    for (int k = 0; k < 8; ++k) {
+        const float t = v[k] * m;   // the product in binary32
+        const uint32_t nm = (t != t) ? (0xffu << (8 * (k & 3))) : 0u;
+        if (k < 4) nan_lo |= nm;
+        else nan_hi |= nm;
+        y[k] = fminf(fmaxf(t, -448.0f), 448.0f);
+    }
+    uint32_t lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+    lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], (int)lo, true);
+    uint32_t hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
+    hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], (int)hi, true);
+    lo = (lo & ~nan_lo) | (0x7f7f7f7fu & nan_lo);
+    hi = (hi & ~nan_hi) | (0x7f7f7f7fu & nan_hi);
     *reinterpret_cast<uint2 *>(p.cache + (int64_t)blk * p.c_sb + (int64_t)off * p.c_ss + 8 * lane) =
         make_uint2(lo, hi);
     if (lane == 0) p.inv_scale[slot * p.s_ss] = bf16_rne(1.0f / m);

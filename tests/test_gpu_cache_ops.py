@@ -132,12 +132,13 @@ def test_fp8_append_matches_oracle_bit_for_bit(explicit):
 
 
 def test_fp8_append_special_values():
-    """Midpoints (ties to even), saturation, signed zeros, tiny values and
-    NaN: the same codes as the oracle."""
+    """Midpoints (ties to even), saturation (finite and infinite), signed
+    zeros, tiny values and NaN: the same codes as the oracle."""
     vals = [oracle.e4m3fn_to_f64(c) for c in range(0x7F)]
     mids = [(vals[c] + vals[c + 1]) / 2 for c in range(0x7E)]
     row = mids + [-m for m in mids] + [1000.0, -1000.0, 449.0, -0.0, 0.0, 1e-6, -1e-6, 2.0 ** -10,
-                                       float("nan"), 3 * 2.0 ** -10]
+                                       float("nan"), 3 * 2.0 ** -10, float("inf"), float("-inf"), 464.0,
+                                       -464.0, 480.0]
     row = row + [0.0] * (512 - len(row))
     x = torch.tensor([row], dtype=torch.float64).to(torch.bfloat16)
     slots = torch.tensor([5], dtype=torch.int64)
