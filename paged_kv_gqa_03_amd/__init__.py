@@ -111,6 +111,26 @@ def _stream(stream):
     return ctypes.c_void_p(int(stream))
 
 
+_BF16 = (torch.bfloat16,)
+_I32 = (torch.int32,)
+_I64 = (torch.int64,)
+_F32 = (torch.float32,)
+
+
+def _dev(**named):
+    """Every tensor argument the library reads or writes through a device
+    pointer must live on the GPU (a host pointer would reach a kernel) and
+    have the element type the C ABI declares.  Values are (tensor, dtypes)
+    or (tensor, None) for any dtype; a None tensor is an absent optional."""
+    for name, (t, dtypes) in named.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("%s must be a device tensor" % name)
+        if dtypes is not None and t.dtype not in dtypes:
+            raise TypeError("%s must be %s, got %s" % (name, " or ".join(str(d) for d in dtypes), t.dtype))
+
+
 def _unit_inner(*ts):
     for t in ts:
         if t is not None and t.stride(-1) != 1:
@@ -147,6 +167,8 @@ def attn_paged_decode(q, k_pool, v_pool, block_table, kv_lens, max_kv_len, out, 
     """q [B, Hq, D]; k_pool / v_pool 4-D (page, slot, head, dim) views with
     identical strides; block_table [B, *] int32; kv_lens [B] int32; out
     [B, Hq, D] bf16.  num_splits 0 asks the planner."""
+    _dev(q=(q, _BF16), k_pool=(k_pool, _BF16), v_pool=(v_pool, _BF16), block_table=(block_table, _I32),
+         kv_lens=(kv_lens, _I32), out=(out, _BF16), workspace=(workspace, None))
     _unit_inner(q, k_pool, v_pool, out, block_table)
     assert k_pool.stride() == v_pool.stride(), "K and V pools must share strides"
     B, Hq, D = q.shape
@@ -166,6 +188,8 @@ def attn_paged_decode_split(q, k_pool, v_pool, block_table, kv_lens, max_kv_len,
                             num_splits, workspace, stream=None):
     """Split kernel only: fp32 partials for `num_splits` splits into the
     workspace (a uint8 device tensor of attn_decode_workspace_bytes)."""
+    _dev(q=(q, _BF16), k_pool=(k_pool, _BF16), v_pool=(v_pool, _BF16), block_table=(block_table, _I32),
+         kv_lens=(kv_lens, _I32), workspace=(workspace, None))
     _unit_inner(q, k_pool, v_pool, block_table)
     assert k_pool.stride() == v_pool.stride()
     B, Hq, D = q.shape
@@ -180,6 +204,7 @@ def attn_paged_decode_split(q, k_pool, v_pool, block_table, kv_lens, max_kv_len,
 
 def attn_decode_combine(workspace, B, Hq, Hkv, D, num_splits, kv_s_head, kv_lens, max_kv_len, out, stream=None):
     """Combine step of decode over a workspace filled by attn_paged_decode_split."""
+    _dev(workspace=(workspace, None), kv_lens=(kv_lens, _I32), out=(out, _BF16))
     _unit_inner(out)
     _check(lib().attn_decode_combine(
         _ptr(workspace), workspace.numel() * workspace.element_size(), int(B), int(Hq), int(Hkv), int(D),
@@ -191,6 +216,8 @@ def attn_decode_combine(workspace, B, Hq, Hkv, D, num_splits, kv_s_head, kv_lens
 def attn_decode(q, k, v, out, scale, kv_lens=None, kv_len=None, num_splits=0, workspace=None,
                 stream=None, num_cus=0):
     """q [B, Hq, D]; k, v 4-D (b, head, pos, dim) views; out [B, Hq, D]."""
+    _dev(q=(q, _BF16), k=(k, _BF16), v=(v, _BF16), out=(out, _BF16), kv_lens=(kv_lens, _I32),
+         workspace=(workspace, None))
     _unit_inner(q, k, v, out)
     B, Hq, D = q.shape
     Hkv, L = k.shape[1], k.shape[2]
@@ -208,6 +235,8 @@ def attn_decode(q, k, v, out, scale, kv_lens=None, kv_len=None, num_splits=0, wo
 
 def attn_split_combine(o_part, ml_part, out_f32=None, out_bf16=None, lse=None, stream=None):
     """o_part [S, R, D] float32, ml_part [S, R, 2] float32 (contiguous)."""
+    _dev(o_part=(o_part, _F32), ml_part=(ml_part, _F32), out_f32=(out_f32, _F32), out_bf16=(out_bf16, _BF16),
+         lse=(lse, _F32))
     S, R, D = o_part.shape
     assert o_part.is_contiguous() and ml_part.is_contiguous()
     for t in (out_f32, out_bf16, lse):
@@ -242,6 +271,10 @@ def attn_paged_prefill(q, qo_indptr, tile_to_batch, tile_to_index, k_pool, v_poo
                        kv_lens, out, page_size, scale, causal_offset=None, mask=None, stream=None):
     """q / out packed [total_q, Hq, D]; work map and index arrays on the
     device (int32); mask None, [B, kv] or [B, q, kv] uint8/bool keep-mask."""
+    _dev(q=(q, _BF16), qo_indptr=(qo_indptr, _I32), tile_to_batch=(tile_to_batch, _I32),
+         tile_to_index=(tile_to_index, _I32), k_pool=(k_pool, _BF16), v_pool=(v_pool, _BF16),
+         block_table=(block_table, _I32), kv_lens=(kv_lens, _I32), out=(out, _BF16),
+         causal_offset=(causal_offset, _I32), mask=(mask, (torch.bool, torch.uint8)))
     _unit_inner(q, k_pool, v_pool, out, block_table)
     assert k_pool.stride() == v_pool.stride()
     total_q, Hq, D = q.shape
@@ -263,6 +296,8 @@ def attn_swa_fp8_decode(q, kv_cache, inv_scale, swa_indices, swa_lens, out, bloc
     """q / out [T, NH, HD] bf16; kv_cache [num_blocks, block_size, HD] uint8
     e4m3fn codes; inv_scale [max_slots, 1] bf16; swa_indices [T, W] int64;
     swa_lens [T] int64."""
+    _dev(q=(q, _BF16), kv_cache=(kv_cache, (torch.uint8,)), inv_scale=(inv_scale, _BF16),
+         swa_indices=(swa_indices, _I64), swa_lens=(swa_lens, _I64), out=(out, _BF16))
     _unit_inner(q, kv_cache, swa_indices, out)
     T, NH, HD = q.shape
     W = swa_indices.shape[1]
@@ -280,6 +315,8 @@ def attn_paged_kv_append(k_new, v_new, new_indptr, start_pos, k_pool, v_pool, bl
     """k_new / v_new packed [N, Hkv, D] bf16 (identical strides); new_indptr
     int32 [B + 1], start_pos int32 [B] on the device; pools are the 4-D
     (page, slot, head, dim) views of attn_paged_decode."""
+    _dev(k_new=(k_new, _BF16), v_new=(v_new, _BF16), new_indptr=(new_indptr, _I32), start_pos=(start_pos, _I32),
+         k_pool=(k_pool, _BF16), v_pool=(v_pool, _BF16), block_table=(block_table, _I32))
     _unit_inner(k_new, v_new, k_pool, v_pool, block_table)
     assert k_new.stride() == v_new.stride() and k_pool.stride() == v_pool.stride()
     N, Hkv, D = k_new.shape
@@ -294,6 +331,8 @@ def attn_swa_fp8_append(x, slots, kv_cache, inv_scale, block_size, multiplier=No
     """x [N, HD] bf16; slots int64 [N]; kv_cache [num_blocks, block_size, HD]
     uint8; inv_scale [slots, 1] bf16; multiplier float32 [N] or None;
     amax float32 [N] output or None."""
+    _dev(x=(x, _BF16), slots=(slots, _I64), kv_cache=(kv_cache, (torch.uint8,)), inv_scale=(inv_scale, _BF16),
+         multiplier=(multiplier, _F32), amax=(amax, _F32))
     _unit_inner(x, kv_cache)
     N, HD = x.shape
     _check(lib().attn_swa_fp8_append(
@@ -306,6 +345,8 @@ def attn_rotary_embed(x, cos_table, sin_table, positions, out=None, stream=None)
     """x [T, H, D] bf16; cos_table / sin_table float32 [rows, D/2];
     positions int32 [T].  Writes out (default: x, in place) and returns it."""
     out = x if out is None else out
+    _dev(x=(x, _BF16), out=(out, _BF16), cos_table=(cos_table, _F32), sin_table=(sin_table, _F32),
+         positions=(positions, _I32))
     _unit_inner(x, out, cos_table, sin_table)
     assert cos_table.stride() == sin_table.stride()
     T, H, D = x.shape
@@ -321,6 +362,8 @@ def attn_prefill(q, k, v, out, scale, is_causal=False, kv_lens=None, mask=None, 
     [B, Lq, Hq, D] (any strides with unit innermost); k / v are (b, j, g, d)
     views [B, Lk, Hkv, D] with identical strides; kv_lens int32 [B] or None
     (all Lk); mask None, [B, Lk] or [B, Lq, Lk] keep-mask."""
+    _dev(q=(q, _BF16), k=(k, _BF16), v=(v, _BF16), out=(out, _BF16), kv_lens=(kv_lens, _I32),
+         mask=(mask, (torch.bool, torch.uint8)))
     _unit_inner(q, k, v, out)
     assert k.stride() == v.stride(), "K and V must share strides"
     B, Lq, Hq, D = q.shape
@@ -369,6 +412,10 @@ def attn_paged_prefill_split(q, qo_indptr, tile_to_batch, tile_to_index, k_pool,
                              num_splits=0, workspace=None, stream=None, target_workgroups=0):
     """attn_paged_prefill with the keys of each tile split over num_splits
     workgroups (0 asks the planner with max_kv_len) and merged by a combine."""
+    _dev(q=(q, _BF16), qo_indptr=(qo_indptr, _I32), tile_to_batch=(tile_to_batch, _I32),
+         tile_to_index=(tile_to_index, _I32), k_pool=(k_pool, _BF16), v_pool=(v_pool, _BF16),
+         block_table=(block_table, _I32), kv_lens=(kv_lens, _I32), out=(out, _BF16),
+         causal_offset=(causal_offset, _I32), mask=(mask, (torch.bool, torch.uint8)), workspace=(workspace, None))
     _unit_inner(q, k_pool, v_pool, out, block_table)
     assert k_pool.stride() == v_pool.stride()
     total_q, Hq, D = q.shape
@@ -392,6 +439,8 @@ def attn_prefill_split(q, k, v, out, scale, is_causal=False, kv_lens=None, mask=
                        workspace=None, stream=None, target_workgroups=0):
     """attn_prefill with split KV and a combine; num_splits 0 asks the
     planner (the tile count of the dense schedule, max_kv_len = Lk)."""
+    _dev(q=(q, _BF16), k=(k, _BF16), v=(v, _BF16), out=(out, _BF16), kv_lens=(kv_lens, _I32),
+         mask=(mask, (torch.bool, torch.uint8)), workspace=(workspace, None))
     _unit_inner(q, k, v, out)
     assert k.stride() == v.stride(), "K and V must share strides"
     B, Lq, Hq, D = q.shape

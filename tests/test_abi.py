@@ -391,3 +391,19 @@ def test_decode_combine_rejects_bad_arguments():
     assert rc == pa.ATTN_ERR_UNSUPPORTED
     rc = lib.attn_decode_combine(FAKE, 1 << 30, 2, 8, 2, 128, 0, 128, FAKE, 300, FAKE, 8 * 128, 128, None)
     assert rc == pa.ATTN_ERR_INVALID_ARG
+
+
+def test_binding_rejects_host_tensors():
+    """The binding passes device pointers only: a host tensor is refused
+    before any library call (its pointer would otherwise reach a kernel)."""
+    B, Hq, Hkv, D, ps = 2, 8, 2, 64, 16
+    q = torch.zeros(B, Hq, D, dtype=torch.bfloat16)
+    pool = torch.zeros(4, ps, Hkv, D, dtype=torch.bfloat16)
+    bt = torch.zeros(B, 2, dtype=torch.int32)
+    lens = torch.full((B,), 20, dtype=torch.int32)
+    with pytest.raises(ValueError, match="q must be a device tensor"):
+        pa.attn_paged_decode(q, pool, pool, bt, lens, 32, torch.empty_like(q), ps, 0.125, num_splits=1)
+    x = torch.zeros(3, 2, 64, dtype=torch.bfloat16)
+    tab = torch.zeros(8, 32, dtype=torch.float32)
+    with pytest.raises(ValueError, match="x must be a device tensor"):
+        pa.attn_rotary_embed(x, tab, tab, torch.zeros(3, dtype=torch.int32))

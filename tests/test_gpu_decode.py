@@ -430,3 +430,16 @@ def test_paged_decode_large_batch(layout, S):
                kv_lens=case["kv_lens"][idx], scale=case["scale"])
     ref, _ = oracle_paged(sub)
     assert_close(out[idx], ref, what="B=2048 %s S=%d" % (layout, S))
+
+
+def test_binding_rejects_wrong_element_types():
+    """Arguments whose element type differs from the C ABI's are refused by
+    the binding (int64 lengths, fp32 queries) instead of being reinterpreted."""
+    case = workloads.tiny_paged_decode(device=DEV)
+    out = torch.empty_like(case["q"])
+    with pytest.raises(TypeError, match="kv_lens must be torch.int32"):
+        pa.attn_paged_decode(case["q"], case["k_pool"], case["v_pool"], case["block_table"],
+                             case["kv_lens"].long(), case["max_kv_len"], out, case["page_size"], case["scale"])
+    with pytest.raises(TypeError, match="q must be torch.bfloat16"):
+        pa.attn_paged_decode(case["q"].float(), case["k_pool"], case["v_pool"], case["block_table"],
+                             case["kv_lens"], case["max_kv_len"], out, case["page_size"], case["scale"])
