@@ -440,7 +440,7 @@ def bench_prefill(torch, pa, dev, steps, warm, masked):
     def call(s):
         pa.attn_paged_prefill(s["q"], s["qo_indptr"], s["t2b"], s["t2i"], s["k_pool"], s["v_pool"],
                               s["block_table"], s["kv_lens"], s["out"], 16, s["scale"],
-                              causal_offset=s["causal_offset"], mask=s["mask"])
+                              causal_offset=s["causal_offset"], mask=s["mask"], tile_rows=R)
     ms = time_calls(torch, call, sets, steps, warm)
     fl = sum(sets[i % len(sets)]["flops"] for i in range(steps)) / steps
     tf = fl / (ms * 1e-3) / 1e12
@@ -473,7 +473,8 @@ def bench_short_q_prefill(torch, pa, dev, steps, warm):
         def call(s, n_split=n_split):
             pa.attn_paged_prefill_split(s["q"], s["qo_indptr"], s["t2b"], s["t2i"], s["k_pool"], s["v_pool"],
                                         s["block_table"], s["kv_lens"], s["out"], 16, s["scale"], mx,
-                                        causal_offset=s["causal_offset"], num_splits=n_split, workspace=ws)
+                                        causal_offset=s["causal_offset"], num_splits=n_split, workspace=ws,
+                                        tile_rows=R)
         ms = time_calls(torch, call, sets, steps, warm)
         gbs = nbytes / (ms * 1e-3) / 1e9
         res[label] = {"us_per_call": round(ms * 1e3, 2), "GB/s": round(gbs, 1),

@@ -25,6 +25,16 @@
  *     consecutive query heads share a KV head.
  *   - A query row with no admissible key (empty sequence, everything masked)
  *     produces an all-zero output row.
+ *   - Non-finite inputs are not checked; inputs are expected to be finite.
+ *     What the kernels do with a NaN (pinned by the tests): a NaN in a
+ *     query row, or in the K row of a key that the query row admits, makes
+ *     that output row NaN, as softmax attention does, whatever the split
+ *     count (a split piece whose sum l is NaN carries m = +inf, so every
+ *     merge through it is NaN).  A NaN in the V row of an admitted key makes
+ *     the rows that admit it NaN.  The K row of a key a query row does not
+ *     admit (past its length or causal frontier, or masked out) never
+ *     reaches that row; the V row of such a key may still reach rows that
+ *     share its 64-key prefill tile.  Infinite inputs are not supported.
  *   - Return value: ATTN_OK (0) or a negative ATTN_ERR_* code; then
  *     attn_last_error() gives a message.  Argument checks happen before any
  *     device work is enqueued, so a failed call leaves outputs untouched.
@@ -92,7 +102,8 @@ int attn_plan_splits(int B, int Hkv, int G, int D, int max_kv_len, int page_size
  * head i of the row sits at partial row slot * heads_per_row + i.  m is a
  * reference value in natural-log units of the scaled score (every
  * exp(score - m) <= e^(8 ln 2)); l = sum exp(score - m), o = sum exp(score -
- * m) v over the piece.  The split kernel writes every slot it owns, so the
+ * m) v over the piece (m = +inf marks a piece whose l is NaN, see the
+ * non-finite inputs convention).  The split kernel writes every slot it owns, so the
  * workspace needs no initialisation (cf. the commit that switched
  * alloc_split_partials to torch::empty).  attn_decode / attn_paged_decode
  * with W = 1 need no workspace.  Returns 0 for empty shapes.
@@ -142,8 +153,7 @@ int attn_decode(const void *q, int64_t q_sb, int64_t q_sh,
  *          slot j % page_size.  Entries past a sequence's last page are
  *          never read.
  *   kv_lens  int32 [B], each in [0, max_kv_len]
- *   max_kv_len  host-side bound on kv_lens, used by the planner;
- *          max_kv_len * page_size must stay below 2^32
+  *   max_kv_len  host-side bound on kv_lens, used by the planner
  *   o      [B, Hq, D] bf16 output
  * Supported: D in {32, 64, 128, 256}, any G (as attn_decode), any page_size >= 1.
  * A slice longer than 510 pages is processed as consecutive sub-pieces.
@@ -160,14 +170,21 @@ int attn_paged_decode(const void *q, int64_t q_sb, int64_t q_sh,
 
 /*
  * The two halves of attn_paged_decode, for callers that schedule them
- * separately (e.g. to combine partials gathered from several devices, or to
- * time each kernel).  attn_paged_decode_split takes the arguments of
- * attn_paged_decode minus the output and writes every piece as an fp32
- * partial into `workspace` (layout at attn_decode_workspace_bytes).
- * attn_decode_combine then writes o [B, Hq, D] bf16 from that workspace; it
- * must be given the same B, Hq, Hkv, D, num_splits (after planning, i.e.
- * the explicit W), KV head stride, kv_lens (NULL = all max_kv_len) and
- * max_kv_len, from which it recomputes where each row's pieces lie.
+ * separately (e.g. to time each kernel).  attn_paged_decode_split takes the
+ * arguments of attn_paged_decode minus the output and writes every piece as
+ * an fp32 partial into `workspace` (layout at attn_decode_workspace_bytes),
+ * together with the `ranges` region: for each row with keys, the first and
+ * last slice holding them.  attn_decode_combine then writes o [B, Hq, D]
+ * bf16 from that workspace: it reads the ranges region to find each row's
+ * pieces (slots r + first .. r + last), so the whole workspace written by the
+ * split call, ranges included, is its input.  It must be given the same B,
+ * Hq, Hkv, D, num_splits (after planning, i.e. the explicit W) and KV head
+ * stride as the split call, which fix the row layout; kv_lens (NULL = all
+ * max_kv_len) only marks the rows without keys, which are written as zeros.
+ * Partials produced elsewhere (another device's share of the keys) can be
+ * merged this way only if they come with a ranges region consistent with
+ * the same W and row layout; attn_split_combine merges partials stored
+ * densely instead.
  */
 int attn_paged_decode_split(const void *q, int64_t q_sb, int64_t q_sh,
                             const void *k_pool, const void *v_pool,
@@ -229,8 +246,12 @@ int attn_prefill_tile_rows(int D, int G);
  *   qo_indptr  device int32 [B + 1]; sequence b owns rows
  *          qo_indptr[b] .. qo_indptr[b+1]
  *   tile_to_batch, tile_to_index  device copies of attn_prefill_plan's
- *          output for tile_rows = attn_prefill_tile_rows(D, Hq / Hkv);
- *          num_tiles tiles
+ *          output; num_tiles tiles
+ *   tile_rows  the tile height the work map was built with; it must equal
+ *          attn_prefill_tile_rows(D, Hq / Hkv), the height this kernel
+ *          computes (a map of another height, e.g. the 64-row tiles of the
+ *          doc's worked example at G = 4, D = 128, would leave rows unwritten
+ *          or computed twice), else ATTN_ERR_INVALID_ARG
  *   k_pool, v_pool, kv_s_*, block_table, bt_sb, page_size  as in
  *          attn_paged_decode; kv_lens [B] = keys held by each sequence
  *          (prior context plus the new rows)
@@ -242,12 +263,12 @@ int attn_prefill_tile_rows(int D, int G);
  *          mask[b*m_sb + j], mask_ndim 3 reads mask[b*m_sb + i*m_sq + j]
  *          with i the local row; combined with causality by AND
  *   o      packed [total_q, Hq, D] bf16: row r, head h at o + r*o_st + h*o_sh
- * Alignment: q/k/v rows 16-byte aligned, o rows 8-byte aligned, mask rows
- * (m_sb, m_sq, pointer) 4-byte aligned; mask bytes at key positions >= kv_lens[b]
- * are never read.  Supported: D in {32, 64, 128, 256}, any G = Hq / Hkv.
+ * Alignment: q/k/v rows 16-byte aligned, o rows 8-byte aligned; mask rows
+ * may start at any byte (e.g. a plain bool [B, q, kv] tensor with kv odd);
+ * mask bytes at key positions >= kv_lens[b] are never used.  Supported: D in {32, 64, 128, 256}, any G = Hq / Hkv.
  */
 int attn_paged_prefill(const void *q, int64_t q_st, int64_t q_sh, const int32_t *qo_indptr,
-                       const int32_t *tile_to_batch, const int32_t *tile_to_index, int num_tiles,
+                       const int32_t *tile_to_batch, const int32_t *tile_to_index, int num_tiles, int tile_rows,
                        const void *k_pool, const void *v_pool,
                        int64_t kv_s_page, int64_t kv_s_slot, int64_t kv_s_head,
                        const int32_t *block_table, int64_t bt_sb, const int32_t *kv_lens,
@@ -316,7 +337,7 @@ size_t attn_prefill_workspace_bytes(int rows, int Hq, int D, int num_splits);
 int attn_prefill_plan_splits(int num_tiles, int Hq, int Hkv, int D, int max_kv_len, int target_workgroups);
 
 int attn_paged_prefill_split(const void *q, int64_t q_st, int64_t q_sh, const int32_t *qo_indptr,
-                             const int32_t *tile_to_batch, const int32_t *tile_to_index, int num_tiles,
+                             const int32_t *tile_to_batch, const int32_t *tile_to_index, int num_tiles, int tile_rows,
                              const void *k_pool, const void *v_pool,
                              int64_t kv_s_page, int64_t kv_s_slot, int64_t kv_s_head,
                              const int32_t *block_table, int64_t bt_sb, const int32_t *kv_lens,

@@ -46,7 +46,7 @@ _SIGS = {
     "attn_split_combine": ([_P, _P, _I, _I, _I, _P, _P, _P, _P], _I),
     "attn_prefill_plan": ([_P, _I, _I, _P, _P, _P, _I, _P], _I),
     "attn_prefill_tile_rows": ([_I, _I], _I),
-    "attn_paged_prefill": ([_P, _L, _L, _P, _P, _P, _I, _P, _P, _L, _L, _L, _P, _L, _P, _P,
+    "attn_paged_prefill": ([_P, _L, _L, _P, _P, _P, _I, _I, _P, _P, _L, _L, _L, _P, _L, _P, _P,
                             _P, _I, _L, _L, _P, _L, _L, _I, _I, _I, _I, _I, _F, _P], _I),
     "attn_swa_fp8_decode": ([_P, _L, _L, _P, _L, _L, _P, _L, _P, _L, _P, _P, _L, _L,
                              _I, _I, _I, _I, _I, _I, _F, _P], _I),
@@ -58,7 +58,7 @@ _SIGS = {
     "attn_rotary_embed": ([_P, _L, _L, _P, _L, _L, _I, _I, _I, _P, _P, _L, _I, _P, _P], _I),
     "attn_prefill_workspace_bytes": ([_I, _I, _I, _I], _Z),
     "attn_prefill_plan_splits": ([_I, _I, _I, _I, _I, _I], _I),
-    "attn_paged_prefill_split": ([_P, _L, _L, _P, _P, _P, _I, _P, _P, _L, _L, _L, _P, _L, _P, _P,
+    "attn_paged_prefill_split": ([_P, _L, _L, _P, _P, _P, _I, _I, _P, _P, _L, _L, _L, _P, _L, _P, _P,
                                   _P, _I, _L, _L, _P, _L, _L, _I, _I, _I, _I, _I, _F,
                                   _I, _I, _P, _Z, _P], _I),
     "attn_prefill_split": ([_P, _L, _L, _L, _P, _P, _L, _L, _L, _P, _I, _I, _P, _I, _L, _L, _P, _L, _L, _L,
@@ -268,9 +268,11 @@ def attn_prefill_plan(q_lens, tile_rows):
 
 
 def attn_paged_prefill(q, qo_indptr, tile_to_batch, tile_to_index, k_pool, v_pool, block_table,
-                       kv_lens, out, page_size, scale, causal_offset=None, mask=None, stream=None):
+                       kv_lens, out, page_size, scale, causal_offset=None, mask=None, stream=None, *, tile_rows):
     """q / out packed [total_q, Hq, D]; work map and index arrays on the
-    device (int32); mask None, [B, kv] or [B, q, kv] uint8/bool keep-mask."""
+    device (int32), built by attn_prefill_plan with `tile_rows` rows per
+    tile (the library refuses a height other than attn_prefill_tile_rows);
+    mask None, [B, kv] or [B, q, kv] uint8/bool keep-mask."""
     _dev(q=(q, _BF16), qo_indptr=(qo_indptr, _I32), tile_to_batch=(tile_to_batch, _I32),
          tile_to_index=(tile_to_index, _I32), k_pool=(k_pool, _BF16), v_pool=(v_pool, _BF16),
          block_table=(block_table, _I32), kv_lens=(kv_lens, _I32), out=(out, _BF16),
@@ -283,7 +285,7 @@ def attn_paged_prefill(q, qo_indptr, tile_to_batch, tile_to_index, k_pool, v_poo
     mask, ndim, m_sb, m_sq = _mask_args(mask)
     _check(lib().attn_paged_prefill(
         _ptr(q), q.stride(0), q.stride(1), _ptr(qo_indptr), _ptr(tile_to_batch), _ptr(tile_to_index),
-        int(tile_to_batch.numel()), _ptr(k_pool), _ptr(v_pool),
+        int(tile_to_batch.numel()), int(tile_rows), _ptr(k_pool), _ptr(v_pool),
         k_pool.stride(0), k_pool.stride(1), k_pool.stride(2), _ptr(block_table), block_table.stride(0),
         _ptr(kv_lens), _ptr(causal_offset), _ptr(mask), ndim, m_sb, m_sq,
         _ptr(out), out.stride(0), out.stride(1), B, Hq, Hkv, D, int(page_size), float(scale),
@@ -409,7 +411,7 @@ def _prefill_workspace(workspace, rows, Hq, D, S, device):
 
 def attn_paged_prefill_split(q, qo_indptr, tile_to_batch, tile_to_index, k_pool, v_pool, block_table,
                              kv_lens, out, page_size, scale, max_kv_len, causal_offset=None, mask=None,
-                             num_splits=0, workspace=None, stream=None, target_workgroups=0):
+                             num_splits=0, workspace=None, stream=None, target_workgroups=0, *, tile_rows):
     """attn_paged_prefill with the keys of each tile split over num_splits
     workgroups (0 asks the planner with max_kv_len) and merged by a combine."""
     _dev(q=(q, _BF16), qo_indptr=(qo_indptr, _I32), tile_to_batch=(tile_to_batch, _I32),
@@ -427,7 +429,7 @@ def attn_paged_prefill_split(q, qo_indptr, tile_to_batch, tile_to_index, k_pool,
     mask, ndim, m_sb, m_sq = _mask_args(mask)
     _check(lib().attn_paged_prefill_split(
         _ptr(q), q.stride(0), q.stride(1), _ptr(qo_indptr), _ptr(tile_to_batch), _ptr(tile_to_index),
-        num_tiles, _ptr(k_pool), _ptr(v_pool),
+        num_tiles, int(tile_rows), _ptr(k_pool), _ptr(v_pool),
         k_pool.stride(0), k_pool.stride(1), k_pool.stride(2), _ptr(block_table), block_table.stride(0),
         _ptr(kv_lens), _ptr(causal_offset), _ptr(mask), ndim, m_sb, m_sq,
         _ptr(out), out.stride(0), out.stride(1), B, Hq, Hkv, D, int(page_size), float(scale),

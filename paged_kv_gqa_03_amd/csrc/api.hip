@@ -301,8 +301,6 @@ static int paged_decode_impl(const void *q, int64_t q_sb, int64_t q_sh,
     if (rc) return rc;
     if (B < 0 || max_kv_len < 0) return fail(ATTN_ERR_INVALID_ARG, "%s: negative B or max_kv_len", fn);
     if (page_size <= 0) return fail(ATTN_ERR_INVALID_ARG, "%s: page_size must be >= 1", fn);
-    if ((uint64_t)max_kv_len * (uint64_t)page_size >= (1ull << 32))
-        return fail(ATTN_ERR_UNSUPPORTED, "%s: max_kv_len * page_size must be < 2^32", fn);
     if (!decode_dim(D)) return fail(ATTN_ERR_UNSUPPORTED, "%s: head dim %d not built (32, 64, 128, 256)", fn, D);
     if (!q || !k_pool || !v_pool || (!o && mode == 0) || !block_table || !kv_lens)
         return fail(ATTN_ERR_INVALID_ARG, "%s: null pointer", fn);
@@ -324,7 +322,7 @@ static int paged_decode_impl(const void *q, int64_t q_sb, int64_t q_sh,
     p.bt = block_table;
     p.bt_sb = bt_sb;
     p.ps = (uint32_t)page_size;
-    p.ps_magic = ((1ull << 32) + (uint64_t)page_size - 1) / (uint64_t)page_size;
+    p.ps_div = pa::make_divu32((uint32_t)page_size);
     p.kv_lens = kv_lens;
     p.o = static_cast<uint16_t *>(o);
     p.o_sb = o_sb; p.o_sh = o_sh;
@@ -500,7 +498,7 @@ int run_prefill(pa::PrefillParams &p, int D, hipStream_t stream) {
 }
 
 int paged_prefill_impl(const void *q, int64_t q_st, int64_t q_sh, const int32_t *qo_indptr,
-                       const int32_t *tile_to_batch, const int32_t *tile_to_index, int num_tiles,
+                       const int32_t *tile_to_batch, const int32_t *tile_to_index, int num_tiles, int tile_rows,
                        const void *k_pool, const void *v_pool,
                        int64_t kv_s_page, int64_t kv_s_slot, int64_t kv_s_head,
                        const int32_t *block_table, int64_t bt_sb, const int32_t *kv_lens,
@@ -513,6 +511,12 @@ int paged_prefill_impl(const void *q, int64_t q_st, int64_t q_sh, const int32_t 
     if (rc) return rc;
     if (!decode_dim(D)) return fail(ATTN_ERR_UNSUPPORTED, "attn_paged_prefill: head dim %d not built (32, 64, 128, 256)", D);
     if (B < 0 || num_tiles < 0) return fail(ATTN_ERR_INVALID_ARG, "attn_paged_prefill: negative B or num_tiles");
+    // The kernel's tile height is fixed per (D, G); a work map built for
+    // another height would leave rows unwritten or computed twice.
+    if (tile_rows != pa::prefill_tile_rows(G, D))
+        return fail(ATTN_ERR_INVALID_ARG,
+                    "attn_paged_prefill: work map built for tile_rows=%d, the kernel takes %d at D=%d, G=%d "
+                    "(attn_prefill_tile_rows)", tile_rows, pa::prefill_tile_rows(G, D), D, G);
     if (page_size <= 0) return fail(ATTN_ERR_INVALID_ARG, "attn_paged_prefill: page_size must be >= 1");
     if (!q || !qo_indptr || !k_pool || !v_pool || !block_table || !kv_lens || !o ||
         (num_tiles > 0 && (!tile_to_batch || !tile_to_index)))
@@ -520,8 +524,8 @@ int paged_prefill_impl(const void *q, int64_t q_st, int64_t q_sh, const int32_t 
     if (!std::isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "attn_paged_prefill: scale is not finite");
     if (mask && mask_ndim != 2 && mask_ndim != 3)
         return fail(ATTN_ERR_INVALID_ARG, "attn_paged_prefill: mask_ndim must be 2 or 3");
-    if (mask && (((uintptr_t)mask & 3u) || (m_sb & 3) || (mask_ndim == 3 && (m_sq & 3)) || m_sb < 0 || m_sq < 0))
-        return fail(ATTN_ERR_UNSUPPORTED, "attn_paged_prefill: mask rows must be 4-byte aligned");
+    if (mask && (m_sb < 0 || m_sq < 0))
+        return fail(ATTN_ERR_INVALID_ARG, "attn_paged_prefill: negative mask stride");
     if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || ((uintptr_t)o & 7u) ||
         !mult8(q_st) || !mult8(q_sh) || !mult8(kv_s_page) || !mult8(kv_s_slot) || !mult8(kv_s_head) ||
         (o_st & 3) || (o_sh & 3))
@@ -544,7 +548,7 @@ int paged_prefill_impl(const void *q, int64_t q_st, int64_t q_sh, const int32_t 
     p.s_page = kv_s_page; p.s_slot = kv_s_slot; p.s_head = kv_s_head;
     p.bt = block_table; p.bt_sb = bt_sb;
     p.ps = (uint32_t)page_size;
-    p.ps_magic = ((1ull << 32) + (uint64_t)page_size - 1) / (uint64_t)page_size;
+    p.ps_div = pa::make_divu32((uint32_t)page_size);
     p.kv_lens = kv_lens;
     p.causal = causal_offset;
     p.mask = mask;
@@ -572,8 +576,8 @@ int dense_prefill_impl(const void *q, int64_t q_sb, int64_t q_sl, int64_t q_sh,
     if (!std::isfinite(scale)) return fail(ATTN_ERR_INVALID_ARG, "attn_prefill: scale is not finite");
     if (mask && mask_ndim != 2 && mask_ndim != 3)
         return fail(ATTN_ERR_INVALID_ARG, "attn_prefill: mask_ndim must be 2 or 3");
-    if (mask && (((uintptr_t)mask & 3u) || (m_sb & 3) || (mask_ndim == 3 && (m_sq & 3)) || m_sb < 0 || m_sq < 0))
-        return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill: mask rows must be 4-byte aligned");
+    if (mask && (m_sb < 0 || m_sq < 0))
+        return fail(ATTN_ERR_INVALID_ARG, "attn_prefill: negative mask stride");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || ((uintptr_t)o & 7u) || !mult8(q_sb) || !mult8(q_sl) ||
         !mult8(q_sh) || !mult8(k_sb) || !mult8(k_sl) || !mult8(k_sh) || (o_sb & 3) || (o_sl & 3) || (o_sh & 3))
         return fail(ATTN_ERR_UNSUPPORTED, "attn_prefill: q/k/v rows must be 16-byte and o rows 8-byte aligned");
@@ -641,7 +645,7 @@ int attn_prefill_plan_splits(int num_tiles, int Hq, int Hkv, int D, int max_kv_l
 }
 
 int attn_paged_prefill(const void *q, int64_t q_st, int64_t q_sh, const int32_t *qo_indptr,
-                       const int32_t *tile_to_batch, const int32_t *tile_to_index, int num_tiles,
+                       const int32_t *tile_to_batch, const int32_t *tile_to_index, int num_tiles, int tile_rows,
                        const void *k_pool, const void *v_pool,
                        int64_t kv_s_page, int64_t kv_s_slot, int64_t kv_s_head,
                        const int32_t *block_table, int64_t bt_sb, const int32_t *kv_lens,
@@ -650,14 +654,15 @@ int attn_paged_prefill(const void *q, int64_t q_st, int64_t q_sh, const int32_t 
                        void *o, int64_t o_st, int64_t o_sh,
                        int B, int Hq, int Hkv, int D, int page_size, float scale,
                        void *stream) {
-    return paged_prefill_impl(q, q_st, q_sh, qo_indptr, tile_to_batch, tile_to_index, num_tiles, k_pool, v_pool,
+    return paged_prefill_impl(q, q_st, q_sh, qo_indptr, tile_to_batch, tile_to_index, num_tiles, tile_rows,
+                              k_pool, v_pool,
                               kv_s_page, kv_s_slot, kv_s_head, block_table, bt_sb, kv_lens, causal_offset, mask,
                               mask_ndim, m_sb, m_sq, o, o_st, o_sh, B, Hq, Hkv, D, page_size, scale, 0, 1, nullptr,
                               0, stream);
 }
 
 int attn_paged_prefill_split(const void *q, int64_t q_st, int64_t q_sh, const int32_t *qo_indptr,
-                             const int32_t *tile_to_batch, const int32_t *tile_to_index, int num_tiles,
+                             const int32_t *tile_to_batch, const int32_t *tile_to_index, int num_tiles, int tile_rows,
                              const void *k_pool, const void *v_pool,
                              int64_t kv_s_page, int64_t kv_s_slot, int64_t kv_s_head,
                              const int32_t *block_table, int64_t bt_sb, const int32_t *kv_lens,
@@ -666,7 +671,8 @@ int attn_paged_prefill_split(const void *q, int64_t q_st, int64_t q_sh, const in
                              void *o, int64_t o_st, int64_t o_sh,
                              int B, int Hq, int Hkv, int D, int page_size, float scale,
                              int total_q, int num_splits, void *workspace, size_t workspace_bytes, void *stream) {
-    return paged_prefill_impl(q, q_st, q_sh, qo_indptr, tile_to_batch, tile_to_index, num_tiles, k_pool, v_pool,
+    return paged_prefill_impl(q, q_st, q_sh, qo_indptr, tile_to_batch, tile_to_index, num_tiles, tile_rows,
+                              k_pool, v_pool,
                               kv_s_page, kv_s_slot, kv_s_head, block_table, bt_sb, kv_lens, causal_offset, mask,
                               mask_ndim, m_sb, m_sq, o, o_st, o_sh, B, Hq, Hkv, D, page_size, scale, total_q,
                               num_splits, workspace, workspace_bytes, stream);
@@ -730,7 +736,7 @@ int attn_swa_fp8_decode(const void *q, int64_t q_st, int64_t q_sh,
     p.o = static_cast<uint16_t *>(o); p.o_st = o_st; p.o_sh = o_sh;
     p.T = T; p.NH = NH; p.W = window; p.bs = block_size;
     p.slots = num_blocks * block_size;
-    p.bs_magic = ((1ull << 32) + (uint64_t)block_size - 1) / (uint64_t)block_size;
+    p.bs_div = pa::make_divu32((uint32_t)block_size);
     p.sl2 = scale * 1.4426950408889634f;
     return launch_status(pa::launch_swa(p, static_cast<hipStream_t>(stream)), "swa kernel");
 }
@@ -788,7 +794,7 @@ int attn_swa_fp8_append(const void *x, int64_t x_st, const int64_t *slots, const
     p.amax = amax_out;
     p.N = N; p.bs = block_size;
     p.num_slots = (int64_t)num_blocks * block_size;
-    p.bs_magic = ((1ull << 32) + (uint64_t)block_size - 1) / (uint64_t)block_size;
+    p.bs_div = pa::make_divu32((uint32_t)block_size);
     return launch_status(pa::launch_swa_quantize(p, static_cast<hipStream_t>(stream)), "swa quantize kernel");
 }
 

@@ -103,7 +103,7 @@ __global__ __launch_bounds__(256) void swa_quantize_kernel(const SwaQuantParams 
     if (lane == 0 && p.amax) p.amax[n] = amax;
     const int64_t slot = p.slots[n];
     if (slot < 0 || slot >= p.num_slots) return;   // not a slot of the cache: nothing is written
-    const uint32_t blk = udiv_magic((uint32_t)slot, p.bs_magic);
+    const uint32_t blk = divu32((uint32_t)slot, p.bs_div);
     const uint32_t off = (uint32_t)slot - blk * (uint32_t)p.bs;
     // Codes from the hardware conversion (v_cvt_pk_fp8_f32: nearest even,
     // OCP e4m3fn on gfx950).  Checked against the format's definition on

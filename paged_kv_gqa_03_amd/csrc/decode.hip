@@ -224,8 +224,8 @@ __global__ __launch_bounds__(64, (G >= 8 ? 1 : 2)) void decode_split_kernel(cons
             int first_pg = 0;
             if constexpr (PAGED) {
                 const int32_t *bt_row = p.bt + b * p.bt_sb;
-                first_pg = (int)udiv_magic((uint32_t)j0, p.ps_magic);
-                const int npg = (int)udiv_magic((uint32_t)last, p.ps_magic) - first_pg + 1;
+                first_pg = (int)divu32((uint32_t)j0, p.ps_div);
+                const int npg = (int)divu32((uint32_t)last, p.ps_div) - first_pg + 1;
                 __builtin_amdgcn_wave_barrier();   // earlier readers of the slice are done
                 for (int i = lane; i < npg; i += 64) pages[i] = bt_row[first_pg + i];
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -238,8 +238,8 @@ __global__ __launch_bounds__(64, (G >= 8 ? 1 : 2)) void decode_split_kernel(cons
                 const int ja = min(j0 + t * TILE + tg, last);
                 const int jb = min(j0 + t * TILE + tg + TG, last);
                 if constexpr (PAGED) {
-                    const uint32_t ia = udiv_magic((uint32_t)ja, p.ps_magic);
-                    const uint32_t ib = udiv_magic((uint32_t)jb, p.ps_magic);
+                    const uint32_t ia = divu32((uint32_t)ja, p.ps_div);
+                    const uint32_t ib = divu32((uint32_t)jb, p.ps_div);
                     ad.pa = pages[ia - first_pg];
                     ad.pb = pages[ib - first_pg];
                     ad.sa = ja - (int)(ia * p.ps);
@@ -416,7 +416,7 @@ __global__ __launch_bounds__(64, (G >= 8 ? 1 : 2)) void decode_split_kernel(cons
                         make_float4(o[h][c][4], o[h][c][5], o[h][c][6], o[h][c][7]);
                 }
                 if (jj == 0)
-                    *reinterpret_cast<float2 *>(p.ml_part + prow * 2) = make_float2(mref[h] * kLn2, lsum[h]);
+                    *reinterpret_cast<float2 *>(p.ml_part + prow * 2) = make_float2(partial_m(mref[h], lsum[h]), lsum[h]);
             }
         }
     }

@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fastdiv.hpp"
+
 namespace pa {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -37,11 +39,19 @@ constexpr int kDppMirror = 0x140;     // lane i <- lane 15-i inside each row
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Unsigned division by a runtime divisor d via a precomputed 64-bit magic
-// ceil(2^32 / d); exact when n * d < 2^32.
-__device__ __forceinline__ uint32_t udiv_magic(uint32_t n, uint64_t magic) {
-    return (uint32_t)(((uint64_t)n * magic) >> 32);
+// NaN test on the bit pattern: stays a real test in translation units
+// compiled with -fno-honor-nans, where x != x folds to false.
+__device__ __forceinline__ bool is_nan_bits(float x) { return (__float_as_uint(x) & 0x7fffffffu) > 0x7f800000u; }
+
+// Reference m of an unnormalised partial (natural-log units).  A NaN that
+// entered a piece's scores (a NaN query or key) leaves its sum l NaN while the
+// reference may still be -inf, which the combine reads as an empty piece; such
+// a piece is marked m = +inf so that every merge through it yields NaN, as
+// softmax attention does.
+__device__ __forceinline__ float partial_m(float m_log2, float l) {
+    return is_nan_bits(l) ? INFINITY : m_log2 * kLn2;
 }
+
 
 __device__ __forceinline__ int wave_id() {
     return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fastdiv.hpp"
+
 namespace pa {
 
 // Most block-table entries one decode sub-piece may span; the host caps a
@@ -24,7 +26,7 @@ struct DecodeParams {
     const int32_t *bt;
     int64_t bt_sb;
     uint32_t ps;
-    uint64_t ps_magic;  // ceil(2^32 / ps)
+    DivU32 ps_div;      // exact division by ps
     const int32_t *kv_lens;  // NULL: every sequence has kv_len_const keys
     int kv_len_const;
     uint16_t *o;
@@ -82,7 +84,7 @@ struct PrefillParams {
     const int32_t *bt;       // NULL: contiguous source
     int64_t bt_sb;
     uint32_t ps;
-    uint64_t ps_magic;
+    DivU32 ps_div;
     const int32_t *kv_lens;  // NULL: kv_len_const for every sequence
     int kv_len_const;
     const int32_t *causal;   // causal offsets (-1 = off), or NULL
@@ -139,7 +141,7 @@ struct SwaParams {
     int64_t o_st, o_sh;
     int T, NH, W, bs;
     int slots;            // num_blocks * bs: indices at or above it are not admitted
-    uint64_t bs_magic;    // ceil(2^32 / bs) for slot -> (block, offset)
+    DivU32 bs_div;        // slot -> (block, offset): exact division by bs
     float sl2;            // scale * log2(e)
 };
 
@@ -168,7 +170,7 @@ struct SwaQuantParams {
     float *amax;           // NULL: not reported
     int N, bs;
     int64_t num_slots;
-    uint64_t bs_magic;
+    DivU32 bs_div;
 };
 
 // Rotary embedding of x [T, H, D] by fp32 cos / sin tables at positions.

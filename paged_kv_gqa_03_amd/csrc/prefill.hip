@@ -108,7 +108,7 @@ struct StageCtx {
 
 __device__ __forceinline__ uint64_t key_off(const PrefillParams &p, const StageCtx &sc, int key) {
     const int kc = min(key, sc.c1 - 1);   // keys past the chunk end repeat its last key
-    const uint32_t pi = udiv_magic((uint32_t)kc, p.ps_magic);
+    const uint32_t pi = divu32((uint32_t)kc, p.ps_div);
     const int page = sc.pages[pi - sc.first_pg];
     const uint32_t slot = (uint32_t)kc - pi * p.ps;
     return (uint64_t)(uint32_t)page * (uint32_t)p.s_page + slot * (uint32_t)p.s_slot;
@@ -179,7 +179,11 @@ struct MaskCtx {
 };
 
 // Bytes [j, j + 8) of mask row `row`; bytes at or past key n read as 0 and
-// are never touched, nor are rows past `rows`.
+// are never touched, nor are rows past `rows`.  Mask rows may start at any
+// byte: the eight bytes come from the aligned dwords that hold them (two, or
+// three when the row is not 4-byte aligned; each of them holds at least one
+// byte of the range, so no read leaves the memory of the mask), joined with
+// v_alignbyte.
 template <int MASK, int NQ>
 __device__ __forceinline__ void load_mask(const MaskCtx &mc, int tid, int n, int kt, MaskStage<MASK, NQ> &m) {
     const int j = kt * BK + 8 * (tid & 7);
@@ -190,8 +194,12 @@ __device__ __forceinline__ void load_mask(const MaskCtx &mc, int tid, int n, int
         if (row < mc.rows) {
             const uint8_t *mp = mc.base + row * mc.m_sq + j;
             if (j + 8 <= n) {
-                m.w[q][0] = *reinterpret_cast<const uint32_t *>(mp);
-                m.w[q][1] = *reinterpret_cast<const uint32_t *>(mp + 4);
+                const uint32_t sh = (uint32_t)reinterpret_cast<uintptr_t>(mp) & 3u;
+                const uint32_t *wp = reinterpret_cast<const uint32_t *>(mp - sh);
+                const uint32_t w0 = wp[0], w1 = wp[1];
+                const uint32_t w2 = sh ? wp[2] : 0u;
+                m.w[q][0] = __builtin_amdgcn_alignbyte(w1, w0, sh);
+                m.w[q][1] = __builtin_amdgcn_alignbyte(w2, w1, sh);
             } else {
                 for (int i = 0; i < 8 && j + i < n; ++i) m.w[q][i >> 2] |= (uint32_t)mp[i] << (8 * (i & 3));
             }
@@ -402,10 +410,12 @@ __global__ __launch_bounds__(256 * TEAMS, D <= 128 ? 2 : 1) void prefill_kernel(
     sc.cc = ttid % CPR;
     const int kg0 = ttid / CPR;
     const bool stager = kg0 < 16;
-    // A sequence of one row tile has its keys read by this workgroup alone
-    // (all query heads of the KV head are packed here): stream them past the
-    // caches.  Longer sequences keep them cached for their other row tiles.
-    sc.stream = qn <= R;
+    // A sequence of one row tile whose KV head's query heads are all packed
+    // here (G = HP) has its keys read by this workgroup alone: stream them
+    // past the caches.  Otherwise other workgroups (the sequence's other row
+    // tiles, or the KV head's other head groups) read the same keys, which
+    // stay cached for them.
+    sc.stream = qn <= R && p.G == HP;
     sc.pages = pages;
     const int64_t seq_base = PAGED ? 0 : (int64_t)b * p.k_sb;   // contiguous: the sequence's K/V
     sc.kbase = p.k + seq_base + (int64_t)g * p.s_head + sc.cc * 8;
@@ -574,8 +584,8 @@ __global__ __launch_bounds__(256 * TEAMS, D <= 128 ? 2 : 1) void prefill_kernel(
         sc.c1 = c1;
         __syncthreads();   // the previous chunk is done with the slice and the buffers
         if constexpr (PAGED) {
-            sc.first_pg = (int)udiv_magic((uint32_t)c0, p.ps_magic);
-            const int npg = (int)udiv_magic((uint32_t)(c1 - 1), p.ps_magic) - sc.first_pg + 1;
+            sc.first_pg = (int)divu32((uint32_t)c0, p.ps_div);
+            const int npg = (int)divu32((uint32_t)(c1 - 1), p.ps_div) - sc.first_pg + 1;
             for (int i = tid; i < npg; i += NT) pages[i] = bt_row[sc.first_pg + i];
         }
         __syncthreads();
@@ -657,8 +667,9 @@ __global__ __launch_bounds__(256 * TEAMS, D <= 128 ? 2 : 1) void prefill_kernel(
                 *reinterpret_cast<float4 *>(op + 16 * m) =
                     make_float4(oacc[rb][m][0], oacc[rb][m][1], oacc[rb][m][2], oacc[rb][m][3]);
             if (lq == 0)
-                *reinterpret_cast<float2 *>(p.ml_part + pr * 2) =
-                    make_float2(m_ref[rb] == -INFINITY ? -INFINITY : m_ref[rb] * kLn2, lacc[rb][0]);
+                *reinterpret_cast<float2 *>(p.ml_part + pr * 2) = make_float2(
+                    m_ref[rb] == -INFINITY && !is_nan_bits(lacc[rb][0]) ? -INFINITY : partial_m(m_ref[rb], lacc[rb][0]),
+                    lacc[rb][0]);
         }
         return;
     }

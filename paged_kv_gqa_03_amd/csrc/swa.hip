@@ -135,7 +135,7 @@ __global__ __launch_bounds__(256, 2) void swa_kernel(const SwaParams p) {
             for (int i = 0; i < 16; ++i) {
                 v[i] = make_uint4(0u, 0u, 0u, 0u);
                 if (idx[i] >= 0 && idx[i] < p.slots) {
-                    const uint32_t blk = udiv_magic((uint32_t)idx[i], p.bs_magic);
+                    const uint32_t blk = divu32((uint32_t)idx[i], p.bs_div);
                     const uint32_t off = (uint32_t)idx[i] - blk * (uint32_t)p.bs;
                     v[i] = *reinterpret_cast<const uint4 *>(p.cache + (int64_t)blk * p.c_sb + (int64_t)off * p.c_ss +
                                                              ch * 16);

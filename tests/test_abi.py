@@ -135,7 +135,6 @@ def call_paged(a):
     (dict(S=1 << 20), pa.ATTN_ERR_INVALID_ARG, "num_splits"),
     (dict(S=4), pa.ATTN_ERR_WORKSPACE, "workspace"),
     (dict(S=4, ws=FAKE + 16, ws_bytes=1 << 30), pa.ATTN_ERR_INVALID_ARG, "aligned"),
-    (dict(ps=1 << 20, max_len=1 << 13), pa.ATTN_ERR_UNSUPPORTED, "2^32"),
     (dict(B=1 << 20, max_len=1 << 12, q_sb=256), pa.ATTN_ERR_UNSUPPORTED, "2^31"),
 ])
 def test_paged_decode_rejects_bad_arguments(over, code, word):
@@ -199,7 +198,7 @@ def test_prefill_workspace_bytes_layout():
 def call_paged_prefill_split(S, ws=None, ws_bytes=0, total_q=40):
     # 2 sequences, Hq=8, Hkv=2, D=128, page size 16, fake device addresses
     return pa.lib().attn_paged_prefill_split(
-        FAKE, 8 * 128, 128, FAKE, FAKE, FAKE, 2, FAKE, FAKE, 16 * 2 * 128, 2 * 128, 128, FAKE, 64, FAKE, None,
+        FAKE, 8 * 128, 128, FAKE, FAKE, FAKE, 2, 32, FAKE, FAKE, 16 * 2 * 128, 2 * 128, 128, FAKE, 64, FAKE, None,
         None, 0, 0, 0, FAKE, 8 * 128, 128, 2, 8, 2, 128, 16, 0.088, total_q, S, ws, ws_bytes, None)
 
 
@@ -330,7 +329,7 @@ def test_rotary_rejects_bad_arguments():
 
 
 def paged_prefill_args(**over):
-    a = dict(q=FAKE, q_st=8 * 128, q_sh=128, indptr=FAKE, t2b=FAKE, t2i=FAKE, nt=2, k=FAKE, v=FAKE,
+    a = dict(q=FAKE, q_st=8 * 128, q_sh=128, indptr=FAKE, t2b=FAKE, t2i=FAKE, nt=2, tr=32, k=FAKE, v=FAKE,
              s_page=16 * 2 * 128, s_slot=2 * 128, s_head=128, bt=FAKE, bt_sb=64, lens=FAKE, causal=None,
              mask=None, ndim=0, m_sb=0, m_sq=0, o=FAKE, o_st=8 * 128, o_sh=128, B=2, Hq=8, Hkv=2, D=128,
              ps=16, scale=0.088)
@@ -340,7 +339,7 @@ def paged_prefill_args(**over):
 
 def call_paged_prefill(a):
     return pa.lib().attn_paged_prefill(
-        a["q"], a["q_st"], a["q_sh"], a["indptr"], a["t2b"], a["t2i"], a["nt"], a["k"], a["v"], a["s_page"],
+        a["q"], a["q_st"], a["q_sh"], a["indptr"], a["t2b"], a["t2i"], a["nt"], a["tr"], a["k"], a["v"], a["s_page"],
         a["s_slot"], a["s_head"], a["bt"], a["bt_sb"], a["lens"], a["causal"], a["mask"], a["ndim"], a["m_sb"],
         a["m_sq"], a["o"], a["o_st"], a["o_sh"], a["B"], a["Hq"], a["Hkv"], a["D"], a["ps"], a["scale"], None)
 
@@ -354,15 +353,34 @@ def call_paged_prefill(a):
     (dict(lens=None), pa.ATTN_ERR_INVALID_ARG, "null"),
     (dict(scale=float("nan")), pa.ATTN_ERR_INVALID_ARG, "scale"),
     (dict(mask=FAKE, ndim=4), pa.ATTN_ERR_INVALID_ARG, "mask_ndim"),
-    (dict(mask=FAKE + 2, ndim=2, m_sb=64), pa.ATTN_ERR_UNSUPPORTED, "4-byte"),
-    (dict(mask=FAKE, ndim=3, m_sb=4096, m_sq=30), pa.ATTN_ERR_UNSUPPORTED, "4-byte"),
+    (dict(mask=FAKE, ndim=3, m_sb=4096, m_sq=-30), pa.ATTN_ERR_INVALID_ARG, "negative mask"),
     (dict(q=FAKE + 8), pa.ATTN_ERR_UNSUPPORTED, "aligned"),
     (dict(o_sh=130), pa.ATTN_ERR_UNSUPPORTED, "aligned"),
     (dict(s_page=1 << 33), pa.ATTN_ERR_UNSUPPORTED, "32-bit"),
+    (dict(tr=0), pa.ATTN_ERR_INVALID_ARG, "tile_rows"),
+    (dict(tr=128), pa.ATTN_ERR_INVALID_ARG, "tile_rows"),
 ])
 def test_paged_prefill_rejects_bad_arguments(over, code, word):
     assert call_paged_prefill(paged_prefill_args(**over)) == code
     assert word in pa.attn_last_error()
+
+
+def test_paged_prefill_refuses_the_worked_examples_64_row_map():
+    """The doc's worked work map (q lens [70, 10, 130] in 64-row tiles) at
+    G = 4, D = 128, where the kernel computes 32-row tiles: the map's height
+    is refused instead of leaving rows 32..63 of every tile unwritten."""
+    ex = json.load(open(os.path.join(GOLDEN, "ragged_work_map.json")))
+    assert ex["tile_rows"] == 64 and pa.attn_prefill_tile_rows(128, 4) == 32
+    _, t2b, _ = pa.attn_prefill_plan(ex["q_lens"], ex["tile_rows"])
+    a = paged_prefill_args(B=3, nt=int(t2b.numel()), tr=ex["tile_rows"], Hq=8, Hkv=2, D=128)
+    assert call_paged_prefill(a) == pa.ATTN_ERR_INVALID_ARG
+    assert "tile_rows=64" in pa.attn_last_error() and "takes 32" in pa.attn_last_error()
+    # the split entry point checks the same contract
+    assert pa.lib().attn_paged_prefill_split(
+        FAKE, 8 * 128, 128, FAKE, FAKE, FAKE, int(t2b.numel()), 64, FAKE, FAKE, 16 * 2 * 128, 2 * 128, 128, FAKE,
+        64, FAKE, None, None, 0, 0, 0, FAKE, 8 * 128, 128, 3, 8, 2, 128, 16, 0.088, 210, 2, FAKE, 1 << 30,
+        None) == pa.ATTN_ERR_INVALID_ARG
+    assert "tile_rows" in pa.attn_last_error()
 
 
 def test_dense_prefill_rejects_bad_arguments():

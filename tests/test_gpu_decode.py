@@ -83,25 +83,108 @@ def test_paged_decode_page_head_slot_layout():
     assert_close(run_paged(case, 0), ref)
 
 
-def test_serving_paged_decode_b32():
-    case = workloads.serving_paged_decode(32, device=DEV)
+@pytest.mark.parametrize("B", [32, 128])
+def test_serving_paged_decode(B):
+    """Config 3 at B = 32 and at B = 128 (the timed configuration, planner
+    split count), every sequence and head against the oracle.  Besides the
+    1e-2 pass bar, a secondary absolute bar of 2e-3: outputs average up to
+    4096 values and are ~0.02 in size, where 1e-2 alone would hide a
+    mis-weighted piece."""
+    case = workloads.serving_paged_decode(B, device=DEV)
     out = run_paged(case, 0)
     cpu = {k: (v.cpu() if torch.is_tensor(v) else v) for k, v in case.items()}
     ref, _ = oracle_paged(cpu)
-    assert_close(out, ref, what="B=32 serving")
+    assert_close(out, ref, what="B=%d serving" % B)
+    assert_close(out, ref, atol=2e-3, what="B=%d serving, secondary bar" % B)
 
 
-def test_serving_paged_decode_b128_sampled_sequences():
-    """B=128 in the timed launch configuration; the oracle checks every 8th
-    sequence (a batch slice is an exact sub-problem)."""
-    case = workloads.serving_paged_decode(128, device=DEV)
-    out = run_paged(case, 0).cpu()
-    idx = torch.arange(0, 128, 8)
-    sub = dict(q=case["q"][idx].cpu(), k_pool=case["k_pool"].cpu(), v_pool=case["v_pool"].cpu(),
-               block_table=case["block_table"][idx].cpu(), kv_lens=case["kv_lens"][idx].cpu(),
-               scale=case["scale"])
-    ref, _ = oracle_paged(sub)
-    assert_close(out[idx], ref, what="B=128 sampled")
+def partition_bounds(lens, rows_per_seq, W):
+    """Per row: (slot, first key, end key) of each piece under the balanced
+    partition (rows laid end to end, W equal slices of the line, the piece of
+    row r in slice w at slot r + w)."""
+    n_rows = [n for n in lens for _ in range(rows_per_seq)]
+    T = sum(n_rows)
+    bounds = [w * T // W for w in range(W + 1)]
+    out, P = [], 0
+    for r, n in enumerate(n_rows):
+        pieces = []
+        for w in range(W):
+            lo, hi = max(bounds[w], P), min(bounds[w + 1], P + n)
+            if lo < hi:
+                pieces.append((r + w, lo - P, hi - P))
+        out.append(pieces)
+        P += n
+    return out
+
+
+@pytest.mark.parametrize("B,Hkv,G,layout,W", [
+    (32, 8, 4, "page_slot_head", 0),     # config 3 B = 32, planner slices: eight KV heads per row
+    (5, 2, 4, "page_head_slot", 23),     # one KV head per row
+])
+def test_split_pieces_match_oracle_partials(B, Hkv, G, layout, W):
+    """Each piece the split kernel leaves in the workspace (read through the
+    documented slot layout) against the oracle's fp64 partial over the same
+    key range: lse = m + ln l and o / l per piece (m is a lazily raised
+    reference, so only these two are unique)."""
+    Hq, D = Hkv * G, 128
+    if B == 32:
+        case = workloads.serving_paged_decode(32)
+    else:
+        case = workloads.paged_decode_case(120, B, Hq, Hkv, D, [1, 700, 0, 2500, 65], 16, layout=layout)
+    lens = case["kv_lens"].tolist()
+    hw = Hkv if layout == "page_slot_head" else 1
+    W = W or pa.attn_plan_splits(B, Hkv, G, D, case["max_kv_len"], 16, case["k_pool"].stride(2))
+    d = to_dev(case, ["q", "k_pool", "v_pool", "block_table", "kv_lens"])
+    nbytes = pa.attn_decode_workspace_bytes(B, Hq, D, W)
+    ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device=DEV)
+    pa.attn_paged_decode_split(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["kv_lens"],
+                               case["max_kv_len"], 16, case["scale"], W, ws)
+    torch.cuda.synchronize()
+    rows_total = (B + W) * Hq
+    o_bytes = rows_total * D * 4
+    ml_off = (o_bytes + 255) // 256 * 256
+    o_all = ws[:o_bytes].view(torch.float32).view(rows_total, D).cpu().double()
+    ml_all = ws[ml_off:ml_off + rows_total * 8].view(torch.float32).view(rows_total, 2).cpu().double()
+    ngrp = Hkv // hw
+    heads_per_row = hw * G
+    pieces = partition_bounds(lens, ngrp, W)
+    S = max(1, max(len(p) for p in pieces))
+    # oracle partials: per sequence and row group the same chunk bounds; rows
+    # of one sequence share its keys, so one bounds row per (sequence, group)
+    # is evaluated as its own oracle call on that group's heads
+    n_checked = 0
+    for grp in range(ngrp):
+        bnd = torch.zeros(B, S + 1, dtype=torch.int32)
+        for b in range(B):
+            ps_ = pieces[b * ngrp + grp]
+            edges = [0] + [hi for _, _, hi in ps_]
+            edges = edges + [edges[-1]] * (S + 1 - len(edges))
+            bnd[b] = torch.tensor(edges, dtype=torch.int32)
+        o_ref, m_ref, l_ref = oracle.paged_decode_partials(case["q"], case["k_pool"], case["v_pool"],
+                                                           case["block_table"], case["kv_lens"], bnd, case["scale"])
+        for b in range(B):
+            for s_i, (slot, lo, hi) in enumerate(pieces[b * ngrp + grp]):
+                h0 = grp * heads_per_row
+                rows = slice(slot * heads_per_row, (slot + 1) * heads_per_row)
+                m_g, l_g, o_g = ml_all[rows, 0], ml_all[rows, 1], o_all[rows]
+                lse_g = m_g + torch.log(l_g)
+                mr, lr, orf = (m_ref[s_i, b, h0:h0 + heads_per_row], l_ref[s_i, b, h0:h0 + heads_per_row],
+                               o_ref[s_i, b, h0:h0 + heads_per_row])
+                lse_r = mr + torch.log(lr)
+                what = "b=%d grp=%d piece %d [%d, %d)" % (b, grp, s_i, lo, hi)
+                # The kernel rounds each weight exp(s - m) to bf16 (unit
+                # roundoff 2^-8) and sums the rounded weights into l, so lse
+                # is within ln(1 + 2^-8) < 2^-8 of the exact value; o / l is
+                # a convex combination of V rows with weights perturbed by
+                # <= 2^-8, within the 1e-2 pass bar, and pieces of >= 64
+                # keys (where the perturbations average out) also within
+                # the secondary 2e-3 bar.
+                assert_close(lse_g, lse_r, atol=2.0 ** -8, rtol=0, what=what + " lse")
+                assert_close(o_g / l_g[:, None], orf / lr[:, None], what=what + " o / l")
+                if hi - lo >= 64:
+                    assert_close(o_g / l_g[:, None], orf / lr[:, None], atol=2e-3, what=what + " o / l, 2e-3")
+                n_checked += 1
+    assert n_checked >= B * ngrp
 
 
 @pytest.mark.parametrize("layout", ["bhld", "blhd"])
@@ -115,6 +198,7 @@ def test_contiguous_decode(layout):
     torch.cuda.synchronize()
     ref, _ = oracle.decode(case["q"].cpu(), case["k"].cpu(), case["v"].cpu(), case["scale"])
     assert_close(out, ref, what="contiguous " + layout)
+    assert_close(out, ref, atol=2e-3, what="contiguous %s, secondary bar" % layout)
 
 
 @pytest.mark.parametrize("S", [1, 3])

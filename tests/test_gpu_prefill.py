@@ -33,7 +33,7 @@ def run_prefill(case, causal=True):
     out = torch.full_like(d["q"], float("nan"))
     pa.attn_paged_prefill(d["q"], d["qo_indptr"], t2b.to(DEV), t2i.to(DEV), d["k_pool"], d["v_pool"],
                           d["block_table"], d["kv_lens"], out, case["page_size"], case["scale"],
-                          causal_offset=d["causal_offset"] if causal else None, mask=mask)
+                          causal_offset=d["causal_offset"] if causal else None, mask=mask, tile_rows=R)
     torch.cuda.synchronize()
     return out
 
@@ -47,8 +47,13 @@ def oracle_prefill(case, causal=True):
 
 @pytest.mark.parametrize("masked", [False, True])
 def test_ragged_prefill_config(masked):
+    """Config 4 at full size, every row and head.  Besides the 1e-2 pass bar,
+    a secondary absolute bar of 2e-3: outputs average up to 2560 values and
+    are ~0.02-0.05 in size, where 1e-2 alone would be loose."""
     case = workloads.ragged_prefill(masked=masked)
-    assert_close(run_prefill(case), oracle_prefill(case), what="ragged prefill masked=%s" % masked)
+    out, ref = run_prefill(case), oracle_prefill(case)
+    assert_close(out, ref, what="ragged prefill masked=%s" % masked)
+    assert_close(out, ref, atol=2e-3, what="ragged prefill masked=%s, secondary bar" % masked)
 
 
 @pytest.mark.parametrize("G", [1, 2, 4, 8])
@@ -210,7 +215,7 @@ def test_decode_with_2d_mask_via_paged_prefill():
     out = torch.full((B, 32, 128), float("nan"), dtype=torch.bfloat16, device=DEV)
     pa.attn_paged_prefill(case["q"].to(DEV), indptr.to(DEV), t2b.to(DEV), t2i.to(DEV), case["k_pool"].to(DEV),
                           case["v_pool"].to(DEV), case["block_table"].to(DEV), case["kv_lens"].to(DEV), out, 16,
-                          case["scale"], causal_offset=None, mask=mask.to(DEV))
+                          case["scale"], causal_offset=None, mask=mask.to(DEV), tile_rows=R)
     torch.cuda.synchronize()
     assert torch.equal(out[4].cpu(), torch.zeros(32, 128, dtype=torch.bfloat16))
     assert_close(out, ref, what="masked decode")
@@ -263,7 +268,7 @@ def run_prefill_split(case, S, causal=True):
                                 d["block_table"], d["kv_lens"], out, case["page_size"], case["scale"],
                                 max(case["kv_lens"].tolist() + [0]),
                                 causal_offset=d["causal_offset"] if causal else None, mask=mask,
-                                num_splits=S, workspace=ws)
+                                num_splits=S, workspace=ws, tile_rows=R)
     torch.cuda.synchronize()
     return out
 
@@ -333,11 +338,11 @@ def test_dense_split_prefill_matches_oracle(B, Lq, Lk, G, layout, S, ndim):
 def test_split_prefill_short_q_long_kv_workload():
     """G = 8, 16 sequences of 16 new rows after 16368 cached keys (Hq = 32,
     Hkv = 4, D = 128, page size 16), planner-chosen splits, in the launch
-    configuration the benchmark times.  At this size the split result is
-    checked against the unsplit kernel everywhere (same math, other
-    summation order) and against the oracle on four whole sequences.  The
-    outputs average 16384 values (~0.01 in size), so the absolute bar is
-    1e-3."""
+    configuration the benchmark times.  Every row of all 16 sequences is
+    checked against the oracle, for the split and the unsplit kernel, at
+    the 1e-2 bar and at a secondary absolute bar of 1e-3: the outputs
+    average 16384 values (~0.01 in size), so 1e-2 alone would hide a
+    mis-weighted split piece."""
     case = workloads.short_q_prefill(device=DEV)
     G = case["Hq"] // case["Hkv"]
     R = pa.attn_prefill_tile_rows(128, G)
@@ -349,21 +354,18 @@ def test_split_prefill_short_q_long_kv_workload():
     assert S > 1
     out_s = torch.full_like(case["q"], float("nan"))
     pa.attn_paged_prefill_split(*args, out_s, 16, case["scale"], max(case["kv_lens"].tolist()),
-                                causal_offset=case["causal_offset"], num_splits=S)
+                                causal_offset=case["causal_offset"], num_splits=S, tile_rows=R)
     out_1 = torch.full_like(case["q"], float("nan"))
-    pa.attn_paged_prefill(*args, out_1, 16, case["scale"], causal_offset=case["causal_offset"])
+    pa.attn_paged_prefill(*args, out_1, 16, case["scale"], causal_offset=case["causal_offset"], tile_rows=R)
     torch.cuda.synchronize()
-    assert_close(out_s, out_1.double().cpu(), atol=1e-3, what="split vs unsplit")
-    # oracle on four sequences: the same pools through their own table rows
+    # every row of every sequence against the oracle, split and unsplit
     cpu = {k: case[k].cpu() for k in ("q", "k_pool", "v_pool", "block_table", "kv_lens", "causal_offset",
                                      "qo_indptr")}
-    for b in (0, 5, 11, 15):
-        r0, r1 = int(cpu["qo_indptr"][b]), int(cpu["qo_indptr"][b + 1])
-        ref, _ = oracle.paged_prefill(cpu["q"][r0:r1], torch.tensor([0, r1 - r0], dtype=torch.int32),
-                                      cpu["k_pool"], cpu["v_pool"], cpu["block_table"][b:b + 1],
-                                      cpu["kv_lens"][b:b + 1], case["scale"],
-                                      causal_offset=cpu["causal_offset"][b:b + 1], mask=None)
-        assert_close(out_s[r0:r1], ref, atol=1e-3, what="sequence %d vs oracle" % b)
+    ref, _ = oracle.paged_prefill(cpu["q"], cpu["qo_indptr"], cpu["k_pool"], cpu["v_pool"], cpu["block_table"],
+                                  cpu["kv_lens"], case["scale"], causal_offset=cpu["causal_offset"], mask=None)
+    for label, out in (("split S=%d" % S, out_s), ("unsplit", out_1)):
+        assert_close(out, ref, what=label + " vs oracle")
+        assert_close(out, ref, atol=1e-3, rtol=1e-2, what=label + " vs oracle, secondary bar")
 
 
 # ------------------------------------------ group sizes beyond 1, 2, 4, 8

@@ -92,7 +92,7 @@ def test_random_paged_prefill(seed):
         pa.attn_paged_prefill_split(d["q"], d["qo_indptr"], t2b.to(DEV), t2i.to(DEV), d["k_pool"], d["v_pool"],
                                     d["block_table"], d["kv_lens"], out, ps, case["scale"],
                                     max(case["kv_lens"].tolist()), causal_offset=d["causal_offset"], mask=mask,
-                                    num_splits=S)
+                                    num_splits=S, tile_rows=R)
     torch.cuda.synchronize()
     ref, _ = oracle.paged_prefill(case["q"], case["qo_indptr"], case["k_pool"], case["v_pool"], case["block_table"],
                                   case["kv_lens"], case["scale"], causal_offset=case["causal_offset"],

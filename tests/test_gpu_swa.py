@@ -37,8 +37,32 @@ def oracle_swa(case):
 
 
 def test_swa_config():
+    """Config 5 at full size against the 1e-2 pass bar, and a secondary bar
+    derived from the arithmetic.  The kernel rounds each weight p_j * inv_j
+    to bf16 (unit roundoff u = 2^-8) for the P.X product, multiplies the
+    exactly converted codes, normalises by the fp32 sum of the unrounded
+    p_j, and rounds the output to bf16: an output is off by at most
+    u * sum_j w_j |x_j| + u * |out| <= u * (max_j |x_j| + |out|) (per token,
+    over its admitted rows), plus fp32 rounding.  Outputs here are O(0.1-1)
+    (windows of 1-128 rows of ~N(0, 1) values), so a fixed 2e-3 does not
+    fit.  The mean error is also held below u * mean |out|: the weight
+    perturbations have either sign and average out over a window, so a
+    mis-weighted tile or row would show there."""
     case = workloads.swa_fp8()
-    assert_close(run_swa(case), oracle_swa(case), what="swa fp8 config")
+    out, ref = run_swa(case), oracle_swa(case)
+    assert_close(out, ref, what="swa fp8 config")
+    T, W = case["indices"].shape
+    slots = case["indices"].clamp(min=0)
+    bs = case["block_size"]
+    codes = case["cache"][slots // bs, slots % bs]                       # [T, W, HD]
+    x = codes.view(torch.float8_e4m3fn).double() * case["inv_scale"].double()[slots]
+    admitted = (torch.arange(W)[None, :] < case["lens"][:, None]) & (case["indices"] >= 0)
+    xmax = (x.abs().amax(dim=2) * admitted).amax(dim=1)                 # [T]
+    u = 2.0 ** -8
+    bound = u * (xmax[:, None, None] + ref.abs()) + 1e-5
+    err = (out.cpu().double() - ref).abs()
+    assert bool((err <= bound).all()), "derived bound exceeded by %d elements" % int((err > bound).sum())
+    assert float(err.mean()) <= u * float(ref.abs().mean()), (float(err.mean()), float(ref.abs().mean()))
 
 
 @pytest.mark.parametrize("W,lens,neg", [

@@ -99,12 +99,13 @@ def contig_decode_case(seed, B, Hq, Hkv, D, kv_len, device="cpu", layout="bhld",
 
 def prefill_case(seed, B, Hq, Hkv, D, ctx_range, q_range, page_size, mask_frac=None,
                  mask_ndim=3, causal=True, device="cpu", q_lens=None, ctx_lens=None,
-                 pool_factor=1.5):
+                 pool_factor=1.5, mask_pad=4):
     """Ragged paged prefill inputs: prior context c_b ~ U[ctx_range], new rows
     q_b ~ U[q_range]; the new tokens' K/V are already in the cache, so the
     sequence holds n_b = c_b + q_b keys and causal_offset[b] = c_b.  With
     mask_frac, a keep-mask (True = keep) drops that fraction of entries at
-    random: 3-D [B, max_q, max_n] or 2-D [B, max_n]."""
+    random: 3-D [B, max_q, max_n] or 2-D [B, max_n], its key dimension padded
+    to a multiple of mask_pad (1: no padding)."""
     g = _gen(seed, device)
     if ctx_lens is None:
         ctx_lens = _randint(ctx_range[0], ctx_range[1], B, g, device).tolist()
@@ -121,9 +122,9 @@ def prefill_case(seed, B, Hq, Hkv, D, ctx_range, q_range, page_size, mask_frac=N
     qo_indptr = torch.tensor([0] + list(_cumsum(q_lens)), dtype=torch.int32, device=device)
     mask = None
     if mask_frac is not None:
-        # key dimension padded to a multiple of 4 (mask rows 4-byte aligned);
-        # entries past a sequence's keys are never read
-        max_n = (max(max(kv_lens) if kv_lens else 1, 1) + 3) // 4 * 4
+        # key dimension padded to a multiple of mask_pad; entries past a
+        # sequence's keys are never used
+        max_n = (max(max(kv_lens) if kv_lens else 1, 1) + mask_pad - 1) // mask_pad * mask_pad
         max_q = max(q_lens) if q_lens else 1
         shape = (B, max_q, max_n) if mask_ndim == 3 else (B, max_n)
         mask = torch.rand(*shape, generator=g, device=device) >= mask_frac
