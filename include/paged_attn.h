@@ -169,6 +169,35 @@ int attn_paged_decode(const void *q, int64_t q_sb, int64_t q_sh,
                       void *stream);
 
 /*
+ * attn_paged_decode for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments and results as attn_paged_decode without the
+ * workspace: the split partials go to a static device buffer of
+ * ATTN_NOALLOC_SCRATCH_BYTES (32 MiB) inside the library, one copy per
+ * device, held until the process ends; the call itself allocates nothing
+ * (no hipMalloc, no allocating library routine).  Its device address is
+ * looked up once per device, on the first call with that device current.
+ *   num_splits  0 = the planner's count, lowered if needed to the largest
+ *               whose partials fit the buffer (attn_decode_workspace_bytes
+ *               <= ATTN_NOALLOC_SCRATCH_BYTES; one slice needs none); an
+ *               explicit count whose partials do not fit returns
+ *               ATTN_ERR_UNSUPPORTED.
+ * The buffer keeps the last call's contents; nothing in it needs to start
+ * at zero (the split kernel writes every slot the combine reads).  Calls
+ * that overlap in time on one device (several streams or threads) share
+ * the buffer and race: serialise them.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int attn_paged_decode_noalloc(const void *q, int64_t q_sb, int64_t q_sh,
+                              const void *k_pool, const void *v_pool,
+                              int64_t kv_s_page, int64_t kv_s_slot, int64_t kv_s_head,
+                              const int32_t *block_table, int64_t bt_sb,
+                              const int32_t *kv_lens, int max_kv_len,
+                              void *o, int64_t o_sb, int64_t o_sh,
+                              int B, int Hq, int Hkv, int D, int page_size, float scale,
+                              int num_splits, void *stream);
+
+/*
  * The two halves of attn_paged_decode, for callers that schedule them
  * separately (e.g. to time each kernel).  attn_paged_decode_split takes the
  * arguments of attn_paged_decode minus the output and writes every piece as

@@ -14,6 +14,7 @@ import torch
 __all__ = [
     "AttnError", "lib", "attn_version", "attn_last_error", "attn_plan_splits",
     "attn_decode_workspace_bytes", "attn_decode", "attn_paged_decode", "attn_paged_decode_split",
+    "attn_paged_decode_noalloc", "NOALLOC_SCRATCH_BYTES",
     "attn_decode_combine", "attn_split_combine",
     "attn_prefill_plan", "attn_prefill_tile_rows", "attn_paged_prefill", "attn_swa_fp8_decode",
     "attn_prefill", "attn_paged_kv_append", "attn_swa_fp8_append", "attn_rotary_embed",
@@ -40,6 +41,8 @@ _SIGS = {
                      _I, _I, _I, _I, _F, _I, _P, _Z, _P], _I),
     "attn_paged_decode": ([_P, _L, _L, _P, _P, _L, _L, _L, _P, _L, _P, _I, _P, _L, _L,
                            _I, _I, _I, _I, _I, _F, _I, _P, _Z, _P], _I),
+    "attn_paged_decode_noalloc": ([_P, _L, _L, _P, _P, _L, _L, _L, _P, _L, _P, _I, _P, _L, _L,
+                                   _I, _I, _I, _I, _I, _F, _I, _P], _I),
     "attn_paged_decode_split": ([_P, _L, _L, _P, _P, _L, _L, _L, _P, _L, _P, _I,
                                  _I, _I, _I, _I, _I, _F, _I, _P, _Z, _P], _I),
     "attn_decode_combine": ([_P, _Z, _I, _I, _I, _I, _I, _L, _P, _I, _P, _L, _L, _P], _I),
@@ -181,6 +184,28 @@ def attn_paged_decode(q, k_pool, v_pool, block_table, kv_lens, max_kv_len, out, 
         _ptr(block_table), block_table.stride(0), _ptr(kv_lens), int(max_kv_len),
         _ptr(out), out.stride(0), out.stride(1), B, Hq, Hkv, D, int(page_size), float(scale),
         int(S), _ptr(ws), nbytes, _stream(stream)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20   # ATTN_NOALLOC_SCRATCH_BYTES
+
+
+def attn_paged_decode_noalloc(q, k_pool, v_pool, block_table, kv_lens, max_kv_len, out, page_size, scale,
+                              num_splits=0, stream=None):
+    """attn_paged_decode with the split partials in the library's static
+    per-device scratch buffer: nothing is allocated (no workspace tensor)."""
+    _dev(q=(q, _BF16), k_pool=(k_pool, _BF16), v_pool=(v_pool, _BF16), block_table=(block_table, _I32),
+         kv_lens=(kv_lens, _I32), out=(out, _BF16))
+    _unit_inner(q, k_pool, v_pool, out, block_table)
+    assert k_pool.stride() == v_pool.stride(), "K and V pools must share strides"
+    B, Hq, D = q.shape
+    Hkv = k_pool.shape[2]
+    _check(lib().attn_paged_decode_noalloc(
+        _ptr(q), q.stride(0), q.stride(1), _ptr(k_pool), _ptr(v_pool),
+        k_pool.stride(0), k_pool.stride(1), k_pool.stride(2),
+        _ptr(block_table), block_table.stride(0), _ptr(kv_lens), int(max_kv_len),
+        _ptr(out), out.stride(0), out.stride(1), B, Hq, Hkv, D, int(page_size), float(scale),
+        int(num_splits), _stream(stream)))
     return out
 
 

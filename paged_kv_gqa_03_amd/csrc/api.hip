@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "kernels.hpp"
@@ -168,6 +169,38 @@ pa::DecodeCombineParams combine_params(const void *workspace, int B, int Hq, int
     c.o_sb = o_sb;
     c.o_sh = o_sh;
     return c;
+}
+
+// Decode workspace of attn_paged_decode_noalloc: a static device array, one
+// copy per device, held until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is a stand-in, not a device
+// address): it looks up each device's address once with hipGetSymbolAddress
+// and passes that.
+static __device__ __align__(256) unsigned char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+// Address of this device's copy of `scratch` (looked up on the first call on
+// the device, with the device current), or nullptr with *rc set.
+void *scratch_address(int *rc) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return *rc = fail(ATTN_ERR_LAUNCH, "attn_paged_decode_noalloc: no current HIP device"), nullptr;
+    if (dev >= kMaxDevices)
+        return *rc = fail(ATTN_ERR_UNSUPPORTED, "attn_paged_decode_noalloc: device %d beyond %d", dev, kMaxDevices),
+               nullptr;
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return *rc = fail(ATTN_ERR_LAUNCH, "attn_paged_decode_noalloc: hipGetSymbolAddress: %s",
+                              hipGetErrorString(e)), nullptr;
+        addr[dev] = ptr;
+    }
+    return addr[dev];
 }
 
 // Shared tail of the decode entry points: partition, workspace, launches.
@@ -344,6 +377,48 @@ int attn_paged_decode(const void *q, int64_t q_sb, int64_t q_sh,
     return paged_decode_impl(q, q_sb, q_sh, k_pool, v_pool, kv_s_page, kv_s_slot, kv_s_head, block_table,
                              bt_sb, kv_lens, max_kv_len, o, o_sb, o_sh, B, Hq, Hkv, D, page_size, scale,
                              num_splits, workspace, workspace_bytes, stream, 0);
+}
+
+int attn_paged_decode_noalloc(const void *q, int64_t q_sb, int64_t q_sh,
+                              const void *k_pool, const void *v_pool,
+                              int64_t kv_s_page, int64_t kv_s_slot, int64_t kv_s_head,
+                              const int32_t *block_table, int64_t bt_sb,
+                              const int32_t *kv_lens, int max_kv_len,
+                              void *o, int64_t o_sb, int64_t o_sh,
+                              int B, int Hq, int Hkv, int D, int page_size, float scale,
+                              int num_splits, void *stream) {
+    const size_t cap = ATTN_NOALLOC_SCRATCH_BYTES;
+    int W = num_splits;
+    const bool plannable = B > 0 && Hkv > 0 && Hq > 0 && Hq % Hkv == 0 && decode_dim(D) && max_kv_len >= 0 &&
+                           page_size > 0;
+    if (W == 0 && plannable) {
+        W = attn_plan_splits(B, Hkv, Hq / Hkv, D, max_kv_len, page_size, kv_s_head, 0);
+        if (W < 0) return W;
+        // The planner's count, lowered to the largest whose partials fit the
+        // static buffer (one slice needs no workspace at all).
+        if (attn_decode_workspace_bytes(B, Hq, D, W) > cap) {
+            int lo = 1, hi = W;
+            while (lo < hi) {
+                const int mid = lo + (hi - lo + 1) / 2;
+                if (attn_decode_workspace_bytes(B, Hq, D, mid) <= cap) lo = mid;
+                else hi = mid - 1;
+            }
+            W = lo;
+        }
+    } else if (W > 1 && plannable && attn_decode_workspace_bytes(B, Hq, D, W) > cap) {
+        return fail(ATTN_ERR_UNSUPPORTED,
+                    "attn_paged_decode_noalloc: %d slices need %zu bytes of partials, above the %zu-byte static "
+                    "scratch buffer", W, attn_decode_workspace_bytes(B, Hq, D, W), cap);
+    }
+    void *ws = nullptr;
+    if (W > 1 && plannable) {
+        int rc = ATTN_OK;
+        ws = scratch_address(&rc);
+        if (!ws) return rc;
+    }
+    return paged_decode_impl(q, q_sb, q_sh, k_pool, v_pool, kv_s_page, kv_s_slot, kv_s_head, block_table, bt_sb,
+                             kv_lens, max_kv_len, o, o_sb, o_sh, B, Hq, Hkv, D, page_size, scale, W, ws,
+                             ws ? cap : 0, stream, 0);
 }
 
 int attn_paged_decode_split(const void *q, int64_t q_sb, int64_t q_sh,
