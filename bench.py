@@ -1,20 +1,23 @@
 """Benchmark of the paged GQA decode hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-cpu-baseline] [--no-extras]
+                    [--no-cpu-baseline] [--no-extras] [--counters]
 
 A step is one attn_paged_decode call (split planner, paged split-KV kernel
 and log-sum-exp combine) over one batch of the workload, with every input
 already resident in HBM.  To keep reads cold, R independent input sets are
-rotated so that more than 1 GB is touched between two uses of a set (more
+rotated so that more than 1.5 GB is touched between two uses of a set (more
 than the 256 MB Infinity Cache plus the L2s).
 
 Prints ONE JSON line: value = algorithmic HBM bytes per call / measured time
 per call (GB/s); us_per_call beside it.  "roofline" covers the split kernel
 (timed alone with HIP events on the launch stream, same split count as the
-timed calls); "traffic" comes from the committed rocprofv3 counter summary
-when its recorded kernel-source hash matches the current source, else null.
-"cpu_baseline" times the CPU oracle on a bounded sample of the same workload.
+timed calls), against the 8 TB/s specification and against a measured
+pure-read streaming probe of the same byte count (attn_hbm_read_probe);
+"traffic" comes from the committed rocprofv3 counter summary of the same
+rotated input sets when its recorded kernel-source hash matches the current
+source, else null.  "cpu_baseline" times the CPU oracle on a bounded sample
+of the same workload.
 """
 import argparse
 import hashlib
@@ -29,8 +32,20 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
-COUNTERS = os.path.join(ROOT, "profiles", "decode_split_b128_counters.json")
+PROFILES = os.path.join(ROOT, "profiles")
 DECODE_SRC = os.path.join(ROOT, "paged_kv_gqa_03_amd", "csrc", "decode.hip")
+
+# Paged decode workloads: batch, query heads, KV heads, page size, lengths
+# (None = U[512, 4096], else that length for every sequence), seed.  D = 128.
+DECODE_WORKLOADS = {
+    "paged_b128": dict(B=128, Hq=32, Hkv=8, ps=16, fixed=None, seed=1004),
+    "paged_b32": dict(B=32, Hq=32, Hkv=8, ps=16, fixed=None, seed=1003),
+    "paged_b128_kv4096": dict(B=128, Hq=32, Hkv=8, ps=16, fixed=4096, seed=1004),
+    "paged_b32_kv4096": dict(B=32, Hq=32, Hkv=8, ps=16, fixed=4096, seed=1003),
+    "paged_b32_ps1": dict(B=32, Hq=32, Hkv=8, ps=1, fixed=None, seed=1011),
+    "paged_b128_g8": dict(B=128, Hq=64, Hkv=8, ps=16, fixed=None, seed=1012),
+    "paged_b128_g32": dict(B=128, Hq=32, Hkv=1, ps=16, fixed=None, seed=1013),
+}
 
 
 def parse():
@@ -39,13 +54,14 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="paged_b128",
-                    choices=["paged_b128", "paged_b32", "paged_b128_kv4096", "paged_b32_kv4096", "contig_b16",
-                             "ragged_prefill", "ragged_prefill_masked", "swa_fp8"])
+                    choices=list(DECODE_WORKLOADS) + ["contig_b16", "ragged_prefill", "ragged_prefill_masked",
+                                                      "swa_fp8"])
     ap.add_argument("--num-splits", type=int, default=0, help="0 = planner")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--counters", action="store_true",
-                    help="untimed: 3 split-kernel launches on set 0 and 3 copies of 1 GiB, for rocprofv3 --pmc")
+                    help="untimed: one decode split-kernel launch per rotated input set (paged workloads; the "
+                         "whole call for contig_b16) and 3 copies of 1 GiB, for rocprofv3 --pmc")
     return ap.parse_args()
 
 
@@ -59,13 +75,25 @@ def decode_bytes(case):
     return kv + bt + 4 * B + 2 * B * Hq * D * 2
 
 
+def contig_bytes():
+    """Contiguous decode B=16 Hq=32 Hkv=8 D=128 kv=2048: K, V, Q and O."""
+    return 16 * 8 * 2048 * 128 * 4 + 2 * 16 * 32 * 128 * 2
+
+
 def make_sets(name, device, n_sets):
     import workloads
-    B = 128 if "b128" in name else 32
-    fixed = 4096 if "kv4096" in name else None
-    base = 1004 if B == 128 else 1003
-    return [workloads.serving_paged_decode(B, device=device, fixed_len=fixed, seed=base + 7919 * r)
+    w = DECODE_WORKLOADS[name]
+    lens = [w["fixed"]] * w["B"] if w["fixed"] else (512, 4096)
+    return [workloads.paged_decode_case(w["seed"] + 7919 * r, w["B"], w["Hq"], w["Hkv"], 128, lens, w["ps"],
+                                        device=device)
             for r in range(n_sets)]
+
+
+def workload_desc(name):
+    w = DECODE_WORKLOADS[name]
+    kv = str(w["fixed"]) if w["fixed"] else "U[512,4096]"
+    return ("paged GQA decode B=%d Hq=%d Hkv=%d D=128 page_size=%d kv_lens %s"
+            % (w["B"], w["Hq"], w["Hkv"], w["ps"], kv))
 
 
 def rotation_count(bytes_per_call):
@@ -78,18 +106,24 @@ def source_hash(path):
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def load_traffic():
-    """HBM bytes (read + write) of one split-kernel launch of this workload,
-    from the committed rocprofv3 counter summary (calibrated FETCH_SIZE +
-    WRITE_SIZE), and its read / algorithmic ratio; (None, None) when the
-    summary is absent or was taken on another kernel source."""
-    if not os.path.exists(COUNTERS):
-        return None, None
-    with open(COUNTERS) as f:
+def counters_path(workload):
+    return os.path.join(PROFILES, "decode_%s_counters.json" % workload)
+
+
+def load_traffic(workload):
+    """HBM bytes (read + write) per split-kernel launch of this workload, mean
+    over the rotated input sets, from the committed rocprofv3 counter summary
+    (calibrated FETCH_SIZE + WRITE_SIZE), with the algorithmic bytes of the
+    same launches and the read / algorithmic ratio; None when the summary is
+    absent or was taken on another kernel source."""
+    path = counters_path(workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
         c = json.load(f)
     if c.get("decode_src_sha256") != source_hash(DECODE_SRC):
-        return None, None
-    return c.get("hbm_bytes_per_launch"), c.get("read_over_algorithmic")
+        return None
+    return c
 
 
 def cpu_model():
@@ -117,6 +151,99 @@ def time_calls(torch, fn, sets, steps, warmup):
     return start.elapsed_time(end) / steps  # ms per call
 
 
+def probe_ceiling(torch, pa, dev, nbytes, steps=20):
+    """Pure-read streaming ceiling at nbytes per launch: attn_hbm_read_probe
+    over rotated buffers of nbytes (cold, as the decode inputs), one, two and
+    three workgroups per CU; the fastest is reported."""
+    nbytes = (int(nbytes) + 15) // 16 * 16
+    R = rotation_count(nbytes)
+    bufs = [torch.full((nbytes // 4,), r + 1, dtype=torch.int32, device=dev) for r in range(R)]
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    best = None
+    for k in (1, 2, 3):
+        wg = k * cus
+        sink = torch.empty(wg * 16, dtype=torch.int32, device=dev)
+        ms = time_calls(torch, lambda b: pa.attn_hbm_read_probe(b, sink, wg), bufs, steps, 4)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        if best is None or gbs > best["GB/s"]:
+            best = {"GB/s": round(gbs, 1), "us": round(ms * 1e3, 2), "workgroups": wg, "bytes": nbytes,
+                    "rotation_sets": R}
+    del bufs
+    torch.cuda.empty_cache()
+    return best
+
+
+def bench_decode(torch, pa, dev, name, steps, warmup, num_splits=0, breakdown=True, probe=True):
+    """One paged decode workload: whole calls (value), then the split kernel
+    and the combine each timed alone with HIP events on the launch stream,
+    and the streaming ceiling at the same byte count."""
+    probe_set = make_sets(name, dev, 1)
+    R = rotation_count(decode_bytes(probe_set[0]))
+    sets = probe_set + make_sets(name, dev, R)[1:]
+    for s in sets:
+        s["out"] = torch.empty_like(s["q"])
+        s["bytes"] = decode_bytes(s)
+    c0 = sets[0]
+    max_len = max(s["max_kv_len"] for s in sets)
+    S = num_splits or pa.attn_plan_splits(c0["B"], c0["Hkv"], c0["Hq"] // c0["Hkv"], c0["D"], max_len,
+                                          c0["page_size"], c0["k_pool"].stride(2))
+    ws = torch.empty(max(pa.attn_decode_workspace_bytes(c0["B"], c0["Hq"], c0["D"], S), 256), dtype=torch.uint8,
+                     device=dev)
+
+    def call(s):
+        pa.attn_paged_decode(s["q"], s["k_pool"], s["v_pool"], s["block_table"], s["kv_lens"], max_len,
+                             s["out"], s["page_size"], s["scale"], num_splits=S, workspace=ws)
+
+    torch.cuda.synchronize()
+    ms = time_calls(torch, call, sets, steps, warmup)
+    mean_bytes = sum(sets[i % R]["bytes"] for i in range(steps)) / steps
+    gbs = mean_bytes / (ms * 1e-3) / 1e9
+    res = {"us_per_call": round(ms * 1e3, 2), "GB/s": round(gbs, 1), "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4),
+           "num_splits": S, "rotation_sets": R, "algorithmic_bytes_per_call": int(mean_bytes)}
+    if breakdown:
+        # The split kernel alone (attn_paged_decode_split: same launch, every
+        # piece written as a partial) and the combine, each bracketed by
+        # events on the stream they are launched on.
+        stream = torch.cuda.current_stream()
+        n_k = max(20, steps)
+        marks = []
+        for i in range(warmup + n_k):
+            s = sets[i % R]
+            e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            e0.record(stream)
+            pa.attn_paged_decode_split(s["q"], s["k_pool"], s["v_pool"], s["block_table"], s["kv_lens"],
+                                       max_len, s["page_size"], s["scale"], S, ws)
+            e1.record(stream)
+            pa.attn_decode_combine(ws, s["B"], s["Hq"], s["Hkv"], s["D"], S, s["k_pool"].stride(2), s["kv_lens"],
+                                   max_len, s["out"])
+            e2.record(stream)
+            if i >= warmup:
+                marks.append((e0, e1, e2, s["bytes"]))
+        torch.cuda.synchronize()
+        ks = [(a.elapsed_time(b), b.elapsed_time(c), nb) for a, b, c, nb in marks]
+        per_call = sorted((k[0] + k[1]) * 1e3 for k in ks)
+
+        def pct(q):
+            return round(per_call[min(len(per_call) - 1, int(q * (len(per_call) - 1) + 0.5))], 2)
+
+        k_ms = sum(k[0] for k in ks) / len(ks)
+        res["kernel_us"] = round(k_ms * 1e3, 2)
+        res["combine_us"] = round(sum(k[1] for k in ks) / len(ks) * 1e3, 2)
+        res["kernel_bytes"] = int(sum(k[2] for k in ks) / len(ks))
+        res["kernel_GB/s"] = round(res["kernel_bytes"] / (k_ms * 1e-3) / 1e9, 1)
+        res["per_call_us"] = {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9), "calls": len(per_call),
+                              "timing": "HIP events around each call's split and combine launches"}
+    del sets
+    torch.cuda.empty_cache()
+    if probe:
+        pr = probe_ceiling(torch, pa, dev, mean_bytes)
+        res["probe"] = pr
+        res["frac_of_probe"] = round(gbs / pr["GB/s"], 4)
+        if breakdown:
+            res["kernel_frac_of_probe"] = round(res["kernel_GB/s"] / pr["GB/s"], 4)
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -129,6 +256,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.counters:
+        run_counters(torch, pa, dev, args.workload, args.num_splits)
+        return
     if args.workload == "contig_b16":
         r = bench_contiguous(torch, pa, dev, args.steps, args.warmup, args.num_splits)
         print(json.dumps({"workload": "contiguous decode B=16 Hq=32 Hkv=8 D=128 kv=2048 bhld", **r}), flush=True)
@@ -142,183 +272,145 @@ def main():
         r = bench_swa(torch, pa, dev, args.steps, args.warmup)
         print(json.dumps({"workload": "fp8 sliding-window decode T=64 NH=128 HD=512 W=128", **r}), flush=True)
         return
-    probe = make_sets(args.workload, dev, 1)
-    per_call = decode_bytes(probe[0])
-    R = rotation_count(per_call)
-    sets = probe + make_sets(args.workload, dev, R)[1:]
-    for s in sets:
-        s["out"] = torch.empty_like(s["q"])
-        s["bytes"] = decode_bytes(s)
-    c0 = sets[0]
-    max_len = max(s["max_kv_len"] for s in sets)
-    S = args.num_splits or pa.attn_plan_splits(c0["B"], c0["Hkv"], c0["Hq"] // c0["Hkv"], c0["D"], max_len,
-                                               c0["page_size"], c0["k_pool"].stride(2))
-    ws_bytes = pa.attn_decode_workspace_bytes(c0["B"], c0["Hq"], c0["D"], S)
-    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
-    if args.counters:
-        run_counters(torch, pa, c0, S, max_len, ws)
-        return
 
-    def call(s):
-        pa.attn_paged_decode(s["q"], s["k_pool"], s["v_pool"], s["block_table"], s["kv_lens"], max_len,
-                             s["out"], s["page_size"], s["scale"], num_splits=S, workspace=ws)
-
-    # --- timed region: K whole calls --------------------------------------
-    torch.cuda.synchronize()
-    ms = time_calls(torch, call, sets, args.steps, args.warmup)
-    mean_bytes = sum(sets[i % R]["bytes"] for i in range(args.steps)) / args.steps
-    gbs = mean_bytes / (ms * 1e-3) / 1e9
-
-    # --- per-kernel breakdown with HIP events on the launch stream ---------
-    # The split kernel alone (attn_paged_decode_split: same launch, every
-    # piece written as a partial) and the combine, each bracketed by events.
-    stream = torch.cuda.current_stream()
-    n_k = max(20, args.steps)
-    marks = []
-    for i in range(args.warmup + n_k):
-        s = sets[i % R]
-        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-        e0.record(stream)
-        pa.attn_paged_decode_split(s["q"], s["k_pool"], s["v_pool"], s["block_table"], s["kv_lens"],
-                                   max_len, s["page_size"], s["scale"], S, ws)
-        e1.record(stream)
-        pa.attn_decode_combine(ws, s["B"], s["Hq"], s["Hkv"], s["D"], S, s["k_pool"].stride(2), s["kv_lens"],
-                               max_len, s["out"])
-        e2.record(stream)
-        if i >= args.warmup:
-            marks.append((e0, e1, e2, s["bytes"]))
-    torch.cuda.synchronize()
-    ks = [(a.elapsed_time(b), b.elapsed_time(c), nb) for a, b, c, nb in marks]
-    # Spread of the per-call times (event pair around each call's two
-    # launches): median with p10 / p90.
-    per_call = sorted((k[0] + k[1]) * 1e3 for k in ks)
-
-    def pct(q):
-        return round(per_call[min(len(per_call) - 1, int(q * (len(per_call) - 1) + 0.5))], 2)
-
-    spread = {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9), "calls": len(per_call),
-              "timing": "HIP events around each call's split and combine launches"}
-    k_ms = sum(k[0] for k in ks) / len(ks)
-    comb = sum(k[1] for k in ks) / len(ks)
-    k_bytes = sum(k[2] for k in ks) / len(ks)
-    kernel = "decode_split_kernel<128,4,8,paged> (balanced partition, %d slices)" % S
-    achieved = k_bytes / (k_ms * 1e-3) / 1e9
-    traffic, read_ratio = load_traffic() if args.workload == "paged_b128" else (None, None)
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "traffic_read_over_algorithmic": read_ratio, "kernel": kernel,
-                "kernel_us": round(k_ms * 1e3, 2), "combine_us": round(comb * 1e3, 2),
-                "algorithmic_bytes_per_launch": int(k_bytes)}
+    # --- timed region: K whole calls, then the per-kernel breakdown ---------
+    r = bench_decode(torch, pa, dev, args.workload, args.steps, args.warmup, args.num_splits)
+    w = DECODE_WORKLOADS[args.workload]
+    G = w["Hq"] // w["Hkv"]
+    kernel = "decode_split_kernel<128,%d,%d,paged,%d> (balanced partition, %d slices)" % (
+        min(G & -G, 8), 8 if w["Hkv"] % 8 == 0 else 1, 4 if (G & -G) <= 4 else 1, r["num_splits"])
+    tr = load_traffic(args.workload)
+    roofline = {"bound": "hbm", "achieved": r["kernel_GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(r["kernel_GB/s"] / HBM_PEAK_GBS, 4),
+                "traffic": tr["hbm_bytes_per_launch"] if tr else None,
+                "traffic_algorithmic_bytes_per_launch": tr["algorithmic_bytes_per_launch"] if tr else None,
+                "traffic_read_over_algorithmic": tr["read_over_algorithmic"] if tr else None,
+                "kernel": kernel, "kernel_us": r["kernel_us"], "combine_us": r["combine_us"],
+                "algorithmic_bytes_per_launch": r["kernel_bytes"],
+                "probe_ceiling_GBs": r["probe"]["GB/s"], "frac_of_probe": r["kernel_frac_of_probe"]}
 
     # --- CPU oracle on a bounded sample -------------------------------------
     cpu = None
     if not args.no_cpu_baseline:
-        import oracle
-        host = {k: (v.cpu() if torch.is_tensor(v) else v) for k, v in c0.items()
-                if k in ("q", "k_pool", "v_pool", "block_table", "kv_lens", "scale")}
-        lens = host["kv_lens"].tolist()
-
-        def sample_bytes(m):
-            return sum(n * c0["Hkv"] * c0["D"] * 4 + (n + 15) // 16 * 4 + 4 for n in lens[:m]) \
-                + 2 * m * c0["Hq"] * c0["D"] * 2
-
-        def run_oracle(m):
-            idx = torch.arange(m)
-            t0 = time.perf_counter()
-            oracle.paged_decode(host["q"][idx], host["k_pool"], host["v_pool"], host["block_table"][idx],
-                                host["kv_lens"][idx], host["scale"])
-            return time.perf_counter() - t0
-
-        # Doubling prefixes of the batch until one takes >= 1 s or the whole
-        # batch is reached; then whole calls repeat until ~10 s are spent.
-        t_budget, m, spent = 10.0, 1, 0.0
-        while True:
-            dt = run_oracle(m)
-            spent += dt
-            if dt >= 1.0 or m == c0["B"]:
-                break
-            m = min(c0["B"], m * 2)
-        calls, tot_t = 1, dt
-        while spent < t_budget:
-            dt = run_oracle(m)
-            spent += dt
-            tot_t += dt
-            calls += 1
-        cpu = {"value": round(calls * sample_bytes(m) / tot_t / 1e9, 3), "unit": "GB/s",
-               "cores": oracle.num_threads(), "kind": "oracle",
-               "sample": "first %d of %d sequences of set 0, %d call(s), %.1f s" % (m, c0["B"], calls, tot_t),
-               "nproc": os.cpu_count(), "cpu_model": cpu_model()}
+        cpu = cpu_baseline(torch, args.workload)
 
     # --- other workloads of the path (context lines, not the headline) -----
     extras = {}
     if not args.no_extras:
         extras = run_extras(torch, pa, dev, args)
 
-    kv_desc = "4096" if "kv4096" in args.workload else "U[512,4096]"
     line = {
         "metric": "paged decode us/call + achieved HBM GB/s (% of peak) at B=32..128, kv 4K",
-        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms, 5), "us_per_call": round(ms * 1e3, 2),
-        "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4), "per_call_us": spread,
+        "value": r["GB/s"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(r["us_per_call"] / 1e3, 5), "us_per_call": r["us_per_call"],
+        "hbm_peak_frac": r["hbm_peak_frac"], "frac_of_probe": r["frac_of_probe"], "per_call_us": r["per_call_us"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) bf16, pages scattered in a 1.5x pool)",
-        "config": {"workload": "paged GQA decode B=%d Hq=32 Hkv=8 D=128 page_size=16 kv_lens %s"
-                               % (c0["B"], kv_desc),
-                   "B": c0["B"], "Hq": 32, "Hkv": 8, "D": 128, "page_size": 16, "kv_lens": kv_desc,
-                   "num_splits": S, "rotation_sets": R, "algorithmic_bytes_per_call": int(mean_bytes)},
+        "config": {"workload": workload_desc(args.workload), "B": w["B"], "Hq": w["Hq"], "Hkv": w["Hkv"], "D": 128,
+                   "page_size": w["ps"], "kv_lens": str(w["fixed"]) if w["fixed"] else "U[512,4096]",
+                   "num_splits": r["num_splits"], "rotation_sets": r["rotation_sets"],
+                   "algorithmic_bytes_per_call": r["algorithmic_bytes_per_call"]},
         "roofline": roofline,
+        "probe": r["probe"],
         "cpu_baseline": cpu,
         "extra": extras,
     }
     print(json.dumps(line), flush=True)
 
 
-def run_counters(torch, pa, c0, S, max_len, ws):
-    """Launches for hardware-counter runs: the split kernel of the timed
-    configuration, then a plain device copy of exactly 1 GiB (reads 1 GiB,
-    writes 1 GiB) that calibrates FETCH_SIZE / WRITE_SIZE."""
-    for _ in range(3):
-        pa.attn_paged_decode_split(c0["q"], c0["k_pool"], c0["v_pool"], c0["block_table"], c0["kv_lens"],
-                                   max_len, c0["page_size"], c0["scale"], S, ws)
-    torch.cuda.synchronize()
-    src = torch.empty(1 << 30, dtype=torch.uint8, device=c0["q"].device).fill_(1)
+def cpu_baseline(torch, workload):
+    """The CPU oracle (never tuned) on set 0 of the workload: doubling prefixes
+    of the batch until one takes >= 1 s or the whole batch is reached, then
+    whole calls repeated until ~10 s are spent."""
+    import oracle
+    c0 = make_sets(workload, "cpu", 1)[0]
+    lens = c0["kv_lens"].tolist()
+    ps = c0["page_size"]
+
+    def sample_bytes(m):
+        return sum(n * c0["Hkv"] * c0["D"] * 4 + (n + ps - 1) // ps * 4 + 4 for n in lens[:m]) \
+            + 2 * m * c0["Hq"] * c0["D"] * 2
+
+    def run_oracle(m):
+        idx = torch.arange(m)
+        t0 = time.perf_counter()
+        oracle.paged_decode(c0["q"][idx], c0["k_pool"], c0["v_pool"], c0["block_table"][idx], c0["kv_lens"][idx],
+                            c0["scale"])
+        return time.perf_counter() - t0
+
+    t_budget, m, spent = 10.0, 1, 0.0
+    while True:
+        dt = run_oracle(m)
+        spent += dt
+        if dt >= 1.0 or m == c0["B"]:
+            break
+        m = min(c0["B"], m * 2)
+    calls, tot_t = 1, dt
+    while spent < t_budget:
+        dt = run_oracle(m)
+        spent += dt
+        tot_t += dt
+        calls += 1
+    return {"value": round(calls * sample_bytes(m) / tot_t / 1e9, 3), "unit": "GB/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "first %d of %d sequences of set 0, %d call(s), %.1f s" % (m, c0["B"], calls, tot_t),
+            "nproc": os.cpu_count(), "cpu_model": cpu_model()}
+
+
+def run_counters(torch, pa, dev, workload, num_splits):
+    """Launches for hardware-counter runs: one decode split-kernel launch per
+    rotated input set of the workload (the whole attn_decode call for the
+    contiguous one), then a plain device copy of exactly 1 GiB, three times
+    (reads 1 GiB, writes 1 GiB), which calibrates FETCH_SIZE / WRITE_SIZE.
+    Prints the algorithmic bytes of each launch, in launch order."""
+    import workloads
+    per_launch = []
+    if workload == "contig_b16":
+        nb = contig_bytes()
+        R = rotation_count(nb)
+        for r in range(R):
+            c = workloads.contig_decode_case(1002 + 7919 * r, 16, 32, 8, 128, 2048, device=dev)
+            out = torch.empty_like(c["q"])
+            S = num_splits or pa.attn_plan_splits(16, 8, 4, 128, 2048, 0, c["k"].stride(1))
+            pa.attn_decode(c["q"], c["k"], c["v"], out, c["scale"], num_splits=S)
+            torch.cuda.synchronize()
+            per_launch.append(nb)
+            del c
+        kernel = "decode_split_kernel (contiguous, one KV head per row) of attn_decode"
+    else:
+        probe_set = make_sets(workload, dev, 1)
+        R = rotation_count(decode_bytes(probe_set[0]))
+        sets = probe_set + make_sets(workload, dev, R)[1:]
+        c0 = sets[0]
+        max_len = max(s["max_kv_len"] for s in sets)
+        S = num_splits or pa.attn_plan_splits(c0["B"], c0["Hkv"], c0["Hq"] // c0["Hkv"], c0["D"], max_len,
+                                              c0["page_size"], c0["k_pool"].stride(2))
+        ws = torch.empty(max(pa.attn_decode_workspace_bytes(c0["B"], c0["Hq"], c0["D"], S), 256),
+                         dtype=torch.uint8, device=dev)
+        for s in sets:
+            pa.attn_paged_decode_split(s["q"], s["k_pool"], s["v_pool"], s["block_table"], s["kv_lens"], max_len,
+                                       s["page_size"], s["scale"], S, ws)
+            torch.cuda.synchronize()
+            per_launch.append(decode_bytes(s))
+        kernel = "decode_split_kernel, %d slices" % S
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
     for _ in range(3):
         dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"counters_run": True, "num_splits": S, "split_kernel_algorithmic_bytes": decode_bytes(c0),
-                      "copy_bytes": 1 << 30}), flush=True)
+    print(json.dumps({"counters_run": True, "workload": workload, "kernel": kernel,
+                      "algorithmic_bytes_per_launch": per_launch, "copy_bytes": 1 << 30}), flush=True)
 
 
 def run_extras(torch, pa, dev, args):
-    """Short timings of the other decode workloads (same protocol)."""
-    import workloads
+    """Short timings of the other workloads (same protocol)."""
     out = {}
     steps, warm = 20, 5
-    for name in ("paged_b32", "paged_b128_kv4096", "paged_b32_kv4096"):
-        probe = make_sets(name, dev, 1)
-        per = decode_bytes(probe[0])
-        R = rotation_count(per)
-        sets = probe + make_sets(name, dev, R)[1:]
-        mx = max(s["max_kv_len"] for s in sets)
-        c0 = sets[0]
-        S = pa.attn_plan_splits(c0["B"], 8, 4, 128, mx, 16, c0["k_pool"].stride(2))
-        ws = torch.empty(max(256, pa.attn_decode_workspace_bytes(c0["B"], 32, 128, S)), dtype=torch.uint8,
-                         device=dev)
-        for s in sets:
-            s["out"] = torch.empty_like(s["q"])
-
-        def call(s):
-            pa.attn_paged_decode(s["q"], s["k_pool"], s["v_pool"], s["block_table"], s["kv_lens"], mx,
-                                 s["out"], 16, s["scale"], num_splits=S, workspace=ws)
-        ms = time_calls(torch, call, sets, steps, warm)
-        nb = sum(decode_bytes(sets[i % R]) for i in range(steps)) / steps
-        out[name] = {"us_per_call": round(ms * 1e3, 2), "GB/s": round(nb / (ms * 1e-3) / 1e9, 1),
-                     "hbm_peak_frac": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "num_splits": S,
-                     "rotation_sets": R}
-        del sets
-        torch.cuda.empty_cache()
+    for name in DECODE_WORKLOADS:
+        if name == args.workload:
+            continue
+        out[name] = bench_decode(torch, pa, dev, name, steps, warm)
     out["contiguous_b16_kv2048"] = bench_contiguous(torch, pa, dev, steps, warm, 0)
     out["ragged_prefill"] = bench_prefill(torch, pa, dev, steps, warm, masked=False)
     out["ragged_prefill_masked"] = bench_prefill(torch, pa, dev, steps, warm, masked=True)
@@ -535,7 +627,7 @@ def bench_contiguous(torch, pa, dev, steps, warm, num_splits):
     """Contiguous decode, B=16 Hq=32 Hkv=8 D=128 kv=2048 (bhld), same protocol."""
     import workloads
     c = workloads.contiguous_decode(device=dev)
-    nb = 16 * 8 * 2048 * 128 * 4 + 2 * 16 * 32 * 128 * 2
+    nb = contig_bytes()
     R = rotation_count(nb)
     cs = [c] + [workloads.contig_decode_case(1002 + 7919 * r, 16, 32, 8, 128, 2048, device=dev)
                 for r in range(1, R)]
@@ -547,8 +639,12 @@ def bench_contiguous(torch, pa, dev, steps, warm, num_splits):
     def ccall(s):
         pa.attn_decode(s["q"], s["k"], s["v"], s["out"], s["scale"], num_splits=S, workspace=ws)
     ms = time_calls(torch, ccall, cs, steps, warm)
-    return {"us_per_call": round(ms * 1e3, 2), "GB/s": round(nb / (ms * 1e-3) / 1e9, 1),
-            "hbm_peak_frac": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "num_splits": S, "rotation_sets": R}
+    del cs
+    torch.cuda.empty_cache()
+    gbs = nb / (ms * 1e-3) / 1e9
+    pr = probe_ceiling(torch, pa, dev, nb)
+    return {"us_per_call": round(ms * 1e3, 2), "GB/s": round(gbs, 1), "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "num_splits": S, "rotation_sets": R, "probe": pr, "frac_of_probe": round(gbs / pr["GB/s"], 4)}
 
 
 if __name__ == "__main__":

@@ -477,6 +477,20 @@ int attn_rotary_embed(const void *x, int64_t x_st, int64_t x_sh, void *out, int6
                       int T, int H, int D, const float *cos_table, const float *sin_table, int64_t tab_st,
                       int table_rows, const int32_t *positions, void *stream);
 
+/* ----------------------------------------------------------- measurement */
+
+/*
+ * Pure-read HBM streaming probe: the measured ceiling that decode's achieved
+ * bandwidth is compared against (beside the 8 TB/s specification).  Reads
+ * every 16-byte word of buf [bytes] exactly once with non-temporal loads,
+ * the grid sweeping the buffer front to back, and writes the XOR of the words
+ * each wave read to sink (uint32 [workgroups * 4 waves * 4], 16-byte
+ * aligned), so that no load is dropped and the XOR over sink equals the XOR
+ * of every 16-byte word of the buffer.  workgroups 0 = one per compute unit
+ * (256 threads each).  buf and bytes must be 16-byte aligned.
+ */
+int attn_hbm_read_probe(const void *buf, size_t bytes, uint32_t *sink, int workgroups, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,7 +19,7 @@ __all__ = [
     "attn_prefill_plan", "attn_prefill_tile_rows", "attn_paged_prefill", "attn_swa_fp8_decode",
     "attn_prefill", "attn_paged_kv_append", "attn_swa_fp8_append", "attn_rotary_embed",
     "attn_prefill_workspace_bytes", "attn_prefill_plan_splits", "attn_paged_prefill_split",
-    "attn_prefill_split", "EXPORTED_SYMBOLS",
+    "attn_prefill_split", "attn_hbm_read_probe", "EXPORTED_SYMBOLS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -66,6 +66,7 @@ _SIGS = {
                                   _I, _I, _P, _Z, _P], _I),
     "attn_prefill_split": ([_P, _L, _L, _L, _P, _P, _L, _L, _L, _P, _I, _I, _P, _I, _L, _L, _P, _L, _L, _L,
                             _I, _I, _I, _I, _I, _F, _I, _P, _Z, _P], _I),
+    "attn_hbm_read_probe": ([_P, _Z, _P, _I, _P], _I),
 }
 EXPORTED_SYMBOLS = tuple(_SIGS)
 
@@ -485,3 +486,13 @@ def attn_prefill_split(q, k, v, out, scale, is_causal=False, kv_lens=None, mask=
         _ptr(out), out.stride(0), out.stride(1), out.stride(2), B, Lq, Hq, Hkv, D, float(scale),
         S, _ptr(ws), nbytes, _stream(stream)))
     return out
+
+
+def attn_hbm_read_probe(buf, sink, workgroups=0, stream=None):
+    """Read every byte of the device tensor buf once (HBM streaming probe);
+    sink: uint32 device tensor of at least workgroups * 16 entries (0 = one
+    workgroup per CU: 16 * CU count), which receives per-wave XORs."""
+    _dev(buf=(buf, None), sink=(sink, (torch.int32,)))
+    assert buf.is_contiguous() and sink.is_contiguous()
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib().attn_hbm_read_probe(_ptr(buf), nbytes, _ptr(sink), int(workgroups), _stream(stream)))

@@ -58,12 +58,27 @@ int device_cus() {
 }
 
 constexpr int kMaxWaves = 1 << 16;     // upper bound on decode slices (num_splits)
-// Decode waves per CU the planner aims at: three when a wave streams whole
-// 2 KB token rows (eight KV heads), two when it streams one head (measured
-// best for each on MI355X with non-temporal K/V loads).
+// One-wave slices (group sizes above 4): waves per CU the planner aims at,
+// three when a wave streams whole 2 KB token rows (eight KV heads), two when
+// it streams one head (measured best for each on MI355X with non-temporal
+// K/V loads).
 constexpr int kWavesPerCuRows = 3;
 constexpr int kWavesPerCuHead = 2;
-constexpr int kMinSliceTokens = 64;    // shortest slice the planner makes, in tokens of a row
+constexpr int kMinSliceTokens = 64;    // shortest one-wave slice, in tokens of a row
+// Four-wave slices (group sizes up to 4), one workgroup per CU at most: with
+// eight KV heads per row, slices on three quarters of the CUs (768 waves;
+// swept on MI355X, B = 128 and B = 32 over kv U[512, 4096]: 192 slices
+// 195.6 / 60.4 us per call against 200.9 / 60.9 at 256 and 210 / 66 for 512
+// slices, which put two workgroups on some CUs); with one head per row, one
+// slice per CU.
+constexpr int kSlicesPerCu4Rows_num = 3, kSlicesPerCu4Rows_den = 4;
+constexpr int kMinSliceTokens4 = 256;  // shortest four-wave slice, in tokens of a row
+
+// Waves per decode slice (one workgroup each): four take alternate tiles of
+// every piece and merge their states in LDS, so the fp32 partials (one per
+// piece) are four times fewer than with one-wave slices of the same total
+// wave count; the kernel is built for that up to Gk = 4 query heads a pass.
+int decode_waves_per_slice(int Gk) { return Gk <= 4 ? 4 : 1; }
 constexpr int kMaxPrefillSplits = 256; // upper bound on prefill KV splits
 constexpr int kPrefillWgPerCu = 1;     // prefill workgroups resident per CU (512 threads, up to 159 KB LDS)
 constexpr int kMinSplitKeyTiles = 8;   // fewest 64-key tiles the prefill planner gives one split
@@ -222,6 +237,7 @@ int run_decode(pa::DecodeParams &p, int D, int G, bool paged, int max_kv_len, in
     p.ngrp = L.ngrp;
     p.R = p.B * p.ngrp;
     p.W = W;
+    p.NW = decode_waves_per_slice(L.Gk);
     if ((int64_t)p.R * (int64_t)max_kv_len >= (1ll << 31))
         return fail(ATTN_ERR_UNSUPPORTED, "decode: rows * max_kv_len must stay below 2^31 tokens");
     if ((int64_t)p.B * p.Hq >= (1ll << 31))
@@ -269,8 +285,13 @@ int attn_plan_splits(int B, int Hkv, int G, int D, int max_kv_len, int page_size
     const int hw = L.HW;
     const long rows = (long)B * L.ngrp;
     const long line = rows * (long)max_kv_len;   // upper bound on the tokens of all rows
-    long W = (line + kMinSliceTokens - 1) / kMinSliceTokens;
-    const long cap = (long)num_cus * (hw == 8 ? kWavesPerCuRows : kWavesPerCuHead);
+    const bool four = decode_waves_per_slice(L.Gk) == 4;
+    const long min_slice = four ? kMinSliceTokens4 : kMinSliceTokens;
+    long W = (line + min_slice - 1) / min_slice;
+    long cap;
+    if (four) cap = hw == 8 ? ((long)num_cus * kSlicesPerCu4Rows_num + kSlicesPerCu4Rows_den - 1) / kSlicesPerCu4Rows_den
+                            : (long)num_cus;
+    else cap = (long)num_cus * (hw == 8 ? kWavesPerCuRows : kWavesPerCuHead);
     if (W > cap) W = cap;
     if (W > kMaxWaves) W = kMaxWaves;
     if (W < 1) W = 1;
@@ -871,6 +892,20 @@ int attn_swa_fp8_append(const void *x, int64_t x_st, const int64_t *slots, const
     p.num_slots = (int64_t)num_blocks * block_size;
     p.bs_div = pa::make_divu32((uint32_t)block_size);
     return launch_status(pa::launch_swa_quantize(p, static_cast<hipStream_t>(stream)), "swa quantize kernel");
+}
+
+int attn_hbm_read_probe(const void *buf, size_t bytes, uint32_t *sink, int workgroups, void *stream) {
+    if (!buf || !sink) return fail(ATTN_ERR_INVALID_ARG, "attn_hbm_read_probe: null pointer");
+    if (workgroups < 0) return fail(ATTN_ERR_INVALID_ARG, "attn_hbm_read_probe: negative workgroup count");
+    if (!aligned16(buf) || (bytes & 15) || ((uintptr_t)sink & 15u))
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_hbm_read_probe: buffer, size and sink must be 16-byte aligned");
+    if (workgroups == 0) {
+        workgroups = device_cus();
+        if (workgroups <= 0) return fail(ATTN_ERR_LAUNCH, "attn_hbm_read_probe: cannot query the device");
+    }
+    if (workgroups > (1 << 20)) return fail(ATTN_ERR_INVALID_ARG, "attn_hbm_read_probe: too many workgroups");
+    return launch_status(pa::launch_stream_read(buf, bytes, sink, workgroups, static_cast<hipStream_t>(stream)),
+                         "stream read probe");
 }
 
 int attn_rotary_embed(const void *x, int64_t x_st, int64_t x_sh, void *out, int64_t o_st, int64_t o_sh,

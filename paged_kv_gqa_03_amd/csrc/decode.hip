@@ -126,8 +126,14 @@ __device__ __forceinline__ float sum_lanes(float x) {
     return x;
 }
 
-template <int D, int G, int HW, bool PAGED>
-__global__ __launch_bounds__(64, (G >= 8 ? 1 : 2)) void decode_split_kernel(const DecodeParams p) {
+// Per-lane state of one wave handed to the others of its workgroup: for each
+// query head, the reference, the sum and the NCH x 8 accumulators, stored
+// field-major so a wave's 64 lanes touch consecutive words.
+template <int G, int NCH>
+constexpr int xch_fields() { return G * (2 + 8 * NCH); }
+
+template <int D, int G, int HW, bool PAGED, int NW>
+__global__ __launch_bounds__(64 * NW, (G >= 8 ? 1 : 2)) void decode_split_kernel(const DecodeParams p) {
     constexpr int JJ = chunk_lanes<D>();
     constexpr int NCH = D / (8 * JJ);   // 16-byte chunks per lane and row
     constexpr int CS = 8 * JJ;          // elements between a lane's chunks
@@ -135,7 +141,11 @@ __global__ __launch_bounds__(64, (G >= 8 ? 1 : 2)) void decode_split_kernel(cons
     static_assert(TG >= 1, "a wave holds at most 64 / JJ KV heads");
     constexpr int TILE = 2 * TG;        // tokens per tile
     constexpr int HWG = HW * G;         // query heads per row
+    constexpr int NT = 64 * NW;         // threads of the workgroup
     const int lane = threadIdx.x & 63;
+    // Wave of the workgroup: the NW waves take alternate tiles of every
+    // piece of the slice and merge their states through LDS at its end.
+    const int wv = NW > 1 ? wave_id() : 0;
     const int w = blockIdx.x;
     const int grp = lane / JJ, jj = lane % JJ;
     const int hw = grp % HW, tg = grp / HW;
@@ -160,7 +170,7 @@ __global__ __launch_bounds__(64, (G >= 8 ? 1 : 2)) void decode_split_kernel(cons
         // whose position lies strictly inside row r sits inside that row's
         // run of slots r + w, which the combine merges whole: mark the slot
         // empty (m = -inf, l = 0; the combine then ignores its o).
-        if (P < a)
+        if (P < a && wv == 0)
             for (int i = lane; i < HWG; i += 64)
                 *reinterpret_cast<float2 *>(p.ml_part + ((int64_t)(r + w) * HWG + i) * 2) =
                     make_float2(-INFINITY, 0.f);
@@ -168,6 +178,7 @@ __global__ __launch_bounds__(64, (G >= 8 ? 1 : 2)) void decode_split_kernel(cons
     }
 
     __shared__ int32_t pages[kDecodeMaxSplitPages];
+    __shared__ float xch[NW > 1 ? NW * xch_fields<G, NCH>() * 64 : 1];
     const uint32_t s_page = (uint32_t)p.s_page, s_slot = (uint32_t)p.s_slot;
     const uint32_t k_sl = (uint32_t)p.k_sl, v_sl = (uint32_t)p.v_sl;
 
@@ -179,7 +190,7 @@ __global__ __launch_bounds__(64, (G >= 8 ? 1 : 2)) void decode_split_kernel(cons
         // The waves holding the row's first and last keys record themselves,
         // so the combine finds the row's pieces (slots r + first .. r + last)
         // without scanning the lengths.
-        if (p.ranges && lane == 0) {
+        if (p.ranges && lane == 0 && wv == 0) {
             if (lo == 0) p.ranges[2 * (int64_t)r] = w;
             if (hi == n) p.ranges[2 * (int64_t)r + 1] = w;
         }
@@ -226,15 +237,25 @@ __global__ __launch_bounds__(64, (G >= 8 ? 1 : 2)) void decode_split_kernel(cons
                 const int32_t *bt_row = p.bt + b * p.bt_sb;
                 first_pg = (int)divu32((uint32_t)j0, p.ps_div);
                 const int npg = (int)divu32((uint32_t)last, p.ps_div) - first_pg + 1;
-                __builtin_amdgcn_wave_barrier();   // earlier readers of the slice are done
-                for (int i = lane; i < npg; i += 64) pages[i] = bt_row[first_pg + i];
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                if constexpr (NW > 1) {
+                    __syncthreads();   // earlier readers of the slice are done
+                    for (int i = threadIdx.x; i < npg; i += NT) pages[i] = bt_row[first_pg + i];
+                    __syncthreads();
+                } else {
+                    __builtin_amdgcn_wave_barrier();   // earlier readers of the slice are done
+                    for (int i = lane; i < npg; i += 64) pages[i] = bt_row[first_pg + i];
+                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                    __builtin_amdgcn_wave_barrier();
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                }
             }
 
-            auto lookup = [&](int t) {
+            // This wave's tiles of the sub-piece: wv, wv + NW, wv + 2 NW, ...;
+            // k below counts them.
+            const int ntw = ntiles > wv ? (ntiles - wv + NW - 1) / NW : 0;
+            auto lookup = [&](int k) {
                 TokAddr ad;
+                const int t = wv + NW * k;
                 const int ja = min(j0 + t * TILE + tg, last);
                 const int jb = min(j0 + t * TILE + tg + TG, last);
                 if constexpr (PAGED) {
@@ -273,8 +294,8 @@ __global__ __launch_bounds__(64, (G >= 8 ? 1 : 2)) void decode_split_kernel(cons
                     load16_stream(vB + c * CS, rg.vb[c]);
                 }
             };
-            auto compute = [&](int t, const KVRegs<NCH> &rg) {
-                const int ja = j0 + t * TILE + tg;
+            auto compute = [&](int k, const KVRegs<NCH> &rg) {
+                const int ja = j0 + (wv + NW * k) * TILE + tg;
                 const bool oka = ja < j1, okb = ja + TG < j1;
                 float xa[G], xb[G];
 #pragma unroll
@@ -341,21 +362,23 @@ __global__ __launch_bounds__(64, (G >= 8 ? 1 : 2)) void decode_split_kernel(cons
             // across the back edge.  Page lookups sit right before their
             // loads and are never carried across iterations; past the last
             // tile the loads repeat the last tile (in bounds, never used).
-            const int tl = ntiles - 1;
-            KVRegs<NCH> r0, r1, r2;
-            issue(lookup(0), r0);
-            issue(lookup(min(1, tl)), r1);
-            int t = 0;
-            for (; t + 2 < ntiles; t += 3) {
-                issue(lookup(t + 2), r2);
-                compute(t, r0);
-                issue(lookup(min(t + 3, tl)), r0);
-                compute(t + 1, r1);
-                issue(lookup(min(t + 4, tl)), r1);
-                compute(t + 2, r2);
+            if (ntw > 0) {
+                const int tl = ntw - 1;
+                KVRegs<NCH> r0, r1, r2;
+                issue(lookup(0), r0);
+                issue(lookup(min(1, tl)), r1);
+                int t = 0;
+                for (; t + 2 < ntw; t += 3) {
+                    issue(lookup(t + 2), r2);
+                    compute(t, r0);
+                    issue(lookup(min(t + 3, tl)), r0);
+                    compute(t + 1, r1);
+                    issue(lookup(min(t + 4, tl)), r1);
+                    compute(t + 2, r2);
+                }
+                if (t < ntw) compute(t, r0);
+                if (t + 1 < ntw) compute(t + 1, r1);
             }
-            if (t < ntiles) compute(t, r0);
-            if (t + 1 < ntiles) compute(t + 1, r1);
         }
 
         // Merge the TG token streams of each head (lanes equal in hw and jj,
@@ -384,14 +407,59 @@ __global__ __launch_bounds__(64, (G >= 8 ? 1 : 2)) void decode_split_kernel(cons
             }
         }
 
-        // Every token stream now holds the head's totals; stream tg writes the
-        // query heads h with h % TG == tg.  A piece covering the whole row is
-        // the row's only piece: written normalised when direct writes are on.
+        // Merge the NW waves' states of the piece: every wave leaves its
+        // (reference, sum, accumulators) in LDS, then wave wv merges the
+        // query heads h with h % NW == wv from all of them.
+        if constexpr (NW > 1) {
+            constexpr int F = 2 + 8 * NCH;
+            __syncthreads();   // the previous piece's readers are done with xch
+            float *mine = xch + wv * (G * F * 64);
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                mine[(h * F + 0) * 64 + lane] = mref[h];
+                mine[(h * F + 1) * 64 + lane] = lsum[h];
+#pragma unroll
+                for (int c = 0; c < NCH; ++c)
+#pragma unroll
+                    for (int x = 0; x < 8; ++x) mine[(h * F + 2 + 8 * c + x) * 64 + lane] = o[h][c][x];
+            }
+            __syncthreads();
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                if (h % NW != wv) continue;
+                float M = -INFINITY;
+#pragma unroll
+                for (int v = 0; v < NW; ++v) M = fmaxf(M, xch[(v * G * F + h * F) * 64 + lane]);
+                float l = 0.f;
+#pragma unroll
+                for (int c = 0; c < NCH; ++c)
+#pragma unroll
+                    for (int x = 0; x < 8; ++x) o[h][c][x] = 0.f;
+#pragma unroll
+                for (int v = 0; v < NW; ++v) {
+                    const float *src = xch + (v * G * F + h * F) * 64 + lane;
+                    const float mv = src[0];
+                    const float f = mv == -INFINITY ? 0.f : exp2_fast(mv - M);
+                    l += f * src[64];
+#pragma unroll
+                    for (int c = 0; c < NCH; ++c)
+#pragma unroll
+                        for (int x = 0; x < 8; ++x) o[h][c][x] += f * src[(2 + 8 * c + x) * 64];
+                }
+                mref[h] = M;
+                lsum[h] = l;
+            }
+        }
+
+        // Every token stream now holds the head's totals; stream tg of wave
+        // wv writes the query heads h with h % NW == wv and (h / NW) % TG ==
+        // tg.  A piece covering the whole row is the row's only piece:
+        // written normalised when direct writes are on.
         const bool direct = p.direct && lo == 0 && hi == n;
         const int64_t slot = (int64_t)r + w;
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            if (h % TG != tg) continue;
+            if (h % NW != wv || (h / NW) % TG != tg) continue;
             const int hq = h0 + h;
             if (direct) {
                 const float inv = lsum[h] > 0.f ? 1.f / lsum[h] : 0.f;
@@ -557,7 +625,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const CombineParams p) {
 
 template <int D, int G, int HW, bool PAGED>
 hipError_t launch_decode_t(const DecodeParams &p, hipStream_t stream) {
-    hipLaunchKernelGGL((decode_split_kernel<D, G, HW, PAGED>), dim3(p.W), dim3(64), 0, stream, p);
+    if (p.NW == 4) {
+        if constexpr (G <= 4) {
+            hipLaunchKernelGGL((decode_split_kernel<D, G, HW, PAGED, 4>), dim3(p.W), dim3(256), 0, stream, p);
+            return hipGetLastError();
+        }
+        return hipErrorInvalidValue;
+    }
+    hipLaunchKernelGGL((decode_split_kernel<D, G, HW, PAGED, 1>), dim3(p.W), dim3(64), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -40,7 +40,8 @@ struct DecodeParams {
     int HW;          // KV heads per row (1, 2, 4, 8; divides Hkv)
     int ngrp;        // rows per sequence: Hkv / HW * passes
     int R;           // B * ngrp rows
-    int W;           // waves (slices of the line)
+    int W;           // slices of the line (one workgroup each)
+    int NW;          // waves per workgroup: 1, or 4 (alternate tiles, merged in LDS; G <= 4)
     int max_sub;     // longest sub-piece (tokens) one LDS page slice covers
     int direct;      // 1: a row covered by one piece is written normalised
     float sl2;       // scale * log2(e)
@@ -194,5 +195,6 @@ hipError_t launch_prefill(const PrefillParams &p, int D, hipStream_t stream);
 hipError_t launch_prefill_combine(const PrefillCombineParams &p, int D, hipStream_t stream);
 hipError_t launch_decode_combine(const DecodeCombineParams &p, int D, hipStream_t stream);
 hipError_t launch_combine(const CombineParams &p, int D, hipStream_t stream);
+hipError_t launch_stream_read(const void *buf, uint64_t bytes, uint32_t *sink, int workgroups, hipStream_t stream);
 
 }  // namespace pa

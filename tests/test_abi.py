@@ -45,23 +45,27 @@ def test_version():
                                            (1, 1, 100000), (512, 8, 4096), (4, 8, 16), (3, 1, 0)])
 @pytest.mark.parametrize("s_head", [128, 16 * 128])
 def test_planner_bounds(B, Hkv, max_len, s_head):
+    # G = 4: four-wave slices, at most one per CU
     W = pa.attn_plan_splits(B, Hkv, 4, 128, max_len, 16, s_head, 256)
     hw = min(8, Hkv) if s_head == 128 else 1
-    assert 1 <= W <= 256 * (3 if hw == 8 else 2)
+    assert 1 <= W <= (192 if hw == 8 else 256)
     rows = B * (Hkv // hw)
-    # no slice shorter than 64 tokens of a row, given the longest possible line
-    assert W == 1 or rows * max_len >= 64 * (W - 1)
+    # no slice shorter than 256 tokens of a row, given the longest possible line
+    assert W == 1 or rows * max_len >= 256 * (W - 1)
     # a larger batch never asks for fewer slices
     assert pa.attn_plan_splits(2 * B, Hkv, 4, 128, max_len, 16, s_head, 256) >= W
 
 
 def test_planner_waves_per_cu_target():
-    # eight KV heads per wave (whole 2 KB token rows): three waves per CU
-    assert pa.attn_plan_splits(128, 8, 4, 128, 4096, 16, 128, 256) == 768
-    assert pa.attn_plan_splits(32, 8, 4, 128, 4096, 16, 128, 304) == 912
-    # one KV head per wave (head-major source): two waves per CU
-    assert pa.attn_plan_splits(16, 8, 4, 128, 2048, 0, 2048 * 128, 256) == 512
-    assert pa.attn_plan_splits(2, 2, 4, 64, 300, 16, 64, 256) == 10   # 600 tokens / 64
+    # G <= 4, eight KV heads per row (whole 2 KB token rows): four-wave
+    # slices on three quarters of the CUs (768 waves on 256 CUs)
+    assert pa.attn_plan_splits(128, 8, 4, 128, 4096, 16, 128, 256) == 192
+    assert pa.attn_plan_splits(32, 8, 4, 128, 4096, 16, 128, 304) == 228
+    # one KV head per row (head-major source): one four-wave slice per CU
+    assert pa.attn_plan_splits(16, 8, 4, 128, 2048, 0, 2048 * 128, 256) == 256
+    assert pa.attn_plan_splits(2, 2, 4, 64, 300, 16, 64, 256) == 3   # 600 tokens / 256
+    # G = 8: one-wave slices, three waves per CU with eight heads per row
+    assert pa.attn_plan_splits(128, 8, 8, 128, 4096, 16, 128, 256) == 768
 
 
 def test_workspace_bytes_layout():
@@ -236,8 +240,8 @@ def test_planner_counts_one_row_per_pass_for_other_group_sizes():
     # (one head per wave), so the line is 4 * B * max_len tokens
     assert pa.attn_plan_splits(2, 1, 32, 128, 640, 16, 128, 256) == 2 * 4 * 640 // 64
     assert pa.attn_plan_splits(2, 1, 8, 128, 640, 16, 128, 256) == 2 * 640 // 64
-    # G = 3: three passes of one head
-    assert pa.attn_plan_splits(1, 2, 3, 128, 640, 16, 128, 256) == 2 * 3 * 640 // 64
+    # G = 3: three passes of one head (four-wave slices of >= 256 tokens)
+    assert pa.attn_plan_splits(1, 2, 3, 128, 640, 16, 128, 256) == 2 * 3 * 640 // 256
 
 
 def test_prefill_tile_rows_head_dim_256():
@@ -425,3 +429,11 @@ def test_binding_rejects_host_tensors():
     tab = torch.zeros(8, 32, dtype=torch.float32)
     with pytest.raises(ValueError, match="x must be a device tensor"):
         pa.attn_rotary_embed(x, tab, tab, torch.zeros(3, dtype=torch.int32))
+
+
+def test_probe_rejects_bad_arguments():
+    lib = pa.lib()
+    assert lib.attn_hbm_read_probe(None, 1024, FAKE, 4, None) == pa.ATTN_ERR_INVALID_ARG
+    assert lib.attn_hbm_read_probe(FAKE, 1000, FAKE, 4, None) == pa.ATTN_ERR_UNSUPPORTED
+    assert lib.attn_hbm_read_probe(FAKE + 8, 1024, FAKE, 4, None) == pa.ATTN_ERR_UNSUPPORTED
+    assert lib.attn_hbm_read_probe(FAKE, 1024, FAKE, -1, None) == pa.ATTN_ERR_INVALID_ARG

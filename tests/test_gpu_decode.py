@@ -359,17 +359,18 @@ def test_partition_every_slice_count(Hkv, layout):
         assert_close(got, ref, what="S=%d of T=%d" % (S, T))
 
 
-def test_planner_on_mostly_empty_batch():
-    """128 sequences of which one holds keys: the planner's slice count
-    (sized from max_kv_len) exceeds the keys, so most slices are empty."""
+@pytest.mark.parametrize("S", [0, 150])
+def test_planner_on_mostly_empty_batch(S):
+    """128 sequences of which one holds keys: the planner sizes its slice
+    count from max_kv_len (128 x 100 keys), far more than the 100 keys there
+    are; with 150 slices most of them are empty."""
     lens = [0] * 128
     lens[77] = 100
     case = workloads.paged_decode_case(270, 128, 32, 8, 128, lens, 16)
-    S = pa.attn_plan_splits(128, 8, 4, 128, 100, 16, case["k_pool"].stride(2))
-    assert S > 100
+    S = S or pa.attn_plan_splits(128, 8, 4, 128, 100, 16, case["k_pool"].stride(2))
     ref, _ = oracle_paged(case)
-    got = run_paged(case, 0, workspace=nan_workspace(128, 32, 128, S))
-    assert_close(got, ref, what="planner S=%d" % S)
+    got = run_paged(case, S, workspace=nan_workspace(128, 32, 128, S))
+    assert_close(got, ref, what="S=%d" % S)
 
 
 # ------------------------------------------------ head dims 32 and 256
