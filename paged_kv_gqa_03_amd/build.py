@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpaged_attn.so")
-SOURCES = ["api.hip", "decode.hip", "prefill.hip", "swa.hip", "cache_ops.hip", "probe.hip"]
+SOURCES = ["api.hip", "decode.hip", "decode_mfma.hip", "prefill.hip", "swa.hip", "cache_ops.hip", "probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -120,17 +120,31 @@ int check_heads(int Hq, int Hkv, int *G) {
     return ATTN_OK;
 }
 
-// Decode row layout for group size G: the kernel is built for Gk query
-// heads per pass (the largest power of two dividing G, at most 8) and a
-// (sequence, KV head) takes G / Gk passes, each a row of its own that
-// streams the KV head again; with one pass, a row may hold HW > 1 adjacent
-// KV heads.
+// Decode row layout for group size G.  Head dims 64 and 128 with G other
+// than 1, 2 or 4 run the MFMA kernel: a row is one KV head and Gk query
+// heads (the largest divisor of G that is at most 32, on NB = ceil(Gk / 16)
+// blocks of 16 MFMA rows), G / Gk passes per KV head.  Otherwise the VALU
+// kernel is built for Gk query heads per pass (the largest power of two
+// dividing G, at most 8) and a (sequence, KV head) takes G / Gk passes, each
+// a row of its own that streams the KV head again; with one pass, a row may
+// hold HW > 1 adjacent KV heads.
 struct DecodeLayout {
-    int Gk, passes, HW, ngrp;
+    int Gk, passes, HW, ngrp, NB;
 };
 
 DecodeLayout decode_layout(int Hkv, int G, int64_t kv_s_head, int D) {
     DecodeLayout L;
+    if ((D == 64 || D == 128) && G != 1 && G != 2 && G != 4) {
+        int gm = G < 32 ? G : 32;
+        while (G % gm != 0) --gm;
+        L.Gk = gm;
+        L.passes = G / gm;
+        L.HW = 1;
+        L.ngrp = Hkv * L.passes;
+        L.NB = (gm + 15) / 16;
+        return L;
+    }
+    L.NB = 0;
     L.Gk = (G & -G) < 8 ? (G & -G) : 8;
     L.passes = G / L.Gk;
     L.HW = L.passes > 1 ? 1 : heads_per_wave(Hkv, kv_s_head, D);
@@ -237,7 +251,8 @@ int run_decode(pa::DecodeParams &p, int D, int G, bool paged, int max_kv_len, in
     p.ngrp = L.ngrp;
     p.R = p.B * p.ngrp;
     p.W = W;
-    p.NW = decode_waves_per_slice(L.Gk);
+    p.NB = L.NB;
+    p.NW = L.NB ? 4 : decode_waves_per_slice(L.Gk);
     if ((int64_t)p.R * (int64_t)max_kv_len >= (1ll << 31))
         return fail(ATTN_ERR_UNSUPPORTED, "decode: rows * max_kv_len must stay below 2^31 tokens");
     if ((int64_t)p.B * p.Hq >= (1ll << 31))
@@ -252,7 +267,7 @@ int run_decode(pa::DecodeParams &p, int D, int G, bool paged, int max_kv_len, in
         p.ranges = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + ws_range_offset(p.B, p.Hq, D, W));
     }
     if (p.B == 0) return ok();
-    hipError_t e = pa::launch_decode(p, D, L.Gk, paged, stream);
+    hipError_t e = L.NB ? pa::launch_decode_mfma(p, D, paged, stream) : pa::launch_decode(p, D, L.Gk, paged, stream);
     if (e != hipSuccess) return launch_status(e, "decode split kernel");
     if (mode == 0) {
         // Rows spanning several slices are merged; empty rows are zeroed;
@@ -285,7 +300,7 @@ int attn_plan_splits(int B, int Hkv, int G, int D, int max_kv_len, int page_size
     const int hw = L.HW;
     const long rows = (long)B * L.ngrp;
     const long line = rows * (long)max_kv_len;   // upper bound on the tokens of all rows
-    const bool four = decode_waves_per_slice(L.Gk) == 4;
+    const bool four = L.NB > 0 || decode_waves_per_slice(L.Gk) == 4;
     const long min_slice = four ? kMinSliceTokens4 : kMinSliceTokens;
     long W = (line + min_slice - 1) / min_slice;
     long cap;

@@ -42,6 +42,7 @@ struct DecodeParams {
     int R;           // B * ngrp rows
     int W;           // slices of the line (one workgroup each)
     int NW;          // waves per workgroup: 1, or 4 (alternate tiles, merged in LDS; G <= 4)
+    int NB;          // > 0: MFMA kernel with NB blocks of 16 query-head rows (decode_mfma.hip)
     int max_sub;     // longest sub-piece (tokens) one LDS page slice covers
     int direct;      // 1: a row covered by one piece is written normalised
     float sl2;       // scale * log2(e)
@@ -187,6 +188,7 @@ struct RotaryParams {
 };
 
 hipError_t launch_decode(const DecodeParams &p, int D, int G, bool paged, hipStream_t stream);
+hipError_t launch_decode_mfma(const DecodeParams &p, int D, bool paged, hipStream_t stream);
 hipError_t launch_swa(const SwaParams &p, hipStream_t stream);
 hipError_t launch_kv_append(const KvAppendParams &p, hipStream_t stream);
 hipError_t launch_swa_quantize(const SwaQuantParams &p, hipStream_t stream);

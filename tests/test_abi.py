@@ -64,8 +64,11 @@ def test_planner_waves_per_cu_target():
     # one KV head per row (head-major source): one four-wave slice per CU
     assert pa.attn_plan_splits(16, 8, 4, 128, 2048, 0, 2048 * 128, 256) == 256
     assert pa.attn_plan_splits(2, 2, 4, 64, 300, 16, 64, 256) == 3   # 600 tokens / 256
-    # G = 8: one-wave slices, three waves per CU with eight heads per row
-    assert pa.attn_plan_splits(128, 8, 8, 128, 4096, 16, 128, 256) == 768
+    # G = 8 at D = 128: the MFMA kernel, one KV head per row, one four-wave
+    # slice per CU; at D = 256 the VALU kernel, one-wave slices, three waves
+    # per CU with four heads per row... (two waves per CU for one head)
+    assert pa.attn_plan_splits(128, 8, 8, 128, 4096, 16, 128, 256) == 256
+    assert pa.attn_plan_splits(128, 8, 8, 256, 4096, 16, 256, 256) == 512
 
 
 def test_workspace_bytes_layout():
@@ -236,12 +239,15 @@ def test_prefill_tile_rows_any_group_size():
 
 
 def test_planner_counts_one_row_per_pass_for_other_group_sizes():
-    # G = 32 over 1 KV head: four passes of 8 query heads, each a row of its own
-    # (one head per wave), so the line is 4 * B * max_len tokens
-    assert pa.attn_plan_splits(2, 1, 32, 128, 640, 16, 128, 256) == 2 * 4 * 640 // 64
-    assert pa.attn_plan_splits(2, 1, 8, 128, 640, 16, 128, 256) == 2 * 640 // 64
-    # G = 3: three passes of one head (four-wave slices of >= 256 tokens)
-    assert pa.attn_plan_splits(1, 2, 3, 128, 640, 16, 128, 256) == 2 * 3 * 640 // 256
+    # D = 128, G = 32 over 1 KV head: one MFMA row of 32 query heads per
+    # (sequence, KV head), four-wave slices of >= 256 tokens
+    assert pa.attn_plan_splits(2, 1, 32, 128, 640, 16, 128, 256) == 2 * 640 // 256
+    assert pa.attn_plan_splits(2, 1, 64, 128, 640, 16, 128, 256) == 2 * 2 * 640 // 256   # two passes of 32
+    assert pa.attn_plan_splits(1, 2, 3, 128, 640, 16, 128, 256) == 2 * 640 // 256
+    # D = 256 keeps the VALU kernel: G = 32 is four passes of 8 (one-wave
+    # slices of >= 64 tokens), G = 3 three passes of one head (four-wave)
+    assert pa.attn_plan_splits(2, 1, 32, 256, 640, 16, 256, 256) == 2 * 4 * 640 // 64
+    assert pa.attn_plan_splits(1, 2, 3, 256, 640, 16, 256, 256) == 2 * 3 * 640 // 256
 
 
 def test_prefill_tile_rows_head_dim_256():

@@ -94,8 +94,11 @@ def test_dense_prefill_mask_rows_at_any_byte():
 NAN = float("nan")
 
 
-def test_decode_nan_query_poisons_only_its_row():
-    case = workloads.paged_decode_case(1130, 4, 32, 8, 128, [300, 1000, 17, 2500], 16)
+# Hq = 32 over 8 KV heads runs the VALU kernel (4 heads a row), 64 over 8 the
+# MFMA kernel (8 heads a row on one 16-row block)
+@pytest.mark.parametrize("Hq", [32, 64])
+def test_decode_nan_query_poisons_only_its_row(Hq):
+    case = workloads.paged_decode_case(1130, 4, Hq, 8, 128, [300, 1000, 17, 2500], 16)
     d = {k: case[k].to(DEV) for k in ("q", "k_pool", "v_pool", "block_table", "kv_lens")}
     for S in (1, 9):
         clean = torch.empty_like(d["q"])
@@ -108,13 +111,14 @@ def test_decode_nan_query_poisons_only_its_row():
                              out, 16, case["scale"], num_splits=S)
         torch.cuda.synchronize()
         assert bool(torch.isnan(out[1, 5]).all()), "S=%d" % S
-        keep = torch.ones(4, 32, dtype=torch.bool)
+        keep = torch.ones(4, Hq, dtype=torch.bool)
         keep[1, 5] = False
         assert torch.equal(out.cpu()[keep], clean.cpu()[keep]), "S=%d" % S
 
 
-def test_decode_nan_key_poisons_the_heads_that_read_it():
-    case = workloads.paged_decode_case(1131, 3, 32, 8, 128, [400, 1500, 64], 16)
+@pytest.mark.parametrize("Hq", [32, 64])
+def test_decode_nan_key_poisons_the_heads_that_read_it(Hq):
+    case = workloads.paged_decode_case(1131, 3, Hq, 8, 128, [400, 1500, 64], 16)
     d = {k: case[k].to(DEV) for k in ("q", "k_pool", "v_pool", "block_table", "kv_lens")}
     j, b, g = 700, 1, 3
     page = int(case["block_table"][b, j // 16])
@@ -128,9 +132,9 @@ def test_decode_nan_key_poisons_the_heads_that_read_it():
         pa.attn_paged_decode(d["q"], kp, d["v_pool"], d["block_table"], d["kv_lens"], case["max_kv_len"],
                              out, 16, case["scale"], num_splits=S)
         torch.cuda.synchronize()
-        G = 4
+        G = Hq // 8
         assert bool(torch.isnan(out[b, g * G:(g + 1) * G]).all()), "S=%d" % S
-        keep = torch.ones(3, 32, dtype=torch.bool)
+        keep = torch.ones(3, Hq, dtype=torch.bool)
         keep[b, g * G:(g + 1) * G] = False
         assert torch.equal(out.cpu()[keep], clean.cpu()[keep]), "S=%d" % S
 
