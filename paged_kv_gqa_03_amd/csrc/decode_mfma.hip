@@ -26,7 +26,7 @@
 // with two row swaps.  Scores are scaled after the dot product (csrc commit
 // that moved the scale after Q.K^T); the reference is raised lazily (by more
 // than 2^8, base 2), as in decode.hip.  Two register stages: while one tile
-// is computed the next one's K and V are in flight.
+// is staged and computed the next one's K and V are in flight.
 #include "decode_common.hpp"
 #include "device_common.hpp"
 #include "kernels.hpp"
@@ -103,8 +103,14 @@ __device__ __forceinline__ void stage_group(uint16_t *vt, int c, int base, const
     }
 }
 
-template <int D, int NB, bool PAGED>
-__global__ __launch_bounds__(256, 1) void decode_mfma_kernel(const DecodeParams p) {
+// KV modes: contiguous K/V; paged, V read key by key; paged with a page size
+// that is a multiple of 4, V read as groups of 4 keys that share a page.  The
+// mode is fixed per launch so the tile loop has no branch on it.
+enum { kContig = 0, kPagedKeys = 1, kPagedQuads = 2 };
+
+template <int D, int NB, int MODE>
+__global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void decode_mfma_kernel(const DecodeParams p) {
+    constexpr bool PAGED = MODE != kContig;
     constexpr int NS = D / 32;    // depth steps of S^T
     constexpr int NM = D / 16;    // 16-dim blocks of O^T
     constexpr int VCH = D / 8;    // 16-byte chunks of a key row
@@ -184,7 +190,11 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(const DecodeParams 
         for (int j0 = lo; j0 < hi; j0 += p.max_sub) {
             const int j1 = min(hi, j0 + p.max_sub);
             const int last = j1 - 1;
-            const int ntiles = (j1 - j0 + BKM - 1) / BKM;
+            // Tiles start at jb: j0 rounded down to a multiple of 4 for V
+            // groups of 4 keys (the up to 3 keys below j0 are in j0's page,
+            // loaded and masked), else j0.
+            const int jb = MODE == kPagedQuads ? (j0 & ~3) : j0;
+            const int ntiles = (j1 - jb + BKM - 1) / BKM;
             int first_pg = 0;
             // Every wave is done with the previous sub-piece's page slice and
             // the previous row's merge area before this one's V^T staging
@@ -214,8 +224,12 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(const DecodeParams 
             };
             // This wave's tiles: wv, wv + NWM, ...; k counts them.
             const int ntw = ntiles > wv ? (ntiles - wv + NWM - 1) / NWM : 0;
+            // The phases below are kept in program order (sched_barrier):
+            // hoisting a tile's loads above the previous compute would hold
+            // three tiles in registers.
             auto issue = [&](int k, MTile<D> &t) {
-                const int base = j0 + (wv + NWM * k) * BKM;
+                __builtin_amdgcn_sched_barrier(0);
+                const int base = jb + (wv + NWM * k) * BKM;
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
                     const uint16_t *kr = kbase + koff(base + 16 * kb + g16) + 8 * lg;
@@ -225,24 +239,23 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(const DecodeParams 
 #pragma unroll
                 for (int gi = 0; gi < VG; ++gi) {
                     const int q = lane + 64 * gi, kg = q / VCH, c = q % VCH;
-                    if constexpr (PAGED) {
-                        if ((p.ps & 3u) == 0 && (j0 & 3) == 0) {
-                            // the group's four keys start on a multiple of 4
-                            // and the page size is one: they share a page
-                            const int j = base + 4 * kg;
-                            const int jr = last - j;   // keys past the end repeat the last one
-                            const uint64_t o0 = voff(j);
+                    if constexpr (MODE == kPagedQuads) {
+                        // the group's four keys start on a multiple of 4 and
+                        // the page size is one: they share a page
+                        const int j = base + 4 * kg;
+                        const int jr = last - j;   // keys past the end repeat the last one
+                        const uint64_t o0 = voff(j);
 #pragma unroll
-                            for (int i = 0; i < 4; ++i)
-                                t.v[gi][i] = ld16_nt(vbase + o0 + (uint32_t)min(i, max(jr, 0)) * s_slot + 8 * c);
-                            continue;
-                        }
+                        for (int i = 0; i < 4; ++i)
+                            t.v[gi][i] = ld16_nt(vbase + o0 + (uint32_t)min(i, max(jr, 0)) * s_slot + 8 * c);
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) t.v[gi][i] = ld16_nt(vbase + voff(base + 4 * kg + i) + 8 * c);
                     }
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) t.v[gi][i] = ld16_nt(vbase + voff(base + 4 * kg + i) + 8 * c);
                 }
             };
             auto stage = [&](const MTile<D> &t) {
+                __builtin_amdgcn_sched_barrier(0);
                 // the previous tile's V^T reads come before these writes
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
                 __builtin_amdgcn_wave_barrier();
@@ -256,7 +269,8 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(const DecodeParams 
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             };
             auto compute = [&](int k, const MTile<D> &t) {
-                const int tbase = j0 + (wv + NWM * k) * BKM;
+                __builtin_amdgcn_sched_barrier(0);
+                const int tbase = jb + (wv + NWM * k) * BKM;
                 // S^T blocks: keys 16 kb + 4 lg + i, head 16 nb + g16.
                 f32x4_t st[NB][2];
 #pragma unroll
@@ -269,7 +283,8 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(const DecodeParams 
                     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                         for (int nb = 0; nb < NB; ++nb) st[nb][kb] = mfma16(as_bf16x8(t.k[kb][s]), qf[nb][s], st[nb][kb]);
-                const int room = j1 - (tbase + 4 * lg);   // key 16 kb + i of the lane is admitted iff < room
+                // key 16 kb + i of the lane is admitted iff skip <= it < room
+                const int room = j1 - (tbase + 4 * lg), skip = j0 - (tbase + 4 * lg);
                 uint32_t pw[NB][4];
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
@@ -279,7 +294,8 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(const DecodeParams 
                     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            x[kb][i] = 16 * kb + i < room ? st[nb][kb][i] * sl2 : -INFINITY;
+                            const bool in = 16 * kb + i < room && (MODE != kPagedQuads || 16 * kb + i >= skip);
+                            x[kb][i] = in ? st[nb][kb][i] * sl2 : -INFINITY;
                             mt = fmaxf(mt, x[kb][i]);
                         }
                     mt = max_over_rows(mt);
@@ -312,16 +328,21 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(const DecodeParams 
                 }
             };
 
+            // Two tiles in flight at every wait: tile k + 1 is issued before
+            // tile k is staged, tile k + 2 as soon as tile k is computed.
+            // Every issue in the loop is unconditional (past the end it
+            // repeats the last tile, never used): a load issued under a
+            // condition would make the compiler wait for all of them.
             if (ntw > 0) {
                 MTile<D> ra, rb;
                 issue(0, ra);
                 int k = 0;
                 for (; k + 1 < ntw; k += 2) {
-                    stage(ra);
                     issue(k + 1, rb);
+                    stage(ra);
                     compute(k, ra);
+                    issue(min(k + 2, ntw - 1), ra);
                     stage(rb);
-                    issue(min(k + 2, ntw - 1), ra);   // past the end: repeats the last tile, never used
                     compute(k + 1, rb);
                 }
                 if (k < ntw) {
@@ -394,20 +415,27 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_kernel(const DecodeParams 
     }
 }
 
-template <int D, bool PAGED>
+template <int D, int MODE>
 hipError_t launch_mfma_d(const DecodeParams &p, hipStream_t stream) {
-    if (p.NB == 1) hipLaunchKernelGGL((decode_mfma_kernel<D, 1, PAGED>), dim3(p.W), dim3(64 * NWM), 0, stream, p);
-    else if (p.NB == 2) hipLaunchKernelGGL((decode_mfma_kernel<D, 2, PAGED>), dim3(p.W), dim3(64 * NWM), 0, stream, p);
+    if (p.NB == 1) hipLaunchKernelGGL((decode_mfma_kernel<D, 1, MODE>), dim3(p.W), dim3(64 * NWM), 0, stream, p);
+    else if (p.NB == 2) hipLaunchKernelGGL((decode_mfma_kernel<D, 2, MODE>), dim3(p.W), dim3(64 * NWM), 0, stream, p);
     else return hipErrorInvalidValue;
     return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_mfma_mode(const DecodeParams &p, bool paged, hipStream_t stream) {
+    if (!paged) return launch_mfma_d<D, kContig>(p, stream);
+    if ((p.ps & 3u) == 0) return launch_mfma_d<D, kPagedQuads>(p, stream);
+    return launch_mfma_d<D, kPagedKeys>(p, stream);
 }
 
 }  // namespace
 
 hipError_t launch_decode_mfma(const DecodeParams &p, int D, bool paged, hipStream_t stream) {
     if (p.W <= 0 || p.R <= 0) return hipSuccess;
-    if (D == 64) return paged ? launch_mfma_d<64, true>(p, stream) : launch_mfma_d<64, false>(p, stream);
-    if (D == 128) return paged ? launch_mfma_d<128, true>(p, stream) : launch_mfma_d<128, false>(p, stream);
+    if (D == 64) return launch_mfma_mode<64>(p, paged, stream);
+    if (D == 128) return launch_mfma_mode<128>(p, paged, stream);
     return hipErrorInvalidValue;
 }
 
