@@ -121,9 +121,11 @@ int check_heads(int Hq, int Hkv, int *G) {
 }
 
 // Decode row layout for group size G.  Head dims 64 and 128 with G other
-// than 1, 2 or 4 run the MFMA kernel: a row is one KV head and Gk query
-// heads (the largest divisor of G that is at most 32, on NB = ceil(Gk / 16)
-// blocks of 16 MFMA rows), G / Gk passes per KV head.  Otherwise the VALU
+// than 1, 2 or 4 run the MFMA kernel: a KV head contributes Gk query heads
+// to a row (the largest divisor of G that is at most 32, on NB = ceil(Gk /
+// 16) blocks of 16 MFMA rows), G / Gk passes per KV head, and with one pass
+// a row holds HW = 4 (else 2, else 1) adjacent KV heads, one wave each, so a
+// workgroup reads those heads of each token together.  Otherwise the VALU
 // kernel is built for Gk query heads per pass (the largest power of two
 // dividing G, at most 8) and a (sequence, KV head) takes G / Gk passes, each
 // a row of its own that streams the KV head again; with one pass, a row may
@@ -139,8 +141,8 @@ DecodeLayout decode_layout(int Hkv, int G, int64_t kv_s_head, int D) {
         while (G % gm != 0) --gm;
         L.Gk = gm;
         L.passes = G / gm;
-        L.HW = 1;
-        L.ngrp = Hkv * L.passes;
+        L.HW = L.passes > 1 ? 1 : Hkv % 4 == 0 ? 4 : Hkv % 2 == 0 ? 2 : 1;
+        L.ngrp = Hkv / L.HW * L.passes;
         L.NB = (gm + 15) / 16;
         return L;
     }

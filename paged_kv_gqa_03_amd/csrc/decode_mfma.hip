@@ -3,11 +3,15 @@
 //
 // Same method and partition as decode.hip (AstrAI csrc commit history: the
 // split-KV decode with (o, m, l) partials and its log-sum-exp combine; the
-// per-element page lookup): rows r = (sequence, KV head, pass) are laid end
-// to end, W slices of the line are one four-wave workgroup each, the waves
-// take alternate 32-key tiles of every piece and merge their states through
-// LDS at its end, and a piece is written directly (normalised) when it is
-// its row's only one, else as an fp32 partial at slot r + w for the combine.
+// per-element page lookup): rows r = (sequence, group of HG adjacent KV
+// heads, pass) are laid end to end and W slices of the line are one
+// four-wave workgroup each.  Wave wv takes KV head wv % HG of the row; with
+// HG = 4 each wave streams its head's keys of the piece alone, with HG = 2
+// or 1 the waves of a head take alternate 32-key tiles and merge their
+// states through LDS at the piece's end.  The waves of a workgroup read the
+// same tokens of HG heads together, which HBM serves measurably faster than
+// one head's keys alone.  A piece is written directly (normalised) when it
+// is its row's only one, else as an fp32 partial at slot r + w.
 //
 // With Gm query heads sharing a KV head (Gm up to 32: NB = 1 or 2 blocks of
 // 16 MFMA rows) a row holds Gm heads, so each key is read once for all of
@@ -108,9 +112,13 @@ __device__ __forceinline__ void stage_group(uint16_t *vt, int c, int base, const
 // mode is fixed per launch so the tile loop has no branch on it.
 enum { kContig = 0, kPagedKeys = 1, kPagedQuads = 2 };
 
-template <int D, int NB, int MODE>
+// HG KV heads per row and workgroup: wave wv takes head wv % HG of the row
+// and tiles wv / HG, + NWT, ... of each piece (NWT = 4 / HG waves per head,
+// merged through LDS when more than one).
+template <int D, int NB, int MODE, int HG>
 __global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void decode_mfma_kernel(const DecodeParams p) {
     constexpr bool PAGED = MODE != kContig;
+    constexpr int NWT = NWM / HG;
     constexpr int NS = D / 32;    // depth steps of S^T
     constexpr int NM = D / 16;    // 16-dim blocks of O^T
     constexpr int VCH = D / 8;    // 16-byte chunks of a key row
@@ -118,7 +126,7 @@ __global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void decode_mfma_kernel(const
     static_assert(VG >= 1 && (BKM / 4) * VCH == 64 * VG, "V staging covers the tile");
     constexpr int F = 2 + 4 * NM;                              // merge floats per lane and block
     constexpr int VT_ELEMS = D * VTLD;                         // one wave's V^T tile
-    constexpr int XCH_FLOATS = NWM * NB * F * 64;
+    constexpr int XCH_FLOATS = NWT > 1 ? NWM * NB * F * 64 : 0;
     constexpr int LDS_BYTES = (NWM * VT_ELEMS * 2 > XCH_FLOATS * 4) ? NWM * VT_ELEMS * 2 : XCH_FLOATS * 4;
     __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
     __shared__ int32_t pages[kDecodeMaxSplitPages];
@@ -127,7 +135,9 @@ __global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void decode_mfma_kernel(const
     const int wv = wave_id();
     const int w = blockIdx.x;
     const int g16 = lane & 15, lg = lane >> 4;   // MFMA row / column within a block, lane group
-    const int Gm = p.G_all / p.passes;           // query heads per row
+    const int hw = wv % HG, wt = wv / HG;        // this wave's head in the row, tile phase
+    const int Gm = p.G_all / p.passes;           // query heads per KV head and row
+    const int HPR = HG * Gm;                     // query heads per row
     uint16_t *vt = reinterpret_cast<uint16_t *>(lds) + wv * VT_ELEMS;
     float *xch = reinterpret_cast<float *>(lds);
 
@@ -140,9 +150,9 @@ __global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void decode_mfma_kernel(const
     if (a >= e) {
         // An empty slice strictly inside row r holds a slot of the row's run:
         // marked empty (m = -inf, l = 0) so the combine ignores it.
-        if (P < a && wv == 0)
-            for (int i = lane; i < Gm; i += 64)
-                *reinterpret_cast<float2 *>(p.ml_part + ((int64_t)(r + w) * Gm + i) * 2) = make_float2(-INFINITY, 0.f);
+        if (P < a)
+            for (int i = threadIdx.x; i < HPR; i += 64 * NWM)
+                *reinterpret_cast<float2 *>(p.ml_part + ((int64_t)(r + w) * HPR + i) * 2) = make_float2(-INFINITY, 0.f);
         return;
     }
     const float sl2 = p.sl2;
@@ -157,8 +167,8 @@ __global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void decode_mfma_kernel(const
             if (hi == n) p.ranges[2 * (int64_t)r + 1] = w;
         }
         const int b = r / p.ngrp, hgrp = r % p.ngrp;
-        const int g = hgrp / p.passes;                           // KV head
-        const int h0 = g * p.G_all + (hgrp % p.passes) * Gm;     // first query head of the row
+        const int g = (hgrp / p.passes) * HG + hw;               // this wave's KV head
+        const int h0 = g * p.G_all + (hgrp % p.passes) * Gm;     // its first query head in the row
 
         // Q^T operands: head h0 + 16 nb + lane % 16 (zero past Gm), dims 32 s + 8 lg.
         bf16x8_t qf[NB][NS];
@@ -223,13 +233,13 @@ __global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void decode_mfma_kernel(const
                 else return (uint64_t)(uint32_t)min(j, last) * v_sl;
             };
             // This wave's tiles: wv, wv + NWM, ...; k counts them.
-            const int ntw = ntiles > wv ? (ntiles - wv + NWM - 1) / NWM : 0;
+            const int ntw = ntiles > wt ? (ntiles - wt + NWT - 1) / NWT : 0;
             // The phases below are kept in program order (sched_barrier):
             // hoisting a tile's loads above the previous compute would hold
             // three tiles in registers.
             auto issue = [&](int k, MTile<D> &t) {
                 __builtin_amdgcn_sched_barrier(0);
-                const int base = jb + (wv + NWM * k) * BKM;
+                const int base = jb + (wt + NWT * k) * BKM;
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
                     const uint16_t *kr = kbase + koff(base + 16 * kb + g16) + 8 * lg;
@@ -270,7 +280,7 @@ __global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void decode_mfma_kernel(const
             };
             auto compute = [&](int k, const MTile<D> &t) {
                 __builtin_amdgcn_sched_barrier(0);
-                const int tbase = jb + (wv + NWM * k) * BKM;
+                const int tbase = jb + (wt + NWT * k) * BKM;
                 // S^T blocks: keys 16 kb + 4 lg + i, head 16 nb + g16.
                 f32x4_t st[NB][2];
 #pragma unroll
@@ -356,46 +366,63 @@ __global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void decode_mfma_kernel(const
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) lsum[nb] = sum_over_rows(lsum[nb]);
 
-        // Merge the waves' states: each leaves (reference, sum, O^T) in LDS,
-        // then wave wv merges the 16-dim blocks m with m % NWM == wv.
-        __syncthreads();   // every wave is done with its V^T tile
+        // With several waves on a head, merge their states: each leaves
+        // (reference, sum, O^T) in LDS, then wave wv merges the 16-dim blocks
+        // m with m % NWT == wt over the waves hw, hw + HG, ...
+        if constexpr (NWT > 1) {
+            __syncthreads();   // every wave is done with its V^T tile
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            float *mine = xch + ((wv * NB + nb) * F) * 64 + lane;
-            mine[0] = mref[nb];
-            mine[64] = lsum[nb];
+            for (int nb = 0; nb < NB; ++nb) {
+                float *mine = xch + ((wv * NB + nb) * F) * 64 + lane;
+                mine[0] = mref[nb];
+                mine[64] = lsum[nb];
 #pragma unroll
-            for (int m = 0; m < NM; ++m)
+                for (int m = 0; m < NM; ++m)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) mine[(2 + 4 * m + i) * 64] = oacc[nb][m][i];
+                    for (int i = 0; i < 4; ++i) mine[(2 + 4 * m + i) * 64] = oacc[nb][m][i];
+            }
+            __syncthreads();
         }
-        __syncthreads();
         const bool direct = p.direct && lo == 0 && hi == n;
         const int64_t slot = (int64_t)r + w;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            const int hl = 16 * nb + g16;   // this lane's query head in the row
-            float M = -INFINITY;
+            const int hl = 16 * nb + g16;   // this lane's query head of the wave's KV head
+            float M, L;
+            float fv[NWT];
+            if constexpr (NWT > 1) {
+                M = -INFINITY;
 #pragma unroll
-            for (int v = 0; v < NWM; ++v) M = fmaxf(M, xch[((v * NB + nb) * F) * 64 + lane]);
-            float fv[NWM], L = 0.f;
+                for (int t = 0; t < NWT; ++t) M = fmaxf(M, xch[(((hw + HG * t) * NB + nb) * F) * 64 + lane]);
+                L = 0.f;
 #pragma unroll
-            for (int v = 0; v < NWM; ++v) {
-                const float mv = xch[((v * NB + nb) * F) * 64 + lane];
-                fv[v] = mv == -INFINITY ? 0.f : exp2_fast(mv - M);
-                L += fv[v] * xch[((v * NB + nb) * F + 1) * 64 + lane];
+                for (int t = 0; t < NWT; ++t) {
+                    const int v = hw + HG * t;
+                    const float mv = xch[((v * NB + nb) * F) * 64 + lane];
+                    fv[t] = mv == -INFINITY ? 0.f : exp2_fast(mv - M);
+                    L += fv[t] * xch[((v * NB + nb) * F + 1) * 64 + lane];
+                }
+            } else {
+                M = mref[nb];
+                L = lsum[nb];
             }
             const float inv = L > 0.f ? 1.f / L : 0.f;
+            const int64_t prow = slot * HPR + hw * Gm + hl;   // partial row of this head
 #pragma unroll
             for (int m = 0; m < NM; ++m) {
-                if (m % NWM != wv) continue;
+                if (m % NWT != wt) continue;
                 float ov[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    float acc = 0.f;
+                    if constexpr (NWT > 1) {
+                        float acc = 0.f;
 #pragma unroll
-                    for (int v = 0; v < NWM; ++v) acc += fv[v] * xch[((v * NB + nb) * F + 2 + 4 * m + i) * 64 + lane];
-                    ov[i] = acc;
+                        for (int t = 0; t < NWT; ++t)
+                            acc += fv[t] * xch[(((hw + HG * t) * NB + nb) * F + 2 + 4 * m + i) * 64 + lane];
+                        ov[i] = acc;
+                    } else {
+                        ov[i] = oacc[nb][m][i];
+                    }
                 }
                 if (hl >= Gm) continue;
                 const int d0 = 16 * m + 4 * lg;
@@ -405,22 +432,29 @@ __global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void decode_mfma_kernel(const
                     v.y = pack_bf16(ov[2] * inv, ov[3] * inv);
                     *reinterpret_cast<uint2 *>(p.o + b * p.o_sb + (int64_t)(h0 + hl) * p.o_sh + d0) = v;
                 } else {
-                    const int64_t prow = slot * Gm + hl;
                     *reinterpret_cast<float4 *>(p.o_part + prow * D + d0) = make_float4(ov[0], ov[1], ov[2], ov[3]);
                 }
             }
-            if (!direct && hl < Gm && wv == 0 && lg == 0)
-                *reinterpret_cast<float2 *>(p.ml_part + (slot * Gm + hl) * 2) = make_float2(partial_m(M, L), L);
+            if (!direct && hl < Gm && wt == 0 && lg == 0)
+                *reinterpret_cast<float2 *>(p.ml_part + prow * 2) = make_float2(partial_m(M, L), L);
         }
     }
 }
 
-template <int D, int MODE>
-hipError_t launch_mfma_d(const DecodeParams &p, hipStream_t stream) {
-    if (p.NB == 1) hipLaunchKernelGGL((decode_mfma_kernel<D, 1, MODE>), dim3(p.W), dim3(64 * NWM), 0, stream, p);
-    else if (p.NB == 2) hipLaunchKernelGGL((decode_mfma_kernel<D, 2, MODE>), dim3(p.W), dim3(64 * NWM), 0, stream, p);
+template <int D, int MODE, int HG>
+hipError_t launch_mfma_hg(const DecodeParams &p, hipStream_t stream) {
+    if (p.NB == 1) hipLaunchKernelGGL((decode_mfma_kernel<D, 1, MODE, HG>), dim3(p.W), dim3(64 * NWM), 0, stream, p);
+    else if (p.NB == 2) hipLaunchKernelGGL((decode_mfma_kernel<D, 2, MODE, HG>), dim3(p.W), dim3(64 * NWM), 0, stream, p);
     else return hipErrorInvalidValue;
     return hipGetLastError();
+}
+
+template <int D, int MODE>
+hipError_t launch_mfma_d(const DecodeParams &p, hipStream_t stream) {
+    if (p.HW == 1) return launch_mfma_hg<D, MODE, 1>(p, stream);
+    if (p.HW == 2) return launch_mfma_hg<D, MODE, 2>(p, stream);
+    if (p.HW == 4) return launch_mfma_hg<D, MODE, 4>(p, stream);
+    return hipErrorInvalidValue;
 }
 
 template <int D>

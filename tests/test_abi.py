@@ -243,7 +243,9 @@ def test_planner_counts_one_row_per_pass_for_other_group_sizes():
     # (sequence, KV head), four-wave slices of >= 256 tokens
     assert pa.attn_plan_splits(2, 1, 32, 128, 640, 16, 128, 256) == 2 * 640 // 256
     assert pa.attn_plan_splits(2, 1, 64, 128, 640, 16, 128, 256) == 2 * 2 * 640 // 256   # two passes of 32
-    assert pa.attn_plan_splits(1, 2, 3, 128, 640, 16, 128, 256) == 2 * 640 // 256
+    # G = 3 over 2 KV heads: one pass, so both KV heads share a row (a wave
+    # each): one row of 640 tokens, slices of >= 256 tokens
+    assert pa.attn_plan_splits(1, 2, 3, 128, 640, 16, 128, 256) == (640 + 255) // 256
     # D = 256 keeps the VALU kernel: G = 32 is four passes of 8 (one-wave
     # slices of >= 64 tokens), G = 3 three passes of one head (four-wave)
     assert pa.attn_plan_splits(2, 1, 32, 256, 640, 16, 256, 256) == 2 * 4 * 640 // 64

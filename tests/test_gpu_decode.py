@@ -133,7 +133,7 @@ def partition_bounds(lens, rows_per_seq, W):
 @pytest.mark.parametrize("B,Hkv,G,layout,W", [
     (32, 8, 4, "page_slot_head", 0),     # config 3 B = 32, planner slices: eight KV heads per row
     (5, 2, 4, "page_head_slot", 23),     # one KV head per row
-    (5, 2, 8, "page_slot_head", 23),     # MFMA rows: one KV head and its 8 query heads per row
+    (5, 2, 8, "page_slot_head", 23),     # MFMA rows: both KV heads (a wave each), 16 query heads per row
 ])
 def test_split_pieces_match_oracle_partials(B, Hkv, G, layout, W):
     """Each piece the split kernel leaves in the workspace (read through the
@@ -146,7 +146,10 @@ def test_split_pieces_match_oracle_partials(B, Hkv, G, layout, W):
     else:
         case = workloads.paged_decode_case(120, B, Hq, Hkv, D, [1, 700, 0, 2500, 65], 16, layout=layout)
     lens = case["kv_lens"].tolist()
-    hw = Hkv if layout == "page_slot_head" and G in (1, 2, 4) else 1
+    if G in (1, 2, 4):
+        hw = Hkv if layout == "page_slot_head" else 1    # KV heads per row, VALU kernel
+    else:
+        hw = 4 if Hkv % 4 == 0 else 2 if Hkv % 2 == 0 else 1   # MFMA kernel, one pass
     W = W or pa.attn_plan_splits(B, Hkv, G, D, case["max_kv_len"], 16, case["k_pool"].stride(2))
     d = to_dev(case, ["q", "k_pool", "v_pool", "block_table", "kv_lens"])
     nbytes = pa.attn_decode_workspace_bytes(B, Hq, D, W)
