@@ -392,7 +392,7 @@ def run_counters(torch, pa, dev, workload, num_splits):
                                        s["page_size"], s["scale"], S, ws)
             torch.cuda.synchronize()
             per_launch.append(decode_bytes(s))
-        kernel = "decode_split_kernel, %d slices" % S
+        kernel = "decode split kernel (attn_paged_decode_split), %d slices" % S
     src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
