@@ -61,7 +61,7 @@ def parse():
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--counters", action="store_true",
                     help="untimed: one decode split-kernel launch per rotated input set (paged workloads; the "
-                         "whole call for contig_b16) and 3 copies of 1 GiB, for rocprofv3 --pmc")
+                         "whole call for contig_b16 and swa_fp8) and 3 copies of 1 GiB, for rocprofv3 --pmc")
     return ap.parse_args()
 
 
@@ -377,6 +377,18 @@ def run_counters(torch, pa, dev, workload, num_splits):
             per_launch.append(nb)
             del c
         kernel = "decode_split_kernel (contiguous, one KV head per row) of attn_decode"
+    elif workload == "swa_fp8":
+        per = swa_bytes(workloads.swa_fp8(device=dev))
+        R = min(32, max(2, math.ceil(6.0e8 / per)))
+        for r in range(R):
+            c = workloads.swa_fp8(device=dev, seed=1006 + 7919 * r)
+            out = torch.empty_like(c["q"])
+            pa.attn_swa_fp8_decode(c["q"], c["cache"], c["inv_scale"], c["indices"], c["lens"], out,
+                                   c["block_size"], c["scale"])
+            torch.cuda.synchronize()
+            per_launch.append(swa_bytes(c))
+            del c
+        kernel = "swa_kernel of attn_swa_fp8_decode"
     else:
         probe_set = make_sets(workload, dev, 1)
         R = rotation_count(decode_bytes(probe_set[0]))

@@ -851,6 +851,7 @@ int attn_swa_fp8_decode(const void *q, int64_t q_st, int64_t q_sh,
     p.slots = num_blocks * block_size;
     p.bs_div = pa::make_divu32((uint32_t)block_size);
     p.sl2 = scale * 1.4426950408889634f;
+    p.o16 = (((uintptr_t)o & 15u) == 0 && (o_st & 7) == 0 && (o_sh & 7) == 0) ? 1 : 0;
     return launch_status(pa::launch_swa(p, static_cast<hipStream_t>(stream)), "swa kernel");
 }
 

@@ -340,9 +340,10 @@ __global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void decode_mfma_kernel(const
 
             // Two tiles in flight at every wait: tile k + 1 is issued before
             // tile k is staged, tile k + 2 as soon as tile k is computed.
-            // Every issue in the loop is unconditional (past the end it
-            // repeats the last tile, never used): a load issued under a
-            // condition would make the compiler wait for all of them.
+            // Every issue in the loop is unconditional: a load issued under
+            // a condition would make the compiler wait for all of them.
+            // Past the end every key is clamped to the piece's last one, so
+            // such a tile reads one key row (never used).
             if (ntw > 0) {
                 MTile<D> ra, rb;
                 issue(0, ra);
@@ -351,7 +352,7 @@ __global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void decode_mfma_kernel(const
                     issue(k + 1, rb);
                     stage(ra);
                     compute(k, ra);
-                    issue(min(k + 2, ntw - 1), ra);
+                    issue(k + 2, ra);
                     stage(rb);
                     compute(k + 1, rb);
                 }

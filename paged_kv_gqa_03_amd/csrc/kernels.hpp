@@ -145,6 +145,7 @@ struct SwaParams {
     int slots;            // num_blocks * bs: indices at or above it are not admitted
     DivU32 bs_div;        // slot -> (block, offset): exact division by bs
     float sl2;            // scale * log2(e)
+    int o16;              // output rows 16-byte aligned: 16-byte stores
 };
 
 // Paged KV append: packed new rows [N, Hkv, D] into their (page, slot).

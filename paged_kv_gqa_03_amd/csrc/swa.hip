@@ -10,8 +10,12 @@
 // both keys and values.
 //
 // Work decomposition (cf. the CuTeDSL stub's plan: one CTA per (token, group
-// of 16 query heads), KV streamed in tiles): one 256-thread workgroup per
-// (16-head group, token).  Per tile of up to 128 window positions:
+// of 16 query heads), KV streamed in tiles): one workgroup per token and
+// GPW adjacent 16-head groups (GPW = 2 when the group count is even, else
+// 1), four waves per group.  The groups of a workgroup share one staged copy
+// of the token's rows, which halves the row traffic from L2 (a token's
+// groups otherwise each gather the same rows).  Per tile of up to 128
+// window positions:
 //   1. the rows (fp8, 512 B each) and inverse scales are staged in LDS in
 //      two dependent load steps (indices, then rows and scales, all issued
 //      before any LDS store); masked positions become zero rows;
@@ -37,6 +41,7 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int HD = 512;
 constexpr int KT = 128;        // window positions per tile
@@ -75,20 +80,26 @@ __device__ __forceinline__ void transpose4x4(uint32_t w0, uint32_t w1, uint32_t 
     out[3] = perm(b23, b01, 0x07060302u);  // b3
 }
 
-__global__ __launch_bounds__(256, 2) void swa_kernel(const SwaParams p) {
+template <int GPW>
+__global__ __launch_bounds__(256 * GPW, GPW == 1 ? 2 : 1) void swa_kernel(const SwaParams p) {
+    constexpr int NTH = 256 * GPW;        // threads
+    constexpr int RPT = KT * 32 / NTH;    // staged 16-byte row chunks per thread
     __shared__ __attribute__((aligned(16))) uint8_t x_lds[KT * XLD];
     __shared__ int32_t admit[KT];   // window position admitted (1) or masked (0)
     __shared__ float inv_lds[KT];
-    __shared__ __attribute__((aligned(16))) uint16_t p_lds[16 * PLD];
-    __shared__ float red_max[4][16], red_sum[4][16];
+    __shared__ __attribute__((aligned(16))) uint16_t p_lds_all[GPW][16 * PLD];
+    __shared__ float red_max_all[GPW][4][16], red_sum_all[GPW][4][16];
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, w = (tid >> 6) & 3, gs = tid >> 8;
     const int r = lane & 15, q4 = lane >> 4;
-    // Workgroup (token t, head group g) at t * (NH / 16) + g: the groups of a
-    // token are adjacent.
-    const int ngrp = p.NH >> 4;
-    const int t = (int)(blockIdx.x / (unsigned)ngrp);
-    const int head = (int)(blockIdx.x - (unsigned)t * (unsigned)ngrp) * 16 + r;
+    uint16_t *p_lds = p_lds_all[gs];
+    float(*red_max)[16] = red_max_all[gs];
+    float(*red_sum)[16] = red_sum_all[gs];
+    // Workgroup (token t, head groups GPW c .. GPW c + GPW - 1) at
+    // t * (NH / 16 / GPW) + c: the workgroups of a token are adjacent.
+    const int nwg = (p.NH >> 4) / GPW;
+    const int t = (int)(blockIdx.x / (unsigned)nwg);
+    const int head = ((int)(blockIdx.x - (unsigned)t * (unsigned)nwg) * GPW + gs) * 16 + r;
     int64_t len = p.lens[t];
     len = len < 0 ? 0 : (len > p.W ? p.W : len);
 
@@ -116,23 +127,24 @@ __global__ __launch_bounds__(256, 2) void swa_kernel(const SwaParams p) {
         const int nkb = (nk + 31) >> 5;   // 32-position blocks in this tile
         __syncthreads();                  // the previous tile is fully consumed
         // Staging with two dependent steps: every thread first loads the
-        // window indices of its 16 rows (keys (tid >> 5) + 8i, chunk tid & 31)
-        // and, below 128, of key tid (for the scale); then all row chunks and
-        // scales go out together, and only then are they stored to LDS.
+        // window indices of its RPT rows (keys (tid >> 5) + (NTH / 32) i,
+        // chunk tid & 31) and, below 128, of key tid (for the scale); then all
+        // row chunks and scales go out together, and only then are they
+        // stored to LDS.
         {
             const int64_t *irow = p.ind + (int64_t)t * p.i_st + j0;
             const int ch = tid & 31;
-            int64_t idx[16];
+            int64_t idx[RPT];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int key = (tid >> 5) + 8 * i;
+            for (int i = 0; i < RPT; ++i) {
+                const int key = (tid >> 5) + (NTH / 32) * i;
                 idx[i] = key < nk ? irow[key] : -1;
             }
             const int64_t idx_s = tid < nk ? irow[tid] : -1;
             if (tile == 0) load_q();
-            uint4 v[16];
+            uint4 v[RPT];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
+            for (int i = 0; i < RPT; ++i) {
                 v[i] = make_uint4(0u, 0u, 0u, 0u);
                 if (idx[i] >= 0 && idx[i] < p.slots) {
                     const uint32_t blk = divu32((uint32_t)idx[i], p.bs_div);
@@ -144,8 +156,8 @@ __global__ __launch_bounds__(256, 2) void swa_kernel(const SwaParams p) {
             const bool ok_s = idx_s >= 0 && idx_s < p.slots;
             const float inv = ok_s ? bf16_lo((uint32_t)p.inv_scale[idx_s * p.s_ss]) : 0.f;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int key = (tid >> 5) + 8 * i;
+            for (int i = 0; i < RPT; ++i) {
+                const int key = (tid >> 5) + (NTH / 32) * i;
                 if (key < nkb * 32) *reinterpret_cast<uint4 *>(&x_lds[key * XLD + ch * 16]) = v[i];
             }
             if (tid < KT) {
@@ -241,25 +253,40 @@ __global__ __launch_bounds__(256, 2) void swa_kernel(const SwaParams p) {
 
     const float invL = L > 0.f ? 1.f / L : 0.f;
     uint16_t *orow = p.o + (int64_t)t * p.o_st + (int64_t)head * p.o_sh;
+    // Lane (r, q4) holds dims 64 mb + 16 q4 + 4 i + mm of head r: 16
+    // consecutive dims (32 bytes) per block mb = 2 w + a.  The output is not
+    // read again here: non-temporal stores, 16 bytes each when the rows are
+    // 16-byte aligned (8-byte pieces were written back to HBM as about 1.8x
+    // the output's bytes).
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < 2; ++a) {
+        uint32_t pk[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int d0 = 64 * (2 * w + a) + 16 * q4 + 4 * i;
-            uint2 v;
-            v.x = pack_bf16(oacc[a][0][i] * invL, oacc[a][1][i] * invL);
-            v.y = pack_bf16(oacc[a][2][i] * invL, oacc[a][3][i] * invL);
-            // The output is not read again here: a non-temporal store
-            // (measured about 5% faster per call than a plain one).
-            __builtin_nontemporal_store(u32x2{v.x, v.y}, reinterpret_cast<u32x2 *>(orow + d0));
+            pk[2 * i] = pack_bf16(oacc[a][0][i] * invL, oacc[a][1][i] * invL);
+            pk[2 * i + 1] = pack_bf16(oacc[a][2][i] * invL, oacc[a][3][i] * invL);
         }
+        uint16_t *dst = orow + 64 * (2 * w + a) + 16 * q4;
+        if (p.o16) {
+            __builtin_nontemporal_store(u32x4{pk[0], pk[1], pk[2], pk[3]}, reinterpret_cast<u32x4 *>(dst));
+            __builtin_nontemporal_store(u32x4{pk[4], pk[5], pk[6], pk[7]}, reinterpret_cast<u32x4 *>(dst + 8));
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                __builtin_nontemporal_store(u32x2{pk[2 * i], pk[2 * i + 1]}, reinterpret_cast<u32x2 *>(dst + 4 * i));
+        }
+    }
 }
 
 }  // namespace
 
 hipError_t launch_swa(const SwaParams &p, hipStream_t stream) {
     if (p.T <= 0) return hipSuccess;
-    hipLaunchKernelGGL(swa_kernel, dim3((unsigned)p.T * (unsigned)(p.NH / 16)), dim3(256), 0, stream, p);
+    const unsigned ngrp = (unsigned)(p.NH / 16);
+    if (ngrp % 2 == 0)
+        hipLaunchKernelGGL(swa_kernel<2>, dim3((unsigned)p.T * (ngrp / 2)), dim3(512), 0, stream, p);
+    else
+        hipLaunchKernelGGL(swa_kernel<1>, dim3((unsigned)p.T * ngrp), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 

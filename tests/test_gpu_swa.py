@@ -112,6 +112,23 @@ def test_swa_strided_query_and_output():
     assert torch.equal(obig[:, 49].cpu(), torch.zeros(5, 512, dtype=torch.bfloat16))
 
 
+@pytest.mark.parametrize("NH", [32, 48])
+def test_swa_output_rows_only_8_byte_aligned(NH):
+    """An output that starts 8 bytes past a 16-byte boundary takes the
+    kernel's 8-byte stores; two head groups per workgroup (NH = 32) and one
+    (NH = 48, an odd group count)."""
+    case = workloads.swa_case(435 + NH, 5, NH, 512, 128, 256, 4, len_range=(1, 128))
+    d = {k: case[k].to(DEV) for k in ("q", "cache", "inv_scale", "indices", "lens")}
+    flat = torch.zeros(5 * NH * 512 + 8, dtype=torch.bfloat16, device=DEV)
+    out = flat[4:4 + 5 * NH * 512].view(5, NH, 512)
+    assert out.data_ptr() % 16 == 8
+    pa.attn_swa_fp8_decode(d["q"], d["cache"], d["inv_scale"], d["indices"], d["lens"], out, 256, case["scale"])
+    torch.cuda.synchronize()
+    assert_close(out, oracle_swa(case), what="NH=%d" % NH)
+    assert torch.equal(flat[:4].cpu(), torch.zeros(4, dtype=torch.bfloat16))
+    assert torch.equal(flat[4 + 5 * NH * 512:].cpu(), torch.zeros(4, dtype=torch.bfloat16))
+
+
 def test_swa_matches_fallback_rounding_within_tolerance():
     """The fallback rounds the dequantised rows to bf16; the exact-product
     result the kernel computes stays within the same tolerance of it."""
