@@ -532,6 +532,13 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeCombine
     const int item = blockIdx.x * 4 + wave_id();
     if (item >= p.B * p.Hq) return;
     const int b = item / p.Hq, hq = item - b * p.Hq;
+    const int hwg = p.Hq / p.ngrp;                 // query heads per row
+    const int r = b * p.ngrp + hq / hwg;           // this head's row
+    // The length and the row's slice range are loaded together (the range
+    // is read even for an empty row; the split kernel leaves it unwritten
+    // then, and it is not used).
+    int2 rg = make_int2(0, 0);
+    if (p.W > 1) rg = *reinterpret_cast<const int2 *>(p.ranges + 2 * (int64_t)r);
     const int n = p.kv_lens ? p.kv_lens[b] : p.kv_len_const;
     uint16_t *dst = p.o + (int64_t)b * p.o_sb + (int64_t)hq * p.o_sh + lane * NC;
     if (n == 0) {   // no keys: the row is zero
@@ -541,17 +548,10 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeCombine
         if (holds) store_row_bf16<NC>(dst, zero, 0.f);
         return;
     }
-    const int hwg = p.Hq / p.ngrp;                 // query heads per row
-    const int r = b * p.ngrp + hq / hwg;           // this head's row
     // The waves that held the row's first and last keys (recorded by the
     // split kernel); with a single slice the row was written directly.
     if (p.W == 1 && p.direct_single) return;
-    int w0 = 0, w1 = 0;
-    if (p.W > 1) {
-        const int2 rg = *reinterpret_cast<const int2 *>(p.ranges + 2 * (int64_t)r);
-        w0 = rg.x;
-        w1 = rg.y;
-    }
+    const int w0 = rg.x, w1 = rg.y;
     if (w0 == w1 && p.direct_single) return;   // written directly by the split kernel
     float acc[NC], L, M;
     merge_partials<D>(p.o_part, p.ml_part, ((int64_t)r + w0) * hwg + hq % hwg, hwg, w1 - w0 + 1, lane, acc, L, M);
