@@ -151,6 +151,31 @@ def time_calls(torch, fn, sets, steps, warmup):
     return start.elapsed_time(end) / steps  # ms per call
 
 
+def time_graph(torch, fn, sets, steps, warmup, replays=3):
+    """ms per call when `steps` calls are captured once in a HIP graph and the
+    graph is replayed: the GPU's own time per call, without the host's cost
+    of issuing each call from Python (as a serving loop that replays graphs
+    would see it)."""
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        for i in range(warmup):
+            fn(sets[i % len(sets)])
+    st.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=st):
+        for i in range(steps):
+            fn(sets[i % len(sets)])
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (replays * steps)
+
+
 def probe_ceiling(torch, pa, dev, nbytes, steps=20):
     """Pure-read streaming ceiling at nbytes per launch: attn_hbm_read_probe
     over rotated buffers of nbytes (cold, as the decode inputs), one, two and
@@ -445,24 +470,7 @@ def bench_cache_ops(torch, pa, dev, steps, warm):
         # These kernels take a few microseconds, less than the host needs to
         # issue a call from Python, so the calls are captured once in a HIP
         # graph and the graph is replayed (as a serving loop would issue them).
-        st = torch.cuda.Stream()
-        with torch.cuda.stream(st):
-            for i in range(warm):
-                fn(sets[i % len(sets)])
-        st.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=st):
-            for i in range(steps):
-                fn(sets[i % len(sets)])
-        graph.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(3):
-            graph.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / (3 * steps)
+        ms = time_graph(torch, fn, sets, steps, warm)
         return {"us_per_call": round(ms * 1e3, 2), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
                 "hbm_peak_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "bytes_per_call": int(nbytes),
                 "rotation_sets": len(sets), "timing": "HIP graph of %d calls, 3 replays" % steps}
@@ -629,9 +637,13 @@ def bench_swa(torch, pa, dev, steps, warm):
         pa.attn_swa_fp8_decode(s["q"], s["cache"], s["inv_scale"], s["indices"], s["lens"], s["out"],
                                s["block_size"], s["scale"])
     ms = time_calls(torch, call, sets, steps, warm)
+    msg = time_graph(torch, call, sets, steps, warm)
     nb = sum(swa_bytes(sets[i % R]) for i in range(steps)) / steps
     gbs = nb / (ms * 1e-3) / 1e9
     return {"us_per_call": round(ms * 1e3, 2), "GB/s": round(gbs, 1), "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "us_per_call_graph": round(msg * 1e3, 2), "hbm_peak_frac_graph": round(nb / (msg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "timing": "us_per_call: calls issued back to back from Python (the host's issue time per call is "
+                      "close to the kernel's); us_per_call_graph: the same calls replayed from a HIP graph",
             "bytes_per_call": int(nb), "rotation_sets": R}
 
 

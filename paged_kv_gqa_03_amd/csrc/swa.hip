@@ -119,8 +119,19 @@ __global__ __launch_bounds__(256 * GPW, GPW == 1 ? 2 : 1) void swa_kernel(const 
         for (int m = 0; m < 4; ++m) oacc[a][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float M = -INFINITY, L = 0.f;
 
+    // The first tile's window indices and Q go out with the token length:
+    // positions below the window exist in the index row whatever the
+    // length (those at or past it are dropped below).
+    int64_t idx0[RPT], idx0_s = -1;
+    if (p.W > 0) {
+        const int64_t *irow = p.ind + (int64_t)t * p.i_st;
+        const int wl = p.W - 1;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) idx0[i] = irow[min((tid >> 5) + (NTH / 32) * i, wl)];
+        idx0_s = irow[min(tid, wl)];
+    }
+    load_q();
     const int ntile = (int)((len + KT - 1) / KT);
-    if (ntile == 0) load_q();
     for (int tile = 0; tile < ntile; ++tile) {
         const int j0 = tile * KT;
         const int nk = (int)min((int64_t)KT, len - j0);
@@ -138,10 +149,9 @@ __global__ __launch_bounds__(256 * GPW, GPW == 1 ? 2 : 1) void swa_kernel(const 
 #pragma unroll
             for (int i = 0; i < RPT; ++i) {
                 const int key = (tid >> 5) + (NTH / 32) * i;
-                idx[i] = key < nk ? irow[key] : -1;
+                idx[i] = key < nk ? (tile == 0 ? idx0[i] : irow[key]) : -1;
             }
-            const int64_t idx_s = tid < nk ? irow[tid] : -1;
-            if (tile == 0) load_q();
+            const int64_t idx_s = tid < nk ? (tile == 0 ? idx0_s : irow[tid]) : -1;
             uint4 v[RPT];
 #pragma unroll
             for (int i = 0; i < RPT; ++i) {
