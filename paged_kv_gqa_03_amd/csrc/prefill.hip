@@ -167,14 +167,18 @@ __device__ __forceinline__ void load_stage(const PrefillParams &p, const StageCt
 // 8(t & 7) .. +8 of mask rows (t >> 3) + 32 q (q < NQ) of the tile's 64 keys,
 // and stores them as 8 bits, so LDS holds 64 bits per mask row.  A 3-D mask
 // has one row per query row of the work-map tile, a 2-D mask one row.
-// Loading only issues loads; the bytes are assembled when the stage is
-// stored (a tile's compute later), so no wait for them sits between the
-// tile's K/V loads and the next compute.
+// With one mask row per thread (NQ = 1) loading only issues loads, and the
+// bytes are assembled when the stage is stored (a tile's compute later), so
+// no wait for them sits between the tile's K/V loads and the next compute.
+// With several rows per thread the three raw words per row would cost too
+// many registers across the compute, so the bytes are assembled at once.
 template <int MASK, int NQ>
 struct MaskStage {
-    uint32_t w[NQ][3];     // the aligned dwords that hold the eight bytes
-    uint32_t sh[NQ];       // byte offset of the first byte in w[q][0]
-    int keep[NQ];          // bytes of the eight that exist (0 past the row's end or rows)
+    static constexpr bool kDefer = NQ == 1;
+    uint32_t w[NQ][kDefer ? 3 : 2];   // deferred: the aligned dwords holding the eight bytes;
+                                      // else the eight bytes, zero past the row's end
+    uint32_t meta[NQ];                // deferred: bits 0-3 bytes that exist, bits 4-5 the
+                                      // offset of the first byte in w[q][0]
 };
 
 struct MaskCtx {
@@ -186,25 +190,45 @@ struct MaskCtx {
 // Bytes [j, j + 8) of mask row `row`; bytes at or past key n count as 0, and
 // rows past `rows` as all 0.  Mask rows may start at any byte.  Every load
 // reads an aligned dword that holds at least one byte of the row below key
-// n (a dword past that is replaced by the one holding byte n - 1, a row past
-// `rows` by the last row), so no read can cross into another page; the
-// loads are unconditional, which keeps the compiler from waiting on them.
+// n, so no read can cross into another page.  Deferred (one row per
+// thread), the loads are unconditional (a dword past byte n - 1 is replaced
+// by the one holding it, a row past `rows` by the last row), which keeps the
+// compiler from waiting on them.
 template <int MASK, int NQ>
 __device__ __forceinline__ void load_mask(const MaskCtx &mc, int tid, int n, int kt, MaskStage<MASK, NQ> &m) {
     const int j = kt * BK + 8 * (tid & 7);
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
         const int row = (tid >> 3) + 32 * q;
-        const uint8_t *rp = mc.base + (int64_t)min(row, mc.rows - 1) * mc.m_sq;
-        // Offsets from rp (kept as offsets so the loads stay global ones):
-        // the aligned dword holding byte j, and the one holding byte n - 1.
-        const uint32_t sh = (uint32_t)reinterpret_cast<uintptr_t>(rp + j) & 3u;
-        const int o0 = j - (int)sh;
-        const int ol = (n - 1) - (int)((uint32_t)reinterpret_cast<uintptr_t>(rp + (n - 1)) & 3u);
-        m.sh[q] = sh;
+        if constexpr (MaskStage<MASK, NQ>::kDefer) {
+            const uint8_t *rp = mc.base + (int64_t)min(row, mc.rows - 1) * mc.m_sq;
+            // Offsets from rp (kept as offsets so the loads stay global
+            // ones): the aligned dword holding byte j, and the one holding
+            // byte n - 1.
+            const uint32_t sh = (uint32_t)reinterpret_cast<uintptr_t>(rp + j) & 3u;
+            const int o0 = j - (int)sh;
+            const int ol = (n - 1) - (int)((uint32_t)reinterpret_cast<uintptr_t>(rp + (n - 1)) & 3u);
 #pragma unroll
-        for (int k = 0; k < 3; ++k) m.w[q][k] = *reinterpret_cast<const uint32_t *>(rp + min(o0 + 4 * k, ol));
-        m.keep[q] = row < mc.rows ? max(0, min(8, n - j)) : 0;
+            for (int k = 0; k < 3; ++k) m.w[q][k] = *reinterpret_cast<const uint32_t *>(rp + min(o0 + 4 * k, ol));
+            m.meta[q] = (uint32_t)(row < mc.rows ? max(0, min(8, n - j)) : 0) | (sh << 4);
+        } else {
+            // Several rows per thread: the two or three dwords (or, at the
+            // row's end, the bytes below n) are read and joined at once.
+            m.w[q][0] = m.w[q][1] = 0u;
+            if (row < mc.rows) {
+                const uint8_t *mp = mc.base + row * mc.m_sq + j;
+                if (j + 8 <= n) {
+                    const uint32_t sh = (uint32_t)reinterpret_cast<uintptr_t>(mp) & 3u;
+                    const uint32_t *wp = reinterpret_cast<const uint32_t *>(mp - sh);
+                    const uint32_t w0 = wp[0], w1 = wp[1];
+                    const uint32_t w2 = sh ? wp[2] : 0u;
+                    m.w[q][0] = __builtin_amdgcn_alignbyte(w1, w0, sh);
+                    m.w[q][1] = __builtin_amdgcn_alignbyte(w2, w1, sh);
+                } else {
+                    for (int i = 0; i < 8 && j + i < n; ++i) m.w[q][i >> 2] |= (uint32_t)mp[i] << (8 * (i & 3));
+                }
+            }
+        }
     }
 }
 
@@ -222,10 +246,15 @@ __device__ __forceinline__ void store_mask(const MaskStage<MASK, NQ> &m, int tid
     for (int q = 0; q < NQ; ++q) {
         const int row = (tid >> 3) + 32 * q;
         if (row < ROWS) {
-            const uint32_t lo = __builtin_amdgcn_alignbyte(m.w[q][1], m.w[q][0], m.sh[q]);
-            const uint32_t hi = __builtin_amdgcn_alignbyte(m.w[q][2], m.w[q][1], m.sh[q]);
-            const uint32_t b = nz_bits4(lo) | (nz_bits4(hi) << 4);
-            bits[row * 8 + (tid & 7)] = (uint8_t)(b & ((1u << m.keep[q]) - 1u));
+            if constexpr (MaskStage<MASK, NQ>::kDefer) {
+                const uint32_t sh = m.meta[q] >> 4, keep = m.meta[q] & 15u;
+                const uint32_t lo = __builtin_amdgcn_alignbyte(m.w[q][1], m.w[q][0], sh);
+                const uint32_t hi = __builtin_amdgcn_alignbyte(m.w[q][2], m.w[q][1], sh);
+                const uint32_t b = nz_bits4(lo) | (nz_bits4(hi) << 4);
+                bits[row * 8 + (tid & 7)] = (uint8_t)(b & ((1u << keep) - 1u));
+            } else {
+                bits[row * 8 + (tid & 7)] = (uint8_t)(nz_bits4(m.w[q][0]) | (nz_bits4(m.w[q][1]) << 4));
+            }
         }
     }
 }
