@@ -71,19 +71,26 @@ int attn_version(void);
  * Decode work partition (AstrAI csrc commit history: the commit that
  * partitions KV across gridDim.z and sizes the split count to fill the
  * device, and the later one that retargets it at a fixed total block count
- * after a grid search).  Decode runs one wave per slice of a balanced
- * partition: the rows (sequence, group of adjacent KV heads) are laid end to
- * end and the line of all their tokens is cut into `num_splits` = W equal
- * slices, whatever the spread of kv_lens.  A row is a group of up to 8 KV
- * heads (4 at D = 256) when the KV head stride `kv_s_head` equals D (heads
- * of a token contiguous), else one head; when G is not 1, 2, 4 or 8 a row is
- * one KV head and one pass over a power-of-two share of its G query heads
- * (see attn_decode).  This planner returns W for `num_cus`
- * compute units (0 = query the current device): about three waves per unit
- * when a wave streams eight KV heads (kv_s_head == D, Hkv >= 8), two otherwise,
- * and no slice shorter than 64 tokens of a row given max_kv_len.  page_size
- * 0 stands for a contiguous source (pass its K head stride as kv_s_head).
- * Host-only and deterministic; returns W >= 1, or a negative error code.
+ * after a grid search).  Decode runs one workgroup per slice of a balanced
+ * partition: the rows are laid end to end and the line of all their tokens is
+ * cut into `num_splits` = W equal slices, whatever the spread of kv_lens.
+ * Rows (see attn_decode for the kernels):
+ *   - G = 1, 2, 4 (any D), VALU kernel: a row is (sequence, group of up to 8
+ *     adjacent KV heads, 4 at D = 256) when the KV head stride `kv_s_head`
+ *     equals D (heads of a token contiguous), else one KV head;
+ *   - other G at D = 64 or 128, MFMA kernel: a row is (sequence, group of 4,
+ *     2 or 1 adjacent KV heads -- the largest dividing Hkv -- and up to 32
+ *     query heads each), or with G > 32 (sequence, KV head, pass of G / Gk);
+ *   - other G at D = 32 or 256, VALU kernel: (sequence, KV head, pass over
+ *     a power-of-two share of its G query heads).
+ * Slices are four-wave workgroups for the first two (a slice of at least 256
+ * tokens; at most 3/4 of the compute units when a row holds 8 KV heads, one
+ * per unit otherwise) and one-wave workgroups for the third (at least 64
+ * tokens; three per unit with 8-head rows, two otherwise).  This planner
+ * returns W for `num_cus` compute units (0 = query the current device) and
+ * the longest row max_kv_len.  page_size 0 stands for a contiguous source
+ * (pass its K head stride as kv_s_head).  Host-only and deterministic;
+ * returns W >= 1, or a negative error code.
  */
 int attn_plan_splits(int B, int Hkv, int G, int D, int max_kv_len, int page_size, int64_t kv_s_head,
                      int num_cus);
@@ -126,9 +133,13 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int D, int num_splits);
  *               on the current device
  *   workspace   >= attn_decode_workspace_bytes(B, Hq, D, W) bytes, device,
  *               256-byte aligned (may be NULL when W = 1)
- * Supported: D in {32, 64, 128, 256}, any G = Hq/Hkv.  A wave handles Gk query
- * heads of a KV head (the largest power of two dividing G, at most 8); for
- * other G each (sequence, KV head) is streamed G / Gk times, once per pass.
+ * Supported: D in {32, 64, 128, 256}, any G = Hq/Hkv.  G = 1, 2 and 4 run the
+ * VALU kernel (dot products on the vector ALUs, a wave holding all G query
+ * heads of its KV heads).  Other G at D = 64 and 128 run the MFMA kernel:
+ * the Gm query heads of a KV head (the largest divisor of G that is at most
+ * 32) sit on the rows of bf16 16x16x32 MFMAs, so each KV head is read once
+ * (G / Gm times for G > 32).  Other G at D = 32 and 256 take passes over
+ * power-of-two shares of at most 8 heads, reading each KV head once per pass.
  * Launches the split kernel, then the combine kernel, which merges rows
  * spread over several slices and zeroes rows without keys.
  */
