@@ -111,6 +111,21 @@ def test_serving_paged_decode(B):
     assert_close(out, ref, atol=2e-3, what="B=%d serving, secondary bar" % B)
 
 
+@pytest.mark.parametrize("Hq,Hkv,seed", [(64, 8, 1012), (32, 1, 1013)])
+def test_mfma_serving_paged_decode(Hq, Hkv, seed):
+    """The MFMA decode at the size its bench lines time: B = 128, kv_lens
+    U[512, 4096], page size 16, planner split count; G = 8 (four KV heads a
+    row, one wave each) and G = 32 (one KV head a row, 32 query heads on two
+    16-row blocks).  Every sequence and head against the oracle, at the pass
+    bar and the secondary 2e-3 bar (every row has at least 512 keys)."""
+    case = workloads.paged_decode_case(seed, 128, Hq, Hkv, 128, (512, 4096), 16, device=DEV)
+    out = run_paged(case, 0)
+    cpu = {k: (v.cpu() if torch.is_tensor(v) else v) for k, v in case.items()}
+    ref, _ = oracle_paged(cpu)
+    assert_close(out, ref, what="Hq=%d Hkv=%d serving" % (Hq, Hkv))
+    assert_close(out, ref, atol=2e-3, what="Hq=%d Hkv=%d serving, secondary bar" % (Hq, Hkv))
+
+
 def partition_bounds(lens, rows_per_seq, W):
     """Per row: (slot, first key, end key) of each piece under the balanced
     partition (rows laid end to end, W equal slices of the line, the piece of
