@@ -51,7 +51,6 @@ __device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
 constexpr int BKM = 32;              // keys per tile
 constexpr int NWM = 4;               // waves per workgroup (slice)
 constexpr float kRaise = 8.0f;       // lazy reference raise threshold, log2 units
-constexpr int VTLD = BKM + 8;        // V^T row stride in LDS (elements): 80 bytes
 
 // Maximum over the four 16-lane rows of the wave (lanes l, l^16, l^32,
 // l^48), in every lane, with two VALU row swaps.
@@ -69,16 +68,11 @@ __device__ __forceinline__ float sum_over_rows(float x) {
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// First V^T slot of staging group kg (keys 4kg .. 4kg+3 of the tile).
-__device__ __forceinline__ int vslot(int kg) { return kg < 4 ? 8 * kg : 8 * (kg - 4) + 4; }
-
-// Loads of one tile held by a lane.
+// K of one tile held by a lane (A-operand layout, see above).
 template <int D>
 struct MTile {
     static constexpr int NS = D / 32;                 // 32-dim steps
-    static constexpr int VG = (BKM / 4) * (D / 8) / 64;   // V groups (4 keys x 8 dims) per lane
     uint4 k[2][NS];
-    uint4 v[VG][4];
 };
 
 __device__ __forceinline__ uint4 ld16_nt(const uint16_t *ptr) {
@@ -87,24 +81,41 @@ __device__ __forceinline__ uint4 ld16_nt(const uint16_t *ptr) {
     return make_uint4(t.x, t.y, t.z, t.w);
 }
 
-// 4 keys x 8 dims (one uint4 per key) -> V^T rows 8c .. 8c+7, slots base .. base+3.
-__device__ __forceinline__ void stage_group(uint16_t *vt, int c, int base, const uint4 (&v)[4]) {
-    const uint32_t k0[4] = {v[0].x, v[0].y, v[0].z, v[0].w};
-    const uint32_t k1[4] = {v[1].x, v[1].y, v[1].z, v[1].w};
-    const uint32_t k2[4] = {v[2].x, v[2].y, v[2].z, v[2].w};
-    const uint32_t k3[4] = {v[3].x, v[3].y, v[3].z, v[3].w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        // v_perm selectors: bytes 0-3 from the second operand, 4-7 from the
-        // first; 0x05040100 = (b.lo16, a.lo16), 0x07060302 = (b.hi16, a.hi16).
-        uint2 lo, hi;
-        lo.x = __builtin_amdgcn_perm(k1[e], k0[e], 0x05040100u);
-        lo.y = __builtin_amdgcn_perm(k3[e], k2[e], 0x05040100u);
-        hi.x = __builtin_amdgcn_perm(k1[e], k0[e], 0x07060302u);
-        hi.y = __builtin_amdgcn_perm(k3[e], k2[e], 0x07060302u);
-        *reinterpret_cast<uint2 *>(&vt[(8 * c + 2 * e) * VTLD + base]) = lo;
-        *reinterpret_cast<uint2 *>(&vt[(8 * c + 2 * e + 1) * VTLD + base]) = hi;
-    }
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+// 16 bytes a lane from global memory straight into LDS (global_load_lds,
+// non-temporal): lane l's bytes land at dst + 16 l (dst is wave-uniform).
+__device__ __forceinline__ void copy16_to_lds(const uint16_t *src, uint16_t *dst) {
+    __builtin_amdgcn_global_load_lds(src, (lds_void_t *)dst, 16, 0, 2);
+}
+
+// A V tile in LDS holds the tile's 32 keys in natural order, one D-dim row
+// per key, its 16-byte chunks permuted by an XOR with an even value that
+// depends on the key (so the 16 rows a transposed operand read takes fall
+// on different banks; the same chunk pair stays adjacent).  Physical chunk
+// of chunk c of row `key`:
+template <int D>
+__device__ __forceinline__ int vchunk(int key, int c) {
+    constexpr int NCH = D / 8, RPB = 256 / (2 * D);   // chunks per row, rows per 256-byte bank line
+    return c ^ (2 * ((key / RPB) % (NCH / 2)));
+}
+
+// s_waitcnt operand that waits for at most n vector memory operations
+// (expcnt and lgkmcnt left at their maximum).
+constexpr int vm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// Wait until at most N vector memory operations are in flight.  The s_nop
+// after it matters: with global_load_lds copies in flight the compiler asks
+// for vmcnt(0) before any use of a register loaded earlier, and it folds
+// that demand into a wait that directly precedes the use.  Behind the s_nop
+// this wait is counted first, the older loads are retired by it, and the
+// compiler adds nothing.
+template <int N>
+__device__ __forceinline__ void wait_tiles() {
+    __builtin_amdgcn_s_waitcnt(vm_wait(N));
+    asm volatile("s_nop 0");
 }
 
 // KV modes: contiguous K/V; paged, V read key by key; paged with a page size
@@ -122,13 +133,19 @@ __global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void decode_mfma_kernel(const
     constexpr int NS = D / 32;    // depth steps of S^T
     constexpr int NM = D / 16;    // 16-dim blocks of O^T
     constexpr int VCH = D / 8;    // 16-byte chunks of a key row
-    constexpr int VG = MTile<D>::VG;
-    static_assert(VG >= 1 && (BKM / 4) * VCH == 64 * VG, "V staging covers the tile");
+    constexpr int KPI = 64 / VCH; // keys per V load instruction (1 KB)
+    constexpr int NVL = BKM / KPI;           // V load instructions per tile
+    constexpr int NLD = 2 * NS + NVL;        // vector memory instructions per tile
     constexpr int F = 2 + 4 * NM;                              // merge floats per lane and block
-    constexpr int VT_ELEMS = D * VTLD;                         // one wave's V^T tile
+    constexpr int VB_ELEMS = BKM * D;                          // one V tile
     constexpr int XCH_FLOATS = NWT > 1 ? NWM * NB * F * 64 : 0;
-    constexpr int LDS_BYTES = (NWM * VT_ELEMS * 2 > XCH_FLOATS * 4) ? NWM * VT_ELEMS * 2 : XCH_FLOATS * 4;
-    __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
+    constexpr int T0_ELEMS = (NWM * VB_ELEMS > 2 * XCH_FLOATS) ? NWM * VB_ELEMS : 2 * XCH_FLOATS;
+    // The waves' first and second V tiles sit in two separate arrays (the
+    // first also holds the merge area): the compiler then knows that reads
+    // of one tile do not depend on copies still landing in the other and
+    // waits only for the tile it reads.
+    __shared__ __attribute__((aligned(16))) uint16_t vt0[T0_ELEMS];
+    __shared__ __attribute__((aligned(16))) uint16_t vt1[NWM * VB_ELEMS];
     __shared__ int32_t pages[kDecodeMaxSplitPages];
 
     const int lane = threadIdx.x & 63;
@@ -138,8 +155,7 @@ __global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void decode_mfma_kernel(const
     const int hw = wv % HG, wt = wv / HG;        // this wave's head in the row, tile phase
     const int Gm = p.G_all / p.passes;           // query heads per KV head and row
     const int HPR = HG * Gm;                     // query heads per row
-    uint16_t *vt = reinterpret_cast<uint16_t *>(lds) + wv * VT_ELEMS;
-    float *xch = reinterpret_cast<float *>(lds);
+    float *xch = reinterpret_cast<float *>(vt0);
 
     const RowScan rs = scan_rows(p);
     const int T = rs.total;
@@ -237,48 +253,41 @@ __global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void decode_mfma_kernel(const
             // The phases below are kept in program order (sched_barrier):
             // hoisting a tile's loads above the previous compute would hold
             // three tiles in registers.
-            auto issue = [&](int k, MTile<D> &t) {
+            // issue: K into registers (A-operand layout), V straight into the
+            // LDS tile `vb` (global_load_lds, 16 bytes a lane, 1 KB of LDS a
+            // instruction: KPI keys of natural rows, chunks swizzled).
+            auto issue = [&](int k, MTile<D> &t, uint16_t *vb) {
                 __builtin_amdgcn_sched_barrier(0);
                 const int base = jb + (wt + NWT * k) * BKM;
+                // Every page lookup of the tile first, then its loads.
+                uint64_t ko[2], vo[NVL];
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) ko[kb] = koff(base + 16 * kb + g16);
+                const int kl = lane / VCH, pc = lane % VCH;   // key in the instruction, physical chunk
+#pragma unroll
+                for (int n = 0; n < NVL; ++n) {
+                    const int tk = KPI * n + kl;              // key of the tile
+                    const int c = vchunk<D>(tk, pc);          // the chunk this lane carries
+                    if constexpr (MODE == kPagedQuads) {
+                        // the key's group of four starts on a multiple of 4
+                        // and the page size is one: they share a page
+                        const int jq = base + (tk & ~3);
+                        vo[n] = voff(jq) + (uint32_t)min(tk & 3, max(last - jq, 0)) * s_slot + 8 * c;
+                    } else {
+                        vo[n] = voff(base + tk) + 8 * c;
+                    }
+                }
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
-                    const uint16_t *kr = kbase + koff(base + 16 * kb + g16) + 8 * lg;
+                    const uint16_t *kr = kbase + ko[kb] + 8 * lg;
 #pragma unroll
                     for (int s = 0; s < NS; ++s) t.k[kb][s] = ld16_nt(kr + 32 * s);
                 }
 #pragma unroll
-                for (int gi = 0; gi < VG; ++gi) {
-                    const int q = lane + 64 * gi, kg = q / VCH, c = q % VCH;
-                    if constexpr (MODE == kPagedQuads) {
-                        // the group's four keys start on a multiple of 4 and
-                        // the page size is one: they share a page
-                        const int j = base + 4 * kg;
-                        const int jr = last - j;   // keys past the end repeat the last one
-                        const uint64_t o0 = voff(j);
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            t.v[gi][i] = ld16_nt(vbase + o0 + (uint32_t)min(i, max(jr, 0)) * s_slot + 8 * c);
-                    } else {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) t.v[gi][i] = ld16_nt(vbase + voff(base + 4 * kg + i) + 8 * c);
-                    }
-                }
+                for (int n = 0; n < NVL; ++n)
+                    copy16_to_lds(vbase + vo[n], vb + KPI * n * D);
             };
-            auto stage = [&](const MTile<D> &t) {
-                __builtin_amdgcn_sched_barrier(0);
-                // the previous tile's V^T reads come before these writes
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-#pragma unroll
-                for (int gi = 0; gi < VG; ++gi) {
-                    const int q = lane + 64 * gi, kg = q / VCH, c = q % VCH;
-                    stage_group(vt, c, vslot(kg), t.v[gi]);
-                }
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            };
-            auto compute = [&](int k, const MTile<D> &t) {
+            auto compute = [&](int k, const MTile<D> &t, const uint16_t *vb) {
                 __builtin_amdgcn_sched_barrier(0);
                 const int tbase = jb + (wt + NWT * k) * BKM;
                 // S^T blocks: keys 16 kb + 4 lg + i, head 16 nb + g16.
@@ -293,6 +302,28 @@ __global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void decode_mfma_kernel(const
                     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                         for (int nb = 0; nb < NB; ++nb) st[nb][kb] = mfma16(as_bf16x8(t.k[kb][s]), qf[nb][s], st[nb][kb]);
+                // V^T operands of O^T += V^T . P^T, read now so that their
+                // latency hides under the softmax.  Lane: dim 16 m + g16,
+                // keys 4 lg .. +3 and 16 + 4 lg .. +3 (the order of the lane
+                // group's eight S^T values), from two transposed reads:
+                // within a 16-lane group, lane i receives element i % 4 of the
+                // 8-byte segments that lanes i/4, i/4 + 4, i/4 + 8, i/4 + 12
+                // address, so lane j addresses dims 16 m + 4 (j % 4) .. +3 of
+                // key 4 lg + j / 4 (then 16 + 4 lg + j / 4).
+                bf16x8_t va[NM];
+                const int ka = 4 * lg + (g16 >> 2), kbk = 16 + 4 * lg + (g16 >> 2);
+#pragma unroll
+                for (int m = 0; m < NM; ++m) {
+                    const int c = 2 * m + ((g16 & 3) >> 1), e = 4 * (g16 & 1);
+                    const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_v4i16_t *)(vb + ka * D + 8 * vchunk<D>(ka, c) + e));
+                    const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_v4i16_t *)(vb + kbk * D + 8 * vchunk<D>(kbk, c) + e));
+                    va[m] = __builtin_bit_cast(
+                        bf16x8_t, make_uint4(__builtin_bit_cast(uint2, lo).x, __builtin_bit_cast(uint2, lo).y,
+                                             __builtin_bit_cast(uint2, hi).x, __builtin_bit_cast(uint2, hi).y));
+                }
+                __builtin_amdgcn_sched_barrier(0);
                 // key 16 kb + i of the lane is admitted iff skip <= it < room
                 const int room = j1 - (tbase + 4 * lg), skip = j0 - (tbase + 4 * lg);
                 uint32_t pw[NB][4];
@@ -328,38 +359,37 @@ __global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void decode_mfma_kernel(const
                 }
                 // O^T += V^T . P^T
 #pragma unroll
-                for (int m = 0; m < NM; ++m) {
-                    const bf16x8_t va =
-                        as_bf16x8(*reinterpret_cast<const uint4 *>(&vt[(16 * m + g16) * VTLD + 8 * lg]));
+                for (int m = 0; m < NM; ++m)
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb)
-                        oacc[nb][m] = mfma16(va, as_bf16x8(make_uint4(pw[nb][0], pw[nb][1], pw[nb][2], pw[nb][3])),
+                        oacc[nb][m] = mfma16(va[m], as_bf16x8(make_uint4(pw[nb][0], pw[nb][1], pw[nb][2], pw[nb][3])),
                                              oacc[nb][m]);
-                }
             };
 
             // Two tiles in flight at every wait: tile k + 1 is issued before
-            // tile k is staged, tile k + 2 as soon as tile k is computed.
-            // Every issue in the loop is unconditional: a load issued under
-            // a condition would make the compiler wait for all of them.
-            // Past the end every key is clamped to the piece's last one, so
-            // such a tile reads one key row (never used).
+            // tile k is computed, tile k + 2 right after.  The V tiles arrive
+            // in LDS outside the compiler's view, so the wait for tile k
+            // (vmcnt: only tile k + 1's NLD instructions still in flight) is
+            // explicit.  Every issue in the loop is unconditional: a load
+            // issued under a condition would make the compiler wait for all
+            // of them.  Past the end every key is clamped to the piece's last
+            // one, so such a tile reads one key row (never used); nothing is
+            // left in flight when the loop ends (the LDS is reused next).
             if (ntw > 0) {
                 MTile<D> ra, rb;
-                issue(0, ra);
+                uint16_t *va_t = vt0 + wv * VB_ELEMS, *vb_t = vt1 + wv * VB_ELEMS;
+                issue(0, ra, va_t);
                 int k = 0;
                 for (; k + 1 < ntw; k += 2) {
-                    issue(k + 1, rb);
-                    stage(ra);
-                    compute(k, ra);
-                    issue(k + 2, ra);
-                    stage(rb);
-                    compute(k + 1, rb);
+                    issue(k + 1, rb, vb_t);
+                    wait_tiles<NLD>();
+                    compute(k, ra, va_t);
+                    issue(k + 2, ra, va_t);
+                    wait_tiles<NLD>();
+                    compute(k + 1, rb, vb_t);
                 }
-                if (k < ntw) {
-                    stage(ra);
-                    compute(k, ra);
-                }
+                __builtin_amdgcn_s_waitcnt(vm_wait(0));
+                if (k < ntw) compute(k, ra, va_t);
             }
         }
 
