@@ -21,16 +21,18 @@
 //   O^T (D x 16 heads)     += V^T (D x 32) . P^T (32 x 16)      D/16 MFMA
 // per row block.  K comes straight from HBM in the A-operand layout (lane l:
 // key l % 16 of a 16-key block, 8 dims at 8 (l / 16) of a 32-dim step).  V
-// is loaded as 4 keys x 8 dims per lane and transposed in registers into a
-// wave-private LDS tile V^T, whose key order puts keys 4g..4g+3 and
-// 16+4g..16+4g+3 at slots 8g..8g+7: exactly the eight S^T values lane
-// group g holds, so P^T feeds the second MFMA from registers.  In the
+// is copied from HBM straight into a wave-private LDS tile of natural key
+// rows (global_load_lds) and read back transposed (ds_read_b64_tr_b16) as
+// V^T operands holding keys 4g..4g+3 and 16+4g..16+4g+3: exactly the eight
+// S^T values lane group g holds, so P^T feeds the second MFMA from
+// registers.  In the
 // transposed form lane l always holds query head l % 16 of a block, so the
 // softmax statistics are per-lane scalars reduced over the four lane groups
 // with two row swaps.  Scores are scaled after the dot product (csrc commit
 // that moved the scale after Q.K^T); the reference is raised lazily (by more
-// than 2^8, base 2), as in decode.hip.  Two register stages: while one tile
-// is staged and computed the next one's K and V are in flight.
+// than 2^8, base 2), as in decode.hip.  Two stages: while one tile is
+// computed the next one's K (registers) and V (the other LDS tile) are in
+// flight.
 #include "decode_common.hpp"
 #include "device_common.hpp"
 #include "kernels.hpp"
