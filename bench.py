@@ -96,6 +96,22 @@ def workload_desc(name):
             % (w["B"], w["Hq"], w["Hkv"], w["ps"], kv))
 
 
+def decode_kernel_label(w, slices):
+    """Name of the split kernel a paged D = 128 workload runs (the library's
+    row layout rule): group sizes 1, 2, 4 on the VALU kernel, others on MFMA
+    rows."""
+    G, Hkv = w["Hq"] // w["Hkv"], w["Hkv"]
+    if G in (1, 2, 4):
+        return "decode_split_kernel<128,%d,%d,paged,4> (balanced partition, %d slices)" % (
+            G, 8 if Hkv % 8 == 0 else 1, slices)
+    gm = min(G, 32)
+    while G % gm:
+        gm -= 1
+    hg = 1 if G // gm > 1 else 4 if Hkv % 4 == 0 else 2 if Hkv % 2 == 0 else 1
+    return "decode_mfma_kernel<128,%d,%d,%d> (balanced partition, %d slices)" % (
+        (gm + 15) // 16, 2 if w["ps"] % 4 == 0 else 1, hg, slices)
+
+
 def rotation_count(bytes_per_call):
     """Input sets to rotate so >= 1.5 GB is read between two uses of a set."""
     return max(2, math.ceil(1.5e9 / bytes_per_call))
@@ -301,9 +317,7 @@ def main():
     # --- timed region: K whole calls, then the per-kernel breakdown ---------
     r = bench_decode(torch, pa, dev, args.workload, args.steps, args.warmup, args.num_splits)
     w = DECODE_WORKLOADS[args.workload]
-    G = w["Hq"] // w["Hkv"]
-    kernel = "decode_split_kernel<128,%d,%d,paged,%d> (balanced partition, %d slices)" % (
-        min(G & -G, 8), 8 if w["Hkv"] % 8 == 0 else 1, 4 if (G & -G) <= 4 else 1, r["num_splits"])
+    kernel = decode_kernel_label(w, r["num_splits"])
     tr = load_traffic(args.workload)
     roofline = {"bound": "hbm", "achieved": r["kernel_GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(r["kernel_GB/s"] / HBM_PEAK_GBS, 4),
