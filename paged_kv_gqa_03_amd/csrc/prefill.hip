@@ -24,9 +24,12 @@
 // equal runs of 64-key tiles, each writes an unnormalised fp32 partial
 // (o, m, l) per row and head, and a combine merges them by log-sum-exp.
 //
-// Per KV tile of 64 keys the workgroup stages K row-major and V transposed
-// (d-major, keys permuted) in LDS; the transpose is done in registers while
-// staging.  Each wave then runs, with v_mfma_f32_16x16x32_bf16, per row block
+// Per KV tile of 64 keys the workgroup stages K and V in LDS.  At D = 128
+// with one team both are copied from HBM straight into LDS as natural key
+// rows (global_load_lds) and V^T operands are read back transposed
+// (ds_read_b64_tr_b16); otherwise K is stored row-major and V transposed
+// (d-major, keys permuted) from registers.  Each wave then runs, with
+// v_mfma_f32_16x16x32_bf16, per row block
 //   S^T (64 keys x 16 rows) = K (64 x 128) . Q^T (128 x 16)     16 MFMA
 //   O^T (128 x 16)        += V^T (128 x 64) . P^T (64 x 16)     16 MFMA
 // and every K or V^T operand read from LDS feeds both row blocks.  In this
@@ -38,10 +41,11 @@
 // in fp32 after the dot product (csrc commit that moved the scale after
 // Q.K^T).  Keys past the causal frontier of the tile are never loaded.
 //
-// Pipeline (per team): two LDS buffers and one register stage.  While a
-// tile is computed from one buffer, the team's next tile (loaded a whole
-// iteration earlier) is stored into the other, and the one after is
-// loaded; one barrier per tile.  Page ids come from a slice of the block table staged in
+// Pipeline (per team): two LDS buffers.  Register staging: while a tile is
+// computed from one buffer, the team's next tile (loaded a whole iteration
+// earlier) is stored into the other, and the one after is loaded.  LDS
+// copies: while a tile is computed from one buffer, the next one lands in
+// the other.  One barrier per tile.  Page ids come from a slice of the block table staged in
 // LDS, so no global load sits between a tile's address math and its K/V
 // loads, and the keep-mask words of a tile travel with its stage.
 #include <type_traits>
@@ -92,6 +96,52 @@ __device__ __forceinline__ int v_phys(int k) {
     const int k32 = k & 31;
     return (k & ~31) + 8 * ((k32 & 15) >> 2) + 4 * (k32 >> 4) + (k32 & 3);
 }
+
+// LDS-copy staging (D = 128 with one team of four waves): a K or V tile is
+// 64 natural key rows of 256 B copied from HBM straight into LDS
+// (global_load_lds, 16 bytes a lane, four key rows an instruction), with
+// the 16-byte chunks of each row XOR-swizzled: K chunk c of key k sits at
+// c ^ (k & 15), so the 16 rows an S^T operand read takes (one chunk each)
+// fall on 16 different 16-byte bank groups; V chunk c at c ^ 2 (k & 7), so
+// the four keys x four 8-byte pieces of a transposed read spread likewise.
+// V^T operands come back with ds_read_b64_tr_b16: within a 16-lane group,
+// lane i receives element i % 4 of the 8-byte pieces that lanes i/4,
+// i/4 + 4, i/4 + 8, i/4 + 12 address.
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+__device__ __forceinline__ int kchunk_swz(int key, int c) { return c ^ (key & 15); }
+__device__ __forceinline__ int vchunk_swz(int key, int c) { return c ^ (2 * (key & 7)); }
+
+// 16 bytes a lane from global memory into LDS at dst + 8 * lane (dst is
+// wave-uniform); non-temporal when nothing else reads the keys.
+__device__ __forceinline__ void copy16_to_lds(const uint16_t *src, uint16_t *dst, bool nt) {
+    if (nt) __builtin_amdgcn_global_load_lds(src, (lds_void_t *)dst, 16, 0, 2);
+    else __builtin_amdgcn_global_load_lds(src, (lds_void_t *)dst, 16, 0, 0);
+}
+
+// V^T operand of the LDS-copy tile at buf + v0 (64 key rows of 128 dims):
+// dims 16 m + g16 (g16 = lane % 16) of keys 32 s2 + 4 lq .. +3 and 32 s2 +
+// 16 + 4 lq .. +3, the key order of the lane group's P^T values.  Each
+// address is one index off the LDS array itself: the compiler attaches the
+// array's alias scope only to accesses a few address steps from it, and a
+// read without it waits for every LDS copy in flight.
+__device__ __forceinline__ bf16x8_t vt_operand(const uint16_t *buf, int v0, int m, int s2, int lane) {
+    const int g16 = lane & 15, lq = lane >> 4;
+    const int ka = 32 * s2 + 4 * lq + (g16 >> 2), kb = ka + 16;
+    const int c = 2 * m + ((g16 & 3) >> 1), e = 4 * (g16 & 1);
+    const v4i16_t lo =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t *)(buf + (v0 + ka * 128 + 8 * vchunk_swz(ka, c) + e)));
+    const v4i16_t hi =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t *)(buf + (v0 + kb * 128 + 8 * vchunk_swz(kb, c) + e)));
+    const uint2 l = __builtin_bit_cast(uint2, lo), h = __builtin_bit_cast(uint2, hi);
+    return as_bf16x8(make_uint4(l.x, l.y, h.x, h.y));
+}
+
+// s_waitcnt operand: every vector memory operation of the wave complete
+// (expcnt and lgkmcnt left at their maximum).
+constexpr int kWaitVmem0 = (7 << 4) | (15 << 8);
 
 // Per-thread share of one KV tile in flight: four K chunks, four V chunks.
 struct Stage {
@@ -315,9 +365,16 @@ __global__ __launch_bounds__(256 * TEAMS, D <= 128 ? 2 : 1) void prefill_kernel(
     constexpr int NM = D / 16;    // 16-row blocks of O^T
     constexpr int CPR = D / 8;    // 16-byte chunks per K/V row
     constexpr int XCH = D / 2 + 4;                            // floats per lane handed from team 1 to team 0
-    constexpr int SBUF = BK * KLD + D * VLD;                  // one K tile + one V^T tile (elements)
+    // D = 128 with one team stages by LDS copies into natural key rows;
+    // otherwise through registers into padded K rows and a V^T tile.
+    constexpr bool kDma = D == 128 && TEAMS == 1;
+    constexpr int SBUF = kDma ? 2 * BK * D : BK * KLD + D * VLD;   // one K tile + one V (or V^T) tile
     static_assert(TEAMS == 1 || 4 * XCH * 64 * 4 <= 4 * SBUF * 2, "team exchange must fit the stage buffers");
-    __shared__ __attribute__((aligned(16))) uint16_t stage_lds[TEAMS * 2 * SBUF];   // [team][buffer]
+    __shared__ __attribute__((aligned(16))) uint16_t stage_lds[kDma ? 8 : TEAMS * 2 * SBUF];   // [team][buffer]
+    // LDS-copy buffers, one array each: the compiler then knows that reads
+    // of one do not wait on copies still landing in the other.
+    __shared__ __attribute__((aligned(16))) uint16_t dma0[kDma ? SBUF : 8];
+    __shared__ __attribute__((aligned(16))) uint16_t dma1[kDma ? SBUF : 8];
     __shared__ int32_t pages[kPages];
     constexpr int MROWS = MASK == 3 ? R : 1;                  // mask rows per tile
     constexpr int NQ = MASK == 3 && R > 32 ? R / 32 : 1;      // mask rows per thread
@@ -454,6 +511,8 @@ __global__ __launch_bounds__(256 * TEAMS, D <= 128 ? 2 : 1) void prefill_kernel(
     const int64_t seq_base = PAGED ? 0 : (int64_t)b * p.k_sb;   // contiguous: the sequence's K/V
     sc.kbase = p.k + seq_base + (int64_t)g * p.s_head + sc.cc * 8;
     sc.vbase = p.v + seq_base + (int64_t)g * p.s_head + sc.cc * 8;
+    const uint16_t *kseq = p.k + seq_base + (int64_t)g * p.s_head;   // LDS-copy staging: row starts
+    const uint16_t *vseq = p.v + seq_base + (int64_t)g * p.s_head;
     const int32_t *bt_row = PAGED ? p.bt + b * p.bt_sb : nullptr;
     Stage st_regs[NPASS];
     auto load_tile = [&](int kt) {
@@ -465,6 +524,23 @@ __global__ __launch_bounds__(256 * TEAMS, D <= 128 ? 2 : 1) void prefill_kernel(
         if (!stager) return;
 #pragma unroll
         for (int ps = 0; ps < NPASS; ++ps) store_stage<D>(sc, kg0 + KGS * ps, st_regs[ps], k_lds, v_lds);
+    };
+    // LDS-copy staging of tile kt into buffer t (K rows, then V rows at
+    // + BK * D): wave w copies keys 16 w .. 16 w + 15, four per instruction
+    // (lane l: key 4 i + l / 16 of them, physical chunk l % 16).  Keys past
+    // the chunk end repeat its last key.
+    auto issue_tile = [&](int kt, uint16_t *t) __attribute__((always_inline)) {
+        const int kr = lane >> 4, pc = lane & 15;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int tk = 16 * w + 4 * i + kr;
+            const int key = min(kt * BK + tk, sc.c1 - 1);
+            uint64_t off;
+            if constexpr (PAGED) off = key_off(p, sc, key);
+            else off = (uint64_t)(uint32_t)key * (uint64_t)p.s_slot;
+            copy16_to_lds(kseq + off + 8 * kchunk_swz(tk, pc), t + (16 * w + 4 * i) * D, sc.stream);
+            copy16_to_lds(vseq + off + 8 * vchunk_swz(tk, pc), t + BK * D + (16 * w + 4 * i) * D, sc.stream);
+        }
     };
 
     MaskCtx mc;
@@ -489,10 +565,9 @@ __global__ __launch_bounds__(256 * TEAMS, D <= 128 ? 2 : 1) void prefill_kernel(
     // length and causal tests are skipped.
     auto kbuf = [&](int buf) { return stage_lds + (2 * team + buf) * SBUF; };
     auto vbuf = [&](int buf) { return stage_lds + (2 * team + buf) * SBUF + BK * KLD; };
-    auto tile_math = [&](auto full_c, int kt, int buf) {
+    auto tile_math = [&](auto full_c, int kt, int buf, const uint16_t *kl, const uint16_t *vl)
+        __attribute__((always_inline)) {
         constexpr bool FULL = decltype(full_c)::value;
-        const uint16_t *kl = kbuf(buf);
-        const uint16_t *vl = vbuf(buf);
         // S^T blocks: keys 16kb + 4lq + i of the tile, rows myrow[rb].
         // Depth step outermost: eight independent accumulators per step, so
         // no MFMA waits on the result of the one before it.
@@ -510,8 +585,9 @@ __global__ __launch_bounds__(256 * TEAMS, D <= 128 ? 2 : 1) void prefill_kernel(
         for (int s = 0; s < NS; ++s)
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
-                const bf16x8_t a = as_bf16x8(
-                    *reinterpret_cast<const uint4 *>(&kl[(16 * kb + (lane & 15)) * KLD + 32 * s + 8 * lq]));
+                const int krow = 16 * kb + (lane & 15);
+                const bf16x8_t a = as_bf16x8(*reinterpret_cast<const uint4 *>(
+                    kDma ? &kl[krow * D + 8 * kchunk_swz(krow, 4 * s + lq)] : &kl[krow * KLD + 32 * s + 8 * lq]));
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb) st[rb][kb] = mfma16(a, qf[rb][s], st[rb][kb]);
             }
@@ -593,7 +669,9 @@ __global__ __launch_bounds__(256 * TEAMS, D <= 128 ? 2 : 1) void prefill_kernel(
                 pb[rb] = as_bf16x8(make_uint4(pw[rb][s2][0], pw[rb][s2][1], pw[rb][s2][2], pw[rb][s2][3]));
 #pragma unroll
             for (int m = 0; m < NM; ++m) {
-                const bf16x8_t a = as_bf16x8(*reinterpret_cast<const uint4 *>(
+                bf16x8_t a;
+                if constexpr (kDma) a = vt_operand(kl, BK * D, m, s2, lane);
+                else a = as_bf16x8(*reinterpret_cast<const uint4 *>(
                     &vl[(16 * m + (lane & 15)) * VLD + v_col(16 * m, 4 * s2 + lq)]));
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb) oacc[rb][m] = mfma16(a, pb[rb], oacc[rb][m]);
@@ -604,8 +682,16 @@ __global__ __launch_bounds__(256 * TEAMS, D <= 128 ? 2 : 1) void prefill_kernel(
         __builtin_amdgcn_s_setprio(0);
     };
     auto compute = [&](int kt, int buf) {
-        if (kt * BK + BK <= lim_wave) tile_math(std::true_type{}, kt, buf);
-        else tile_math(std::false_type{}, kt, buf);
+        if (kt * BK + BK <= lim_wave) tile_math(std::true_type{}, kt, buf, kbuf(buf), vbuf(buf));
+        else tile_math(std::false_type{}, kt, buf, kbuf(buf), vbuf(buf));
+    };
+    // LDS-copy tiles: the buffer is a compile-time choice (bc), so each
+    // instance reads one array.
+    auto compute_dma = [&](int kt, auto bc) __attribute__((always_inline)) {
+        constexpr int B = decltype(bc)::value;
+        const uint16_t *t = B == 0 ? dma0 : dma1;
+        if (kt * BK + BK <= lim_wave) tile_math(std::true_type{}, kt, B, t, t + BK * D);
+        else tile_math(std::false_type{}, kt, B, t, t + BK * D);
     };
 
     // Keys in chunks whose pages fit the LDS slice; chunks start on tile
@@ -626,6 +712,42 @@ __global__ __launch_bounds__(256 * TEAMS, D <= 128 ? 2 : 1) void prefill_kernel(
         // This team's tiles of the chunk: t0 + team, t0 + team + TEAMS, ...
         const int kt0 = t0 + team;
         const int nit = (t1 - t0 + TEAMS - 1) / TEAMS;
+        if constexpr (kDma) {
+            // Tile kt + 1 lands in one buffer while tile kt is computed from
+            // the other; tile kt + 2 goes out once every wave is past kt.
+            // The copies are outside the compiler's register tracking, so
+            // the wait for them (all of the wave's vector memory operations,
+            // mask loads included) is explicit, before the barrier.
+            if (kt0 < t1) {
+                issue_tile(kt0, dma0);
+                if constexpr (MASK != 0) load_mask<MASK, NQ>(mc, ttid, n, kt0, mst);
+                __builtin_amdgcn_s_waitcnt(kWaitVmem0);
+                if constexpr (MASK != 0) store_mask<MASK, NQ, MROWS>(mst, ttid, mbits[0][0]);
+            }
+            if (kt0 + 1 < t1) {
+                issue_tile(kt0 + 1, dma1);
+                if constexpr (MASK != 0) load_mask<MASK, NQ>(mc, ttid, n, kt0 + 1, mst);
+            }
+            __syncthreads();
+            auto step = [&](auto bc, int it) __attribute__((always_inline)) {
+                constexpr int B = decltype(bc)::value;
+                const int kt = kt0 + it;
+                compute_dma(kt, bc);
+                if constexpr (MASK != 0)
+                    if (kt + 1 < t1) store_mask<MASK, NQ, MROWS>(mst, ttid, mbits[0][B ^ 1]);
+                __builtin_amdgcn_s_waitcnt(kWaitVmem0);
+                __syncthreads();
+                if (kt + 2 < t1) {
+                    issue_tile(kt + 2, B == 0 ? dma0 : dma1);
+                    if constexpr (MASK != 0) load_mask<MASK, NQ>(mc, ttid, n, kt + 2, mst);
+                }
+            };
+            for (int it = 0; it < nit; it += 2) {
+                step(std::integral_constant<int, 0>{}, it);
+                if (it + 1 < nit) step(std::integral_constant<int, 1>{}, it + 1);
+            }
+            continue;
+        }
         if (kt0 < t1) {
             load_tile(kt0);
             if constexpr (MASK != 0) load_mask<MASK, NQ>(mc, ttid, n, kt0, mst);
