@@ -365,16 +365,17 @@ __global__ __launch_bounds__(256 * TEAMS, D <= 128 ? 2 : 1) void prefill_kernel(
     constexpr int NM = D / 16;    // 16-row blocks of O^T
     constexpr int CPR = D / 8;    // 16-byte chunks per K/V row
     constexpr int XCH = D / 2 + 4;                            // floats per lane handed from team 1 to team 0
-    // D = 128 with one team stages by LDS copies into natural key rows;
-    // otherwise through registers into padded K rows and a V^T tile.
-    constexpr bool kDma = D == 128 && TEAMS == 1;
+    // D = 128 stages by LDS copies into natural key rows; other head dims
+    // through registers into padded K rows and a V^T tile.
+    constexpr bool kDma = D == 128;
     constexpr int SBUF = kDma ? 2 * BK * D : BK * KLD + D * VLD;   // one K tile + one V (or V^T) tile
-    static_assert(TEAMS == 1 || 4 * XCH * 64 * 4 <= 4 * SBUF * 2, "team exchange must fit the stage buffers");
+    static_assert(TEAMS == 1 || kDma || 4 * XCH * 64 * 4 <= 4 * SBUF * 2, "team exchange must fit the stage buffers");
+    static_assert(TEAMS == 1 || !kDma || 2 * XCH * 64 * 4 <= TEAMS * SBUF * 2, "team exchange must fit the copy buffers");
     __shared__ __attribute__((aligned(16))) uint16_t stage_lds[kDma ? 8 : TEAMS * 2 * SBUF];   // [team][buffer]
-    // LDS-copy buffers, one array each: the compiler then knows that reads
-    // of one do not wait on copies still landing in the other.
-    __shared__ __attribute__((aligned(16))) uint16_t dma0[kDma ? SBUF : 8];
-    __shared__ __attribute__((aligned(16))) uint16_t dma1[kDma ? SBUF : 8];
+    // LDS-copy buffers [team], one array per buffer: the compiler then knows
+    // that reads of one do not wait on copies still landing in the other.
+    __shared__ __attribute__((aligned(16))) uint16_t dma0[kDma ? TEAMS * SBUF : 8];
+    __shared__ __attribute__((aligned(16))) uint16_t dma1[kDma ? TEAMS * SBUF : 8];
     __shared__ int32_t pages[kPages];
     constexpr int MROWS = MASK == 3 ? R : 1;                  // mask rows per tile
     constexpr int NQ = MASK == 3 && R > 32 ? R / 32 : 1;      // mask rows per thread
@@ -587,7 +588,8 @@ __global__ __launch_bounds__(256 * TEAMS, D <= 128 ? 2 : 1) void prefill_kernel(
             for (int kb = 0; kb < 4; ++kb) {
                 const int krow = 16 * kb + (lane & 15);
                 const bf16x8_t a = as_bf16x8(*reinterpret_cast<const uint4 *>(
-                    kDma ? &kl[krow * D + 8 * kchunk_swz(krow, 4 * s + lq)] : &kl[krow * KLD + 32 * s + 8 * lq]));
+                    kDma ? &kl[team * SBUF + krow * D + 8 * kchunk_swz(krow, 4 * s + lq)]
+                         : &kl[krow * KLD + 32 * s + 8 * lq]));
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb) st[rb][kb] = mfma16(a, qf[rb][s], st[rb][kb]);
             }
@@ -670,7 +672,7 @@ __global__ __launch_bounds__(256 * TEAMS, D <= 128 ? 2 : 1) void prefill_kernel(
 #pragma unroll
             for (int m = 0; m < NM; ++m) {
                 bf16x8_t a;
-                if constexpr (kDma) a = vt_operand(kl, BK * D, m, s2, lane);
+                if constexpr (kDma) a = vt_operand(kl, team * SBUF + BK * D, m, s2, lane);
                 else a = as_bf16x8(*reinterpret_cast<const uint4 *>(
                     &vl[(16 * m + (lane & 15)) * VLD + v_col(16 * m, 4 * s2 + lq)]));
 #pragma unroll
@@ -689,9 +691,10 @@ __global__ __launch_bounds__(256 * TEAMS, D <= 128 ? 2 : 1) void prefill_kernel(
     // instance reads one array.
     auto compute_dma = [&](int kt, auto bc) __attribute__((always_inline)) {
         constexpr int B = decltype(bc)::value;
+        // the array itself: the team's offset is part of each read's index
         const uint16_t *t = B == 0 ? dma0 : dma1;
-        if (kt * BK + BK <= lim_wave) tile_math(std::true_type{}, kt, B, t, t + BK * D);
-        else tile_math(std::false_type{}, kt, B, t, t + BK * D);
+        if (kt * BK + BK <= lim_wave) tile_math(std::true_type{}, kt, B, t, t);
+        else tile_math(std::false_type{}, kt, B, t, t);
     };
 
     // Keys in chunks whose pages fit the LDS slice; chunks start on tile
@@ -719,27 +722,27 @@ __global__ __launch_bounds__(256 * TEAMS, D <= 128 ? 2 : 1) void prefill_kernel(
             // the wait for them (all of the wave's vector memory operations,
             // mask loads included) is explicit, before the barrier.
             if (kt0 < t1) {
-                issue_tile(kt0, dma0);
+                issue_tile(kt0, dma0 + team * SBUF);
                 if constexpr (MASK != 0) load_mask<MASK, NQ>(mc, ttid, n, kt0, mst);
                 __builtin_amdgcn_s_waitcnt(kWaitVmem0);
-                if constexpr (MASK != 0) store_mask<MASK, NQ, MROWS>(mst, ttid, mbits[0][0]);
+                if constexpr (MASK != 0) store_mask<MASK, NQ, MROWS>(mst, ttid, mbits[team][0]);
             }
-            if (kt0 + 1 < t1) {
-                issue_tile(kt0 + 1, dma1);
-                if constexpr (MASK != 0) load_mask<MASK, NQ>(mc, ttid, n, kt0 + 1, mst);
+            if (kt0 + TEAMS < t1) {
+                issue_tile(kt0 + TEAMS, dma1 + team * SBUF);
+                if constexpr (MASK != 0) load_mask<MASK, NQ>(mc, ttid, n, kt0 + TEAMS, mst);
             }
             __syncthreads();
             auto step = [&](auto bc, int it) __attribute__((always_inline)) {
                 constexpr int B = decltype(bc)::value;
-                const int kt = kt0 + it;
-                compute_dma(kt, bc);
+                const int kt = kt0 + TEAMS * it;
+                if (kt < t1) compute_dma(kt, bc);
                 if constexpr (MASK != 0)
-                    if (kt + 1 < t1) store_mask<MASK, NQ, MROWS>(mst, ttid, mbits[0][B ^ 1]);
+                    if (kt + TEAMS < t1) store_mask<MASK, NQ, MROWS>(mst, ttid, mbits[team][B ^ 1]);
                 __builtin_amdgcn_s_waitcnt(kWaitVmem0);
                 __syncthreads();
-                if (kt + 2 < t1) {
-                    issue_tile(kt + 2, B == 0 ? dma0 : dma1);
-                    if constexpr (MASK != 0) load_mask<MASK, NQ>(mc, ttid, n, kt + 2, mst);
+                if (kt + 2 * TEAMS < t1) {
+                    issue_tile(kt + 2 * TEAMS, (B == 0 ? dma0 : dma1) + team * SBUF);
+                    if constexpr (MASK != 0) load_mask<MASK, NQ>(mc, ttid, n, kt + 2 * TEAMS, mst);
                 }
             };
             for (int it = 0; it < nit; it += 2) {
@@ -779,7 +782,9 @@ __global__ __launch_bounds__(256 * TEAMS, D <= 128 ? 2 : 1) void prefill_kernel(
     if constexpr (TEAMS == 2) {
         // Team 1's (O, reference, sum) go through the stage buffers (free
         // since the last barrier) to the matching wave of team 0, which merges.
-        float *xch = reinterpret_cast<float *>(stage_lds) + w * (XCH * 64);
+        // With LDS-copy buffers, waves 0-1 use the first array, 2-3 the second.
+        float *xch = kDma ? reinterpret_cast<float *>(w < 2 ? dma0 : dma1) + (w & 1) * (XCH * 64)
+                          : reinterpret_cast<float *>(stage_lds) + w * (XCH * 64);
         if (team == 1) {
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) {
