@@ -25,8 +25,8 @@
 // (o, m, l) per row and head, and a combine merges them by log-sum-exp.
 //
 // Per KV tile of 64 keys the workgroup stages K and V in LDS.  At D = 128
-// with one team both are copied from HBM straight into LDS as natural key
-// rows (global_load_lds) and V^T operands are read back transposed
+// both are copied from HBM straight into LDS as natural key rows
+// (global_load_lds) and V^T operands are read back transposed
 // (ds_read_b64_tr_b16); otherwise K is stored row-major and V transposed
 // (d-major, keys permuted) from registers.  Each wave then runs, with
 // v_mfma_f32_16x16x32_bf16, per row block
@@ -97,7 +97,7 @@ __device__ __forceinline__ int v_phys(int k) {
     return (k & ~31) + 8 * ((k32 & 15) >> 2) + 4 * (k32 >> 4) + (k32 & 3);
 }
 
-// LDS-copy staging (D = 128 with one team of four waves): a K or V tile is
+// LDS-copy staging (D = 128): a K or V tile is
 // 64 natural key rows of 256 B copied from HBM straight into LDS
 // (global_load_lds, 16 bytes a lane, four key rows an instruction), with
 // the 16-byte chunks of each row XOR-swizzled: K chunk c of key k sits at
