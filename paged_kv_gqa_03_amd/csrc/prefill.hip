@@ -45,9 +45,10 @@
 // computed from one buffer, the team's next tile (loaded a whole iteration
 // earlier) is stored into the other, and the one after is loaded.  LDS
 // copies: while a tile is computed from one buffer, the next one lands in
-// the other.  One barrier per tile.  Page ids come from a slice of the block table staged in
-// LDS, so no global load sits between a tile's address math and its K/V
-// loads, and the keep-mask words of a tile travel with its stage.
+// the other.  One barrier per tile.  Page ids come from a slice of the
+// block table staged in LDS, so no global load sits between a tile's
+// address math and its K/V loads, and the keep-mask words of a tile travel
+// with its stage.
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -97,10 +98,10 @@ __device__ __forceinline__ int v_phys(int k) {
     return (k & ~31) + 8 * ((k32 & 15) >> 2) + 4 * (k32 >> 4) + (k32 & 3);
 }
 
-// LDS-copy staging (D = 128): a K or V tile is
-// 64 natural key rows of 256 B copied from HBM straight into LDS
-// (global_load_lds, 16 bytes a lane, four key rows an instruction), with
-// the 16-byte chunks of each row XOR-swizzled: K chunk c of key k sits at
+// LDS-copy staging (D = 128): a K or V tile is 64 natural key rows of
+// 256 B copied from HBM straight into LDS (global_load_lds, 16 bytes a lane,
+// four key rows an instruction), with the 16-byte chunks of each row
+// XOR-swizzled: K chunk c of key k sits at
 // c ^ (k & 15), so the 16 rows an S^T operand read takes (one chunk each)
 // fall on 16 different 16-byte bank groups; V chunk c at c ^ 2 (k & 7), so
 // the four keys x four 8-byte pieces of a transposed read spread likewise.
