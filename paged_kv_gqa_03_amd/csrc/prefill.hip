@@ -583,17 +583,34 @@ __global__ __launch_bounds__(256 * TEAMS, D <= 128 ? 2 : 1) void prefill_kernel(
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) st[rb][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        // K operand of depth step s, key block kb.
+        auto kop = [&](int s, int kb) __attribute__((always_inline)) {
+            const int krow = 16 * kb + (lane & 15);
+            return as_bf16x8(*reinterpret_cast<const uint4 *>(
+                kDma ? &kl[team * SBUF + krow * D + 8 * kchunk_swz(krow, 4 * s + lq)]
+                     : &kl[krow * KLD + 32 * s + 8 * lq]));
+        };
+        // Operand reads run two depth steps ahead: step s + 2 is read while
+        // step s's MFMAs run (scheduling barriers keep that order), so an
+        // MFMA never waits on a read issued just before it.
+        bf16x8_t ka[2][4];
 #pragma unroll
-        for (int s = 0; s < NS; ++s)
+        for (int j = 0; j < (NS < 2 ? NS : 2); ++j)
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                const int krow = 16 * kb + (lane & 15);
-                const bf16x8_t a = as_bf16x8(*reinterpret_cast<const uint4 *>(
-                    kDma ? &kl[team * SBUF + krow * D + 8 * kchunk_swz(krow, 4 * s + lq)]
-                         : &kl[krow * KLD + 32 * s + 8 * lq]));
+            for (int kb = 0; kb < 4; ++kb) ka[j][kb] = kop(j, kb);
 #pragma unroll
-                for (int rb = 0; rb < RB; ++rb) st[rb][kb] = mfma16(a, qf[rb][s], st[rb][kb]);
+        for (int s = 0; s < NS; ++s) {
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) st[rb][kb] = mfma16(ka[s & 1][kb], qf[rb][s], st[rb][kb]);
+            if (s + 2 < NS) {
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) ka[s & 1][kb] = kop(s + 2, kb);
             }
+        }
+        __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_setprio(0);
         // Scores of keys not admitted become -inf (then P = 0).
 #pragma unroll
@@ -646,6 +663,25 @@ __global__ __launch_bounds__(256 * TEAMS, D <= 128 ? 2 : 1) void prefill_kernel(
                 for (int m = 0; m < NM; ++m) oacc[rb][m] *= alpha;
             }
         }
+        // V^T operand of 16-dim block m, key half s2.
+        auto vop = [&](int m, int s2) __attribute__((always_inline)) {
+            if constexpr (kDma) return vt_operand(kl, team * SBUF + BK * D, m, s2, lane);
+            else return as_bf16x8(*reinterpret_cast<const uint4 *>(
+                &vl[(16 * m + (lane & 15)) * VLD + v_col(16 * m, 4 * s2 + lq)]));
+        };
+        // O^T runs in stages of MB 16-dim blocks, two stages of V^T operands
+        // in flight; the first two are read here, so that their latency hides
+        // under the exponentials.
+        constexpr int MB = NM >= 2 ? 2 : 1;
+        constexpr int NMS = NM / MB;
+        bf16x8_t va[2][MB][2];
+#pragma unroll
+        for (int j = 0; j < (NMS < 2 ? NMS : 2); ++j)
+#pragma unroll
+            for (int mm = 0; mm < MB; ++mm)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) va[j][mm][s2] = vop(MB * j + mm, s2);
+        __builtin_amdgcn_sched_barrier(0);
         // P = 2^(s * scale * log2 e - reference), rounded to bf16 pairs.
         uint32_t pw[RB][2][4];
 #pragma unroll
@@ -663,25 +699,36 @@ __global__ __launch_bounds__(256 * TEAMS, D <= 128 ? 2 : 1) void prefill_kernel(
                 }
         }
         __builtin_amdgcn_s_setprio(2);
-        // O^T += V^T . P^T, and the row sums.
+        // O^T += V^T . P^T, stage j + 2's operands read while stage j's
+        // MFMAs run; then the row sums.
+        bf16x8_t pb[2][RB];
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-            bf16x8_t pb[RB];
+        for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
-                pb[rb] = as_bf16x8(make_uint4(pw[rb][s2][0], pw[rb][s2][1], pw[rb][s2][2], pw[rb][s2][3]));
+                pb[s2][rb] = as_bf16x8(make_uint4(pw[rb][s2][0], pw[rb][s2][1], pw[rb][s2][2], pw[rb][s2][3]));
 #pragma unroll
-            for (int m = 0; m < NM; ++m) {
-                bf16x8_t a;
-                if constexpr (kDma) a = vt_operand(kl, team * SBUF + BK * D, m, s2, lane);
-                else a = as_bf16x8(*reinterpret_cast<const uint4 *>(
-                    &vl[(16 * m + (lane & 15)) * VLD + v_col(16 * m, 4 * s2 + lq)]));
+        for (int j = 0; j < NMS; ++j) {
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int rb = 0; rb < RB; ++rb) oacc[rb][m] = mfma16(a, pb[rb], oacc[rb][m]);
+            for (int mm = 0; mm < MB; ++mm)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb)
+                        oacc[rb][MB * j + mm] = mfma16(va[j & 1][mm][s2], pb[s2][rb], oacc[rb][MB * j + mm]);
+            if (j + 2 < NMS) {
+#pragma unroll
+                for (int mm = 0; mm < MB; ++mm)
+#pragma unroll
+                    for (int s2 = 0; s2 < 2; ++s2) va[j & 1][mm][s2] = vop(MB * (j + 2) + mm, s2);
             }
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb) lacc[rb] = mfma16(ones, pb[rb], lacc[rb]);
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) lacc[rb] = mfma16(ones, pb[s2][rb], lacc[rb]);
         __builtin_amdgcn_s_setprio(0);
     };
     auto compute = [&](int kt, int buf) {
