@@ -48,7 +48,10 @@
 // the other.  One barrier per tile.  Page ids come from a slice of the
 // block table staged in LDS, so no global load sits between a tile's
 // address math and its K/V loads, and the keep-mask words of a tile travel
-// with its stage.
+// with its stage.  Inside a tile the LDS operand reads run ahead of the
+// MFMAs: K two depth steps ahead, V^T two stages of two 16-dim blocks ahead,
+// its first two stages read before the exponentials, so no MFMA waits on a
+// read issued just before it.
 #include <type_traits>
 
 #include "device_common.hpp"
