@@ -85,8 +85,8 @@ __global__ __launch_bounds__(256 * GPW, GPW == 1 ? 2 : 1) void swa_kernel(const 
     constexpr int NTH = 256 * GPW;        // threads
     constexpr int RPT = KT * 32 / NTH;    // staged 16-byte row chunks per thread
     __shared__ __attribute__((aligned(16))) uint8_t x_lds[KT * XLD];
-    __shared__ int32_t admit[KT];   // window position admitted (1) or masked (0)
-    __shared__ float inv_lds[KT];
+    __shared__ __attribute__((aligned(16))) int32_t admit[KT];   // window position admitted (1) or masked (0)
+    __shared__ __attribute__((aligned(16))) float inv_lds[KT];
     __shared__ __attribute__((aligned(16))) uint16_t p_lds_all[GPW][16 * PLD];
     __shared__ float red_max_all[GPW][4][16], red_sum_all[GPW][4][16];
 
@@ -180,21 +180,63 @@ __global__ __launch_bounds__(256 * GPW, GPW == 1 ? 2 : 1) void swa_kernel(const 
         // Scores of positions 32w .. 32w+31 (S^T blocks kb = 2w, 2w+1).
         float x[2][4];
         float mt = -INFINITY;
-        if (w < nkb) {
+        // Admission and inverse scale of the lane's eight positions (keys
+        // 16 (2w + h2) + 4 q4 + i), read as vectors: ahead of the MFMAs and
+        // kept for P' in the two-group kernel; after them, and again for P',
+        // in the one-group kernel, which has not the registers to hold them.
+        constexpr bool EARLY = GPW == 2;
+        int4 adm[2];
+        float4 ivs[2];
+        auto read_scales = [&](bool with_admit) __attribute__((always_inline)) {
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
-                const int kb = 2 * w + h2;
-                f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                const uint8_t *xr = &x_lds[(16 * kb + r) * XLD + 8 * q4];
+                const int key0 = 16 * (2 * w + h2) + 4 * q4;
+                if (with_admit) adm[h2] = *reinterpret_cast<const int4 *>(&admit[key0]);
+                ivs[h2] = *reinterpret_cast<const float4 *>(&inv_lds[key0]);
+            }
+        };
+        if (w < nkb) {
+            if constexpr (EARLY) read_scales(true);
+            // The wave's two 16-position blocks side by side (two independent
+            // accumulator chains); the operands of a group of depth steps are
+            // read one group ahead of the MFMAs that use them, so no MFMA
+            // waits on a read issued just before it.
+            const uint8_t *xr0 = &x_lds[(32 * w + r) * XLD + 8 * q4];
+            const uint8_t *xr1 = xr0 + 16 * XLD;
+            f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+            constexpr int SG = GPW == 2 ? 4 : 2;   // depth steps per group (fewer registers at GPW = 1)
+            constexpr int NG = 16 / SG;
+            uint2 cb[2][2][SG];
 #pragma unroll
-                for (int s = 0; s < 16; ++s) {
-                    const uint2 c8 = *reinterpret_cast<const uint2 *>(xr + 32 * s);
-                    acc = mfma16(fp8x8_to_bf16(c8.x, c8.y), qf[s], acc);
+            for (int i = 0; i < SG; ++i) {
+                cb[0][0][i] = *reinterpret_cast<const uint2 *>(xr0 + 32 * i);
+                cb[0][1][i] = *reinterpret_cast<const uint2 *>(xr1 + 32 * i);
+            }
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                __builtin_amdgcn_sched_barrier(0);
+                if (g + 1 < NG) {
+#pragma unroll
+                    for (int i = 0; i < SG; ++i) {
+                        cb[(g + 1) & 1][0][i] = *reinterpret_cast<const uint2 *>(xr0 + 32 * (SG * (g + 1) + i));
+                        cb[(g + 1) & 1][1][i] = *reinterpret_cast<const uint2 *>(xr1 + 32 * (SG * (g + 1) + i));
+                    }
                 }
 #pragma unroll
+                for (int i = 0; i < SG; ++i)
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2)
+                        acc[h2] = mfma16(fp8x8_to_bf16(cb[g & 1][h2][i].x, cb[g & 1][h2][i].y), qf[SG * g + i], acc[h2]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (!EARLY) read_scales(true);
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const int a4[4] = {adm[h2].x, adm[h2].y, adm[h2].z, adm[h2].w};
+                const float v4[4] = {ivs[h2].x, ivs[h2].y, ivs[h2].z, ivs[h2].w};
+#pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int key = 16 * kb + 4 * q4 + i;
-                    x[h2][i] = admit[key] ? acc[i] * p.sl2 * inv_lds[key] : -INFINITY;
+                    x[h2][i] = a4[i] ? acc[h2][i] * p.sl2 * v4[i] : -INFINITY;
                     mt = fmaxf(mt, x[h2][i]);
                 }
             }
@@ -215,6 +257,7 @@ __global__ __launch_bounds__(256 * GPW, GPW == 1 ? 2 : 1) void swa_kernel(const 
         M = M_new;
         float psum = 0.f;
         if (w < nkb) {
+            if constexpr (!EARLY) read_scales(false);
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
                 const int key0 = 16 * (2 * w + h2) + 4 * q4;
@@ -225,8 +268,8 @@ __global__ __launch_bounds__(256 * GPW, GPW == 1 ? 2 : 1) void swa_kernel(const 
                     psum += pv[i];
                 }
                 uint2 pk;
-                pk.x = pack_bf16(pv[0] * inv_lds[key0], pv[1] * inv_lds[key0 + 1]);
-                pk.y = pack_bf16(pv[2] * inv_lds[key0 + 2], pv[3] * inv_lds[key0 + 3]);
+                pk.x = pack_bf16(pv[0] * ivs[h2].x, pv[1] * ivs[h2].y);
+                pk.y = pack_bf16(pv[2] * ivs[h2].z, pv[3] * ivs[h2].w);
                 *reinterpret_cast<uint2 *>(&p_lds[r * PLD + key0]) = pk;
             }
         }
@@ -241,24 +284,46 @@ __global__ __launch_bounds__(256 * GPW, GPW == 1 ? 2 : 1) void swa_kernel(const 
             for (int m = 0; m < 4; ++m) oacc[a][m] *= alpha;
 
         // O^T for dims 128w .. 128w+127: block (mb, mm) covers dims
-        // 64mb + 4R + mm for A-row R.
-        for (int ks = 0; ks < nkb; ++ks) {
-            const bf16x8_t bp = __builtin_bit_cast(bf16x8_t,
-                *reinterpret_cast<const uint4 *>(&p_lds[r * PLD + 32 * ks + 8 * q4]));
+        // 64mb + 4R + mm for A-row R.  The next 32-position block's operands
+        // are read while this one's MFMAs run (reads past the tile's last
+        // block stay inside the staged arrays and go unused).
+        bf16x8_t bpb[2];
+        uint32_t dwb[2][2][8];
+        auto read_block = [&](int ks, int b) __attribute__((always_inline)) {
+            bpb[b] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(&p_lds[r * PLD + 32 * ks + 8 * q4]));
 #pragma unroll
             for (int a = 0; a < 2; ++a) {
-                const int mb = 2 * w + a;
-                const uint8_t *xc = &x_lds[(32 * ks + 8 * q4) * XLD + 64 * mb + 4 * r];
-                uint32_t dw[8];
+                const uint8_t *xc = &x_lds[(32 * ks + 8 * q4) * XLD + 64 * (2 * w + a) + 4 * r];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) dw[e] = *reinterpret_cast<const uint32_t *>(xc + e * XLD);
-                uint32_t lo[4], hi[4];
-                transpose4x4(dw[0], dw[1], dw[2], dw[3], lo);
-                transpose4x4(dw[4], dw[5], dw[6], dw[7], hi);
+                for (int e = 0; e < 8; ++e) dwb[b][a][e] = *reinterpret_cast<const uint32_t *>(xc + e * XLD);
+            }
+        };
+        // (The one-group kernel, at two workgroups per CU, has not the
+        // registers for the second block's operands: it reads each block
+        // just before its MFMAs.)
+        constexpr bool AHEAD = GPW == 2;
+        if constexpr (AHEAD) read_block(0, 0);
 #pragma unroll
-                for (int mm = 0; mm < 4; ++mm) oacc[a][mm] = mfma16(fp8x8_to_bf16(lo[mm], hi[mm]), bp, oacc[a][mm]);
+        for (int ks = 0; ks < KT / 32; ++ks) {
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (AHEAD) {
+                if (ks + 1 < KT / 32) read_block(ks + 1, (ks + 1) & 1);
+            }
+            if (ks < nkb) {
+                if constexpr (!AHEAD) read_block(ks, ks & 1);
+#pragma unroll
+                for (int a = 0; a < 2; ++a) {
+                    const uint32_t *dw = dwb[ks & 1][a];
+                    uint32_t lo[4], hi[4];
+                    transpose4x4(dw[0], dw[1], dw[2], dw[3], lo);
+                    transpose4x4(dw[4], dw[5], dw[6], dw[7], hi);
+#pragma unroll
+                    for (int mm = 0; mm < 4; ++mm)
+                        oacc[a][mm] = mfma16(fp8x8_to_bf16(lo[mm], hi[mm]), bpb[ks & 1], oacc[a][mm]);
+                }
             }
         }
+        __builtin_amdgcn_sched_barrier(0);
     }
 
     const float invL = L > 0.f ? 1.f / L : 0.f;
