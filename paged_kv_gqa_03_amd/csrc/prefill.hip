@@ -534,18 +534,43 @@ __global__ __launch_bounds__(256 * TEAMS, D <= 128 ? 2 : 1) void prefill_kernel(
     // + BK * D): wave w copies keys 16 w .. 16 w + 15, four per instruction
     // (lane l: key 4 i + l / 16 of them, physical chunk l % 16).  Keys past
     // the chunk end repeat its last key.
+    // The four key groups' offsets first (their page lookups from LDS go
+    // out together and are waited for once), then the eight copies, under
+    // one wave-uniform choice of the streaming hint.
     auto issue_tile = [&](int kt, uint16_t *t) __attribute__((always_inline)) {
         const int kr = lane >> 4, pc = lane & 15;
+        uint64_t off[4];
+        if constexpr (PAGED) {
+            uint32_t pi[4], slot[4];
+            int pg[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int tk = 16 * w + 4 * i + kr;
-            const int key = min(kt * BK + tk, sc.c1 - 1);
-            uint64_t off;
-            if constexpr (PAGED) off = key_off(p, sc, key);
-            else off = (uint64_t)(uint32_t)key * (uint64_t)p.s_slot;
-            copy16_to_lds(kseq + off + 8 * kchunk_swz(tk, pc), t + (16 * w + 4 * i) * D, sc.stream);
-            copy16_to_lds(vseq + off + 8 * vchunk_swz(tk, pc), t + BK * D + (16 * w + 4 * i) * D, sc.stream);
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t key = (uint32_t)min(kt * BK + 16 * w + 4 * i + kr, sc.c1 - 1);
+                pi[i] = divu32(key, p.ps_div);
+                slot[i] = key - pi[i] * p.ps;
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pg[i] = sc.pages[pi[i] - sc.first_pg];
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                off[i] = (uint64_t)(uint32_t)pg[i] * (uint32_t)p.s_page + slot[i] * (uint32_t)p.s_slot;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                off[i] = (uint64_t)(uint32_t)min(kt * BK + 16 * w + 4 * i + kr, sc.c1 - 1) * (uint64_t)p.s_slot;
         }
+        auto copies = [&](auto nt_c) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int tk = 16 * w + 4 * i + kr;
+                copy16_to_lds(kseq + off[i] + 8 * kchunk_swz(tk, pc), t + (16 * w + 4 * i) * D, decltype(nt_c)::value);
+                copy16_to_lds(vseq + off[i] + 8 * vchunk_swz(tk, pc), t + BK * D + (16 * w + 4 * i) * D,
+                              decltype(nt_c)::value);
+            }
+        };
+        if (__builtin_amdgcn_readfirstlane((int)sc.stream)) copies(std::true_type{});
+        else copies(std::false_type{});
     };
 
     MaskCtx mc;
