@@ -430,14 +430,24 @@ __global__ __launch_bounds__(256 * TEAMS, D <= 128 ? 2 : 1) void prefill_kernel(
             hq[rb] = hbase + w % HP;
         }
     }
-    const int q0 = p.dense_lq > 0 ? 0 : p.qo_indptr[b];
-    const int qn = p.dense_lq > 0 ? p.dense_lq : p.qo_indptr[b + 1] - q0;
-    const int n = p.kv_lens ? p.kv_lens[b] : p.kv_len_const;
+    // The sequence's row range, length and causal offset, loaded together:
+    // an array the call does not give is read at a stand-in address (the
+    // first word of Q, always readable) and its value replaced, so no load
+    // waits behind another.
+    const bool dense = p.dense_lq > 0;
+    const int32_t *stand_in = reinterpret_cast<const int32_t *>(p.q);
+    const int v_q0 = *(dense ? stand_in : p.qo_indptr + b);
+    const int v_q1 = *(dense ? stand_in : p.qo_indptr + b + 1);
+    const int v_n = *(p.kv_lens ? p.kv_lens + b : stand_in);
+    const int v_c = *(p.causal ? p.causal + b : stand_in);
+    const int q0 = dense ? 0 : v_q0;
+    const int qn = dense ? p.dense_lq : v_q1 - q0;
+    const int n = p.kv_lens ? v_n : p.kv_len_const;
     // Causality: an offset array (-1 = off for that sequence), or bottom-right
     // alignment c = n - qn for every sequence; key j is admitted for local row
     // i iff j <= c + i (c may be negative: early rows then see no key).
-    const bool causal_on = p.causal ? p.causal[b] >= 0 : p.causal_br != 0;
-    const int c = p.causal ? p.causal[b] : n - qn;
+    const bool causal_on = p.causal ? v_c >= 0 : p.causal_br != 0;
+    const int c = p.causal ? v_c : n - qn;
     const int64_t qrow0 = (int64_t)b * p.q_sb + (int64_t)q0 * p.q_st;   // Q row 0 of the sequence
     const int64_t orow0 = (int64_t)b * p.o_sb + (int64_t)q0 * p.o_st;
     const int row0 = ti * R;
