@@ -920,6 +920,48 @@ __global__ __launch_bounds__(256 * TEAMS, D <= 128 ? 2 : 1) void prefill_kernel(
         }
         return;
     }
+    // One team with 16-byte aligned output rows: each wave stages its
+    // normalised rows in its own LDS region (rows padded by 8 elements, so
+    // the 8-byte writes of a 16-row block hit distinct banks) and writes
+    // whole rows back with 16-byte stores, four 256-byte rows (D = 128) per
+    // instruction.  A block's 8-byte pieces scatter over 16 rows, and
+    // issuing them took about 12 times as long.  The stage buffers are free
+    // since the last barrier, and a wave reads back only what it wrote.
+    if constexpr (TEAMS == 1) {
+        const bool aligned16 = ((reinterpret_cast<uintptr_t>(p.o) | (uint64_t)orow0 * 2 | (uint64_t)p.o_st * 2 |
+                                 (uint64_t)p.o_sh * 2) & 15) == 0;
+        if (aligned16) {
+            constexpr int SD = D + 8;                 // staged row stride (elements)
+            constexpr int LU = D / 8;                 // lanes per row (16 bytes each)
+            constexpr int UPI = 64 / LU;              // rows per store instruction
+            constexpr int NI = RB * 16 / UPI;         // store instructions per wave
+            uint16_t *stg = kDma ? (w < 2 ? dma0 : dma1) + (w & 1) * (RB * 16 * SD)
+                                 : stage_lds + w * (RB * 16 * SD);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                const float l_row = lacc[rb][0];
+                const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
+#pragma unroll
+                for (int m = 0; m < NM; ++m) {
+                    uint2 wv;
+                    wv.x = pack_bf16(oacc[rb][m][0] * inv, oacc[rb][m][1] * inv);
+                    wv.y = pack_bf16(oacc[rb][m][2] * inv, oacc[rb][m][3] * inv);
+                    *reinterpret_cast<uint2 *>(stg + (rb * 16 + (lane & 15)) * SD + 16 * m + 4 * lq) = wv;
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < NI; ++k) {
+                const int u = k * UPI + lane / LU, c = lane % LU;   // staged row, 16-byte chunk
+                const int rb = u / 16, rr = u % 16;
+                const uint4 v = *reinterpret_cast<const uint4 *>(stg + u * SD + 8 * c);
+                const int row = row0 + (rb == 0 ? rboff[0] : rboff[RB - 1]) + rr;
+                const int h = rb == 0 ? hq[0] : hq[RB - 1];
+                if (row < qn)
+                    *reinterpret_cast<uint4 *>(p.o + orow0 + (int64_t)row * p.o_st + (int64_t)h * p.o_sh + 8 * c) = v;
+            }
+            return;
+        }
+    }
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         const float l_row = lacc[rb][0];

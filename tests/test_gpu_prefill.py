@@ -467,6 +467,37 @@ def test_prefill_full_grid_one_team(G, D, mask_ndim, ps):
     assert_close(run_prefill(case), oracle_prefill(case), what="full grid G=%d D=%d" % (G, D))
 
 
+@pytest.mark.parametrize("G,D,mask_ndim", [(4, 128, None), (2, 64, 3), (1, 32, None)])
+def test_prefill_one_team_output_rows_only_8_byte_aligned(G, D, mask_ndim):
+    """One-team grids stage each wave's output rows in LDS and write whole
+    rows with 16-byte stores when the output rows are 16-byte aligned.  Here
+    the output is a view 4 elements into a flat buffer (rows 8-byte aligned
+    only), so the kernel writes its 8-byte pieces directly: same result, and
+    nothing written outside the view.  The aligned path is the one every
+    other one-team test above takes."""
+    Hkv = 8
+    case = workloads.prefill_case(1200 + G * D, 96, Hkv * G, Hkv, D, (0, 120), (20, 70), 16,
+                                  mask_frac=None if mask_ndim is None else 0.2, mask_ndim=mask_ndim or 3)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert grid_workgroups(case) >= 2 * cus
+    R = pa.attn_prefill_tile_rows(D, G)
+    _, t2b, t2i = pa.attn_prefill_plan(case["q_lens"], R)
+    d = {k: case[k].to(DEV) for k in ("q", "k_pool", "v_pool", "block_table", "kv_lens", "qo_indptr",
+                                     "causal_offset")}
+    mask = case["mask"].to(DEV) if case["mask"] is not None else None
+    n = d["q"].numel()
+    flat = torch.zeros(n + 8, dtype=torch.bfloat16, device=DEV)
+    out = flat[4:4 + n].view(d["q"].shape)
+    assert out.data_ptr() % 16 == 8
+    pa.attn_paged_prefill(d["q"], d["qo_indptr"], t2b.to(DEV), t2i.to(DEV), d["k_pool"], d["v_pool"],
+                          d["block_table"], d["kv_lens"], out, 16, case["scale"],
+                          causal_offset=d["causal_offset"], mask=mask, tile_rows=R)
+    torch.cuda.synchronize()
+    assert_close(out, oracle_prefill(case), what="8-byte aligned output G=%d D=%d" % (G, D))
+    assert torch.equal(flat[:4].cpu(), torch.zeros(4, dtype=torch.bfloat16))
+    assert torch.equal(flat[4 + n:].cpu(), torch.zeros(4, dtype=torch.bfloat16))
+
+
 def test_split_prefill_full_grid_one_team():
     case = workloads.prefill_case(1150, 64, 32, 8, 128, (100, 900), (1, 40), 16)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
