@@ -418,6 +418,27 @@ __global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void decode_mfma_kernel(const
         }
         const bool direct = p.direct && lo == 0 && hi == n;
         const int64_t slot = (int64_t)r + w;
+        // Merge inputs of this wave (the waves of its head: references, sums
+        // and its 16-dim blocks m = wt, wt + NWT, ...), read from LDS all
+        // together before any of the math, so the reads do not wait one by
+        // one.
+        constexpr int MPW = NWT > 1 ? NM / NWT : 1;   // 16-dim blocks a wave merges
+        float xm[NB][NWT], xl[NB][NWT], xo[NB][MPW][4][NWT];
+        if constexpr (NWT > 1) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int t = 0; t < NWT; ++t) {
+                    const float *src = xch + (((hw + HG * t) * NB + nb) * F) * 64 + lane;
+                    xm[nb][t] = src[0];
+                    xl[nb][t] = src[64];
+#pragma unroll
+                    for (int mm = 0; mm < MPW; ++mm)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) xo[nb][mm][i][t] = src[(2 + 4 * (wt + NWT * mm) + i) * 64];
+                }
+            __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             const int hl = 16 * nb + g16;   // this lane's query head of the wave's KV head
@@ -426,14 +447,12 @@ __global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void decode_mfma_kernel(const
             if constexpr (NWT > 1) {
                 M = -INFINITY;
 #pragma unroll
-                for (int t = 0; t < NWT; ++t) M = fmaxf(M, xch[(((hw + HG * t) * NB + nb) * F) * 64 + lane]);
+                for (int t = 0; t < NWT; ++t) M = fmaxf(M, xm[nb][t]);
                 L = 0.f;
 #pragma unroll
                 for (int t = 0; t < NWT; ++t) {
-                    const int v = hw + HG * t;
-                    const float mv = xch[((v * NB + nb) * F) * 64 + lane];
-                    fv[t] = mv == -INFINITY ? 0.f : exp2_fast(mv - M);
-                    L += fv[t] * xch[((v * NB + nb) * F + 1) * 64 + lane];
+                    fv[t] = xm[nb][t] == -INFINITY ? 0.f : exp2_fast(xm[nb][t] - M);
+                    L += fv[t] * xl[nb][t];
                 }
             } else {
                 M = mref[nb];
@@ -442,19 +461,18 @@ __global__ __launch_bounds__(256, NB == 1 ? 2 : 1) void decode_mfma_kernel(const
             const float inv = L > 0.f ? 1.f / L : 0.f;
             const int64_t prow = slot * HPR + hw * Gm + hl;   // partial row of this head
 #pragma unroll
-            for (int m = 0; m < NM; ++m) {
-                if (m % NWT != wt) continue;
+            for (int mm = 0; mm < (NWT > 1 ? MPW : NM); ++mm) {
+                const int m = NWT > 1 ? wt + NWT * mm : mm;
                 float ov[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     if constexpr (NWT > 1) {
                         float acc = 0.f;
 #pragma unroll
-                        for (int t = 0; t < NWT; ++t)
-                            acc += fv[t] * xch[(((hw + HG * t) * NB + nb) * F + 2 + 4 * m + i) * 64 + lane];
+                        for (int t = 0; t < NWT; ++t) acc += fv[t] * xo[nb][mm][i][t];
                         ov[i] = acc;
                     } else {
-                        ov[i] = oacc[nb][m][i];
+                        ov[i] = oacc[nb][mm][i];
                     }
                 }
                 if (hl >= Gm) continue;
