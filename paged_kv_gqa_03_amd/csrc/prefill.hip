@@ -543,28 +543,49 @@ __global__ __launch_bounds__(256 * TEAMS, D <= 128 ? 2 : 1) void prefill_kernel(
     // LDS-copy staging of tile kt into buffer t (K rows, then V rows at
     // + BK * D): wave w copies keys 16 w .. 16 w + 15, four per instruction
     // (lane l: key 4 i + l / 16 of them, physical chunk l % 16).  Keys past
-    // the chunk end repeat its last key.
+    // the chunk end read keys of the chunk at or below its last key.
     // The four key groups' offsets first (their page lookups from LDS go
     // out together and are waited for once), then the eight copies, under
     // one wave-uniform choice of the streaming hint.
+    // Page size a multiple of 16, and slot index and slot stride below 2^24
+    // (their product, below 2^32, then comes from a 24-bit multiply).
+    const bool ps16 = (p.ps & 15) == 0 && p.ps < (1 << 24) && p.s_slot < (1 << 24);
     auto issue_tile = [&](int kt, uint16_t *t) __attribute__((always_inline)) {
         const int kr = lane >> 4, pc = lane & 15;
         uint64_t off[4];
         if constexpr (PAGED) {
-            uint32_t pi[4], slot[4];
-            int pg[4];
+            if (ps16) {
+                // The wave's 16 keys start on a multiple of 16, so with a page
+                // size that is one they share a page: one wave-uniform lookup.
+                // Past the chunk's last key the group is moved back to the
+                // last key's group (keys there are not admitted; they read
+                // keys of the same tile).
+                const int g = __builtin_amdgcn_readfirstlane(min(kt * BK + 16 * w, (sc.c1 - 1) & ~15));
+                const uint32_t gpi = divu32((uint32_t)g, p.ps_div);
+                const uint32_t pg = (uint32_t)__builtin_amdgcn_readfirstlane(sc.pages[gpi - sc.first_pg]);
+                const uint64_t pbase = (uint64_t)pg * (uint32_t)p.s_page;
+                const uint32_t kbase = gpi * (uint32_t)p.ps;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t key = (uint32_t)min(kt * BK + 16 * w + 4 * i + kr, sc.c1 - 1);
-                pi[i] = divu32(key, p.ps_div);
-                slot[i] = key - pi[i] * p.ps;
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t key = (uint32_t)min(g + 4 * i + kr, sc.c1 - 1);
+                    off[i] = pbase + ((key - kbase) & 0xffffffu) * ((uint32_t)p.s_slot & 0xffffffu);
+                }
+            } else {
+                uint32_t pi[4], slot[4];
+                int pg[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t key = (uint32_t)min(kt * BK + 16 * w + 4 * i + kr, sc.c1 - 1);
+                    pi[i] = divu32(key, p.ps_div);
+                    slot[i] = key - pi[i] * p.ps;
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) pg[i] = sc.pages[pi[i] - sc.first_pg];
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    off[i] = (uint64_t)(uint32_t)pg[i] * (uint32_t)p.s_page + slot[i] * (uint32_t)p.s_slot;
             }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) pg[i] = sc.pages[pi[i] - sc.first_pg];
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                off[i] = (uint64_t)(uint32_t)pg[i] * (uint32_t)p.s_page + slot[i] * (uint32_t)p.s_slot;
         } else {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
