@@ -271,7 +271,11 @@ int run_decode(pa::DecodeParams &p, int D, int G, bool paged, int max_kv_len, in
     if (p.B == 0) return ok();
     hipError_t e = L.NB ? pa::launch_decode_mfma(p, D, paged, stream) : pa::launch_decode(p, D, L.Gk, paged, stream);
     if (e != hipSuccess) return launch_status(e, "decode split kernel");
-    if (mode == 0) {
+    // One length for every row (no kv_lens), not zero, and W dividing R:
+    // every slice boundary falls on a row boundary, so each row lies in one
+    // slice and was written directly; nothing is left to combine.
+    const bool whole_rows = !p.kv_lens && p.kv_len_const > 0 && p.R % W == 0;
+    if (mode == 0 && !whole_rows) {
         // Rows spanning several slices are merged; empty rows are zeroed;
         // rows written directly are left alone.
         pa::DecodeCombineParams c = combine_params(workspace, p.B, p.Hq, D, W, p.ngrp, p.kv_lens,

@@ -245,6 +245,32 @@ def test_contiguous_decode_ragged_lengths(S):
     assert_close(out, ref)
 
 
+@pytest.mark.parametrize("Hq,Hkv,D", [(16, 4, 64), (32, 4, 128)])
+@pytest.mark.parametrize("S", [1, 2, 3, 4, 6, 8, 12, 24])
+def test_contiguous_decode_one_length_every_split_count(Hq, Hkv, D, S):
+    """No kv_lens, so every row has kv_len keys: when S divides the row count
+    every slice holds whole rows, all written by the split kernel, and no
+    combine runs; other S merge split rows.  The output starts as NaN, so a
+    row left unwritten fails.  (16, 4, 64) runs the VALU kernel, (32, 4, 128)
+    the MFMA one (G = 8)."""
+    case = workloads.contig_decode_case(31 + S, 6, Hq, Hkv, D, 300, device=DEV)
+    out = torch.full_like(case["q"], float("nan"))
+    pa.attn_decode(case["q"], case["k"], case["v"], out, case["scale"], num_splits=S)
+    torch.cuda.synchronize()
+    ref, _ = oracle.decode(case["q"].cpu(), case["k"].cpu(), case["v"].cpu(), case["scale"])
+    assert_close(out, ref, what="contiguous one length, S=%d" % S)
+    assert_close(out, ref, atol=2e-3, what="contiguous one length, S=%d, secondary bar" % S)
+
+
+@pytest.mark.parametrize("S", [1, 4])
+def test_contiguous_decode_zero_length_rows_are_zeroed(S):
+    case = workloads.contig_decode_case(41, 4, 16, 4, 64, 8, device=DEV)
+    out = torch.full_like(case["q"], float("nan"))
+    pa.attn_decode(case["q"], case["k"], case["v"], out, case["scale"], kv_len=0, num_splits=S)
+    torch.cuda.synchronize()
+    assert torch.equal(out.float().cpu(), torch.zeros(out.shape))
+
+
 def test_workspace_poisoned_with_nan_is_fully_overwritten():
     case = workloads.paged_decode_case(12, 6, 32, 8, 128, [1, 100, 900, 1500, 16, 1024], 16)
     S = 7
