@@ -130,9 +130,14 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int D, int num_splits);
  *   kv_lens  device int32 [B], each in [0, kv_len]; NULL = all equal kv_len
  *   scale    multiplies q.k before the softmax (normally 1/sqrt(D))
  *   num_splits  slices W of the balanced partition; 0 = attn_plan_splits()
- *               on the current device
+ *               on the current device, except that with kv_lens NULL and
+ *               kv_len > 0, when the rows (B times the KV head groups) number
+ *               between half that count and the count, W = the rows (one
+ *               slice per row; never above the planner's count)
  *   workspace   >= attn_decode_workspace_bytes(B, Hq, D, W) bytes, device,
  *               256-byte aligned (may be NULL when W = 1)
+ * With kv_lens NULL, kv_len > 0 and W dividing the rows, every slice holds
+ * whole rows, each written directly, and no combine kernel is launched.
  * Supported: D in {32, 64, 128, 256}, any G = Hq/Hkv.  G = 1, 2 and 4 run the
  * VALU kernel (dot products on the vector ALUs, a wave holding all G query
  * heads of its KV heads).  Other G at D = 64 and 128 run the MFMA kernel:

@@ -255,7 +255,8 @@ def attn_decode(q, k, v, out, scale, kv_lens=None, kv_len=None, num_splits=0, wo
         _ptr(k), k.stride(0), k.stride(1), k.stride(2),
         _ptr(v), v.stride(0), v.stride(1), v.stride(2),
         _ptr(out), out.stride(0), out.stride(1), _ptr(kv_lens), int(kv_len),
-        B, Hq, Hkv, D, float(scale), int(S), _ptr(ws), nbytes, _stream(stream)))
+        B, Hq, Hkv, D, float(scale), int(num_splits or (S if num_cus else 0)), _ptr(ws), nbytes,
+        _stream(stream)))
     return out
 
 

@@ -240,13 +240,20 @@ void *scratch_address(int *rc) {
 int run_decode(pa::DecodeParams &p, int D, int G, bool paged, int max_kv_len, int num_splits,
                void *workspace, size_t workspace_bytes, int page_size, int64_t kv_s_head, hipStream_t stream,
                int mode) {
+    const DecodeLayout L = decode_layout(p.Hkv, G, kv_s_head, D);
     int W = num_splits;
     if (W == 0) {
         W = attn_plan_splits(p.B, p.Hkv, G, D, max_kv_len, page_size, kv_s_head, 0);
         if (W < 0) return W;
+        // One length for every row: when the rows number between half the
+        // planned count and the count, one slice per row leaves the planned
+        // waves at least half busy and needs no combine (contiguous decode
+        // B = 16, 128 rows of 2048 keys: 30.3 against 31.1-31.9 us per call
+        // at 256 slices on MI355X).
+        const int64_t rows = (int64_t)p.B * L.ngrp;
+        if (mode == 0 && !p.kv_lens && p.kv_len_const > 0 && rows <= W && 2 * rows >= W) W = (int)rows;
     }
     if (W < 1 || W > kMaxWaves) return fail(ATTN_ERR_INVALID_ARG, "num_splits %d outside [1, %d]", W, kMaxWaves);
-    const DecodeLayout L = decode_layout(p.Hkv, G, kv_s_head, D);
     p.G_all = G;
     p.passes = L.passes;
     p.HW = L.HW;
